@@ -1,0 +1,24 @@
+"""CPU oracle for one EAGLE-3 speculative-decoding step.  TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, float64 numpy implementation of what the step computes, written
+from the pages' statement of the method (cited per function by page title and
+section).  Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU
+baseline leg may import it.  It shares no code with the HIP path and never
+imports it; the product path must never route through it.
+
+Modules
+  numerics  storage rounding, softmax / log-sum-exp, the fp32 decision helpers
+            and the integer inverse-CDF sampler
+  llama     the LLaMA-shaped target forward (tree-masked or causal) and the
+            EAGLE-3 draft head
+  tree      tree mask, depths, the static-branching builder and the dynamic
+            (confidence-ranked) builder
+  accept    greedy longest-path acceptance and chain rejection sampling
+  step      KV compaction and the vanilla / speculative driver loops
+
+Functions whose result no pin fixes say "parity unpinned" in their docstring:
+  tree.build_dynamic_tree  (the frontier/re-rank policy is this build's reading
+                            of a step the pages name but do not spell out;
+                            its invariants and hand-worked cases are pinned, the
+                            policy itself is not)
+"""

@@ -1,0 +1,135 @@
+"""Pins of acceptance: the greedy walk, and rejection sampling against its closed form
+(the emitted token is distributed exactly as the target p, Leviathan et al. A.1 as cited
+by "EAGLE-3: Engineering Implementation of LLM Inference Acceleration", III.5)."""
+import numpy as np
+from scipy.stats import chi2
+
+from oracle.accept import chain_rejection, emitted_row, greedy_walk
+from oracle.numerics import sample_inverse_cdf
+
+
+def test_greedy_walk_hand_cases():
+    tokens = [5, 1, 2, 3, 4, 7]
+    parents = [-1, 0, 0, 1, 1, 2]
+    # root predicts 2 -> node 2; node 2 predicts 7 -> node 5; node 5 predicts 9 (no child)
+    argmax = [2, 0, 7, 0, 0, 9]
+    assert greedy_walk(tokens, parents, argmax) == ([0, 2, 5], 9)
+    # nothing matches: path is the root only, next root is the root's argmax
+    assert greedy_walk(tokens, parents, [8, 0, 0, 0, 0, 0]) == ([0], 8)
+    assert emitted_row([5, 2, 7], 5) == [5, 2, 7, -1, -1]
+
+
+def _rand_dist(rng, V, conc=1.0):
+    p = rng.gamma(conc, 1.0, V)
+    return (p / p.sum()).astype(np.float32)
+
+
+def _draws(rng, n, K, V, p_rows, q_rows):
+    """First emitted token after the root for n independent cycles (drafts drawn from q)."""
+    out = np.empty(n, dtype=np.int64)
+    for s in range(n):
+        u = (rng.integers(0, 1 << 24, K + 1 + K) * 2.0 ** -24).astype(np.float32)
+        d = [sample_inverse_cdf(q_rows[j], u[K + 1 + j]) for j in range(K)]
+        n_acc, nxt = chain_rejection(d, q_rows, p_rows, u[:K + 1])
+        out[s] = d[0] if n_acc >= 1 else nxt
+    return out
+
+
+def _chi2_pvalue(counts, probs):
+    exp = probs * counts.sum()
+    order = np.argsort(exp)
+    # merge small bins until every expected count is >= 5
+    obs_m, exp_m, acc_o, acc_e = [], [], 0.0, 0.0
+    for i in order:
+        acc_o += counts[i]
+        acc_e += exp[i]
+        if acc_e >= 5:
+            obs_m.append(acc_o)
+            exp_m.append(acc_e)
+            acc_o = acc_e = 0.0
+    if acc_e > 0:
+        obs_m[-1] += acc_o
+        exp_m[-1] += acc_e
+    obs_m, exp_m = np.array(obs_m), np.array(exp_m)
+    stat = np.sum((obs_m - exp_m) ** 2 / exp_m)
+    return chi2.sf(stat, len(obs_m) - 1)
+
+
+def test_rejection_marginal_chi_square_v64():
+    rng = np.random.default_rng(1234)
+    V, K = 64, 1
+    p = np.stack([_rand_dist(rng, V) for _ in range(K + 1)])
+    q = np.stack([_rand_dist(rng, V) for _ in range(K)])
+    draws = _draws(rng, 100_000, K, V, p, q)
+    assert _chi2_pvalue(np.bincount(draws, minlength=V).astype(float), p[0].astype(np.float64)) > 1e-3
+
+
+def test_rejection_total_variation_v8():
+    rng = np.random.default_rng(77)
+    V, K = 8, 1
+    p = np.stack([_rand_dist(rng, V) for _ in range(K + 1)])
+    q = np.stack([_rand_dist(rng, V) for _ in range(K)])
+    draws = _draws(rng, 200_000, K, V, p, q)
+    tv = 0.5 * np.abs(np.bincount(draws, minlength=V) / len(draws) - p[0]).sum()
+    assert tv < 0.005
+
+
+def test_rejection_two_token_joint_v8():
+    """Chain of two drafts over a toy conditional model: the first two emitted tokens
+    follow p1(t1) p2(t2 | t1).  When a cycle stops after one token the next token is
+    drawn from the target directly (what the next cycle's root would be)."""
+    rng = np.random.default_rng(99)
+    V = 8
+    P1, Q1 = _rand_dist(rng, V), _rand_dist(rng, V)
+    P2 = np.stack([_rand_dist(rng, V) for _ in range(V)])
+    Q2 = np.stack([_rand_dist(rng, V) for _ in range(V)])
+    P3 = _rand_dist(rng, V)
+    n = 100_000
+    joint = np.zeros((V, V))
+    for s in range(n):
+        u = (rng.integers(0, 1 << 24, 6) * 2.0 ** -24).astype(np.float32)
+        d1 = sample_inverse_cdf(Q1, u[3])
+        d2 = sample_inverse_cdf(Q2[d1], u[4])
+        n_acc, nxt = chain_rejection([d1, d2], np.stack([Q1, Q2[d1]]), np.stack([P1, P2[d1], P3]), u[:3])
+        if n_acc == 0:
+            t1 = nxt
+            t2 = sample_inverse_cdf(P2[t1], u[5])
+        elif n_acc == 1:
+            t1, t2 = d1, nxt
+        else:
+            t1, t2 = d1, d2
+        joint[t1, t2] += 1
+    expect = (P1[:, None].astype(np.float64) * P2.astype(np.float64)).ravel()
+    assert _chi2_pvalue(joint.ravel(), expect) > 1e-3
+
+
+def test_acceptance_probability_worked_example():
+    """p(d) = 0.6, q(d) = 0.8: accepted with probability 0.75; p = 0.6, q = 0.4: always.
+    Exhaustive over the 2**24-point uniform grid."""
+    V = 4
+    grid = np.arange(1 << 24, dtype=np.float64) * 2.0 ** -24
+    for pd, qd, expect in [(0.6, 0.8, 0.75), (0.6, 0.4, 1.0)]:
+        p = np.array([pd, 1 - pd, 0, 0], np.float32)
+        q = np.array([qd, 1 - qd, 0, 0], np.float32)
+        ratio = np.float32(p[0] / q[0])
+        frac = np.mean(grid.astype(np.float32) < ratio)
+        assert abs(frac - expect) < 2e-7
+        # the routine's decision agrees on sampled uniforms
+        for u in grid[::1 << 18].astype(np.float32):
+            n_acc, _ = chain_rejection([0], q[None], np.stack([p, p]), np.array([u, 0.5], np.float32))
+            assert (n_acc == 1) == (u < ratio)
+
+
+def test_greedy_draft_residual_zeroes_the_draft_token():
+    """Greedy drafts (q one-hot): a rejected draft token can never be the replacement."""
+    rng = np.random.default_rng(8)
+    V = 16
+    p = _rand_dist(rng, V)
+    for d in range(V):
+        q = np.zeros(V, np.float32)
+        q[d] = 1
+        for u_final in np.linspace(0, 1 - 2.0 ** -24, 50).astype(np.float32):
+            u = np.array([0.9999, u_final], np.float32)
+            n_acc, nxt = chain_rejection([d], q[None], np.stack([p, p]), u)
+            if n_acc == 0:
+                assert nxt != d
