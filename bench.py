@@ -1,0 +1,188 @@
+"""Throughput of one EAGLE-3 speculative step (draft tree + verify + accept +
+compact) on one MI355X, on the LLaMA-3.1-8B-shaped workload with seeded
+random weights.
+
+Prints ONE JSON line: verified tree tokens/s (= batch * (n_nodes + 1) per step),
+ms per step, the roofline of the dominant kernel (the 64-row MFMA GEMM that
+streams the verify weights) from HIP events on the library's stream, and the
+CPU oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+BF16_PEAK = 2.5e15         # MI355X dense bf16 MFMA, flop/s
+
+
+def max_seq_for(w, steps):
+    return w.prompt_len + (steps + 2) * (w.depth + 1) + w.rows + (w.depth - 1) * w.topk + 64
+
+
+def run_gpu(w, steps, warmup, prof_out=None):
+    import torch
+
+    from speculative_decoding_step_amd import binding as B
+    from speculative_decoding_step_amd import configs
+    from speculative_decoding_step_amd.engine import Engine, Spec
+
+    t0 = time.time()
+    prompts = [p for p in configs.prompts_np(w)]
+    eng = Engine(w.shape, Spec.of(w), w.batch, max_seq_for(w, steps + warmup), w.target_seed, w.head_seed,
+                 prefill_chunk=512)
+    print(f"[bench] weights + context ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    eng.prefill(prompts)
+    torch.cuda.synchronize()
+    print(f"[bench] prefill done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        eng.step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done", file=sys.stderr, flush=True)
+    # timed region: exactly `steps` steps, HIP events on the library stream per kernel
+    B.eagle3_profile(eng.ctx, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eng.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    prof = {k: B.eagle3_profile_read(eng.ctx, k) for k in (B.PROF_GEMM_M64, B.PROF_GEMM_M16, B.PROF_ATTN)}
+    B.eagle3_profile(eng.ctx, False)
+    status = eng.device_status()
+    if status:
+        raise RuntimeError(f"device status flags {status:#x}")
+    eng.close()
+    return ms, prof
+
+
+def cpu_baseline(w):
+    """The oracle (float64 numpy) on a bounded sample of the same step.
+
+    Sample: the tree-verify target pass over the step's rows on 1-layer and
+    2-layer slices of the 8B shape (committed KV of prompt_len positions,
+    seeded), giving the per-layer and LM-head costs, plus the oracle's whole
+    draft stage (catch-up row, depth-D expansion, full-vocabulary head) on a
+    short committed draft context.  Step time = 32 layers + LM head + draft.
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.llama import KVCache, Shape, target_forward
+    from oracle.step import OracleSequence, SpecConfig
+    from oracle.tree import tree_mask
+    from speculative_decoding_step_amd import configs, synth
+
+    ms = w.shape
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    rng = np.random.default_rng(0)
+    P, n = w.prompt_len, w.rows
+    parents = [-1] + [int(rng.integers(0, i)) for i in range(1, n)]
+    dep = [0] * n
+    for i in range(1, n):
+        dep[i] = dep[parents[i]] + 1
+    m = tree_mask(parents)
+    vis = [list(np.nonzero(m[i])[0]) for i in range(n)]
+    toks = synth.tokens_np(1, "cpu_tree", n, ms.vocab)
+    times = {}
+    for L in (1, 2):
+        sms = configs.ModelShape(L, ms.d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, ms.vocab, ms.rope_theta,
+                                 (0, 0, min(1, L - 1)), ms.dtype)
+        W, H = configs.weights_np(sms, w.target_seed, w.head_seed)
+        shp = Shape(L, ms.d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, ms.vocab, ms.rope_theta, ms.eps,
+                    ms.dtype, sms.taps)
+        cache = KVCache(L, P + 1, ms.n_kv_heads, ms.head_dim)
+        for l in range(L):
+            cache.k[l][:P] = synth.normal_np(7, f"k{l}", (P, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
+            cache.v[l][:P] = synth.normal_np(7, f"v{l}", (P, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
+        cache.length = P
+        t0 = time.perf_counter()
+        target_forward(W, shp, cache, toks, P + np.array(dep), vis)
+        times[L] = time.perf_counter() - t0
+        if L == 2:
+            # draft stage on the same weights, committed draft context of 32 positions
+            spec = SpecConfig(w.mode, w.depth, w.topk, w.n_nodes)
+            seq = OracleSequence(W, H, shp, spec, 32 + 2 * n + w.depth * w.topk)
+            Pd = 32
+            seq.cache.length = Pd
+            seq.dcache.k[0][:Pd - 1] = synth.normal_np(8, "dk", (Pd - 1, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
+            seq.dcache.v[0][:Pd - 1] = synth.normal_np(8, "dv", (Pd - 1, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
+            seq.dcache.length = Pd - 1
+            seq.aux_new = synth.normal_np(9, "aux", (1, 3 * ms.d), 1.0, "bf16").astype(np.float64)
+            seq.next_tok = [int(toks[0])]
+            seq.root = int(toks[0])
+            t0 = time.perf_counter()
+            seq.draft_tree()
+            times["draft"] = time.perf_counter() - t0
+        del W, H
+    t_layer = times[2] - times[1]
+    t_head = max(times[1] - t_layer, 0.0)
+    t_step = ms.n_layers * t_layer + t_head + times["draft"]
+    work = times[1] + times[2] + times["draft"]
+    return {"value": round(w.batch * w.rows / t_step, 3), "unit": "verified tree tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"float64 numpy oracle, batch 1: tree verify of {n} rows over {P} committed positions on "
+                       f"1- and 2-layer slices of the 8B shape ({times[1]:.1f}s, {times[2]:.1f}s) and the draft "
+                       f"stage ({times['draft']:.1f}s); step = {ms.n_layers} x layer ({t_layer:.2f}s) + LM head "
+                       f"({t_head:.2f}s) + draft = {t_step:.1f}s; {work:.0f}s of CPU work")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_tree_b1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the step shards by sequence "
+              "with no exchange; run one process per GPU). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    from speculative_decoding_step_amd import configs
+
+    w = configs.WORKLOADS[args.workload]
+    ms, prof = run_gpu(w, args.steps, args.warmup)
+    rows = w.batch * w.rows
+    n64, t64, b64, f64 = prof[0]
+    achieved = b64 / (t64 / 1e3) if t64 > 0 else 0.0
+    line = {
+        "metric": "verified tree tokens/s",
+        "value": round(rows / (ms / 1e3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "us_per_step": round(ms * 1e3, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.shape.dtype,
+        "data": "synthetic: seeded N(0,0.02) weights, uniform prompt ids",
+        "config": {"workload": w.name, "batch": w.batch, "prompt_len": w.prompt_len, "tree_depth": w.depth,
+                   "topk": w.topk, "tree_nodes": w.n_nodes, "rows_per_step": rows},
+        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
+                     "kernel": "k_gemm_bf16<4> (64-row MFMA weight-streaming GEMM)",
+                     "launches_per_step": n64 / args.steps,
+                     "kernel_ms_per_step": round(t64 / args.steps, 4)},
+        "hbm_gbps_step": None,
+        "cpu_baseline": None,
+    }
+    algo_step_bytes = prof[0][2] + prof[1][2]
+    line["hbm_gbps_step"] = round(algo_step_bytes / args.steps / (ms / 1e3) / 1e9, 1)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,269 @@
+/*
+ * eagle3.h — C ABI of the MI355X (gfx950) EAGLE-3 speculative-decoding step.
+ *
+ * One step has five parts, each behind one call:
+ *   eagle3_draft_tree   the EAGLE-3 head (fused 3d->d FC over three target taps,
+ *                       [input_norm(e) ; hidden_norm(x)] into one decoder layer,
+ *                       shared LM head) drafts a tree by top-k expansion
+ *                       ("EAGLE-3: Engineering Implementation of LLM Inference
+ *                       Acceleration", VIII-IX and XI.1-XI.2; EAGLE-2's dynamic
+ *                       tree, VI.7 Draft Sequence);
+ *   eagle3_verify_tree  one target pass over every tree node with tree-masked
+ *                       attention at position prefix + depth ("Advanced
+ *                       speculative decoding: tree drafts and EAGLE", Why trees,
+ *                       Implementation: forward_with_mask);
+ *   eagle3_accept       greedy longest-path acceptance, or sequential rejection
+ *                       sampling with residual norm(max(0, p - q)) and a bonus
+ *                       token ("EAGLE-3: Engineering Implementation ...", III.5,
+ *                       X.3-X.6);
+ *   eagle3_compact_kv   the accepted nodes' K/V move to contiguous positions and
+ *                       the next catch-up inputs are gathered ("Advanced
+ *                       speculative decoding ...", Implementation, the note on
+ *                       compacting KV slots).
+ *
+ * Conventions
+ *   - Every pointer argument is a DEVICE pointer unless marked (host).
+ *   - The caller allocates every buffer (weights, KV caches, workspace, I/O) and
+ *     keeps it alive for the context's lifetime; the library borrows pointers,
+ *     never frees them and never allocates device memory.
+ *   - All calls are asynchronous on the context's stream, except where a
+ *     function says it synchronises.  One context serves one stream and is not
+ *     thread-safe; calls that overlap on one context race.
+ *   - Element type "T" is the shape's storage dtype: float for EAGLE3_F32,
+ *     bfloat16 (uint16 bits, round-to-nearest-even) for EAGLE3_BF16.
+ *   - Linear weights are [out_features, in_features] row-major (y = x W^T).
+ *   - Errors: synchronous argument checks return a nonzero eagle3_status and
+ *     launch nothing.  Data-dependent faults found on the device (a capacity
+ *     overflow, a malformed tree) set bits in the context's device status word
+ *     (read by eagle3_device_status) and the affected sequence's work is
+ *     skipped; no call traps or faults on such input.
+ */
+#ifndef EAGLE3_H
+#define EAGLE3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EAGLE3_OK = 0,
+  EAGLE3_EINVAL = 1,       /* bad argument: NULL, size out of range, bad shape */
+  EAGLE3_ECAPACITY = 2,    /* request exceeds max_batch / max_rows / workspace */
+  EAGLE3_EUNSUPPORTED = 3, /* valid but not supported (e.g. > 64 tree rows)     */
+  EAGLE3_EHIP = 4          /* a HIP runtime call failed                         */
+} eagle3_status;
+
+/* Device status bits (eagle3_device_status). */
+#define EAGLE3_DEV_KV_OVERFLOW   0x1  /* seq_len + rows exceeded the KV capacity  */
+#define EAGLE3_DEV_BAD_TREE      0x2  /* parent index >= child index, or < 0      */
+#define EAGLE3_DEV_BAD_TOKEN     0x4  /* token id outside [0, vocab)              */
+#define EAGLE3_DEV_BAD_PATH      0x8  /* path length 0 or > depth + 1             */
+
+enum { EAGLE3_F32 = 0, EAGLE3_BF16 = 1 };
+enum { EAGLE3_GREEDY_TREE = 0, EAGLE3_SAMPLE_CHAIN = 1 };
+enum { EAGLE3_LM_ALL = 0, EAGLE3_LM_LAST = 1, EAGLE3_LM_NONE = 2 };
+
+/* LLaMA-shaped target (also the draft layer's head layout: Hq, Hkv, hd, ffn). */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rope_theta;   /* rotate-half RoPE, inverse frequencies theta^(-2i/hd)      */
+  float rms_eps;      /* RMSNorm epsilon                                          */
+  int32_t dtype;      /* EAGLE3_F32 or EAGLE3_BF16: weights, activations, KV, aux */
+  int32_t taps[3];    /* residual stream entering 0-indexed layer taps[i], i.e.
+                         HF hidden_states[taps[i]] ("EAGLE-3: Engineering ...",
+                         IX.1-IX.3); concatenated as [l ; m ; h]                 */
+} eagle3_shape;
+
+/* Draft policy.  GREEDY_TREE: dynamic tree of `depth` levels, top-`topk` per
+ * expansion, `n_nodes` kept (root excluded), ranked by cumulative draft
+ * log-probability.  SAMPLE_CHAIN: chain of `depth` drafts each drawn from
+ * q = softmax(draft logits / temperature) (or its argmax when draft_greedy);
+ * requires topk == 1 and n_nodes == depth. */
+typedef struct {
+  int32_t mode, depth, topk, n_nodes;
+  float temperature;
+  int32_t draft_greedy;
+} eagle3_spec_cfg;
+
+typedef struct {
+  const void *attn_norm;           /* [d]                 */
+  const void *wq, *wk, *wv;        /* [Hq*hd, d], [Hkv*hd, d], [Hkv*hd, d] */
+  const void *wo;                  /* [d, Hq*hd]          */
+  const void *ffn_norm;            /* [d]                 */
+  const void *w_gate, *w_up;       /* [ffn, d]            */
+  const void *w_down;              /* [d, ffn]            */
+} eagle3_layer_weights;
+
+typedef struct {
+  const void *embed;                    /* [V, d], shared with the draft head       */
+  const eagle3_layer_weights *layers;   /* (host) array [n_layers], copied at create */
+  const void *final_norm;               /* [d]                                      */
+  const void *lm_head;                  /* [V, d], shared with the draft head       */
+} eagle3_target_weights;
+
+/* EAGLE-3 head ("EAGLE-3: Engineering ...", VIII.1-VIII.5, IX.5). */
+typedef struct {
+  const void *fc;                  /* [d, 3d]  fusion FC, bias-free         */
+  const void *input_norm;          /* [d]      RMSNorm of the embedding e   */
+  const void *hidden_norm;         /* [d]      RMSNorm of the feature x     */
+  const void *wq, *wk, *wv;        /* [Hq*hd, 2d], [Hkv*hd, 2d], [Hkv*hd, 2d] */
+  const void *wo;                  /* [d, Hq*hd]                            */
+  const void *post_norm;           /* [d]                                   */
+  const void *w_gate, *w_up;       /* [ffn, d]                              */
+  const void *w_down;              /* [d, ffn]                              */
+  const void *final_norm;          /* [d]      norm before the shared head  */
+} eagle3_head_weights;
+
+typedef struct eagle3_ctx eagle3_ctx;
+
+/* Bytes of the two KV caches for max_batch sequences of max_seq slots.
+ *   target: [n_layers][2 (K,V)][max_batch][Hkv][max_seq][hd] of T
+ *   draft : [2 (K,V)][max_batch][Hkv][max_seq][hd] of T
+ * A sequence needs max_seq >= committed length + n_nodes + 1 (target) and
+ * >= committed length + (depth - 1) * topk (draft). */
+eagle3_status eagle3_kv_bytes(const eagle3_shape *shape, int32_t max_batch, int32_t max_seq,
+                              size_t *target_bytes /* host */, size_t *draft_bytes /* host */);
+
+/* Workspace bytes for calls of at most max_batch sequences and max_rows rows
+ * (B * rows of one verify, B * (depth+1) catch-up rows, or one prefill chunk). */
+eagle3_status eagle3_workspace_bytes(const eagle3_shape *shape, const eagle3_spec_cfg *cfg,
+                                     int32_t max_batch, int32_t max_rows, int32_t max_seq,
+                                     size_t *bytes /* host */);
+
+/* Create a context.  All pointers are borrowed.  `stream` is a hipStream_t
+ * (NULL = the null stream).  Returns EINVAL for an inconsistent shape or cfg
+ * and EUNSUPPORTED for n_nodes + 1 > 64 or (depth - 1) * topk > 64. */
+eagle3_status eagle3_create(const eagle3_shape *shape /* host */, const eagle3_spec_cfg *cfg /* host */,
+                            const eagle3_target_weights *target /* host struct */,
+                            const eagle3_head_weights *head /* host struct */,
+                            int32_t max_batch, int32_t max_rows, int32_t max_seq,
+                            void *workspace, size_t workspace_bytes,
+                            void *kv_target, void *kv_draft, void *stream,
+                            eagle3_ctx **out /* host */);
+eagle3_status eagle3_destroy(eagle3_ctx *ctx);
+
+/* Target pass over n_rows new rows of each of `batch` sequences (cache slots
+ * [seq_begin, seq_begin + batch)).  Row i of sequence b has token
+ * tokens[b*n_rows+i] at RoPE position pos[b*n_rows+i] (pos NULL: seq_lens[b]+i)
+ * and writes its K/V to slot seq_lens[b] + i.  It sees every committed slot
+ * [0, seq_lens[b]) and, when mask is given, the rows whose bit is set in
+ * mask[b*n_rows+i] (bit j = row j; tree mode, n_rows <= 64); mask NULL is the
+ * causal chain (prefill): row i sees rows 0..i.  seq_lens is not changed.
+ * Outputs (each may be NULL):
+ *   logits [B*n_rows, V] float (lm_mode ALL) or [B, V] (LM_LAST: last row of
+ *          each sequence); argmax / margin [B*n_rows] or [B] likewise: the
+ *          largest logit's index (lowest index on ties) and top1 - top2;
+ *   aux    [B*n_rows, 3d] of T: the storage-rounded residual entering each tap. */
+eagle3_status eagle3_verify_tree(eagle3_ctx *ctx, int32_t seq_begin, int32_t batch,
+                                 const int32_t *seq_lens, int32_t n_rows,
+                                 const int32_t *tokens, const int32_t *pos, const uint64_t *mask,
+                                 int32_t lm_mode, float *logits, int32_t *argmax, float *margin,
+                                 void *aux);
+
+/* Draft catch-up over committed positions without drafting (the draft's
+ * prefill phase, "Speculative Decoding (EAGLE3) in the vLLM Neuron Framework",
+ * The propose() Method).  For sequence b (slot seq_begin + b) the n_rows rows
+ * are positions start[b] .. start[b]+n_rows-1; row j pairs aux[b*n_rows+j]
+ * (target taps at that position, [3d] of T) with the embedding of
+ * next_tok[b*n_rows+j] (the token at the following position).  Writes the
+ * draft K/V of those positions. */
+eagle3_status eagle3_draft_prefill(eagle3_ctx *ctx, int32_t seq_begin, int32_t batch,
+                                   const int32_t *start, int32_t n_rows,
+                                   const void *aux, const int32_t *next_tok);
+
+/* Draft stage of one step for sequences [0, batch).
+ *   seq_lens [B]   committed target length P_b; the root sits at position P_b.
+ *   new_len  [B]   catch-up rows c_b in [1, depth+1]: positions P_b - c_b .. P_b - 1.
+ *   aux_new  [B, depth+1, 3d] of T and next_tok [B, depth+1]: catch-up inputs
+ *                  (row j of b valid for j < c_b); next_tok[b][c_b - 1] is the root.
+ *   uniforms [B, depth] float in [0,1) (SAMPLE_CHAIN only, else NULL).
+ * Outputs, [B, n_nodes+1] each, root first, nodes ordered by (depth, creation):
+ *   tokens, parents (root -1), depth, pos (= P_b + depth), mask (bit j of row i
+ *   set iff j is i or an ancestor of i), score (cumulative draft log-prob,
+ *   root 0).  q [B, depth, V] float (SAMPLE_CHAIN: the draft distributions the
+ *   drafts were drawn from; else NULL). */
+eagle3_status eagle3_draft_tree(eagle3_ctx *ctx, int32_t batch, const int32_t *seq_lens,
+                                const int32_t *new_len, const void *aux_new, const int32_t *next_tok,
+                                const float *uniforms,
+                                int32_t *tokens, int32_t *parents, int32_t *depth, int32_t *pos,
+                                uint64_t *mask, float *score, float *q);
+
+/* Tree construction alone, from given draft logits (no draft model): the same
+ * kernels as eagle3_draft_tree with logits_table [B, 1 + (depth-1)*topk, V]
+ * float, where row 0 is the root's draft row and row 1 + r is expansion row r
+ * (expansion rows are numbered in creation order across depths).  roots [B].
+ * Outputs as eagle3_draft_tree. */
+eagle3_status eagle3_tree_from_logits(eagle3_ctx *ctx, int32_t batch, const int32_t *roots,
+                                      const int32_t *seq_lens, const float *logits_table,
+                                      const float *uniforms,
+                                      int32_t *tokens, int32_t *parents, int32_t *depth, int32_t *pos,
+                                      uint64_t *mask, float *score, float *q);
+
+/* Acceptance over trees of n_rows = n_nodes + 1 rows per sequence.
+ *   GREEDY_TREE: argmax [B, n_rows] (target argmax per tree row); logits, q,
+ *                uniforms unused (NULL).
+ *   SAMPLE_CHAIN: logits [B, n_rows, V] target logits; q [B, depth, V];
+ *                uniforms [B, depth+1]: uniforms[b][i] decides draft i+1,
+ *                uniforms[b][depth] drives the one residual or bonus draw.
+ * Outputs: path [B, depth+1] (tree row indices, root first, -1 padded),
+ * path_len [B], next_root [B], emitted [B, depth+1] (committed tokens, -1
+ * padded; may be NULL). */
+eagle3_status eagle3_accept(eagle3_ctx *ctx, int32_t batch, int32_t n_rows,
+                            const int32_t *tokens, const int32_t *parents, const int32_t *argmax,
+                            const float *logits, const float *q, const float *uniforms,
+                            int32_t *path, int32_t *path_len, int32_t *next_root, int32_t *emitted);
+
+/* Compaction after acceptance.  For sequence b and j < path_len[b]: target
+ * K/V of slot seq_lens[b] + path[b][j] moves to slot seq_lens[b] + j in every
+ * layer and KV head (all sources are read before any destination is written).
+ * Then aux_new[b][j] = aux_tree[b][path[b][j]], next_tok[b][j] =
+ * tokens[b][path[b][j+1]] (next_root[b] for the last), new_len[b] =
+ * path_len[b] and seq_lens[b] += path_len[b].  The draft cache needs no move:
+ * its speculative entries are simply overwritten by the next step.
+ *   aux_tree [B, n_rows, 3d] of T (from eagle3_verify_tree); aux_new
+ *   [B, depth+1, 3d] of T; next_tok [B, depth+1]; new_len [B]. */
+eagle3_status eagle3_compact_kv(eagle3_ctx *ctx, int32_t batch, int32_t *seq_lens, int32_t n_rows,
+                                const int32_t *path, const int32_t *path_len, const int32_t *tokens,
+                                const int32_t *next_root, const void *aux_tree,
+                                void *aux_new, int32_t *next_tok, int32_t *new_len);
+
+/* One token per row from softmax(logits / temperature), drawn by the same
+ * integer inverse CDF as the acceptance sampler (temperature > 0), or the
+ * argmax (lowest index on ties) when temperature == 0.  logits [n, V] float,
+ * uniforms [n] in [0, 1) (unused at temperature 0), tokens [n] out; n <= the
+ * context's max_rows.  This is vanilla decoding's sampling step and the root
+ * draw after a prefill. */
+eagle3_status eagle3_sample(eagle3_ctx *ctx, int32_t n, const float *logits, float temperature,
+                            const float *uniforms, int32_t *tokens);
+
+/* Human-readable name of a status code (static string). */
+const char *eagle3_status_string(eagle3_status s);
+
+/* Reads and clears the device status word; synchronises the context's stream. */
+eagle3_status eagle3_device_status(eagle3_ctx *ctx, int32_t *flags /* host */);
+
+/* Per-kernel timing.  eagle3_profile(ctx, 1) clears the counters and makes
+ * every later launch of the weight-streaming GEMM and attention kernels record
+ * a HIP event pair on the context's stream; eagle3_profile(ctx, 0) stops.
+ * eagle3_profile_read synchronises the stream and returns, for kernel id
+ * `kernel` (EAGLE3_PROF_*), the number of launches, their summed duration in
+ * ms, and the summed algorithmic bytes (weights + activations + outputs each
+ * read or written once) and flops of those launches. */
+enum {
+  EAGLE3_PROF_GEMM_M64 = 0,  /* MFMA GEMM, 64-row tiles (verify, prefill)     */
+  EAGLE3_PROF_GEMM_M16 = 1,  /* MFMA GEMM, 16-row tiles (draft, last-row LM)  */
+  EAGLE3_PROF_ATTN = 2,      /* tree-masked attention (all modes)             */
+  EAGLE3_PROF_COUNT = 3
+};
+eagle3_status eagle3_profile(eagle3_ctx *ctx, int32_t enable);
+eagle3_status eagle3_profile_read(eagle3_ctx *ctx, int32_t kernel, int64_t *launches /* host */,
+                                  double *total_ms /* host */, double *bytes /* host */,
+                                  double *flops /* host */);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE3_H */

@@ -1,0 +1,74 @@
+// Device helpers shared by the EAGLE-3 step kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define E3_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;  // bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 <-> f32
+E3_DEV float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round to nearest, ties to even (NaN kept quiet).
+E3_DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Storage element access for T = float or bf16_t.
+template <typename T> E3_DEV float ld(const T* p, size_t i);
+template <> E3_DEV float ld<float>(const float* p, size_t i) { return p[i]; }
+template <> E3_DEV float ld<bf16_t>(const bf16_t* p, size_t i) { return bf2f(p[i]); }
+template <typename T> E3_DEV void st(T* p, size_t i, float v);
+template <> E3_DEV void st<float>(float* p, size_t i, float v) { p[i] = v; }
+template <> E3_DEV void st<bf16_t>(bf16_t* p, size_t i, float v) { p[i] = f2bf(v); }
+
+// ---------------------------------------------------------------- reductions
+E3_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+E3_DEV double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+E3_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum for blockDim.x a multiple of 64 (<= 1024); `red` holds >= 16 floats.
+E3_DEV float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// (value, index) order used by every top-k and argmax: larger value first,
+// lower index on ties.
+E3_DEV bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && (unsigned)ia < (unsigned)ib);
+}
+
+// Status bits (mirrors eagle3.h).
+#define E3_DEV_KV_OVERFLOW 0x1
+#define E3_DEV_BAD_TREE 0x2
+#define E3_DEV_BAD_TOKEN 0x4
+#define E3_DEV_BAD_PATH 0x8
+
+E3_DEV void raise_flag(int* status, int bit) { atomicOr(status, bit); }

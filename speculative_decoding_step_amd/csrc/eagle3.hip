@@ -1,0 +1,759 @@
+// C ABI of the EAGLE-3 step: context, workspace layout and the launch
+// sequences of draft_tree / verify_tree / accept / compact_kv (see eagle3.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/eagle3.h"
+#include "common.hpp"
+#include "kernels.hpp"
+#include "tree.hpp"
+
+using namespace e3;
+
+namespace {
+
+constexpr int KMAX = 16;  // largest top-k the vocabulary kernels keep
+constexpr int ATT_CHUNK = 256;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename P>
+  P* take(size_t count) {
+    off = align_up(off, 256);
+    P* p = base ? (P*)(base + off) : nullptr;
+    off += count * sizeof(P);
+    return p;
+  }
+};
+
+struct ProfRec {
+  int kernel;
+  hipEvent_t a, b;
+  double bytes, flops;
+};
+
+}  // namespace
+
+struct eagle3_ctx {
+  eagle3_shape sh;
+  eagle3_spec_cfg cfg;
+  eagle3_target_weights tw;
+  std::vector<eagle3_layer_weights> layers;
+  eagle3_head_weights hw;
+  int B, R, S_cap;
+  bool bf16;
+  size_t esz;
+  hipStream_t st;
+  char* kv_t;
+  char* kv_d;
+  // workspace
+  int* status;
+  float *xres, *dx, *part;
+  size_t part_elems;
+  void *hbuf, *abuf, *qbuf, *gbuf;
+  float *o_part, *ml_part;
+  int att_splits;
+  float* logits;
+  float *tk_pv, *tk_pmax, *tk_vals, *tk_lse;
+  int *tk_pi, *tk_ids;
+  double *tk_psum, *tk_lse64;
+  RowMeta rm;
+  int *rtok, *gidx, *roots;
+  float *a_last, *a_rows;
+  DraftRows dr;
+  TreeState ts;
+  int* chain_tok;
+  int emax, n_cand;
+  // profiling
+  bool prof = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t pool_used = 0;
+};
+
+namespace {
+
+size_t carve(eagle3_ctx* c, char* base) {
+  const eagle3_shape& s = c->sh;
+  const int R = c->R, B = c->B, d = s.d_model, V = s.vocab;
+  const int qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
+  const size_t es = c->esz;
+  Carver cv{base};
+  c->status = cv.take<int>(64);
+  c->xres = cv.take<float>((size_t)R * d);
+  c->dx = cv.take<float>((size_t)R * d);
+  const int nmax = std::max({qdim + 2 * kvdim, 2 * s.ffn, d});
+  const size_t prow = std::max(R, 512);
+  c->part_elems = prow * nmax;
+  c->part = cv.take<float>(c->part_elems);
+  c->hbuf = cv.take<char>((size_t)R * 2 * d * es);
+  c->abuf = cv.take<char>((size_t)R * std::max(qdim, s.ffn) * es);
+  c->qbuf = cv.take<char>((size_t)R * qdim * es);
+  c->gbuf = cv.take<char>((size_t)R * d * es);
+  c->att_splits = std::max(1, (c->S_cap + ATT_CHUNK - 1) / ATT_CHUNK);
+  c->o_part = cv.take<float>((size_t)c->att_splits * R * qdim);
+  c->ml_part = cv.take<float>((size_t)c->att_splits * R * s.n_heads * 2);
+  c->logits = cv.take<float>((size_t)R * V);
+  const int ns = topk_slices(V);
+  c->tk_pv = cv.take<float>((size_t)R * ns * KMAX);
+  c->tk_pi = cv.take<int>((size_t)R * ns * KMAX);
+  c->tk_pmax = cv.take<float>((size_t)R * ns);
+  c->tk_psum = cv.take<double>((size_t)R * ns);
+  c->tk_ids = cv.take<int>((size_t)R * KMAX);
+  c->tk_vals = cv.take<float>((size_t)R * KMAX);
+  c->tk_lse = cv.take<float>(R);
+  c->tk_lse64 = cv.take<double>(R);
+  c->rm.seq = cv.take<int>(R);
+  c->rm.pos = cv.take<int>(R);
+  c->rm.slot = cv.take<int>(R);
+  c->rm.lim = cv.take<int>(R);
+  c->rm.tail0 = cv.take<int>(R);
+  c->rm.mask = cv.take<uint64_t>(R);
+  c->rtok = cv.take<int>(R);
+  c->gidx = cv.take<int>(R);
+  c->roots = cv.take<int>(B);
+  const int D = c->cfg.depth, k = c->cfg.topk;
+  c->emax = std::max(1, (D - 1) * k);
+  c->n_cand = c->cfg.mode == EAGLE3_GREEDY_TREE ? k + (D - 1) * k * k : D;
+  c->a_last = cv.take<float>((size_t)B * d);
+  c->a_rows = cv.take<float>((size_t)B * c->emax * d);
+  c->dr.batch = B;
+  c->dr.tok = cv.take<int>(R);
+  c->dr.src = cv.take<int>(R);
+  c->dr.seq = cv.take<int>(R);
+  c->dr.pos = cv.take<int>(R);
+  c->dr.slot = cv.take<int>(R);
+  c->dr.lim = cv.take<int>(R);
+  c->dr.tail0 = cv.take<int>(R);
+  c->dr.mask = cv.take<uint64_t>(R);
+  const int cmax = std::max(c->n_cand, 1);
+  c->ts.batch = B;
+  c->ts.topk = k;
+  c->ts.cmax = cmax;
+  c->ts.emax = c->emax;
+  c->ts.tok = cv.take<int>((size_t)B * cmax);
+  c->ts.par = cv.take<int>((size_t)B * cmax);
+  c->ts.dep = cv.take<int>((size_t)B * cmax);
+  c->ts.score = cv.take<float>((size_t)B * cmax);
+  c->ts.erow = cv.take<int>((size_t)B * cmax);
+  c->ts.front = cv.take<int>((size_t)B * k);
+  c->ts.emask = cv.take<uint64_t>((size_t)B * c->emax);
+  c->chain_tok = cv.take<int>((size_t)B * (D + 1));
+  return align_up(cv.off, 256);
+}
+
+eagle3_status check_shape(const eagle3_shape* s, const eagle3_spec_cfg* c) {
+  if (!s || !c) return EAGLE3_EINVAL;
+  if (s->n_layers < 1 || s->d_model < 1 || s->n_heads < 1 || s->n_kv_heads < 1 || s->head_dim < 2 ||
+      s->ffn < 1 || s->vocab < 2)
+    return EAGLE3_EINVAL;
+  if (s->n_heads % s->n_kv_heads || s->head_dim % 2 || s->head_dim > 256) return EAGLE3_EINVAL;
+  if (s->dtype != EAGLE3_F32 && s->dtype != EAGLE3_BF16) return EAGLE3_EINVAL;
+  for (int i = 0; i < 3; ++i)
+    if (s->taps[i] < 0 || s->taps[i] >= s->n_layers) return EAGLE3_EINVAL;
+  if (s->dtype == EAGLE3_BF16) {
+    const int qdim = s->n_heads * s->head_dim;
+    if (s->d_model % 256 || qdim % 256 || s->ffn % 256) return EAGLE3_EUNSUPPORTED;
+  }
+  if (s->vocab > 64 * 4096) return EAGLE3_EUNSUPPORTED;
+  if (c->depth < 1 || c->topk < 1 || c->topk > KMAX || c->n_nodes < 1 || c->topk > s->vocab) return EAGLE3_EINVAL;
+  if (c->n_nodes + 1 > 64 || (c->depth - 1) * c->topk > 64) return EAGLE3_EUNSUPPORTED;
+  if (c->mode == EAGLE3_GREEDY_TREE) {
+    const int nc = c->topk + (c->depth - 1) * c->topk * c->topk;
+    if (nc < c->n_nodes || nc > TREE_CMAX) return EAGLE3_EUNSUPPORTED;
+  } else if (c->mode == EAGLE3_SAMPLE_CHAIN) {
+    if (c->topk != 1 || c->n_nodes != c->depth || !(c->temperature > 0.f)) return EAGLE3_EINVAL;
+  } else {
+    return EAGLE3_EINVAL;
+  }
+  return EAGLE3_OK;
+}
+
+// ------------------------------------------------------------- small kernels
+
+__global__ void k_verify_meta(int batch, int seq_begin, int n_rows, const int* __restrict__ seq_lens,
+                              const int* __restrict__ tokens, const int* __restrict__ pos_in,
+                              const uint64_t* __restrict__ mask_in, int S_cap, RowMeta rm, int* __restrict__ rtok,
+                              int* __restrict__ gidx, int* status) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= batch * n_rows) return;
+  const int b = r / n_rows, i = r % n_rows;
+  const int P = seq_lens[b];
+  const int slot = P + i;
+  const bool ok = P >= 0 && P + n_rows <= S_cap;
+  if (!ok && i == 0) raise_flag(status, E3_DEV_KV_OVERFLOW);
+  rm.seq[r] = ok ? seq_begin + b : -1;
+  rm.pos[r] = pos_in ? pos_in[r] : slot;
+  rm.slot[r] = slot;
+  rm.lim[r] = mask_in ? P : slot + 1;
+  rm.tail0[r] = P;
+  rm.mask[r] = mask_in ? mask_in[r] : 0ull;
+  rtok[r] = tokens[r];
+  if (i == n_rows - 1) gidx[b] = r;
+}
+
+// Catch-up rows of the draft: row b*(D+1)+j is position P_b - c_b + j.
+__global__ void k_catchup_meta(int batch, int W, const int* __restrict__ seq_lens, const int* __restrict__ new_len,
+                               const int* __restrict__ next_tok, int S_cap, RowMeta rm, int* __restrict__ rtok,
+                               int* __restrict__ gidx, int* __restrict__ roots, int* status) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= batch * W) return;
+  const int b = r / W, j = r % W;
+  const int P = seq_lens[b], c = new_len[b];
+  const bool cok = c >= 1 && c <= W && P - c >= 0 && P <= S_cap;
+  const bool valid = cok && j < c;
+  const int pos = P - c + j;
+  if (!cok && j == 0) raise_flag(status, E3_DEV_BAD_PATH);
+  rm.seq[r] = valid && pos < S_cap ? b : -1;
+  rm.pos[r] = valid ? pos : 0;
+  rm.slot[r] = valid ? pos : 0;
+  rm.lim[r] = valid ? pos + 1 : 0;
+  rm.tail0[r] = 0;
+  rm.mask[r] = 0ull;
+  rtok[r] = valid ? next_tok[r] : -1;
+  if (j == 0) {
+    const int last = cok ? c - 1 : 0;
+    gidx[b] = b * W + last;
+    roots[b] = next_tok[b * W + last];
+  }
+}
+
+__global__ void k_prefill_meta(int batch, int seq_begin, int n_rows, const int* __restrict__ start,
+                               const int* __restrict__ next_tok, int S_cap, RowMeta rm, int* __restrict__ rtok,
+                               int* status) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= batch * n_rows) return;
+  const int b = r / n_rows, j = r % n_rows;
+  const int pos = start[b] + j;
+  const bool ok = pos >= 0 && pos < S_cap;
+  if (!ok) raise_flag(status, E3_DEV_KV_OVERFLOW);
+  rm.seq[r] = ok ? seq_begin + b : -1;
+  rm.pos[r] = pos;
+  rm.slot[r] = ok ? pos : 0;
+  rm.lim[r] = pos + 1;
+  rm.tail0[r] = 0;
+  rm.mask[r] = 0ull;
+  rtok[r] = next_tok[r];
+}
+
+template <typename T>
+__global__ void k_store_tap(const float* __restrict__ x, int d, T* __restrict__ aux, int aux_ld, int col0) {
+  const int r = blockIdx.x;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) st<T>(aux, (size_t)r * aux_ld + col0 + i, x[(size_t)r * d + i]);
+}
+
+__global__ void k_argmax_margin(int n, const int* __restrict__ ids, const float* __restrict__ vals, int kk,
+                                int* __restrict__ am, float* __restrict__ mg) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n) return;
+  if (am) am[r] = ids[(size_t)r * kk];
+  if (mg) mg[r] = kk > 1 ? vals[(size_t)r * kk] - vals[(size_t)r * kk + 1] : 0.f;
+}
+
+__global__ void k_seq_roots(int batch, int K1, const int* __restrict__ roots_in, int* __restrict__ roots) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) roots[b] = roots_in[b];
+  (void)K1;
+}
+
+inline unsigned nb(size_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+// ------------------------------------------------------------ profiling
+void prof_begin(eagle3_ctx* c, int kernel, double bytes, double flops, ProfRec* rec) {
+  if (!c->prof) return;
+  if (c->pool_used + 2 > c->pool.size()) {
+    for (int i = 0; i < 256; ++i) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) break;
+      c->pool.push_back(e);
+    }
+  }
+  if (c->pool_used + 2 > c->pool.size()) return;
+  rec->kernel = kernel;
+  rec->a = c->pool[c->pool_used++];
+  rec->b = c->pool[c->pool_used++];
+  rec->bytes = bytes;
+  rec->flops = flops;
+  (void)hipEventRecord(rec->a, c->st);
+}
+void prof_end(eagle3_ctx* c, ProfRec* rec) {
+  if (!c->prof || !rec->a) return;
+  (void)hipEventRecord(rec->b, c->st);
+  c->recs.push_back(*rec);
+}
+
+// ----------------------------------------------------------------- GEMM plan
+int plan_splits(eagle3_ctx* c, int M, int N, int K, int m_tile) {
+  if (!c->bf16) return 1;
+  const int tiles = ((N + 63) / 64) * ((M + m_tile - 1) / m_tile);
+  int S = (512 + tiles - 1) / tiles;
+  S = std::max(1, std::min(S, K / 256));
+  const int mpad = (M + m_tile - 1) / m_tile * m_tile;
+  while (S > 1 && (size_t)S * mpad * N > c->part_elems) --S;
+  return gemm_splits(true, K, S);
+}
+
+// X [M, K] of T times the stacked weights; returns the number of splits in c->part.
+int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, float* out_direct = nullptr) {
+  const int N = gemm_ntot(sg);
+  const int m_tile = M <= 16 ? 16 : 64;
+  const int S = out_direct ? 1 : plan_splits(c, M, N, K, m_tile);
+  ProfRec rec{};
+  const double bytes = (double)N * K * c->esz + (double)M * K * c->esz + (double)M * N * 4.0;
+  prof_begin(c, m_tile == 16 ? EAGLE3_PROF_GEMM_M16 : EAGLE3_PROF_GEMM_M64, bytes, 2.0 * M * N * K, &rec);
+  const int used = gemm(c->bf16, X, M, K, sg, out_direct ? out_direct : c->part, (size_t)M * N, S, m_tile, c->st);
+  prof_end(c, &rec);
+  return used;
+}
+
+void run_attention(eagle3_ctx* c, const void* kc, const void* vc, const RowMeta& rm, int R) {
+  const eagle3_shape& s = c->sh;
+  ProfRec rec{};
+  prof_begin(c, EAGLE3_PROF_ATTN, 0.0, 0.0, &rec);
+  attention(c->bf16, c->qbuf, kc, vc, (size_t)s.n_kv_heads * c->S_cap * s.head_dim, (size_t)c->S_cap * s.head_dim, rm,
+            R, s.n_heads, s.n_kv_heads, s.head_dim, c->S_cap, c->o_part, c->ml_part, c->att_splits, c->abuf, c->st);
+  prof_end(c, &rec);
+}
+
+char* kv_layer(eagle3_ctx* c, char* base, int l, int which) {
+  const eagle3_shape& s = c->sh;
+  const size_t blk = (size_t)c->B * s.n_kv_heads * c->S_cap * s.head_dim * c->esz;
+  return base + ((size_t)l * 2 + which) * blk;
+}
+
+// Target pass over R rows whose metadata is in c->rm and tokens in c->rtok.
+// lm: EAGLE3_LM_ALL (rows 0..R-1), LM_LAST (rows c->gidx[0..nlast)), LM_NONE.
+void target_forward(eagle3_ctx* c, int R, void* aux, int lm, int nlast, float* logits, int* argmax, float* margin) {
+  const eagle3_shape& s = c->sh;
+  const int d = s.d_model, qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
+  const bool bf = c->bf16;
+  hipStream_t st = c->st;
+  embed_rows(bf, c->tw.embed, c->rtok, c->xres, R, d, s.vocab, c->status, st);
+  for (int l = 0; l < s.n_layers; ++l) {
+    const eagle3_layer_weights& L = c->layers[l];
+    for (int t = 0; t < 3; ++t)
+      if (aux && s.taps[t] == l) {
+        if (bf)
+          k_store_tap<bf16_t><<<R, 256, 0, st>>>(c->xres, d, (bf16_t*)aux, 3 * d, t * d);
+        else
+          k_store_tap<float><<<R, 256, 0, st>>>(c->xres, d, (float*)aux, 3 * d, t * d);
+      }
+    rmsnorm(bf, c->xres, L.attn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
+    const GemmSegs qkv = make_segs(L.wq, qdim, L.wk, kvdim, L.wv, kvdim);
+    int S = run_gemm(c, c->hbuf, R, d, qkv);
+    char* kc = kv_layer(c, c->kv_t, l, 0);
+    char* vc = kv_layer(c, c->kv_t, l, 1);
+    rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, c->rm, c->qbuf, kc, vc,
+            (size_t)s.n_kv_heads * c->S_cap * s.head_dim, (size_t)c->S_cap * s.head_dim, s.n_heads, s.n_kv_heads,
+            s.head_dim, s.rope_theta, st);
+    run_attention(c, kc, vc, c->rm, R);
+    S = run_gemm(c, c->abuf, R, qdim, make_segs(L.wo, d));
+    resid_add(c->xres, c->part, S, (size_t)R * d, R, d, d, st);
+    rmsnorm(bf, c->xres, L.ffn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
+    const GemmSegs gu = make_segs(L.w_gate, s.ffn, L.w_up, s.ffn);
+    S = run_gemm(c, c->hbuf, R, d, gu);
+    silu_mul(bf, c->abuf, c->part, S, (size_t)R * 2 * s.ffn, R, s.ffn, 2 * s.ffn, st);
+    S = run_gemm(c, c->abuf, R, s.ffn, make_segs(L.w_down, d));
+    resid_add(c->xres, c->part, S, (size_t)R * d, R, d, d, st);
+  }
+  if (lm == EAGLE3_LM_NONE) return;
+  int n = R;
+  const float* fin = c->xres;
+  if (lm == EAGLE3_LM_LAST) {
+    gather_rows_f32(c->dx, c->xres, c->gidx, nlast, d, st);
+    fin = c->dx;
+    n = nlast;
+  }
+  rmsnorm(bf, fin, c->tw.final_norm, c->gbuf, d, n, d, s.rms_eps, nullptr, 0, st);
+  float* lg = logits ? logits : c->logits;
+  run_gemm(c, c->gbuf, n, d, make_segs(c->tw.lm_head, s.vocab), lg);
+  if (argmax || margin) {
+    topk_lse(lg, n, s.vocab, s.vocab, 2, 1.f, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids, c->tk_vals,
+             nullptr, nullptr, st);
+    k_argmax_margin<<<nb(n, 128), 128, 0, st>>>(n, c->tk_ids, c->tk_vals, 2, argmax, margin);
+  }
+}
+
+// The draft decoder layer over R rows: x (fp32 [R, d]) is g or a on entry and
+// a on exit; tokens in tok; row metadata rm (draft KV cache).
+void draft_layer(eagle3_ctx* c, int R, const int* tok, float* x, const RowMeta& rm) {
+  const eagle3_shape& s = c->sh;
+  const eagle3_head_weights& H = c->hw;
+  const int d = s.d_model, qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
+  const bool bf = c->bf16;
+  hipStream_t st = c->st;
+  draft_input(bf, c->tw.embed, tok, x, H.input_norm, H.hidden_norm, c->hbuf, R, d, s.vocab, s.rms_eps, c->status, st);
+  const GemmSegs qkv = make_segs(H.wq, qdim, H.wk, kvdim, H.wv, kvdim);
+  int S = run_gemm(c, c->hbuf, R, 2 * d, qkv);
+  char* kc = kv_layer(c, c->kv_d, 0, 0);
+  char* vc = kv_layer(c, c->kv_d, 0, 1);
+  rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, rm, c->qbuf, kc, vc,
+          (size_t)s.n_kv_heads * c->S_cap * s.head_dim, (size_t)c->S_cap * s.head_dim, s.n_heads, s.n_kv_heads,
+          s.head_dim, s.rope_theta, st);
+  run_attention(c, kc, vc, rm, R);
+  S = run_gemm(c, c->abuf, R, qdim, make_segs(H.wo, d));
+  resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
+  rmsnorm(bf, x, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
+  const GemmSegs gu = make_segs(H.w_gate, s.ffn, H.w_up, s.ffn);
+  S = run_gemm(c, c->hbuf, R, d, gu);
+  silu_mul(bf, c->abuf, c->part, S, (size_t)R * 2 * s.ffn, R, s.ffn, 2 * s.ffn, st);
+  S = run_gemm(c, c->abuf, R, s.ffn, make_segs(H.w_down, d));
+  resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
+}
+
+// Draft logits of n rows of a (fp32 [n, d]) -> c->logits; top-K + lse.
+void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature) {
+  const eagle3_shape& s = c->sh;
+  rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st);
+  run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->tw.lm_head, s.vocab), c->logits);
+  topk_lse(c->logits, n, s.vocab, s.vocab, K, temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids,
+           c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
+}
+
+RowMeta dr_meta(eagle3_ctx* c) {
+  RowMeta m;
+  m.seq = c->dr.seq;
+  m.pos = c->dr.pos;
+  m.slot = c->dr.slot;
+  m.lim = c->dr.lim;
+  m.tail0 = c->dr.tail0;
+  m.mask = c->dr.mask;
+  return m;
+}
+
+// Tree / chain construction after the root's draft row is in c->logits
+// (top-k in c->tk_*).  table != null: rows come from the table instead of
+// the draft model.
+eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const float* table, const float* uniforms,
+                         const TreeOut& out, float* q) {
+  const eagle3_shape& s = c->sh;
+  const int D = c->cfg.depth, k = c->cfg.topk, V = s.vocab, d = s.d_model;
+  hipStream_t st = c->st;
+  TreeState ts = c->ts;
+  ts.batch = batch;
+  DraftRows dr = c->dr;
+  dr.batch = batch;
+  const size_t tstride = (size_t)(1 + c->emax) * V;  // table row stride between sequences
+  if (c->cfg.mode == EAGLE3_GREEDY_TREE) {
+    tree_children(ts, 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
+    for (int dd = 1; dd < D; ++dd) {
+      const int n = batch * k;
+      tree_frontier(ts, dd, seq_lens, dr, c->S_cap, c->status, st);
+      if (table) {
+        // expansion rows (dd-1)k .. dd k - 1 of each sequence
+        for (int b = 0; b < batch; ++b)
+          topk_lse(table + b * tstride + (size_t)(1 + (dd - 1) * k) * V, k, V, V, k, 1.f, c->tk_pv + (size_t)b * k * topk_slices(V) * KMAX,
+                   c->tk_pi + (size_t)b * k * topk_slices(V) * KMAX, c->tk_pmax + (size_t)b * k * topk_slices(V),
+                   c->tk_psum + (size_t)b * k * topk_slices(V), c->tk_ids + (size_t)b * k * k, c->tk_vals + (size_t)b * k * k,
+                   c->tk_lse + b * k, c->tk_lse64 + b * k, st);
+      } else {
+        tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, n, d, st);
+        draft_layer(c, n, dr.tok, c->dx, dr_meta(c));
+        if (dd + 1 < D) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, n, k, c->emax, d, st);
+        draft_lm(c, n, c->dx, k, 1.f);
+      }
+      tree_children(ts, dd + 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
+    }
+    tree_finalize(ts, c->n_cand, c->cfg.n_nodes, c->roots, seq_lens, out, c->status, st);
+  } else {
+    const int K = D;
+    const float T = c->cfg.temperature;
+    const float* z0 = table ? table : c->logits;
+    const int ld0 = table ? (int)tstride : V;
+    chain_draw(0, K, z0, ld0, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok, batch, st);
+    for (int j = 1; j < K; ++j) {
+      if (table) {
+        const float* zj = table + (size_t)j * V;
+        for (int b = 0; b < batch; ++b)
+          topk_lse(zj + b * tstride, 1, V, V, 1, T, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids + b,
+                   c->tk_vals + b, c->tk_lse + b, c->tk_lse64 + b, st);
+        chain_draw(j, K, zj, (int)tstride, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok,
+                   batch, st);
+      } else {
+        chain_rows(j - 1, K, c->chain_tok, seq_lens, c->emax, dr, c->S_cap, st);
+        tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, batch, d, st);
+        draft_layer(c, batch, dr.tok, c->dx, dr_meta(c));
+        if (j + 1 < K) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, batch, 1, c->emax, d, st);
+        draft_lm(c, batch, c->dx, 1, T);
+        chain_draw(j, K, c->logits, V, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok,
+                   batch, st);
+      }
+    }
+    chain_finalize(K, c->roots, seq_lens, c->chain_tok, out, batch, st);
+  }
+  return EAGLE3_OK;
+}
+
+eagle3_status last_error() { return hipGetLastError() == hipSuccess ? EAGLE3_OK : EAGLE3_EHIP; }
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+const char* eagle3_status_string(eagle3_status s) {
+  switch (s) {
+    case EAGLE3_OK: return "ok";
+    case EAGLE3_EINVAL: return "invalid argument";
+    case EAGLE3_ECAPACITY: return "capacity exceeded";
+    case EAGLE3_EUNSUPPORTED: return "unsupported";
+    case EAGLE3_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+eagle3_status eagle3_kv_bytes(const eagle3_shape* s, int32_t max_batch, int32_t max_seq, size_t* tb, size_t* db) {
+  if (!s || !tb || !db || max_batch < 1 || max_seq < 1) return EAGLE3_EINVAL;
+  const size_t es = s->dtype == EAGLE3_BF16 ? 2 : 4;
+  const size_t per = (size_t)max_batch * s->n_kv_heads * max_seq * s->head_dim * es;
+  *tb = (size_t)s->n_layers * 2 * per;
+  *db = 2 * per;
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_workspace_bytes(const eagle3_shape* s, const eagle3_spec_cfg* cfg, int32_t max_batch,
+                                     int32_t max_rows, int32_t max_seq, size_t* bytes) {
+  eagle3_status e = check_shape(s, cfg);
+  if (e) return e;
+  if (!bytes || max_batch < 1 || max_rows < 1 || max_seq < 1) return EAGLE3_EINVAL;
+  eagle3_ctx tmp;
+  tmp.sh = *s;
+  tmp.cfg = *cfg;
+  tmp.B = max_batch;
+  tmp.R = max_rows;
+  tmp.S_cap = max_seq;
+  tmp.bf16 = s->dtype == EAGLE3_BF16;
+  tmp.esz = tmp.bf16 ? 2 : 4;
+  *bytes = carve(&tmp, nullptr);
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, const eagle3_target_weights* tw,
+                            const eagle3_head_weights* hw, int32_t max_batch, int32_t max_rows, int32_t max_seq,
+                            void* ws, size_t ws_bytes, void* kv_t, void* kv_d, void* stream, eagle3_ctx** out) {
+  eagle3_status e = check_shape(s, cfg);
+  if (e) return e;
+  if (!tw || !hw || !out || !ws || !kv_t || !kv_d || !tw->layers || max_batch < 1 || max_rows < 1 || max_seq < 1)
+    return EAGLE3_EINVAL;
+  const int W = cfg->depth + 1;
+  if (max_batch * W > max_rows || max_batch * cfg->topk > max_rows) return EAGLE3_ECAPACITY;
+  if (!tw->embed || !tw->final_norm || !tw->lm_head) return EAGLE3_EINVAL;
+  for (int l = 0; l < s->n_layers; ++l) {
+    const eagle3_layer_weights& L = tw->layers[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.w_gate || !L.w_up || !L.w_down)
+      return EAGLE3_EINVAL;
+  }
+  if (!hw->fc || !hw->input_norm || !hw->hidden_norm || !hw->wq || !hw->wk || !hw->wv || !hw->wo || !hw->post_norm ||
+      !hw->w_gate || !hw->w_up || !hw->w_down || !hw->final_norm)
+    return EAGLE3_EINVAL;
+  eagle3_ctx* c = new (std::nothrow) eagle3_ctx();
+  if (!c) return EAGLE3_EINVAL;
+  c->sh = *s;
+  c->cfg = *cfg;
+  c->tw = *tw;
+  c->layers.assign(tw->layers, tw->layers + s->n_layers);
+  c->tw.layers = nullptr;
+  c->hw = *hw;
+  c->B = max_batch;
+  c->R = max_rows;
+  c->S_cap = max_seq;
+  c->bf16 = s->dtype == EAGLE3_BF16;
+  c->esz = c->bf16 ? 2 : 4;
+  c->st = (hipStream_t)stream;
+  c->kv_t = (char*)kv_t;
+  c->kv_d = (char*)kv_d;
+  const size_t need = carve(c, (char*)ws);
+  if (ws_bytes < need) {
+    delete c;
+    return EAGLE3_ECAPACITY;
+  }
+  if (hipMemsetAsync(c->status, 0, 64 * sizeof(int), c->st) != hipSuccess) {
+    delete c;
+    return EAGLE3_EHIP;
+  }
+  *out = c;
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_destroy(eagle3_ctx* c) {
+  if (!c) return EAGLE3_EINVAL;
+  for (hipEvent_t ev : c->pool) (void)hipEventDestroy(ev);
+  delete c;
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_verify_tree(eagle3_ctx* c, int32_t seq_begin, int32_t batch, const int32_t* seq_lens,
+                                 int32_t n_rows, const int32_t* tokens, const int32_t* pos, const uint64_t* mask,
+                                 int32_t lm_mode, float* logits, int32_t* argmax, float* margin, void* aux) {
+  if (!c || !seq_lens || !tokens || batch < 1 || n_rows < 1) return EAGLE3_EINVAL;
+  if (seq_begin < 0 || seq_begin + batch > c->B) return EAGLE3_ECAPACITY;
+  if ((size_t)batch * n_rows > (size_t)c->R) return EAGLE3_ECAPACITY;
+  if (mask && n_rows > 64) return EAGLE3_EUNSUPPORTED;
+  if (lm_mode < EAGLE3_LM_ALL || lm_mode > EAGLE3_LM_NONE) return EAGLE3_EINVAL;
+  const int R = batch * n_rows;
+  k_verify_meta<<<nb(R, 128), 128, 0, c->st>>>(batch, seq_begin, n_rows, seq_lens, tokens, pos, mask, c->S_cap, c->rm,
+                                                c->rtok, c->gidx, c->status);
+  target_forward(c, R, aux, lm_mode, batch, logits, argmax, margin);
+  return last_error();
+}
+
+eagle3_status eagle3_draft_prefill(eagle3_ctx* c, int32_t seq_begin, int32_t batch, const int32_t* start,
+                                   int32_t n_rows, const void* aux, const int32_t* next_tok) {
+  if (!c || !start || !aux || !next_tok || batch < 1 || n_rows < 1) return EAGLE3_EINVAL;
+  if (seq_begin < 0 || seq_begin + batch > c->B) return EAGLE3_ECAPACITY;
+  if ((size_t)batch * n_rows > (size_t)c->R) return EAGLE3_ECAPACITY;
+  const int R = batch * n_rows, d = c->sh.d_model;
+  k_prefill_meta<<<nb(R, 128), 128, 0, c->st>>>(batch, seq_begin, n_rows, start, next_tok, c->S_cap, c->rm, c->rtok,
+                                                 c->status);
+  int S = run_gemm(c, aux, R, 3 * d, make_segs(c->hw.fc, d));
+  sum_store(c->dx, c->part, S, (size_t)R * d, R, d, d, c->st);
+  draft_layer(c, R, c->rtok, c->dx, c->rm);
+  return last_error();
+}
+
+eagle3_status eagle3_draft_tree(eagle3_ctx* c, int32_t batch, const int32_t* seq_lens, const int32_t* new_len,
+                                const void* aux_new, const int32_t* next_tok, const float* uniforms, int32_t* tokens,
+                                int32_t* parents, int32_t* depth, int32_t* pos, uint64_t* mask, float* score,
+                                float* q) {
+  if (!c || !seq_lens || !new_len || !aux_new || !next_tok || !tokens || !parents || !depth || !pos || !mask || !score)
+    return EAGLE3_EINVAL;
+  if (batch < 1 || batch > c->B) return EAGLE3_ECAPACITY;
+  const bool chain = c->cfg.mode == EAGLE3_SAMPLE_CHAIN;
+  if (chain && ((!uniforms && !c->cfg.draft_greedy) || !q)) return EAGLE3_EINVAL;
+  const eagle3_shape& s = c->sh;
+  const int W = c->cfg.depth + 1, d = s.d_model;
+  const int Rc = batch * W;
+  hipStream_t st = c->st;
+  k_catchup_meta<<<nb(Rc, 128), 128, 0, st>>>(batch, W, seq_lens, new_len, next_tok, c->S_cap, c->rm, c->rtok,
+                                               c->gidx, c->roots, c->status);
+  int S = run_gemm(c, aux_new, Rc, 3 * d, make_segs(c->hw.fc, d));
+  sum_store(c->dx, c->part, S, (size_t)Rc * d, Rc, d, d, st);
+  draft_layer(c, Rc, c->rtok, c->dx, c->rm);
+  gather_rows_f32(c->a_last, c->dx, c->gidx, batch, d, st);
+  draft_lm(c, batch, c->a_last, chain ? 1 : c->cfg.topk, chain ? c->cfg.temperature : 1.f);
+  TreeOut out{tokens, parents, depth, pos, mask, score};
+  build_tree(c, batch, seq_lens, nullptr, uniforms, out, q);
+  return last_error();
+}
+
+eagle3_status eagle3_tree_from_logits(eagle3_ctx* c, int32_t batch, const int32_t* roots, const int32_t* seq_lens,
+                                      const float* table, const float* uniforms, int32_t* tokens, int32_t* parents,
+                                      int32_t* depth, int32_t* pos, uint64_t* mask, float* score, float* q) {
+  if (!c || !roots || !seq_lens || !table || !tokens || !parents || !depth || !pos || !mask || !score)
+    return EAGLE3_EINVAL;
+  if (batch < 1 || batch > c->B) return EAGLE3_ECAPACITY;
+  const bool chain = c->cfg.mode == EAGLE3_SAMPLE_CHAIN;
+  if (chain && ((!uniforms && !c->cfg.draft_greedy) || !q)) return EAGLE3_EINVAL;
+  const int V = c->sh.vocab;
+  const size_t tstride = (size_t)(1 + c->emax) * V;
+  k_seq_roots<<<nb(batch, 64), 64, 0, c->st>>>(batch, 0, roots, c->roots);
+  const int K = chain ? 1 : c->cfg.topk;
+  const float T = chain ? c->cfg.temperature : 1.f;
+  topk_lse(table, batch, V, (int)tstride, K, T, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids, c->tk_vals,
+           c->tk_lse, c->tk_lse64, c->st);
+  TreeOut out{tokens, parents, depth, pos, mask, score};
+  build_tree(c, batch, seq_lens, table, uniforms, out, q);
+  return last_error();
+}
+
+eagle3_status eagle3_accept(eagle3_ctx* c, int32_t batch, int32_t n_rows, const int32_t* tokens,
+                            const int32_t* parents, const int32_t* argmax, const float* logits, const float* q,
+                            const float* uniforms, int32_t* path, int32_t* path_len, int32_t* next_root,
+                            int32_t* emitted) {
+  if (!c || !tokens || !path || !path_len || !next_root || batch < 1 || n_rows < 1) return EAGLE3_EINVAL;
+  if (batch > c->B || n_rows > 64) return EAGLE3_ECAPACITY;
+  if (c->cfg.mode == EAGLE3_GREEDY_TREE) {
+    if (!parents || !argmax) return EAGLE3_EINVAL;
+    accept_greedy(batch, n_rows, c->cfg.depth, tokens, parents, argmax, path, path_len, next_root, emitted, c->status,
+                  c->st);
+  } else {
+    const int K = c->cfg.depth;
+    if (n_rows != K + 1 || !logits || !q || !uniforms) return EAGLE3_EINVAL;
+    if ((size_t)batch * n_rows > (size_t)c->R) return EAGLE3_ECAPACITY;
+    const int V = c->sh.vocab;
+    topk_lse(logits, batch * n_rows, V, V, 1, c->cfg.temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum,
+             c->tk_ids, c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
+    accept_chain(batch, K, V, tokens, logits, c->tk_lse64, c->cfg.temperature, q, uniforms, path, path_len, next_root,
+                 emitted, c->st);
+  }
+  return last_error();
+}
+
+eagle3_status eagle3_compact_kv(eagle3_ctx* c, int32_t batch, int32_t* seq_lens, int32_t n_rows, const int32_t* path,
+                                const int32_t* path_len, const int32_t* tokens, const int32_t* next_root,
+                                const void* aux_tree, void* aux_new, int32_t* next_tok, int32_t* new_len) {
+  if (!c || !seq_lens || !path || !path_len || !tokens || !next_root || !aux_tree || !aux_new || !next_tok || !new_len)
+    return EAGLE3_EINVAL;
+  if (batch < 1 || batch > c->B || n_rows < 1 || n_rows > 64) return EAGLE3_ECAPACITY;
+  const eagle3_shape& s = c->sh;
+  const int maxp = c->cfg.depth + 1;
+  compact_kv(c->bf16, batch, seq_lens, path, path_len, maxp, n_rows, c->kv_t, s.n_layers, c->B, s.n_kv_heads, c->S_cap,
+             s.head_dim, c->status, c->st);
+  compact_finish(c->bf16, batch, seq_lens, n_rows, maxp, path, path_len, tokens, next_root, aux_tree, 3 * s.d_model,
+                 aux_new, next_tok, new_len, c->st);
+  return last_error();
+}
+
+eagle3_status eagle3_sample(eagle3_ctx* c, int32_t n, const float* logits, float temperature, const float* uniforms,
+                            int32_t* tokens) {
+  if (!c || !logits || !tokens || n < 1 || temperature < 0.f) return EAGLE3_EINVAL;
+  if (temperature > 0.f && !uniforms) return EAGLE3_EINVAL;
+  if (n > c->R) return EAGLE3_ECAPACITY;
+  const int V = c->sh.vocab;
+  topk_lse(logits, n, V, V, 1, temperature > 0.f ? temperature : 1.f, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum,
+           c->tk_ids, c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
+  sample_rows(n, logits, V, temperature, c->tk_lse64, c->tk_ids, uniforms, tokens, c->st);
+  return last_error();
+}
+
+eagle3_status eagle3_device_status(eagle3_ctx* c, int32_t* flags) {
+  if (!c || !flags) return EAGLE3_EINVAL;
+  int v = 0;
+  if (hipMemcpyAsync(&v, c->status, sizeof(int), hipMemcpyDeviceToHost, c->st) != hipSuccess) return EAGLE3_EHIP;
+  if (hipStreamSynchronize(c->st) != hipSuccess) return EAGLE3_EHIP;
+  if (hipMemsetAsync(c->status, 0, sizeof(int), c->st) != hipSuccess) return EAGLE3_EHIP;
+  *flags = v;
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_profile(eagle3_ctx* c, int32_t enable) {
+  if (!c) return EAGLE3_EINVAL;
+  if (hipStreamSynchronize(c->st) != hipSuccess) return EAGLE3_EHIP;
+  c->recs.clear();
+  c->pool_used = 0;
+  c->prof = enable != 0;
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_profile_read(eagle3_ctx* c, int32_t kernel, int64_t* launches, double* total_ms, double* bytes,
+                                  double* flops) {
+  if (!c || !launches || !total_ms || !bytes || !flops || kernel < 0 || kernel >= EAGLE3_PROF_COUNT)
+    return EAGLE3_EINVAL;
+  if (hipStreamSynchronize(c->st) != hipSuccess) return EAGLE3_EHIP;
+  int64_t n = 0;
+  double ms = 0, by = 0, fl = 0;
+  for (const ProfRec& r : c->recs) {
+    if (r.kernel != kernel) continue;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return EAGLE3_EHIP;
+    ++n;
+    ms += t;
+    by += r.bytes;
+    fl += r.flops;
+  }
+  *launches = n;
+  *total_ms = ms;
+  *bytes = by;
+  *flops = fl;
+  return EAGLE3_OK;
+}
+
+}  // extern "C"

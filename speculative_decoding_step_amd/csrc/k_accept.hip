@@ -1,0 +1,248 @@
+// Acceptance and KV compaction.
+//
+// Greedy: from the root follow the child whose token equals the target's
+// argmax at the current node, until none does ("Advanced speculative
+// decoding: tree drafts and EAGLE", Implementation).
+// Sampling (chains): accept d_i iff u_i < p_i(d_i) / q_i(d_i); at the first
+// rejection draw from max(0, p_i - q_i), else draw a bonus from p_K
+// ("EAGLE-3: Engineering Implementation of LLM Inference Acceleration",
+// III.5, X.3-X.6).  Draws use the integer inverse CDF over
+// W_v = floor(w_v * 2^48) with r = floor(u * sum W), so the pick does not
+// depend on summation order.
+// Compaction: the accepted nodes' K/V move to consecutive slots after the
+// committed prefix (the page's note on compacting KV slots).
+#include "common.hpp"
+#include "tree.hpp"
+
+namespace e3 {
+
+static inline unsigned nblk(size_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+__global__ void k_accept_greedy(int batch, int n_rows, int maxp, const int* __restrict__ tokens,
+                                const int* __restrict__ parents, const int* __restrict__ argmax, int* __restrict__ path,
+                                int* __restrict__ path_len, int* __restrict__ next_root, int* __restrict__ emitted,
+                                int* status) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const int* tk = tokens + (size_t)b * n_rows;
+  const int* pa = parents + (size_t)b * n_rows;
+  const int* am = argmax + (size_t)b * n_rows;
+  int* pb = path + (size_t)b * maxp;
+  for (int c = 1; c < n_rows; ++c)
+    if (pa[c] < 0 || pa[c] >= c) {
+      raise_flag(status, E3_DEV_BAD_TREE);
+      break;
+    }
+  int node = 0, len = 1;
+  pb[0] = 0;
+  while (true) {
+    const int pred = am[node];
+    int child = -1;
+    for (int c = node + 1; c < n_rows; ++c)
+      if (pa[c] == node && tk[c] == pred) {
+        child = c;
+        break;
+      }
+    if (child < 0) break;
+    if (len >= maxp) {
+      raise_flag(status, E3_DEV_BAD_PATH);
+      break;
+    }
+    pb[len++] = child;
+    node = child;
+  }
+  next_root[b] = am[node];
+  path_len[b] = len;
+  for (int j = len; j < maxp; ++j) pb[j] = -1;
+  if (emitted)
+    for (int j = 0; j < maxp; ++j) emitted[(size_t)b * maxp + j] = j < len ? tk[pb[j]] : -1;
+}
+
+// One block of 1024 threads per sequence.  lse64[b*(K+1)+i] = log-sum-exp of
+// row i's logits / T in double; p_i(v) = fl32(exp(z / T - lse)).
+__global__ __launch_bounds__(1024) void k_accept_chain(int K, int V, const int* __restrict__ tokens,
+                                                       const float* __restrict__ logits,
+                                                       const double* __restrict__ lse64, double temp,
+                                                       const float* __restrict__ q, const float* __restrict__ uniforms,
+                                                       int* __restrict__ path, int* __restrict__ path_len,
+                                                       int* __restrict__ next_root, int* __restrict__ emitted) {
+  __shared__ unsigned long long scan[1024];
+  __shared__ int nacc, pick, use_p;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int rows = K + 1;
+  const int* tk = tokens + (size_t)b * rows;
+  const float* u = uniforms + (size_t)b * rows;
+  if (tid == 0) {
+    int n = K;
+    for (int i = 0; i < K; ++i) {
+      const int t = tk[i + 1];
+      const float* z = logits + ((size_t)b * rows + i) * V;
+      const float p = (float)exp((double)z[t] / temp - lse64[(size_t)b * rows + i]);
+      const float qq = q[((size_t)b * K + i) * V + t];
+      const float ratio = p / qq;
+      if (!(u[i] < ratio)) {
+        n = i;
+        break;
+      }
+    }
+    nacc = n;
+    use_p = n == K;  // bonus: draw from p_K
+    pick = -1;
+  }
+  __syncthreads();
+  const int row = nacc;
+  const float* z = logits + ((size_t)b * rows + row) * V;
+  const float* qr = q + ((size_t)b * K + (row < K ? row : 0)) * V;
+  const double l = lse64[(size_t)b * rows + row];
+  const int per = (V + 1023) / 1024;
+  const int v0 = tid * per, v1 = min(V, v0 + per);
+  const unsigned long long uu = (unsigned long long)(u[K] * 16777216.0f);
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const bool fromp = use_p;
+    unsigned long long mine = 0ull;
+    for (int v = v0; v < v1; ++v) {
+      const float p = (float)exp((double)z[v] / temp - l);
+      const float w = fromp ? p : fmaxf(p - qr[v], 0.f);
+      mine += (unsigned long long)ldexpf(w, 48);
+    }
+    scan[tid] = mine;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const unsigned long long add = tid >= o ? scan[tid - o] : 0ull;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const unsigned long long S = scan[1023];
+    if (S == 0ull) {  // residual all zero in fp32: draw from p instead
+      __syncthreads();
+      if (tid == 0) use_p = 1;
+      __syncthreads();
+      continue;
+    }
+    const unsigned long long r = (S >> 24) * uu + (((S & 0xffffffull) * uu) >> 24);
+    const unsigned long long lo = tid ? scan[tid - 1] : 0ull;
+    if (r >= lo && r < scan[tid]) {
+      unsigned long long acc = lo;
+      for (int v = v0; v < v1; ++v) {
+        const float p = (float)exp((double)z[v] / temp - l);
+        const float w = fromp ? p : fmaxf(p - qr[v], 0.f);
+        acc += (unsigned long long)ldexpf(w, 48);
+        if (acc > r) {
+          pick = v;
+          break;
+        }
+      }
+    }
+    break;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int maxp = K + 1;
+    for (int j = 0; j < maxp; ++j) {
+      path[(size_t)b * maxp + j] = j <= nacc ? j : -1;
+      if (emitted) emitted[(size_t)b * maxp + j] = j <= nacc ? tk[j] : -1;
+    }
+    path_len[b] = nacc + 1;
+    next_root[b] = pick;
+  }
+}
+
+// grid (B, L*2*Hkv): per (sequence, layer, K|V, head) move path rows to slots P..P+n-1.
+template <typename E>
+__global__ __launch_bounds__(128) void k_compact_kv(const int* __restrict__ seq_lens, const int* __restrict__ path,
+                                                    const int* __restrict__ path_len, int maxp, int n_rows,
+                                                    E* __restrict__ kv,
+                                                    int max_batch, int Hkv, int S_cap, int hd, int* status) {
+  extern __shared__ unsigned char smem[];
+  E* buf = (E*)smem;
+  const int b = blockIdx.x, lh = blockIdx.y;
+  const int lkv = lh / Hkv, g = lh % Hkv;  // lkv = layer*2 + (0 K | 1 V)
+  const int P = seq_lens[b], n = path_len[b];
+  const int* pb = path + (size_t)b * maxp;
+  bool ok = n >= 1 && n <= maxp && pb[0] == 0;
+  for (int j = 1; ok && j < n; ++j) ok = pb[j] > pb[j - 1] && pb[j] < n_rows;
+  if (!ok) {
+    if (threadIdx.x == 0 && lh == 0) raise_flag(status, E3_DEV_BAD_PATH);
+    return;
+  }
+  if (P < 0 || P + pb[n - 1] >= S_cap) {
+    if (threadIdx.x == 0 && lh == 0) raise_flag(status, E3_DEV_KV_OVERFLOW);
+    return;
+  }
+  E* base = kv + ((((size_t)lkv * max_batch + b) * Hkv + g) * S_cap) * hd;
+  for (int idx = threadIdx.x; idx < n * hd; idx += blockDim.x) {
+    const int j = idx / hd, i = idx % hd;
+    buf[idx] = base[(size_t)(P + path[(size_t)b * maxp + j]) * hd + i];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < n * hd; idx += blockDim.x) {
+    const int j = idx / hd, i = idx % hd;
+    base[(size_t)(P + j) * hd + i] = buf[idx];
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void k_compact_finish(int* __restrict__ seq_lens, int n_rows, int maxp,
+                                                        const int* __restrict__ path, const int* __restrict__ path_len,
+                                                        const int* __restrict__ tokens, const int* __restrict__ next_root,
+                                                        const E* __restrict__ aux_tree, int aux_w, E* __restrict__ aux_new,
+                                                        int* __restrict__ next_tok, int* __restrict__ new_len) {
+  const int b = blockIdx.x;
+  const int n = path_len[b];
+  const int* pb = path + (size_t)b * maxp;
+  bool ok = n >= 1 && n <= maxp && pb[0] == 0;
+  for (int j = 1; ok && j < n; ++j) ok = pb[j] > pb[j - 1] && pb[j] < n_rows;
+  if (!ok) return;
+  for (int idx = threadIdx.x; idx < n * aux_w; idx += blockDim.x) {
+    const int j = idx / aux_w, i = idx % aux_w;
+    aux_new[((size_t)b * maxp + j) * aux_w + i] = aux_tree[((size_t)b * n_rows + pb[j]) * aux_w + i];
+  }
+  for (int j = threadIdx.x; j < maxp; j += blockDim.x)
+    next_tok[(size_t)b * maxp + j] =
+        j < n ? (j + 1 < n ? tokens[(size_t)b * n_rows + pb[j + 1]] : next_root[b]) : -1;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    new_len[b] = n;
+    seq_lens[b] += n;
+  }
+}
+
+void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const int* parents, const int* argmax,
+                   int* path, int* path_len, int* next_root, int* emitted, int* status, hipStream_t st) {
+  k_accept_greedy<<<nblk(batch, 64), 64, 0, st>>>(batch, n_rows, depth + 1, tokens, parents, argmax, path, path_len,
+                                                  next_root, emitted, status);
+}
+
+void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,
+                  float temperature, const float* q, const float* uniforms, int* path, int* path_len, int* next_root,
+                  int* emitted, hipStream_t st) {
+  k_accept_chain<<<batch, 1024, 0, st>>>(K, V, tokens, logits, lse64, (double)temperature, q, uniforms, path,
+                                         path_len, next_root, emitted);
+}
+
+void compact_kv(bool bf16, int batch, const int* seq_lens, const int* path, const int* path_len, int maxp, int n_rows, void* kv,
+                int n_layers, int max_batch, int Hkv, int S_cap, int hd, int* status, hipStream_t st) {
+  dim3 grid(batch, n_layers * 2 * Hkv);
+  if (bf16)
+    k_compact_kv<uint16_t><<<grid, 128, maxp * hd * 2, st>>>(seq_lens, path, path_len, maxp, n_rows, (uint16_t*)kv, max_batch,
+                                                             Hkv, S_cap, hd, status);
+  else
+    k_compact_kv<uint32_t><<<grid, 128, maxp * hd * 4, st>>>(seq_lens, path, path_len, maxp, n_rows, (uint32_t*)kv, max_batch,
+                                                             Hkv, S_cap, hd, status);
+}
+
+void compact_finish(bool bf16, int batch, int* seq_lens, int n_rows, int maxp, const int* path, const int* path_len,
+                    const int* tokens, const int* next_root, const void* aux_tree, int aux_w, void* aux_new,
+                    int* next_tok, int* new_len, hipStream_t st) {
+  if (bf16)
+    k_compact_finish<uint16_t><<<batch, 256, 0, st>>>(seq_lens, n_rows, maxp, path, path_len, tokens, next_root,
+                                                      (const uint16_t*)aux_tree, aux_w, (uint16_t*)aux_new, next_tok,
+                                                      new_len);
+  else
+    k_compact_finish<uint32_t><<<batch, 256, 0, st>>>(seq_lens, n_rows, maxp, path, path_len, tokens, next_root,
+                                                      (const uint32_t*)aux_tree, aux_w, (uint32_t*)aux_new, next_tok,
+                                                      new_len);
+}
+
+}  // namespace e3

@@ -1,0 +1,281 @@
+// Weight-streaming GEMM for the step's linear layers: out = X W^T.
+//
+// X [M, K] activations (rows of one verify / draft pass), W [N, K] weights in
+// nn.Linear layout.  At the batch-1 shapes M is 1..64 and every weight byte is
+// read once per pass, so the kernel is HBM-bound: each wave streams 16 weight
+// rows straight from global memory into MFMA operand registers (16-byte loads
+// along K, next K-tile prefetched while the current one is multiplied), and
+// the activation tile is staged once per workgroup in LDS and shared by the
+// four waves.  K is optionally split across workgroups (fp32 partials, summed
+// in a fixed order by the consumer kernel), which keeps enough workgroups in
+// flight on 256 CUs when N is small.
+//
+// MFMA v_mfma_f32_16x16x32_bf16: A (16x32) and B (32x16) fragments hold, in
+// lane l, row/column (l % 16) and K elements 8*(l/16) .. 8*(l/16)+7; the
+// 16x16 fp32 result holds rows 4*(l/16)+r (r = 0..3), column l % 16.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace e3 {
+
+GemmSegs make_segs(const void* w0, int r0, const void* w1, int r1, const void* w2, int r2) {
+  GemmSegs s{};
+  const void* w[3] = {w0, w1, w2};
+  int r[3] = {r0, r1, r2};
+  s.nseg = 0;
+  s.tiles0[0] = 0;
+  int col = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (!w[i] || r[i] <= 0) break;
+    s.w[i] = w[i];
+    s.rows[i] = r[i];
+    s.col0[i] = col;
+    col += r[i];
+    s.tiles0[i + 1] = s.tiles0[i] + (r[i] + 63) / 64;
+    s.nseg = i + 1;
+  }
+  for (int i = s.nseg; i < 3; ++i) s.tiles0[i + 1] = s.tiles0[i];
+  return s;
+}
+
+int gemm_ntot(const GemmSegs& s) { return s.nseg ? s.col0[s.nseg - 1] + s.rows[s.nseg - 1] : 0; }
+
+__device__ __forceinline__ void seg_of(const GemmSegs& s, int tile, int& seg, int& n0) {
+  seg = 0;
+  while (seg + 1 < s.nseg && tile >= s.tiles0[seg + 1]) ++seg;
+  n0 = (tile - s.tiles0[seg]) * 64;
+}
+
+constexpr int KT = 256;       // K per LDS tile
+constexpr int KSTEPS = KT / 32;
+constexpr int XPAD = 8;       // bf16 elements of padding per LDS row
+
+// MB = number of 16-row M blocks per workgroup (1 or 4).
+template <int MB>
+__global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X, int M, int K,
+                                                   GemmSegs segs, float* __restrict__ out, int ldo,
+                                                   size_t split_stride, int kchunk) {
+  __shared__ __attribute__((aligned(16))) bf16_t xs[16 * MB][KT + XPAD];
+  int seg, n0;
+  seg_of(segs, blockIdx.x, seg, n0);
+  const bf16_t* __restrict__ W = (const bf16_t*)segs.w[seg];
+  const int nrows = segs.rows[seg];
+  const int m0 = blockIdx.z * 16 * MB;
+  const int kb = blockIdx.y * kchunk;
+  const int ke = min(K, kb + kchunk);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // weight fragment source: row n0 + 16*wv + lr, K offset 8*lg within each 32-step
+  const int wrow = n0 + 16 * wv + lr;
+  const bool wok = wrow < nrows;
+  const bf16_t* __restrict__ wp = W + (size_t)(wok ? wrow : 0) * K + 8 * lg;
+
+  // activation staging: chunk c = tid + 256*i covers row c/32, columns 8*(c%32)
+  constexpr int XCH = 2 * MB;  // 16-byte chunks per thread per tile
+  u32x4 xr[XCH];
+  u32x4 wa[KSTEPS], wb[KSTEPS];
+  f32x4 acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_w = [&](u32x4* dst, int kt) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      dst[s] = wok ? *(const u32x4*)(wp + kt + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto load_x = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int c = tid + 256 * i, row = c >> 5, col = (c & 31) * 8;
+      const int m = m0 + row;
+      xr[i] = (m < M) ? *(const u32x4*)(X + (size_t)m * K + kt + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_x = [&]() {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int c = tid + 256 * i, row = c >> 5, col = (c & 31) * 8;
+      *(u32x4*)&xs[row][col] = xr[i];
+    }
+  };
+
+  if (kb < ke) {
+    load_w(wa, kb);
+    load_x(kb);
+  }
+  for (int kt = kb; kt < ke; kt += KT) {
+    __syncthreads();
+    store_x();
+    __syncthreads();
+    const bool more = kt + KT < ke;
+    if (more) {
+      load_w(wb, kt + KT);
+      load_x(kt + KT);
+    }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, wa[s]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)&xs[16 * mb + lr][32 * s + 8 * lg]);
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mb], 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) wa[s] = wb[s];
+    }
+  }
+  // result: acc[mb][r] = out[m0 + 16mb + 4lg + r][n0 + 16wv + lr]
+  if (!wok) return;
+  float* o = out + blockIdx.y * split_stride + segs.col0[seg] + wrow;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 16 * mb + 4 * lg + r;
+      if (m < M) o[(size_t)m * ldo] = acc[mb][r];
+    }
+  }
+}
+
+// fp32 GEMM (the tiny fp32 workload): 32 x 64 output tile per workgroup, each
+// thread 2 x 4 outputs, K tiles of 32 staged in LDS for both operands.
+__global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ X, int M, int K, GemmSegs segs,
+                                                  float* __restrict__ out, int ldo, size_t split_stride,
+                                                  int kchunk) {
+  __shared__ float xs[32][33];
+  __shared__ float ws[64][33];
+  int seg, n0;
+  seg_of(segs, blockIdx.x, seg, n0);
+  const float* __restrict__ W = (const float*)segs.w[seg];
+  const int nrows = segs.rows[seg];
+  const int m0 = blockIdx.z * 32;
+  const int kb = blockIdx.y * kchunk, ke = min(K, kb + kchunk);
+  const int tid = threadIdx.x, tn = tid & 15, tm = tid >> 4;  // 16 x 16 threads
+  float acc[2][4] = {};
+  for (int kt = kb; kt < ke; kt += 32) {
+    for (int i = tid; i < 32 * 32; i += 256) {
+      const int r = i >> 5, c = i & 31, m = m0 + r, k = kt + c;
+      xs[r][c] = (m < M && k < ke) ? X[(size_t)m * K + k] : 0.f;
+    }
+    for (int i = tid; i < 64 * 32; i += 256) {
+      const int r = i >> 5, c = i & 31, n = n0 + r, k = kt + c;
+      ws[r][c] = (n < nrows && k < ke) ? W[(size_t)n * K + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < 32; ++c) {
+      float a0 = xs[tm * 2][c], a1 = xs[tm * 2 + 1][c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float b = ws[tn + 16 * j][c];
+        acc[0][j] += a0 * b;
+        acc[1][j] += a1 * b;
+      }
+    }
+    __syncthreads();
+  }
+  float* o = out + blockIdx.y * split_stride + segs.col0[seg];
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + tm * 2 + i, n = n0 + tn + 16 * j;
+      if (m < M && n < nrows) o[(size_t)m * ldo + n] = acc[i][j];
+    }
+}
+
+int gemm_splits(bool bf16, int K, int splits) {
+  const int unit = bf16 ? KT : 32;
+  const int kt = (K + unit - 1) / unit;
+  if (splits < 1) splits = 1;
+  if (splits > kt) splits = kt;
+  const int per = (kt + splits - 1) / splits;
+  return (kt + per - 1) / per;
+}
+
+int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out, size_t split_stride,
+         int splits, int m_tile, hipStream_t st) {
+  splits = gemm_splits(bf16, K, splits);
+  if (M <= 0) return splits;
+  const int ldo = gemm_ntot(segs);
+  const int ntiles = segs.tiles0[segs.nseg];
+  if (bf16) {
+    // split K into `splits` chunks that are multiples of the LDS tile
+    const int ktiles = K / KT;
+    const int per = (ktiles + splits - 1) / splits;
+    const int kchunk = per * KT;
+    const int S = (ktiles + per - 1) / per;
+    if (m_tile == 16) {
+      dim3 grid(ntiles, S, (M + 15) / 16);
+      k_gemm_bf16<1><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, out, ldo, split_stride, kchunk);
+    } else {
+      dim3 grid(ntiles, S, (M + 63) / 64);
+      k_gemm_bf16<4><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, out, ldo, split_stride, kchunk);
+    }
+  } else {
+    const int per = ((K + 31) / 32 + splits - 1) / splits;
+    const int kchunk = per * 32;
+    const int S = (K + kchunk - 1) / kchunk;
+    dim3 grid(ntiles, S, (M + 31) / 32);
+    k_gemm_f32<<<grid, 256, 0, st>>>((const float*)X, M, K, segs, out, ldo, split_stride, kchunk);
+  }
+  return splits;
+}
+
+// ------------------------------------------------------------- partial consumers
+
+__global__ void k_resid_add(float* __restrict__ x, const float* __restrict__ part, int S, size_t sstride,
+                            int M, int N, int ldp) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)M * N) return;
+  const int m = i / N, n = i % N;
+  float s = 0.f;
+  for (int k = 0; k < S; ++k) s += part[k * sstride + (size_t)m * ldp + n];
+  x[i] += s;
+}
+
+__global__ void k_sum_store(float* __restrict__ out, const float* __restrict__ part, int S, size_t sstride,
+                            int M, int N, int ldp) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)M * N) return;
+  const int m = i / N, n = i % N;
+  float s = 0.f;
+  for (int k = 0; k < S; ++k) s += part[k * sstride + (size_t)m * ldp + n];
+  out[i] = s;
+}
+
+template <typename T>
+__global__ void k_silu_mul(T* __restrict__ out, const float* __restrict__ part, int S, size_t sstride, int M,
+                           int F, int ldp) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)M * F) return;
+  const int m = i / F, n = i % F;
+  float g = 0.f, u = 0.f;
+  for (int k = 0; k < S; ++k) {
+    g += part[k * sstride + (size_t)m * ldp + n];
+    u += part[k * sstride + (size_t)m * ldp + F + n];
+  }
+  st<T>(out, i, g / (1.f + expf(-g)) * u);
+}
+
+static inline unsigned nblk(size_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+void resid_add(float* x, const float* part, int S, size_t sstride, int M, int N, int ldp, hipStream_t st) {
+  if (M <= 0) return;
+  k_resid_add<<<nblk((size_t)M * N, 256), 256, 0, st>>>(x, part, S, sstride, M, N, ldp);
+}
+void sum_store(float* out, const float* part, int S, size_t sstride, int M, int N, int ldp, hipStream_t st) {
+  if (M <= 0) return;
+  k_sum_store<<<nblk((size_t)M * N, 256), 256, 0, st>>>(out, part, S, sstride, M, N, ldp);
+}
+void silu_mul(bool bf16, void* out, const float* part, int S, size_t sstride, int M, int F, int ldp,
+              hipStream_t st) {
+  if (M <= 0) return;
+  if (bf16)
+    k_silu_mul<bf16_t><<<nblk((size_t)M * F, 256), 256, 0, st>>>((bf16_t*)out, part, S, sstride, M, F, ldp);
+  else
+    k_silu_mul<float><<<nblk((size_t)M * F, 256), 256, 0, st>>>((float*)out, part, S, sstride, M, F, ldp);
+}
+
+}  // namespace e3

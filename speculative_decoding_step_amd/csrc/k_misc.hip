@@ -1,0 +1,302 @@
+// Row-wise kernels of the step: embedding gather, RMSNorm (+ aux tap capture),
+// the draft head's [input_norm(e) ; hidden_norm(x)] input, rotary embedding
+// with the KV-cache write, and the vocabulary top-k / log-sum-exp.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace e3 {
+
+static inline unsigned nblk(size_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+// ------------------------------------------------------------------ embedding
+template <typename T>
+__global__ void k_embed(const T* __restrict__ table, const int* __restrict__ tokens, float* __restrict__ x,
+                        int d, int V, int* status) {
+  const int r = blockIdx.x;
+  int t = tokens[r];
+  if (t < 0 || t >= V) {
+    if (threadIdx.x == 0 && t != -1) raise_flag(status, E3_DEV_BAD_TOKEN);
+    for (int i = threadIdx.x; i < d; i += blockDim.x) x[(size_t)r * d + i] = 0.f;
+    return;
+  }
+  for (int i = threadIdx.x; i < d; i += blockDim.x) x[(size_t)r * d + i] = ld<T>(table, (size_t)t * d + i);
+}
+
+void embed_rows(bool bf16, const void* table, const int* tokens, float* x, int R, int d, int V, int* status,
+                hipStream_t st) {
+  if (R <= 0) return;
+  if (bf16)
+    k_embed<bf16_t><<<R, 256, 0, st>>>((const bf16_t*)table, tokens, x, d, V, status);
+  else
+    k_embed<float><<<R, 256, 0, st>>>((const float*)table, tokens, x, d, V, status);
+}
+
+// -------------------------------------------------------------------- rmsnorm
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, const T* __restrict__ w,
+                                                 T* __restrict__ out, int out_ld, int d, float eps,
+                                                 T* __restrict__ tap, int tap_ld) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  const float* xr = x + (size_t)r * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float v = xr[i];
+    ss += v * v;
+    if (tap) st<T>(tap, (size_t)r * tap_ld + i, v);
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+  for (int i = threadIdx.x; i < d; i += blockDim.x)
+    st<T>(out, (size_t)r * out_ld + i, xr[i] * inv * ld<T>(w, i));
+}
+
+void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, int R, int d, float eps, void* tap,
+             int tap_ld, hipStream_t st) {
+  if (R <= 0) return;
+  if (bf16)
+    k_rmsnorm<bf16_t><<<R, 256, 0, st>>>(x, (const bf16_t*)w, (bf16_t*)out, out_ld, d, eps, (bf16_t*)tap, tap_ld);
+  else
+    k_rmsnorm<float><<<R, 256, 0, st>>>(x, (const float*)w, (float*)out, out_ld, d, eps, (float*)tap, tap_ld);
+}
+
+// ---------------------------------------------------------------- draft input
+template <typename T>
+__global__ __launch_bounds__(256) void k_draft_input(const T* __restrict__ embed, const int* __restrict__ tokens,
+                                                     const float* __restrict__ x, const T* __restrict__ w_in,
+                                                     const T* __restrict__ w_hid, T* __restrict__ out, int d,
+                                                     int V, float eps, int* status) {
+  __shared__ float red[16];
+  const int r = blockIdx.x;
+  int t = tokens[r];
+  const bool ok = t >= 0 && t < V;
+  if (!ok && threadIdx.x == 0 && t != -1) raise_flag(status, E3_DEV_BAD_TOKEN);
+  if (!ok) t = 0;
+  const float* xr = x + (size_t)r * d;
+  float se = 0.f, sx = 0.f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float e = ok ? ld<T>(embed, (size_t)t * d + i) : 0.f;
+    se += e * e;
+    sx += xr[i] * xr[i];
+  }
+  se = block_sum(se, red);
+  sx = block_sum(sx, red);
+  const float ie = 1.f / sqrtf(se / (float)d + eps), ix = 1.f / sqrtf(sx / (float)d + eps);
+  T* o = out + (size_t)r * 2 * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float e = ok ? ld<T>(embed, (size_t)t * d + i) : 0.f;
+    st<T>(o, i, e * ie * ld<T>(w_in, i));
+    st<T>(o, d + i, xr[i] * ix * ld<T>(w_hid, i));
+  }
+}
+
+void draft_input(bool bf16, const void* embed, const int* tokens, const float* x, const void* w_in,
+                 const void* w_hid, void* out, int R, int d, int V, float eps, int* status, hipStream_t st) {
+  if (R <= 0) return;
+  if (bf16)
+    k_draft_input<bf16_t><<<R, 256, 0, st>>>((const bf16_t*)embed, tokens, x, (const bf16_t*)w_in,
+                                             (const bf16_t*)w_hid, (bf16_t*)out, d, V, eps, status);
+  else
+    k_draft_input<float><<<R, 256, 0, st>>>((const float*)embed, tokens, x, (const float*)w_in,
+                                            (const float*)w_hid, (float*)out, d, V, eps, status);
+}
+
+// ----------------------------------------------------------- rope + KV write
+// One block per row; QKV partial columns [q heads | k heads | v heads].
+// Angles: pos * theta^(-2i/hd) evaluated in double, then cos/sin in double.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_kv(const float* __restrict__ part, int S, size_t sstride,
+                                                 const int* __restrict__ rseq, const int* __restrict__ rpos,
+                                                 const int* __restrict__ rslot, T* __restrict__ q_out,
+                                                 T* __restrict__ kc, T* __restrict__ vc, size_t seq_stride,
+                                                 size_t head_stride, int Hq, int Hkv, int hd, float theta) {
+  const int r = blockIdx.x;
+  const int b = rseq[r];
+  const int ncol = (Hq + 2 * Hkv) * hd;
+  const int half = hd / 2;
+  const double pos = (double)rpos[r];
+  const float* pr = part + (size_t)r * ncol;
+  auto val = [&](int c) {
+    float s = 0.f;
+    for (int k = 0; k < S; ++k) s += pr[k * sstride + c];
+    return s;
+  };
+  // q and k heads: pairs (i, i + half) rotated by angle pos * inv_freq[i]
+  const int npairs = (Hq + Hkv) * half;
+  for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
+    const int h = p / half, i = p % half;
+    const int c0 = h * hd + i, c1 = c0 + half;
+    const float x1 = val(c0), x2 = val(c1);
+    const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
+    double sn, cs;
+    sincos(pos * inv, &sn, &cs);
+    const float c = (float)cs, s = (float)sn;
+    const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
+    if (h < Hq) {
+      st<T>(q_out, (size_t)r * Hq * hd + h * hd + i, y1);
+      st<T>(q_out, (size_t)r * Hq * hd + h * hd + i + half, y2);
+    } else if (b >= 0) {
+      const int g = h - Hq;
+      T* kp = kc + (size_t)b * seq_stride + (size_t)g * head_stride + (size_t)rslot[r] * hd;
+      st<T>(kp, i, y1);
+      st<T>(kp, i + half, y2);
+    }
+  }
+  if (b < 0) return;
+  for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x) {
+    const int g = e / hd, i = e % hd;
+    T* vp = vc + (size_t)b * seq_stride + (size_t)g * head_stride + (size_t)rslot[r] * hd;
+    st<T>(vp, i, val((Hq + Hkv) * hd + e));
+  }
+}
+
+void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const RowMeta& rm, void* q_out, void* kc,
+             void* vc, size_t seq_stride, size_t head_stride, int Hq, int Hkv, int hd, float theta,
+             hipStream_t st) {
+  if (R <= 0) return;
+  if (bf16)
+    k_rope_kv<bf16_t><<<R, 256, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, (bf16_t*)q_out, (bf16_t*)kc,
+                                         (bf16_t*)vc, seq_stride, head_stride, Hq, Hkv, hd, theta);
+  else
+    k_rope_kv<float><<<R, 256, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, (float*)q_out, (float*)kc,
+                                        (float*)vc, seq_stride, head_stride, Hq, Hkv, hd, theta);
+}
+
+// ------------------------------------------------------------- top-k + lse
+constexpr int TK_SLICE = 4096;  // vocabulary entries per partial block
+constexpr int TK_KMAX = 16;
+
+int topk_slices(int V) { return (V + TK_SLICE - 1) / TK_SLICE; }
+
+struct VI {
+  float v;
+  int i;
+};
+
+E3_DEV VI vi_best(VI a, VI b) { return better(a.v, a.i, b.v, b.i) ? a : b; }
+
+E3_DEV VI wave_best(VI x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    VI y{__shfl_xor(x.v, o, 64), __shfl_xor(x.i, o, 64)};
+    x = vi_best(x, y);
+  }
+  return x;
+}
+
+// grid (R, nslices), block 256.  Per slice: the K best (value, index) and the
+// slice's max and sum of exp(z - max) in double, with z = logit / temperature.
+__global__ __launch_bounds__(256) void k_topk_partial(const float* __restrict__ logits, int V, int ld, int K,
+                                                      double temp, float* __restrict__ pv, int* __restrict__ pi,
+                                                      float* __restrict__ pmax, double* __restrict__ psum) {
+  __shared__ float vals[TK_SLICE];
+  __shared__ unsigned char taken[TK_SLICE];
+  __shared__ VI wred[4];
+  __shared__ double dred[4];
+  const int r = blockIdx.x, sl = blockIdx.y, ns = gridDim.y;
+  const int v0 = sl * TK_SLICE, n = min(TK_SLICE, V - v0);
+  const float* row = logits + (size_t)r * ld + v0;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  VI best{-INFINITY, 0x7fffffff};
+  for (int i = tid; i < n; i += 256) {
+    const float v = row[i];
+    vals[i] = v;
+    taken[i] = 0;
+    best = vi_best(best, VI{v, v0 + i});
+  }
+  best = wave_best(best);
+  if (lane == 0) wred[w] = best;
+  __syncthreads();
+  const VI top = vi_best(vi_best(wred[0], wred[1]), vi_best(wred[2], wred[3]));
+  const double m = (double)top.v / temp;
+  double s = 0.0;
+  for (int i = tid; i < n; i += 256) s += exp((double)vals[i] / temp - m);
+  s = wave_sum_d(s);
+  if (lane == 0) dred[w] = s;
+  __syncthreads();
+  const size_t o = (size_t)r * ns + sl;
+  if (tid == 0) {
+    pmax[o] = (float)top.v;
+    psum[o] = dred[0] + dred[1] + dred[2] + dred[3];
+  }
+  for (int k = 0; k < K; ++k) {
+    VI b{-INFINITY, 0x7fffffff};
+    for (int i = tid; i < n; i += 256)
+      if (!taken[i]) b = vi_best(b, VI{vals[i], v0 + i});
+    b = wave_best(b);
+    __syncthreads();
+    if (lane == 0) wred[w] = b;
+    __syncthreads();
+    const VI t = vi_best(vi_best(wred[0], wred[1]), vi_best(wred[2], wred[3]));
+    if (tid == 0) {
+      pv[o * K + k] = t.v;
+      pi[o * K + k] = t.i;
+    }
+    if (t.i >= v0 && t.i < v0 + n && ((t.i - v0) % 256) == tid) taken[t.i - v0] = 1;
+    __syncthreads();
+  }
+}
+
+// grid (R), block 64: merge the slices' candidates, combine the sums in slice order.
+__global__ __launch_bounds__(64) void k_topk_merge(int ns, int K, double temp, const float* __restrict__ pv,
+                                                   const int* __restrict__ pi, const float* __restrict__ pmax,
+                                                   const double* __restrict__ psum, int* __restrict__ out_ids,
+                                                   float* __restrict__ out_vals, float* __restrict__ lse32,
+                                                   double* __restrict__ lse64) {
+  __shared__ unsigned char taken[64 * TK_KMAX];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int nc = ns * K;
+  const float* cv = pv + (size_t)r * nc;
+  const int* ci = pi + (size_t)r * nc;
+  for (int c = tid; c < nc; c += 64) taken[c] = 0;
+  __syncthreads();
+  for (int k = 0; k < K; ++k) {
+    VI b{-INFINITY, 0x7fffffff};
+    int bc = -1;
+    for (int c = tid; c < nc; c += 64)
+      if (!taken[c] && better(cv[c], ci[c], b.v, b.i)) {
+        b = VI{cv[c], ci[c]};
+        bc = c;
+      }
+    VI w = wave_best(b);
+    if (b.i == w.i && b.v == w.v && bc >= 0) taken[bc] = 1;
+    if (tid == 0) {
+      out_ids[(size_t)r * K + k] = w.i;
+      out_vals[(size_t)r * K + k] = w.v;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    float mx = -INFINITY;
+    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, pmax[(size_t)r * ns + s]);
+    const double M = (double)mx / temp;
+    double S = 0.0;
+    for (int s = 0; s < ns; ++s) S += psum[(size_t)r * ns + s] * exp((double)pmax[(size_t)r * ns + s] / temp - M);
+    const double l = M + log(S);
+    if (lse64) lse64[r] = l;
+    if (lse32) lse32[r] = (float)l;
+  }
+}
+
+void topk_lse(const float* logits, int R, int V, int ld, int K, float temperature, float* pv, int* pi, float* pmax,
+              double* psum, int* out_ids, float* out_vals, float* lse32, double* lse64, hipStream_t st) {
+  if (R <= 0) return;
+  const int ns = topk_slices(V);
+  const double t = (double)temperature;
+  k_topk_partial<<<dim3(R, ns), 256, 0, st>>>(logits, V, ld, K, t, pv, pi, pmax, psum);
+  k_topk_merge<<<R, 64, 0, st>>>(ns, K, t, pv, pi, pmax, psum, out_ids, out_vals, lse32, lse64);
+}
+
+// -------------------------------------------------------------- row gather
+__global__ void k_gather_rows_f32(float* __restrict__ dst, const float* __restrict__ src,
+                                  const int* __restrict__ idx, int d) {
+  const int r = blockIdx.x, s = idx[r];
+  for (int i = threadIdx.x; i < d; i += blockDim.x) dst[(size_t)r * d + i] = s >= 0 ? src[(size_t)s * d + i] : 0.f;
+}
+
+void gather_rows_f32(float* dst, const float* src, const int* idx, int n, int d, hipStream_t st) {
+  if (n <= 0) return;
+  k_gather_rows_f32<<<n, 256, 0, st>>>(dst, src, idx, d);
+}
+
+}  // namespace e3

@@ -1,0 +1,313 @@
+// Draft-tree construction: candidates, frontier selection, final re-rank and
+// the ancestry masks ("Advanced speculative decoding: tree drafts and EAGLE",
+// Why trees and Implementation; EAGLE-2's dynamic tree as summarised in
+// "EAGLE-3: Engineering Implementation of LLM Inference Acceleration", VI.7).
+//
+// Reading implemented (per sequence, k = topk, D = depth):
+//   score(root) = 0, score(child) = fl32(score(parent) + fl32(logit - lse)),
+//   children = the top-k logits of the expanded row (value desc, id asc);
+//   the frontier of depth d is the k best depth-d candidates by (score desc,
+//   creation index asc); after depth D the N best of all candidates are kept
+//   and numbered root first, then by (depth, creation index).
+// Candidate c (creation index) lives at cand[b][c]; depth-1 candidates are
+// 0..k-1, those created at depth d >= 2 are k + (d-2) k^2 + rank*k + child.
+// Expansion row e = (d-1) k + rank is the draft row that expanded the rank-th
+// frontier node of depth d; its draft K/V sits at slot P_b + e and its tail
+// mask (bits of the expansion rows on its ancestor chain and itself) is
+// emask[b][e].
+#include "common.hpp"
+#include "tree.hpp"
+
+namespace e3 {
+
+static inline unsigned nblk(size_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+// Children of the rows just expanded.  depth_new = depth of the children.
+// Rows: depth_new == 1 -> one root row per sequence (row b); else k rows per
+// sequence (row b*k + rank).
+__global__ void k_tree_children(TreeState ts, int depth_new, const int* __restrict__ ids,
+                                const float* __restrict__ vals, const float* __restrict__ lse, int kk) {
+  const int k = ts.topk;
+  const int per = depth_new == 1 ? k : k * k;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= ts.batch * per) return;
+  const int b = i / per, j = i % per;
+  const int rank = j / k, child = j % k;
+  const int row = depth_new == 1 ? b : b * k + rank;
+  const int base = depth_new == 1 ? 0 : k + (depth_new - 2) * k * k;
+  const int c = base + j;
+  const float lp = vals[(size_t)row * kk + child] - lse[row];
+  float ps = 0.f;
+  int par = -1;
+  if (depth_new > 1) {
+    par = ts.front[b * k + rank];
+    ps = ts.score[(size_t)b * ts.cmax + par];
+  }
+  const size_t o = (size_t)b * ts.cmax + c;
+  ts.tok[o] = ids[(size_t)row * kk + child];
+  ts.par[o] = par;
+  ts.dep[o] = depth_new;
+  ts.score[o] = ps + lp;
+  ts.erow[o] = -1;
+}
+
+E3_DEV bool cand_better(float sa, int ca, float sb, int cb) { return sa > sb || (sa == sb && ca < cb); }
+
+// Frontier of depth d (the k best candidates of that depth), one block per
+// sequence.  Also fills the expansion rows' draft inputs: token, parent row,
+// RoPE position P + d - 1, KV slot P + e, and the tail mask.
+__global__ __launch_bounds__(256) void k_tree_frontier(TreeState ts, int d, const int* __restrict__ seq_lens,
+                                                       DraftRows dr, int S_cap, int* status) {
+  const int b = blockIdx.x, k = ts.topk;
+  const int c0 = d == 1 ? 0 : k + (d - 2) * k * k;
+  const int n = d == 1 ? k : k * k;
+  const size_t base = (size_t)b * ts.cmax;
+  for (int c = threadIdx.x; c < n; c += blockDim.x) {
+    const float sc = ts.score[base + c0 + c];
+    int rank = 0;
+    for (int o = 0; o < n; ++o) {
+      const float so = ts.score[base + c0 + o];
+      rank += cand_better(so, c0 + o, sc, c0 + c);
+    }
+    if (rank < k) ts.front[b * k + rank] = c0 + c;
+  }
+  __syncthreads();
+  const int P = seq_lens[b];
+  for (int rank = threadIdx.x; rank < k; rank += blockDim.x) {
+    const int c = ts.front[b * k + rank];
+    const int e = (d - 1) * k + rank;
+    ts.erow[base + c] = e;
+    const int par = ts.par[base + c];
+    const int pe = par < 0 ? -1 : ts.erow[base + par];
+    const uint64_t pm = pe < 0 ? 0ull : ts.emask[(size_t)b * ts.emax + pe];
+    const uint64_t m = pm | (1ull << e);
+    ts.emask[(size_t)b * ts.emax + e] = m;
+    const int r = b * k + rank;
+    const bool fits = P >= 0 && P + e < S_cap;
+    if (!fits) raise_flag(status, E3_DEV_KV_OVERFLOW);
+    dr.tok[r] = ts.tok[base + c];
+    dr.src[r] = pe < 0 ? -1 - b : b * ts.emax + pe;  // -1-b: the catch-up row's a
+    dr.seq[r] = fits ? b : -1;
+    dr.pos[r] = P + d - 1;
+    dr.slot[r] = P + e;
+    dr.lim[r] = P;
+    dr.tail0[r] = P;
+    dr.mask[r] = m;
+  }
+}
+
+// x of the expansion rows: a of the parent's expansion row, or of the catch-up row.
+__global__ void k_tree_gather_x(float* __restrict__ x, const int* __restrict__ src, const float* __restrict__ a_rows,
+                                const float* __restrict__ a_last, int d_model) {
+  const int r = blockIdx.x, s = src[r];
+  const float* from = s < 0 ? a_last + (size_t)(-1 - s) * d_model : a_rows + (size_t)s * d_model;
+  for (int i = threadIdx.x; i < d_model; i += blockDim.x) x[(size_t)r * d_model + i] = from[i];
+}
+
+// Store the expansion rows' outputs a (needed as x by their children).
+__global__ void k_tree_store_a(float* __restrict__ a_rows, const float* __restrict__ a, const int* __restrict__ slot,
+                               const int* __restrict__ seq_lens, int k, int emax, int d_model) {
+  const int r = blockIdx.x, b = r / k;
+  const int e = slot[r] - seq_lens[b];
+  for (int i = threadIdx.x; i < d_model; i += blockDim.x)
+    a_rows[((size_t)b * emax + e) * d_model + i] = a[(size_t)r * d_model + i];
+}
+
+// Final selection, numbering and masks, one block (512 threads) per sequence.
+__global__ __launch_bounds__(512) void k_tree_finalize(TreeState ts, int n_cand, int n_nodes,
+                                                       const int* __restrict__ roots, const int* __restrict__ seq_lens,
+                                                       TreeOut out, int* status) {
+  __shared__ int node_of[TREE_CMAX];  // creation index -> node index (0 = not kept)
+  __shared__ int pidx[65];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const size_t base = (size_t)b * ts.cmax;
+  const int rows = n_nodes + 1;
+  for (int c = tid; c < n_cand; c += blockDim.x) {
+    const float sc = ts.score[base + c];
+    int rank = 0;
+    for (int o = 0; o < n_cand; ++o) rank += cand_better(ts.score[base + o], o, sc, c);
+    node_of[c] = rank < n_nodes ? -1 : 0;  // -1: kept, index assigned below
+  }
+  __syncthreads();
+  for (int c = tid; c < n_cand; c += blockDim.x) {
+    if (node_of[c] != -1) continue;
+    const int dc = ts.dep[base + c];
+    int pos = 1;
+    for (int o = 0; o < n_cand; ++o) {
+      if (node_of[o] == 0) continue;
+      const int od = ts.dep[base + o];
+      pos += (od < dc) || (od == dc && o < c);
+    }
+    node_of[c] = -1 - pos;  // encoded until every thread has read the kept flags
+  }
+  __syncthreads();
+  for (int c = tid; c < n_cand; c += blockDim.x)
+    if (node_of[c] < -1) node_of[c] = -node_of[c] - 1;
+  __syncthreads();
+  const int P = seq_lens[b];
+  const size_t ob = (size_t)b * rows;
+  if (tid == 0) {
+    out.tokens[ob] = roots[b];
+    out.parents[ob] = -1;
+    out.depth[ob] = 0;
+    out.pos[ob] = P;
+    out.score[ob] = 0.f;
+    pidx[0] = -1;
+  }
+  for (int c = tid; c < n_cand; c += blockDim.x) {
+    const int i = node_of[c];
+    if (i <= 0) continue;
+    const int pc = ts.par[base + c];
+    const int pi = pc < 0 ? 0 : node_of[pc];
+    if (pc >= 0 && pi <= 0) raise_flag(status, E3_DEV_BAD_TREE);
+    out.tokens[ob + i] = ts.tok[base + c];
+    out.parents[ob + i] = pi;
+    out.depth[ob + i] = ts.dep[base + c];
+    out.pos[ob + i] = P + ts.dep[base + c];
+    out.score[ob + i] = ts.score[base + c];
+    pidx[i] = pi;
+  }
+  __syncthreads();
+  for (int i = tid; i < rows; i += blockDim.x) {
+    uint64_t m = 0ull;
+    int j = i, guard = 0;
+    while (j >= 0 && guard++ <= 64) {
+      m |= 1ull << j;
+      j = pidx[j];
+    }
+    out.mask[ob + i] = m;
+  }
+}
+
+// ---------------------------------------------------------------- sampled chain
+// Per row b: draw from q = softmax(z / T) (z = logits row b) by the integer
+// inverse CDF over W_v = floor(q_v * 2^48), r = floor(u * sum W); or take the
+// argmax (top1) for greedy drafts.  q_out (optional) receives q (one-hot for
+// greedy drafts).  out_tok[b * tok_stride + tok_off] receives the token.
+__global__ __launch_bounds__(1024) void k_draw(const float* __restrict__ logits, int ld, int V, double temp,
+                                               const double* __restrict__ lse64, const int* __restrict__ top1,
+                                               const float* __restrict__ uniforms, int u_stride, int greedy,
+                                               float* __restrict__ q_out, size_t q_stride, int* __restrict__ out_tok,
+                                               int tok_stride) {
+  __shared__ unsigned long long scan[1024];
+  __shared__ int pick;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const float* z = logits + (size_t)b * ld;
+  float* q = q_out ? q_out + (size_t)b * q_stride : nullptr;
+  if (greedy) {
+    const int t = top1[b];
+    if (q)
+      for (int v = tid; v < V; v += blockDim.x) q[v] = v == t ? 1.f : 0.f;
+    if (tid == 0) out_tok[(size_t)b * tok_stride] = t;
+    return;
+  }
+  const double l = lse64[b];
+  const int per = (V + blockDim.x - 1) / blockDim.x;
+  const int v0 = tid * per, v1 = min(V, v0 + per);
+  unsigned long long mine = 0ull;
+  for (int v = v0; v < v1; ++v) {
+    const float qv = (float)exp((double)z[v] / temp - l);
+    if (q) q[v] = qv;
+    mine += (unsigned long long)ldexpf(qv, 48);
+  }
+  scan[tid] = mine;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan of the per-thread totals
+    const unsigned long long add = tid >= o ? scan[tid - o] : 0ull;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const unsigned long long S = scan[1023];
+  const unsigned long long u = (unsigned long long)(uniforms[(size_t)b * u_stride] * 16777216.0f);
+  const unsigned long long r = (S >> 24) * u + (((S & 0xffffffull) * u) >> 24);
+  if (tid == 0) pick = -1;
+  __syncthreads();
+  const unsigned long long lo = tid ? scan[tid - 1] : 0ull;
+  if (S > 0 && r >= lo && r < scan[tid]) {
+    unsigned long long acc = lo;
+    for (int v = v0; v < v1; ++v) {
+      acc += (unsigned long long)ldexpf((float)exp((double)z[v] / temp - l), 48);
+      if (acc > r) {
+        pick = v;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) out_tok[(size_t)b * tok_stride] = pick;
+}
+
+// Chain expansion row j (0-based) of sequence b expands draft d_{j+1}.
+__global__ void k_chain_rows(int j, int K, const int* __restrict__ chain_tok, const int* __restrict__ seq_lens,
+                             int emax, DraftRows dr, int S_cap) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= dr.batch) return;
+  const int P = seq_lens[b];
+  dr.tok[b] = chain_tok[b * (K + 1) + 1 + j];
+  dr.src[b] = j == 0 ? -1 - b : b * emax + (j - 1);
+  dr.seq[b] = (P >= 0 && P + j < S_cap) ? b : -1;
+  dr.pos[b] = P + j;
+  dr.slot[b] = P + j;
+  dr.lim[b] = P;
+  dr.tail0[b] = P;
+  dr.mask[b] = (j + 1 >= 64) ? ~0ull : ((1ull << (j + 1)) - 1ull);
+}
+
+__global__ void k_chain_finalize(int K, const int* __restrict__ roots, const int* __restrict__ seq_lens,
+                                 int* __restrict__ chain_tok, TreeOut out, int batch) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= batch * (K + 1)) return;
+  const int b = i / (K + 1), n = i % (K + 1);
+  const int t = n == 0 ? roots[b] : chain_tok[i];
+  out.tokens[i] = t;
+  out.parents[i] = n - 1;
+  out.depth[i] = n;
+  out.pos[i] = seq_lens[b] + n;
+  out.mask[i] = (n + 1 >= 64) ? ~0ull : ((1ull << (n + 1)) - 1ull);
+  out.score[i] = 0.f;
+}
+
+// ------------------------------------------------------------------- launches
+void tree_children(const TreeState& ts, int depth_new, const int* ids, const float* vals, const float* lse, int kk,
+                   hipStream_t st) {
+  const int per = depth_new == 1 ? ts.topk : ts.topk * ts.topk;
+  k_tree_children<<<nblk((size_t)ts.batch * per, 128), 128, 0, st>>>(ts, depth_new, ids, vals, lse, kk);
+}
+void tree_frontier(const TreeState& ts, int d, const int* seq_lens, const DraftRows& dr, int S_cap, int* status,
+                   hipStream_t st) {
+  k_tree_frontier<<<ts.batch, 256, 0, st>>>(ts, d, seq_lens, dr, S_cap, status);
+}
+void tree_gather_x(float* x, const int* src, const float* a_rows, const float* a_last, int n, int d_model,
+                   hipStream_t st) {
+  if (n > 0) k_tree_gather_x<<<n, 256, 0, st>>>(x, src, a_rows, a_last, d_model);
+}
+void tree_store_a(float* a_rows, const float* a, const int* slot, const int* seq_lens, int n, int k, int emax,
+                  int d_model, hipStream_t st) {
+  if (n > 0) k_tree_store_a<<<n, 256, 0, st>>>(a_rows, a, slot, seq_lens, k, emax, d_model);
+}
+void tree_finalize(const TreeState& ts, int n_cand, int n_nodes, const int* roots, const int* seq_lens,
+                   const TreeOut& out, int* status, hipStream_t st) {
+  k_tree_finalize<<<ts.batch, 512, 0, st>>>(ts, n_cand, n_nodes, roots, seq_lens, out, status);
+}
+void chain_draw(int j, int K, const float* logits, int ld, int V, float temperature, const double* lse64,
+                const int* top1, const float* uniforms, int draft_greedy, float* q_out, int* chain_tok, int batch,
+                hipStream_t st) {
+  k_draw<<<batch, 1024, 0, st>>>(logits, ld, V, (double)temperature, lse64, top1, uniforms ? uniforms + j : nullptr, K,
+                                 draft_greedy, q_out + (size_t)j * V, (size_t)K * V, chain_tok + 1 + j, K + 1);
+}
+void sample_rows(int n, const float* logits, int V, float temperature, const double* lse64, const int* top1,
+                 const float* uniforms, int* tokens, hipStream_t st) {
+  k_draw<<<n, 1024, 0, st>>>(logits, V, V, (double)temperature, lse64, top1, uniforms, 1, temperature == 0.f, nullptr,
+                             0, tokens, 1);
+}
+void chain_rows(int j, int K, const int* chain_tok, const int* seq_lens, int emax, const DraftRows& dr, int S_cap,
+                hipStream_t st) {
+  k_chain_rows<<<nblk(dr.batch, 64), 64, 0, st>>>(j, K, chain_tok, seq_lens, emax, dr, S_cap);
+}
+void chain_finalize(int K, const int* roots, const int* seq_lens, int* chain_tok, const TreeOut& out, int batch,
+                    hipStream_t st) {
+  k_chain_finalize<<<nblk((size_t)batch * (K + 1), 128), 128, 0, st>>>(K, roots, seq_lens, chain_tok, out, batch);
+}
+
+}  // namespace e3

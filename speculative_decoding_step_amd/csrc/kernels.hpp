@@ -1,0 +1,77 @@
+// Host-side launch wrappers of the EAGLE-3 step kernels (all on one hipStream_t).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace e3 {
+
+// Up to three weight matrices stacked along N (e.g. Wq;Wk;Wv).  Each is
+// [rows, K] row-major; output column of segment i starts at col0[i].
+struct GemmSegs {
+  const void* w[3];
+  int rows[3];
+  int col0[3];
+  int tiles0[4];  // prefix of 64-row N tiles per segment
+  int nseg;
+};
+
+GemmSegs make_segs(const void* w0, int r0, const void* w1 = nullptr, int r1 = 0,
+                   const void* w2 = nullptr, int r2 = 0);
+
+// out[s][m][n] (split s of the K reduction) = sum_k X[m][k] W[n][k].
+// Returns the number of splits used; out must hold splits * split_stride floats.
+// m_tile is 16 or 64 (bf16 MFMA tiles); ignored for float.
+int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out,
+         size_t split_stride, int splits, int m_tile, hipStream_t st);
+// Number of K splits gemm() will actually use for a requested count.
+int gemm_splits(bool bf16, int K, int splits);
+int gemm_ntot(const GemmSegs& s);
+
+// Consumers of split partials part[s][m][ldp].
+void resid_add(float* x, const float* part, int S, size_t sstride, int M, int N, int ldp, hipStream_t st);
+void silu_mul(bool bf16, void* out, const float* part, int S, size_t sstride, int M, int F, int ldp,
+              hipStream_t st);
+void sum_store(float* out, const float* part, int S, size_t sstride, int M, int N, int ldp, hipStream_t st);
+
+// Embedding rows (T) -> fp32 residual rows; invalid token -> zeros + flag.
+void embed_rows(bool bf16, const void* table, const int* tokens, float* x, int R, int d, int V,
+                int* status, hipStream_t st);
+// out[r] = T(x[r] * rsqrt(mean(x^2)+eps) * w); if tap != null also tap[r*tap_ld] = T(x[r]).
+void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, int R, int d, float eps,
+             void* tap, int tap_ld, hipStream_t st);
+// Draft input: out[r] = [T(rms(embed[tok[r]]) * w_in) ; T(rms(x[r]) * w_hid)], [R, 2d].
+void draft_input(bool bf16, const void* embed, const int* tokens, const float* x, const void* w_in,
+                 const void* w_hid, void* out, int R, int d, int V, float eps, int* status, hipStream_t st);
+
+// Row metadata of one forward pass.
+struct RowMeta {
+  int* seq;        // cache slot (sequence) of the row, -1 = padding row
+  int* pos;        // RoPE position
+  int* slot;       // KV slot this row writes
+  int* lim;        // keys [0, lim) visible
+  int* tail0;      // first slot addressed by mask bit 0
+  uint64_t* mask;  // extra visible slots tail0 + j for set bits j
+};
+
+// Rotary embedding + KV write from the QKV partials [S][R][(Hq+2Hkv)*hd].
+void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const RowMeta& rm,
+             void* q_out, void* kc, void* vc, size_t seq_stride, size_t head_stride, int Hq, int Hkv,
+             int hd, float theta, hipStream_t st);
+
+// Attention of rows over their visible keys, split over key chunks, then combined.
+void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride,
+               size_t head_stride, const RowMeta& rm, int R, int Hq, int Hkv, int hd, int key_bound,
+               float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st);
+
+// Row-wise top-k + log-sum-exp over fp32 logits [R, ld] (first V columns).
+// z = logits / temperature (in double); ids/vals are of the raw logits.
+void topk_lse(const float* logits, int R, int V, int ld, int K, float temperature, float* pv, int* pi,
+              float* pmax, double* psum, int* out_ids, float* out_vals, float* lse32, double* lse64,
+              hipStream_t st);
+int topk_slices(int V);
+
+// Gather rows: dst[i] = src[idx[i]] (fp32 rows of d) with idx < 0 -> zeros.
+void gather_rows_f32(float* dst, const float* src, const int* idx, int n, int d, hipStream_t st);
+
+}  // namespace e3

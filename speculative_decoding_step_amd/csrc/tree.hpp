@@ -1,0 +1,76 @@
+// Device-side state of the draft tree builder and its launch wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace e3 {
+
+constexpr int TREE_CMAX = 1024;  // candidates per sequence: k + (D-1) k^2
+
+struct TreeState {
+  int batch, topk, cmax, emax;  // cmax: candidate capacity, emax = (D-1) k expansion rows
+  int* tok;                     // [B][cmax] candidate token
+  int* par;                     // [B][cmax] parent's creation index, -1 = root
+  int* dep;                     // [B][cmax] depth (root's children: 1)
+  float* score;                 // [B][cmax] cumulative draft log-prob
+  int* erow;                    // [B][cmax] expansion row of the candidate, -1 if not expanded
+  int* front;                   // [B][k] frontier (creation indices, rank order)
+  uint64_t* emask;              // [B][emax] draft tail mask of each expansion row
+};
+
+// Inputs of the draft rows of one expansion (or chain) pass.
+struct DraftRows {
+  int batch;
+  int* tok;        // [rows] token whose embedding forms e
+  int* src;        // [rows] where x comes from: >= 0 row of a_rows, -1-b the catch-up row of b
+  int* seq;        // RowMeta fields, see kernels.hpp
+  int* pos;
+  int* slot;
+  int* lim;
+  int* tail0;
+  uint64_t* mask;
+};
+
+struct TreeOut {
+  int* tokens;
+  int* parents;
+  int* depth;
+  int* pos;
+  uint64_t* mask;
+  float* score;
+};
+
+void tree_children(const TreeState& ts, int depth_new, const int* ids, const float* vals, const float* lse, int kk,
+                   hipStream_t st);
+void tree_frontier(const TreeState& ts, int d, const int* seq_lens, const DraftRows& dr, int S_cap, int* status,
+                   hipStream_t st);
+void tree_gather_x(float* x, const int* src, const float* a_rows, const float* a_last, int n, int d_model,
+                   hipStream_t st);
+void tree_store_a(float* a_rows, const float* a, const int* slot, const int* seq_lens, int n, int k, int emax,
+                  int d_model, hipStream_t st);
+void tree_finalize(const TreeState& ts, int n_cand, int n_nodes, const int* roots, const int* seq_lens,
+                   const TreeOut& out, int* status, hipStream_t st);
+void chain_draw(int j, int K, const float* logits, int ld, int V, float temperature, const double* lse64,
+                const int* top1, const float* uniforms, int draft_greedy, float* q_out, int* chain_tok, int batch,
+                hipStream_t st);
+void sample_rows(int n, const float* logits, int V, float temperature, const double* lse64, const int* top1,
+                 const float* uniforms, int* tokens, hipStream_t st);
+void chain_rows(int j, int K, const int* chain_tok, const int* seq_lens, int emax, const DraftRows& dr, int S_cap,
+                hipStream_t st);
+void chain_finalize(int K, const int* roots, const int* seq_lens, int* chain_tok, const TreeOut& out, int batch,
+                    hipStream_t st);
+
+// ------------------------------------------------------------ accept/compact
+void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const int* parents, const int* argmax,
+                   int* path, int* path_len, int* next_root, int* emitted, int* status, hipStream_t st);
+void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,
+                  float temperature, const float* q, const float* uniforms, int* path, int* path_len,
+                  int* next_root, int* emitted, hipStream_t st);
+void compact_kv(bool bf16, int batch, const int* seq_lens, const int* path, const int* path_len, int maxp,
+                int n_rows, void* kv, int n_layers, int max_batch, int Hkv, int S_cap, int hd, int* status, hipStream_t st);
+void compact_finish(bool bf16, int batch, int* seq_lens, int n_rows, int maxp, const int* path, const int* path_len,
+                    const int* tokens, const int* next_root, const void* aux_tree, int aux_w, void* aux_new,
+                    int* next_tok, int* new_len, hipStream_t st);
+
+}  // namespace e3

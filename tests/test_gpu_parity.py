@@ -1,0 +1,351 @@
+"""GPU parity of each C-ABI call against the oracle on the same seeded inputs.
+
+Integer and index work (trees, masks, paths, samples, compaction) must match
+bit for bit given equal float inputs; logits within 2e-2 absolute (bf16) or
+1e-4 relative (fp32); argmax wherever the oracle's top-2 margin exceeds that.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (kv_view, logits_close, make_engine, margin_tol, oracle_weights, random_tree, to_dev,
+                      toy_shape, top2_margin)
+from oracle.accept import chain_rejection, greedy_walk
+from oracle.llama import KVCache, causal_visible, target_forward
+from oracle.numerics import probs_f32, sample_inverse_cdf
+from oracle.step import build_sampled_chain
+from oracle.tree import mask_words, tree_from_table, tree_mask
+from speculative_decoding_step_amd import binding as B
+from speculative_decoding_step_amd import synth
+from speculative_decoding_step_amd.engine import Spec
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _status_clear(eng):
+    assert eng.device_status() == 0
+
+
+# ------------------------------------------------------------------ verify_tree
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_verify_prefill_and_tree_vs_oracle(dtype):
+    print(f"\n[verify parity {dtype}]", flush=True)
+    ms = toy_shape(dtype=dtype, vocab=1000)
+    spec = Spec("greedy_tree", 4, 3, 12)
+    eng = make_engine(ms, spec, max_seq=160, sigma=0.05, prefill_chunk=24)
+    shp, W, H = oracle_weights(ms, sigma=0.05)
+    prompt = synth.tokens_np(31, "p", 50, ms.vocab)
+    eng.prefill([prompt])
+    torch.cuda.synchronize()
+    _status_clear(eng)
+    # oracle prefill
+    cache = KVCache(shp.n_layers, 160, shp.n_kv_heads, shp.head_dim)
+    lg, k, v, aux = target_forward(W, shp, cache, prompt, np.arange(50), causal_visible(50))
+    for l in range(shp.n_layers):
+        cache.k[l][:50], cache.v[l][:50] = k[l], v[l]
+    cache.length = 50
+    kvg = kv_view(eng)[:, :, 0, :, :50].float().cpu().numpy()      # [L, 2, Hkv, 50, hd]
+    for l in range(shp.n_layers):
+        err_k = np.abs(kvg[l, 0].transpose(1, 0, 2) - k[l]).max()
+        err_v = np.abs(kvg[l, 1].transpose(1, 0, 2) - v[l]).max()
+        assert err_k < (2e-2 if dtype == "bf16" else 1e-4) and err_v < (2e-2 if dtype == "bf16" else 1e-4)
+    # the prefill's last-position aux (what the catch-up consumes)
+    aux_g = eng.aux_new[0, 0].float().cpu().numpy()
+    assert np.abs(aux_g - aux[-1]).max() < (2e-2 if dtype == "bf16" else 1e-4)
+    # tree verify at P = 50
+    rng = np.random.default_rng(5)
+    n = 13
+    tokens, parents = random_tree(rng, n, ms.vocab)
+    dep = [0] * n
+    for i in range(1, n):
+        dep[i] = dep[parents[i]] + 1
+    m = tree_mask(parents)
+    ref, rk, rv, raux = target_forward(W, shp, cache, tokens, 50 + np.array(dep),
+                                       [list(np.nonzero(m[i])[0]) for i in range(n)])
+    seq_lens = to_dev([50])
+    logits = torch.zeros(n, ms.vocab, dtype=torch.float32, device="cuda")
+    am = torch.zeros(n, dtype=torch.int32, device="cuda")
+    mg = torch.zeros(n, dtype=torch.float32, device="cuda")
+    auxo = torch.zeros(n, 3 * ms.d, dtype=eng.tdt, device="cuda")
+    mw = torch.as_tensor(mask_words(parents).view(np.int64), device="cuda")
+    B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq_lens), n, _p(to_dev(tokens)), _p(to_dev(50 + np.array(dep))), _p(mw),
+                         B.LM_ALL, _p(logits), _p(am), _p(mg), _p(auxo))
+    torch.cuda.synchronize()
+    _status_clear(eng)
+    g = logits.cpu().numpy()
+    err, ok = logits_close(g, ref, dtype)
+    print(f"  tree logits err {err:.3g}", flush=True)
+    assert ok
+    amg = am.cpu().numpy()
+    for i in range(n):
+        if top2_margin(ref[i]) > 2 * margin_tol(dtype, ref[i]):
+            assert amg[i] == int(np.argmax(ref[i]))
+    assert np.abs(auxo.float().cpu().numpy() - raux).max() < (2e-2 if dtype == "bf16" else 1e-4)
+    kvt = kv_view(eng)[:, :, 0, :, 50:50 + n].float().cpu().numpy()
+    for l in range(shp.n_layers):
+        assert np.abs(kvt[l, 0].transpose(1, 0, 2) - rk[l]).max() < (2e-2 if dtype == "bf16" else 1e-4)
+    eng.close()
+
+
+# ------------------------------------------------------------- tree from logits
+def _tree_engine(D, k, N, V, mode="greedy_tree", T=0.0, batch=1, draft_greedy=False):
+    ms = toy_shape(dtype="bf16", vocab=V, layers=1, d=256, heads=4, kv=4, hd=64, ffn=256, taps=(0, 0, 0))
+    return make_engine(ms, Spec(mode, D, k, N, T, draft_greedy), batch=batch, max_seq=128)
+
+
+def _run_tree_from_logits(eng, roots, table, uniforms=None):
+    Bn = len(roots)
+    R = eng.rows
+    outs = dict(tokens=torch.zeros(Bn, R, dtype=torch.int32, device="cuda"),
+                parents=torch.zeros(Bn, R, dtype=torch.int32, device="cuda"),
+                depth=torch.zeros(Bn, R, dtype=torch.int32, device="cuda"),
+                pos=torch.zeros(Bn, R, dtype=torch.int32, device="cuda"),
+                mask=torch.zeros(Bn, R, dtype=torch.int64, device="cuda"),
+                score=torch.zeros(Bn, R, dtype=torch.float32, device="cuda"))
+    q = torch.zeros(Bn, eng.spec.depth, eng.ms.vocab, dtype=torch.float32, device="cuda") if eng.sampling else None
+    seq_lens = to_dev([40 + b for b in range(Bn)])
+    tab = torch.as_tensor(np.ascontiguousarray(table, dtype=np.float32), device="cuda")
+    u = None if uniforms is None else torch.as_tensor(uniforms, device="cuda")
+    B.eagle3_tree_from_logits(eng.ctx, Bn, _p(to_dev(roots)), _p(seq_lens), _p(tab), _p(u), _p(outs["tokens"]),
+                              _p(outs["parents"]), _p(outs["depth"]), _p(outs["pos"]), _p(outs["mask"]),
+                              _p(outs["score"]), _p(q))
+    torch.cuda.synchronize()
+    _status_clear(eng)
+    res = {k: v.cpu().numpy() for k, v in outs.items()}
+    if q is not None:
+        res["q"] = q.cpu().numpy()
+    return res
+
+
+def test_tree_from_logits_hand_worked_golden():
+    g = json.load(open(os.path.join(GOLDEN, "dynamic_tree_hand.json")))
+    table = np.log(np.array(g["probs"], dtype=np.float64)).astype(np.float32)
+    for n, exp in g["expect"].items():
+        eng = _tree_engine(g["depth"], g["topk"], int(n), table.shape[1])
+        r = _run_tree_from_logits(eng, [g["root"]], table[None])
+        assert list(r["tokens"][0]) == exp["tokens"]
+        assert list(r["parents"][0]) == exp["parents"]
+        assert list(r["depth"][0]) == exp["depth"]
+        assert list(r["pos"][0]) == [40 + x for x in exp["depth"]]
+        assert [int(x) for x in r["mask"][0].view(np.uint64)] == [int(x) for x in mask_words(exp["parents"])]
+        eng.close()
+
+
+@pytest.mark.parametrize("D,k,N,V,Bn", [(6, 4, 32, 32000, 2), (6, 10, 60, 128256, 1), (4, 4, 16, 5000, 3),
+                                        (4, 1, 4, 1024, 2), (3, 2, 5, 7, 4)])
+def test_tree_from_logits_matches_oracle(D, k, N, V, Bn):
+    print(f"\n[tree D{D} k{k} N{N} V{V} B{Bn}]", flush=True)
+    rng = np.random.default_rng(D * 1000 + k * 100 + N)
+    E = (D - 1) * k
+    table = rng.normal(0, 3, size=(Bn, 1 + E, V)).astype(np.float32)
+    if V > 64:  # plant exact ties in logits to exercise the tie rules
+        table[:, :, 7] = table[:, :, 3]
+    roots = list(rng.integers(0, V, Bn))
+    eng = _tree_engine(D, k, N, V, batch=Bn)
+    r = _run_tree_from_logits(eng, roots, table)
+    for b in range(Bn):
+        t = tree_from_table(int(roots[b]), table[b], D, k, N)
+        assert list(r["tokens"][b]) == t.tokens
+        assert list(r["parents"][b]) == t.parents
+        assert list(r["depth"][b]) == t.depth
+        assert list(r["pos"][b]) == [40 + b + x for x in t.depth]
+        assert np.array_equal(r["score"][b], np.array(t.score, dtype=np.float32))
+        assert [int(x) for x in r["mask"][b].view(np.uint64)] == [int(x) for x in mask_words(t.parents)]
+    eng.close()
+
+
+@pytest.mark.parametrize("greedy", [False, True])
+def test_sampled_chain_from_logits_matches_oracle(greedy):
+    K, V, Bn, T = 5, 3000, 4, 1.0
+    rng = np.random.default_rng(17)
+    table = rng.normal(0, 2, size=(Bn, K, V)).astype(np.float32)
+    u = synth.uniform24_np(5, "ud", Bn * K).reshape(Bn, K)
+    roots = list(rng.integers(0, V, Bn))
+    eng = _tree_engine(K, 1, K, V, mode="sample_chain", T=T, batch=Bn, draft_greedy=greedy)
+    r = _run_tree_from_logits(eng, roots, table, None if greedy else u)
+    for b in range(Bn):
+        cnt = [0]
+
+        def expand(d, info):
+            cnt[0] += 1
+            return [table[b, cnt[0]]]
+
+        toks, q = build_sampled_chain(int(roots[b]), table[b, 0], expand, K, T, u[b], greedy)
+        assert list(r["tokens"][b]) == toks
+        assert list(r["parents"][b]) == [-1, 0, 1, 2, 3, 4]
+        np.testing.assert_allclose(r["q"][b], q, rtol=2e-7, atol=0)
+    eng.close()
+
+
+# ------------------------------------------------------------------ accept
+def test_accept_greedy_matches_walk():
+    rng = np.random.default_rng(3)
+    D, k, N, V, Bn = 6, 4, 32, 50, 8
+    eng = _tree_engine(D, k, N, V, batch=Bn)
+    n = N + 1
+    toks, pars, am = [], [], []
+    for b in range(Bn):
+        # a planted branch: argmax follows it for a random length
+        t, p = random_tree(rng, n, V)
+        a = [int(x) for x in rng.integers(0, V, n)]
+        node = 0
+        for _ in range(int(rng.integers(0, D + 1))):
+            kids = [c for c in range(n) if p[c] == node]
+            if not kids:
+                break
+            c = kids[int(rng.integers(len(kids)))]
+            a[node] = t[c]
+            node = c
+        toks.append(t)
+        pars.append(p)
+        am.append(a)
+    maxp = D + 1
+    path = torch.zeros(Bn, maxp, dtype=torch.int32, device="cuda")
+    plen = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    nxt = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    em = torch.zeros(Bn, maxp, dtype=torch.int32, device="cuda")
+    B.eagle3_accept(eng.ctx, Bn, n, _p(to_dev(toks)), _p(to_dev(pars)), _p(to_dev(am)), None, None, None, _p(path),
+                    _p(plen), _p(nxt), _p(em))
+    torch.cuda.synchronize()
+    for b in range(Bn):
+        ref_path, ref_next = greedy_walk(toks[b], pars[b], am[b])
+        assert plen[b].item() == len(ref_path)
+        assert list(path[b].cpu().numpy()) == ref_path + [-1] * (maxp - len(ref_path))
+        assert nxt[b].item() == ref_next
+        assert list(em[b].cpu().numpy()[:len(ref_path)]) == [toks[b][i] for i in ref_path]
+    _status_clear(eng)
+    eng.close()
+
+
+def _chain_inputs(rng, Bn, K, V, T):
+    logits = rng.normal(0, 1.5, size=(Bn, K + 1, V)).astype(np.float32)
+    qlog = (logits[:, :K] + rng.normal(0, 1.0, size=(Bn, K, V))).astype(np.float32)
+    q = np.stack([[probs_f32(qlog[b, i], T) for i in range(K)] for b in range(Bn)])
+    u_d = rng.integers(0, 1 << 24, size=(Bn, K)) * 2.0 ** -24
+    drafts = np.array([[sample_inverse_cdf(q[b, i], np.float32(u_d[b, i])) for i in range(K)] for b in range(Bn)])
+    return logits, q, drafts
+
+
+def test_accept_chain_matches_oracle():
+    rng = np.random.default_rng(4)
+    K, V, Bn, T = 5, 4000, 16, 1.0
+    eng = _tree_engine(K, 1, K, V, mode="sample_chain", T=T, batch=Bn)
+    logits, q, drafts = _chain_inputs(rng, Bn, K, V, T)
+    u = (rng.integers(0, 1 << 24, size=(Bn, K + 1)) * 2.0 ** -24).astype(np.float32)
+    u[:, :K] *= 0.3  # bias toward accepting so several drafts pass
+    toks = np.concatenate([rng.integers(0, V, (Bn, 1)), drafts], axis=1)
+    path = torch.zeros(Bn, K + 1, dtype=torch.int32, device="cuda")
+    plen = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    nxt = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    em = torch.zeros(Bn, K + 1, dtype=torch.int32, device="cuda")
+    B.eagle3_accept(eng.ctx, Bn, K + 1, _p(to_dev(toks)), None, None, _p(to_dev(logits, torch.float32)),
+                    _p(to_dev(q, torch.float32)), _p(to_dev(u, torch.float32)), _p(path), _p(plen), _p(nxt), _p(em))
+    torch.cuda.synchronize()
+    seen = set()
+    for b in range(Bn):
+        p = np.stack([probs_f32(logits[b, i], T) for i in range(K + 1)])
+        n_acc, tok = chain_rejection(toks[b, 1:], q[b], p, u[b])
+        seen.add(n_acc)
+        assert plen[b].item() == n_acc + 1
+        assert nxt[b].item() == tok
+        assert list(em[b].cpu().numpy()) == [int(x) for x in toks[b, :n_acc + 1]] + [-1] * (K - n_acc)
+    assert len(seen) >= 2
+    eng.close()
+
+
+def test_sample_rows_match_oracle():
+    rng = np.random.default_rng(6)
+    V, n = 32000, 24
+    eng = _tree_engine(2, 2, 3, V, batch=1)
+    logits = rng.normal(0, 2, size=(n, V)).astype(np.float32)
+    u = (rng.integers(0, 1 << 24, size=n) * 2.0 ** -24).astype(np.float32)
+    out = torch.zeros(n, dtype=torch.int32, device="cuda")
+    for T in (1.0, 0.7, 0.0):
+        B.eagle3_sample(eng.ctx, n, _p(to_dev(logits, torch.float32)), T, _p(to_dev(u, torch.float32)), _p(out))
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for i in range(n):
+            ref = int(np.argmax(logits[i])) if T == 0 else sample_inverse_cdf(probs_f32(logits[i], T), u[i])
+            assert got[i] == ref
+    eng.close()
+
+
+# ------------------------------------------------------------------ compaction
+def test_compact_kv_moves_path_rows():
+    rng = np.random.default_rng(8)
+    D, k, N, V, Bn = 6, 4, 32, 300, 3
+    eng = _tree_engine(D, k, N, V, batch=Bn)
+    kv = kv_view(eng)
+    kv.copy_(torch.randn(kv.shape, device="cuda").to(eng.tdt))
+    before = kv.clone()
+    n = N + 1
+    P = [17, 40, 3]
+    maxp = D + 1
+    paths, lens, toks = [], [], []
+    for b in range(Bn):
+        t, par = random_tree(rng, n, V)
+        # a root-to-node path of random length
+        node, pth = 0, [0]
+        for _ in range(int(rng.integers(0, D + 1))):
+            kids = [c for c in range(n) if par[c] == node]
+            if not kids:
+                break
+            node = kids[int(rng.integers(len(kids)))]
+            pth.append(node)
+        paths.append(pth + [-1] * (maxp - len(pth)))
+        lens.append(len(pth))
+        toks.append(t)
+    seq = to_dev(P)
+    nroot = to_dev(rng.integers(0, V, Bn))
+    aux_tree = torch.randn(Bn, n, 3 * eng.ms.d, device="cuda").to(eng.tdt)
+    aux_new = torch.zeros(Bn, maxp, 3 * eng.ms.d, device="cuda").to(eng.tdt)
+    ntok = torch.zeros(Bn, maxp, dtype=torch.int32, device="cuda")
+    nlen = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    B.eagle3_compact_kv(eng.ctx, Bn, _p(seq), n, _p(to_dev(paths)), _p(to_dev(lens)), _p(to_dev(toks)), _p(nroot),
+                        _p(aux_tree), _p(aux_new), _p(ntok), _p(nlen))
+    torch.cuda.synchronize()
+    _status_clear(eng)
+    after = kv
+    for b in range(Bn):
+        L = lens[b]
+        for j in range(L):
+            assert torch.equal(after[:, :, b, :, P[b] + j], before[:, :, b, :, P[b] + paths[b][j]])
+        assert torch.equal(after[:, :, b, :, :P[b]], before[:, :, b, :, :P[b]])
+        assert seq[b].item() == P[b] + L and nlen[b].item() == L
+        for j in range(L):
+            assert torch.equal(aux_new[b, j], aux_tree[b, paths[b][j]])
+        want = [toks[b][paths[b][j + 1]] for j in range(L - 1)] + [int(nroot[b].item())]
+        assert list(ntok[b].cpu().numpy()[:L]) == want
+    eng.close()
+
+
+def test_device_status_flags_bad_inputs():
+    """Capacity overflow and a malformed path raise device flags; nothing faults."""
+    D, k, N, V = 4, 2, 6, 100
+    eng = _tree_engine(D, k, N, V, batch=1)
+    n = N + 1
+    seq = to_dev([eng.max_seq - 2])            # no room for 7 tree rows
+    toks = to_dev(np.arange(n)[None])
+    logits = torch.zeros(n, V, device="cuda")
+    B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq), n, _p(toks), None, _p(torch.zeros(1, n, dtype=torch.int64,
+                                                                                  device="cuda")),
+                         B.LM_ALL, _p(logits), None, None, None)
+    assert eng.device_status() & B.DEV_KV_OVERFLOW
+    bad_path = to_dev([[0, 3, 2, -1, -1]])     # not increasing
+    aux = torch.zeros(1, n, 3 * eng.ms.d, device="cuda").to(eng.tdt)
+    B.eagle3_compact_kv(eng.ctx, 1, _p(to_dev([5])), n, _p(bad_path), _p(to_dev([3])), _p(toks), _p(to_dev([1])),
+                        _p(aux), _p(torch.zeros(1, D + 1, 3 * eng.ms.d, device="cuda").to(eng.tdt)),
+                        _p(torch.zeros(1, D + 1, dtype=torch.int32, device="cuda")),
+                        _p(torch.zeros(1, dtype=torch.int32, device="cuda")))
+    assert eng.device_status() & B.DEV_BAD_PATH
+    with pytest.raises(B.Eagle3Error):
+        B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq), 65, _p(toks), None, _p(toks), B.LM_ALL, None, None, None, None)
+    eng.close()
