@@ -76,7 +76,8 @@ def test_verify_prefill_and_tree_vs_oracle(dtype):
     mg = torch.zeros(n, dtype=torch.float32, device="cuda")
     auxo = torch.zeros(n, 3 * ms.d, dtype=eng.tdt, device="cuda")
     mw = torch.as_tensor(mask_words(parents).view(np.int64), device="cuda")
-    B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq_lens), n, _p(to_dev(tokens)), _p(to_dev(50 + np.array(dep))), _p(mw),
+    tok_d, pos_d = to_dev(tokens), to_dev(50 + np.array(dep))
+    B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq_lens), n, _p(tok_d), _p(pos_d), _p(mw),
                          B.LM_ALL, _p(logits), _p(am), _p(mg), _p(auxo))
     torch.cuda.synchronize()
     _status_clear(eng)
@@ -114,7 +115,8 @@ def _run_tree_from_logits(eng, roots, table, uniforms=None):
     seq_lens = to_dev([40 + b for b in range(Bn)])
     tab = torch.as_tensor(np.ascontiguousarray(table, dtype=np.float32), device="cuda")
     u = None if uniforms is None else torch.as_tensor(uniforms, device="cuda")
-    B.eagle3_tree_from_logits(eng.ctx, Bn, _p(to_dev(roots)), _p(seq_lens), _p(tab), _p(u), _p(outs["tokens"]),
+    roots_d = to_dev(roots)
+    B.eagle3_tree_from_logits(eng.ctx, Bn, _p(roots_d), _p(seq_lens), _p(tab), _p(u), _p(outs["tokens"]),
                               _p(outs["parents"]), _p(outs["depth"]), _p(outs["pos"]), _p(outs["mask"]),
                               _p(outs["score"]), _p(q))
     torch.cuda.synchronize()
@@ -212,7 +214,8 @@ def test_accept_greedy_matches_walk():
     plen = torch.zeros(Bn, dtype=torch.int32, device="cuda")
     nxt = torch.zeros(Bn, dtype=torch.int32, device="cuda")
     em = torch.zeros(Bn, maxp, dtype=torch.int32, device="cuda")
-    B.eagle3_accept(eng.ctx, Bn, n, _p(to_dev(toks)), _p(to_dev(pars)), _p(to_dev(am)), None, None, None, _p(path),
+    keep = [to_dev(toks), to_dev(pars), to_dev(am)]
+    B.eagle3_accept(eng.ctx, Bn, n, _p(keep[0]), _p(keep[1]), _p(keep[2]), None, None, None, _p(path),
                     _p(plen), _p(nxt), _p(em))
     torch.cuda.synchronize()
     for b in range(Bn):
@@ -246,8 +249,9 @@ def test_accept_chain_matches_oracle():
     plen = torch.zeros(Bn, dtype=torch.int32, device="cuda")
     nxt = torch.zeros(Bn, dtype=torch.int32, device="cuda")
     em = torch.zeros(Bn, K + 1, dtype=torch.int32, device="cuda")
-    B.eagle3_accept(eng.ctx, Bn, K + 1, _p(to_dev(toks)), None, None, _p(to_dev(logits, torch.float32)),
-                    _p(to_dev(q, torch.float32)), _p(to_dev(u, torch.float32)), _p(path), _p(plen), _p(nxt), _p(em))
+    keep = [to_dev(toks), to_dev(logits, torch.float32), to_dev(q, torch.float32), to_dev(u, torch.float32)]
+    B.eagle3_accept(eng.ctx, Bn, K + 1, _p(keep[0]), None, None, _p(keep[1]), _p(keep[2]), _p(keep[3]), _p(path),
+                    _p(plen), _p(nxt), _p(em))
     torch.cuda.synchronize()
     seen = set()
     for b in range(Bn):
@@ -268,8 +272,9 @@ def test_sample_rows_match_oracle():
     logits = rng.normal(0, 2, size=(n, V)).astype(np.float32)
     u = (rng.integers(0, 1 << 24, size=n) * 2.0 ** -24).astype(np.float32)
     out = torch.zeros(n, dtype=torch.int32, device="cuda")
+    lg_d, u_d = to_dev(logits, torch.float32), to_dev(u, torch.float32)
     for T in (1.0, 0.7, 0.0):
-        B.eagle3_sample(eng.ctx, n, _p(to_dev(logits, torch.float32)), T, _p(to_dev(u, torch.float32)), _p(out))
+        B.eagle3_sample(eng.ctx, n, _p(lg_d), T, _p(u_d), _p(out))
         torch.cuda.synchronize()
         got = out.cpu().numpy()
         for i in range(n):
@@ -309,7 +314,8 @@ def test_compact_kv_moves_path_rows():
     aux_new = torch.zeros(Bn, maxp, 3 * eng.ms.d, device="cuda").to(eng.tdt)
     ntok = torch.zeros(Bn, maxp, dtype=torch.int32, device="cuda")
     nlen = torch.zeros(Bn, dtype=torch.int32, device="cuda")
-    B.eagle3_compact_kv(eng.ctx, Bn, _p(seq), n, _p(to_dev(paths)), _p(to_dev(lens)), _p(to_dev(toks)), _p(nroot),
+    keep = [to_dev(paths), to_dev(lens), to_dev(toks)]
+    B.eagle3_compact_kv(eng.ctx, Bn, _p(seq), n, _p(keep[0]), _p(keep[1]), _p(keep[2]), _p(nroot),
                         _p(aux_tree), _p(aux_new), _p(ntok), _p(nlen))
     torch.cuda.synchronize()
     _status_clear(eng)
@@ -335,16 +341,15 @@ def test_device_status_flags_bad_inputs():
     seq = to_dev([eng.max_seq - 2])            # no room for 7 tree rows
     toks = to_dev(np.arange(n)[None])
     logits = torch.zeros(n, V, device="cuda")
-    B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq), n, _p(toks), None, _p(torch.zeros(1, n, dtype=torch.int64,
-                                                                                  device="cuda")),
-                         B.LM_ALL, _p(logits), None, None, None)
+    zmask = torch.zeros(1, n, dtype=torch.int64, device="cuda")
+    B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq), n, _p(toks), None, _p(zmask), B.LM_ALL, _p(logits), None, None, None)
     assert eng.device_status() & B.DEV_KV_OVERFLOW
     bad_path = to_dev([[0, 3, 2, -1, -1]])     # not increasing
     aux = torch.zeros(1, n, 3 * eng.ms.d, device="cuda").to(eng.tdt)
-    B.eagle3_compact_kv(eng.ctx, 1, _p(to_dev([5])), n, _p(bad_path), _p(to_dev([3])), _p(toks), _p(to_dev([1])),
-                        _p(aux), _p(torch.zeros(1, D + 1, 3 * eng.ms.d, device="cuda").to(eng.tdt)),
-                        _p(torch.zeros(1, D + 1, dtype=torch.int32, device="cuda")),
-                        _p(torch.zeros(1, dtype=torch.int32, device="cuda")))
+    keep = [to_dev([5]), to_dev([3]), to_dev([1]), torch.zeros(1, D + 1, 3 * eng.ms.d, device="cuda").to(eng.tdt),
+            torch.zeros(1, D + 1, dtype=torch.int32, device="cuda"), torch.zeros(1, dtype=torch.int32, device="cuda")]
+    B.eagle3_compact_kv(eng.ctx, 1, _p(keep[0]), n, _p(bad_path), _p(keep[1]), _p(toks), _p(keep[2]),
+                        _p(aux), _p(keep[3]), _p(keep[4]), _p(keep[5]))
     assert eng.device_status() & B.DEV_BAD_PATH
     with pytest.raises(B.Eagle3Error):
         B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq), 65, _p(toks), None, _p(toks), B.LM_ALL, None, None, None, None)
