@@ -26,7 +26,10 @@ def max_seq_for(w, steps):
     return w.prompt_len + (steps + 2) * (w.depth + 1) + w.rows + (w.depth - 1) * w.topk + 64
 
 
-def run_gpu(w, steps, warmup, prof_out=None):
+def run_gpu(w, steps, warmup):
+    """Timed region: `steps` replays of the captured step graph (after `warmup`
+    replays).  Then `steps` eager steps with a HIP event pair around every GEMM
+    and attention launch on the library's stream give per-kernel durations."""
     import torch
 
     from speculative_decoding_step_amd import binding as B
@@ -35,32 +38,68 @@ def run_gpu(w, steps, warmup, prof_out=None):
 
     t0 = time.time()
     prompts = [p for p in configs.prompts_np(w)]
-    eng = Engine(w.shape, Spec.of(w), w.batch, max_seq_for(w, steps + warmup), w.target_seed, w.head_seed,
+    eng = Engine(w.shape, Spec.of(w), w.batch, max_seq_for(w, 2 * (steps + warmup)), w.target_seed, w.head_seed,
                  prefill_chunk=512)
     print(f"[bench] weights + context ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     eng.prefill(prompts)
     torch.cuda.synchronize()
     print(f"[bench] prefill done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    eng.step()                                   # one eager step, then capture
+    eng.capture()
     for _ in range(warmup):
-        eng.step()
+        eng.replay()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done", file=sys.stderr, flush=True)
-    # timed region: exactly `steps` steps, HIP events on the library stream per kernel
+    print("[bench] graph captured, warmup done", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eng.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    print(f"[bench] timed {steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
     B.eagle3_profile(eng.ctx, True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         eng.step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / steps
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
     prof = {k: B.eagle3_profile_read(eng.ctx, k) for k in (B.PROF_GEMM_M64, B.PROF_GEMM_M16, B.PROF_ATTN)}
     B.eagle3_profile(eng.ctx, False)
     status = eng.device_status()
     if status:
         raise RuntimeError(f"device status flags {status:#x}")
     eng.close()
-    return ms, prof
+    return ms, eager_ms, prof
+
+
+def _slice_weights(w, n_layers):
+    """float64 weights of the first n_layers target layers plus the head, seeded as
+    on the GPU.  The torch twin of the seeded generator (integer-only, so its
+    values equal the numpy generator's bit for bit) runs on the GPU when there
+    is one, and the values are copied to host memory."""
+    import numpy as np
+    import torch
+
+    from speculative_decoding_step_amd import configs, synth
+
+    ms = w.shape
+    sms = configs.ModelShape(n_layers, ms.d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, ms.vocab,
+                             ms.rope_theta, (0, 0, n_layers - 1), ms.dtype)
+
+    def gen(seed, name, shape, kind):
+        if kind == "norm":
+            return np.ones(shape)
+        dev = "cuda" if torch.cuda.is_available() else "cpu"
+        return synth.normal_t(seed, name, shape, dev, 0.02, ms.dtype, chunk=1 << 25).cpu().to(torch.float64).numpy()
+
+    W = {"layers": [dict() for _ in range(n_layers)]}
+    for name, shape, kind in configs.target_tensor_specs(sms):
+        if name[0] == "l" and name[1].isdigit():
+            l, key = name[1:].split(".", 1)
+            W["layers"][int(l)][key] = gen(w.target_seed, name, shape, kind)
+        else:
+            W[name] = gen(w.target_seed, name, shape, kind)
+    H = {name[2:]: gen(w.head_seed, name, shape, kind) for name, shape, kind in configs.head_tensor_specs(sms)}
+    return sms, W, H
 
 
 def cpu_baseline(w):
@@ -78,10 +117,13 @@ def cpu_baseline(w):
     from oracle.llama import KVCache, Shape, target_forward
     from oracle.step import OracleSequence, SpecConfig
     from oracle.tree import tree_mask
-    from speculative_decoding_step_amd import configs, synth
+    from speculative_decoding_step_amd import synth
 
     ms = w.shape
     cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    t_gen = time.time()
+    sms, W, H = _slice_weights(w, 2)
+    t_gen = time.time() - t_gen
     rng = np.random.default_rng(0)
     P, n = w.prompt_len, w.rows
     parents = [-1] + [int(rng.integers(0, i)) for i in range(1, n)]
@@ -91,37 +133,33 @@ def cpu_baseline(w):
     m = tree_mask(parents)
     vis = [list(np.nonzero(m[i])[0]) for i in range(n)]
     toks = synth.tokens_np(1, "cpu_tree", n, ms.vocab)
+    cache = KVCache(2, P + 1, ms.n_kv_heads, ms.head_dim)
+    for l in range(2):
+        cache.k[l][:P] = synth.normal_np(7, f"k{l}", (P, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
+        cache.v[l][:P] = synth.normal_np(7, f"v{l}", (P, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
+    cache.length = P
     times = {}
     for L in (1, 2):
-        sms = configs.ModelShape(L, ms.d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, ms.vocab, ms.rope_theta,
-                                 (0, 0, min(1, L - 1)), ms.dtype)
-        W, H = configs.weights_np(sms, w.target_seed, w.head_seed)
         shp = Shape(L, ms.d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, ms.vocab, ms.rope_theta, ms.eps,
-                    ms.dtype, sms.taps)
-        cache = KVCache(L, P + 1, ms.n_kv_heads, ms.head_dim)
-        for l in range(L):
-            cache.k[l][:P] = synth.normal_np(7, f"k{l}", (P, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
-            cache.v[l][:P] = synth.normal_np(7, f"v{l}", (P, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
-        cache.length = P
+                    ms.dtype, (0, 0, 0))
         t0 = time.perf_counter()
         target_forward(W, shp, cache, toks, P + np.array(dep), vis)
         times[L] = time.perf_counter() - t0
-        if L == 2:
-            # draft stage on the same weights, committed draft context of 32 positions
-            spec = SpecConfig(w.mode, w.depth, w.topk, w.n_nodes)
-            seq = OracleSequence(W, H, shp, spec, 32 + 2 * n + w.depth * w.topk)
-            Pd = 32
-            seq.cache.length = Pd
-            seq.dcache.k[0][:Pd - 1] = synth.normal_np(8, "dk", (Pd - 1, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
-            seq.dcache.v[0][:Pd - 1] = synth.normal_np(8, "dv", (Pd - 1, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
-            seq.dcache.length = Pd - 1
-            seq.aux_new = synth.normal_np(9, "aux", (1, 3 * ms.d), 1.0, "bf16").astype(np.float64)
-            seq.next_tok = [int(toks[0])]
-            seq.root = int(toks[0])
-            t0 = time.perf_counter()
-            seq.draft_tree()
-            times["draft"] = time.perf_counter() - t0
-        del W, H
+    shp = Shape(2, ms.d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, ms.vocab, ms.rope_theta, ms.eps,
+                ms.dtype, (0, 0, 1))
+    spec = SpecConfig(w.mode, w.depth, w.topk, w.n_nodes)
+    Pd = 32
+    seq = OracleSequence(W, H, shp, spec, Pd + 2 * n + w.depth * w.topk)
+    seq.cache.length = Pd
+    seq.dcache.k[0][:Pd - 1] = synth.normal_np(8, "dk", (Pd - 1, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
+    seq.dcache.v[0][:Pd - 1] = synth.normal_np(8, "dv", (Pd - 1, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
+    seq.dcache.length = Pd - 1
+    seq.aux_new = synth.normal_np(9, "aux", (1, 3 * ms.d), 1.0, "bf16").astype(np.float64)
+    seq.next_tok = [int(toks[0])]
+    seq.root = int(toks[0])
+    t0 = time.perf_counter()
+    seq.draft_tree()
+    times["draft"] = time.perf_counter() - t0
     t_layer = times[2] - times[1]
     t_head = max(times[1] - t_layer, 0.0)
     t_step = ms.n_layers * t_layer + t_head + times["draft"]
@@ -131,7 +169,8 @@ def cpu_baseline(w):
             "sample": (f"float64 numpy oracle, batch 1: tree verify of {n} rows over {P} committed positions on "
                        f"1- and 2-layer slices of the 8B shape ({times[1]:.1f}s, {times[2]:.1f}s) and the draft "
                        f"stage ({times['draft']:.1f}s); step = {ms.n_layers} x layer ({t_layer:.2f}s) + LM head "
-                       f"({t_head:.2f}s) + draft = {t_step:.1f}s; {work:.0f}s of CPU work")}
+                       f"({t_head:.2f}s) + draft = {t_step:.1f}s; {work:.0f}s of CPU work "
+                       f"(+{t_gen:.0f}s generating the slice's seeded weights)")}
 
 
 def main():
@@ -149,7 +188,7 @@ def main():
     from speculative_decoding_step_amd import configs
 
     w = configs.WORKLOADS[args.workload]
-    ms, prof = run_gpu(w, args.steps, args.warmup)
+    ms, eager_ms, prof = run_gpu(w, args.steps, args.warmup)
     rows = w.batch * w.rows
     n64, t64, b64, f64 = prof[0]
     achieved = b64 / (t64 / 1e3) if t64 > 0 else 0.0
@@ -161,6 +200,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "eager_ms_per_step": round(eager_ms, 4),
         "us_per_step": round(ms * 1e3, 1),
         "higher_is_better": True,
         "scaling": "weak",

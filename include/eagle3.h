@@ -230,6 +230,14 @@ eagle3_status eagle3_compact_kv(eagle3_ctx *ctx, int32_t batch, int32_t *seq_len
                                 const int32_t *next_root, const void *aux_tree,
                                 void *aux_new, int32_t *next_tok, int32_t *new_len);
 
+/* Rebind the context to another stream (a hipStream_t; NULL = null stream).
+ * Later calls launch there.  The step's calls (eagle3_draft_tree,
+ * eagle3_verify_tree, eagle3_accept, eagle3_compact_kv) make no host
+ * synchronisation, allocate nothing and keep every variable quantity in
+ * device memory, so a step can be captured into a HIP graph on a capturing
+ * stream and replayed; replays see the device state as it is at replay time. */
+eagle3_status eagle3_set_stream(eagle3_ctx *ctx, void *stream);
+
 /* One token per row from softmax(logits / temperature), drawn by the same
  * integer inverse CDF as the acceptance sampler (temperature > 0), or the
  * argmax (lowest index on ties) when temperature == 0.  logits [n, V] float,
@@ -256,7 +264,8 @@ enum {
   EAGLE3_PROF_GEMM_M64 = 0,  /* MFMA GEMM, 64-row tiles (verify, prefill)     */
   EAGLE3_PROF_GEMM_M16 = 1,  /* MFMA GEMM, 16-row tiles (draft, last-row LM)  */
   EAGLE3_PROF_ATTN = 2,      /* tree-masked attention (all modes)             */
-  EAGLE3_PROF_COUNT = 3
+  EAGLE3_PROF_GEMM_BIG = 3,  /* MFMA GEMM, 128 x 128 tiles (more than 64 rows) */
+  EAGLE3_PROF_COUNT = 4
 };
 eagle3_status eagle3_profile(eagle3_ctx *ctx, int32_t enable);
 eagle3_status eagle3_profile_read(eagle3_ctx *ctx, int32_t kernel, int64_t *launches /* host */,

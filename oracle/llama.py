@@ -136,6 +136,9 @@ def target_forward(W: dict, shp: Shape, cache: KVCache, tokens, positions, visib
         h2 = rnd(rms_norm(x, L["ffn_norm"], shp.eps))
         act = rnd(silu(h2 @ L["w_gate"].T) * (h2 @ L["w_up"].T))
         x = x + act @ L["w_down"].T
+    for ti, t in enumerate(shp.taps):       # hidden_states[L]: the last layer's output
+        if t == shp.n_layers:
+            aux[:, ti * d:(ti + 1) * d] = rnd(x)
     logits = rnd(rms_norm(x, W["final_norm"], shp.eps)) @ W["lm_head"].T
     return logits, new_k, new_v, aux
 

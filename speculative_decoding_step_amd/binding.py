@@ -16,13 +16,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeagle3.s
 F32, BF16 = 0, 1
 GREEDY_TREE, SAMPLE_CHAIN = 0, 1
 LM_ALL, LM_LAST, LM_NONE = 0, 1, 2
-PROF_GEMM_M64, PROF_GEMM_M16, PROF_ATTN = 0, 1, 2
+PROF_GEMM_M64, PROF_GEMM_M16, PROF_ATTN, PROF_GEMM_BIG = 0, 1, 2, 3
 DEV_KV_OVERFLOW, DEV_BAD_TREE, DEV_BAD_TOKEN, DEV_BAD_PATH = 1, 2, 4, 8
 
 EXPORTS = [
     "eagle3_kv_bytes", "eagle3_workspace_bytes", "eagle3_create", "eagle3_destroy", "eagle3_verify_tree",
     "eagle3_draft_prefill", "eagle3_draft_tree", "eagle3_tree_from_logits", "eagle3_accept", "eagle3_compact_kv",
-    "eagle3_sample", "eagle3_status_string", "eagle3_device_status", "eagle3_profile", "eagle3_profile_read",
+    "eagle3_sample", "eagle3_set_stream", "eagle3_status_string", "eagle3_device_status", "eagle3_profile", "eagle3_profile_read",
 ]
 
 
@@ -82,6 +82,7 @@ def lib():
             "eagle3_accept": [P, I32, I32, P, P, P, P, P, P, P, P, P, P],
             "eagle3_compact_kv": [P, I32, P, I32, P, P, P, P, P, P, P, P],
             "eagle3_sample": [P, I32, P, C.c_float, P, P],
+            "eagle3_set_stream": [P, P],
             "eagle3_device_status": [P, C.POINTER(I32)],
             "eagle3_profile": [P, I32],
             "eagle3_profile_read": [P, I32, C.POINTER(C.c_int64), C.POINTER(C.c_double), C.POINTER(C.c_double),
@@ -169,6 +170,10 @@ def eagle3_compact_kv(ctx, batch, seq_lens, n_rows, path, path_len, tokens, next
 
 def eagle3_sample(ctx, n, logits, temperature, uniforms, tokens):
     _check(lib().eagle3_sample(ctx, n, logits, temperature, uniforms, tokens), "eagle3_sample")
+
+
+def eagle3_set_stream(ctx, stream):
+    _check(lib().eagle3_set_stream(ctx, stream), "eagle3_set_stream")
 
 
 def eagle3_device_status(ctx) -> int:

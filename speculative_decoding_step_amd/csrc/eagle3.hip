@@ -56,6 +56,7 @@ struct eagle3_ctx {
   char* kv_d;
   // workspace
   int* status;
+  double* inv_freq;
   float *xres, *dx, *part;
   size_t part_elems;
   void *hbuf, *abuf, *qbuf, *gbuf;
@@ -88,6 +89,7 @@ size_t carve(eagle3_ctx* c, char* base) {
   const size_t es = c->esz;
   Carver cv{base};
   c->status = cv.take<int>(64);
+  c->inv_freq = cv.take<double>(s.head_dim / 2);
   c->xres = cv.take<float>((size_t)R * d);
   c->dx = cv.take<float>((size_t)R * d);
   const int nmax = std::max({qdim + 2 * kvdim, 2 * s.ffn, d});
@@ -304,22 +306,23 @@ int plan_splits(eagle3_ctx* c, int M, int N, int K, int m_tile) {
 // X [M, K] of T times the stacked weights; returns the number of splits in c->part.
 int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, float* out_direct = nullptr) {
   const int N = gemm_ntot(sg);
-  const int m_tile = M <= 16 ? 16 : 64;
-  const int S = out_direct ? 1 : plan_splits(c, M, N, K, m_tile);
+  const int m_tile = M <= 16 ? 16 : (M <= 64 ? 64 : 128);
+  const int S = (out_direct || m_tile == 128) ? 1 : plan_splits(c, M, N, K, m_tile);
   ProfRec rec{};
   const double bytes = (double)N * K * c->esz + (double)M * K * c->esz + (double)M * N * 4.0;
-  prof_begin(c, m_tile == 16 ? EAGLE3_PROF_GEMM_M16 : EAGLE3_PROF_GEMM_M64, bytes, 2.0 * M * N * K, &rec);
+  const int kid = m_tile == 16 ? EAGLE3_PROF_GEMM_M16 : (m_tile == 64 ? EAGLE3_PROF_GEMM_M64 : EAGLE3_PROF_GEMM_BIG);
+  prof_begin(c, kid, bytes, 2.0 * M * N * K, &rec);
   const int used = gemm(c->bf16, X, M, K, sg, out_direct ? out_direct : c->part, (size_t)M * N, S, m_tile, c->st);
   prof_end(c, &rec);
   return used;
 }
 
-void run_attention(eagle3_ctx* c, const void* kc, const void* vc, const RowMeta& rm, int R) {
+void run_attention(eagle3_ctx* c, const void* kc, const void* vc, const RowMeta& rm, int R, int rps) {
   const eagle3_shape& s = c->sh;
   ProfRec rec{};
   prof_begin(c, EAGLE3_PROF_ATTN, 0.0, 0.0, &rec);
   attention(c->bf16, c->qbuf, kc, vc, (size_t)s.n_kv_heads * c->S_cap * s.head_dim, (size_t)c->S_cap * s.head_dim, rm,
-            R, s.n_heads, s.n_kv_heads, s.head_dim, c->S_cap, c->o_part, c->ml_part, c->att_splits, c->abuf, c->st);
+            R, rps, s.n_heads, s.n_kv_heads, s.head_dim, c->S_cap, c->o_part, c->ml_part, c->att_splits, c->abuf, c->st);
   prof_end(c, &rec);
 }
 
@@ -331,7 +334,8 @@ char* kv_layer(eagle3_ctx* c, char* base, int l, int which) {
 
 // Target pass over R rows whose metadata is in c->rm and tokens in c->rtok.
 // lm: EAGLE3_LM_ALL (rows 0..R-1), LM_LAST (rows c->gidx[0..nlast)), LM_NONE.
-void target_forward(eagle3_ctx* c, int R, void* aux, int lm, int nlast, float* logits, int* argmax, float* margin) {
+void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast, float* logits, int* argmax,
+                    float* margin) {
   const eagle3_shape& s = c->sh;
   const int d = s.d_model, qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
   const bool bf = c->bf16;
@@ -351,10 +355,10 @@ void target_forward(eagle3_ctx* c, int R, void* aux, int lm, int nlast, float* l
     int S = run_gemm(c, c->hbuf, R, d, qkv);
     char* kc = kv_layer(c, c->kv_t, l, 0);
     char* vc = kv_layer(c, c->kv_t, l, 1);
-    rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, c->rm, c->qbuf, kc, vc,
+    rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, c->rm, c->inv_freq, c->qbuf, kc, vc,
             (size_t)s.n_kv_heads * c->S_cap * s.head_dim, (size_t)c->S_cap * s.head_dim, s.n_heads, s.n_kv_heads,
-            s.head_dim, s.rope_theta, st);
-    run_attention(c, kc, vc, c->rm, R);
+            s.head_dim, st);
+    run_attention(c, kc, vc, c->rm, R, rps);
     S = run_gemm(c, c->abuf, R, qdim, make_segs(L.wo, d));
     resid_add(c->xres, c->part, S, (size_t)R * d, R, d, d, st);
     rmsnorm(bf, c->xres, L.ffn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
@@ -384,7 +388,7 @@ void target_forward(eagle3_ctx* c, int R, void* aux, int lm, int nlast, float* l
 
 // The draft decoder layer over R rows: x (fp32 [R, d]) is g or a on entry and
 // a on exit; tokens in tok; row metadata rm (draft KV cache).
-void draft_layer(eagle3_ctx* c, int R, const int* tok, float* x, const RowMeta& rm) {
+void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const RowMeta& rm) {
   const eagle3_shape& s = c->sh;
   const eagle3_head_weights& H = c->hw;
   const int d = s.d_model, qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
@@ -395,10 +399,10 @@ void draft_layer(eagle3_ctx* c, int R, const int* tok, float* x, const RowMeta& 
   int S = run_gemm(c, c->hbuf, R, 2 * d, qkv);
   char* kc = kv_layer(c, c->kv_d, 0, 0);
   char* vc = kv_layer(c, c->kv_d, 0, 1);
-  rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, rm, c->qbuf, kc, vc,
+  rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, rm, c->inv_freq, c->qbuf, kc, vc,
           (size_t)s.n_kv_heads * c->S_cap * s.head_dim, (size_t)c->S_cap * s.head_dim, s.n_heads, s.n_kv_heads,
-          s.head_dim, s.rope_theta, st);
-  run_attention(c, kc, vc, rm, R);
+          s.head_dim, st);
+  run_attention(c, kc, vc, rm, R, rps);
   S = run_gemm(c, c->abuf, R, qdim, make_segs(H.wo, d));
   resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
   rmsnorm(bf, x, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
@@ -456,7 +460,7 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
                    c->tk_lse + b * k, c->tk_lse64 + b * k, st);
       } else {
         tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, n, d, st);
-        draft_layer(c, n, dr.tok, c->dx, dr_meta(c));
+        draft_layer(c, n, k, dr.tok, c->dx, dr_meta(c));
         if (dd + 1 < D) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, n, k, c->emax, d, st);
         draft_lm(c, n, c->dx, k, 1.f);
       }
@@ -480,7 +484,7 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
       } else {
         chain_rows(j - 1, K, c->chain_tok, seq_lens, c->emax, dr, c->S_cap, st);
         tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, batch, d, st);
-        draft_layer(c, batch, dr.tok, c->dx, dr_meta(c));
+        draft_layer(c, batch, 1, dr.tok, c->dx, dr_meta(c));
         if (j + 1 < K) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, batch, 1, c->emax, d, st);
         draft_lm(c, batch, c->dx, 1, T);
         chain_draw(j, K, c->logits, V, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok,
@@ -579,6 +583,18 @@ eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, c
     delete c;
     return EAGLE3_EHIP;
   }
+  {
+    // rotary inverse frequencies theta^(-2i/hd) in double
+    std::vector<double> inv(s->head_dim / 2);
+    for (int i = 0; i < s->head_dim / 2; ++i)
+      inv[i] = std::pow((double)s->rope_theta, -2.0 * (double)i / (double)s->head_dim);
+    if (hipMemcpyAsync(c->inv_freq, inv.data(), inv.size() * sizeof(double), hipMemcpyHostToDevice, c->st) !=
+            hipSuccess ||
+        hipStreamSynchronize(c->st) != hipSuccess) {
+      delete c;
+      return EAGLE3_EHIP;
+    }
+  }
   *out = c;
   return EAGLE3_OK;
 }
@@ -601,7 +617,7 @@ eagle3_status eagle3_verify_tree(eagle3_ctx* c, int32_t seq_begin, int32_t batch
   const int R = batch * n_rows;
   k_verify_meta<<<nb(R, 128), 128, 0, c->st>>>(batch, seq_begin, n_rows, seq_lens, tokens, pos, mask, c->S_cap, c->rm,
                                                 c->rtok, c->gidx, c->status);
-  target_forward(c, R, aux, lm_mode, batch, logits, argmax, margin);
+  target_forward(c, R, n_rows, aux, lm_mode, batch, logits, argmax, margin);
   return last_error();
 }
 
@@ -615,7 +631,7 @@ eagle3_status eagle3_draft_prefill(eagle3_ctx* c, int32_t seq_begin, int32_t bat
                                                  c->status);
   int S = run_gemm(c, aux, R, 3 * d, make_segs(c->hw.fc, d));
   sum_store(c->dx, c->part, S, (size_t)R * d, R, d, d, c->st);
-  draft_layer(c, R, c->rtok, c->dx, c->rm);
+  draft_layer(c, R, n_rows, c->rtok, c->dx, c->rm);
   return last_error();
 }
 
@@ -636,7 +652,7 @@ eagle3_status eagle3_draft_tree(eagle3_ctx* c, int32_t batch, const int32_t* seq
                                                c->gidx, c->roots, c->status);
   int S = run_gemm(c, aux_new, Rc, 3 * d, make_segs(c->hw.fc, d));
   sum_store(c->dx, c->part, S, (size_t)Rc * d, Rc, d, d, st);
-  draft_layer(c, Rc, c->rtok, c->dx, c->rm);
+  draft_layer(c, Rc, W, c->rtok, c->dx, c->rm);
   gather_rows_f32(c->a_last, c->dx, c->gidx, batch, d, st);
   draft_lm(c, batch, c->a_last, chain ? 1 : c->cfg.topk, chain ? c->cfg.temperature : 1.f);
   TreeOut out{tokens, parents, depth, pos, mask, score};
@@ -712,6 +728,12 @@ eagle3_status eagle3_sample(eagle3_ctx* c, int32_t n, const float* logits, float
            c->tk_ids, c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
   sample_rows(n, logits, V, temperature, c->tk_lse64, c->tk_ids, uniforms, tokens, c->st);
   return last_error();
+}
+
+eagle3_status eagle3_set_stream(eagle3_ctx* c, void* stream) {
+  if (!c) return EAGLE3_EINVAL;
+  c->st = (hipStream_t)stream;
+  return EAGLE3_OK;
 }
 
 eagle3_status eagle3_device_status(eagle3_ctx* c, int32_t* flags) {

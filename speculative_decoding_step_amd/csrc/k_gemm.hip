@@ -51,17 +51,26 @@ constexpr int KSTEPS = KT / 32;
 constexpr int XPAD = 8;       // bf16 elements of padding per LDS row
 
 // MB = number of 16-row M blocks per workgroup (1 or 4).
+// Work item lam = (m-tile, K split, N tile), m-tile fastest.  Workgroups are
+// dispatched round-robin over the 8 XCDs, so workgroup L runs item
+// (L % 8) * per + L / 8: the m-tiles of one weight tile land on the same XCD
+// back to back and re-read that tile from its L2 rather than from HBM.
 template <int MB>
 __global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X, int M, int K,
                                                    GemmSegs segs, float* __restrict__ out, int ldo,
-                                                   size_t split_stride, int kchunk) {
+                                                   size_t split_stride, int kchunk, int mtiles, int S, int nwork) {
   __shared__ __attribute__((aligned(16))) bf16_t xs[16 * MB][KT + XPAD];
+  const int per = (nwork + 7) >> 3;
+  const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lam >= nwork) return;
+  const int mt = lam % mtiles, rest = lam / mtiles;
+  const int split = rest % S, ntile = rest / S;
   int seg, n0;
-  seg_of(segs, blockIdx.x, seg, n0);
+  seg_of(segs, ntile, seg, n0);
   const bf16_t* __restrict__ W = (const bf16_t*)segs.w[seg];
   const int nrows = segs.rows[seg];
-  const int m0 = blockIdx.z * 16 * MB;
-  const int kb = blockIdx.y * kchunk;
+  const int m0 = mt * 16 * MB;
+  const int kb = split * kchunk;
   const int ke = min(K, kb + kchunk);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X,
   }
   // result: acc[mb][r] = out[m0 + 16mb + 4lg + r][n0 + 16wv + lr]
   if (!wok) return;
-  float* o = out + blockIdx.y * split_stride + segs.col0[seg] + wrow;
+  float* o = out + split * split_stride + segs.col0[seg] + wrow;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -137,6 +146,101 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X,
       const int m = m0 + 16 * mb + 4 * lg + r;
       if (m < M) o[(size_t)m * ldo] = acc[mb][r];
     }
+  }
+}
+
+// Large-M GEMM (prefill chunks, batch-64 verify): 128 x 128 output tile per
+// workgroup, K in steps of 64 through double-buffered LDS for both operands.
+// Four waves in a 2 x 2 arrangement each own a 64 x 64 sub-tile (4 x 4 MFMA
+// blocks of 16 x 16).  The next K step's tiles are fetched into registers
+// while the current one is multiplied.  Tile order: m-tile fastest, dealt
+// round-robin over the 8 XCDs as in the skinny kernel, so the m-tiles that
+// share a weight tile read it from the same L2.
+constexpr int BT = 128, BKK = 64, BPAD = 8;
+
+struct BigTiles {
+  int tiles0[4];  // prefix of 128-row N tiles per segment
+};
+
+__global__ __launch_bounds__(256) void k_gemm_bf16_big(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
+                                                       BigTiles bt, float* __restrict__ out, int ldo, int mtiles,
+                                                       int nwork) {
+  __shared__ __attribute__((aligned(16))) bf16_t as[2][BT][BKK + BPAD];
+  __shared__ __attribute__((aligned(16))) bf16_t bs[2][BT][BKK + BPAD];
+  const int per = (nwork + 7) >> 3;
+  const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lam >= nwork) return;
+  const int mt = lam % mtiles, ntile = lam / mtiles;
+  int seg = 0;
+  while (seg + 1 < segs.nseg && ntile >= bt.tiles0[seg + 1]) ++seg;
+  const int n0 = (ntile - bt.tiles0[seg]) * BT;
+  const bf16_t* __restrict__ W = (const bf16_t*)segs.w[seg];
+  const int nrows = segs.rows[seg];
+  const int m0 = mt * BT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wm = (wv & 1) * 64, wn = (wv >> 1) * 64;
+  // global staging: chunk c = tid + 256 i (i < 4) covers tile row c / 8, K columns 8 (c % 8)
+  u32x4 ar[4], br[4];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
+      const int m = m0 + row, n = n0 + row;
+      ar[i] = m < M ? *(const u32x4*)(X + (size_t)m * K + k0 + col) : u32x4{0u, 0u, 0u, 0u};
+      br[i] = n < nrows ? *(const u32x4*)(W + (size_t)n * K + k0 + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
+      *(u32x4*)&as[buf][row][col] = ar[i];
+      *(u32x4*)&bs[buf][row][col] = br[i];
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < K; k0 += BKK) {
+    const bool more = k0 + BKK < K;
+    if (more) fetch(k0 + BKK);
+#pragma unroll
+    for (int ks = 0; ks < BKK / 32; ++ks) {
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)&as[buf][wm + 16 * i + lr][32 * ks + 8 * lg]);
+        b[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)&bs[buf][wn + 16 * i + lr][32 * ks + 8 * lg]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // acc[i][j][r] = out[m0 + wm + 16 i + 4 lg + r][n0 + wn + 16 j + lr]
+  float* o = out + segs.col0[seg];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn + 16 * j + lr;
+    if (n >= nrows) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + 16 * i + 4 * lg + r;
+        if (m < M) o[(size_t)m * ldo + n] = acc[i][j][r];
+      }
   }
 }
 
@@ -200,19 +304,31 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
   if (M <= 0) return splits;
   const int ldo = gemm_ntot(segs);
   const int ntiles = segs.tiles0[segs.nseg];
+  if (bf16 && m_tile > 64) {
+    BigTiles bt;
+    bt.tiles0[0] = 0;
+    for (int i = 0; i < 3; ++i) bt.tiles0[i + 1] = bt.tiles0[i] + (i < segs.nseg ? (segs.rows[i] + BT - 1) / BT : 0);
+    const int mtiles = (M + BT - 1) / BT;
+    const int nwork = mtiles * bt.tiles0[segs.nseg];
+    const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
+    k_gemm_bf16_big<<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, bt, out, ldo, mtiles, nwork);
+    return 1;
+  }
   if (bf16) {
     // split K into `splits` chunks that are multiples of the LDS tile
     const int ktiles = K / KT;
     const int per = (ktiles + splits - 1) / splits;
     const int kchunk = per * KT;
     const int S = (ktiles + per - 1) / per;
-    if (m_tile == 16) {
-      dim3 grid(ntiles, S, (M + 15) / 16);
-      k_gemm_bf16<1><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, out, ldo, split_stride, kchunk);
-    } else {
-      dim3 grid(ntiles, S, (M + 63) / 64);
-      k_gemm_bf16<4><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, out, ldo, split_stride, kchunk);
-    }
+    const int mtiles = (M + m_tile - 1) / m_tile;
+    const int nwork = mtiles * S * ntiles;
+    const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
+    if (m_tile == 16)
+      k_gemm_bf16<1><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, out, ldo, split_stride, kchunk, mtiles, S,
+                                           nwork);
+    else
+      k_gemm_bf16<4><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, out, ldo, split_stride, kchunk, mtiles, S,
+                                           nwork);
   } else {
     const int per = ((K + 31) / 32 + splits - 1) / splits;
     const int kchunk = per * 32;

@@ -102,64 +102,65 @@ void draft_input(bool bf16, const void* embed, const int* tokens, const float* x
 }
 
 // ----------------------------------------------------------- rope + KV write
-// One block per row; QKV partial columns [q heads | k heads | v heads].
-// Angles: pos * theta^(-2i/hd) evaluated in double, then cos/sin in double.
+// One block per (row, head) over QKV partial columns [q heads | k heads | v heads].
+// The angle pos * inv_freq[i] (inv_freq = theta^(-2i/hd), tabulated in double
+// on the host) is formed and reduced modulo 2 pi in double; cos/sin of the
+// reduced angle are then taken in float.
 template <typename T>
-__global__ __launch_bounds__(256) void k_rope_kv(const float* __restrict__ part, int S, size_t sstride,
-                                                 const int* __restrict__ rseq, const int* __restrict__ rpos,
-                                                 const int* __restrict__ rslot, T* __restrict__ q_out,
-                                                 T* __restrict__ kc, T* __restrict__ vc, size_t seq_stride,
-                                                 size_t head_stride, int Hq, int Hkv, int hd, float theta) {
-  const int r = blockIdx.x;
+__global__ __launch_bounds__(64) void k_rope_kv(const float* __restrict__ part, int S, size_t sstride,
+                                                const int* __restrict__ rseq, const int* __restrict__ rpos,
+                                                const int* __restrict__ rslot, const double* __restrict__ inv_freq,
+                                                T* __restrict__ q_out, T* __restrict__ kc, T* __restrict__ vc,
+                                                size_t seq_stride, size_t head_stride, int Hq, int Hkv, int hd) {
+  const int r = blockIdx.x, h = blockIdx.y;
   const int b = rseq[r];
   const int ncol = (Hq + 2 * Hkv) * hd;
   const int half = hd / 2;
-  const double pos = (double)rpos[r];
-  const float* pr = part + (size_t)r * ncol;
+  const float* pr = part + (size_t)r * ncol + (size_t)h * hd;
   auto val = [&](int c) {
     float s = 0.f;
     for (int k = 0; k < S; ++k) s += pr[k * sstride + c];
     return s;
   };
-  // q and k heads: pairs (i, i + half) rotated by angle pos * inv_freq[i]
-  const int npairs = (Hq + Hkv) * half;
-  for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
-    const int h = p / half, i = p % half;
-    const int c0 = h * hd + i, c1 = c0 + half;
-    const float x1 = val(c0), x2 = val(c1);
-    const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
-    double sn, cs;
-    sincos(pos * inv, &sn, &cs);
-    const float c = (float)cs, s = (float)sn;
-    const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
+  if (h >= Hq + Hkv) {  // V: copy
+    if (b < 0) return;
+    T* vp = vc + (size_t)b * seq_stride + (size_t)(h - Hq - Hkv) * head_stride + (size_t)rslot[r] * hd;
+    for (int i = threadIdx.x; i < hd; i += blockDim.x) st<T>(vp, i, val(i));
+    return;
+  }
+  if (h >= Hq && b < 0) return;
+  const double pos = (double)rpos[r];
+  constexpr double TWO_PI = 6.283185307179586476925286766559;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const float x1 = val(i), x2 = val(i + half);
+    const double ang = pos * inv_freq[i];
+    const float red = (float)(ang - TWO_PI * rint(ang / TWO_PI));
+    float sn, cs;
+    sincosf(red, &sn, &cs);
+    const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
     if (h < Hq) {
-      st<T>(q_out, (size_t)r * Hq * hd + h * hd + i, y1);
-      st<T>(q_out, (size_t)r * Hq * hd + h * hd + i + half, y2);
-    } else if (b >= 0) {
-      const int g = h - Hq;
-      T* kp = kc + (size_t)b * seq_stride + (size_t)g * head_stride + (size_t)rslot[r] * hd;
+      T* qp = q_out + ((size_t)r * Hq + h) * hd;
+      st<T>(qp, i, y1);
+      st<T>(qp, i + half, y2);
+    } else {
+      T* kp = kc + (size_t)b * seq_stride + (size_t)(h - Hq) * head_stride + (size_t)rslot[r] * hd;
       st<T>(kp, i, y1);
       st<T>(kp, i + half, y2);
     }
   }
-  if (b < 0) return;
-  for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x) {
-    const int g = e / hd, i = e % hd;
-    T* vp = vc + (size_t)b * seq_stride + (size_t)g * head_stride + (size_t)rslot[r] * hd;
-    st<T>(vp, i, val((Hq + Hkv) * hd + e));
-  }
 }
 
-void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const RowMeta& rm, void* q_out, void* kc,
-             void* vc, size_t seq_stride, size_t head_stride, int Hq, int Hkv, int hd, float theta,
+void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const RowMeta& rm, const double* inv_freq,
+             void* q_out, void* kc, void* vc, size_t seq_stride, size_t head_stride, int Hq, int Hkv, int hd,
              hipStream_t st) {
   if (R <= 0) return;
+  dim3 grid(R, Hq + 2 * Hkv);
   if (bf16)
-    k_rope_kv<bf16_t><<<R, 256, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, (bf16_t*)q_out, (bf16_t*)kc,
-                                         (bf16_t*)vc, seq_stride, head_stride, Hq, Hkv, hd, theta);
+    k_rope_kv<bf16_t><<<grid, 64, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, inv_freq, (bf16_t*)q_out,
+                                           (bf16_t*)kc, (bf16_t*)vc, seq_stride, head_stride, Hq, Hkv, hd);
   else
-    k_rope_kv<float><<<R, 256, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, (float*)q_out, (float*)kc,
-                                        (float*)vc, seq_stride, head_stride, Hq, Hkv, hd, theta);
+    k_rope_kv<float><<<grid, 64, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, inv_freq, (float*)q_out,
+                                          (float*)kc, (float*)vc, seq_stride, head_stride, Hq, Hkv, hd);
 }
 
 // ------------------------------------------------------------- top-k + lse

@@ -21,7 +21,8 @@ GemmSegs make_segs(const void* w0, int r0, const void* w1 = nullptr, int r1 = 0,
 
 // out[s][m][n] (split s of the K reduction) = sum_k X[m][k] W[n][k].
 // Returns the number of splits used; out must hold splits * split_stride floats.
-// m_tile is 16 or 64 (bf16 MFMA tiles); ignored for float.
+// m_tile is 16 or 64 (skinny bf16 MFMA tiles, K split allowed) or 128 (the
+// large-M bf16 kernel, no K split: returns 1); ignored for float.
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out,
          size_t split_stride, int splits, int m_tile, hipStream_t st);
 // Number of K splits gemm() will actually use for a requested count.
@@ -55,13 +56,15 @@ struct RowMeta {
 };
 
 // Rotary embedding + KV write from the QKV partials [S][R][(Hq+2Hkv)*hd].
+// inv_freq: [hd/2] doubles theta^(-2i/hd).
 void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const RowMeta& rm,
-             void* q_out, void* kc, void* vc, size_t seq_stride, size_t head_stride, int Hq, int Hkv,
-             int hd, float theta, hipStream_t st);
+             const double* inv_freq, void* q_out, void* kc, void* vc, size_t seq_stride, size_t head_stride,
+             int Hq, int Hkv, int hd, hipStream_t st);
 
 // Attention of rows over their visible keys, split over key chunks, then combined.
+// rps: rows per sequence (rows of one sequence are consecutive; R % rps == 0).
 void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride,
-               size_t head_stride, const RowMeta& rm, int R, int Hq, int Hkv, int hd, int key_bound,
+               size_t head_stride, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
                float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st);
 
 // Row-wise top-k + log-sum-exp over fp32 logits [R, ld] (first V columns).

@@ -206,6 +206,31 @@ class Engine:
         self.compact()
         self.step_idx += 1
 
+    def capture(self):
+        """Capture one step (draft, verify, accept, compact) into a HIP graph.
+
+        Replays run the same kernels on the device state current at replay
+        time; call replay() instead of step()."""
+        cap = torch.cuda.Stream(self.dev)
+        cap.wait_stream(self.stream)
+        g = torch.cuda.CUDAGraph()
+        B.eagle3_set_stream(self.ctx, cap.cuda_stream)
+        try:
+            with torch.cuda.graph(g, stream=cap):
+                self.draft()
+                self.verify()
+                self.accept()
+                self.compact()
+        finally:
+            B.eagle3_set_stream(self.ctx, self.stream.cuda_stream)
+        self.stream.wait_stream(cap)
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
+        self.step_idx += 1
+
     # ------------------------------------------------------------------ drivers
     def generate(self, prompts, max_new: int, uniforms=None):
         """Speculative decoding of every sequence until each has max_new tokens.

@@ -169,3 +169,28 @@ def test_sampled_chain_first_token_distribution_v64():
     print(f"\n  chi-square {stat:.1f} dof {len(obs_m) - 1} p={pval:.3g}", flush=True)
     assert pval > 1e-3
     eng.close()
+
+
+def test_graph_replay_matches_eager_steps():
+    """The captured step graph, replayed with eager work and synchronisations in
+    between, gives bit-identical tokens, paths and KV to eager steps."""
+    ms = toy_shape(dtype="bf16", vocab=64, layers=2)
+    spec = Spec("greedy_tree", 4, 3, 10)
+    prompt = synth.tokens_np(44, "p", 24, ms.vocab)
+    a = make_engine(ms, spec, max_seq=160, seed=21, sigma=0.3)
+    b = make_engine(ms, spec, max_seq=160, seed=21, sigma=0.3)
+    a.prefill([prompt])
+    b.prefill([prompt])
+    b.capture()
+    for i in range(8):
+        a.step()
+        b.replay()
+        torch.cuda.synchronize()
+        _ = b.seq_lens.sum().item()            # eager work between replays
+        for name in ("tokens", "parents", "mask", "path", "path_len", "next_root", "seq_lens", "next_tok",
+                     "argmax"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), (i, name)
+        assert torch.equal(a.kv_target, b.kv_target), i
+    assert a.device_status() == 0 and b.device_status() == 0
+    a.close()
+    b.close()

@@ -35,24 +35,26 @@ def _status_clear(eng):
 
 
 # ------------------------------------------------------------------ verify_tree
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_verify_prefill_and_tree_vs_oracle(dtype):
-    print(f"\n[verify parity {dtype}]", flush=True)
+@pytest.mark.parametrize("dtype,chunk", [("f32", 24), ("bf16", 24), ("bf16", 96)])
+def test_verify_prefill_and_tree_vs_oracle(dtype, chunk):
+    """Prefill in chunks (a 96-row chunk takes the large-M GEMM), then a tree verify."""
+    print(f"\n[verify parity {dtype} chunk {chunk}]", flush=True)
     ms = toy_shape(dtype=dtype, vocab=1000)
     spec = Spec("greedy_tree", 4, 3, 12)
-    eng = make_engine(ms, spec, max_seq=160, sigma=0.05, prefill_chunk=24)
+    eng = make_engine(ms, spec, max_seq=160, sigma=0.05, prefill_chunk=chunk)
     shp, W, H = oracle_weights(ms, sigma=0.05)
-    prompt = synth.tokens_np(31, "p", 50, ms.vocab)
+    P = 50 if chunk < 64 else 110
+    prompt = synth.tokens_np(31, "p", P, ms.vocab)
     eng.prefill([prompt])
     torch.cuda.synchronize()
     _status_clear(eng)
     # oracle prefill
     cache = KVCache(shp.n_layers, 160, shp.n_kv_heads, shp.head_dim)
-    lg, k, v, aux = target_forward(W, shp, cache, prompt, np.arange(50), causal_visible(50))
+    lg, k, v, aux = target_forward(W, shp, cache, prompt, np.arange(P), causal_visible(P))
     for l in range(shp.n_layers):
-        cache.k[l][:50], cache.v[l][:50] = k[l], v[l]
-    cache.length = 50
-    kvg = kv_view(eng)[:, :, 0, :, :50].float().cpu().numpy()      # [L, 2, Hkv, 50, hd]
+        cache.k[l][:P], cache.v[l][:P] = k[l], v[l]
+    cache.length = P
+    kvg = kv_view(eng)[:, :, 0, :, :P].float().cpu().numpy()      # [L, 2, Hkv, P, hd]
     for l in range(shp.n_layers):
         err_k = np.abs(kvg[l, 0].transpose(1, 0, 2) - k[l]).max()
         err_v = np.abs(kvg[l, 1].transpose(1, 0, 2) - v[l]).max()
@@ -60,7 +62,7 @@ def test_verify_prefill_and_tree_vs_oracle(dtype):
     # the prefill's last-position aux (what the catch-up consumes)
     aux_g = eng.aux_new[0, 0].float().cpu().numpy()
     assert np.abs(aux_g - aux[-1]).max() < (2e-2 if dtype == "bf16" else 1e-4)
-    # tree verify at P = 50
+    # tree verify at P
     rng = np.random.default_rng(5)
     n = 13
     tokens, parents = random_tree(rng, n, ms.vocab)
@@ -68,15 +70,15 @@ def test_verify_prefill_and_tree_vs_oracle(dtype):
     for i in range(1, n):
         dep[i] = dep[parents[i]] + 1
     m = tree_mask(parents)
-    ref, rk, rv, raux = target_forward(W, shp, cache, tokens, 50 + np.array(dep),
+    ref, rk, rv, raux = target_forward(W, shp, cache, tokens, P + np.array(dep),
                                        [list(np.nonzero(m[i])[0]) for i in range(n)])
-    seq_lens = to_dev([50])
+    seq_lens = to_dev([P])
     logits = torch.zeros(n, ms.vocab, dtype=torch.float32, device="cuda")
     am = torch.zeros(n, dtype=torch.int32, device="cuda")
     mg = torch.zeros(n, dtype=torch.float32, device="cuda")
     auxo = torch.zeros(n, 3 * ms.d, dtype=eng.tdt, device="cuda")
     mw = torch.as_tensor(mask_words(parents).view(np.int64), device="cuda")
-    tok_d, pos_d = to_dev(tokens), to_dev(50 + np.array(dep))
+    tok_d, pos_d = to_dev(tokens), to_dev(P + np.array(dep))
     B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq_lens), n, _p(tok_d), _p(pos_d), _p(mw),
                          B.LM_ALL, _p(logits), _p(am), _p(mg), _p(auxo))
     torch.cuda.synchronize()
@@ -90,7 +92,7 @@ def test_verify_prefill_and_tree_vs_oracle(dtype):
         if top2_margin(ref[i]) > 2 * margin_tol(dtype, ref[i]):
             assert amg[i] == int(np.argmax(ref[i]))
     assert np.abs(auxo.float().cpu().numpy() - raux).max() < (2e-2 if dtype == "bf16" else 1e-4)
-    kvt = kv_view(eng)[:, :, 0, :, 50:50 + n].float().cpu().numpy()
+    kvt = kv_view(eng)[:, :, 0, :, P:P + n].float().cpu().numpy()
     for l in range(shp.n_layers):
         assert np.abs(kvt[l, 0].transpose(1, 0, 2) - rk[l]).max() < (2e-2 if dtype == "bf16" else 1e-4)
     eng.close()

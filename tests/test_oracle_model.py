@@ -96,3 +96,19 @@ def test_tree_rows_equal_per_path_recompute(toy_model):
         ref, _, _, _ = target_forward(W, shp, c2, full, np.arange(len(full)), causal_visible(len(full)))
         worst = max(worst, np.abs(logits[node] - ref[-1]).max())
     assert worst < 1e-9
+
+
+def test_tap_at_layer_count_is_the_last_output(toy_model):
+    """hidden_states[L] (a tap index equal to the layer count) is the output of
+    the last layer: the residual entering layer L of a deeper model."""
+    ms, shp, W, H = toy_model(taps=(0, 1, 2), layers=2)
+    deeper = dict(W)
+    deeper["layers"] = W["layers"] + [W["layers"][0]]
+    from dataclasses import replace
+    shp3 = replace(shp, n_layers=3)
+    toks = [3, 1, 4, 1]
+    c2 = KVCache(2, 8, shp.n_kv_heads, shp.head_dim)
+    c3 = KVCache(3, 8, shp.n_kv_heads, shp.head_dim)
+    _, _, _, a2 = target_forward(W, shp, c2, toks, np.arange(4), causal_visible(4))
+    _, _, _, a3 = target_forward(deeper, shp3, c3, toks, np.arange(4), causal_visible(4))
+    np.testing.assert_array_equal(a2, a3)
