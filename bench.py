@@ -211,7 +211,7 @@ def main():
                    "topk": w.topk, "tree_nodes": w.n_nodes, "rows_per_step": rows},
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
-                     "kernel": "k_gemm_bf16<4> (64-row MFMA weight-streaming GEMM)",
+                     "kernel": "k_gemm_bf16<4,2,128> (64-row MFMA weight-streaming GEMM)",
                      "launches_per_step": n64 / args.steps,
                      "kernel_ms_per_step": round(t64 / args.steps, 4)},
         "hbm_gbps_step": None,

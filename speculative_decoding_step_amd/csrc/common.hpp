@@ -59,6 +59,36 @@ E3_DEV float block_sum(float v, float* red) {
   return t;
 }
 
+// Split-K partials: sum over k < S of p[k * stride], added in split order.
+// The loads are issued eight at a time so that they are in flight together.
+E3_DEV float sum_splits(const float* __restrict__ p, int S, size_t stride) {
+  float s = 0.f;
+  for (int k0 = 0; k0 < S; k0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (k0 + j < S) ? p[(size_t)(k0 + j) * stride] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < S) s += v[j];
+  }
+  return s;
+}
+
+E3_DEV float4 sum_splits4(const float4* __restrict__ p, int S, size_t stride4) {
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < S; k0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (k0 + j < S) ? p[(size_t)(k0 + j) * stride4] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < S) {
+        s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
+      }
+  }
+  return s;
+}
+
 // (value, index) order used by every top-k and argmax: larger value first,
 // lower index on ties.
 E3_DEV bool better(float va, int ia, float vb, int ib) {

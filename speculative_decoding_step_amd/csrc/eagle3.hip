@@ -295,12 +295,16 @@ void prof_end(eagle3_ctx* c, ProfRec* rec) {
 // ----------------------------------------------------------------- GEMM plan
 int plan_splits(eagle3_ctx* c, int M, int N, int K, int m_tile) {
   if (!c->bf16) return 1;
-  const int tiles = ((N + 63) / 64) * ((M + m_tile - 1) / m_tile);
-  int S = (512 + tiles - 1) / tiles;
-  S = std::max(1, std::min(S, K / 256));
+  // about 512 workgroups in flight: enough to cover 256 CUs without a tail
+  const int rows = gemm_rows_per_tile(true, m_tile);
+  const int tiles = ((N + rows - 1) / rows) * ((M + m_tile - 1) / m_tile);
+  // about 512 workgroups, but at most 8 splits: every split adds M x N fp32
+  // partials that the consumer kernel reads back
+  int S = (512 + tiles / 2) / tiles;
+  S = std::max(1, std::min(8, S));
   const int mpad = (M + m_tile - 1) / m_tile * m_tile;
   while (S > 1 && (size_t)S * mpad * N > c->part_elems) --S;
-  return gemm_splits(true, K, S);
+  return gemm_splits(true, K, S, m_tile);
 }
 
 // X [M, K] of T times the stacked weights; returns the number of splits in c->part.
@@ -341,16 +345,27 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
   const bool bf = c->bf16;
   hipStream_t st = c->st;
   embed_rows(bf, c->tw.embed, c->rtok, c->xres, R, d, s.vocab, c->status, st);
-  for (int l = 0; l < s.n_layers; ++l) {
-    const eagle3_layer_weights& L = c->layers[l];
+  // Residual entering layer l (after adding S partials of the previous GEMM, if
+  // any): captured into the aux columns of every tap equal to l and normalised
+  // with w into out.
+  auto enter = [&](int l, int S, const void* w, void* out) {
+    int first = -1;
     for (int t = 0; t < 3; ++t)
-      if (aux && s.taps[t] == l) {
+      if (aux && s.taps[t] == l && first < 0) first = t;
+    void* tap = first < 0 ? nullptr : (char*)aux + (size_t)first * d * c->esz;
+    add_rmsnorm(bf, c->xres, S ? c->part : nullptr, S, (size_t)R * d, d, w, out, d, R, d, s.rms_eps, tap, 3 * d, st);
+    for (int t = first + 1; first >= 0 && t < 3; ++t)
+      if (s.taps[t] == l) {
         if (bf)
           k_store_tap<bf16_t><<<R, 256, 0, st>>>(c->xres, d, (bf16_t*)aux, 3 * d, t * d);
         else
           k_store_tap<float><<<R, 256, 0, st>>>(c->xres, d, (float*)aux, 3 * d, t * d);
       }
-    rmsnorm(bf, c->xres, L.attn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
+  };
+  enter(0, 0, c->layers[0].attn_norm, c->hbuf);
+  bool final_normed = false;
+  for (int l = 0; l < s.n_layers; ++l) {
+    const eagle3_layer_weights& L = c->layers[l];
     const GemmSegs qkv = make_segs(L.wq, qdim, L.wk, kvdim, L.wv, kvdim);
     int S = run_gemm(c, c->hbuf, R, d, qkv);
     char* kc = kv_layer(c, c->kv_t, l, 0);
@@ -360,13 +375,20 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
             s.head_dim, st);
     run_attention(c, kc, vc, c->rm, R, rps);
     S = run_gemm(c, c->abuf, R, qdim, make_segs(L.wo, d));
-    resid_add(c->xres, c->part, S, (size_t)R * d, R, d, d, st);
-    rmsnorm(bf, c->xres, L.ffn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
+    add_rmsnorm(bf, c->xres, c->part, S, (size_t)R * d, d, L.ffn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
     const GemmSegs gu = make_segs(L.w_gate, s.ffn, L.w_up, s.ffn);
     S = run_gemm(c, c->hbuf, R, d, gu);
     silu_mul(bf, c->abuf, c->part, S, (size_t)R * 2 * s.ffn, R, s.ffn, 2 * s.ffn, st);
     S = run_gemm(c, c->abuf, R, s.ffn, make_segs(L.w_down, d));
-    resid_add(c->xres, c->part, S, (size_t)R * d, R, d, d, st);
+    if (l + 1 < s.n_layers) {
+      enter(l + 1, S, c->layers[l + 1].attn_norm, c->hbuf);
+    } else if (lm == EAGLE3_LM_ALL) {
+      add_rmsnorm(bf, c->xres, c->part, S, (size_t)R * d, d, c->tw.final_norm, c->gbuf, d, R, d, s.rms_eps, nullptr,
+                  0, st);
+      final_normed = true;
+    } else {
+      resid_add(c->xres, c->part, S, (size_t)R * d, R, d, d, st);
+    }
   }
   if (lm == EAGLE3_LM_NONE) return;
   int n = R;
@@ -376,7 +398,7 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
     fin = c->dx;
     n = nlast;
   }
-  rmsnorm(bf, fin, c->tw.final_norm, c->gbuf, d, n, d, s.rms_eps, nullptr, 0, st);
+  if (!final_normed) rmsnorm(bf, fin, c->tw.final_norm, c->gbuf, d, n, d, s.rms_eps, nullptr, 0, st);
   float* lg = logits ? logits : c->logits;
   run_gemm(c, c->gbuf, n, d, make_segs(c->tw.lm_head, s.vocab), lg);
   if (argmax || margin) {
@@ -404,8 +426,7 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
           s.head_dim, st);
   run_attention(c, kc, vc, rm, R, rps);
   S = run_gemm(c, c->abuf, R, qdim, make_segs(H.wo, d));
-  resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
-  rmsnorm(bf, x, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
+  add_rmsnorm(bf, x, c->part, S, (size_t)R * d, d, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
   const GemmSegs gu = make_segs(H.w_gate, s.ffn, H.w_up, s.ffn);
   S = run_gemm(c, c->hbuf, R, d, gu);
   silu_mul(bf, c->abuf, c->part, S, (size_t)R * 2 * s.ffn, R, s.ffn, 2 * s.ffn, st);

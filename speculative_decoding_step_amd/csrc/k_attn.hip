@@ -85,37 +85,85 @@ __global__ __launch_bounds__(64) void k_attn_partial(const T* __restrict__ q, co
   }
 }
 
+// Merge the ns chunk partials of one (row, head): out = sum_s e_s o_s / sum_s e_s l_s
+// with e_s = exp(m_s - max_s m_s), summed in chunk order.  Partials are read
+// eight chunks at a time so that their loads overlap.
 template <typename T>
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ o_part,
                                                       const float* __restrict__ ml_part, int ns, int R, int Hq,
                                                       int hd, T* __restrict__ out) {
   const int r = blockIdx.x, h = blockIdx.y;
+  const size_t sstride = (size_t)R * Hq;  // (row, head) entries per chunk
+  const size_t oi0 = (size_t)r * Hq + h;
+  const float2* ml = (const float2*)ml_part;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml_part[2 * (((size_t)s * R + r) * Hq + h)]);
-  float den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t oi = ((size_t)s * R + r) * Hq + h;
-    if (ml_part[2 * oi] != -INFINITY) den += ml_part[2 * oi + 1] * expf(ml_part[2 * oi] - M);
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (s0 + j < ns) ? ml[(s0 + j) * sstride + oi0] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) M = fmaxf(M, v[j].x);
   }
   for (int i = threadIdx.x; i < hd; i += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const size_t oi = ((size_t)s * R + r) * Hq + h;
-      if (ml_part[2 * oi] != -INFINITY) acc += o_part[oi * hd + i] * expf(ml_part[2 * oi] - M);
+    float den = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      float2 v[8];
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool in = s0 + j < ns;
+        v[j] = in ? ml[(s0 + j) * sstride + oi0] : make_float2(-INFINITY, 0.f);
+        o[j] = in ? o_part[((s0 + j) * sstride + oi0) * hd + i] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (v[j].x != -INFINITY) {
+          const float e = expf(v[j].x - M);
+          den += v[j].y * e;
+          acc += o[j] * e;
+        }
     }
-    st<T>(out, ((size_t)r * Hq + h) * hd + i, den > 0.f ? acc / den : 0.f);
+    st<T>(out, oi0 * hd + i, den > 0.f ? acc / den : 0.f);
   }
 }
 
 // ---------------------------------------------------------------- MFMA path
 // bf16 flash-decoding with grouped queries.  A workgroup (4 waves) owns one
 // sequence, one KV head g, 64 query vectors (row i, query head g*G + hl,
-// numbered i*G + hl, 16 per wave) and one chunk of keys; key tiles of 64 are
-// staged in LDS (K row-major, V transposed) and shared by the four waves.
-// S = Q K^T and O += P V run on v_mfma_f32_16x16x32_bf16; the online softmax
-// (max, sum) stays in fp32, and P enters the PV product as two bf16 terms
-// (P = hi + lo, two MFMAs) so it keeps about 16 significant bits.
+// numbered i*G + hl, 16 per wave) and one chunk of keys.  Key tiles of 64 are
+// staged in LDS (K row-major, V transposed) and shared by the four waves; the
+// next tile is loaded into registers while the current one is used.
+//
+// Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
+// A = 16 keys, B = the wave's 16 queries), so that a lane holds four keys of
+// its own query.  Those accumulator registers are then, unchanged in place,
+// the B operand of O^T += V^T P^T: one 32-key MFMA step takes keys
+// 4*lg + e and 16 + 4*lg + e (e = 0..3) in lane group lg, and the V^T operand
+// is read from LDS in the same key order.  P enters as two bf16 terms
+// (hi + lo, two MFMAs), keeping about 16 significant bits.
+//
+// Online softmax in base 2 with a lazy maximum: the running maximum m of a
+// query is raised (and O, l rescaled) only when a tile's maximum exceeds it by
+// more than 8, so exp2(s - m) <= 256.  Exact in real arithmetic; the partial
+// maximum is stored in natural-log units for the combine step.
+//
+// Work items (query block fastest, then KV head, key chunk, sequence) are
+// dealt to the 8 XCDs in contiguous runs, so the query blocks that read the
+// same K/V chunk share one L2.
 constexpr int AKT = 64;  // keys per LDS tile
+constexpr int VPAD = 8;  // bf16 padding per transposed-V row
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float LAZY = 8.f;  // log2 headroom before the running maximum moves
+
+// LDS position of V(key, dim) in the transposed tile: groups of 8 keys are
+// XOR-swizzled by the dimension's 8-group so that the transposing stores of
+// one wave spread over the banks while 8 consecutive keys stay contiguous.
+E3_DEV int vt_index(int dim, int key) {
+  return dim * (AKT + VPAD) + ((((key >> 3) ^ (dim >> 3)) & 7) << 3) + (key & 7);
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
@@ -123,39 +171,33 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const bf16_t* __restrict__ q,
                                                    size_t head_stride, const int* __restrict__ rseq,
                                                    const int* __restrict__ rlim, const int* __restrict__ rt0,
                                                    const uint64_t* __restrict__ rmask, int R, int rps, int qblocks,
-                                                   int Hq, int Hkv, int S_cap, float scale, int chunk,
-                                                   float* __restrict__ o_part, float* __restrict__ ml_part) {
+                                                   int Hq, int Hkv, int ns, int nwork, int S_cap, float scale,
+                                                   int chunk, float* __restrict__ o_part, float* __restrict__ ml_part) {
   __shared__ __attribute__((aligned(16))) bf16_t ks[AKT][HD + 8];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[HD][AKT + 8];
-  __shared__ __attribute__((aligned(16))) bf16_t ps[2][4][16][AKT + 8];  // [hi|lo][wave][query][key]
+  __shared__ __attribute__((aligned(16))) bf16_t vt[HD * (AKT + VPAD)];
   __shared__ int red_end[4], red_seq[4];
+  const int per = (nwork + 7) >> 3;
+  const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lam >= nwork) return;
+  const int qb = lam % qblocks;
+  int t = lam / qblocks;
+  const int g = t % Hkv;
+  t /= Hkv;
+  const int sp = t % ns, bs = t / ns;
   const int G = Hq / Hkv;
-  const int bs = blockIdx.x / qblocks, qb = blockIdx.x % qblocks;
-  const int g = blockIdx.y, sp = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int nq = rps * G;
 
-  // output-row metadata: this lane accumulates query vectors 16w + 4lg + r
-  int o_row[4], o_h[4], o_lim[4], o_t0[4];
-  uint64_t o_mask[4];
-  bool o_ok[4];
-  int my_end = 0, my_seq = -1;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int v = qb * 64 + 16 * w + 4 * lg + r;
-    o_ok[r] = v < nq;
-    o_row[r] = bs * rps + (o_ok[r] ? v / G : 0);
-    o_h[r] = g * G + (o_ok[r] ? v % G : 0);
-    const int sq = o_ok[r] ? rseq[o_row[r]] : -1;
-    o_ok[r] = o_ok[r] && sq >= 0;
-    o_lim[r] = rlim[o_row[r]];
-    o_t0[r] = rt0[o_row[r]];
-    o_mask[r] = rmask[o_row[r]];
-    if (o_ok[r]) {
-      my_end = max(my_end, min(key_end(o_lim[r], o_t0[r], o_mask[r]), S_cap));
-      my_seq = max(my_seq, sq);
-    }
-  }
+  // the lane's query vector: 16w + lr of the block
+  const int v = qb * 64 + 16 * w + lr;
+  bool ok = v < nq;
+  const int row = bs * rps + (ok ? v / G : 0), h = g * G + (ok ? v % G : 0);
+  const int sq = ok ? rseq[row] : -1;
+  ok = ok && sq >= 0;
+  const int lim = rlim[row], t0 = rt0[row];
+  const uint64_t mask = rmask[row];
+  int my_end = ok ? min(key_end(lim, t0, mask), S_cap) : 0;
+  int my_seq = ok ? sq : -1;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     my_end = max(my_end, __shfl_xor(my_end, o, 64));
@@ -169,118 +211,124 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const bf16_t* __restrict__ q,
   const int kend = max(max(red_end[0], red_end[1]), max(red_end[2], red_end[3]));
   const int cs = max(max(red_seq[0], red_seq[1]), max(red_seq[2], red_seq[3]));
   const int c0 = sp * chunk, c1 = min(c0 + chunk, kend);
+  const int vis_all = ok ? min(lim, c1) : -1;  // keys below this are visible to the lane's query
 
-  float m[4], l[4];
-  f32x4 O[HD / 16];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.f;
-  }
+  float m = -INFINITY, lsum = 0.f;  // running maximum (log2 units) and the lane's share of the sum
+  f32x4 O[HD / 16];  // O^T: dims 16b + 4lg + r of the lane's query
 #pragma unroll
   for (int b = 0; b < HD / 16; ++b) O[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (cs >= 0 && c0 < c1) {
-    // Q fragment of the lane's A row: query vector 16w + lr
-    u32x4 qf[HD / 32];
+    const float qscale = scale * LOG2E;
+    u32x4 qf[HD / 32];  // B operand: the lane's query, dims 32kk + 8lg .. +7
     {
-      const int v = qb * 64 + 16 * w + lr;
-      const bool ok = v < nq;
-      const int row = bs * rps + (ok ? v / G : 0), h = g * G + (ok ? v % G : 0);
       const bf16_t* qp = q + ((size_t)row * Hq + h) * HD + 8 * lg;
 #pragma unroll
       for (int kk = 0; kk < HD / 32; ++kk) qf[kk] = ok ? *(const u32x4*)(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
     }
     const bf16_t* kb = kc + (size_t)cs * seq_stride + (size_t)g * head_stride;
     const bf16_t* vb = vc + (size_t)cs * seq_stride + (size_t)g * head_stride;
-    constexpr int CH = AKT * HD / 8;  // 16-byte chunks per tile
-    for (int kt = c0; kt < c1; kt += AKT) {
-      __syncthreads();
-      for (int c = tid; c < CH; c += 256) {
-        const int key = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
-        const int j = kt + key;
-        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (j < c1) {
-          kv = *(const u32x4*)(kb + (size_t)j * HD + d8);
-          vv = *(const u32x4*)(vb + (size_t)j * HD + d8);
-        }
-        *(u32x4*)&ks[key][d8] = kv;
-        const bf16_t* ve = (const bf16_t*)&vv;
+    constexpr int CPK = HD / 8;           // 16-byte chunks per key row
+    constexpr int NCH = AKT * CPK / 256;  // chunks per thread per tile
+    static_assert(NCH * 256 == AKT * CPK, "tile splits evenly over the threads");
+    u32x4 kr[NCH], vr[NCH];
+    auto load_tile = [&](int kt) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vt[d8 + e][key] = ve[e];
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + 256 * i, key = c / CPK, d8 = (c % CPK) * 8;
+        const int j = kt + key;
+        if (j < c1) {
+          kr[i] = *(const u32x4*)(kb + (size_t)j * HD + d8);
+          vr[i] = *(const u32x4*)(vb + (size_t)j * HD + d8);
+        } else {
+          kr[i] = u32x4{0u, 0u, 0u, 0u};
+          vr[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+    load_tile(c0);
+    for (int kt = c0; kt < c1; kt += AKT) {
+      __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + 256 * i, key = c / CPK, d8 = (c % CPK) * 8;
+        *(u32x4*)&ks[key][d8] = kr[i];
+        const bf16_t* ve = (const bf16_t*)&vr[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vt[vt_index(d8 + e, key)] = ve[e];
       }
       __syncthreads();
+      if (kt + AKT < c1) load_tile(kt + AKT);  // in flight during this tile's math
+      // S^T blocks: S[kb4][r] = score(key kt + 16 kb4 + 4 lg + r, the lane's query)
       f32x4 S[4];
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4) {
         S[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < HD / 32; ++kk) {
-          const bf16x8 bk = __builtin_bit_cast(bf16x8, *(const u32x4*)&ks[16 * kb4 + lr][32 * kk + 8 * lg]);
-          S[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[kk]), bk, S[kb4], 0, 0, 0);
+          const bf16x8 ak = __builtin_bit_cast(bf16x8, *(const u32x4*)&ks[16 * kb4 + lr][32 * kk + 8 * lg]);
+          S[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf16x8, qf[kk]), S[kb4], 0, 0, 0);
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[kb4][r] *= qscale;
       }
-      // S[kb4][r] = score(query 16w + 4lg + r, key kt + 16 kb4 + lr)
+      if (kt + AKT > vis_all) {  // tile reaches past the committed keys (or the lane has no query)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float tmax = -INFINITY;
+        for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) {
-          const int j = kt + 16 * kb4 + lr;
-          const bool vis = o_ok[r] && j < c1 && visible(j, o_lim[r], o_t0[r], o_mask[r]);
-          const float x = vis ? S[kb4][r] * scale : -INFINITY;
-          S[kb4][r] = x;
-          tmax = fmaxf(tmax, x);
-        }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
-        const float mn = fmaxf(m[r], tmax);
-        const float alpha = (mn == -INFINITY) ? 1.f : expf(m[r] - mn);
-        float psum = 0.f;
-#pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) {
-          const float p = (S[kb4][r] == -INFINITY) ? 0.f : expf(S[kb4][r] - mn);
-          S[kb4][r] = p;
-          psum += p;
-        }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) psum += __shfl_xor(psum, o, 64);
-        l[r] = l[r] * alpha + psum;
-        m[r] = mn;
-#pragma unroll
-        for (int b = 0; b < HD / 16; ++b) O[b][r] *= alpha;
-#pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) {
-          const bf16_t hi = f2bf(S[kb4][r]);
-          ps[0][w][4 * lg + r][16 * kb4 + lr] = hi;
-          ps[1][w][4 * lg + r][16 * kb4 + lr] = f2bf(S[kb4][r] - bf2f(hi));
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int j = kt + 16 * kb4 + 4 * lg + r;
+            if (!(ok && j < c1 && visible(j, lim, t0, mask))) S[kb4][r] = -INFINITY;
+          }
       }
-      __syncthreads();
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int k2 = 0; k2 < AKT / 32; ++k2) {
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, *(const u32x4*)&ps[0][w][lr][32 * k2 + 8 * lg]);
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)&ps[1][w][lr][32 * k2 + 8 * lg]);
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, S[kb4][r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      if (tmax > m + LAZY) {  // same decision in the four lanes of a query
+        const float alpha = exp2f(m - tmax);  // 0 when m = -inf
+        m = tmax;
+        lsum *= alpha;
+#pragma unroll
+        for (int b = 0; b < HD / 16; ++b) O[b] *= alpha;
+      }
+      bf16x8 ph[2], pl[2];
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = S[kb4][r] == -INFINITY ? 0.f : exp2f(S[kb4][r] - m);
+          lsum += p;
+          const __bf16 hi = (__bf16)p;
+          ph[kb4 >> 1][4 * (kb4 & 1) + r] = hi;
+          pl[kb4 >> 1][4 * (kb4 & 1) + r] = (__bf16)(p - (float)hi);
+        }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int b = 0; b < HD / 16; ++b) {
-          const bf16x8 vbf = __builtin_bit_cast(bf16x8, *(const u32x4*)&vt[16 * b + lr][32 * k2 + 8 * lg]);
-          O[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vbf, O[b], 0, 0, 0);
-          O[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vbf, O[b], 0, 0, 0);
+          const int dim = 16 * b + lr;
+          const u32x2 v0 = *(const u32x2*)&vt[vt_index(dim, 32 * k2 + 4 * lg)];
+          const u32x2 v1 = *(const u32x2*)&vt[vt_index(dim, 32 * k2 + 16 + 4 * lg)];
+          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+          O[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ph[k2], O[b], 0, 0, 0);
+          O[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl[k2], O[b], 0, 0, 0);
         }
-      }
     }
   }
-  // partials of the lane's four query vectors
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (v < nq) {
+    const size_t oi = ((size_t)sp * R + row) * Hq + h;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int v = qb * 64 + 16 * w + 4 * lg + r;
-    if (v >= nq) continue;
-    const size_t oi = ((size_t)sp * R + o_row[r]) * Hq + o_h[r];
-#pragma unroll
-    for (int b = 0; b < HD / 16; ++b) o_part[oi * HD + 16 * b + lr] = O[b][r];
-    if (lr == 0) {
-      ml_part[2 * oi] = m[r];
-      ml_part[2 * oi + 1] = l[r];
+    for (int b = 0; b < HD / 16; ++b)
+      *(f32x4*)&o_part[oi * HD + 16 * b + 4 * lg] = O[b];
+    if (lg == 0) {
+      ml_part[2 * oi] = m * LN2;
+      ml_part[2 * oi + 1] = lsum;
     }
   }
 }
@@ -296,15 +344,16 @@ void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t 
   if (bf16 && (hd == 64 || hd == 128) && rps > 0 && R % rps == 0) {
     const int G = Hq / Hkv;
     const int qblocks = (rps * G + 63) / 64;
-    dim3 grid((R / rps) * qblocks, Hkv, ns);
+    const int nwork = (R / rps) * qblocks * Hkv * ns;
+    const int nblocks = (nwork + 7) / 8 * 8;
     if (hd == 128)
-      k_attn_mfma<128><<<grid, 256, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
-                                             head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, rps, qblocks, Hq, Hkv,
-                                             key_bound, scale, ATT_CHUNK, o_part, ml_part);
+      k_attn_mfma<128><<<nblocks, 256, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
+                                                head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, rps, qblocks, Hq,
+                                                Hkv, ns, nwork, key_bound, scale, ATT_CHUNK, o_part, ml_part);
     else
-      k_attn_mfma<64><<<grid, 256, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
-                                            head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, rps, qblocks, Hq, Hkv,
-                                            key_bound, scale, ATT_CHUNK, o_part, ml_part);
+      k_attn_mfma<64><<<nblocks, 256, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
+                                               head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, rps, qblocks, Hq,
+                                               Hkv, ns, nwork, key_bound, scale, ATT_CHUNK, o_part, ml_part);
     k_attn_combine<bf16_t><<<dim3(R, Hq), 128, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, (bf16_t*)out);
     return;
   }

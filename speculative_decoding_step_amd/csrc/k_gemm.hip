@@ -46,27 +46,45 @@ __device__ __forceinline__ void seg_of(const GemmSegs& s, int tile, int& seg, in
   n0 = (tile - s.tiles0[seg]) * 64;
 }
 
-constexpr int KT = 256;       // K per LDS tile
-constexpr int KSTEPS = KT / 32;
-constexpr int XPAD = 8;       // bf16 elements of padding per LDS row
+constexpr int XPAD = 8;  // bf16 elements of padding per LDS row
 
-// MB = number of 16-row M blocks per workgroup (1 or 4).
+// Tile prefix over the stacked segments for a given tile height.
+struct TileMap {
+  int tiles0[4];
+};
+
+__host__ TileMap tile_map(const GemmSegs& s, int rows_per_tile) {
+  TileMap t;
+  t.tiles0[0] = 0;
+  for (int i = 0; i < 3; ++i)
+    t.tiles0[i + 1] = t.tiles0[i] + (i < s.nseg ? (s.rows[i] + rows_per_tile - 1) / rows_per_tile : 0);
+  return t;
+}
+
+// Skinny GEMM: MB 16-row activation blocks (M <= 16 MB per workgroup), each of
+// the 4 waves owns NB 16-row weight blocks, K in LDS tiles of KTT.
 // Work item lam = (m-tile, K split, N tile), m-tile fastest.  Workgroups are
 // dispatched round-robin over the 8 XCDs, so workgroup L runs item
 // (L % 8) * per + L / 8: the m-tiles of one weight tile land on the same XCD
 // back to back and re-read that tile from its L2 rather than from HBM.
-template <int MB>
-__global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X, int M, int K,
-                                                   GemmSegs segs, float* __restrict__ out, int ldo,
-                                                   size_t split_stride, int kchunk, int mtiles, int S, int nwork) {
-  __shared__ __attribute__((aligned(16))) bf16_t xs[16 * MB][KT + XPAD];
+template <int MB, int NB, int KTT>
+__global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
+                                                   TileMap tm, float* __restrict__ out, int ldo, size_t split_stride,
+                                                   int kchunk, int mtiles, int S, int nwork) {
+  constexpr int KS = KTT / 32;
+  constexpr int ROWS = 64 * NB;             // weight rows per workgroup
+  constexpr int CPR = KTT / 8;              // 16-byte chunks per activation row
+  constexpr int XCH = 16 * MB * CPR / 256;  // chunks per thread
+  static_assert(XCH * 256 == 16 * MB * CPR, "activation tile splits evenly over the threads");
+  __shared__ __attribute__((aligned(16))) bf16_t xs[16 * MB][KTT + XPAD];
   const int per = (nwork + 7) >> 3;
   const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (lam >= nwork) return;
   const int mt = lam % mtiles, rest = lam / mtiles;
   const int split = rest % S, ntile = rest / S;
-  int seg, n0;
-  seg_of(segs, ntile, seg, n0);
+  int seg = 0;
+  while (seg + 1 < segs.nseg && ntile >= tm.tiles0[seg + 1]) ++seg;
+  const int n0 = (ntile - tm.tiles0[seg]) * ROWS;
   const bf16_t* __restrict__ W = (const bf16_t*)segs.w[seg];
   const int nrows = segs.rows[seg];
   const int m0 = mt * 16 * MB;
@@ -75,28 +93,34 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X,
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
 
-  // weight fragment source: row n0 + 16*wv + lr, K offset 8*lg within each 32-step
-  const int wrow = n0 + 16 * wv + lr;
-  const bool wok = wrow < nrows;
-  const bf16_t* __restrict__ wp = W + (size_t)(wok ? wrow : 0) * K + 8 * lg;
-
-  // activation staging: chunk c = tid + 256*i covers row c/32, columns 8*(c%32)
-  constexpr int XCH = 2 * MB;  // 16-byte chunks per thread per tile
+  // weight fragment sources: rows n0 + 16 (NB wv + nb) + lr, K offset 8 lg in each 32-step
+  const bf16_t* wp[NB];
+  bool wok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = n0 + 16 * (NB * wv + nb) + lr;
+    wok[nb] = r < nrows;
+    wp[nb] = W + (size_t)(wok[nb] ? r : 0) * K + 8 * lg;
+  }
   u32x4 xr[XCH];
-  u32x4 wa[KSTEPS], wb[KSTEPS];
-  f32x4 acc[MB];
+  u32x4 wa[NB][KS], wb[NB][KS];
+  f32x4 acc[NB][MB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[nb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_w = [&](u32x4* dst, int kt) {
+  auto load_w = [&](u32x4 (*dst)[KS], int kt) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      dst[s] = wok ? *(const u32x4*)(wp + kt + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        dst[nb][s] = wok[nb] ? *(const u32x4*)(wp[nb] + kt + 32 * s) : u32x4{0u, 0u, 0u, 0u};
   };
   auto load_x = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int c = tid + 256 * i, row = c >> 5, col = (c & 31) * 8;
+      const int c = tid + 256 * i, row = c / CPR, col = (c % CPR) * 8;
       const int m = m0 + row;
       xr[i] = (m < M) ? *(const u32x4*)(X + (size_t)m * K + kt + col) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -104,7 +128,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X,
   auto store_x = [&]() {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int c = tid + 256 * i, row = c >> 5, col = (c & 31) * 8;
+      const int c = tid + 256 * i, row = c / CPR, col = (c % CPR) * 8;
       *(u32x4*)&xs[row][col] = xr[i];
     }
   };
@@ -113,41 +137,53 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X,
     load_w(wa, kb);
     load_x(kb);
   }
-  for (int kt = kb; kt < ke; kt += KT) {
+  for (int kt = kb; kt < ke; kt += KTT) {
     __syncthreads();
     store_x();
     __syncthreads();
-    const bool more = kt + KT < ke;
+    const bool more = kt + KTT < ke;
     if (more) {
-      load_w(wb, kt + KT);
-      load_x(kt + KT);
+      load_w(wb, kt + KTT);
+      load_x(kt + KTT);
     }
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8 b = __builtin_bit_cast(bf16x8, wa[s]);
+    for (int s = 0; s < KS; ++s) {
+      bf16x8 a[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)&xs[16 * mb + lr][32 * s + 8 * lg]);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb)
+        a[mb] = __builtin_bit_cast(bf16x8, *(const u32x4*)&xs[16 * mb + lr][32 * s + 8 * lg]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, wa[nb][s]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[nb][mb], 0, 0, 0);
       }
     }
     if (more) {
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) wa[s] = wb[s];
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) wa[nb][s] = wb[nb][s];
     }
   }
-  // result: acc[mb][r] = out[m0 + 16mb + 4lg + r][n0 + 16wv + lr]
-  if (!wok) return;
-  float* o = out + split * split_stride + segs.col0[seg] + wrow;
+  // result: acc[nb][mb][r] = out[m0 + 16 mb + 4 lg + r][n0 + 16 (NB wv + nb) + lr]
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
+  for (int nb = 0; nb < NB; ++nb) {
+    if (!wok[nb]) continue;
+    float* o = out + split * split_stride + segs.col0[seg] + n0 + 16 * (NB * wv + nb) + lr;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 16 * mb + 4 * lg + r;
-      if (m < M) o[(size_t)m * ldo] = acc[mb][r];
-    }
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * mb + 4 * lg + r;
+        if (m < M) o[(size_t)m * ldo] = acc[nb][mb][r];
+      }
   }
 }
+
+// K tile and weight rows per workgroup of the two skinny variants.
+constexpr int KT16 = 256, KT64 = 128;       // M <= 16: <1, 1, 256>; M <= 64: <4, 2, 128>
+constexpr int ROWS16 = 64, ROWS64 = 128;
 
 // Large-M GEMM (prefill chunks, batch-64 verify): 128 x 128 output tile per
 // workgroup, K in steps of 64 through double-buffered LDS for both operands.
@@ -289,8 +325,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ X, i
     }
 }
 
-int gemm_splits(bool bf16, int K, int splits) {
-  const int unit = bf16 ? KT : 32;
+int gemm_splits(bool bf16, int K, int splits, int m_tile) {
+  const int unit = !bf16 ? 32 : (m_tile == 16 ? KT16 : KT64);
   const int kt = (K + unit - 1) / unit;
   if (splits < 1) splits = 1;
   if (splits > kt) splits = kt;
@@ -298,12 +334,13 @@ int gemm_splits(bool bf16, int K, int splits) {
   return (kt + per - 1) / per;
 }
 
+int gemm_rows_per_tile(bool bf16, int m_tile) {
+  if (!bf16) return 64;
+  return m_tile == 16 ? ROWS16 : (m_tile == 64 ? ROWS64 : BT);
+}
+
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out, size_t split_stride,
          int splits, int m_tile, hipStream_t st) {
-  splits = gemm_splits(bf16, K, splits);
-  if (M <= 0) return splits;
-  const int ldo = gemm_ntot(segs);
-  const int ntiles = segs.tiles0[segs.nseg];
   if (bf16 && m_tile > 64) {
     BigTiles bt;
     bt.tiles0[0] = 0;
@@ -311,25 +348,31 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
     const int mtiles = (M + BT - 1) / BT;
     const int nwork = mtiles * bt.tiles0[segs.nseg];
     const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
-    k_gemm_bf16_big<<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, bt, out, ldo, mtiles, nwork);
+    if (M > 0) k_gemm_bf16_big<<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, bt, out, gemm_ntot(segs), mtiles, nwork);
     return 1;
   }
+  splits = gemm_splits(bf16, K, splits, m_tile);
+  if (M <= 0) return splits;
+  const int ldo = gemm_ntot(segs);
   if (bf16) {
-    // split K into `splits` chunks that are multiples of the LDS tile
-    const int ktiles = K / KT;
+    const int unit = m_tile == 16 ? KT16 : KT64;
+    const int ktiles = K / unit;
     const int per = (ktiles + splits - 1) / splits;
-    const int kchunk = per * KT;
+    const int kchunk = per * unit;
     const int S = (ktiles + per - 1) / per;
+    const TileMap tm = tile_map(segs, m_tile == 16 ? ROWS16 : ROWS64);
+    const int ntiles = tm.tiles0[segs.nseg];
     const int mtiles = (M + m_tile - 1) / m_tile;
     const int nwork = mtiles * S * ntiles;
     const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
     if (m_tile == 16)
-      k_gemm_bf16<1><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, out, ldo, split_stride, kchunk, mtiles, S,
-                                           nwork);
+      k_gemm_bf16<1, 1, KT16><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk,
+                                                     mtiles, S, nwork);
     else
-      k_gemm_bf16<4><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, out, ldo, split_stride, kchunk, mtiles, S,
-                                           nwork);
+      k_gemm_bf16<4, 2, KT64><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk,
+                                                     mtiles, S, nwork);
   } else {
+    const int ntiles = segs.tiles0[segs.nseg];
     const int per = ((K + 31) / 32 + splits - 1) / splits;
     const int kchunk = per * 32;
     const int S = (K + kchunk - 1) / kchunk;
@@ -346,9 +389,7 @@ __global__ void k_resid_add(float* __restrict__ x, const float* __restrict__ par
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (size_t)M * N) return;
   const int m = i / N, n = i % N;
-  float s = 0.f;
-  for (int k = 0; k < S; ++k) s += part[k * sstride + (size_t)m * ldp + n];
-  x[i] += s;
+  x[i] += sum_splits(part + (size_t)m * ldp + n, S, sstride);
 }
 
 __global__ void k_sum_store(float* __restrict__ out, const float* __restrict__ part, int S, size_t sstride,
@@ -356,8 +397,7 @@ __global__ void k_sum_store(float* __restrict__ out, const float* __restrict__ p
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (size_t)M * N) return;
   const int m = i / N, n = i % N;
-  float s = 0.f;
-  for (int k = 0; k < S; ++k) s += part[k * sstride + (size_t)m * ldp + n];
+  const float s = sum_splits(part + (size_t)m * ldp + n, S, sstride);
   out[i] = s;
 }
 
@@ -367,11 +407,8 @@ __global__ void k_silu_mul(T* __restrict__ out, const float* __restrict__ part, 
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (size_t)M * F) return;
   const int m = i / F, n = i % F;
-  float g = 0.f, u = 0.f;
-  for (int k = 0; k < S; ++k) {
-    g += part[k * sstride + (size_t)m * ldp + n];
-    u += part[k * sstride + (size_t)m * ldp + F + n];
-  }
+  const float g = sum_splits(part + (size_t)m * ldp + n, S, sstride);
+  const float u = sum_splits(part + (size_t)m * ldp + F + n, S, sstride);
   st<T>(out, i, g / (1.f + expf(-g)) * u);
 }
 

@@ -32,32 +32,108 @@ void embed_rows(bool bf16, const void* table, const int* tokens, float* x, int R
 }
 
 // -------------------------------------------------------------------- rmsnorm
-template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, const T* __restrict__ w,
-                                                 T* __restrict__ out, int out_ld, int d, float eps,
-                                                 T* __restrict__ tap, int tap_ld) {
+// One block per row, one float4 column group per thread (NV groups when the
+// row is wider than 4 * blockDim), so the whole row and all its split
+// partials are loaded at once.  Optional steps, in order:
+//   x[r] += sum_s part[s][r]   (the split-K partials of the preceding GEMM)
+//   tap[r] = T(x[r])           (the aux feature capture)
+//   out[r] = T(x[r] * rsqrt(mean(x^2) + eps) * w)
+template <typename T, int NV>
+__global__ __launch_bounds__(1024) void k_add_rmsnorm(float* __restrict__ x, const float* __restrict__ part, int S,
+                                                      size_t sstride, int ldp, const T* __restrict__ w,
+                                                      T* __restrict__ out, int out_ld, int d, float eps,
+                                                      T* __restrict__ tap, int tap_ld) {
   __shared__ float red[16];
-  const int r = blockIdx.x;
-  const float* xr = x + (size_t)r * d;
+  const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, d4 = d >> 2;
+  float4* xr = (float4*)(x + (size_t)r * d);
+  float4 v[NV];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    const float v = xr[i];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = tid + nt * i;
+    if (c < d4) {
+      v[i] = xr[c];
+      if (part) {
+        const float4 a = sum_splits4((const float4*)(part + (size_t)r * ldp) + c, S, sstride >> 2);
+        v[i].x += a.x; v[i].y += a.y; v[i].z += a.z; v[i].w += a.w;
+        xr[c] = v[i];
+      }
+      ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+      if (tap) {
+        T* tp = tap + (size_t)r * tap_ld + 4 * c;
+        st<T>(tp, 0, v[i].x); st<T>(tp, 1, v[i].y); st<T>(tp, 2, v[i].z); st<T>(tp, 3, v[i].w);
+      }
+    }
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = tid + nt * i;
+    if (c < d4) {
+      const int e = 4 * c;
+      T* op = out + (size_t)r * out_ld + e;
+      st<T>(op, 0, v[i].x * inv * ld<T>(w, e));
+      st<T>(op, 1, v[i].y * inv * ld<T>(w, e + 1));
+      st<T>(op, 2, v[i].z * inv * ld<T>(w, e + 2));
+      st<T>(op, 3, v[i].w * inv * ld<T>(w, e + 3));
+    }
+  }
+}
+
+// Rows whose width is not a multiple of 4 (or wider than 8192): element loop.
+template <typename T>
+__global__ __launch_bounds__(256) void k_add_rmsnorm_any(float* __restrict__ x, const float* __restrict__ part,
+                                                         int S, size_t sstride, int ldp, const T* __restrict__ w,
+                                                         T* __restrict__ out, int out_ld, int d, float eps,
+                                                         T* __restrict__ tap, int tap_ld) {
+  __shared__ float red[16];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  float* xr = x + (size_t)r * d;
+  float ss = 0.f;
+  for (int i = tid; i < d; i += 256) {
+    float v = xr[i];
+    if (part) {
+      v += sum_splits(part + (size_t)r * ldp + i, S, sstride);
+      xr[i] = v;
+    }
     ss += v * v;
     if (tap) st<T>(tap, (size_t)r * tap_ld + i, v);
   }
   ss = block_sum(ss, red);
   const float inv = 1.f / sqrtf(ss / (float)d + eps);
-  for (int i = threadIdx.x; i < d; i += blockDim.x)
-    st<T>(out, (size_t)r * out_ld + i, xr[i] * inv * ld<T>(w, i));
+  for (int i = tid; i < d; i += 256) st<T>(out, (size_t)r * out_ld + i, xr[i] * inv * ld<T>(w, i));
+}
+
+template <typename T>
+static void launch_add_rmsnorm(float* x, const float* part, int S, size_t sstride, int ldp, const T* w, T* out,
+                               int out_ld, int R, int d, float eps, T* tap, int tap_ld, hipStream_t st) {
+  const int d4 = d / 4;
+  if (d % 4 == 0 && d4 <= 2048) {
+    const int nt = std::min(1024, (d4 + 63) / 64 * 64);
+    if (d4 <= nt)
+      k_add_rmsnorm<T, 1><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld);
+    else
+      k_add_rmsnorm<T, 2><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld);
+  } else {
+    k_add_rmsnorm_any<T><<<R, 256, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld);
+  }
+}
+
+void add_rmsnorm(bool bf16, float* x, const float* part, int S, size_t sstride, int ldp, const void* w, void* out,
+                 int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st) {
+  if (R <= 0) return;
+  if (bf16)
+    launch_add_rmsnorm<bf16_t>(x, part, S, sstride, ldp, (const bf16_t*)w, (bf16_t*)out, out_ld, R, d, eps,
+                               (bf16_t*)tap, tap_ld, st);
+  else
+    launch_add_rmsnorm<float>(x, part, S, sstride, ldp, (const float*)w, (float*)out, out_ld, R, d, eps,
+                              (float*)tap, tap_ld, st);
 }
 
 void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, int R, int d, float eps, void* tap,
              int tap_ld, hipStream_t st) {
-  if (R <= 0) return;
-  if (bf16)
-    k_rmsnorm<bf16_t><<<R, 256, 0, st>>>(x, (const bf16_t*)w, (bf16_t*)out, out_ld, d, eps, (bf16_t*)tap, tap_ld);
-  else
-    k_rmsnorm<float><<<R, 256, 0, st>>>(x, (const float*)w, (float*)out, out_ld, d, eps, (float*)tap, tap_ld);
+  add_rmsnorm(bf16, (float*)x, nullptr, 0, 0, 0, w, out, out_ld, R, d, eps, tap, tap_ld, st);
 }
 
 // ---------------------------------------------------------------- draft input
@@ -117,11 +193,7 @@ __global__ __launch_bounds__(64) void k_rope_kv(const float* __restrict__ part, 
   const int ncol = (Hq + 2 * Hkv) * hd;
   const int half = hd / 2;
   const float* pr = part + (size_t)r * ncol + (size_t)h * hd;
-  auto val = [&](int c) {
-    float s = 0.f;
-    for (int k = 0; k < S; ++k) s += pr[k * sstride + c];
-    return s;
-  };
+  auto val = [&](int c) { return sum_splits(pr + c, S, sstride); };
   if (h >= Hq + Hkv) {  // V: copy
     if (b < 0) return;
     T* vp = vc + (size_t)b * seq_stride + (size_t)(h - Hq - Hkv) * head_stride + (size_t)rslot[r] * hd;

@@ -26,7 +26,9 @@ GemmSegs make_segs(const void* w0, int r0, const void* w1 = nullptr, int r1 = 0,
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out,
          size_t split_stride, int splits, int m_tile, hipStream_t st);
 // Number of K splits gemm() will actually use for a requested count.
-int gemm_splits(bool bf16, int K, int splits);
+int gemm_splits(bool bf16, int K, int splits, int m_tile);
+// Weight rows per workgroup of the kernel gemm() picks.
+int gemm_rows_per_tile(bool bf16, int m_tile);
 int gemm_ntot(const GemmSegs& s);
 
 // Consumers of split partials part[s][m][ldp].
@@ -39,6 +41,9 @@ void sum_store(float* out, const float* part, int S, size_t sstride, int M, int 
 void embed_rows(bool bf16, const void* table, const int* tokens, float* x, int R, int d, int V,
                 int* status, hipStream_t st);
 // out[r] = T(x[r] * rsqrt(mean(x^2)+eps) * w); if tap != null also tap[r*tap_ld] = T(x[r]).
+// add_rmsnorm first adds the S split partials part[s][r][0..d) (row stride ldp) into x.
+void add_rmsnorm(bool bf16, float* x, const float* part, int S, size_t sstride, int ldp, const void* w, void* out,
+                 int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st);
 void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, int R, int d, float eps,
              void* tap, int tap_ld, hipStream_t st);
 // Draft input: out[r] = [T(rms(embed[tok[r]]) * w_in) ; T(rms(x[r]) * w_hid)], [R, 2d].
