@@ -173,6 +173,21 @@ def cpu_baseline(w):
                        f"(+{t_gen:.0f}s generating the slice's seeded weights)")}
 
 
+def copy_probe(mib):
+    """Five copies of a MIB-MiB device buffer into another: each dispatch reads and
+    writes exactly mib * 2^20 bytes."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,7 +195,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_tree_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the reference point that "
+                         "scales the HBM byte counters of a profiler run) and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the step shards by sequence "
               "with no exchange; run one process per GPU). Use --gpus 1.", file=sys.stderr)
@@ -211,7 +232,7 @@ def main():
                    "topk": w.topk, "tree_nodes": w.n_nodes, "rows_per_step": rows},
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
-                     "kernel": "k_gemm_bf16<4,2,128> (64-row MFMA weight-streaming GEMM)",
+                     "kernel": "k_gemm_bf16<4,1,128,8> (64-row MFMA weight-streaming GEMM)",
                      "launches_per_step": n64 / args.steps,
                      "kernel_ms_per_step": round(t64 / args.steps, 4)},
         "hbm_gbps_step": None,

@@ -295,12 +295,13 @@ void prof_end(eagle3_ctx* c, ProfRec* rec) {
 // ----------------------------------------------------------------- GEMM plan
 int plan_splits(eagle3_ctx* c, int M, int N, int K, int m_tile) {
   if (!c->bf16) return 1;
-  // about 512 workgroups in flight: enough to cover 256 CUs without a tail
   const int rows = gemm_rows_per_tile(true, m_tile);
   const int tiles = ((N + rows - 1) / rows) * ((M + m_tile - 1) / m_tile);
-  // about 512 workgroups, but at most 8 splits: every split adds M x N fp32
-  // partials that the consumer kernel reads back
-  int S = (512 + tiles / 2) / tiles;
+  // about 256 eight-wave (M <= 64) or 512 four-wave (M <= 16) workgroups, but
+  // at most 8 splits: every split adds M x N fp32 partials that the consumer
+  // kernel reads back
+  const int target = m_tile == 16 ? 512 : 256;
+  int S = (target + tiles / 2) / tiles;
   S = std::max(1, std::min(8, S));
   const int mpad = (M + m_tile - 1) / m_tile * m_tile;
   while (S > 1 && (size_t)S * mpad * N > c->part_elems) --S;

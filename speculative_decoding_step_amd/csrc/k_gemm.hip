@@ -62,21 +62,23 @@ __host__ TileMap tile_map(const GemmSegs& s, int rows_per_tile) {
 }
 
 // Skinny GEMM: MB 16-row activation blocks (M <= 16 MB per workgroup), each of
-// the 4 waves owns NB 16-row weight blocks, K in LDS tiles of KTT.
+// the NW waves owns NB 16-row weight blocks, K in LDS tiles of KTT.  K must be
+// a multiple of KTT (the shapes are checked on the host).
 // Work item lam = (m-tile, K split, N tile), m-tile fastest.  Workgroups are
 // dispatched round-robin over the 8 XCDs, so workgroup L runs item
 // (L % 8) * per + L / 8: the m-tiles of one weight tile land on the same XCD
 // back to back and re-read that tile from its L2 rather than from HBM.
-template <int MB, int NB, int KTT>
-__global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
+template <int MB, int NB, int KTT, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
                                                    TileMap tm, float* __restrict__ out, int ldo, size_t split_stride,
                                                    int kchunk, int mtiles, int S, int nwork) {
   constexpr int KS = KTT / 32;
-  constexpr int ROWS = 64 * NB;             // weight rows per workgroup
+  constexpr int NT = 64 * NW;               // threads
+  constexpr int ROWS = 16 * NB * NW;        // weight rows per workgroup
   constexpr int CPR = KTT / 8;              // 16-byte chunks per activation row
-  constexpr int XCH = 16 * MB * CPR / 256;  // chunks per thread
-  static_assert(XCH * 256 == 16 * MB * CPR, "activation tile splits evenly over the threads");
-  __shared__ __attribute__((aligned(16))) bf16_t xs[16 * MB][KTT + XPAD];
+  constexpr int XCH = 16 * MB * CPR / NT;   // chunks per thread
+  static_assert(XCH * NT == 16 * MB * CPR, "activation tile splits evenly over the threads");
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2][16 * MB][KTT + XPAD];
   const int per = (nwork + 7) >> 3;
   const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (lam >= nwork) return;
@@ -93,7 +95,9 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X,
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
 
-  // weight fragment sources: rows n0 + 16 (NB wv + nb) + lr, K offset 8 lg in each 32-step
+  // weight fragment sources: rows n0 + 16 (NB wv + nb) + lr, K offset 8 lg in each 32-step.
+  // Rows past the segment read row 0 instead (their results are not stored),
+  // and activation rows past M repeat row M - 1, so every load is unconditional.
   const bf16_t* wp[NB];
   bool wok[NB];
 #pragma unroll
@@ -102,69 +106,93 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X,
     wok[nb] = r < nrows;
     wp[nb] = W + (size_t)(wok[nb] ? r : 0) * K + 8 * lg;
   }
-  u32x4 xr[XCH];
-  u32x4 wa[NB][KS], wb[NB][KS];
+  const bf16_t* xp[XCH];
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int c = tid + NT * i, row = c / CPR, col = (c % CPR) * 8;
+    xp[i] = X + (size_t)min(m0 + row, M - 1) * K + col;
+  }
+  u32x4 x0[XCH], x1[XCH];
+  u32x4 w0[NB][KS], w1[NB][KS], w2[NB][KS];
   f32x4 acc[NB][MB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int i = 0; i < MB; ++i) acc[nb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_w = [&](u32x4 (*dst)[KS], int kt) {
+  auto load_w = [&](u32x4 (&dst)[NB][KS], int kt) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        dst[nb][s] = wok[nb] ? *(const u32x4*)(wp[nb] + kt + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < KS; ++s) dst[nb][s] = *(const u32x4*)(wp[nb] + kt + 32 * s);
   };
-  auto load_x = [&](int kt) {
+  auto load_x = [&](u32x4 (&dst)[XCH], int kt) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) dst[i] = *(const u32x4*)(xp[i] + kt);
+  };
+  auto store_x = [&](const u32x4 (&src)[XCH], int buf) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int c = tid + 256 * i, row = c / CPR, col = (c % CPR) * 8;
-      const int m = m0 + row;
-      xr[i] = (m < M) ? *(const u32x4*)(X + (size_t)m * K + kt + col) : u32x4{0u, 0u, 0u, 0u};
+      const int c = tid + NT * i, row = c / CPR, col = (c % CPR) * 8;
+      *(u32x4*)&xs[buf][row][col] = src[i];
     }
   };
-  auto store_x = [&]() {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int c = tid + 256 * i, row = c / CPR, col = (c % CPR) * 8;
-      *(u32x4*)&xs[row][col] = xr[i];
-    }
-  };
-
-  if (kb < ke) {
-    load_w(wa, kb);
-    load_x(kb);
-  }
-  for (int kt = kb; kt < ke; kt += KTT) {
-    __syncthreads();
-    store_x();
-    __syncthreads();
-    const bool more = kt + KTT < ke;
-    if (more) {
-      load_w(wb, kt + KTT);
-      load_x(kt + KTT);
-    }
+  auto mul = [&](const u32x4 (&wc)[NB][KS], int buf) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       bf16x8 a[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        a[mb] = __builtin_bit_cast(bf16x8, *(const u32x4*)&xs[16 * mb + lr][32 * s + 8 * lg]);
+        a[mb] = __builtin_bit_cast(bf16x8, *(const u32x4*)&xs[buf][16 * mb + lr][32 * s + 8 * lg]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, wa[nb][s]);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, wc[nb][s]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[nb][mb], 0, 0, 0);
+        for (int mb = 0; mb < MB; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[nb][mb], 0, 0, 0);
       }
     }
-    if (more) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) wa[nb][s] = wb[nb][s];
+  };
+  // Pipeline over K steps of KTT.  Weights: three register buffers, so while
+  // step i is multiplied, steps i + 1 and i + 2 are in flight.  Activations:
+  // two register buffers and two LDS tiles; the tile of step i + 1 is written
+  // to LDS at the end of step i (its loads were issued a step earlier), and one
+  // barrier per step both publishes it and retires the tile just read.  Past
+  // the last step the loads repeat the last step's addresses.
+  const int nsteps = (ke - kb) / KTT;
+  const int klast = kb + (nsteps - 1) * KTT;
+  auto step = [&](int i, const u32x4 (&cur)[NB][KS], u32x4 (&ahead)[NB][KS], const u32x4 (&xnext)[XCH],
+                  u32x4 (&xafter)[XCH]) {
+    // xnext holds the activations of step i + 1; xafter receives those of step i + 2
+    load_x(xafter, min(kb + (i + 2) * KTT, klast));
+    load_w(ahead, min(kb + (i + 2) * KTT, klast));
+    __builtin_amdgcn_sched_barrier(0);  // issue the loads before the multiplies
+    mul(cur, i & 1);
+    store_x(xnext, (i + 1) & 1);
+    __syncthreads();
+  };
+  if (nsteps > 0) {
+    load_x(x0, kb);
+    load_x(x1, min(kb + KTT, klast));
+    load_w(w0, kb);
+    load_w(w1, min(kb + KTT, klast));
+    store_x(x0, 0);
+    __syncthreads();
+    int i = 0;
+    for (; i + 6 <= nsteps; i += 6) {
+      step(i, w0, w2, x1, x0);
+      step(i + 1, w1, w0, x0, x1);
+      step(i + 2, w2, w1, x1, x0);
+      step(i + 3, w0, w2, x0, x1);
+      step(i + 4, w1, w0, x1, x0);
+      step(i + 5, w2, w1, x0, x1);
     }
+    // remaining steps: the buffer roles continue from i (a multiple of 6)
+    if (i < nsteps) step(i, w0, w2, x1, x0);
+    if (i + 1 < nsteps) step(i + 1, w1, w0, x0, x1);
+    if (i + 2 < nsteps) step(i + 2, w2, w1, x1, x0);
+    if (i + 3 < nsteps) step(i + 3, w0, w2, x0, x1);
+    if (i + 4 < nsteps) step(i + 4, w1, w0, x1, x0);
   }
   // result: acc[nb][mb][r] = out[m0 + 16 mb + 4 lg + r][n0 + 16 (NB wv + nb) + lr]
 #pragma unroll
@@ -181,9 +209,10 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(const bf16_t* __restrict__ X,
   }
 }
 
-// K tile and weight rows per workgroup of the two skinny variants.
-constexpr int KT16 = 256, KT64 = 128;       // M <= 16: <1, 1, 256>; M <= 64: <4, 2, 128>
-constexpr int ROWS16 = 64, ROWS64 = 128;
+// K tile and weight rows per workgroup of the two skinny variants:
+// M <= 16: <MB 1, NB 2, KTT 256, 4 waves>; M <= 64: <MB 4, NB 1, KTT 128, 8 waves>.
+constexpr int KT16 = 256, KT64 = 128;
+constexpr int ROWS16 = 16 * 2 * 4, ROWS64 = 16 * 1 * 8;
 
 // Large-M GEMM (prefill chunks, batch-64 verify): 128 x 128 output tile per
 // workgroup, K in steps of 64 through double-buffered LDS for both operands.
@@ -366,10 +395,10 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
     const int nwork = mtiles * S * ntiles;
     const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
     if (m_tile == 16)
-      k_gemm_bf16<1, 1, KT16><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk,
+      k_gemm_bf16<1, 2, KT16, 4><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk,
                                                      mtiles, S, nwork);
     else
-      k_gemm_bf16<4, 2, KT64><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk,
+      k_gemm_bf16<4, 1, KT64, 8><<<grid, 512, 0, st>>>((const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk,
                                                      mtiles, S, nwork);
   } else {
     const int ntiles = segs.tiles0[segs.nseg];
