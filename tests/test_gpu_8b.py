@@ -1,16 +1,22 @@
-"""Full-size parity at the 8B shape, in the launch configuration bench.py times.
+"""Full-size parity at the 8B shape, in the launch configurations bench.py times.
 
-The oracle cannot run all 32 layers at this size in a test, so the check takes
-the outputs it can compute one by one: with the prompt (2048 tokens) prefilled
-on the GPU, a 61-row tree is verified through the C ABI and its tap entering
-layer 2 (hidden_states[2]) and the K/V written by layers 0 and 1 are compared
-with the oracle run on the model's first two layers (same seeded weights)."""
+The oracle cannot run all 32 layers at this size in a test, so the checks take
+the outputs it can compute one by one: K/V written by layers 0 and 1 and the
+tap entering layer 2 (hidden_states[2]) are compared with the oracle run on the
+model's first two layers (same seeded weights), and every integer result of a
+step (tree topology and masks, accepted paths, rejection-sampling decisions,
+compaction) is checked bit-exactly against the oracle given the GPU's own
+logits, over every sequence of the batch."""
+import functools
+
 import numpy as np
 import pytest
 import torch
 
 from gpu_util import kv_view, random_tree, to_dev
+from oracle.accept import chain_rejection, greedy_walk
 from oracle.llama import KVCache, Shape, causal_visible, target_forward
+from oracle.numerics import probs_f32, sample_inverse_cdf
 from oracle.tree import mask_words, tree_mask
 from speculative_decoding_step_amd import binding as B
 from speculative_decoding_step_amd import configs, synth
@@ -25,6 +31,72 @@ def _p(t):
 
 def _gen(seed, name, shape):
     return synth.normal_t(seed, name, shape, "cuda", 0.02, "bf16").to(torch.float64).cpu().numpy()
+
+
+@functools.lru_cache(maxsize=1)
+def _two_layer_weights(seed):
+    ms = configs.L8B
+    d = ms.d
+    qd, kvd = ms.n_heads * ms.head_dim, ms.n_kv_heads * ms.head_dim
+    layers = []
+    for l in range(2):
+        L = {"attn_norm": np.ones(d), "ffn_norm": np.ones(d)}
+        for key, shape in [("wq", (qd, d)), ("wk", (kvd, d)), ("wv", (kvd, d)), ("wo", (d, qd)),
+                           ("w_gate", (ms.ffn, d)), ("w_up", (ms.ffn, d)), ("w_down", (d, ms.ffn))]:
+            L[key] = _gen(seed, f"l{l}.{key}", shape)
+        layers.append(L)
+    return layers
+
+
+def _two_layer_oracle(seed, prompt, tokens, parents):
+    """Oracle on target layers 0 and 1 for a prompt and a tree after it.
+
+    Returns (prompt K [2][P, Hkv, hd], tree K, tree V [2][n, Hkv, hd], tree rows
+    of hidden_states[2] [n, d]).  Tokens are remapped onto the embedding rows
+    they use so that only those rows are materialised."""
+    ms = configs.L8B
+    d, P, n = ms.d, len(prompt), len(tokens)
+    used = sorted(set(int(t) for t in prompt) | set(int(t) for t in tokens))
+    remap = {t: i for i, t in enumerate(used)}
+    emb = synth.normal_t(seed, "embed", (ms.vocab, d), "cuda", 0.02, "bf16")
+    W = {"embed": emb[torch.as_tensor(used, device="cuda")].to(torch.float64).cpu().numpy(),
+         "final_norm": np.ones(d), "lm_head": np.zeros((1, d)), "layers": _two_layer_weights(seed)}
+    del emb
+    shp = Shape(2, d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, 1, ms.rope_theta, ms.eps, "bf16", (2, 2, 2))
+    cache = KVCache(2, P + n + 1, ms.n_kv_heads, ms.head_dim)
+    _, k, v, _ = target_forward(W, shp, cache, [remap[int(t)] for t in prompt], np.arange(P), causal_visible(P))
+    for l in range(2):
+        cache.k[l][:P], cache.v[l][:P] = k[l], v[l]
+    cache.length = P
+    dep = [0] * n
+    for i in range(1, n):
+        dep[i] = dep[parents[i]] + 1
+    m = tree_mask(parents)
+    _, tk, tv, aux = target_forward(W, shp, cache, [remap[int(t)] for t in tokens], P + np.array(dep),
+                                    [list(np.nonzero(m[i])[0]) for i in range(n)])
+    return k, tk, tv, aux[:, :d]
+
+
+def _close(g, ref, what):
+    e = np.abs(np.asarray(g, dtype=np.float64) - ref).max()
+    scale = np.abs(ref).max()
+    assert e <= 1e-2 * scale, (what, e, scale)
+    return e, scale
+
+
+def _check_tree(P, tokens, parents, depth, pos, mask, D):
+    """Topology of one drafted tree: BFS order, depths, positions, ancestry masks, distinct siblings."""
+    n = len(tokens)
+    assert parents[0] == -1 and depth[0] == 0 and pos[0] == P
+    for i in range(1, n):
+        assert 0 <= parents[i] < i
+        assert depth[i] == depth[parents[i]] + 1 <= D
+        assert depth[i] >= depth[i - 1]
+        assert pos[i] == P + depth[i]
+    assert np.array_equal(np.asarray(mask, dtype=np.uint64), mask_words(list(parents)))
+    for i in range(n):
+        kids = [tokens[c] for c in range(n) if parents[c] == i]
+        assert len(kids) == len(set(kids))
 
 
 def test_8b_tree_verify_first_two_layers_vs_oracle():
@@ -59,37 +131,122 @@ def test_8b_tree_verify_first_two_layers_vs_oracle():
     del eng
     torch.cuda.empty_cache()
 
-    # oracle on layers 0 and 1 (tokens remapped onto the embedding rows they use)
-    used = sorted(set(int(t) for t in prompt) | set(tokens))
-    remap = {t: i for i, t in enumerate(used)}
-    emb = synth.normal_t(w.target_seed, "embed", (ms.vocab, d), "cuda", 0.02, "bf16")
-    W = {"embed": emb[torch.as_tensor(used, device="cuda")].to(torch.float64).cpu().numpy(),
-         "final_norm": np.ones(d), "lm_head": np.zeros((1, d)), "layers": []}
-    del emb
-    qd, kvd = ms.n_heads * ms.head_dim, ms.n_kv_heads * ms.head_dim
+    k, tk, tv, aux = _two_layer_oracle(w.target_seed, prompt, tokens, parents)
+    e, scale = _close(g_aux, aux, "tap 2")
+    print(f"  tap-2 max err {e:.3g} (scale {scale:.3g})", flush=True)
     for l in range(2):
-        L = {"attn_norm": np.ones(d), "ffn_norm": np.ones(d)}
-        for key, shape in [("wq", (qd, d)), ("wk", (kvd, d)), ("wv", (kvd, d)), ("wo", (d, qd)),
-                           ("w_gate", (ms.ffn, d)), ("w_up", (ms.ffn, d)), ("w_down", (d, ms.ffn))]:
-            L[key] = _gen(w.target_seed, f"l{l}.{key}", shape)
-        W["layers"].append(L)
-    shp = Shape(2, d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, 1, ms.rope_theta, ms.eps, "bf16", (2, 2, 2))
-    cache = KVCache(2, P + n + 1, ms.n_kv_heads, ms.head_dim)
-    pr = [remap[int(t)] for t in prompt]
-    _, k, v, _ = target_forward(W, shp, cache, pr, np.arange(P), causal_visible(P))
+        _close(g_tree_k[l].transpose(1, 0, 2), tk[l], ("tree K", l))
+        _close(g_tree_v[l].transpose(1, 0, 2), tv[l], ("tree V", l))
+        _close(g_pre_k[l].transpose(1, 0, 2), k[l][sample_pos], ("prompt K", l))
+
+
+def test_8b_batch64_ragged_tree_step():
+    """Batch 64 with ragged prompts in [128, 4096] and a depth-4, top-4, 16-node
+    tree (1088 verify rows): one whole step.  All 64 trees, accepted paths and
+    compactions are checked exactly; verify K/V and taps of the shortest and
+    the longest sequence against the two-layer oracle."""
+    w = configs.WORKLOADS["llama8b_tree_b64"]
+    ms, Bn, n, D = w.shape, w.batch, w.rows, w.depth
+    prompts = configs.prompts_np(w)
+    lens = np.array([len(p) for p in prompts])
+    print(f"\n[8B batch {Bn}] prompt lengths {lens.min()}..{lens.max()} rows {Bn * n}", flush=True)
+    eng = Engine(ms, Spec.of(w), Bn, int(lens.max()) + 64, w.target_seed, w.head_seed, prefill_chunk=512)
+    eng.prefill(prompts)
+    torch.cuda.synchronize()
+    print("  prefill done", flush=True)
+    eng.draft()
+    eng.verify()
+    eng.accept()
+    torch.cuda.synchronize()
+    assert eng.device_status() == 0
+    tokens, parents = eng.tokens.cpu().numpy(), eng.parents.cpu().numpy()
+    depth, pos = eng.depth.cpu().numpy(), eng.pos.cpu().numpy()
+    mask = eng.mask.cpu().numpy().view(np.uint64)
+    am = eng.argmax.cpu().numpy().reshape(Bn, n)
+    path, plen = eng.path.cpu().numpy(), eng.path_len.cpu().numpy()
+    nroot, emitted = eng.next_root.cpu().numpy(), eng.emitted.cpu().numpy()
+    aux_tree = eng.aux_tree[:, :, :ms.d].float().cpu().numpy()
+    kv = kv_view(eng)
+    layers = [0, 1, ms.n_layers - 1]
+    pre = [kv[layers, :, b, :, int(lens[b]):int(lens[b]) + n].clone() for b in range(Bn)]
+    eng.compact()
+    torch.cuda.synchronize()
+    assert eng.device_status() == 0
+    seq_after = eng.seq_lens.cpu().numpy()
+    for b in range(Bn):
+        P = int(lens[b])
+        _check_tree(P, tokens[b], parents[b], depth[b], pos[b], mask[b], D)
+        walk, nxt = greedy_walk(list(tokens[b]), list(parents[b]), list(am[b]))
+        assert list(path[b, :plen[b]]) == walk and nroot[b] == nxt
+        assert list(emitted[b, :plen[b]]) == [int(tokens[b][i]) for i in walk]
+        assert seq_after[b] == P + plen[b]
+        moved = kv[layers, :, b, :, P:P + int(plen[b])]
+        assert torch.equal(moved, pre[b][..., torch.as_tensor(walk, device="cuda"), :])
+    print(f"  path lengths {np.bincount(plen)}", flush=True)
+    checks = [int(np.argmin(lens)), int(np.argmax(lens))]
+    g_tree = {b: pre[b][:2].float().cpu().numpy() for b in checks}    # [2 layers, K/V, Hkv, n, hd]
+    eng.close()
+    del eng, pre, kv
+    torch.cuda.empty_cache()
+    for b in checks:
+        k, tk, tv, aux = _two_layer_oracle(w.target_seed, prompts[b], tokens[b], list(parents[b]))
+        e, _ = _close(aux_tree[b], aux, ("tap 2", b))
+        for l in range(2):
+            _close(g_tree[b][l, 0].transpose(1, 0, 2), tk[l], ("tree K", b, l))
+            _close(g_tree[b][l, 1].transpose(1, 0, 2), tv[l], ("tree V", b, l))
+        print(f"  seq {b} (P={lens[b]}): tap-2 err {e:.3g}", flush=True)
+
+
+def test_8b_sampling_chain_b4_steps():
+    """Temperature-1 chain (K = 5) at batch 4, prompts of 64: two whole steps.
+    Each draft token must be the inverse-CDF draw from the q row the draft
+    produced, and every acceptance decision, resample and bonus must equal the
+    oracle's rejection sampler given the GPU's p (from its verify logits), q and
+    uniforms; the chain rows' layer-0/1 K/V match the two-layer oracle."""
+    w = configs.WORKLOADS["llama8b_sample_chain_b4"]
+    ms, Bn, K = w.shape, w.batch, w.depth
+    prompts = configs.prompts_np(w)
+    eng = Engine(ms, Spec.of(w), Bn, w.max_len, w.target_seed, w.head_seed, prefill_chunk=512)
+    print(f"\n[8B sampling chain] batch {Bn} K={K}", flush=True)
+    eng.prefill(prompts, synth.uniform24_t(5000, "u_root", Bn, "cuda"))
+    seen = set()
+    for s in range(2):
+        u_d = synth.uniform24_t(5000, f"u_draft{s}", Bn * K, "cuda").view(Bn, K)
+        u_a = synth.uniform24_t(5000, f"u_accept{s}", Bn * (K + 1), "cuda").view(Bn, K + 1)
+        eng.set_uniforms(u_d, u_a)
+        P = eng.seq_lens.cpu().numpy()
+        eng.draft()
+        eng.verify()
+        eng.accept()
+        torch.cuda.synchronize()
+        assert eng.device_status() == 0
+        toks, par = eng.tokens.cpu().numpy(), eng.parents.cpu().numpy()
+        q = eng.q.cpu().numpy()
+        lg = eng.logits.cpu().numpy().reshape(Bn, K + 1, ms.vocab)
+        ud, ua = u_d.cpu().numpy(), u_a.cpu().numpy()
+        plen, nroot, em = eng.path_len.cpu().numpy(), eng.next_root.cpu().numpy(), eng.emitted.cpu().numpy()
+        if s == 0:
+            chain_kv = kv_view(eng)[:2, :, 0, :, int(P[0]):int(P[0]) + K + 1].float().cpu().numpy()
+            chain0 = [int(t) for t in toks[0]]
+        for b in range(Bn):
+            assert list(par[b]) == list(range(-1, K))
+            assert list(eng.pos[b].cpu().numpy()) == [int(P[b]) + i for i in range(K + 1)]
+            for i in range(K):
+                assert abs(float(q[b, i].astype(np.float64).sum()) - 1.0) < 1e-4
+                assert toks[b, i + 1] == sample_inverse_cdf(q[b, i], ud[b, i])
+            p = np.stack([probs_f32(lg[b, i], 1.0) for i in range(K + 1)])
+            n_acc, tok = chain_rejection(toks[b, 1:], q[b], p, ua[b])
+            seen.add(n_acc)
+            assert plen[b] == n_acc + 1 and nroot[b] == tok
+            assert list(em[b]) == [int(x) for x in toks[b, :n_acc + 1]] + [-1] * (K - n_acc)
+        eng.compact()
+        torch.cuda.synchronize()
+        assert list(eng.seq_lens.cpu().numpy()) == [int(P[b]) + int(plen[b]) for b in range(Bn)]
+    print(f"  accepted counts seen {sorted(seen)}", flush=True)
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    k, tk, tv, _ = _two_layer_oracle(w.target_seed, prompts[0], chain0, list(range(-1, K)))
     for l in range(2):
-        cache.k[l][:P], cache.v[l][:P] = k[l], v[l]
-    cache.length = P
-    m = tree_mask(parents)
-    _, tk, tv, aux = target_forward(W, shp, cache, [remap[t] for t in tokens], P + np.array(dep),
-                                    [list(np.nonzero(m[i])[0]) for i in range(n)])
-    scale = np.abs(aux[:, :d]).max()
-    err = np.abs(g_aux - aux[:, :d]).max()
-    print(f"  tap-2 max err {err:.3g} (scale {scale:.3g})", flush=True)
-    assert err <= 1e-2 * scale
-    for l in range(2):
-        for g, ref in [(g_tree_k[l], tk[l]), (g_tree_v[l], tv[l])]:
-            e = np.abs(g.transpose(1, 0, 2) - ref).max()
-            assert e <= 1e-2 * np.abs(ref).max(), (l, e)
-        e = np.abs(g_pre_k[l].transpose(1, 0, 2) - k[l][sample_pos]).max()
-        assert e <= 1e-2 * np.abs(k[l][sample_pos]).max(), (l, e)
+        _close(chain_kv[l, 0].transpose(1, 0, 2), tk[l], ("chain K", l))
+        _close(chain_kv[l, 1].transpose(1, 0, 2), tv[l], ("chain V", l))
