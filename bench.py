@@ -41,7 +41,14 @@ def run_gpu(w, steps, warmup):
     eng = Engine(w.shape, Spec.of(w), w.batch, max_seq_for(w, 2 * (steps + warmup)), w.target_seed, w.head_seed,
                  prefill_chunk=512)
     print(f"[bench] weights + context ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    eng.prefill(prompts)
+    if eng.sampling:                             # seeded uniforms, fixed across the replays
+        from speculative_decoding_step_amd import synth
+        K = w.depth
+        eng.prefill(prompts, synth.uniform24_t(5000, "u_root", w.batch, "cuda"))
+        eng.set_uniforms(synth.uniform24_t(5000, "u_draft", w.batch * K, "cuda").view(w.batch, K),
+                         synth.uniform24_t(5000, "u_accept", w.batch * (K + 1), "cuda").view(w.batch, K + 1))
+    else:
+        eng.prefill(prompts)
     torch.cuda.synchronize()
     print(f"[bench] prefill done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     eng.step()                                   # one eager step, then capture
@@ -62,7 +69,8 @@ def run_gpu(w, steps, warmup):
         eng.step()
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
-    prof = {k: B.eagle3_profile_read(eng.ctx, k) for k in (B.PROF_GEMM_M64, B.PROF_GEMM_M16, B.PROF_ATTN)}
+    prof = {k: B.eagle3_profile_read(eng.ctx, k)
+            for k in (B.PROF_GEMM_M64, B.PROF_GEMM_M16, B.PROF_ATTN, B.PROF_GEMM_BIG)}
     B.eagle3_profile(eng.ctx, False)
     status = eng.device_status()
     if status:
@@ -173,6 +181,106 @@ def cpu_baseline(w):
                        f"(+{t_gen:.0f}s generating the slice's seeded weights)")}
 
 
+KERNEL_NAMES = {
+    0: "k_gemm_bf16<4,1,128,8> (64-row MFMA weight-streaming GEMM)",
+    1: "k_gemm_bf16<1,2,256,4> (16-row MFMA weight-streaming GEMM)",
+    3: "k_gemm_bf16_big (128x128-tile MFMA GEMM)",
+}
+
+
+def step_bytes(w):
+    """Algorithmic HBM bytes of one step: every weight the step's passes read
+    (target layers + LM head once; draft FC once; draft layer + LM head per draft
+    forward, depth forwards per step) plus the K/V the attention reads."""
+    import numpy as np
+
+    from speculative_decoding_step_amd import configs
+
+    s = w.shape
+    e = 2 if s.dtype == "bf16" else 4
+    q, kv = s.n_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    tgt_layer = s.d * q + 2 * s.d * kv + q * s.d + 3 * s.d * s.ffn
+    drf_layer = 2 * s.d * q + 2 * 2 * s.d * kv + q * s.d + 3 * s.d * s.ffn
+    lm = s.vocab * s.d
+    weights = s.n_layers * tgt_layer + lm + 3 * s.d * s.d + w.depth * (drf_layer + lm)
+    ctx = float(np.sum(configs.prompt_lengths(w)))
+    kv_bytes = 2 * kv * e * (s.n_layers * (ctx + w.batch * w.rows) + w.depth * ctx)
+    return weights * e + kv_bytes
+
+
+def roofline(w, prof, steps):
+    """Roofline of the dominant kernel (largest total time among the GEMM kinds):
+    HBM-bound weight streaming for the skinny kernels, MFMA-bound for the
+    large-M kernel.  achieved = algorithmic bytes (or flops) / event time."""
+    kinds = [k for k in (0, 1, 3) if prof[k][0] > 0]
+    k = max(kinds, key=lambda x: prof[x][1])
+    n, t_ms, by, fl = prof[k]
+    if k == 3:
+        achieved = fl / (t_ms / 1e3)
+        out = {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
+               "frac": round(achieved / BF16_PEAK, 4)}
+    else:
+        achieved = by / (t_ms / 1e3)
+        out = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+               "frac": round(achieved / HBM_PEAK, 4)}
+    out["traffic"] = measured_traffic(w, k)
+    out.update({"kernel": KERNEL_NAMES[k], "launches_per_step": n / steps, "kernel_ms_per_step": round(t_ms / steps, 4),
+                "algorithmic_bytes_per_launch": round(by / n), "flops_per_launch": round(fl / n)})
+    return out
+
+
+def _kernel_source_digest():
+    import hashlib
+
+    path = os.path.join(ROOT, "speculative_decoding_step_amd", "csrc", "k_gemm.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(w, kind):
+    """HBM bytes per launch of the dominant kernel from the counter summary in
+    profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by the copy calibration),
+    or None when there is none for this workload or the kernel source changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_kind") != kind or t.get("source_digest") != _kernel_source_digest():
+        return None
+    return t["bytes_per_launch"]
+
+
+def traffic_from_counters(workload, kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, mib):
+    """Writes profiles/traffic_<workload>.json from rocprofv3 --pmc FETCH_SIZE and
+    WRITE_SIZE runs of bench.py and of --copy-probe MIB (the copy kernel reads
+    and writes MIB MiB per dispatch: its counters give the scale factors)."""
+    import csv
+
+    names = {0: "k_gemm_bf16<4, 1, 128, 8>", 1: "k_gemm_bf16<1, 2, 256, 4>", 3: "k_gemm_bf16_big"}
+
+    def per_dispatch(path, needle):
+        vals = [float(r["Counter_Value"]) * 1024.0 for r in csv.DictReader(open(path)) if needle in r["Kernel_Name"]]
+        return vals
+
+    nbytes = mib << 20
+    f_copy = per_dispatch(copy_fetch_csv, "copyBuffer")
+    w_copy = per_dispatch(copy_write_csv, "copyBuffer")
+    f_scale = nbytes / (sum(f_copy) / len(f_copy))
+    w_scale = nbytes / (sum(w_copy) / len(w_copy))
+    fv = per_dispatch(fetch_csv, names[kind])
+    wv = per_dispatch(write_csv, names[kind])
+    per_launch = sum(fv) / len(fv) * f_scale + sum(wv) / len(wv) * w_scale
+    out = {"workload": workload, "kernel_kind": kind, "kernel": names[kind], "source_digest": _kernel_source_digest(),
+           "bytes_per_launch": round(per_launch), "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "dispatches": [len(fv), len(wv)]}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def copy_probe(mib):
     """Five copies of a MIB-MiB device buffer into another: each dispatch reads and
     writes exactly mib * 2^20 bytes."""
@@ -198,7 +306,15 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the reference point that "
                          "scales the HBM byte counters of a profiler run) and exit")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="only write profiles/traffic_<workload>.json from the counter CSVs of a bench run and a "
+                         "--copy-probe run, then exit")
+    ap.add_argument("--traffic-kind", type=int, default=0, help="kernel kind for --traffic-from (0, 1 or 3)")
+    ap.add_argument("--traffic-mib", type=int, default=1024, help="copy size of the --copy-probe run, MiB")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from_counters(args.workload, args.traffic_kind, *args.traffic_from, args.traffic_mib)
+        return
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
@@ -211,8 +327,6 @@ def main():
     w = configs.WORKLOADS[args.workload]
     ms, eager_ms, prof = run_gpu(w, args.steps, args.warmup)
     rows = w.batch * w.rows
-    n64, t64, b64, f64 = prof[0]
-    achieved = b64 / (t64 / 1e3) if t64 > 0 else 0.0
     line = {
         "metric": "verified tree tokens/s",
         "value": round(rows / (ms / 1e3), 2),
@@ -230,16 +344,10 @@ def main():
         "data": "synthetic: seeded N(0,0.02) weights, uniform prompt ids",
         "config": {"workload": w.name, "batch": w.batch, "prompt_len": w.prompt_len, "tree_depth": w.depth,
                    "topk": w.topk, "tree_nodes": w.n_nodes, "rows_per_step": rows},
-        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
-                     "kernel": "k_gemm_bf16<4,1,128,8> (64-row MFMA weight-streaming GEMM)",
-                     "launches_per_step": n64 / args.steps,
-                     "kernel_ms_per_step": round(t64 / args.steps, 4)},
-        "hbm_gbps_step": None,
+        "roofline": roofline(w, prof, args.steps),
+        "hbm_gbps_step": round(step_bytes(w) / (ms / 1e3) / 1e9, 1),
         "cpu_baseline": None,
     }
-    algo_step_bytes = prof[0][2] + prof[1][2]
-    line["hbm_gbps_step"] = round(algo_step_bytes / args.steps / (ms / 1e3) / 1e9, 1)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -30,6 +30,23 @@ template <typename T> E3_DEV void st(T* p, size_t i, float v);
 template <> E3_DEV void st<float>(float* p, size_t i, float v) { p[i] = v; }
 template <> E3_DEV void st<bf16_t>(bf16_t* p, size_t i, float v) { p[i] = f2bf(v); }
 
+// Four consecutive elements as float4 (16-byte or 8-byte loads/stores).
+template <typename T> E3_DEV float4 ld4(const T* p, size_t i);
+template <> E3_DEV float4 ld4<float>(const float* p, size_t i) { return *(const float4*)(p + i); }
+template <> E3_DEV float4 ld4<bf16_t>(const bf16_t* p, size_t i) {
+  const uint2 u = *(const uint2*)(p + i);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+template <typename T> E3_DEV void st4(T* p, size_t i, float4 v);
+template <> E3_DEV void st4<float>(float* p, size_t i, float4 v) { *(float4*)(p + i) = v; }
+template <> E3_DEV void st4<bf16_t>(bf16_t* p, size_t i, float4 v) {
+  uint2 u;
+  u.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+  u.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+  *(uint2*)(p + i) = u;
+}
+
 // ---------------------------------------------------------------- reductions
 E3_DEV float wave_sum(float v) {
 #pragma unroll
@@ -91,8 +108,10 @@ E3_DEV float4 sum_splits4(const float4* __restrict__ p, int S, size_t stride4) {
 
 // (value, index) order used by every top-k and argmax: larger value first,
 // lower index on ties.
+// Written with non-short-circuit operators so that it compiles to compares and
+// mask arithmetic rather than branches.
 E3_DEV bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && (unsigned)ia < (unsigned)ib);
+  return (va > vb) | ((va == vb) & ((unsigned)ia < (unsigned)ib));
 }
 
 // Status bits (mirrors eagle3.h).

@@ -269,7 +269,9 @@ __global__ void k_seq_roots(int batch, int K1, const int* __restrict__ roots_in,
 inline unsigned nb(size_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
 // ------------------------------------------------------------ profiling
-void prof_begin(eagle3_ctx* c, int kernel, double bytes, double flops, ProfRec* rec) {
+// With record = false the caller hands the event pair to a launch that records
+// it itself (at the kernel's start and end).
+void prof_begin(eagle3_ctx* c, int kernel, double bytes, double flops, ProfRec* rec, bool record = true) {
   if (!c->prof) return;
   if (c->pool_used + 2 > c->pool.size()) {
     for (int i = 0; i < 256; ++i) {
@@ -284,11 +286,11 @@ void prof_begin(eagle3_ctx* c, int kernel, double bytes, double flops, ProfRec* 
   rec->b = c->pool[c->pool_used++];
   rec->bytes = bytes;
   rec->flops = flops;
-  (void)hipEventRecord(rec->a, c->st);
+  if (record) (void)hipEventRecord(rec->a, c->st);
 }
-void prof_end(eagle3_ctx* c, ProfRec* rec) {
+void prof_end(eagle3_ctx* c, ProfRec* rec, bool record = true) {
   if (!c->prof || !rec->a) return;
-  (void)hipEventRecord(rec->b, c->st);
+  if (record) (void)hipEventRecord(rec->b, c->st);
   c->recs.push_back(*rec);
 }
 
@@ -316,9 +318,11 @@ int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, flo
   ProfRec rec{};
   const double bytes = (double)N * K * c->esz + (double)M * K * c->esz + (double)M * N * 4.0;
   const int kid = m_tile == 16 ? EAGLE3_PROF_GEMM_M16 : (m_tile == 64 ? EAGLE3_PROF_GEMM_M64 : EAGLE3_PROF_GEMM_BIG);
-  prof_begin(c, kid, bytes, 2.0 * M * N * K, &rec);
-  const int used = gemm(c->bf16, X, M, K, sg, out_direct ? out_direct : c->part, (size_t)M * N, S, m_tile, c->st);
-  prof_end(c, &rec);
+  // the bf16 kernels record the pair at their own start and end
+  prof_begin(c, kid, bytes, 2.0 * M * N * K, &rec, !c->bf16);
+  const int used = gemm(c->bf16, X, M, K, sg, out_direct ? out_direct : c->part, (size_t)M * N, S, m_tile, c->st,
+                        c->bf16 ? rec.a : nullptr, c->bf16 ? rec.b : nullptr);
+  prof_end(c, &rec, !c->bf16);
   return used;
 }
 

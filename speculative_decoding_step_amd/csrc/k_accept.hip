@@ -18,44 +18,45 @@ namespace e3 {
 
 static inline unsigned nblk(size_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
-__global__ void k_accept_greedy(int batch, int n_rows, int maxp, const int* __restrict__ tokens,
-                                const int* __restrict__ parents, const int* __restrict__ argmax, int* __restrict__ path,
-                                int* __restrict__ path_len, int* __restrict__ next_root, int* __restrict__ emitted,
-                                int* status) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= batch) return;
-  const int* tk = tokens + (size_t)b * n_rows;
-  const int* pa = parents + (size_t)b * n_rows;
-  const int* am = argmax + (size_t)b * n_rows;
-  int* pb = path + (size_t)b * maxp;
-  for (int c = 1; c < n_rows; ++c)
-    if (pa[c] < 0 || pa[c] >= c) {
-      raise_flag(status, E3_DEV_BAD_TREE);
-      break;
-    }
-  int node = 0, len = 1;
-  pb[0] = 0;
+// One wave per sequence, lane i holding tree row i (n_rows <= 64): the walk
+// reads the current node's argmax as a scalar and finds the matching child
+// with a ballot (the lowest such index).
+__global__ __launch_bounds__(64) void k_accept_greedy(int batch, int n_rows, int maxp, const int* __restrict__ tokens,
+                                                      const int* __restrict__ parents, const int* __restrict__ argmax,
+                                                      int* __restrict__ path, int* __restrict__ path_len,
+                                                      int* __restrict__ next_root, int* __restrict__ emitted,
+                                                      int* status) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const bool in = lane < n_rows;
+  const size_t rb = (size_t)b * n_rows;
+  const int tk = in ? tokens[rb + lane] : -1;
+  const int pa = in ? parents[rb + lane] : -2;
+  const int am = in ? argmax[rb + lane] : -1;
+  const bool bad = in && lane >= 1 && (pa < 0 || pa >= lane);
+  if (__ballot(bad) != 0ull && lane == 0) raise_flag(status, E3_DEV_BAD_TREE);
+  int node = 0, len = 1, mine = lane == 0 ? 0 : -1;  // lane j holds path[j]
   while (true) {
-    const int pred = am[node];
-    int child = -1;
-    for (int c = node + 1; c < n_rows; ++c)
-      if (pa[c] == node && tk[c] == pred) {
-        child = c;
-        break;
-      }
-    if (child < 0) break;
+    const int pred = __builtin_amdgcn_readlane(am, node);
+    const unsigned long long hit = __ballot(in && pa == node && tk == pred);
+    if (hit == 0ull) break;
     if (len >= maxp) {
-      raise_flag(status, E3_DEV_BAD_PATH);
+      if (lane == 0) raise_flag(status, E3_DEV_BAD_PATH);
       break;
     }
-    pb[len++] = child;
+    const int child = __ffsll((long long)hit) - 1;
+    if (lane == len) mine = child;
+    ++len;
     node = child;
   }
-  next_root[b] = am[node];
-  path_len[b] = len;
-  for (int j = len; j < maxp; ++j) pb[j] = -1;
-  if (emitted)
-    for (int j = 0; j < maxp; ++j) emitted[(size_t)b * maxp + j] = j < len ? tk[pb[j]] : -1;
+  const int tok_mine = __shfl(tk, mine < 0 ? 0 : mine, 64);
+  if (lane == 0) {
+    next_root[b] = __builtin_amdgcn_readlane(am, node);
+    path_len[b] = len;
+  }
+  for (int j = lane; j < maxp; j += 64) {
+    path[(size_t)b * maxp + j] = j < len ? mine : -1;
+    if (emitted) emitted[(size_t)b * maxp + j] = j < len ? tok_mine : -1;
+  }
 }
 
 // One block of 1024 threads per sequence.  lse64[b*(K+1)+i] = log-sum-exp of
@@ -182,26 +183,47 @@ __global__ __launch_bounds__(128) void k_compact_kv(const int* __restrict__ seq_
   }
 }
 
+// grid (B, maxp): block (b, j) copies the aux row of path node j (if j < n)
+// in 16-byte chunks; block (b, 0) also writes next_tok, new_len and seq_lens.
 template <typename E>
 __global__ __launch_bounds__(256) void k_compact_finish(int* __restrict__ seq_lens, int n_rows, int maxp,
                                                         const int* __restrict__ path, const int* __restrict__ path_len,
                                                         const int* __restrict__ tokens, const int* __restrict__ next_root,
                                                         const E* __restrict__ aux_tree, int aux_w, E* __restrict__ aux_new,
                                                         int* __restrict__ next_tok, int* __restrict__ new_len) {
-  const int b = blockIdx.x;
+  const int b = blockIdx.x, jrow = blockIdx.y;
   const int n = path_len[b];
   const int* pb = path + (size_t)b * maxp;
   bool ok = n >= 1 && n <= maxp && pb[0] == 0;
   for (int j = 1; ok && j < n; ++j) ok = pb[j] > pb[j - 1] && pb[j] < n_rows;
   if (!ok) return;
-  for (int idx = threadIdx.x; idx < n * aux_w; idx += blockDim.x) {
-    const int j = idx / aux_w, i = idx % aux_w;
-    aux_new[((size_t)b * maxp + j) * aux_w + i] = aux_tree[((size_t)b * n_rows + pb[j]) * aux_w + i];
+  if (jrow < n) {
+    const E* src = aux_tree + ((size_t)b * n_rows + pb[jrow]) * aux_w;
+    E* dst = aux_new + ((size_t)b * maxp + jrow) * aux_w;
+    const int bytes = aux_w * (int)sizeof(E);
+    if ((bytes & 15) == 0) {
+      const int n16 = bytes >> 4;
+      for (int c0 = threadIdx.x; c0 < n16; c0 += 8 * blockDim.x) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + u * blockDim.x;
+          if (c < n16) v[u] = ((const uint4*)src)[c];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + u * blockDim.x;
+          if (c < n16) ((uint4*)dst)[c] = v[u];
+        }
+      }
+    } else {
+      for (int i = threadIdx.x; i < aux_w; i += blockDim.x) dst[i] = src[i];
+    }
   }
+  if (jrow != 0) return;
   for (int j = threadIdx.x; j < maxp; j += blockDim.x)
     next_tok[(size_t)b * maxp + j] =
         j < n ? (j + 1 < n ? tokens[(size_t)b * n_rows + pb[j + 1]] : next_root[b]) : -1;
-  __syncthreads();
   if (threadIdx.x == 0) {
     new_len[b] = n;
     seq_lens[b] += n;
@@ -210,8 +232,8 @@ __global__ __launch_bounds__(256) void k_compact_finish(int* __restrict__ seq_le
 
 void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const int* parents, const int* argmax,
                    int* path, int* path_len, int* next_root, int* emitted, int* status, hipStream_t st) {
-  k_accept_greedy<<<nblk(batch, 64), 64, 0, st>>>(batch, n_rows, depth + 1, tokens, parents, argmax, path, path_len,
-                                                  next_root, emitted, status);
+  k_accept_greedy<<<batch, 64, 0, st>>>(batch, n_rows, depth + 1, tokens, parents, argmax, path, path_len, next_root,
+                                        emitted, status);
 }
 
 void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,
@@ -236,11 +258,11 @@ void compact_finish(bool bf16, int batch, int* seq_lens, int n_rows, int maxp, c
                     const int* tokens, const int* next_root, const void* aux_tree, int aux_w, void* aux_new,
                     int* next_tok, int* new_len, hipStream_t st) {
   if (bf16)
-    k_compact_finish<uint16_t><<<batch, 256, 0, st>>>(seq_lens, n_rows, maxp, path, path_len, tokens, next_root,
+    k_compact_finish<uint16_t><<<dim3(batch, maxp), 256, 0, st>>>(seq_lens, n_rows, maxp, path, path_len, tokens, next_root,
                                                       (const uint16_t*)aux_tree, aux_w, (uint16_t*)aux_new, next_tok,
                                                       new_len);
   else
-    k_compact_finish<uint32_t><<<batch, 256, 0, st>>>(seq_lens, n_rows, maxp, path, path_len, tokens, next_root,
+    k_compact_finish<uint32_t><<<dim3(batch, maxp), 256, 0, st>>>(seq_lens, n_rows, maxp, path, path_len, tokens, next_root,
                                                       (const uint32_t*)aux_tree, aux_w, (uint32_t*)aux_new, next_tok,
                                                       new_len);
 }

@@ -13,6 +13,8 @@
 // MFMA v_mfma_f32_16x16x32_bf16: A (16x32) and B (32x16) fragments hold, in
 // lane l, row/column (l % 16) and K elements 8*(l/16) .. 8*(l/16)+7; the
 // 16x16 fp32 result holds rows 4*(l/16)+r (r = 0..3), column l % 16.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -369,7 +371,8 @@ int gemm_rows_per_tile(bool bf16, int m_tile) {
 }
 
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out, size_t split_stride,
-         int splits, int m_tile, hipStream_t st) {
+         int splits, int m_tile, hipStream_t st, hipEvent_t ev_start,
+         hipEvent_t ev_stop) {
   if (bf16 && m_tile > 64) {
     BigTiles bt;
     bt.tiles0[0] = 0;
@@ -377,7 +380,9 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
     const int mtiles = (M + BT - 1) / BT;
     const int nwork = mtiles * bt.tiles0[segs.nseg];
     const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
-    if (M > 0) k_gemm_bf16_big<<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, bt, out, gemm_ntot(segs), mtiles, nwork);
+    if (M > 0)
+      hipExtLaunchKernelGGL(k_gemm_bf16_big, dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0, (const bf16_t*)X, M, K,
+                            segs, bt, out, gemm_ntot(segs), mtiles, nwork);
     return 1;
   }
   splits = gemm_splits(bf16, K, splits, m_tile);
@@ -395,11 +400,11 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
     const int nwork = mtiles * S * ntiles;
     const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
     if (m_tile == 16)
-      k_gemm_bf16<1, 2, KT16, 4><<<grid, 256, 0, st>>>((const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk,
-                                                     mtiles, S, nwork);
+      hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, KT16, 4>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
+                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork);
     else
-      k_gemm_bf16<4, 1, KT64, 8><<<grid, 512, 0, st>>>((const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk,
-                                                     mtiles, S, nwork);
+      hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, KT64, 8>), dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0,
+                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork);
   } else {
     const int ntiles = segs.tiles0[segs.nseg];
     const int per = ((K + 31) / 32 + splits - 1) / splits;

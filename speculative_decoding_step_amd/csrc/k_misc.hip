@@ -14,12 +14,31 @@ __global__ void k_embed(const T* __restrict__ table, const int* __restrict__ tok
                         int d, int V, int* status) {
   const int r = blockIdx.x;
   int t = tokens[r];
+  float* xr = x + (size_t)r * d;
   if (t < 0 || t >= V) {
     if (threadIdx.x == 0 && t != -1) raise_flag(status, E3_DEV_BAD_TOKEN);
-    for (int i = threadIdx.x; i < d; i += blockDim.x) x[(size_t)r * d + i] = 0.f;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = 0.f;
     return;
   }
-  for (int i = threadIdx.x; i < d; i += blockDim.x) x[(size_t)r * d + i] = ld<T>(table, (size_t)t * d + i);
+  const T* er = table + (size_t)t * d;
+  if ((d & 3) == 0) {
+    const int d4 = d >> 2;
+    for (int c0 = threadIdx.x; c0 < d4; c0 += 4 * blockDim.x) {
+      float4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + j * blockDim.x;
+        if (c < d4) v[j] = ld4<T>(er, 4 * c);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + j * blockDim.x;
+        if (c < d4) ((float4*)xr)[c] = v[j];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = ld<T>(er, i);
+  }
 }
 
 void embed_rows(bool bf16, const void* table, const int* tokens, float* x, int R, int d, int V, int* status,
@@ -137,11 +156,55 @@ void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, in
 }
 
 // ---------------------------------------------------------------- draft input
+// One block per row, one float4 column group per thread (NV groups when the
+// row is wider): out[r] = [input_norm(embed[token]) ; hidden_norm(x[r])].
+// Rows whose width is not a multiple of 4 use the element loop.
+template <typename T, int NV>
+__global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embed, const int* __restrict__ tokens,
+                                                      const float* __restrict__ x, const T* __restrict__ w_in,
+                                                      const T* __restrict__ w_hid, T* __restrict__ out, int d,
+                                                      int V, float eps, int* status) {
+  __shared__ float red[16];
+  const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, d4 = d >> 2;
+  int t = tokens[r];
+  const bool ok = t >= 0 && t < V;
+  if (!ok && tid == 0 && t != -1) raise_flag(status, E3_DEV_BAD_TOKEN);
+  if (!ok) t = 0;
+  const float* xr = x + (size_t)r * d;
+  const T* er = embed + (size_t)t * d;
+  float4 e[NV], h[NV];
+  float se = 0.f, sx = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = tid + nt * i;
+    if (c < d4) {
+      e[i] = ok ? ld4<T>(er, 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      h[i] = *(const float4*)(xr + 4 * c);
+      se += e[i].x * e[i].x + e[i].y * e[i].y + e[i].z * e[i].z + e[i].w * e[i].w;
+      sx += h[i].x * h[i].x + h[i].y * h[i].y + h[i].z * h[i].z + h[i].w * h[i].w;
+    }
+  }
+  se = block_sum(se, red);
+  sx = block_sum(sx, red);
+  const float ie = 1.f / sqrtf(se / (float)d + eps), ix = 1.f / sqrtf(sx / (float)d + eps);
+  T* o = out + (size_t)r * 2 * d;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = tid + nt * i;
+    if (c < d4) {
+      const float4 wi = ld4<T>(w_in, 4 * c), wh = ld4<T>(w_hid, 4 * c);
+      st4<T>(o, 4 * c, make_float4(e[i].x * ie * wi.x, e[i].y * ie * wi.y, e[i].z * ie * wi.z, e[i].w * ie * wi.w));
+      st4<T>(o, d + 4 * c,
+             make_float4(h[i].x * ix * wh.x, h[i].y * ix * wh.y, h[i].z * ix * wh.z, h[i].w * ix * wh.w));
+    }
+  }
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_draft_input(const T* __restrict__ embed, const int* __restrict__ tokens,
-                                                     const float* __restrict__ x, const T* __restrict__ w_in,
-                                                     const T* __restrict__ w_hid, T* __restrict__ out, int d,
-                                                     int V, float eps, int* status) {
+__global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ embed, const int* __restrict__ tokens,
+                                                         const float* __restrict__ x, const T* __restrict__ w_in,
+                                                         const T* __restrict__ w_hid, T* __restrict__ out, int d,
+                                                         int V, float eps, int* status) {
   __shared__ float red[16];
   const int r = blockIdx.x;
   int t = tokens[r];
@@ -166,15 +229,30 @@ __global__ __launch_bounds__(256) void k_draft_input(const T* __restrict__ embed
   }
 }
 
+template <typename T>
+static void launch_draft_input(const T* embed, const int* tokens, const float* x, const T* w_in, const T* w_hid,
+                               T* out, int R, int d, int V, float eps, int* status, hipStream_t st) {
+  const int d4 = d / 4;
+  if (d % 4 == 0 && d4 <= 2048) {
+    const int nt = std::min(1024, (d4 + 63) / 64 * 64);
+    if (d4 <= nt)
+      k_draft_input<T, 1><<<R, nt, 0, st>>>(embed, tokens, x, w_in, w_hid, out, d, V, eps, status);
+    else
+      k_draft_input<T, 2><<<R, nt, 0, st>>>(embed, tokens, x, w_in, w_hid, out, d, V, eps, status);
+  } else {
+    k_draft_input_any<T><<<R, 256, 0, st>>>(embed, tokens, x, w_in, w_hid, out, d, V, eps, status);
+  }
+}
+
 void draft_input(bool bf16, const void* embed, const int* tokens, const float* x, const void* w_in,
                  const void* w_hid, void* out, int R, int d, int V, float eps, int* status, hipStream_t st) {
   if (R <= 0) return;
   if (bf16)
-    k_draft_input<bf16_t><<<R, 256, 0, st>>>((const bf16_t*)embed, tokens, x, (const bf16_t*)w_in,
-                                             (const bf16_t*)w_hid, (bf16_t*)out, d, V, eps, status);
+    launch_draft_input<bf16_t>((const bf16_t*)embed, tokens, x, (const bf16_t*)w_in, (const bf16_t*)w_hid,
+                               (bf16_t*)out, R, d, V, eps, status, st);
   else
-    k_draft_input<float><<<R, 256, 0, st>>>((const float*)embed, tokens, x, (const float*)w_in,
-                                            (const float*)w_hid, (float*)out, d, V, eps, status);
+    launch_draft_input<float>((const float*)embed, tokens, x, (const float*)w_in, (const float*)w_hid, (float*)out,
+                              R, d, V, eps, status, st);
 }
 
 // ----------------------------------------------------------- rope + KV write
@@ -248,103 +326,146 @@ struct VI {
 
 E3_DEV VI vi_best(VI a, VI b) { return better(a.v, a.i, b.v, b.i) ? a : b; }
 
+// Best (value, index) of a full wave, returned uniformly to every lane.  Within
+// each 16-lane row: DPP exchanges with lanes xor 1, xor 2 (quad permutes), then
+// the half-row and row mirrors; across rows: a swizzle with lane xor 16, then
+// lanes 0 and 32 are read as scalars.  The order is a total order, so the
+// result does not depend on the reduction tree.  Every lane must be active.
+template <int CTRL>
+E3_DEV VI vi_dpp(VI a) {
+  const VI b{__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a.v), CTRL, 0xF, 0xF, false)),
+             __builtin_amdgcn_update_dpp(0, a.i, CTRL, 0xF, 0xF, false)};
+  return vi_best(a, b);
+}
+
 E3_DEV VI wave_best(VI x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    VI y{__shfl_xor(x.v, o, 64), __shfl_xor(x.i, o, 64)};
-    x = vi_best(x, y);
-  }
-  return x;
+  x = vi_dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = vi_dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = vi_dpp<0x141>(x);  // row_half_mirror
+  x = vi_dpp<0x140>(x);  // row_mirror
+  const VI y{__int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x.v), 0x401F)),
+             __builtin_amdgcn_ds_swizzle(x.i, 0x401F)};  // lane xor 16 within each 32
+  x = vi_best(x, y);
+  const VI h0{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x.v), 0)), __builtin_amdgcn_readlane(x.i, 0)};
+  const VI h1{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x.v), 32)), __builtin_amdgcn_readlane(x.i, 32)};
+  return vi_best(h0, h1);
 }
 
 // grid (R, nslices), block 256.  Per slice: the K best (value, index) and the
 // slice's max and sum of exp(z - max) in double, with z = logit / temperature.
+// The slice is held in registers (16 values per thread, loaded at once); each
+// of the K rounds picks the best value not yet taken, a thread marking its
+// winner in a 16-bit mask.
+constexpr int TK_PER = TK_SLICE / 256;  // values per thread
+
 __global__ __launch_bounds__(256) void k_topk_partial(const float* __restrict__ logits, int V, int ld, int K,
                                                       double temp, float* __restrict__ pv, int* __restrict__ pi,
                                                       float* __restrict__ pmax, double* __restrict__ psum) {
-  __shared__ float vals[TK_SLICE];
-  __shared__ unsigned char taken[TK_SLICE];
-  __shared__ VI wred[4];
+  __shared__ VI wred[2][4];
+  __shared__ VI res[TK_KMAX];
   __shared__ double dred[4];
   const int r = blockIdx.x, sl = blockIdx.y, ns = gridDim.y;
   const int v0 = sl * TK_SLICE, n = min(TK_SLICE, V - v0);
   const float* row = logits + (size_t)r * ld + v0;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  VI best{-INFINITY, 0x7fffffff};
-  for (int i = tid; i < n; i += 256) {
-    const float v = row[i];
-    vals[i] = v;
-    taken[i] = 0;
-    best = vi_best(best, VI{v, v0 + i});
+  float v[TK_PER];
+#pragma unroll
+  for (int j = 0; j < TK_PER; ++j) {
+    const int i = tid + 256 * j;  // coalesced: consecutive threads, consecutive entries
+    v[j] = i < n ? row[i] : -INFINITY;
   }
-  best = wave_best(best);
-  if (lane == 0) wred[w] = best;
+  unsigned taken = 0;
+#pragma unroll
+  for (int j = 0; j < TK_PER; ++j)
+    if (tid + 256 * j >= n) taken |= 1u << j;
+  auto local_best = [&]() {  // taken entries become (-inf, INT_MAX), which never wins
+    VI b{-INFINITY, 0x7fffffff};
+#pragma unroll
+    for (int j = 0; j < TK_PER; ++j) {
+      const bool tk = (taken >> j) & 1u;
+      b = vi_best(b, VI{tk ? -INFINITY : v[j], tk ? 0x7fffffff : v0 + tid + 256 * j});
+    }
+    return b;
+  };
+  VI best = wave_best(local_best());
+  if (lane == 0) wred[0][w] = best;
   __syncthreads();
-  const VI top = vi_best(vi_best(wred[0], wred[1]), vi_best(wred[2], wred[3]));
+  const VI top = vi_best(vi_best(wred[0][0], wred[0][1]), vi_best(wred[0][2], wred[0][3]));
   const double m = (double)top.v / temp;
   double s = 0.0;
-  for (int i = tid; i < n; i += 256) s += exp((double)vals[i] / temp - m);
+#pragma unroll
+  for (int j = 0; j < TK_PER; ++j)
+    if (tid + 256 * j < n) s += exp((double)v[j] / temp - m);
   s = wave_sum_d(s);
   if (lane == 0) dred[w] = s;
-  __syncthreads();
   const size_t o = (size_t)r * ns + sl;
+  for (int k = 0; k < K; ++k) {
+    const VI b = wave_best(local_best());
+    if (lane == 0) wred[(k + 1) & 1][w] = b;
+    __syncthreads();  // one barrier per round: the two halves of wred alternate
+    const VI t = vi_best(vi_best(wred[(k + 1) & 1][0], wred[(k + 1) & 1][1]),
+                         vi_best(wred[(k + 1) & 1][2], wred[(k + 1) & 1][3]));
+    if (tid == 0) res[k] = t;  // global stores wait until after the rounds: a barrier would drain them
+    const int li = t.i - v0;
+    if (li >= 0 && li < n && (li & 255) == tid) taken |= 1u << (li >> 8);
+  }
+  __syncthreads();
+  if (tid < K) {
+    pv[o * K + tid] = res[tid].v;
+    pi[o * K + tid] = res[tid].i;
+  }
   if (tid == 0) {
     pmax[o] = (float)top.v;
     psum[o] = dred[0] + dred[1] + dred[2] + dred[3];
   }
-  for (int k = 0; k < K; ++k) {
-    VI b{-INFINITY, 0x7fffffff};
-    for (int i = tid; i < n; i += 256)
-      if (!taken[i]) b = vi_best(b, VI{vals[i], v0 + i});
-    b = wave_best(b);
-    __syncthreads();
-    if (lane == 0) wred[w] = b;
-    __syncthreads();
-    const VI t = vi_best(vi_best(wred[0], wred[1]), vi_best(wred[2], wred[3]));
-    if (tid == 0) {
-      pv[o * K + k] = t.v;
-      pi[o * K + k] = t.i;
-    }
-    if (t.i >= v0 && t.i < v0 + n && ((t.i - v0) % 256) == tid) taken[t.i - v0] = 1;
-    __syncthreads();
-  }
 }
 
-// grid (R), block 64: merge the slices' candidates, combine the sums in slice order.
+// grid (R), block 64: merge the slices' candidates (held in registers) and
+// combine the slices' sums.
+constexpr int TK_MERGE_PER = 16;  // candidates per lane: ns * K <= 64 * TK_KMAX
+
 __global__ __launch_bounds__(64) void k_topk_merge(int ns, int K, double temp, const float* __restrict__ pv,
                                                    const int* __restrict__ pi, const float* __restrict__ pmax,
                                                    const double* __restrict__ psum, int* __restrict__ out_ids,
                                                    float* __restrict__ out_vals, float* __restrict__ lse32,
                                                    double* __restrict__ lse64) {
-  __shared__ unsigned char taken[64 * TK_KMAX];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int nc = ns * K;
   const float* cv = pv + (size_t)r * nc;
   const int* ci = pi + (size_t)r * nc;
-  for (int c = tid; c < nc; c += 64) taken[c] = 0;
-  __syncthreads();
+  float v[TK_MERGE_PER];
+  int id[TK_MERGE_PER];
+  unsigned taken = 0;
+#pragma unroll
+  for (int j = 0; j < TK_MERGE_PER; ++j) {
+    const int c = tid + 64 * j;
+    v[j] = c < nc ? cv[c] : -INFINITY;
+    id[j] = c < nc ? ci[c] : 0x7fffffff;
+    if (c >= nc) taken |= 1u << j;
+  }
+  // slice maxima and sums: lane s holds slice s (ns <= 64 for V <= 64 * 4096)
+  const float pm = tid < ns ? pmax[(size_t)r * ns + tid] : -INFINITY;
+  const double ps = tid < ns ? psum[(size_t)r * ns + tid] : 0.0;
   for (int k = 0; k < K; ++k) {
     VI b{-INFINITY, 0x7fffffff};
-    int bc = -1;
-    for (int c = tid; c < nc; c += 64)
-      if (!taken[c] && better(cv[c], ci[c], b.v, b.i)) {
-        b = VI{cv[c], ci[c]};
-        bc = c;
-      }
-    VI w = wave_best(b);
-    if (b.i == w.i && b.v == w.v && bc >= 0) taken[bc] = 1;
-    if (tid == 0) {
-      out_ids[(size_t)r * K + k] = w.i;
-      out_vals[(size_t)r * K + k] = w.v;
+    int bj = -1;
+#pragma unroll
+    for (int j = 0; j < TK_MERGE_PER; ++j) {
+      const bool take = !((taken >> j) & 1u) & better(v[j], id[j], b.v, b.i);
+      b = take ? VI{v[j], id[j]} : b;
+      bj = take ? j : bj;
     }
-    __syncthreads();
+    const VI wb = wave_best(b);
+    if (bj >= 0 && b.i == wb.i && b.v == wb.v) taken |= 1u << bj;
+    if (tid == 0) {
+      out_ids[(size_t)r * K + k] = wb.i;
+      out_vals[(size_t)r * K + k] = wb.v;
+    }
   }
+  const float mx = wave_max(pm);
+  const double M = (double)mx / temp;
+  const double S = wave_sum_d(tid < ns ? ps * exp((double)pm / temp - M) : 0.0);
   if (tid == 0) {
-    float mx = -INFINITY;
-    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, pmax[(size_t)r * ns + s]);
-    const double M = (double)mx / temp;
-    double S = 0.0;
-    for (int s = 0; s < ns; ++s) S += psum[(size_t)r * ns + s] * exp((double)pmax[(size_t)r * ns + s] / temp - M);
     const double l = M + log(S);
     if (lse64) lse64[r] = l;
     if (lse32) lse32[r] = (float)l;

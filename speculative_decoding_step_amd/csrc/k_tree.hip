@@ -58,17 +58,17 @@ E3_DEV bool cand_better(float sa, int ca, float sb, int cb) { return sa > sb || 
 // RoPE position P + d - 1, KV slot P + e, and the tail mask.
 __global__ __launch_bounds__(256) void k_tree_frontier(TreeState ts, int d, const int* __restrict__ seq_lens,
                                                        DraftRows dr, int S_cap, int* status) {
+  __shared__ float sc_s[256];  // k * k <= 256 (k <= 16)
   const int b = blockIdx.x, k = ts.topk;
   const int c0 = d == 1 ? 0 : k + (d - 2) * k * k;
   const int n = d == 1 ? k : k * k;
   const size_t base = (size_t)b * ts.cmax;
+  for (int c = threadIdx.x; c < n; c += blockDim.x) sc_s[c] = ts.score[base + c0 + c];
+  __syncthreads();
   for (int c = threadIdx.x; c < n; c += blockDim.x) {
-    const float sc = ts.score[base + c0 + c];
+    const float sc = sc_s[c];
     int rank = 0;
-    for (int o = 0; o < n; ++o) {
-      const float so = ts.score[base + c0 + o];
-      rank += cand_better(so, c0 + o, sc, c0 + c);
-    }
+    for (int o = 0; o < n; ++o) rank += cand_better(sc_s[o], c0 + o, sc, c0 + c);
     if (rank < k) ts.front[b * k + rank] = c0 + c;
   }
   __syncthreads();
@@ -96,12 +96,35 @@ __global__ __launch_bounds__(256) void k_tree_frontier(TreeState ts, int d, cons
   }
 }
 
+// Row copies of d_model floats: each thread moves up to four float4 (loads
+// issued together); d_model % 4 == 0 (checked on the host), else element loop.
+E3_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, int d) {
+  if ((d & 3) == 0) {
+    const int d4 = d >> 2;
+    for (int c0 = threadIdx.x; c0 < d4; c0 += 4 * blockDim.x) {
+      float4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + j * blockDim.x;
+        if (c < d4) v[j] = ((const float4*)src)[c];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + j * blockDim.x;
+        if (c < d4) ((float4*)dst)[c] = v[j];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = src[i];
+  }
+}
+
 // x of the expansion rows: a of the parent's expansion row, or of the catch-up row.
 __global__ void k_tree_gather_x(float* __restrict__ x, const int* __restrict__ src, const float* __restrict__ a_rows,
                                 const float* __restrict__ a_last, int d_model) {
   const int r = blockIdx.x, s = src[r];
   const float* from = s < 0 ? a_last + (size_t)(-1 - s) * d_model : a_rows + (size_t)s * d_model;
-  for (int i = threadIdx.x; i < d_model; i += blockDim.x) x[(size_t)r * d_model + i] = from[i];
+  copy_row(x + (size_t)r * d_model, from, d_model);
 }
 
 // Store the expansion rows' outputs a (needed as x by their children).
@@ -109,40 +132,63 @@ __global__ void k_tree_store_a(float* __restrict__ a_rows, const float* __restri
                                const int* __restrict__ seq_lens, int k, int emax, int d_model) {
   const int r = blockIdx.x, b = r / k;
   const int e = slot[r] - seq_lens[b];
-  for (int i = threadIdx.x; i < d_model; i += blockDim.x)
-    a_rows[((size_t)b * emax + e) * d_model + i] = a[(size_t)r * d_model + i];
+  copy_row(a_rows + ((size_t)b * emax + e) * d_model, a + (size_t)r * d_model, d_model);
 }
 
 // Final selection, numbering and masks, one block (512 threads) per sequence.
+// The candidates are sorted in LDS (bitonic, by score descending then creation
+// index ascending, as one 64-bit key); the first n_nodes are kept and numbered
+// by (depth, creation index).
+E3_DEV unsigned long long cand_key(float score, int c) {
+  const uint32_t u = __float_as_uint(score + 0.0f);  // -0 -> +0: equal scores get equal keys
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // ascending in score
+  return ((unsigned long long)(~ord) << 32) | (uint32_t)c;           // descending score, ascending index
+}
+
 __global__ __launch_bounds__(512) void k_tree_finalize(TreeState ts, int n_cand, int n_nodes,
                                                        const int* __restrict__ roots, const int* __restrict__ seq_lens,
                                                        TreeOut out, int* status) {
   __shared__ int node_of[TREE_CMAX];  // creation index -> node index (0 = not kept)
+  __shared__ unsigned long long keys[TREE_CMAX];
+  __shared__ int kept[64], kdep[64];
   __shared__ int pidx[65];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const size_t base = (size_t)b * ts.cmax;
   const int rows = n_nodes + 1;
-  for (int c = tid; c < n_cand; c += blockDim.x) {
-    const float sc = ts.score[base + c];
-    int rank = 0;
-    for (int o = 0; o < n_cand; ++o) rank += cand_better(ts.score[base + o], o, sc, c);
-    node_of[c] = rank < n_nodes ? -1 : 0;  // -1: kept, index assigned below
+  int np = 1;
+  while (np < n_cand) np <<= 1;  // n_cand <= TREE_CMAX (checked on the host)
+  for (int c = tid; c < np; c += nt) {
+    keys[c] = c < n_cand ? cand_key(ts.score[base + c], c) : ~0ull;
+    node_of[c] = 0;
   }
   __syncthreads();
-  for (int c = tid; c < n_cand; c += blockDim.x) {
-    if (node_of[c] != -1) continue;
-    const int dc = ts.dep[base + c];
-    int pos = 1;
-    for (int o = 0; o < n_cand; ++o) {
-      if (node_of[o] == 0) continue;
-      const int od = ts.dep[base + o];
-      pos += (od < dc) || (od == dc && o < c);
+  for (int k = 2; k <= np; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < np; i += nt) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long x = keys[i], y = keys[l];
+          if ((x > y) == ((i & k) == 0)) {
+            keys[i] = y;
+            keys[l] = x;
+          }
+        }
+      }
+      __syncthreads();
     }
-    node_of[c] = -1 - pos;  // encoded until every thread has read the kept flags
+  const int nk = min(n_nodes, n_cand);
+  if (tid < nk) {
+    const int c = (int)(uint32_t)keys[tid];
+    kept[tid] = c;
+    kdep[tid] = ts.dep[base + c];
   }
   __syncthreads();
-  for (int c = tid; c < n_cand; c += blockDim.x)
-    if (node_of[c] < -1) node_of[c] = -node_of[c] - 1;
+  if (tid < nk) {
+    const int c = kept[tid], dc = kdep[tid];
+    int pos = 1;
+    for (int o = 0; o < nk; ++o) pos += (kdep[o] < dc) || (kdep[o] == dc && kept[o] < c);
+    node_of[c] = pos;
+  }
   __syncthreads();
   const int P = seq_lens[b];
   const size_t ob = (size_t)b * rows;
