@@ -299,10 +299,10 @@ int plan_splits(eagle3_ctx* c, int M, int N, int K, int m_tile) {
   if (!c->bf16) return 1;
   const int rows = gemm_rows_per_tile(true, m_tile);
   const int tiles = ((N + rows - 1) / rows) * ((M + m_tile - 1) / m_tile);
-  // about 256 eight-wave (M <= 64) or 512 four-wave (M <= 16) workgroups, but
+  // about 256 eight-wave (M <= 64) or 512 four-wave (other) workgroups, but
   // at most 8 splits: every split adds M x N fp32 partials that the consumer
   // kernel reads back
-  const int target = m_tile == 16 ? 512 : 256;
+  const int target = m_tile == 64 ? 256 : 512;  // large-M kernel: two workgroups per CU
   int S = (target + tiles / 2) / tiles;
   S = std::max(1, std::min(8, S));
   const int mpad = (M + m_tile - 1) / m_tile * m_tile;
@@ -314,7 +314,7 @@ int plan_splits(eagle3_ctx* c, int M, int N, int K, int m_tile) {
 int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, float* out_direct = nullptr) {
   const int N = gemm_ntot(sg);
   const int m_tile = M <= 16 ? 16 : (M <= 64 ? 64 : 128);
-  const int S = (out_direct || m_tile == 128) ? 1 : plan_splits(c, M, N, K, m_tile);
+  const int S = out_direct ? 1 : plan_splits(c, M, N, K, m_tile);
   ProfRec rec{};
   const double bytes = (double)N * K * c->esz + (double)M * K * c->esz + (double)M * N * 4.0;
   const int kid = m_tile == 16 ? EAGLE3_PROF_GEMM_M16 : (m_tile == 64 ? EAGLE3_PROF_GEMM_M64 : EAGLE3_PROF_GEMM_BIG);

@@ -21,8 +21,8 @@ GemmSegs make_segs(const void* w0, int r0, const void* w1 = nullptr, int r1 = 0,
 
 // out[s][m][n] (split s of the K reduction) = sum_k X[m][k] W[n][k].
 // Returns the number of splits used; out must hold splits * split_stride floats.
-// m_tile is 16 or 64 (skinny bf16 MFMA tiles, K split allowed) or 128 (the
-// large-M bf16 kernel, no K split: returns 1); ignored for float.  When
+// m_tile is 16 or 64 (skinny bf16 MFMA tiles) or 128 (the large-M bf16
+// kernel); ignored for float.  When
 // ev_start/ev_stop are given, the bf16 launch records them at the kernel's own
 // start and end (profiling).
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out,
