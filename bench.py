@@ -229,10 +229,12 @@ def roofline(w, prof, steps):
     return out
 
 
-def _kernel_source_digest():
+def _kernel_source_digest(kind):
+    """Digest of the source file that holds the kernel of this kind."""
     import hashlib
 
-    path = os.path.join(ROOT, "speculative_decoding_step_amd", "csrc", "k_gemm.hip")
+    name = "k_gemm_big.hip" if kind == 3 else "k_gemm.hip"
+    path = os.path.join(ROOT, "speculative_decoding_step_amd", "csrc", name)
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
@@ -247,7 +249,7 @@ def measured_traffic(w, kind):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_kind") != kind or t.get("source_digest") != _kernel_source_digest():
+    if t.get("kernel_kind") != kind or t.get("source_digest") != _kernel_source_digest(kind):
         return None
     return t["bytes_per_launch"]
 
@@ -272,7 +274,7 @@ def traffic_from_counters(workload, kind, fetch_csv, write_csv, copy_fetch_csv, 
     fv = per_dispatch(fetch_csv, names[kind])
     wv = per_dispatch(write_csv, names[kind])
     per_launch = sum(fv) / len(fv) * f_scale + sum(wv) / len(wv) * w_scale
-    out = {"workload": workload, "kernel_kind": kind, "kernel": names[kind], "source_digest": _kernel_source_digest(),
+    out = {"workload": workload, "kernel_kind": kind, "kernel": names[kind], "source_digest": _kernel_source_digest(kind),
            "bytes_per_launch": round(per_launch), "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "dispatches": [len(fv), len(wv)]}
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")

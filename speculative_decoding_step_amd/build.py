@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libeagle3.so")
-SOURCES = ["eagle3.hip", "k_gemm.hip", "k_misc.hip", "k_attn.hip", "k_tree.hip", "k_accept.hip"]
+SOURCES = ["eagle3.hip", "k_gemm.hip", "k_gemm_big.hip", "k_misc.hip", "k_attn.hip", "k_tree.hip", "k_accept.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

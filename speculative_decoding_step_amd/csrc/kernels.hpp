@@ -28,6 +28,11 @@ GemmSegs make_segs(const void* w0, int r0, const void* w1 = nullptr, int r1 = 0,
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out,
          size_t split_stride, int splits, int m_tile, hipStream_t st,
          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+// The large-M kernel behind gemm() for m_tile 128: weight rows per tile and
+// K step (K must be a multiple of it); returns the number of splits used.
+constexpr int GEMM_BIG_ROWS = 256, GEMM_BIG_KSTEP = 32;
+int gemm_big(const void* X, int M, int K, const GemmSegs& segs, float* out, size_t split_stride, int splits,
+             hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 // Number of K splits gemm() will actually use for a requested count.
 int gemm_splits(bool bf16, int K, int splits, int m_tile);
 // Weight rows per workgroup of the kernel gemm() picks.
