@@ -326,6 +326,26 @@ int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, flo
   return used;
 }
 
+// abuf = T(silu(X w_gate^T) * (X w_up^T)) for X [M, K]: fused into the GEMM's
+// epilogue for bf16 with M > 16 (the 64-row and large-M kernels), else GEMM
+// partials + silu_mul (the 16-row kernel needs its K splits to fill the chip).
+void run_gateup(eagle3_ctx* c, const void* X, int M, int K, const void* w_gate, const void* w_up, int F) {
+  if (c->bf16 && M > 16) {
+    ProfRec rec{};
+    const double bytes = 2.0 * F * K * c->esz + (double)M * K * c->esz + (double)M * F * c->esz;
+    const int kid = M > 64 ? EAGLE3_PROF_GEMM_BIG : EAGLE3_PROF_GEMM_M64;
+    prof_begin(c, kid, bytes, 4.0 * M * F * K, &rec, false);
+    if (M > 64)
+      gemm_big_silu(X, M, K, w_gate, w_up, F, c->abuf, c->st, rec.a, rec.b);
+    else
+      gemm_silu(X, M, K, w_gate, w_up, F, c->abuf, c->st, rec.a, rec.b);
+    prof_end(c, &rec, false);
+    return;
+  }
+  const int S = run_gemm(c, X, M, K, make_segs(w_gate, F, w_up, F));
+  silu_mul(c->bf16, c->abuf, c->part, S, (size_t)M * 2 * F, M, F, 2 * F, c->st);
+}
+
 void run_attention(eagle3_ctx* c, const void* kc, const void* vc, const RowMeta& rm, int R, int rps) {
   const eagle3_shape& s = c->sh;
   ProfRec rec{};
@@ -381,9 +401,7 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
     run_attention(c, kc, vc, c->rm, R, rps);
     S = run_gemm(c, c->abuf, R, qdim, make_segs(L.wo, d));
     add_rmsnorm(bf, c->xres, c->part, S, (size_t)R * d, d, L.ffn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
-    const GemmSegs gu = make_segs(L.w_gate, s.ffn, L.w_up, s.ffn);
-    S = run_gemm(c, c->hbuf, R, d, gu);
-    silu_mul(bf, c->abuf, c->part, S, (size_t)R * 2 * s.ffn, R, s.ffn, 2 * s.ffn, st);
+    run_gateup(c, c->hbuf, R, d, L.w_gate, L.w_up, s.ffn);
     S = run_gemm(c, c->abuf, R, s.ffn, make_segs(L.w_down, d));
     if (l + 1 < s.n_layers) {
       enter(l + 1, S, c->layers[l + 1].attn_norm, c->hbuf);
@@ -432,9 +450,7 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
   run_attention(c, kc, vc, rm, R, rps);
   S = run_gemm(c, c->abuf, R, qdim, make_segs(H.wo, d));
   add_rmsnorm(bf, x, c->part, S, (size_t)R * d, d, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
-  const GemmSegs gu = make_segs(H.w_gate, s.ffn, H.w_up, s.ffn);
-  S = run_gemm(c, c->hbuf, R, d, gu);
-  silu_mul(bf, c->abuf, c->part, S, (size_t)R * 2 * s.ffn, R, s.ffn, 2 * s.ffn, st);
+  run_gateup(c, c->hbuf, R, d, H.w_gate, H.w_up, s.ffn);
   S = run_gemm(c, c->abuf, R, s.ffn, make_segs(H.w_down, d));
   resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
 }

@@ -72,10 +72,17 @@ __host__ TileMap tile_map(const GemmSegs& s, int rows_per_tile) {
 // dispatched round-robin over the 8 XCDs, so workgroup L runs item
 // (L % 8) * per + L / 8: the m-tiles of one weight tile land on the same XCD
 // back to back and re-read that tile from its L2 rather than from HBM.
-template <int MB, int NB, int KTT, int NW>
+//
+// FUSE (NB = 1, no K split): the two segments are the gate and up projections
+// (F rows each); waves 0 .. NW/2 - 1 own gate rows and waves NW/2 .. NW - 1 the
+// up rows of the same 16 NW / 2 columns, and the epilogue exchanges the up
+// values through LDS and writes act[m][n] = bf16(silu(g) * u).
+template <int MB, int NB, int KTT, int NW, bool FUSE = false>
 __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
                                                    TileMap tm, float* __restrict__ out, int ldo, size_t split_stride,
-                                                   int kchunk, int mtiles, int S, int nwork) {
+                                                   int kchunk, int mtiles, int S, int nwork,
+                                                   bf16_t* __restrict__ act) {
+  static_assert(!FUSE || NB == 1, "the fused gate/up epilogue pairs single-block waves");
   constexpr int KS = KTT / 32;
   constexpr int NT = 64 * NW;               // threads
   constexpr int ROWS = 16 * NB * NW;        // weight rows per workgroup
@@ -89,14 +96,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
   const int mt = lam % mtiles, rest = lam / mtiles;
   const int split = rest % S, ntile = rest / S;
   int seg = 0;
-  while (seg + 1 < segs.nseg && ntile >= tm.tiles0[seg + 1]) ++seg;
-  const int n0 = (ntile - tm.tiles0[seg]) * ROWS;
-  const bf16_t* __restrict__ W = (const bf16_t*)segs.w[seg];
+  while (!FUSE && seg + 1 < segs.nseg && ntile >= tm.tiles0[seg + 1]) ++seg;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool up_wave = FUSE && wv >= NW / 2;
+  const int n0 = FUSE ? ntile * (ROWS / 2) : (ntile - tm.tiles0[seg]) * ROWS;
+  const bf16_t* __restrict__ W = (const bf16_t*)segs.w[FUSE ? (up_wave ? 1 : 0) : seg];
   const int nrows = segs.rows[seg];
   const int m0 = mt * 16 * MB;
   const int kb = split * kchunk;
   const int ke = min(K, kb + kchunk);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
 
   // weight fragment sources: rows n0 + 16 (NB wv + nb) + lr, K offset 8 lg in each 32-step.
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
   bool wok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int r = n0 + 16 * (NB * wv + nb) + lr;
+    const int r = FUSE ? n0 + 16 * (wv % (NW / 2)) + lr : n0 + 16 * (NB * wv + nb) + lr;
     wok[nb] = r < nrows;
     wp[nb] = W + (size_t)(wok[nb] ? r : 0) * K + 8 * lg;
   }
@@ -198,6 +206,28 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
     if (i + 3 < nsteps) step(i + 3, w0, w2, x0, x1);
     if (i + 4 < nsteps) step(i + 4, w1, w0, x1, x0);
   }
+  if (FUSE) {
+    __shared__ float ub[NW / 2][16 * MB][17];  // up values: [wave pair][row][column]
+    if (up_wave) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ub[wv - NW / 2][16 * mb + 4 * lg + r][lr] = acc[0][mb][r];
+    }
+    __syncthreads();
+    if (!up_wave && wok[0]) {
+      const int n = n0 + 16 * wv + lr;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ml = 16 * mb + 4 * lg + r, m = m0 + ml;
+          const float g = acc[0][mb][r], u = ub[wv][ml][lr];
+          if (m < M) act[(size_t)m * nrows + n] = f2bf(g / (1.f + expf(-g)) * u);
+        }
+    }
+    return;
+  }
   // result: acc[nb][mb][r] = out[m0 + 16 mb + 4 lg + r][n0 + 16 (NB wv + nb) + lr]
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -272,6 +302,19 @@ int gemm_splits(bool bf16, int K, int splits, int m_tile) {
   return (kt + per - 1) / per;
 }
 
+void gemm_silu(const void* X, int M, int K, const void* w_gate, const void* w_up, int F, void* act, hipStream_t st,
+               hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (M <= 0) return;
+  const GemmSegs segs = make_segs(w_gate, F, w_up, F);
+  const TileMap tm{};
+  constexpr int COLS = ROWS64 / 2;  // output columns per workgroup
+  const int nwork = (F + COLS - 1) / COLS;
+  const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
+  hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, KT64, 8, true>), dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0,
+                        (const bf16_t*)X, M, K, segs, tm, (float*)nullptr, 0, (size_t)0, K, 1, 1, nwork,
+                        (bf16_t*)act);
+}
+
 int gemm_rows_per_tile(bool bf16, int m_tile) {
   if (!bf16) return 64;
   return m_tile == 16 ? ROWS16 : (m_tile == 64 ? ROWS64 : GEMM_BIG_ROWS);
@@ -298,10 +341,10 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
     const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
     if (m_tile == 16)
       hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, KT16, 4>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
-                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork);
+                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork, nullptr);
     else
       hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, KT64, 8>), dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0,
-                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork);
+                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork, nullptr);
   } else {
     const int ntiles = segs.tiles0[segs.nseg];
     const int per = ((K + 31) / 32 + splits - 1) / splits;

@@ -28,10 +28,16 @@ struct BigTiles {
 
 E3_DEV int swz(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 1) & 3)); }  // in 16-byte chunks
 
+// FUSE: the two segments are the gate and up projections (F rows each); a
+// tile covers 128 output columns n0 .. n0 + 127 of both, arranged so that in
+// each wave the 16-column blocks alternate gate, up, gate, up ... over the
+// same columns, and the epilogue writes act[m][n] = bf16(silu(g) * u)
+// directly (no K split).
+template <bool FUSE>
 __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
                                                           BigTiles bt, float* __restrict__ out, int ldo,
                                                           size_t split_stride, int kchunk, int S, int mtiles,
-                                                          int nwork) {
+                                                          int nwork, bf16_t* __restrict__ act, int F) {
   __shared__ __attribute__((aligned(16))) u32x4 as[2][BM * 4];
   __shared__ __attribute__((aligned(16))) u32x4 bs[2][BN * 4];
   const int per = (nwork + 7) >> 3;
@@ -60,8 +66,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, n = n0 + (c >> 2);
-    bp[i] = W + (size_t)(n < nrows ? n : 0) * K + (c & 3) * 8;
+    const int c = tid + 256 * i;
+    if (FUSE) {  // tile row q: half h = q / 128, 16-row block j, row l; odd blocks are up rows
+      const int q = c >> 2, h = q >> 7, j = (q & 127) >> 4, l = q & 15;
+      const int n = ntile * 128 + 64 * h + 16 * (j >> 1) + l;
+      const bf16_t* Wg = (const bf16_t*)segs.w[j & 1];
+      bp[i] = Wg + (size_t)(n < F ? n : 0) * K + (c & 3) * 8;
+    } else {
+      const int n = n0 + (c >> 2);
+      bp[i] = W + (size_t)(n < nrows ? n : 0) * K + (c & 3) * 8;
+    }
   }
   u32x4 ar0[2], br0[4], ar1[2], br1[4];
   auto fetch = [&](u32x4 (&ar)[2], u32x4 (&br)[4], int k0) {
@@ -120,6 +134,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
     step(s + 1, ar0, br0, ar1, br1);
   }
   if (s < nsteps) step(s, ar1, br1, ar0, br0);
+  if (FUSE) {  // acc[i][2t] = gate, acc[i][2t + 1] = up at column ntile*128 + wn/2 + 16 t + lr
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = ntile * 128 + (wn >> 1) + 16 * t + lr;
+      if (n >= F) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm + 16 * i + 4 * lg + r;
+          const float g = acc[i][2 * t][r], u = acc[i][2 * t + 1][r];
+          if (m < M) act[(size_t)m * F + n] = f2bf(g / (1.f + expf(-g)) * u);
+        }
+    }
+    return;
+  }
   // acc[i][j][r] = out[m0 + wm + 16 i + 4 lg + r][n0 + wn + 16 j + lr]
   float* o = out + split * split_stride + segs.col0[seg];
 #pragma unroll
@@ -149,9 +179,22 @@ int gemm_big(const void* X, int M, int K, const GemmSegs& segs, float* out, size
   const int nwork = mtiles * S * bt.tiles0[segs.nseg];
   const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
   if (M > 0)
-    hipExtLaunchKernelGGL(k_gemm_bf16_big, dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0, (const bf16_t*)X, M, K,
-                          segs, bt, out, gemm_ntot(segs), split_stride, kchunk, S, mtiles, nwork);
+    hipExtLaunchKernelGGL(k_gemm_bf16_big<false>, dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
+                          (const bf16_t*)X, M, K, segs, bt, out, gemm_ntot(segs), split_stride, kchunk, S, mtiles,
+                          nwork, (bf16_t*)nullptr, 0);
   return S;
+}
+
+void gemm_big_silu(const void* X, int M, int K, const void* w_gate, const void* w_up, int F, void* act,
+                   hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (M <= 0) return;
+  const GemmSegs segs = make_segs(w_gate, F, w_up, F);
+  BigTiles bt{};
+  const int mtiles = (M + BM - 1) / BM;
+  const int nwork = mtiles * ((F + 127) / 128);
+  const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
+  hipExtLaunchKernelGGL(k_gemm_bf16_big<true>, dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0, (const bf16_t*)X,
+                        M, K, segs, bt, (float*)nullptr, 0, (size_t)0, K, 1, mtiles, nwork, (bf16_t*)act, F);
 }
 
 }  // namespace e3

@@ -33,6 +33,12 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
 constexpr int GEMM_BIG_ROWS = 256, GEMM_BIG_KSTEP = 32;
 int gemm_big(const void* X, int M, int K, const GemmSegs& segs, float* out, size_t split_stride, int splits,
              hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+// act[m][n] = bf16(silu(X w_gate^T) * (X w_up^T)) in one GEMM launch, no partials:
+// gemm_silu for bf16 with 16 < M <= 64 (skinny kernel), gemm_big_silu for M > 64.
+void gemm_silu(const void* X, int M, int K, const void* w_gate, const void* w_up, int F, void* act, hipStream_t st,
+               hipEvent_t ev_start, hipEvent_t ev_stop);
+void gemm_big_silu(const void* X, int M, int K, const void* w_gate, const void* w_up, int F, void* act,
+                   hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 // Number of K splits gemm() will actually use for a requested count.
 int gemm_splits(bool bf16, int K, int splits, int m_tile);
 // Weight rows per workgroup of the kernel gemm() picks.
