@@ -182,9 +182,9 @@ def cpu_baseline(w):
 
 
 KERNEL_NAMES = {
-    0: "k_gemm_bf16<4,1,128,8> (64-row MFMA weight-streaming GEMM)",
-    1: "k_gemm_bf16<1,2,256,4> (16-row MFMA weight-streaming GEMM)",
-    3: "k_gemm_bf16_big (128x128-tile MFMA GEMM)",
+    0: "k_gemm_bf16<4,*,*> (64-row MFMA weight-streaming GEMMs, packed weights)",
+    1: "k_gemm_bf16<1,2,4,*> (16-row MFMA weight-streaming GEMMs, packed weights)",
+    3: "k_gemm_bf16_big (128x256-tile MFMA GEMM)",
 }
 
 

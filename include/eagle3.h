@@ -31,7 +31,10 @@
  *     thread-safe; calls that overlap on one context race.
  *   - Element type "T" is the shape's storage dtype: float for EAGLE3_F32,
  *     bfloat16 (uint16 bits, round-to-nearest-even) for EAGLE3_BF16.
- *   - Linear weights are [out_features, in_features] row-major (y = x W^T).
+ *   - Linear weights W are [out_features, in_features] (y = x W^T): row-major
+ *     for EAGLE3_F32, and for EAGLE3_BF16 in the packed slab layout that
+ *     eagle3_pack_linear produces (the embedding table and the norm vectors
+ *     are never packed).
  *   - Errors: synchronous argument checks return a nonzero eagle3_status and
  *     launch nothing.  Data-dependent faults found on the device (a capacity
  *     overflow, a malformed tree) set bits in the context's device status word
@@ -144,6 +147,28 @@ eagle3_status eagle3_create(const eagle3_shape *shape /* host */, const eagle3_s
                             void *kv_target, void *kv_draft, void *stream,
                             eagle3_ctx **out /* host */);
 eagle3_status eagle3_destroy(eagle3_ctx *ctx);
+
+/* Convert one linear weight W [rows, cols] (row-major, out_features x
+ * in_features) into the layout the context's GEMM kernels stream.
+ *   EAGLE3_BF16: cols % 128 == 0 (else EUNSUPPORTED); dst receives
+ *     R16 * cols elements, R16 = 16 ceil(rows / 16) (rows >= rows are zero
+ *     padding).  The columns are cut into 128-wide slabs stored one after the
+ *     other; slab t holds the 16-row blocks in order, each as four 16 x 32
+ *     MFMA operand fragments of 64 lanes x 8 consecutive bf16 (lane l: row
+ *     l % 16, columns 8 (l / 16) .. + 7 of the fragment).  Element (n, k)
+ *     lands at index
+ *     ((k / 128 * (R16 / 16) + n / 16) * 4 + (k % 128) / 32) * 512
+ *       + ((n % 16) + 16 * ((k % 32) / 8)) * 8 + k % 8.
+ *     This lets every weight load of the bf16 GEMMs be one contiguous 1 KiB
+ *     fragment per wave, with all workgroups sweeping the same slab at once.
+ *   EAGLE3_F32: a plain copy of rows * cols floats (fp32 weights are used
+ *     row-major).
+ * src and dst are caller-owned device buffers that must not overlap (EINVAL).
+ * Asynchronous on `stream` (a hipStream_t; NULL = null stream).  Which
+ * weights take this layout: wq, wk, wv, wo, w_gate, w_up, w_down of every
+ * target layer and of the head, the head's fc, and the shared lm_head. */
+eagle3_status eagle3_pack_linear(int32_t dtype, const void *src, void *dst, int32_t rows, int32_t cols,
+                                 void *stream);
 
 /* Target pass over n_rows new rows of each of `batch` sequences (cache slots
  * [seq_begin, seq_begin + batch)).  Row i of sequence b has token

@@ -23,6 +23,7 @@ EXPORTS = [
     "eagle3_kv_bytes", "eagle3_workspace_bytes", "eagle3_create", "eagle3_destroy", "eagle3_verify_tree",
     "eagle3_draft_prefill", "eagle3_draft_tree", "eagle3_tree_from_logits", "eagle3_accept", "eagle3_compact_kv",
     "eagle3_sample", "eagle3_set_stream", "eagle3_status_string", "eagle3_device_status", "eagle3_profile", "eagle3_profile_read",
+    "eagle3_pack_linear",
 ]
 
 
@@ -75,6 +76,7 @@ def lib():
             "eagle3_create": [C.POINTER(Shape), C.POINTER(SpecCfg), C.POINTER(TargetWeights), C.POINTER(HeadWeights),
                               I32, I32, I32, P, C.c_size_t, P, P, P, C.POINTER(P)],
             "eagle3_destroy": [P],
+            "eagle3_pack_linear": [I32, P, P, I32, I32, P],
             "eagle3_verify_tree": [P, I32, I32, P, I32, P, P, P, I32, P, P, P, P],
             "eagle3_draft_prefill": [P, I32, I32, P, I32, P, P],
             "eagle3_draft_tree": [P, I32, P, P, P, P, P, P, P, P, P, P, P, P],
@@ -132,6 +134,10 @@ def eagle3_create(shape: Shape, cfg: SpecCfg, target: TargetWeights, head: HeadW
 
 def eagle3_destroy(ctx: int):
     _check(lib().eagle3_destroy(ctx), "eagle3_destroy")
+
+
+def eagle3_pack_linear(dtype: int, src: int, dst: int, rows: int, cols: int, stream: int):
+    _check(lib().eagle3_pack_linear(dtype, src, dst, rows, cols, stream), "eagle3_pack_linear")
 
 
 def eagle3_verify_tree(ctx, seq_begin, batch, seq_lens, n_rows, tokens, pos, mask, lm_mode, logits, argmax, margin,

@@ -327,13 +327,14 @@ int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, flo
 }
 
 // abuf = T(silu(X w_gate^T) * (X w_up^T)) for X [M, K]: fused into the GEMM's
-// epilogue for bf16 with M > 16 (the 64-row and large-M kernels), else GEMM
-// partials + silu_mul (the 16-row kernel needs its K splits to fill the chip).
+// epilogue for bf16 when the fused launch has enough workgroups without a K
+// split (M > 64, or F / 64 >= 128 column groups), else GEMM partials +
+// silu_mul.
 void run_gateup(eagle3_ctx* c, const void* X, int M, int K, const void* w_gate, const void* w_up, int F) {
-  if (c->bf16 && M > 16) {
+  if (c->bf16 && (M > 64 || F / 64 >= 128)) {
     ProfRec rec{};
     const double bytes = 2.0 * F * K * c->esz + (double)M * K * c->esz + (double)M * F * c->esz;
-    const int kid = M > 64 ? EAGLE3_PROF_GEMM_BIG : EAGLE3_PROF_GEMM_M64;
+    const int kid = M > 64 ? EAGLE3_PROF_GEMM_BIG : (M > 16 ? EAGLE3_PROF_GEMM_M64 : EAGLE3_PROF_GEMM_M16);
     prof_begin(c, kid, bytes, 4.0 * M * F * K, &rec, false);
     if (M > 64)
       gemm_big_silu(X, M, K, w_gate, w_up, F, c->abuf, c->st, rec.a, rec.b);
@@ -639,6 +640,23 @@ eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, c
   }
   *out = c;
   return EAGLE3_OK;
+}
+
+eagle3_status eagle3_pack_linear(int32_t dtype, const void* src, void* dst, int32_t rows, int32_t cols,
+                                 void* stream) {
+  if (!src || !dst || rows < 1 || cols < 1) return EAGLE3_EINVAL;
+  if (dtype != EAGLE3_F32 && dtype != EAGLE3_BF16) return EAGLE3_EINVAL;
+  const bool bf = dtype == EAGLE3_BF16;
+  const size_t sbytes = (size_t)rows * cols * (bf ? 2 : 4);
+  const size_t dbytes = bf ? (size_t)(rows + 15) / 16 * 16 * cols * 2 : sbytes;
+  const char *s0 = (const char*)src, *d0 = (const char*)dst;
+  if (s0 < d0 + dbytes && d0 < s0 + sbytes) return EAGLE3_EINVAL;  // overlapping buffers
+  const hipStream_t st = (hipStream_t)stream;
+  if (!bf)
+    return hipMemcpyAsync(dst, src, sbytes, hipMemcpyDeviceToDevice, st) == hipSuccess ? EAGLE3_OK : EAGLE3_EHIP;
+  if (cols % PACK_KB) return EAGLE3_EUNSUPPORTED;
+  pack_linear(src, dst, rows, cols, st);
+  return hipGetLastError() == hipSuccess ? EAGLE3_OK : EAGLE3_EHIP;
 }
 
 eagle3_status eagle3_destroy(eagle3_ctx* c) {

@@ -1,14 +1,24 @@
 // Weight-streaming GEMM for the step's linear layers: out = X W^T.
 //
-// X [M, K] activations (rows of one verify / draft pass), W [N, K] weights in
-// nn.Linear layout.  At the batch-1 shapes M is 1..64 and every weight byte is
-// read once per pass, so the kernel is HBM-bound: each wave streams 16 weight
-// rows straight from global memory into MFMA operand registers (16-byte loads
-// along K, next K-tile prefetched while the current one is multiplied), and
-// the activation tile is staged once per workgroup in LDS and shared by the
-// four waves.  K is optionally split across workgroups (fp32 partials, summed
-// in a fixed order by the consumer kernel), which keeps enough workgroups in
-// flight on 256 CUs when N is small.
+// X [M, K] activations (rows of one verify / draft pass); W [N, K] is a bf16
+// weight in the packed layout below (fp32 weights stay row-major).  At the
+// batch-1 shapes M is 1..64 and every weight byte is read once per pass, so
+// the kernel is HBM-bound: each wave streams its 16-row weight blocks
+// straight from global memory into MFMA operand registers with nontemporal
+// 16-byte loads (one fully used 1 KiB fragment per wave instruction), two K
+// steps ahead of the multiply, and the activation tile is staged in LDS and
+// shared by the waves.  K is optionally split across workgroups (fp32
+// partials, summed in a fixed order by the consumer kernel), which keeps
+// enough workgroups in flight on 256 CUs when N is small.
+//
+// Packed weight layout ("slab" layout): K is cut into 128-wide slabs and the
+// slabs are stored one after the other; inside slab t come the 16-row blocks
+// rb = 0 .. N/16 - 1 in order, each as four MFMA fragments (K 32f .. 32f + 31
+// of the slab, f = 0..3) of 64 lanes x 8 consecutive bf16: lane l holds row
+// 16 rb + l % 16 and K 8 (l / 16) .. + 7 of the fragment.  All workgroups
+// work through the K slabs at roughly the same pace, so at any moment the
+// whole chip reads one contiguous region of each weight (good DRAM page
+// locality), and every fragment load is a contiguous 1 KiB.
 //
 // MFMA v_mfma_f32_16x16x32_bf16: A (16x32) and B (32x16) fragments hold, in
 // lane l, row/column (l % 16) and K elements 8*(l/16) .. 8*(l/16)+7; the
@@ -65,31 +75,55 @@ __host__ TileMap tile_map(const GemmSegs& s, int rows_per_tile) {
   return t;
 }
 
-// Skinny GEMM: MB 16-row activation blocks (M <= 16 MB per workgroup), each of
-// the NW waves owns NB 16-row weight blocks, K in LDS tiles of KTT.  K must be
-// a multiple of KTT (the shapes are checked on the host).
-// Work item lam = (m-tile, K split, N tile), m-tile fastest.  Workgroups are
-// dispatched round-robin over the 8 XCDs, so workgroup L runs item
-// (L % 8) * per + L / 8: the m-tiles of one weight tile land on the same XCD
-// back to back and re-read that tile from its L2 rather than from HBM.
+// Packing: one thread per 16-byte destination chunk (a coalesced store; the
+// source reads are 16-byte gathers).  Rows N .. 16 ceil(N / 16) - 1 of the
+// last block are zeros.
+__global__ void k_pack_linear(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, int N, int K) {
+  const int nb16 = (N + 15) >> 4;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)nb16 * 16 * K / 8) return;
+  const int lane = (int)(i & 63);
+  size_t f = i >> 6;
+  const int fi = (int)(f & 3);
+  f >>= 2;
+  const size_t rb = f % nb16, t = f / nb16;
+  const size_t n = rb * 16 + (lane & 15);
+  const size_t k = t * PACK_KB + 32 * fi + 8 * (lane >> 4);
+  *(u32x4*)(dst + i * 8) = n < (size_t)N ? *(const u32x4*)(src + n * K + k) : u32x4{0u, 0u, 0u, 0u};
+}
+
+void pack_linear(const void* src, void* dst, int N, int K, hipStream_t st) {
+  const size_t chunks = (size_t)((N + 15) / 16) * 16 * K / 8;
+  if (chunks == 0) return;
+  k_pack_linear<<<(unsigned)((chunks + 255) / 256), 256, 0, st>>>((const bf16_t*)src, (bf16_t*)dst, N, K);
+}
+
+// Skinny GEMM: MB 16-row activation blocks (M <= 16 MB per workgroup); each
+// of the NW waves owns NB 16-row weight blocks; K in steps of one 128-wide
+// slab.  Work item lam = (m-tile, K split, N tile), m-tile fastest.
+// Workgroups are dispatched round-robin over the 8 XCDs, so workgroup L runs
+// item (L % 8) * per + L / 8: the m-tiles of one weight tile land on the
+// same XCD back to back and re-read that tile from its L2 rather than HBM.
 //
-// FUSE (NB = 1, no K split): the two segments are the gate and up projections
-// (F rows each); waves 0 .. NW/2 - 1 own gate rows and waves NW/2 .. NW - 1 the
-// up rows of the same 16 NW / 2 columns, and the epilogue exchanges the up
-// values through LDS and writes act[m][n] = bf16(silu(g) * u).
-template <int MB, int NB, int KTT, int NW, bool FUSE = false>
+// FUSE (NB = 2, no K split): the two segments are the gate and up
+// projections (F rows each); wave w's block 0 is gate rows and block 1 the up
+// rows of the same 16 columns, and the epilogue writes
+// act[m][n] = bf16(silu(g) * u) straight from the accumulators.
+template <int MB, int NB, int NW, bool FUSE>
 __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
                                                    TileMap tm, float* __restrict__ out, int ldo, size_t split_stride,
                                                    int kchunk, int mtiles, int S, int nwork,
                                                    bf16_t* __restrict__ act) {
-  static_assert(!FUSE || NB == 1, "the fused gate/up epilogue pairs single-block waves");
-  constexpr int KS = KTT / 32;
+  static_assert(!FUSE || NB == 2, "the fused gate/up epilogue pairs a gate and an up block in each wave");
+  constexpr int KT = PACK_KB;               // K per step: one slab
+  constexpr int KS = KT / 32;               // fragments per block and step
   constexpr int NT = 64 * NW;               // threads
-  constexpr int ROWS = 16 * NB * NW;        // weight rows per workgroup
-  constexpr int CPR = KTT / 8;              // 16-byte chunks per activation row
+  constexpr int ROWS = FUSE ? 16 * NW : 16 * NB * NW;  // output columns per workgroup
+  constexpr int CPR = KT / 8;               // 16-byte chunks per activation row
   constexpr int XCH = 16 * MB * CPR / NT;   // chunks per thread
+  constexpr int D = 3;                      // register ring depth (steps)
   static_assert(XCH * NT == 16 * MB * CPR, "activation tile splits evenly over the threads");
-  __shared__ __attribute__((aligned(16))) bf16_t xs[2][16 * MB][KTT + XPAD];
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2][16 * MB][KT + XPAD];
   const int per = (nwork + 7) >> 3;
   const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (lam >= nwork) return;
@@ -98,25 +132,26 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
   int seg = 0;
   while (!FUSE && seg + 1 < segs.nseg && ntile >= tm.tiles0[seg + 1]) ++seg;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const bool up_wave = FUSE && wv >= NW / 2;
-  const int n0 = FUSE ? ntile * (ROWS / 2) : (ntile - tm.tiles0[seg]) * ROWS;
-  const bf16_t* __restrict__ W = (const bf16_t*)segs.w[FUSE ? (up_wave ? 1 : 0) : seg];
-  const int nrows = segs.rows[seg];
+  const int n0 = FUSE ? ntile * ROWS : (ntile - tm.tiles0[seg]) * ROWS;
+  const int nrows = segs.rows[seg];  // FUSE: F, the rows of each of the two matrices
+  const size_t slab = (size_t)((nrows + 15) >> 4) * (4 * 512);  // elements per K slab
   const int m0 = mt * 16 * MB;
   const int kb = split * kchunk;
   const int ke = min(K, kb + kchunk);
   const int lr = lane & 15, lg = lane >> 4;
 
-  // weight fragment sources: rows n0 + 16 (NB wv + nb) + lr, K offset 8 lg in each 32-step.
-  // Rows past the segment read row 0 instead (their results are not stored),
-  // and activation rows past M repeat row M - 1, so every load is unconditional.
+  // The wave's weight blocks: lane's 16 bytes of fragment 0 of slab 0.  A
+  // block past the segment reads block 0 instead, the padding rows of a
+  // partial last block are zeros (neither result is stored), and activation
+  // rows past M repeat row M - 1, so every load is unconditional.
   const bf16_t* wp[NB];
   bool wok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int r = FUSE ? n0 + 16 * (wv % (NW / 2)) + lr : n0 + 16 * (NB * wv + nb) + lr;
-    wok[nb] = r < nrows;
-    wp[nb] = W + (size_t)(wok[nb] ? r : 0) * K + 8 * lg;
+    const int r0 = FUSE ? n0 + 16 * wv : n0 + 16 * (NB * wv + nb);
+    wok[nb] = r0 < nrows;
+    const bf16_t* W = (const bf16_t*)segs.w[FUSE ? nb : seg];
+    wp[nb] = W + (size_t)(wok[nb] ? r0 >> 4 : 0) * (4 * 512) + 8 * lane;
   }
   const bf16_t* xp[XCH];
 #pragma unroll
@@ -124,32 +159,31 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
     const int c = tid + NT * i, row = c / CPR, col = (c % CPR) * 8;
     xp[i] = X + (size_t)min(m0 + row, M - 1) * K + col;
   }
-  u32x4 x0[XCH], x1[XCH];
-  u32x4 w0[NB][KS], w1[NB][KS], w2[NB][KS];
+  u32x4 xr[D][XCH];
+  u32x4 wr[D][NB][KS];
   f32x4 acc[NB][MB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int i = 0; i < MB; ++i) acc[nb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto load_w = [&](u32x4 (&dst)[NB][KS], int kt) {
+  auto load = [&](int slot, int kt) {  // kt: first K of the step (a slab boundary)
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) xr[slot][i] = *(const u32x4*)(xp[i] + kt);
+    const size_t off = (size_t)(kt / KT) * slab;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) dst[nb][s] = *(const u32x4*)(wp[nb] + kt + 32 * s);
+      for (int s = 0; s < KS; ++s)
+        wr[slot][nb][s] = __builtin_nontemporal_load((const u32x4*)(wp[nb] + off + 512 * s));
   };
-  auto load_x = [&](u32x4 (&dst)[XCH], int kt) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) dst[i] = *(const u32x4*)(xp[i] + kt);
-  };
-  auto store_x = [&](const u32x4 (&src)[XCH], int buf) {
+  auto store_x = [&](int slot, int buf) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int c = tid + NT * i, row = c / CPR, col = (c % CPR) * 8;
-      *(u32x4*)&xs[buf][row][col] = src[i];
+      *(u32x4*)&xs[buf][row][col] = xr[slot][i];
     }
   };
-  auto mul = [&](const u32x4 (&wc)[NB][KS], int buf) {
+  auto mul = [&](int slot, int buf) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       bf16x8 a[MB];
@@ -158,80 +192,60 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
         a[mb] = __builtin_bit_cast(bf16x8, *(const u32x4*)&xs[buf][16 * mb + lr][32 * s + 8 * lg]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, wc[nb][s]);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, wr[slot][nb][s]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[nb][mb], 0, 0, 0);
       }
     }
   };
-  // Pipeline over K steps of KTT.  Weights: three register buffers, so while
-  // step i is multiplied, steps i + 1 and i + 2 are in flight.  Activations:
-  // two register buffers and two LDS tiles; the tile of step i + 1 is written
-  // to LDS at the end of step i (its loads were issued a step earlier), and one
-  // barrier per step both publishes it and retires the tile just read.  Past
-  // the last step the loads repeat the last step's addresses.
-  const int nsteps = (ke - kb) / KTT;
-  const int klast = kb + (nsteps - 1) * KTT;
-  auto step = [&](int i, const u32x4 (&cur)[NB][KS], u32x4 (&ahead)[NB][KS], const u32x4 (&xnext)[XCH],
-                  u32x4 (&xafter)[XCH]) {
-    // xnext holds the activations of step i + 1; xafter receives those of step i + 2
-    load_x(xafter, min(kb + (i + 2) * KTT, klast));
-    load_w(ahead, min(kb + (i + 2) * KTT, klast));
+  // Pipeline over K steps: a ring of D register slots holds the loads of
+  // steps i .. i + D - 1 (weights and activations alike).  Step i (slot
+  // j = i % D) first issues the loads of step i + D - 1 into the slot step
+  // i - 1 freed, multiplies slot j against LDS tile i & 1, then writes the
+  // activations of step i + 1 (loaded D - 2 steps earlier) to the other LDS
+  // tile; one barrier per step publishes that tile and retires the one just
+  // read.  Past the last step the loads repeat the last step's addresses.
+  const int nsteps = (ke - kb) / KT;
+  const int klast = kb + (nsteps - 1) * KT;
+  auto step = [&](int i, int j) {
+    load((j + D - 1) % D, min(kb + (i + D - 1) * KT, klast));
     __builtin_amdgcn_sched_barrier(0);  // issue the loads before the multiplies
-    mul(cur, i & 1);
-    store_x(xnext, (i + 1) & 1);
+    mul(j, i & 1);
+    store_x((j + 1) % D, (i + 1) & 1);
     __syncthreads();
   };
   if (nsteps > 0) {
-    load_x(x0, kb);
-    load_x(x1, min(kb + KTT, klast));
-    load_w(w0, kb);
-    load_w(w1, min(kb + KTT, klast));
-    store_x(x0, 0);
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) load(j, min(kb + j * KT, klast));
+    store_x(0, 0);
     __syncthreads();
     int i = 0;
-    for (; i + 6 <= nsteps; i += 6) {
-      step(i, w0, w2, x1, x0);
-      step(i + 1, w1, w0, x0, x1);
-      step(i + 2, w2, w1, x1, x0);
-      step(i + 3, w0, w2, x0, x1);
-      step(i + 4, w1, w0, x1, x0);
-      step(i + 5, w2, w1, x0, x1);
+    for (; i + D <= nsteps; i += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) step(i + j, j);
     }
-    // remaining steps: the buffer roles continue from i (a multiple of 6)
-    if (i < nsteps) step(i, w0, w2, x1, x0);
-    if (i + 1 < nsteps) step(i + 1, w1, w0, x0, x1);
-    if (i + 2 < nsteps) step(i + 2, w2, w1, x1, x0);
-    if (i + 3 < nsteps) step(i + 3, w0, w2, x0, x1);
-    if (i + 4 < nsteps) step(i + 4, w1, w0, x1, x0);
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j)
+      if (i + j < nsteps) step(i + j, j);
   }
   if (FUSE) {
-    __shared__ float ub[NW / 2][16 * MB][17];  // up values: [wave pair][row][column]
-    if (up_wave) {
+    const int n = n0 + 16 * wv + lr;
+    if (n >= nrows) return;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ub[wv - NW / 2][16 * mb + 4 * lg + r][lr] = acc[0][mb][r];
-    }
-    __syncthreads();
-    if (!up_wave && wok[0]) {
-      const int n = n0 + 16 * wv + lr;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ml = 16 * mb + 4 * lg + r, m = m0 + ml;
-          const float g = acc[0][mb][r], u = ub[wv][ml][lr];
-          if (m < M) act[(size_t)m * nrows + n] = f2bf(g / (1.f + expf(-g)) * u);
-        }
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * mb + 4 * lg + r;
+        const float g = acc[0][mb][r], u = acc[1][mb][r];
+        if (m < M) act[(size_t)m * nrows + n] = f2bf(g / (1.f + expf(-g)) * u);
+      }
     return;
   }
   // result: acc[nb][mb][r] = out[m0 + 16 mb + 4 lg + r][n0 + 16 (NB wv + nb) + lr]
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    if (!wok[nb]) continue;
+    if (n0 + 16 * (NB * wv + nb) + lr >= nrows) continue;
     float* o = out + split * split_stride + segs.col0[seg] + n0 + 16 * (NB * wv + nb) + lr;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -243,10 +257,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
   }
 }
 
-// K tile and weight rows per workgroup of the two skinny variants:
-// M <= 16: <MB 1, NB 2, KTT 256, 4 waves>; M <= 64: <MB 4, NB 1, KTT 128, 8 waves>.
-constexpr int KT16 = 256, KT64 = 128;
-constexpr int ROWS16 = 16 * 2 * 4, ROWS64 = 16 * 1 * 8;
+// The skinny variants: M <= 16: <MB 1, NB 2, 4 waves>; M <= 64: <MB 4, NB 1,
+// 8 waves>; both cover 128 weight rows per workgroup.  Fused gate/up: 4 waves
+// of one gate + one up block, 64 output columns per workgroup.
+constexpr int ROWS16 = 16 * 2 * 4, ROWS64 = 16 * 1 * 8, SILU_COLS = 16 * 4;
 
 // fp32 GEMM (the tiny fp32 workload): 32 x 64 output tile per workgroup, each
 // thread 2 x 4 outputs, K tiles of 32 staged in LDS for both operands.
@@ -294,7 +308,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ X, i
 }
 
 int gemm_splits(bool bf16, int K, int splits, int m_tile) {
-  const int unit = !bf16 ? 32 : (m_tile == 16 ? KT16 : (m_tile == 64 ? KT64 : GEMM_BIG_KSTEP));
+  const int unit = !bf16 ? 32 : (m_tile <= 64 ? PACK_KB : GEMM_BIG_KSTEP);
   const int kt = (K + unit - 1) / unit;
   if (splits < 1) splits = 1;
   if (splits > kt) splits = kt;
@@ -307,12 +321,16 @@ void gemm_silu(const void* X, int M, int K, const void* w_gate, const void* w_up
   if (M <= 0) return;
   const GemmSegs segs = make_segs(w_gate, F, w_up, F);
   const TileMap tm{};
-  constexpr int COLS = ROWS64 / 2;  // output columns per workgroup
-  const int nwork = (F + COLS - 1) / COLS;
+  const int nwork = (F + SILU_COLS - 1) / SILU_COLS;
   const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
-  hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, KT64, 8, true>), dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0,
-                        (const bf16_t*)X, M, K, segs, tm, (float*)nullptr, 0, (size_t)0, K, 1, 1, nwork,
-                        (bf16_t*)act);
+  if (M <= 16)
+    hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, 4, true>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
+                          (const bf16_t*)X, M, K, segs, tm, (float*)nullptr, 0, (size_t)0, K, 1, 1, nwork,
+                          (bf16_t*)act);
+  else
+    hipExtLaunchKernelGGL((k_gemm_bf16<4, 2, 4, true>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
+                          (const bf16_t*)X, M, K, segs, tm, (float*)nullptr, 0, (size_t)0, K, 1, 1, nwork,
+                          (bf16_t*)act);
 }
 
 int gemm_rows_per_tile(bool bf16, int m_tile) {
@@ -329,10 +347,9 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
   if (M <= 0) return splits;
   const int ldo = gemm_ntot(segs);
   if (bf16) {
-    const int unit = m_tile == 16 ? KT16 : KT64;
-    const int ktiles = K / unit;
+    const int ktiles = K / PACK_KB;
     const int per = (ktiles + splits - 1) / splits;
-    const int kchunk = per * unit;
+    const int kchunk = per * PACK_KB;
     const int S = (ktiles + per - 1) / per;
     const TileMap tm = tile_map(segs, m_tile == 16 ? ROWS16 : ROWS64);
     const int ntiles = tm.tiles0[segs.nseg];
@@ -340,11 +357,13 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
     const int nwork = mtiles * S * ntiles;
     const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
     if (m_tile == 16)
-      hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, KT16, 4>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
-                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork, nullptr);
+      hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, 4, false>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
+                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
+                            (bf16_t*)nullptr);
     else
-      hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, KT64, 8>), dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0,
-                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork, nullptr);
+      hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, 8, false>), dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0,
+                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
+                            (bf16_t*)nullptr);
   } else {
     const int ntiles = segs.tiles0[segs.nseg];
     const int per = ((K + 31) / 32 + splits - 1) / splits;

@@ -1,5 +1,6 @@
 // Large-M bf16 GEMM (prefill chunks, batch-64 verify): out = X W^T with
-// X [M, K] and W [N, K] (nn.Linear layout), fp32 partials per K split.
+// X [M, K] row-major and W [N, K] in the packed slab layout, fp32 partials
+// per K split.
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -11,7 +12,8 @@ namespace e3 {
 
 // Large-M GEMM (prefill chunks, batch-64 verify): 128 (M) x 256 (N) output
 // tile per workgroup, K in steps of 32 through double-buffered LDS for both
-// operands.  Four waves in a 2 x 2 arrangement each own a 64 x 128 sub-tile
+// operands; a step's weight tile is one packed fragment (1 KiB, contiguous)
+// of each of the tile's sixteen 16-row blocks.  Four waves in a 2 x 2 arrangement each own a 64 x 128 sub-tile
 // (4 x 8 MFMA blocks of 16 x 16), so every operand fragment read from LDS
 // feeds 4 or 8 MFMAs.  LDS rows are 64 bytes (four 16-byte chunks) with the
 // chunk index XOR-swizzled by (row / 2) % 4: any eight consecutive lanes of
@@ -55,8 +57,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int wm = (wv & 1) * 64, wn = (wv >> 1) * 128;
-  // staging: A chunk c = tid + 256 i (i < 2), B chunk c = tid + 256 i (i < 4): row c / 4, K chunk c % 4.
-  // Rows past M (or past the segment) read row M - 1 (row 0); their results are not stored.
+  // staging: A chunk c = tid + 256 i (i < 2): row c / 4, K chunk c % 4.  B
+  // chunk c = tid + 256 i (i < 4): lane c % 64 of the fragment of tile block
+  // c / 64, i.e. tile row 16 (c / 64) + c % 16, K chunk (c % 64) / 16.  Rows
+  // past M read row M - 1 and blocks past the segment read block 0; their
+  // results are not stored.
   const bf16_t* ap[2];
   const bf16_t* bp[4];
 #pragma unroll
@@ -64,25 +69,30 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
     const int c = tid + 256 * i;
     ap[i] = X + (size_t)min(m0 + (c >> 2), M - 1) * K + (c & 3) * 8;
   }
+  const int bn = FUSE ? F : nrows;  // rows of the packed matrix (both FUSE matrices have F)
+  const size_t slab = (size_t)((bn + 15) >> 4) * (4 * 512);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    if (FUSE) {  // tile row q: half h = q / 128, 16-row block j, row l; odd blocks are up rows
-      const int q = c >> 2, h = q >> 7, j = (q & 127) >> 4, l = q & 15;
-      const int n = ntile * 128 + 64 * h + 16 * (j >> 1) + l;
-      const bf16_t* Wg = (const bf16_t*)segs.w[j & 1];
-      bp[i] = Wg + (size_t)(n < F ? n : 0) * K + (c & 3) * 8;
+    const int c = tid + 256 * i, jj = c >> 6, l = c & 63;
+    int rb;
+    const bf16_t* Wb;
+    if (FUSE) {  // tile block jj: half h = jj / 8, block j = jj % 8 of it; odd blocks are up rows
+      const int h = jj >> 3, j = jj & 7;
+      rb = ntile * 8 + 4 * h + (j >> 1);
+      Wb = (const bf16_t*)segs.w[j & 1];
     } else {
-      const int n = n0 + (c >> 2);
-      bp[i] = W + (size_t)(n < nrows ? n : 0) * K + (c & 3) * 8;
+      rb = (n0 >> 4) + jj;
+      Wb = W;
     }
+    bp[i] = Wb + (size_t)(16 * rb < bn ? rb : 0) * (4 * 512) + 8 * l;
   }
   u32x4 ar0[2], br0[4], ar1[2], br1[4];
   auto fetch = [&](u32x4 (&ar)[2], u32x4 (&br)[4], int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) ar[i] = *(const u32x4*)(ap[i] + k0);
+    const size_t off = (size_t)(k0 / PACK_KB) * slab + ((k0 % PACK_KB) / 32) * 512;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) br[i] = *(const u32x4*)(bp[i] + k0);
+    for (int i = 0; i < 4; ++i) br[i] = *(const u32x4*)(bp[i] + off);
   };
   auto stash = [&](const u32x4 (&ar)[2], const u32x4 (&br)[4], int buf) {
 #pragma unroll
@@ -92,8 +102,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      bs[buf][swz(c >> 2, c & 3)] = br[i];
+      const int c = tid + 256 * i, l = c & 63;
+      bs[buf][swz(16 * (c >> 6) + (l & 15), l >> 4)] = br[i];
     }
   };
   f32x4 acc[4][8];

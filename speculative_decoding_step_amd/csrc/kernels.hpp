@@ -6,8 +6,17 @@
 
 namespace e3 {
 
-// Up to three weight matrices stacked along N (e.g. Wq;Wk;Wv).  Each is
-// [rows, K] row-major; output column of segment i starts at col0[i].
+// bf16 linear weights are stored in the packed slab layout read by every bf16
+// GEMM kernel (k_gemm.hip): W [N, K] with K % PACK_KB == 0, rows padded with
+// zeros to N16 = 16 ceil(N / 16), element (n, k) at
+// ((k / 128 * (N16 / 16) + n / 16) * 4 + (k % 128) / 32) * 512
+// + ((n % 16) + 16 * ((k % 32) / 8)) * 8 + k % 8.  fp32 weights stay row-major.
+constexpr int PACK_KB = 128;
+// dst (N16 x K elements) = the packed form of the row-major bf16 matrix src [N, K] (no overlap).
+void pack_linear(const void* src, void* dst, int N, int K, hipStream_t st);
+
+// Up to three weight matrices stacked along N (e.g. Wq;Wk;Wv), each [rows, K]
+// (packed for bf16); output column of segment i starts at col0[i].
 struct GemmSegs {
   const void* w[3];
   int rows[3];
@@ -34,7 +43,7 @@ constexpr int GEMM_BIG_ROWS = 256, GEMM_BIG_KSTEP = 32;
 int gemm_big(const void* X, int M, int K, const GemmSegs& segs, float* out, size_t split_stride, int splits,
              hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 // act[m][n] = bf16(silu(X w_gate^T) * (X w_up^T)) in one GEMM launch, no partials:
-// gemm_silu for bf16 with 16 < M <= 64 (skinny kernel), gemm_big_silu for M > 64.
+// gemm_silu for bf16 with M <= 64 (skinny kernels), gemm_big_silu for M > 64.
 void gemm_silu(const void* X, int M, int K, const void* w_gate, const void* w_up, int F, void* act, hipStream_t st,
                hipEvent_t ev_start, hipEvent_t ev_stop);
 void gemm_big_silu(const void* X, int M, int K, const void* w_gate, const void* w_up, int F, void* act,

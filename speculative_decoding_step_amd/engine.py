@@ -51,13 +51,19 @@ class Engine:
         self.max_rows = max_rows or max(batch * self.rows, batch * self.W, batch * spec.topk, prefill_chunk)
         d, V = ms.d, ms.vocab
 
-        # ---- weights (seeded, generated on the device)
+        # ---- weights (seeded, generated on the device; linear weights are then
+        # converted to the library's packed layout, see eagle3_pack_linear).
+        # A caller-supplied `weights` dict must already hold packed matrices.
+        self.stream = torch.cuda.current_stream(self.dev)
         self.w = weights if weights is not None else {}
         if weights is None:
-            for name, shp, kind in configs.target_tensor_specs(ms):
-                self.w[name] = self._tensor(target_seed, name, shp, kind, sigma)
-            for name, shp, kind in configs.head_tensor_specs(ms):
-                self.w[name] = self._tensor(head_seed, name, shp, kind, sigma)
+            for seed, specs in ((target_seed, configs.target_tensor_specs(ms)),
+                                (head_seed, configs.head_tensor_specs(ms))):
+                for name, shp, kind in specs:
+                    t = self._tensor(seed, name, shp, kind, sigma)
+                    if kind == "mat" and name != "embed":
+                        t = self._pack(t)
+                    self.w[name] = t
         w = self.w
         self.shape = B.Shape(ms.n_layers, d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, V, ms.rope_theta,
                              ms.eps, B.BF16 if self.bf16 else B.F32, (C.c_int32 * 3)(*ms.taps))
@@ -80,7 +86,6 @@ class Engine:
         self.kv_draft = torch.empty(kvd, dtype=torch.uint8, device=self.dev)
         wsb = B.eagle3_workspace_bytes(self.shape, self.cfg, batch, self.max_rows, max_seq)
         self.workspace = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
-        self.stream = torch.cuda.current_stream(self.dev)
         self.ctx = B.eagle3_create(self.shape, self.cfg, self.tw, self.hw, batch, self.max_rows, max_seq,
                                    self.workspace.data_ptr(), wsb, self.kv_target.data_ptr(), self.kv_draft.data_ptr(),
                                    self.stream.cuda_stream)
@@ -116,6 +121,14 @@ class Engine:
         if kind == "norm":
             return torch.ones(shape, dtype=self.tdt, device=self.dev)
         return synth.normal_t(seed, name, shape, self.dev, sigma, self.ms.dtype)
+
+    def _pack(self, t):
+        """The packed copy of a row-major linear weight [out, in] (the original is dropped)."""
+        rows = (t.shape[0] + 15) // 16 * 16 if self.bf16 else t.shape[0]
+        p = torch.empty((rows, t.shape[1]), dtype=t.dtype, device=t.device)
+        B.eagle3_pack_linear(B.BF16 if self.bf16 else B.F32, t.data_ptr(), p.data_ptr(), t.shape[0], t.shape[1],
+                             self.stream.cuda_stream)
+        return p
 
     def close(self):
         if getattr(self, "ctx", None):

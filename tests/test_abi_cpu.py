@@ -4,6 +4,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 from speculative_decoding_step_amd import binding as B
@@ -53,3 +54,36 @@ def test_create_rejects_null_pointers():
     cfg = B.SpecCfg(B.GREEDY_TREE, 6, 10, 60, 0.0, 0)
     with pytest.raises(B.Eagle3Error, match="invalid"):
         B.eagle3_create(s, cfg, B.TargetWeights(), B.HeadWeights(), 1, 512, 2304, None, 0, None, None, None)
+
+
+def packed_index(N, K):
+    """Destination index of every element (n, k) of a packed bf16 [N, K] weight,
+    written from the formula eagle3.h states for eagle3_pack_linear."""
+    R16 = (N + 15) // 16 * 16
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    return ((k // 128 * (R16 // 16) + n // 16) * 4 + (k % 128) // 32) * 512 + ((n % 16) + 16 * ((k % 32) // 8)) * 8 + k % 8
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (1024, 256), (7, 256), (5000, 128)])
+def test_pack_layout_is_a_permutation(N, K):
+    R16 = (N + 15) // 16 * 16
+    idx = packed_index(N, K).ravel()
+    assert len(np.unique(idx)) == N * K and idx.min() >= 0 and idx.max() < R16 * K
+    full = packed_index(R16, K).ravel()  # with the padding rows it is a permutation
+    assert np.array_equal(np.sort(full), np.arange(R16 * K))
+    # one MFMA fragment (64 lanes x 8) is a contiguous 1 KiB: rows 0..15, K 0..31
+    frag = packed_index(R16, K)[:16, :32]
+    assert np.array_equal(np.sort(frag.ravel()), np.arange(512))
+
+
+def test_pack_linear_validation():
+    a, b = 1 << 20, 1 << 32   # never dereferenced: every case below fails its argument checks
+    with pytest.raises(B.Eagle3Error, match="unsupported"):
+        B.eagle3_pack_linear(B.BF16, a, b, 16, 96, None)       # cols % 128
+    with pytest.raises(B.Eagle3Error, match="invalid"):
+        B.eagle3_pack_linear(B.BF16, a, a + 64, 16, 128, None)  # overlapping buffers
+    with pytest.raises(B.Eagle3Error, match="invalid"):
+        B.eagle3_pack_linear(B.BF16, None, b, 16, 128, None)
+    with pytest.raises(B.Eagle3Error, match="invalid"):
+        B.eagle3_pack_linear(7, a, b, 16, 128, None)           # dtype

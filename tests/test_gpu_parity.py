@@ -356,3 +356,21 @@ def test_device_status_flags_bad_inputs():
     with pytest.raises(B.Eagle3Error):
         B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq), 65, _p(toks), None, _p(toks), B.LM_ALL, None, None, None, None)
     eng.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (4096, 1024), (7, 256), (5000, 128)])
+def test_pack_linear_bit_exact(N, K):
+    """eagle3_pack_linear moves every bf16 bit pattern to the index eagle3.h
+    states and zero-fills the padding rows of a partial last 16-row block."""
+    from test_abi_cpu import packed_index
+    R16 = (N + 15) // 16 * 16
+    rng = np.random.default_rng(N + K)
+    w = rng.integers(0, 1 << 16, size=(N, K), dtype=np.uint16)
+    src = torch.as_tensor(w.view(np.int16), device="cuda")
+    dst = torch.full((R16 * K,), -1, dtype=torch.int16, device="cuda")
+    B.eagle3_pack_linear(B.BF16, src.data_ptr(), dst.data_ptr(), N, K, torch.cuda.current_stream().cuda_stream)
+    got = dst.cpu().numpy().view(np.uint16)
+    ref = np.zeros(R16 * K, np.uint16)
+    ref[packed_index(N, K).ravel()] = w.ravel()
+    assert np.array_equal(got, ref)
