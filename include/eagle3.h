@@ -71,7 +71,7 @@ enum { EAGLE3_LM_ALL = 0, EAGLE3_LM_LAST = 1, EAGLE3_LM_NONE = 2 };
 
 /* LLaMA-shaped target (also the draft layer's head layout: Hq, Hkv, hd, ffn). */
 typedef struct {
-  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn, vocab;  /* head_dim % 4 == 0, <= 256 */
   float rope_theta;   /* rotate-half RoPE, inverse frequencies theta^(-2i/hd)      */
   float rms_eps;      /* RMSNorm epsilon                                          */
   int32_t dtype;      /* EAGLE3_F32 or EAGLE3_BF16: weights, activations, KV, aux */

@@ -157,7 +157,7 @@ eagle3_status check_shape(const eagle3_shape* s, const eagle3_spec_cfg* c) {
   if (s->n_layers < 1 || s->d_model < 1 || s->n_heads < 1 || s->n_kv_heads < 1 || s->head_dim < 2 ||
       s->ffn < 1 || s->vocab < 2)
     return EAGLE3_EINVAL;
-  if (s->n_heads % s->n_kv_heads || s->head_dim % 2 || s->head_dim > 256) return EAGLE3_EINVAL;
+  if (s->n_heads % s->n_kv_heads || s->head_dim % 4 || s->head_dim > 256) return EAGLE3_EINVAL;
   if (s->dtype != EAGLE3_F32 && s->dtype != EAGLE3_BF16) return EAGLE3_EINVAL;
   for (int i = 0; i < 3; ++i)
     if (s->taps[i] < 0 || s->taps[i] >= s->n_layers) return EAGLE3_EINVAL;

@@ -87,18 +87,26 @@ __global__ __launch_bounds__(64) void k_attn_partial(const T* __restrict__ q, co
   }
 }
 
-// Merge the chunk partials of one (row, head): out = sum_s e_s o_s / sum_s e_s l_s
-// with e_s = exp(m_s - max_s m_s), summed in chunk order.  Only the chunks that
-// can hold a key the row sees are read (the row's key end comes from its
-// metadata); partials are read eight chunks at a time so their loads overlap.
+// Merge the chunk partials of each (row, head): out = sum_s e_s o_s / sum_s e_s l_s
+// with e_s = exp(m_s - M), M = max_s m_s, summed in chunk order.  Only the
+// chunks that can hold a key the row sees are read (the row's key end comes
+// from its metadata).  A workgroup covers 256 / (hd / 4) heads of one row and
+// a thread one 4-dim slice of one head; the (m, l) pairs and output slices of
+// up to CMB_BATCH chunks are loaded together, so a row costs two dependent
+// memory round trips (metadata, then partials).  Past CMB_BATCH chunks the
+// running sums are rescaled when a later batch raises the maximum.
+constexpr int CMB_BATCH = 16;
 template <typename T>
-__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ o_part,
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ o_part,
                                                       const float* __restrict__ ml_part, int ns, int R, int Hq,
                                                       int hd, const int* __restrict__ rseq,
                                                       const int* __restrict__ rlim, const int* __restrict__ rt0,
                                                       const uint64_t* __restrict__ rmask, int S_cap, int chunk,
                                                       T* __restrict__ out) {
-  const int r = blockIdx.x, h = blockIdx.y;
+  const int r = blockIdx.x;
+  const int tph = hd >> 2;  // threads per head
+  const int h = blockIdx.y * (blockDim.x / tph) + threadIdx.x / tph, d4 = threadIdx.x % tph;
+  if (h >= Hq) return;  // no barrier below
   const size_t sstride = (size_t)R * Hq;  // (row, head) entries per chunk
   const size_t oi0 = (size_t)r * Hq + h;
   int nsr = 0;
@@ -107,35 +115,50 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
     nsr = min(ns, (kend + chunk - 1) / chunk);
   }
   const float2* ml = (const float2*)ml_part;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < nsr; s0 += 8) {
-    float2 v[8];
+  const float4* o4 = (const float4*)o_part;
+  float M = -INFINITY, den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < nsr; s0 += CMB_BATCH) {
+    float2 v[CMB_BATCH];
+    float4 o[CMB_BATCH];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (s0 + j < nsr) ? ml[(s0 + j) * sstride + oi0] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) M = fmaxf(M, v[j].x);
-  }
-  for (int i = threadIdx.x; i < hd; i += blockDim.x) {
-    float den = 0.f, acc = 0.f;
-    for (int s0 = 0; s0 < nsr; s0 += 8) {
-      float2 v[8];
-      float o[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool in = s0 + j < nsr;
-        v[j] = in ? ml[(s0 + j) * sstride + oi0] : make_float2(-INFINITY, 0.f);
-        o[j] = in ? o_part[((s0 + j) * sstride + oi0) * hd + i] : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (v[j].x != -INFINITY) {
-          const float e = expf(v[j].x - M);
-          den += v[j].y * e;
-          acc += o[j] * e;
-        }
+    for (int j = 0; j < CMB_BATCH; ++j) {
+      const bool in = s0 + j < nsr;
+      v[j] = in ? ml[(s0 + j) * sstride + oi0] : make_float2(-INFINITY, 0.f);
+      o[j] = in ? o4[((s0 + j) * sstride + oi0) * tph + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    st<T>(out, oi0 * hd + i, den > 0.f ? acc / den : 0.f);
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < CMB_BATCH; ++j) Mb = fmaxf(Mb, v[j].x);
+    if (Mb > M) {
+      if (M != -INFINITY) {
+        const float c = expf(M - Mb);
+        den *= c;
+        acc.x *= c, acc.y *= c, acc.z *= c, acc.w *= c;
+      }
+      M = Mb;
+    }
+#pragma unroll
+    for (int j = 0; j < CMB_BATCH; ++j)
+      if (v[j].x != -INFINITY) {
+        const float e = expf(v[j].x - M);
+        den += v[j].y * e;
+        acc.x += o[j].x * e, acc.y += o[j].y * e, acc.z += o[j].z * e, acc.w += o[j].w * e;
+      }
   }
+  const size_t ob = oi0 * hd + 4 * d4;
+  st<T>(out, ob, den > 0.f ? acc.x / den : 0.f);
+  st<T>(out, ob + 1, den > 0.f ? acc.y / den : 0.f);
+  st<T>(out, ob + 2, den > 0.f ? acc.z / den : 0.f);
+  st<T>(out, ob + 3, den > 0.f ? acc.w / den : 0.f);
+}
+
+template <typename T>
+void combine(const float* o_part, const float* ml_part, int ns, int R, int Hq, int hd, const RowMeta& rm,
+             int key_bound, int chunk, T* out, hipStream_t st) {
+  const int hpb = 256 / (hd / 4);
+  k_attn_combine<T><<<dim3(R, (Hq + hpb - 1) / hpb), 256, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, rm.seq, rm.lim,
+                                                                   rm.tail0, rm.mask, key_bound, chunk, out);
 }
 
 // ---------------------------------------------------------------- MFMA path
@@ -372,20 +395,24 @@ void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t 
     const int nq = rps * G;
     const int nw = std::min(8, std::max(4, (nq + 15) / 16));  // waves: 16 queries each
     const int qblocks = (nq + 16 * nw - 1) / (16 * nw);
+    // Longer key chunks when the launch has work to spare: fewer partials to
+    // write and merge, and each workgroup's set-up spread over more tiles.
+    const long tiles256 = (long)(R / rps) * qblocks * Hkv * ns;
+    const int chunk = tiles256 >= 4096 ? 3 * ATT_CHUNK : (tiles256 >= 2048 ? 2 * ATT_CHUNK : ATT_CHUNK);
+    ns = (key_bound + chunk - 1) / chunk;
     const int nwork = (R / rps) * qblocks * Hkv * ns;
     const int nblocks = (nwork + 7) / 8 * 8;
     if (hd == 128)
       k_attn_mfma<128><<<nblocks, 64 * nw, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc,
                                                      seq_stride, head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R,
-                                                     rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, ATT_CHUNK,
+                                                     rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk,
                                                      o_part, ml_part);
     else
       k_attn_mfma<64><<<nblocks, 64 * nw, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc,
                                                     seq_stride, head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R,
-                                                    rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, ATT_CHUNK,
+                                                    rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk,
                                                     o_part, ml_part);
-    k_attn_combine<bf16_t><<<dim3(R, Hq), 128, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, rm.seq, rm.lim, rm.tail0,
-                                                        rm.mask, key_bound, ATT_CHUNK, (bf16_t*)out);
+    combine<bf16_t>(o_part, ml_part, ns, R, Hq, hd, rm, key_bound, chunk, (bf16_t*)out, st);
     return;
   }
   dim3 grid(R, Hq, ns);
@@ -393,14 +420,12 @@ void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t 
     k_attn_partial<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
                                                 head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, Hq, Hkv, hd,
                                                 key_bound, scale, o_part, ml_part);
-    k_attn_combine<bf16_t><<<dim3(R, Hq), 128, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, rm.seq, rm.lim, rm.tail0,
-                                                        rm.mask, key_bound, ATT_CHUNK, (bf16_t*)out);
+    combine<bf16_t>(o_part, ml_part, ns, R, Hq, hd, rm, key_bound, ATT_CHUNK, (bf16_t*)out, st);
   } else {
     k_attn_partial<float><<<grid, 64, 0, st>>>((const float*)q, (const float*)kc, (const float*)vc, seq_stride,
                                                head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, Hq, Hkv, hd, key_bound,
                                                scale, o_part, ml_part);
-    k_attn_combine<float><<<dim3(R, Hq), 128, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, rm.seq, rm.lim, rm.tail0,
-                                                       rm.mask, key_bound, ATT_CHUNK, (float*)out);
+    combine<float>(o_part, ml_part, ns, R, Hq, hd, rm, key_bound, ATT_CHUNK, (float*)out, st);
   }
 }
 
