@@ -260,7 +260,8 @@ def traffic_from_counters(workload, kind, fetch_csv, write_csv, copy_fetch_csv, 
     and writes MIB MiB per dispatch: its counters give the scale factors)."""
     import csv
 
-    names = {0: "k_gemm_bf16<4, 1, 128, 8>", 1: "k_gemm_bf16<1, 2, 256, 4>", 3: "k_gemm_bf16_big"}
+    # kernel-name prefixes: the 64-row kernels (plain and fused gate/up), the 16-row ones, the large-M one
+    names = {0: "k_gemm_bf16<4, ", 1: "k_gemm_bf16<1, ", 3: "k_gemm_bf16_big"}
 
     def per_dispatch(path, needle):
         vals = [float(r["Counter_Value"]) * 1024.0 for r in csv.DictReader(open(path)) if needle in r["Kernel_Name"]]
