@@ -299,11 +299,16 @@ int plan_splits(eagle3_ctx* c, int M, int N, int K, int m_tile) {
   if (!c->bf16) return 1;
   const int rows = gemm_rows_per_tile(true, m_tile);
   const int tiles = ((N + rows - 1) / rows) * ((M + m_tile - 1) / m_tile);
-  // about 256 eight-wave (M <= 64) or 512 four-wave (other) workgroups, but
-  // at most 8 splits: every split adds M x N fp32 partials that the consumer
-  // kernel reads back
-  const int target = m_tile == 64 ? 256 : 512;  // large-M kernel: two workgroups per CU
-  int S = (target + tiles / 2) / tiles;
+  // Skinny kernels: about 256 eight-wave (M <= 64) or 512 four-wave (M <= 16)
+  // workgroups.  Large-M kernel (two workgroups per CU): the most splits that
+  // still fit one round of 512 workgroups, since a partial second round costs
+  // more than the split saves (measured at M = 1088).  At most 8 splits: every
+  // split adds M x N fp32 partials that the consumer kernel reads back.
+  int S;
+  if (m_tile > 64)
+    S = std::max(1, 512 / tiles);
+  else
+    S = ((m_tile == 64 ? 256 : 512) + tiles / 2) / tiles;
   S = std::max(1, std::min(8, S));
   const int mpad = (M + m_tile - 1) / m_tile * m_tile;
   while (S > 1 && (size_t)S * mpad * N > c->part_elems) --S;

@@ -11,24 +11,42 @@
 namespace e3 {
 
 // Large-M GEMM (prefill chunks, batch-64 verify): 128 (M) x 256 (N) output
-// tile per workgroup, K in steps of 32 through double-buffered LDS for both
-// operands; a step's weight tile is one packed fragment (1 KiB, contiguous)
-// of each of the tile's sixteen 16-row blocks.  Four waves in a 2 x 2 arrangement each own a 64 x 128 sub-tile
-// (4 x 8 MFMA blocks of 16 x 16), so every operand fragment read from LDS
-// feeds 4 or 8 MFMAs.  LDS rows are 64 bytes (four 16-byte chunks) with the
-// chunk index XOR-swizzled by (row / 2) % 4: any eight consecutive lanes of
-// a fragment read (eight rows, one chunk) or of a staging store (two rows)
-// then touch distinct banks.  Global loads run two
-// K steps ahead through two register buffers.  Tile
-// order: m-tile fastest, dealt round-robin over the 8 XCDs as in the skinny
-// kernel, so the m-tiles that share a weight tile read it from the same L2.
+// tile per workgroup, K in steps of 32.  Four waves in a 2 x 2 arrangement
+// each own a 64 x 128 sub-tile (4 x 8 MFMA blocks of 16 x 16), so every
+// operand fragment read from LDS feeds 4 or 8 MFMAs.
+//
+// Operand tiles go from global memory straight into LDS (global_load_lds,
+// 16 bytes per lane, landing in lane order) already in MFMA fragment order:
+// a step's A tile is 8 fragments (16 activation rows x 32 K each, lane l
+// fetching row l % 16, K 8 (l / 16) .. + 7 of row-major X) and its B tile 16
+// fragments, each one contiguous 1 KiB of the packed weight.  Fragment reads
+// are then plain lane-order 16-byte LDS reads (conflict-free), and staging
+// costs no registers and no LDS store instructions.  Three LDS stages: the
+// copies of step s + 2 are issued during step s, and one barrier per step
+// both publishes step s and retires the stage that is refilled next.  The
+// copies are issued from inline asm and the wait for them (vmcnt) is explicit:
+// the compiler's own wait insertion cannot tell the stages apart and would
+// otherwise drain all of them at every step.
+//
+// Tile order: m-tile fastest, dealt round-robin over the 8 XCDs as in the
+// skinny kernel, so the m-tiles that share a weight tile read it from the
+// same L2.
 constexpr int BM = 128, BN = GEMM_BIG_ROWS, BKK = GEMM_BIG_KSTEP;
+constexpr int AFR = BM / 16, BFR = BN / 16;  // fragments per stage
 
 struct BigTiles {
   int tiles0[4];  // prefix of BN-row N tiles per segment
 };
 
-E3_DEV int swz(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 1) & 3)); }  // in 16-byte chunks
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from g into LDS at l + 16 * lane (l wave-uniform).
+E3_DEV void lds_copy16(const void* g, void* l) {
+  const unsigned base = (unsigned)(size_t)(lds_ptr_t)l;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(base)),
+               "v"(g)
+               : "memory", "m0");
+}
 
 // FUSE: the two segments are the gate and up projections (F rows each); a
 // tile covers 128 output columns n0 .. n0 + 127 of both, arranged so that in
@@ -40,40 +58,32 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
                                                           BigTiles bt, float* __restrict__ out, int ldo,
                                                           size_t split_stride, int kchunk, int S, int mtiles,
                                                           int nwork, bf16_t* __restrict__ act, int F) {
-  __shared__ __attribute__((aligned(16))) u32x4 as[2][BM * 4];
-  __shared__ __attribute__((aligned(16))) u32x4 bs[2][BN * 4];
+  __shared__ __attribute__((aligned(1024))) bf16_t sa0[AFR * 512], sa1[AFR * 512], sa2[AFR * 512];
+  __shared__ __attribute__((aligned(1024))) bf16_t sb0[BFR * 512], sb1[BFR * 512], sb2[BFR * 512];
   const int per = (nwork + 7) >> 3;
   const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (lam >= nwork) return;
   const int mt = lam % mtiles, rest = lam / mtiles;
   const int split = rest % S, ntile = rest / S;
   int seg = 0;
-  while (seg + 1 < segs.nseg && ntile >= bt.tiles0[seg + 1]) ++seg;
+  while (!FUSE && seg + 1 < segs.nseg && ntile >= bt.tiles0[seg + 1]) ++seg;
   const int n0 = (ntile - bt.tiles0[seg]) * BN;
   const int kb = split * kchunk, ke = min(K, kb + kchunk);
-  const bf16_t* __restrict__ W = (const bf16_t*)segs.w[seg];
-  const int nrows = segs.rows[seg];
+  const int nrows = FUSE ? F : segs.rows[seg];  // rows of the packed matrix (both FUSE matrices have F)
+  const size_t slab = (size_t)((nrows + 15) >> 4) * (4 * 512);
   const int m0 = mt * BM;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int wm = (wv & 1) * 64, wn = (wv >> 1) * 128;
-  // staging: A chunk c = tid + 256 i (i < 2): row c / 4, K chunk c % 4.  B
-  // chunk c = tid + 256 i (i < 4): lane c % 64 of the fragment of tile block
-  // c / 64, i.e. tile row 16 (c / 64) + c % 16, K chunk (c % 64) / 16.  Rows
-  // past M read row M - 1 and blocks past the segment read block 0; their
-  // results are not stored.
+  const int wm = wv & 1, wn = wv >> 1;
+  // this wave's copies: A fragments 2 wv, 2 wv + 1 and B fragments 4 wv .. 4 wv + 3 of every stage.
+  // Rows past M read row M - 1 and blocks past the segment read block 0; their results are not stored.
   const bf16_t* ap[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) ap[i] = X + (size_t)min(m0 + 16 * (2 * wv + i) + lr, M - 1) * K + 8 * lg;
   const bf16_t* bp[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
-    ap[i] = X + (size_t)min(m0 + (c >> 2), M - 1) * K + (c & 3) * 8;
-  }
-  const int bn = FUSE ? F : nrows;  // rows of the packed matrix (both FUSE matrices have F)
-  const size_t slab = (size_t)((bn + 15) >> 4) * (4 * 512);
-#pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, jj = c >> 6, l = c & 63;
+    const int jj = 4 * wv + i;  // tile block
     int rb;
     const bf16_t* Wb;
     if (FUSE) {  // tile block jj: half h = jj / 8, block j = jj % 8 of it; odd blocks are up rows
@@ -82,95 +92,83 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
       Wb = (const bf16_t*)segs.w[j & 1];
     } else {
       rb = (n0 >> 4) + jj;
-      Wb = W;
+      Wb = (const bf16_t*)segs.w[seg];
     }
-    bp[i] = Wb + (size_t)(16 * rb < bn ? rb : 0) * (4 * 512) + 8 * l;
+    bp[i] = Wb + (size_t)(16 * rb < nrows ? rb : 0) * (4 * 512) + 8 * lane;
   }
-  u32x4 ar0[2], br0[4], ar1[2], br1[4];
-  auto fetch = [&](u32x4 (&ar)[2], u32x4 (&br)[4], int k0) {
+  auto issue = [&](bf16_t* sa, bf16_t* sb, int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ar[i] = *(const u32x4*)(ap[i] + k0);
+    for (int i = 0; i < 2; ++i) lds_copy16(ap[i] + k0, sa + (2 * wv + i) * 512);
     const size_t off = (size_t)(k0 / PACK_KB) * slab + ((k0 % PACK_KB) / 32) * 512;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) br[i] = *(const u32x4*)(bp[i] + off);
-  };
-  auto stash = [&](const u32x4 (&ar)[2], const u32x4 (&br)[4], int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      as[buf][swz(c >> 2, c & 3)] = ar[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, l = c & 63;
-      bs[buf][swz(16 * (c >> 6) + (l & 15), l >> 4)] = br[i];
-    }
+    for (int i = 0; i < 4; ++i) lds_copy16(bp[i] + off, sb + (4 * wv + i) * 512);
   };
   f32x4 acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mul = [&](int buf) {
+  auto mul = [&](const bf16_t* sa, const bf16_t* sb) {
     bf16x8 a[4], b[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(bf16x8, as[buf][swz(wm + 16 * i + lr, lg)]);
+    for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sa + (4 * wm + i) * 512 + 8 * lane));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = __builtin_bit_cast(bf16x8, bs[buf][swz(wn + 16 * j + lr, lg)]);
+    for (int j = 0; j < 8; ++j) b[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sb + (8 * wn + j) * 512 + 8 * lane));
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
-  // LDS holds K step s (double-buffered), registers hold step s + 1, and the
-  // loads of step s + 2 are issued before step s is multiplied, so every load
-  // has two multiply phases to arrive.  Past the last step the loads repeat
-  // the last step's addresses.
+  // Step s: this wave's 6 copies of step s were issued two steps earlier and
+  // only the 6 of step s + 1 were issued after them, so vmcnt(6) means step s
+  // has landed; the barrier makes every wave's copies visible and guarantees
+  // that all waves finished reading the stage the copies of step s + 2 refill
+  // (it was read in step s - 1).  Past the last step the copies repeat the
+  // last step's addresses into stages nobody reads again.
   const int nsteps = (ke - kb) / BKK, klast = ke - BKK;
-  auto step = [&](int s, const u32x4 (&anext)[2], const u32x4 (&bnext)[4], u32x4 (&aafter)[2], u32x4 (&bafter)[4]) {
-    fetch(aafter, bafter, min(kb + (s + 2) * BKK, klast));
-    __builtin_amdgcn_sched_barrier(0);
-    mul(s & 1);
-    stash(anext, bnext, (s + 1) & 1);
-    __syncthreads();
+  auto step = [&](int s, const bf16_t* ca, const bf16_t* cb, bf16_t* na, bf16_t* nb) {
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+    issue(na, nb, min(kb + (s + 2) * BKK, klast));
+    mul(ca, cb);
   };
-  fetch(ar0, br0, kb);
-  fetch(ar1, br1, min(kb + BKK, klast));
-  stash(ar0, br0, 0);
-  __syncthreads();
+  issue(sa0, sb0, kb);
+  issue(sa1, sb1, min(kb + BKK, klast));
   int s = 0;
-  for (; s + 2 <= nsteps; s += 2) {
-    step(s, ar1, br1, ar0, br0);
-    step(s + 1, ar0, br0, ar1, br1);
+  for (; s + 3 <= nsteps; s += 3) {
+    step(s, sa0, sb0, sa2, sb2);
+    step(s + 1, sa1, sb1, sa0, sb0);
+    step(s + 2, sa2, sb2, sa1, sb1);
   }
-  if (s < nsteps) step(s, ar1, br1, ar0, br0);
-  if (FUSE) {  // acc[i][2t] = gate, acc[i][2t + 1] = up at column ntile*128 + wn/2 + 16 t + lr
+  if (s < nsteps) step(s, sa0, sb0, sa2, sb2);
+  if (s + 1 < nsteps) step(s + 1, sa1, sb1, sa0, sb0);
+  __builtin_amdgcn_s_waitcnt(0);  // the trailing copies land before the workgroup's LDS is released
+  if (FUSE) {  // acc[i][2t] = gate, acc[i][2t + 1] = up at column ntile*128 + wn*64 + 16 t + lr
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int n = ntile * 128 + (wn >> 1) + 16 * t + lr;
+      const int n = ntile * 128 + 64 * wn + 16 * t + lr;
       if (n >= F) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm + 16 * i + 4 * lg + r;
+          const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
           const float g = acc[i][2 * t][r], u = acc[i][2 * t + 1][r];
           if (m < M) act[(size_t)m * F + n] = f2bf(g / (1.f + expf(-g)) * u);
         }
     }
     return;
   }
-  // acc[i][j][r] = out[m0 + wm + 16 i + 4 lg + r][n0 + wn + 16 j + lr]
+  // acc[i][j][r] = out[m0 + 64 wm + 16 i + 4 lg + r][n0 + 128 wn + 16 j + lr]
   float* o = out + split * split_stride + segs.col0[seg];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int n = n0 + wn + 16 * j + lr;
+    const int n = n0 + 128 * wn + 16 * j + lr;
     if (n >= nrows) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm + 16 * i + 4 * lg + r;
+        const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
         if (m < M) o[(size_t)m * ldo + n] = acc[i][j][r];
       }
   }
