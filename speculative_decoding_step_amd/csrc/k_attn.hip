@@ -21,8 +21,12 @@ E3_DEV int key_end(int lim, int t0, uint64_t mask) {
   return mask ? max(lim, t0 + 64 - __clzll(mask)) : lim;
 }
 
+// Bitwise form (no short-circuit): callers select on the result, and the
+// select must not turn into nested divergent branches (written with || and &&
+// inside a divergent branch, the masked writes were lost in generated code).
 E3_DEV bool visible(int j, int lim, int t0, uint64_t mask) {
-  return j < lim || (j >= t0 && j - t0 < 64 && ((mask >> (j - t0)) & 1ull));
+  const unsigned dt = (unsigned)(j - t0);
+  return (j < lim) | ((dt < 64u) & (((mask >> (dt & 63u)) & 1ull) != 0ull));
 }
 
 template <typename T>
@@ -165,18 +169,32 @@ void combine(const float* o_part, const float* ml_part, int ns, int R, int Hq, i
 // bf16 flash-decoding with grouped queries.  A workgroup of NW waves (4..8)
 // owns one sequence, one KV head g, 16 NW query vectors (row i, query head
 // g*G + hl, numbered i*G + hl, 16 per wave) and one chunk of keys.  Key tiles
-// of 64 are staged in LDS (K row-major, V transposed) and shared by the waves;
-// the next tile is loaded into registers while the current one is used.  A
-// workgroup whose chunk starts past every key its rows see exits without
-// writing: the combine step reads only chunks below each row's key end.
+// of 64 are shared by the waves through LDS.  A workgroup whose chunk starts
+// past every key its rows see exits without writing: the combine step reads
+// only chunks below each row's key end.
+//
+// Staging: every tile is copied from the KV cache straight into LDS
+// (global_load_lds, 16 bytes per lane, landing in lane order), three tiles
+// deep (the copies of tile t + 2 are issued while tile t is used), with one
+// barrier per tile and no staging registers.  K lands in the order of the
+// score product's A fragments (16 keys x 32 dims, lane l: key l % 16, dims
+// 8 (l / 16) .. + 7).  V lands in blocks of 4 keys x 16 dims (128 bytes,
+// keys outer); the PV product reads its transposed operand from them with
+// ds_read_b64_tr_b16: when lane j of a 16-lane group points at key j / 4,
+// dims 4 (j % 4) .. + 3 of a block, lane q receives the 4 keys of dim q.
+// Source rows past the chunk end are clamped to its last key (finite data;
+// those keys are masked out of the scores).  The copies are issued from
+// inline asm and waited for explicitly: each wave issues PW copies per tile
+// (indices past the tile's count repeat its last copy, an identical write),
+// so vmcnt(PW) at the top of tile t leaves exactly tile t + 1's in flight.
 //
 // Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
 // A = 16 keys, B = the wave's 16 queries), so that a lane holds four keys of
 // its own query.  Those accumulator registers are then, unchanged in place,
 // the B operand of O^T += V^T P^T: one 32-key MFMA step takes keys
 // 4*lg + e and 16 + 4*lg + e (e = 0..3) in lane group lg, and the V^T operand
-// is read from LDS in the same key order.  P enters as two bf16 terms
-// (hi + lo, two MFMAs), keeping about 16 significant bits.
+// is read in the same key order.  P enters as two bf16 terms (hi + lo, two
+// MFMAs), keeping about 16 significant bits.
 //
 // Online softmax in base 2 with a lazy maximum: the running maximum m of a
 // query is raised (and O, l rescaled) only when a tile's scaled maximum
@@ -189,38 +207,45 @@ void combine(const float* o_part, const float* ml_part, int ns, int R, int Hq, i
 // dealt to the 8 XCDs in contiguous runs, so the query blocks that read the
 // same K/V chunk share one L2.
 constexpr int AKT = 64;  // keys per LDS tile
-constexpr int VPAD = 8;  // bf16 padding per transposed-V row
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float LAZY = 8.f;     // log2 headroom before the running maximum moves
 constexpr float M_EMPTY = -1e30f;
 
-// LDS position of V(key, dim) in the transposed tile: groups of 8 keys are
-// XOR-swizzled by the dimension's 8-group so that the transposing stores of
-// one wave spread over the banks while 8 consecutive keys stay contiguous.
-E3_DEV int vt_index(int dim, int key) {
-  return dim * (AKT + VPAD) + ((((key >> 3) ^ (dim >> 3)) & 7) << 3) + (key & 7);
-}
-
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* attn_lds_t;
 
-template <int HD>
-__global__ __launch_bounds__(512) void k_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-                                                   const bf16_t* __restrict__ vc, size_t seq_stride,
-                                                   size_t head_stride, const int* __restrict__ rseq,
-                                                   const int* __restrict__ rlim, const int* __restrict__ rt0,
-                                                   const uint64_t* __restrict__ rmask, int R, int rps, int qblocks,
-                                                   int Hq, int Hkv, int ns, int nwork, int S_cap, float scale,
-                                                   int chunk, float* __restrict__ o_part, float* __restrict__ ml_part) {
-  __shared__ __attribute__((aligned(16))) bf16_t ks[AKT][HD + 8];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[HD * (AKT + VPAD)];
+// 16 bytes per lane from g into LDS at l + 16 * lane (l wave-uniform).
+E3_DEV void attn_copy16(const void* g, void* l) {
+  const unsigned base = (unsigned)(size_t)(attn_lds_t)l;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(base)),
+               "v"(g)
+               : "memory", "m0");
+}
+
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
+                                                       const bf16_t* __restrict__ vc, size_t seq_stride,
+                                                       size_t head_stride, const int* __restrict__ rseq,
+                                                       const int* __restrict__ rlim, const int* __restrict__ rt0,
+                                                       const uint64_t* __restrict__ rmask, int R, int rps,
+                                                       int qblocks, int Hq, int Hkv, int ns, int nwork, int S_cap,
+                                                       float scale, int chunk, float* __restrict__ o_part,
+                                                       float* __restrict__ ml_part) {
+  constexpr int TILE = AKT * HD;               // bf16 elements of one K (or V) tile
+  constexpr int NCP = 2 * TILE / 512;          // 1 KiB copies per tile: K fragments, then V block groups
+  constexpr int PW = (NCP + NW - 1) / NW;      // copies per wave and tile
+  constexpr int KF = HD / 32;                  // K fragments per 16-key block
+  constexpr int VB = HD / 16;                  // V blocks per 4-key group
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE];  // K then V
   __shared__ int red_end[8], red_seq[8];
   const int per = (nwork + 7) >> 3;
   const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (lam >= nwork) return;
-  const int NW = blockDim.x >> 6, QB = 16 * NW;
+  constexpr int QB = 16 * NW;
   const int qb = lam % qblocks;
   int t = lam / qblocks;
   const int g = t % Hkv;
@@ -259,6 +284,35 @@ __global__ __launch_bounds__(512) void k_attn_mfma(const bf16_t* __restrict__ q,
   if (cs < 0 || c0 >= c1) return;  // no row of the block sees a key of this chunk
   const int vis_all = ok ? min(lim, c1) : -1;  // keys below this are visible to the lane's query
 
+  const bf16_t* kb = kc + (size_t)cs * seq_stride + (size_t)g * head_stride;
+  const bf16_t* vb = vc + (size_t)cs * seq_stride + (size_t)g * head_stride;
+  // this wave's copies of a tile: index f = w + NW i (i < PW), clamped to the last one
+  const bf16_t* src[PW];
+  int dst[PW], ckey[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int f = min(w + NW * i, NCP - 1);
+    int key, d0;
+    if (f < NCP / 2) {  // K fragment (16-key block kb4, dims 32 kk ..): lane: key lr, dims 8 lg ..
+      const int kb4 = f / KF, kk = f % KF;
+      key = 16 * kb4 + lr;
+      d0 = 32 * kk + 8 * lg;
+      dst[i] = f * 512;
+    } else {  // V blocks 8 (f - NCP / 2) .. + 7: lane: block + l / 8, key 2-chunk (l % 8) / 2, dim half l % 2
+      const int bi = 8 * (f - NCP / 2) + (lane >> 3), c = lane & 7;
+      key = 4 * (bi / VB) + (c >> 1);
+      d0 = 16 * (bi % VB) + 8 * (c & 1);
+      dst[i] = TILE + (f - NCP / 2) * 512;
+    }
+    ckey[i] = key;  // key within the tile
+    src[i] = (f < NCP / 2 ? kb : vb) + (size_t)key * HD + d0;
+  }
+  auto issue = [&](bf16_t* stg, int kt) {  // rows past the chunk end repeat its last key
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      attn_copy16(src[i] + (size_t)(min(kt + ckey[i], c1 - 1) - ckey[i]) * HD, stg + dst[i]);
+  };
+
   float m = M_EMPTY, lsum = 0.f;  // running maximum (log2 units) and the lane's share of the sum
   f32x4 O[HD / 16];               // O^T: dims 16b + 4lg + r of the lane's query
 #pragma unroll
@@ -271,49 +325,21 @@ __global__ __launch_bounds__(512) void k_attn_mfma(const bf16_t* __restrict__ q,
 #pragma unroll
     for (int kk = 0; kk < HD / 32; ++kk) qf[kk] = ok ? *(const u32x4*)(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
   }
-  const bf16_t* kb = kc + (size_t)cs * seq_stride + (size_t)g * head_stride;
-  const bf16_t* vb = vc + (size_t)cs * seq_stride + (size_t)g * head_stride;
-  constexpr int CPK = HD / 8;             // 16-byte chunks per key row
-  constexpr int MAXCH = AKT * CPK / 256;  // chunks per thread at 4 waves (the fewest)
-  const int nt = blockDim.x;
-  u32x4 kr[MAXCH], vr[MAXCH];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < MAXCH; ++i) {
-      const int c = tid + nt * i, key = c / CPK, d8 = (c % CPK) * 8;
-      const int j = kt + key;
-      if (c < AKT * CPK && j < c1) {
-        kr[i] = *(const u32x4*)(kb + (size_t)j * HD + d8);
-        vr[i] = *(const u32x4*)(vb + (size_t)j * HD + d8);
-      } else {
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  load_tile(c0);
-  for (int kt = c0; kt < c1; kt += AKT) {
-    __syncthreads();  // every wave is done with the previous tile
-#pragma unroll
-    for (int i = 0; i < MAXCH; ++i) {
-      const int c = tid + nt * i, key = c / CPK, d8 = (c % CPK) * 8;
-      if (c < AKT * CPK) {
-        *(u32x4*)&ks[key][d8] = kr[i];
-        const bf16_t* ve = (const bf16_t*)&vr[i];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vt[vt_index(d8 + e, key)] = ve[e];
-      }
-    }
-    __syncthreads();
-    if (kt + AKT < c1) load_tile(kt + AKT);  // in flight during this tile's math
+  // Complete the query loads here, visibly to the compiler: its own wait for them would otherwise land inside
+  // the tile loop, where (not seeing the asm copies) it would drain every tile in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  auto tile = [&](const bf16_t* stg, int kt) {
+    const bf16_t* ks = stg;
+    const bf16_t* vs = stg + TILE;
     // S^T blocks: S[kb4][r] = raw score(key kt + 16 kb4 + 4 lg + r, the lane's query)
     f32x4 S[4];
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4) {
       S[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < HD / 32; ++kk) {
-        const bf16x8 ak = __builtin_bit_cast(bf16x8, *(const u32x4*)&ks[16 * kb4 + lr][32 * kk + 8 * lg]);
+      for (int kk = 0; kk < KF; ++kk) {
+        const bf16x8 ak = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + (kb4 * KF + kk) * 512 + 8 * lane));
         S[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf16x8, qf[kk]), S[kb4], 0, 0, 0);
       }
     }
@@ -323,7 +349,8 @@ __global__ __launch_bounds__(512) void k_attn_mfma(const bf16_t* __restrict__ q,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = kt + 16 * kb4 + 4 * lg + r;
-          if (!(ok && j < c1 && visible(j, lim, t0, mask))) S[kb4][r] = -INFINITY;
+          const bool vis = ok & (j < c1) & visible(j, lim, t0, mask);  // one select per score
+          S[kb4][r] = vis ? S[kb4][r] : -INFINITY;
         }
     }
     float tmax = -INFINITY;
@@ -356,18 +383,47 @@ __global__ __launch_bounds__(512) void k_attn_mfma(const bf16_t* __restrict__ q,
         pl[kb4 >> 1][4 * (kb4 & 1) + r] = lo[0];
         pl[kb4 >> 1][4 * (kb4 & 1) + r + 1] = lo[1];
       }
+    // V^T operand of dim block b, keys {32 k2 + 4 lg + e} then {32 k2 + 16 + 4 lg + e}: the 4-key groups
+    // 8 k2 + lg and 8 k2 + 4 + lg, read transposed (lane lr points at 4 lr elements into the block)
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int b = 0; b < HD / 16; ++b) {
-        const int dim = 16 * b + lr;
-        const u32x2 v0 = *(const u32x2*)&vt[vt_index(dim, 32 * k2 + 4 * lg)];
-        const u32x2 v1 = *(const u32x2*)&vt[vt_index(dim, 32 * k2 + 16 + 4 * lg)];
-        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+        const bf16_t* b0 = vs + ((8 * k2 + lg) * VB + b) * 64 + 4 * lr;
+        const bf16_t* b1 = vs + ((8 * k2 + 4 + lg) * VB + b) * 64 + 4 * lr;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(attn_lds_t)b0);
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(attn_lds_t)b1);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
+                                                           __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]});
         O[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ph[k2], O[b], 0, 0, 0);
         O[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl[k2], O[b], 0, 0, 0);
       }
+  };
+
+  // Tile t: this wave's PW copies of tile t were issued two tiles earlier and only tile t + 1's PW after them
+  // (none when t is the last tile), so vmcnt(PW) (vmcnt(0) at the last tile) means tile t has landed; the
+  // barrier publishes every wave's copies and guarantees that all waves finished tile t - 1, whose stage the
+  // copies of tile t + 2 refill.
+  const int ntl = (c1 - c0 + AKT - 1) / AKT;
+  issue(st0, c0);
+  if (ntl > 1) issue(st1, c0 + AKT);
+  auto run = [&](int i, bf16_t* cur, bf16_t* nxt2) {
+    if (i + 1 < ntl)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PW) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (i + 2 < ntl) issue(nxt2, c0 + (i + 2) * AKT);
+    tile(cur, c0 + i * AKT);
+  };
+  int i = 0;
+  for (; i + 3 <= ntl; i += 3) {
+    run(i, st0, st2);
+    run(i + 1, st1, st0);
+    run(i + 2, st2, st1);
   }
+  if (i < ntl) run(i, st0, st2);
+  if (i + 1 < ntl) run(i + 1, st1, st0);
+
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   if (v < nq) {
@@ -380,6 +436,24 @@ __global__ __launch_bounds__(512) void k_attn_mfma(const bf16_t* __restrict__ q,
       ml_part[2 * oi + 1] = lsum;
     }
   }
+}
+
+template <int HD>
+void launch_attn(int nw, unsigned nblocks, hipStream_t st, const bf16_t* q, const bf16_t* kc, const bf16_t* vc,
+                 size_t seq_stride, size_t head_stride, const RowMeta& rm, int R, int rps, int qblocks, int Hq,
+                 int Hkv, int ns, int nwork, int key_bound, float scale, int chunk, float* o_part, float* ml_part) {
+#define E3_ATTN_LAUNCH(N)                                                                                             \
+  k_attn_mfma<HD, N><<<nblocks, 64 * N, 0, st>>>(q, kc, vc, seq_stride, head_stride, rm.seq, rm.lim, rm.tail0,       \
+                                                 rm.mask, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, \
+                                                 o_part, ml_part)
+  switch (nw) {
+    case 4: E3_ATTN_LAUNCH(4); break;
+    case 5: E3_ATTN_LAUNCH(5); break;
+    case 6: E3_ATTN_LAUNCH(6); break;
+    case 7: E3_ATTN_LAUNCH(7); break;
+    default: E3_ATTN_LAUNCH(8); break;
+  }
+#undef E3_ATTN_LAUNCH
 }
 
 void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride, size_t head_stride,
@@ -403,15 +477,11 @@ void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t 
     const int nwork = (R / rps) * qblocks * Hkv * ns;
     const int nblocks = (nwork + 7) / 8 * 8;
     if (hd == 128)
-      k_attn_mfma<128><<<nblocks, 64 * nw, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc,
-                                                     seq_stride, head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R,
-                                                     rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk,
-                                                     o_part, ml_part);
+      launch_attn<128>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
+                       head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part, ml_part);
     else
-      k_attn_mfma<64><<<nblocks, 64 * nw, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc,
-                                                    seq_stride, head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R,
-                                                    rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk,
-                                                    o_part, ml_part);
+      launch_attn<64>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
+                      head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part, ml_part);
     combine<bf16_t>(o_part, ml_part, ns, R, Hq, hd, rm, key_bound, chunk, (bf16_t*)out, st);
     return;
   }
