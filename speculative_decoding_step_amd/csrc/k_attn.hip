@@ -9,6 +9,7 @@
 // kernel merges them in chunk order.  Masked keys are skipped, not added as
 // -inf.
 #include <algorithm>
+#include <climits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -174,19 +175,24 @@ void combine(const float* o_part, const float* ml_part, int ns, int R, int Hq, i
 // only chunks below each row's key end.
 //
 // Staging: every tile is copied from the KV cache straight into LDS
-// (global_load_lds, 16 bytes per lane, landing in lane order), three tiles
-// deep (the copies of tile t + 2 are issued while tile t is used), with one
-// barrier per tile and no staging registers.  K lands in the order of the
+// (global_load_lds, 16 bytes per lane, landing in lane order), NST - 1 tiles
+// ahead (four stages: the copies of tile t + 3 are issued while tile t is
+// used; 128 KiB of LDS at head_dim 128), with one barrier per tile and no
+// staging registers.  A copy's source is a wave-uniform base in scalar
+// registers (K or V of the sequence and head, advanced a whole tile at a
+// time) plus a fixed per-lane offset.  K lands in the order of the
 // score product's A fragments (16 keys x 32 dims, lane l: key l % 16, dims
 // 8 (l / 16) .. + 7).  V lands in blocks of 4 keys x 16 dims (128 bytes,
 // keys outer); the PV product reads its transposed operand from them with
 // ds_read_b64_tr_b16: when lane j of a 16-lane group points at key j / 4,
 // dims 4 (j % 4) .. + 3 of a block, lane q receives the 4 keys of dim q.
-// Source rows past the chunk end are clamped to its last key (finite data;
-// those keys are masked out of the scores).  The copies are issued from
-// inline asm and waited for explicitly: each wave issues PW copies per tile
-// (indices past the tile's count repeat its last copy, an identical write),
-// so vmcnt(PW) at the top of tile t leaves exactly tile t + 1's in flight.
+// In the chunk's last tile, source rows past the chunk end are clamped to
+// its last key (finite data; those keys are masked out of the scores, and a
+// non-finite V row would turn the zero weight into NaN).  The copies are
+// issued from inline asm and waited for explicitly: each wave issues PW
+// copies per tile (indices past the tile's count repeat its last copy, an
+// identical write), so the vmcnt at the top of tile t leaves exactly the
+// later tiles' copies in flight.
 //
 // Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
 // A = 16 keys, B = the wave's 16 queries), so that a lane holds four keys of
@@ -196,12 +202,19 @@ void combine(const float* o_part, const float* ml_part, int ns, int R, int Hq, i
 // is read in the same key order.  P enters as two bf16 terms (hi + lo, two
 // MFMAs), keeping about 16 significant bits.
 //
+// Masking costs nothing on tiles that every query of the wave sees whole (a
+// wave-uniform test against the smallest committed length); other tiles build
+// a 64-bit visibility word per query (committed prefix | shifted tree mask,
+// cut at the chunk end) and select -inf per score from it.
+//
 // Online softmax in base 2 with a lazy maximum: the running maximum m of a
 // query is raised (and O, l rescaled) only when a tile's scaled maximum
 // exceeds it by more than 8, so p = exp2(s * c - m) <= 256 (c = log2(e) /
-// sqrt(hd)).  Exact in real arithmetic.  m starts at -1e30 rather than -inf so
-// that masked scores (-inf) give p = 0 without a test; the partial maximum is
-// stored in natural-log units (-inf when the row saw no key in the chunk).
+// sqrt(hd)).  Exact in real arithmetic.  The rescale runs as a wave-uniform
+// branch when any query of the wave raises its maximum.  m starts at -1e30
+// rather than -inf so that masked scores (-inf) give p = 0 without a test;
+// the partial maximum is stored in natural-log units (-inf when the row saw
+// no key in the chunk).
 //
 // Work items (query block fastest, then KV head, key chunk, sequence) are
 // dealt to the 8 XCDs in contiguous runs, so the query blocks that read the
@@ -218,15 +231,16 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* attn_lds_t;
 
-// 16 bytes per lane from g into LDS at l + 16 * lane (l wave-uniform).
-E3_DEV void attn_copy16(const void* g, void* l) {
+// 16 bytes per lane from sbase + voff (sbase wave-uniform, voff a per-lane byte
+// offset) into LDS at l + 16 * lane (l wave-uniform).
+E3_DEV void attn_copy16(const void* sbase, unsigned voff, void* l) {
   const unsigned base = (unsigned)(size_t)(attn_lds_t)l;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(base)),
-               "v"(g)
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(base)),
+               "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
 
-template <int HD, int NW>
+template <int HD, int NW, int NST>
 __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
                                                        const bf16_t* __restrict__ vc, size_t seq_stride,
                                                        size_t head_stride, const int* __restrict__ rseq,
@@ -240,7 +254,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   constexpr int PW = (NCP + NW - 1) / NW;      // copies per wave and tile
   constexpr int KF = HD / 32;                  // K fragments per 16-key block
   constexpr int VB = HD / 16;                  // V blocks per 4-key group
-  __shared__ __attribute__((aligned(1024))) bf16_t st0[2 * TILE], st1[2 * TILE], st2[2 * TILE];  // K then V
+  __shared__ __attribute__((aligned(1024))) bf16_t stg[NST][2 * TILE];  // NST stages, each K then V
   __shared__ int red_end[8], red_seq[8];
   const int per = (nwork + 7) >> 3;
   const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -252,7 +266,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   t /= Hkv;
   const int sp = t % ns, bs = t / ns;
   const int G = Hq / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in scalar registers
   const int nq = rps * G;
 
   // the lane's query vector: 16w + lr of the block
@@ -280,14 +295,24 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
     kend = max(kend, red_end[i]);
     cs = max(cs, red_seq[i]);
   }
+  kend = __builtin_amdgcn_readfirstlane(kend);
+  cs = __builtin_amdgcn_readfirstlane(cs);
   const int c0 = sp * chunk, c1 = min(c0 + chunk, kend);
   if (cs < 0 || c0 >= c1) return;  // no row of the block sees a key of this chunk
-  const int vis_all = ok ? min(lim, c1) : -1;  // keys below this are visible to the lane's query
+  // Keys below vis_min are visible to every query of the wave, so tiles below it need no mask (a wave-uniform
+  // test).  Lanes without a query vector never force masking (their results are not stored); rows without a
+  // sequence see no key.
+  int vis_min = v >= nq ? INT_MAX : (ok ? min(lim, c1) : -1);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) vis_min = min(vis_min, __shfl_xor(vis_min, o, 64));
+  vis_min = __builtin_amdgcn_readfirstlane(vis_min);
 
   const bf16_t* kb = kc + (size_t)cs * seq_stride + (size_t)g * head_stride;
   const bf16_t* vb = vc + (size_t)cs * seq_stride + (size_t)g * head_stride;
-  // this wave's copies of a tile: index f = w + NW i (i < PW), clamped to the last one
-  const bf16_t* src[PW];
+  // this wave's copies of a tile: index f = w + NW i (i < PW), clamped to the last one; the source is a
+  // wave-uniform base (K or V of this sequence and head, advanced by whole tiles) plus a per-lane offset
+  const bf16_t* cbase[PW];
+  unsigned voff[PW];
   int dst[PW], ckey[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
@@ -305,12 +330,20 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
       dst[i] = TILE + (f - NCP / 2) * 512;
     }
     ckey[i] = key;  // key within the tile
-    src[i] = (f < NCP / 2 ? kb : vb) + (size_t)key * HD + d0;
+    cbase[i] = f < NCP / 2 ? kb : vb;
+    voff[i] = (unsigned)(key * HD + d0) * 2u;
   }
-  auto issue = [&](bf16_t* stg, int kt) {  // rows past the chunk end repeat its last key
+  auto issue = [&](bf16_t* stgp, int kt) {
+    if (kt + AKT <= c1) {  // whole tile inside the chunk
 #pragma unroll
-    for (int i = 0; i < PW; ++i)
-      attn_copy16(src[i] + (size_t)(min(kt + ckey[i], c1 - 1) - ckey[i]) * HD, stg + dst[i]);
+      for (int i = 0; i < PW; ++i) attn_copy16(cbase[i] + (size_t)kt * HD, voff[i], stgp + dst[i]);
+    } else {  // the chunk's last tile: rows past its end repeat its last key (finite data, masked out)
+#pragma unroll
+      for (int i = 0; i < PW; ++i) {
+        const int back = kt + ckey[i] - min(kt + ckey[i], c1 - 1);  // rows moved back, >= 0
+        attn_copy16(cbase[i] + (size_t)kt * HD, voff[i] - (unsigned)(back * HD * 2), stgp + dst[i]);
+      }
+    }
   };
 
   float m = M_EMPTY, lsum = 0.f;  // running maximum (log2 units) and the lane's share of the sum
@@ -329,9 +362,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   // the tile loop, where (not seeing the asm copies) it would drain every tile in flight.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  auto tile = [&](const bf16_t* stg, int kt) {
-    const bf16_t* ks = stg;
-    const bf16_t* vs = stg + TILE;
+  auto tile = [&](const bf16_t* stgp, int kt) {
+    const bf16_t* ks = stgp + 8 * lane;                                 // + constant fragment offsets
+    const bf16_t* vs = stgp + TILE + lg * (VB * 64) + 4 * lr;          // + constant block offsets
     // S^T blocks: S[kb4][r] = raw score(key kt + 16 kb4 + 4 lg + r, the lane's query)
     f32x4 S[4];
 #pragma unroll
@@ -339,19 +372,24 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
       S[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KF; ++kk) {
-        const bf16x8 ak = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + (kb4 * KF + kk) * 512 + 8 * lane));
+        const bf16x8 ak = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + (kb4 * KF + kk) * 512));
         S[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf16x8, qf[kk]), S[kb4], 0, 0, 0);
       }
     }
-    if (kt + AKT > vis_all) {  // tile reaches past the committed keys (or the lane has no query)
+    if (kt + AKT > vis_min) {  // some query of the wave does not see every key of the tile (wave-uniform)
+      // visibility of keys kt .. kt + 63 for the lane's query, one bit per key: the committed prefix, the
+      // tree slots t0 + j (bit j of mask), cut at the chunk end.  Every select below is branch-free.
+      const int np = lim - kt, d = t0 - kt, ne = c1 - kt;  // ne >= 1
+      const uint64_t pre = np >= 64 ? ~0ull : (np <= 0 ? 0ull : (1ull << np) - 1ull);
+      const uint64_t tr = (d >= 64 || d <= -64) ? 0ull : (d >= 0 ? mask << d : mask >> -d);
+      const uint64_t end = ne >= 64 ? ~0ull : (1ull << ne) - 1ull;
+      uint64_t vis = (pre | tr) & end;
+      vis = v >= nq ? ~0ull : (ok ? vis : 0ull);
+      const uint64_t vl = vis >> (4 * lg);  // bit 16 kb4 + r: key kt + 16 kb4 + 4 lg + r
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = kt + 16 * kb4 + 4 * lg + r;
-          const bool vis = ok & (j < c1) & visible(j, lim, t0, mask);  // one select per score
-          S[kb4][r] = vis ? S[kb4][r] : -INFINITY;
-        }
+        for (int r = 0; r < 4; ++r) S[kb4][r] = ((vl >> (16 * kb4 + r)) & 1ull) ? S[kb4][r] : -INFINITY;
     }
     float tmax = -INFINITY;
 #pragma unroll
@@ -360,9 +398,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float tm = tmax * qscale;  // -inf when the tile is fully masked
-    if (tm > m + LAZY) {             // same decision in the four lanes of a query
-      const float alpha = __builtin_amdgcn_exp2f(m - tm);  // 0 while m is M_EMPTY
-      m = tm;
+    const bool raise = tm > m + LAZY;  // same decision in the four lanes of a query
+    if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform: rare once the maxima have settled
+      const float mn = raise ? tm : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 1 where the maximum stays, 0 while m is M_EMPTY
+      m = mn;
       lsum *= alpha;
 #pragma unroll
       for (int b = 0; b < HD / 16; ++b) O[b] *= alpha;
@@ -384,13 +424,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
         pl[kb4 >> 1][4 * (kb4 & 1) + r + 1] = lo[1];
       }
     // V^T operand of dim block b, keys {32 k2 + 4 lg + e} then {32 k2 + 16 + 4 lg + e}: the 4-key groups
-    // 8 k2 + lg and 8 k2 + 4 + lg, read transposed (lane lr points at 4 lr elements into the block)
+    // 8 k2 + lg and 8 k2 + 4 + lg, read transposed (lane lr points at 4 lr elements into the block; the
+    // lane's part of the address is in vs)
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int b = 0; b < HD / 16; ++b) {
-        const bf16_t* b0 = vs + ((8 * k2 + lg) * VB + b) * 64 + 4 * lr;
-        const bf16_t* b1 = vs + ((8 * k2 + 4 + lg) * VB + b) * 64 + 4 * lr;
+        const bf16_t* b0 = vs + (8 * k2 * VB + b) * 64;
+        const bf16_t* b1 = vs + ((8 * k2 + 4) * VB + b) * 64;
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(attn_lds_t)b0);
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(attn_lds_t)b1);
         const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
@@ -400,29 +441,26 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
       }
   };
 
-  // Tile t: this wave's PW copies of tile t were issued two tiles earlier and only tile t + 1's PW after them
-  // (none when t is the last tile), so vmcnt(PW) (vmcnt(0) at the last tile) means tile t has landed; the
-  // barrier publishes every wave's copies and guarantees that all waves finished tile t - 1, whose stage the
-  // copies of tile t + 2 refill.
+  // NST-stage ring: tile t lives in stage t % NST and its copies are issued NST - 1 tiles ahead.  At the top
+  // of tile t this wave has issued the copies of tiles 0 .. min(ntl - 1, t + NST - 2), PW per tile, in order,
+  // so vmcnt(PW * a) with a = min(NST - 2, ntl - 1 - t) tiles issued after t means tile t has landed.  The
+  // barrier then publishes every wave's copies of tile t and guarantees that all waves finished tile t - 1,
+  // whose stage the copies of tile t + NST - 1 refill.
+  static_assert(NST == 3 || NST == 4, "the wait below covers at most two tiles in flight after the current one");
+  static_assert(PW * (NST - 2) <= 63, "copies in flight exceed the vmcnt range");
   const int ntl = (c1 - c0 + AKT - 1) / AKT;
-  issue(st0, c0);
-  if (ntl > 1) issue(st1, c0 + AKT);
-  auto run = [&](int i, bf16_t* cur, bf16_t* nxt2) {
-    if (i + 1 < ntl)
+  for (int t = 0; t < NST - 1 && t < ntl; ++t) issue(stg[t], c0 + t * AKT);
+  for (int t = 0; t < ntl; ++t) {
+    const int after = min(NST - 2, ntl - 1 - t);
+    if (after >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * PW) : "memory");
+    else if (after == 1)
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PW) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (i + 2 < ntl) issue(nxt2, c0 + (i + 2) * AKT);
-    tile(cur, c0 + i * AKT);
-  };
-  int i = 0;
-  for (; i + 3 <= ntl; i += 3) {
-    run(i, st0, st2);
-    run(i + 1, st1, st0);
-    run(i + 2, st2, st1);
+    if (t + NST - 1 < ntl) issue(stg[(t + NST - 1) % NST], c0 + (t + NST - 1) * AKT);
+    tile(stg[t % NST], c0 + t * AKT);
   }
-  if (i < ntl) run(i, st0, st2);
-  if (i + 1 < ntl) run(i + 1, st1, st0);
 
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
@@ -438,12 +476,12 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   }
 }
 
-template <int HD>
+template <int HD, int NST>
 void launch_attn(int nw, unsigned nblocks, hipStream_t st, const bf16_t* q, const bf16_t* kc, const bf16_t* vc,
                  size_t seq_stride, size_t head_stride, const RowMeta& rm, int R, int rps, int qblocks, int Hq,
                  int Hkv, int ns, int nwork, int key_bound, float scale, int chunk, float* o_part, float* ml_part) {
 #define E3_ATTN_LAUNCH(N)                                                                                             \
-  k_attn_mfma<HD, N><<<nblocks, 64 * N, 0, st>>>(q, kc, vc, seq_stride, head_stride, rm.seq, rm.lim, rm.tail0,       \
+  k_attn_mfma<HD, N, NST><<<nblocks, 64 * N, 0, st>>>(q, kc, vc, seq_stride, head_stride, rm.seq, rm.lim, rm.tail0,       \
                                                  rm.mask, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, \
                                                  o_part, ml_part)
   switch (nw) {
@@ -472,15 +510,18 @@ void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t 
     // Longer key chunks when the launch has work to spare: fewer partials to
     // write and merge, and each workgroup's set-up spread over more tiles.
     const long tiles256 = (long)(R / rps) * qblocks * Hkv * ns;
-    const int chunk = tiles256 >= 4096 ? 3 * ATT_CHUNK : (tiles256 >= 2048 ? 2 * ATT_CHUNK : ATT_CHUNK);
+    const int chunk = tiles256 >= 8192   ? 6 * ATT_CHUNK
+                      : tiles256 >= 4096 ? 3 * ATT_CHUNK
+                      : tiles256 >= 2048 ? 2 * ATT_CHUNK
+                                         : ATT_CHUNK;
     ns = (key_bound + chunk - 1) / chunk;
     const int nwork = (R / rps) * qblocks * Hkv * ns;
     const int nblocks = (nwork + 7) / 8 * 8;
     if (hd == 128)
-      launch_attn<128>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
+      launch_attn<128, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
                        head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part, ml_part);
     else
-      launch_attn<64>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
+      launch_attn<64, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
                       head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part, ml_part);
     combine<bf16_t>(o_part, ml_part, ns, R, Hq, hd, rm, key_bound, chunk, (bf16_t*)out, st);
     return;
