@@ -13,7 +13,8 @@ Modules
             EAGLE-3 draft head
   tree      tree mask, depths, the static-branching builder and the dynamic
             (confidence-ranked) builder
-  accept    greedy longest-path acceptance and chain rejection sampling
+  accept    greedy longest-path acceptance, chain rejection sampling and
+            level-by-level rejection sampling over a tree
   step      KV compaction and the vanilla / speculative driver loops
 
 Functions whose result no pin fixes say "parity unpinned" in their docstring:

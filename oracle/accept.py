@@ -1,4 +1,5 @@
-"""Acceptance: greedy longest path over a tree, and chain rejection sampling.
+"""Acceptance: greedy longest path over a tree, chain rejection sampling, and
+level-by-level rejection sampling over a tree.
 
 Sources (page title, section):
   * "Advanced speculative decoding: tree drafts and EAGLE", Implementation
@@ -14,12 +15,16 @@ Sources (page title, section):
   * "Speculative Decoding (EAGLE3) in the vLLM Neuron Framework", Rejection
     Sampling (greedy drafts: draft probability 1, recovered token from
     max(p - q, 0) with the draft token zeroed; output [B, K+1] padded with -1).
+  * "Advanced speculative decoding: tree drafts and EAGLE", Exercises (trees
+    under sampling: a node's candidates are tested in turn, each rejection
+    turns p into norm(max(0, p - q)), all rejected draws from the final
+    residual).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .numerics import argmax_first, sample_inverse_cdf
+from .numerics import argmax_first, int_weights, sample_inverse_cdf
 
 
 def greedy_walk(tokens, parents, argmax_rows):
@@ -73,6 +78,53 @@ def chain_rejection(draft_tokens, q32, p32, u32):
             tok = sample_inverse_cdf(p32[i], u32[K])
         return i, tok
     return K, sample_inverse_cdf(p32[K], u32[K])
+
+
+def tree_rejection(tokens, parents, p32, u32, topk, max_depth):
+    """Level-by-level rejection sampling over a draft tree ("Advanced speculative
+    decoding: tree drafts and EAGLE", Exercises, trees under sampling).
+
+    tokens, parents [n] (root row 0, parents[i] < i); p32 [n, V] the target
+    distribution at every tree row (float32); u32 [max_depth * topk + 1].
+    At the current node (depth d) its children are considered in row order:
+    child i (token x) is accepted with probability min(1, p'(x) / q(x)), where
+    p' is the node's residual target distribution.  The tree's children are
+    chosen deterministically (draft top-k), so each candidate's q is the point
+    mass at its token, the test is u < p'(x), and a rejection updates
+    p' <- norm(max(0, p' - q)), i.e. removes x's mass.  An accepted child
+    becomes the current node; when every child is rejected (or the node has
+    none) one token is drawn from the final residual and the walk stops.
+
+    Fixed point, as in the draws: W_v = floor(p(v) * 2**48); the residual mass
+    before child i is S_i = sum of W over the tokens not yet removed, and child i
+    is accepted iff floor(u * S_i) < W_x with u = u32[d * topk + i].  The final
+    draw uses u32[max_depth * topk].  Returns (path row indices, next token).
+    """
+    n = len(tokens)
+    path, node = [0], 0
+    while True:
+        d = len(path) - 1
+        W = int_weights(p32[node])
+        kids = [c for c in range(n) if parents[c] == node] if d < max_depth else []
+        removed = set()
+        S = int(sum(int(w) for w in W))
+        accepted = None
+        for i, c in enumerate(kids[:topk]):
+            x = int(tokens[c])
+            w_x = 0 if x in removed else int(W[x])
+            s_i = S - sum(int(W[t]) for t in removed)
+            u_int = int(np.float64(np.float32(u32[d * topk + i])) * (1 << 24))
+            if (u_int * s_i) >> 24 < w_x:
+                accepted = c
+                break
+            removed.add(x)
+        if accepted is None:
+            resid = np.asarray(p32[node], dtype=np.float32).copy()
+            for t in removed:
+                resid[t] = 0
+            return path, sample_inverse_cdf(resid, u32[max_depth * topk])
+        path.append(accepted)
+        node = accepted
 
 
 def emitted_row(path_tokens, width):
