@@ -45,8 +45,9 @@ def run_gpu(w, steps, warmup):
         from speculative_decoding_step_amd import synth
         K = w.depth
         eng.prefill(prompts, synth.uniform24_t(5000, "u_root", w.batch, "cuda"))
+        na = eng.n_u_accept
         eng.set_uniforms(synth.uniform24_t(5000, "u_draft", w.batch * K, "cuda").view(w.batch, K),
-                         synth.uniform24_t(5000, "u_accept", w.batch * (K + 1), "cuda").view(w.batch, K + 1))
+                         synth.uniform24_t(5000, "u_accept", w.batch * na, "cuda").view(w.batch, na))
     else:
         eng.prefill(prompts)
     torch.cuda.synchronize()

@@ -15,7 +15,8 @@
  *   eagle3_accept       greedy longest-path acceptance, or sequential rejection
  *                       sampling with residual norm(max(0, p - q)) and a bonus
  *                       token ("EAGLE-3: Engineering Implementation ...", III.5,
- *                       X.3-X.6);
+ *                       X.3-X.6), over a chain or level by level over a tree
+ *                       ("Advanced speculative decoding ...", Exercises);
  *   eagle3_compact_kv   the accepted nodes' K/V move to contiguous positions and
  *                       the next catch-up inputs are gathered ("Advanced
  *                       speculative decoding ...", Implementation, the note on
@@ -66,7 +67,7 @@ typedef enum {
 #define EAGLE3_DEV_BAD_PATH      0x8  /* path length 0 or > depth + 1             */
 
 enum { EAGLE3_F32 = 0, EAGLE3_BF16 = 1 };
-enum { EAGLE3_GREEDY_TREE = 0, EAGLE3_SAMPLE_CHAIN = 1 };
+enum { EAGLE3_GREEDY_TREE = 0, EAGLE3_SAMPLE_CHAIN = 1, EAGLE3_SAMPLE_TREE = 2 };
 enum { EAGLE3_LM_ALL = 0, EAGLE3_LM_LAST = 1, EAGLE3_LM_NONE = 2 };
 
 /* LLaMA-shaped target (also the draft layer's head layout: Hq, Hkv, hd, ffn). */
@@ -84,7 +85,10 @@ typedef struct {
  * expansion, `n_nodes` kept (root excluded), ranked by cumulative draft
  * log-probability.  SAMPLE_CHAIN: chain of `depth` drafts each drawn from
  * q = softmax(draft logits / temperature) (or its argmax when draft_greedy);
- * requires topk == 1 and n_nodes == depth. */
+ * requires topk == 1 and n_nodes == depth.  SAMPLE_TREE: the GREEDY_TREE
+ * draft, accepted by level-by-level rejection sampling at `temperature` > 0
+ * ("Advanced speculative decoding: tree drafts and EAGLE", Exercises, trees
+ * under sampling). */
 typedef struct {
   int32_t mode, depth, topk, n_nodes;
   float temperature;
@@ -233,6 +237,20 @@ eagle3_status eagle3_tree_from_logits(eagle3_ctx *ctx, int32_t batch, const int3
  *   SAMPLE_CHAIN: logits [B, n_rows, V] target logits; q [B, depth, V];
  *                uniforms [B, depth+1]: uniforms[b][i] decides draft i+1,
  *                uniforms[b][depth] drives the one residual or bonus draw.
+ *   SAMPLE_TREE: logits [B, n_rows, V] target logits (p = softmax(logits /
+ *                temperature)); parents as from eagle3_draft_tree; q unused;
+ *                uniforms [B, depth*topk + 1] in [0, 1).  From the root, the
+ *                current node's children are tested in row order: child i (a
+ *                top-k pick, so its draft distribution is the point mass at
+ *                its token x) is accepted iff u < p'(x), p' the node's
+ *                residual, with u = uniforms[b][d*topk + i] (d = the node's
+ *                depth); a rejection removes x from p'.  An accepted child
+ *                becomes the current node; when every child is rejected, or
+ *                the node has none, next_root is drawn from the residual with
+ *                uniforms[b][depth*topk] and the walk ends.  Decisions use the
+ *                samplers' fixed point: W_v = floor(p(v) * 2^48), accept iff
+ *                floor(u * S) < W_x with S the integer mass not yet removed.
+ *                A malformed tree or token raises BAD_TREE / BAD_TOKEN.
  * Outputs: path [B, depth+1] (tree row indices, root first, -1 padded),
  * path_len [B], next_root [B], emitted [B, depth+1] (committed tokens, -1
  * padded; may be NULL). */

@@ -29,7 +29,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .accept import argmax_rows_f32, chain_rejection, greedy_walk
+from .accept import argmax_rows_f32, chain_rejection, greedy_walk, tree_rejection
 from .llama import (KVCache, Shape, causal_visible, draft_fuse, draft_layer, draft_logits,
                     target_forward)
 from .numerics import argmax_first, probs_f32, sample_inverse_cdf
@@ -38,7 +38,7 @@ from .tree import Tree, build_dynamic_tree, tree_mask
 
 @dataclass
 class SpecConfig:
-    mode: str               # "greedy_tree" or "sample_chain"
+    mode: str               # "greedy_tree", "sample_chain" or "sample_tree"
     depth: int              # D (chain length K in sample_chain mode)
     topk: int               # k (1 in sample_chain mode)
     n_nodes: int            # N, draft nodes excluding the root
@@ -166,13 +166,14 @@ class OracleSequence:
     def draft_tree(self, u_draft=None):
         """The draft stage: catch-up, then the tree (or sampled chain).
 
-        Returns (Tree, q) where q is [K, V] float32 in sample_chain mode, else None.
+        Returns (Tree, q) where q is [K, V] float32 in sample_chain mode, else None
+        (sample_tree drafts the greedy mode's tree: its candidates are top-k picks).
         """
         a_last = self.draft_catchup()
         root_logits = f32(draft_logits(self.H, self.W, self.shp, a_last))
         expand = self._expander(a_last)
         s = self.spec
-        if s.mode == "greedy_tree":
+        if s.mode in ("greedy_tree", "sample_tree"):
             return build_dynamic_tree(self.root, root_logits, expand, s.depth, s.topk, s.n_nodes), None
         toks, q = build_sampled_chain(self.root, root_logits, expand, s.depth, s.temperature,
                                       u_draft, s.draft_greedy)
@@ -193,6 +194,9 @@ class OracleSequence:
     def accept(self, tree: Tree, logits, q=None, u_accept=None):
         if self.spec.mode == "greedy_tree":
             return greedy_walk(tree.tokens, tree.parents, argmax_rows_f32(logits))
+        if self.spec.mode == "sample_tree":
+            p = np.stack([probs_f32(f32(logits[i]), self.spec.temperature) for i in range(len(tree.tokens))])
+            return tree_rejection(tree.tokens, tree.parents, p, u_accept, self.spec.topk, self.spec.depth)
         K = self.spec.depth
         p = np.stack([probs_f32(f32(logits[i]), self.spec.temperature) for i in range(K + 1)])
         n_acc, nxt = chain_rejection(tree.tokens[1:], q, p, u_accept)

@@ -14,7 +14,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeagle3.so")
 
 F32, BF16 = 0, 1
-GREEDY_TREE, SAMPLE_CHAIN = 0, 1
+GREEDY_TREE, SAMPLE_CHAIN, SAMPLE_TREE = 0, 1, 2
 LM_ALL, LM_LAST, LM_NONE = 0, 1, 2
 PROF_GEMM_M64, PROF_GEMM_M16, PROF_ATTN, PROF_GEMM_BIG = 0, 1, 2, 3
 DEV_KV_OVERFLOW, DEV_BAD_TREE, DEV_BAD_TOKEN, DEV_BAD_PATH = 1, 2, 4, 8

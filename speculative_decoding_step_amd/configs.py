@@ -38,7 +38,7 @@ class Workload:
     cid: int
     name: str
     shape: ModelShape
-    mode: str               # "greedy_tree" | "sample_chain"
+    mode: str               # "greedy_tree" | "sample_chain" | "sample_tree"
     depth: int
     topk: int
     n_nodes: int
@@ -79,6 +79,9 @@ WORKLOADS = {
                                         4, 64, 192, temperature=1.0, max_len=256),
     "llama8b_tree_b64": Workload(5, "llama8b_tree_b64", L8B, "greedy_tree", 4, 4, 16, 64, 4096, 32,
                                  ragged_min=128),
+    # the batch-1 tree under sampling: the same draft tree, accepted by level-by-level rejection sampling at T = 1
+    "llama8b_sample_tree_b1": Workload(6, "llama8b_sample_tree_b1", L8B, "sample_tree", 6, 10, 60, 1, 2048, 128,
+                                       temperature=1.0),
 }
 
 

@@ -124,7 +124,7 @@ size_t carve(eagle3_ctx* c, char* base) {
   c->roots = cv.take<int>(B);
   const int D = c->cfg.depth, k = c->cfg.topk;
   c->emax = std::max(1, (D - 1) * k);
-  c->n_cand = c->cfg.mode == EAGLE3_GREEDY_TREE ? k + (D - 1) * k * k : D;
+  c->n_cand = c->cfg.mode != EAGLE3_SAMPLE_CHAIN ? k + (D - 1) * k * k : D;
   c->a_last = cv.take<float>((size_t)B * d);
   c->a_rows = cv.take<float>((size_t)B * c->emax * d);
   c->dr.batch = B;
@@ -168,9 +168,10 @@ eagle3_status check_shape(const eagle3_shape* s, const eagle3_spec_cfg* c) {
   if (s->vocab > 64 * 4096) return EAGLE3_EUNSUPPORTED;
   if (c->depth < 1 || c->topk < 1 || c->topk > KMAX || c->n_nodes < 1 || c->topk > s->vocab) return EAGLE3_EINVAL;
   if (c->n_nodes + 1 > 64 || (c->depth - 1) * c->topk > 64) return EAGLE3_EUNSUPPORTED;
-  if (c->mode == EAGLE3_GREEDY_TREE) {
+  if (c->mode == EAGLE3_GREEDY_TREE || c->mode == EAGLE3_SAMPLE_TREE) {
     const int nc = c->topk + (c->depth - 1) * c->topk * c->topk;
     if (nc < c->n_nodes || nc > TREE_CMAX) return EAGLE3_EUNSUPPORTED;
+    if (c->mode == EAGLE3_SAMPLE_TREE && !(c->temperature > 0.f)) return EAGLE3_EINVAL;
   } else if (c->mode == EAGLE3_SAMPLE_CHAIN) {
     if (c->topk != 1 || c->n_nodes != c->depth || !(c->temperature > 0.f)) return EAGLE3_EINVAL;
   } else {
@@ -494,7 +495,7 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
   DraftRows dr = c->dr;
   dr.batch = batch;
   const size_t tstride = (size_t)(1 + c->emax) * V;  // table row stride between sequences
-  if (c->cfg.mode == EAGLE3_GREEDY_TREE) {
+  if (c->cfg.mode != EAGLE3_SAMPLE_CHAIN) {  // trees (greedy or sampled acceptance alike)
     tree_children(ts, 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
     for (int dd = 1; dd < D; ++dd) {
       const int n = batch * k;
@@ -755,6 +756,14 @@ eagle3_status eagle3_accept(eagle3_ctx* c, int32_t batch, int32_t n_rows, const 
     if (!parents || !argmax) return EAGLE3_EINVAL;
     accept_greedy(batch, n_rows, c->cfg.depth, tokens, parents, argmax, path, path_len, next_root, emitted, c->status,
                   c->st);
+  } else if (c->cfg.mode == EAGLE3_SAMPLE_TREE) {
+    if (!parents || !logits || !uniforms) return EAGLE3_EINVAL;
+    if ((size_t)batch * n_rows > (size_t)c->R) return EAGLE3_ECAPACITY;
+    const int V = c->sh.vocab;
+    topk_lse(logits, batch * n_rows, V, V, 1, c->cfg.temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum,
+             c->tk_ids, c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
+    accept_tree(batch, n_rows, V, c->cfg.topk, c->cfg.depth, tokens, parents, logits, c->tk_lse64,
+                c->cfg.temperature, uniforms, path, path_len, next_root, emitted, c->status, c->st);
   } else {
     const int K = c->cfg.depth;
     if (n_rows != K + 1 || !logits || !q || !uniforms) return EAGLE3_EINVAL;

@@ -9,6 +9,14 @@
 // III.5, X.3-X.6).  Draws use the integer inverse CDF over
 // W_v = floor(w_v * 2^48) with r = floor(u * sum W), so the pick does not
 // depend on summation order.
+// Sampling (trees): level by level, a node's children are tested in row
+// order; each was chosen by the draft's top-k, so its draft distribution is
+// the point mass at its token and it is accepted iff u < p'(x) with p' the
+// node's residual; a rejection removes x's mass (norm(max(0, p' - q))); when
+// every child is rejected, or the node has none, one token is drawn from the
+// final residual ("Advanced speculative decoding: tree drafts and EAGLE",
+// Exercises, trees under sampling).  In the same fixed point: child i is
+// accepted iff floor(u * S_i) < W_x, S_i the integer mass not yet removed.
 // Compaction: the accepted nodes' K/V move to consecutive slots after the
 // committed prefix (the page's note on compacting KV slots).
 #include "common.hpp"
@@ -149,6 +157,155 @@ __global__ __launch_bounds__(1024) void k_accept_chain(int K, int V, const int* 
   }
 }
 
+// Block-wide inclusive prefix sum of one value per thread (1024 threads):
+// sc[tid] receives the prefix, the total is returned to every thread.
+__device__ unsigned long long block_prefix(unsigned long long* sc, unsigned long long x) {
+  const int tid = threadIdx.x;
+  __syncthreads();  // earlier readers of sc are done
+  sc[tid] = x;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const unsigned long long add = tid >= o ? sc[tid - o] : 0ull;
+    __syncthreads();
+    sc[tid] += add;
+    __syncthreads();
+  }
+  return sc[1023];
+}
+
+// floor(p(v) * 2^48), p(v) = fl32(exp(z_v / T - lse)) (the samplers' integer weight)
+__device__ __forceinline__ unsigned long long int_weight(const float* z, int v, double temp, double lse) {
+  return (unsigned long long)ldexpf((float)exp((double)z[v] / temp - lse), 48);
+}
+
+// One block of 1024 threads per sequence, n_rows <= 64, topk <= 64.
+// lse64[b*n_rows + i] = log-sum-exp of row i's logits / T in double.
+// uniforms [B, maxd*topk + 1]: child i of the node at depth d uses
+// uniforms[d*topk + i], the final draw uses uniforms[maxd*topk].
+__global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int topk, int maxd,
+                                                      const int* __restrict__ tokens, const int* __restrict__ parents,
+                                                      const float* __restrict__ logits,
+                                                      const double* __restrict__ lse64, double temp,
+                                                      const float* __restrict__ uniforms, int* __restrict__ path,
+                                                      int* __restrict__ path_len, int* __restrict__ next_root,
+                                                      int* __restrict__ emitted, int* status) {
+  __shared__ unsigned long long scan[1024];
+  __shared__ unsigned long long wkid[64];
+  __shared__ int kid[64], rej[64], pathv[64];
+  __shared__ int s_node, s_len, s_nk, s_nrej, s_go, s_pick;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int* tk = tokens + (size_t)b * n_rows;
+  const int* pa = parents + (size_t)b * n_rows;
+  const float* u = uniforms + (size_t)b * ((size_t)maxd * topk + 1);
+  const int maxp = maxd + 1;
+  if (tid == 0) {
+    bool bad_tree = false, bad_tok = false;
+    for (int i = 1; i < n_rows; ++i) bad_tree |= pa[i] < 0 || pa[i] >= i;
+    for (int i = 0; i < n_rows; ++i) bad_tok |= tk[i] < 0 || tk[i] >= V;
+    if (bad_tree) raise_flag(status, E3_DEV_BAD_TREE);
+    if (bad_tok) raise_flag(status, E3_DEV_BAD_TOKEN);
+    s_node = 0;
+    s_len = 1;
+    pathv[0] = 0;
+    s_pick = -1;
+  }
+  const int per = (V + 1023) / 1024;
+  const int v0 = min(V, tid * per), v1 = min(V, v0 + per);
+  while (true) {
+    __syncthreads();
+    const int node = s_node, len = s_len, d = len - 1;
+    // the node's children in row order (only later rows, so the walk always ends); depth-maxd nodes are leaves
+    if (tid == 0) {
+      int nk = 0;
+      if (d < maxd)
+        for (int j = node + 1; j < n_rows; ++j)
+          if (pa[j] == node) {
+            if (nk < topk) kid[nk] = j;
+            ++nk;
+          }
+      if (nk > topk) raise_flag(status, E3_DEV_BAD_TREE);
+      s_nk = min(nk, topk);
+    }
+    __syncthreads();
+    const int nk = s_nk;
+    const float* z = logits + ((size_t)b * n_rows + node) * V;
+    const double l = lse64[(size_t)b * n_rows + node];
+    unsigned long long mine = 0ull;
+    for (int v = v0; v < v1; ++v) mine += int_weight(z, v, temp, l);
+    const unsigned long long S = block_prefix(scan, mine);
+    if (tid < nk) {
+      const int x = tk[kid[tid]];
+      wkid[tid] = (x >= 0 && x < V) ? int_weight(z, x, temp, l) : 0ull;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long rem = S;
+      int acc = -1, i = 0;
+      for (; i < nk; ++i) {
+        const int x = tk[kid[i]];
+        bool dup = false;
+        for (int j = 0; j < i; ++j) dup |= rej[j] == x;
+        const unsigned long long wx = dup ? 0ull : wkid[i];
+        const unsigned long long uu = (unsigned long long)(u[d * topk + i] * 16777216.0f);
+        const unsigned long long r = (rem >> 24) * uu + (((rem & 0xffffffull) * uu) >> 24);  // floor(u * rem)
+        if (r < wx) {
+          acc = kid[i];
+          break;
+        }
+        rem -= wx;
+        rej[i] = x;
+      }
+      if (acc >= 0) {
+        pathv[len] = acc;
+        s_len = len + 1;
+        s_node = acc;
+        s_go = 1;
+      } else {
+        s_nrej = i;
+        s_go = 0;
+      }
+    }
+    __syncthreads();
+    if (!s_go) break;
+  }
+  // final draw from the residual at the last node: its p with the rejected candidates removed
+  const int node = s_node, nrej = s_nrej;
+  const float* z = logits + ((size_t)b * n_rows + node) * V;
+  const double l = lse64[(size_t)b * n_rows + node];
+  auto w_res = [&](int v) -> unsigned long long {
+    for (int j = 0; j < nrej; ++j)
+      if (rej[j] == v) return 0ull;
+    return int_weight(z, v, temp, l);
+  };
+  unsigned long long mine = 0ull;
+  for (int v = v0; v < v1; ++v) mine += w_res(v);
+  const unsigned long long S = block_prefix(scan, mine);
+  const unsigned long long uu = (unsigned long long)(u[(size_t)maxd * topk] * 16777216.0f);
+  const unsigned long long r = (S >> 24) * uu + (((S & 0xffffffull) * uu) >> 24);
+  const unsigned long long lo = tid ? scan[tid - 1] : 0ull;
+  if (S > 0ull && r >= lo && r < scan[tid]) {  // exactly one thread's slice holds the pick
+    unsigned long long acc = lo;
+    for (int v = v0; v < v1; ++v) {
+      acc += w_res(v);
+      if (acc > r) {
+        s_pick = v;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int len = s_len;
+  if (tid < maxp) {
+    const int row = tid < len ? pathv[tid] : -1;
+    path[(size_t)b * maxp + tid] = row;
+    if (emitted) emitted[(size_t)b * maxp + tid] = row >= 0 ? tk[row] : -1;
+  }
+  if (tid == 0) {
+    path_len[b] = len;
+    next_root[b] = s_pick;
+  }
+}
+
 // grid (B, L*2*Hkv): per (sequence, layer, K|V, head) move path rows to slots P..P+n-1.
 template <typename E>
 __global__ __launch_bounds__(128) void k_compact_kv(const int* __restrict__ seq_lens, const int* __restrict__ path,
@@ -234,6 +391,13 @@ void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const in
                    int* path, int* path_len, int* next_root, int* emitted, int* status, hipStream_t st) {
   k_accept_greedy<<<batch, 64, 0, st>>>(batch, n_rows, depth + 1, tokens, parents, argmax, path, path_len, next_root,
                                         emitted, status);
+}
+
+void accept_tree(int batch, int n_rows, int V, int topk, int depth, const int* tokens, const int* parents,
+                 const float* logits, const double* lse64, float temperature, const float* uniforms, int* path,
+                 int* path_len, int* next_root, int* emitted, int* status, hipStream_t st) {
+  k_accept_tree<<<batch, 1024, 0, st>>>(n_rows, V, topk, depth, tokens, parents, logits, lse64, (double)temperature,
+                                        uniforms, path, path_len, next_root, emitted, status);
 }
 
 void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,

@@ -19,7 +19,7 @@ from . import configs, synth
 
 @dataclass
 class Spec:
-    mode: str          # "greedy_tree" | "sample_chain"
+    mode: str          # "greedy_tree" | "sample_chain" | "sample_tree"
     depth: int
     topk: int
     n_nodes: int
@@ -67,7 +67,8 @@ class Engine:
         w = self.w
         self.shape = B.Shape(ms.n_layers, d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, V, ms.rope_theta,
                              ms.eps, B.BF16 if self.bf16 else B.F32, (C.c_int32 * 3)(*ms.taps))
-        self.cfg = B.SpecCfg(B.GREEDY_TREE if spec.mode == "greedy_tree" else B.SAMPLE_CHAIN, spec.depth, spec.topk,
+        modes = {"greedy_tree": B.GREEDY_TREE, "sample_chain": B.SAMPLE_CHAIN, "sample_tree": B.SAMPLE_TREE}
+        self.cfg = B.SpecCfg(modes[spec.mode], spec.depth, spec.topk,
                              spec.n_nodes, spec.temperature, int(spec.draft_greedy))
         self._layers = (B.LayerWeights * ms.n_layers)()
         for l in range(ms.n_layers):
@@ -103,8 +104,12 @@ class Engine:
         self.pos = torch.zeros(batch, R, **i32)
         self.mask = torch.zeros(batch, R, dtype=torch.int64, device=self.dev)
         self.score = torch.zeros(batch, R, dtype=torch.float32, device=self.dev)
-        self.sampling = spec.mode == "sample_chain"
-        self.q = torch.zeros(batch, spec.depth, V, dtype=torch.float32, device=self.dev) if self.sampling else None
+        self.chain = spec.mode == "sample_chain"
+        self.sampling = spec.mode in ("sample_chain", "sample_tree")
+        # acceptance uniforms per sequence: one per draft + the final draw (chain), one per (depth, child) + the
+        # final draw (tree)
+        self.n_u_accept = spec.depth + 1 if self.chain else spec.depth * spec.topk + 1
+        self.q = torch.zeros(batch, spec.depth, V, dtype=torch.float32, device=self.dev) if self.chain else None
         self.logits = torch.zeros(batch * R, V, dtype=torch.float32, device=self.dev) if self.sampling else None
         self.argmax = torch.zeros(batch * R, **i32)
         self.margin = torch.zeros(batch * R, dtype=torch.float32, device=self.dev)
@@ -114,7 +119,7 @@ class Engine:
         self.next_root = torch.zeros(batch, **i32)
         self.emitted = torch.zeros(batch, Wd, **i32)
         self.u_draft = torch.zeros(batch, spec.depth, dtype=torch.float32, device=self.dev)
-        self.u_accept = torch.zeros(batch, spec.depth + 1, dtype=torch.float32, device=self.dev)
+        self.u_accept = torch.zeros(batch, self.n_u_accept, dtype=torch.float32, device=self.dev)
         self.step_idx = 0
 
     def _tensor(self, seed, name, shape, kind, sigma):
@@ -193,7 +198,7 @@ class Engine:
 
     def draft(self):
         B.eagle3_draft_tree(self.ctx, self.B, _ptr(self.seq_lens), _ptr(self.new_len), _ptr(self.aux_new),
-                            _ptr(self.next_tok), _ptr(self.u_draft) if self.sampling else None, _ptr(self.tokens),
+                            _ptr(self.next_tok), _ptr(self.u_draft) if self.chain else None, _ptr(self.tokens),
                             _ptr(self.parents), _ptr(self.depth), _ptr(self.pos), _ptr(self.mask), _ptr(self.score),
                             _ptr(self.q))
 

@@ -171,6 +171,83 @@ def test_sampled_chain_first_token_distribution_v64():
     eng.close()
 
 
+def test_sampled_tree_first_token_distribution_v64():
+    """Vocab-64 tree under sampling (depth 3, top-3, 8 nodes, T = 1): the first token the
+    step decides after a fixed root is distributed as the target p(. | prompt, root),
+    whatever the draft tree: chi-square over 1e5 seeded draws."""
+    ms = configs.ModelShape(2, 256, 4, 2, 64, 512, 64, 1e4, (0, 1, 1), dtype="f32")
+    D, k, N, Bn, reps = 3, 3, 8, 1000, 100
+    spec = Spec("sample_tree", D, k, N, 1.0)
+    shp, W, H = oracle_weights(ms, seed=37, sigma=0.1)
+    prompt = list(synth.tokens_np(47, "p", 8, ms.vocab))
+    eng = make_engine(ms, spec, batch=Bn, max_seq=40, seed=37, sigma=0.1, prefill_chunk=16)
+    eng.prefill([prompt] * Bn, synth.uniform24_t(5000, "u_root", Bn, "cuda"))
+    root = 11
+    eng.next_tok[:, 0] = root
+    saved = [t.clone() for t in (eng.seq_lens, eng.new_len, eng.aux_new, eng.next_tok)]
+    nu = eng.n_u_accept
+    counts = np.zeros(ms.vocab)
+    lens = np.zeros(D + 2)
+    for s in range(reps):
+        for t, v in zip((eng.seq_lens, eng.new_len, eng.aux_new, eng.next_tok), saved):
+            t.copy_(v)
+        eng.set_uniforms(None, synth.uniform24_t(5000, f"u_tree{s}", Bn * nu, "cuda").view(Bn, nu))
+        eng.step()
+        em = eng.emitted.cpu().numpy()
+        pl = eng.path_len.cpu().numpy()
+        nr = eng.next_root.cpu().numpy()
+        counts += np.bincount(np.where(pl >= 2, em[:, 1], nr), minlength=ms.vocab)
+        lens += np.bincount(pl, minlength=D + 2)
+    assert eng.device_status() == 0
+    cache = KVCache(shp.n_layers, 16, shp.n_kv_heads, shp.head_dim)
+    full = prompt + [root]
+    lg, _, _, _ = target_forward(W, shp, cache, full, np.arange(len(full)), causal_visible(len(full)))
+    p = probs_f32(lg[-1].astype(np.float32), 1.0).astype(np.float64)
+    exp = p * counts.sum()
+    keep = exp >= 5
+    obs_m = np.append(counts[keep], counts[~keep].sum())
+    exp_m = np.append(exp[keep], exp[~keep].sum())
+    if exp_m[-1] < 5:
+        obs_m, exp_m = obs_m[:-1], exp_m[:-1]
+    stat = ((obs_m - exp_m) ** 2 / exp_m).sum()
+    pval = chi2.sf(stat, len(obs_m) - 1)
+    print(f"\n  chi-square {stat:.1f} dof {len(obs_m) - 1} p={pval:.3g}; path lengths {lens[1:].astype(int)}",
+          flush=True)
+    assert pval > 1e-3
+    eng.close()
+
+
+def test_sampled_tree_steps_match_oracle_f32():
+    """Tree drafts accepted by rejection sampling, six steps on an fp32 toy model: every
+    step's tree, accepted path and next token equal the oracle's for the same uniforms."""
+    ms = toy_shape(dtype="f32", vocab=96, layers=2)
+    D, k, N, T = 3, 3, 8, 0.8
+    spec = Spec("sample_tree", D, k, N, T)
+    shp, W, H = oracle_weights(ms, seed=29, sigma=0.3)
+    prompt = synth.tokens_np(52, "p", 24, ms.vocab)
+    eng = make_engine(ms, spec, max_seq=96, seed=29, sigma=0.3)
+    u_root = synth.uniform24_t(5000, "u_root", 1, "cuda")
+    eng.prefill([prompt], u_root)
+    seq = OracleSequence(W, H, shp, SpecConfig("sample_tree", D, k, N, T), 96)
+    seq.prefill(prompt, np.float32(u_root.cpu().numpy()[0]))
+    assert eng.next_tok[0, 0].item() == seq.root
+    nu = eng.n_u_accept
+    lens = []
+    for s in range(6):
+        u = synth.uniform24_t(5000, f"u_acc{s}", nu, "cuda").view(1, nu)
+        eng.set_uniforms(None, u)
+        eng.step()
+        tree, path, nxt = seq.step(u_accept=u.cpu().numpy()[0])
+        assert eng.device_status() == 0
+        assert list(eng.tokens[0].cpu().numpy()) == tree.tokens
+        n = eng.path_len[0].item()
+        assert list(eng.path[0].cpu().numpy()[:n]) == path
+        assert eng.next_root[0].item() == nxt
+        lens.append(n)
+    print(f"\n  accepted path lengths {lens}", flush=True)
+    eng.close()
+
+
 def test_graph_replay_matches_eager_steps():
     """The captured step graph, replayed with eager work and synchronisations in
     between, gives bit-identical tokens, paths and KV to eager steps."""

@@ -13,7 +13,7 @@ import torch
 
 from gpu_util import (kv_view, logits_close, make_engine, margin_tol, oracle_weights, random_tree, to_dev,
                       toy_shape, top2_margin)
-from oracle.accept import chain_rejection, greedy_walk
+from oracle.accept import chain_rejection, greedy_walk, tree_rejection
 from oracle.llama import KVCache, causal_visible, target_forward
 from oracle.numerics import probs_f32, sample_inverse_cdf
 from oracle.step import build_sampled_chain
@@ -264,6 +264,107 @@ def test_accept_chain_matches_oracle():
         assert nxt[b].item() == tok
         assert list(em[b].cpu().numpy()) == [int(x) for x in toks[b, :n_acc + 1]] + [-1] * (K - n_acc)
     assert len(seen) >= 2
+    eng.close()
+
+
+def _random_tree(rng, D, k, N, V):
+    """Rows in (depth, creation) order: each level's nodes pick a parent on the previous
+    level with fewer than k children; siblings hold distinct tokens."""
+    tokens, parents, depth, kids = [int(rng.integers(0, V))], [-1], [0], [set()]
+    level = [0]
+    while len(tokens) < N + 1:
+        d = depth[level[0]] + 1
+        if d > D:
+            break
+        nxt = []
+        slots = [(p, j) for p in level for j in range(k)]
+        rng.shuffle(slots)
+        for p, _ in slots[:min(len(slots), N + 1 - len(tokens))]:
+            t = int(rng.integers(0, V))
+            while t in kids[p]:
+                t = int(rng.integers(0, V))
+            kids[p].add(t)
+            tokens.append(t)
+            parents.append(p)
+            depth.append(d)
+            kids.append(set())
+            nxt.append(len(tokens) - 1)
+        level = nxt
+    # renumber so that each level's rows follow their parents' order (children of one node stay in creation order)
+    order = sorted(range(len(tokens)), key=lambda i: (depth[i], i))
+    new = {o: i for i, o in enumerate(order)}
+    return ([tokens[o] for o in order], [-1 if parents[o] < 0 else new[parents[o]] for o in order],
+            [depth[o] for o in order])
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_accept_tree_matches_oracle(T):
+    """Level-by-level rejection sampling over trees: path, path length, next token and the
+    emitted row equal the oracle's bit for bit on random trees, target rows that favour
+    each node's candidates (so long paths occur) and seeded uniforms."""
+    rng = np.random.default_rng(11)
+    D, k, N, V, Bn = 4, 3, 14, 3000, 24
+    eng = _tree_engine(D, k, N, V, mode="sample_tree", T=T, batch=Bn)
+    R = N + 1
+    toks = np.zeros((Bn, R), np.int32)
+    pars = np.zeros((Bn, R), np.int32)
+    trees = []
+    for b in range(Bn):
+        t, pa, _ = _random_tree(rng, D, k, N, V)
+        assert len(t) == R
+        toks[b], pars[b] = t, pa
+        trees.append((t, pa))
+    logits = rng.normal(0, 1.0, size=(Bn, R, V)).astype(np.float32)
+    for b in range(Bn):
+        for i in range(1, R):
+            logits[b, pars[b, i], toks[b, i]] += rng.uniform(2.0, 7.0)
+    nu = D * k + 1
+    u = (rng.integers(0, 1 << 24, size=(Bn, nu)) * 2.0 ** -24).astype(np.float32)
+    maxp = D + 1
+    path = torch.zeros(Bn, maxp, dtype=torch.int32, device="cuda")
+    plen = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    nxt = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    em = torch.zeros(Bn, maxp, dtype=torch.int32, device="cuda")
+    keep = [to_dev(toks), to_dev(pars), to_dev(logits, torch.float32), to_dev(u, torch.float32)]
+    B.eagle3_accept(eng.ctx, Bn, R, _p(keep[0]), _p(keep[1]), None, _p(keep[2]), None, _p(keep[3]), _p(path),
+                    _p(plen), _p(nxt), _p(em))
+    torch.cuda.synchronize()
+    assert eng.device_status() == 0
+    lens = set()
+    for b in range(Bn):
+        p = np.stack([probs_f32(logits[b, i], T) for i in range(R)])
+        ref_path, ref_next = tree_rejection(trees[b][0], trees[b][1], p, u[b], k, D)
+        lens.add(len(ref_path))
+        assert plen[b].item() == len(ref_path)
+        assert list(path[b].cpu().numpy()) == ref_path + [-1] * (maxp - len(ref_path))
+        assert nxt[b].item() == ref_next
+        assert list(em[b].cpu().numpy()) == [trees[b][0][i] for i in ref_path] + [-1] * (maxp - len(ref_path))
+    assert len(lens) >= 3  # short and long walks both covered
+    eng.close()
+
+
+def test_accept_tree_flags_malformed_input():
+    """A parent index not below its row, or a token outside the vocabulary, raises the
+    context's status bits (the walk still ends and every lookup stays in range)."""
+    D, k, N, V = 3, 2, 4, 500
+    eng = _tree_engine(D, k, N, V, mode="sample_tree", T=1.0, batch=2)
+    R = N + 1
+    toks = np.array([[1, 2, 3, 4, 5], [1, 2, 3, V + 7, 5]], np.int32)
+    pars = np.array([[-1, 0, 3, 0, 1], [-1, 0, 0, 1, 1]], np.int32)
+    logits = np.zeros((2, R, V), np.float32)
+    u = np.full((2, D * k + 1), 0.5, np.float32)
+    maxp = D + 1
+    outs = [torch.zeros(2, maxp, dtype=torch.int32, device="cuda"), torch.zeros(2, dtype=torch.int32, device="cuda"),
+            torch.zeros(2, dtype=torch.int32, device="cuda"), torch.zeros(2, maxp, dtype=torch.int32, device="cuda")]
+    keep = [to_dev(toks), to_dev(pars), to_dev(logits, torch.float32), to_dev(u, torch.float32)]
+    B.eagle3_accept(eng.ctx, 2, R, _p(keep[0]), _p(keep[1]), None, _p(keep[2]), None, _p(keep[3]),
+                    *[_p(t) for t in outs])
+    torch.cuda.synchronize()
+    flags = eng.device_status()
+    assert flags & B.DEV_BAD_TREE and flags & B.DEV_BAD_TOKEN
+    for b in range(2):
+        n = outs[1][b].item()
+        assert 1 <= n <= maxp and 0 <= outs[2][b].item() < V
     eng.close()
 
 
