@@ -66,6 +66,7 @@ struct eagle3_ctx {
   float *tk_pv, *tk_pmax, *tk_vals, *tk_lse;
   int *tk_pi, *tk_ids;
   double *tk_psum, *tk_lse64;
+  unsigned long long* tk_wsum;  // per-row slice sums of integer sampling weights
   RowMeta rm;
   int *rtok, *gidx, *roots;
   float *a_last, *a_rows;
@@ -113,6 +114,7 @@ size_t carve(eagle3_ctx* c, char* base) {
   c->tk_vals = cv.take<float>((size_t)R * KMAX);
   c->tk_lse = cv.take<float>(R);
   c->tk_lse64 = cv.take<double>(R);
+  c->tk_wsum = cv.take<unsigned long long>((size_t)R * accept_tree_slices(V));
   c->rm.seq = cv.take<int>(R);
   c->rm.pos = cv.take<int>(R);
   c->rm.slot = cv.take<int>(R);
@@ -762,7 +764,7 @@ eagle3_status eagle3_accept(eagle3_ctx* c, int32_t batch, int32_t n_rows, const 
     const int V = c->sh.vocab;
     topk_lse(logits, batch * n_rows, V, V, 1, c->cfg.temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum,
              c->tk_ids, c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
-    accept_tree(batch, n_rows, V, c->cfg.topk, c->cfg.depth, tokens, parents, logits, c->tk_lse64,
+    accept_tree(batch, n_rows, V, c->cfg.topk, c->cfg.depth, tokens, parents, logits, c->tk_lse64, c->tk_wsum,
                 c->cfg.temperature, uniforms, path, path_len, next_root, emitted, c->status, c->st);
   } else {
     const int K = c->cfg.depth;

@@ -178,39 +178,68 @@ __device__ __forceinline__ unsigned long long int_weight(const float* z, int v, 
   return (unsigned long long)ldexpf((float)exp((double)z[v] / temp - lse), 48);
 }
 
-// One block of 1024 threads per sequence, n_rows <= 64, topk <= 64.
-// lse64[b*n_rows + i] = log-sum-exp of row i's logits / T in double.
+constexpr int WS_SLICE = 4096;  // vocabulary entries per weight slice
+
+// grid (slices, rows), 256 threads: wsum[row * ns + s] = sum of the integer
+// weights floor(p(v) * 2^48) over slice s of the row (exact, order-free).
+__global__ __launch_bounds__(256) void k_row_wsum(int V, int ns, const float* __restrict__ logits,
+                                                  const double* __restrict__ lse64, double temp,
+                                                  unsigned long long* __restrict__ wsum) {
+  __shared__ unsigned long long red[256];
+  const int s = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const float* z = logits + (size_t)row * V;
+  const double l = lse64[row];
+  const int v1 = min(V, (s + 1) * WS_SLICE);
+  unsigned long long acc = 0ull;
+  for (int v = s * WS_SLICE + tid; v < v1; v += 256) acc += int_weight(z, v, temp, l);
+  red[tid] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) wsum[(size_t)row * ns + s] = red[0];
+}
+
+// One block of 1024 threads per sequence, n_rows <= 64, topk <= 64, ns <= 64,
+// depth * topk + 1 <= 1024.  lse64[b*n_rows + i] = log-sum-exp of row i's logits / T in double; wsum
+// [b*n_rows + i][ns] the rows' slice sums of integer weights (k_row_wsum).
 // uniforms [B, maxd*topk + 1]: child i of the node at depth d uses
-// uniforms[d*topk + i], the final draw uses uniforms[maxd*topk].
-__global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int topk, int maxd,
+// uniforms[d*topk + i], the final draw uses uniforms[maxd*topk].  A visited
+// node costs one weight per child; the final draw finds the slice holding
+// r = floor(u * S) from the slice sums (less the rejected tokens' weights)
+// and scans that slice only, so the pick is the full inverse CDF's.
+__global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int topk, int maxd, int ns,
                                                       const int* __restrict__ tokens, const int* __restrict__ parents,
                                                       const float* __restrict__ logits,
-                                                      const double* __restrict__ lse64, double temp,
+                                                      const double* __restrict__ lse64,
+                                                      const unsigned long long* __restrict__ wsum, double temp,
                                                       const float* __restrict__ uniforms, int* __restrict__ path,
                                                       int* __restrict__ path_len, int* __restrict__ next_root,
                                                       int* __restrict__ emitted, int* status) {
   __shared__ unsigned long long scan[1024];
-  __shared__ unsigned long long wkid[64];
-  __shared__ int kid[64], rej[64], pathv[64];
-  __shared__ int s_node, s_len, s_nk, s_nrej, s_go, s_pick;
+  __shared__ unsigned long long wkid[64], wsl[64];
+  __shared__ int kid[64], rej[64], pathv[64], tk[64], pa[64];
+  __shared__ float u[1024];
+  __shared__ unsigned long long s_rem, s_rin;
+  __shared__ int s_node, s_len, s_nk, s_nrej, s_go, s_pick, s_slice;
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int* tk = tokens + (size_t)b * n_rows;
-  const int* pa = parents + (size_t)b * n_rows;
-  const float* u = uniforms + (size_t)b * ((size_t)maxd * topk + 1);
-  const int maxp = maxd + 1;
+  const int maxp = maxd + 1, nu = maxd * topk + 1;
+  // the sequence's tree and uniforms, staged once (the walk below is sequential)
+  if (tid < n_rows) {
+    const int t = tokens[(size_t)b * n_rows + tid], p = parents[(size_t)b * n_rows + tid];
+    tk[tid] = t;
+    pa[tid] = p;
+    if (tid >= 1 && (p < 0 || p >= tid)) raise_flag(status, E3_DEV_BAD_TREE);
+    if (t < 0 || t >= V) raise_flag(status, E3_DEV_BAD_TOKEN);
+  }
+  for (int i = tid; i < nu; i += 1024) u[i] = uniforms[(size_t)b * nu + i];
   if (tid == 0) {
-    bool bad_tree = false, bad_tok = false;
-    for (int i = 1; i < n_rows; ++i) bad_tree |= pa[i] < 0 || pa[i] >= i;
-    for (int i = 0; i < n_rows; ++i) bad_tok |= tk[i] < 0 || tk[i] >= V;
-    if (bad_tree) raise_flag(status, E3_DEV_BAD_TREE);
-    if (bad_tok) raise_flag(status, E3_DEV_BAD_TOKEN);
     s_node = 0;
     s_len = 1;
     pathv[0] = 0;
     s_pick = -1;
   }
-  const int per = (V + 1023) / 1024;
-  const int v0 = min(V, tid * per), v1 = min(V, v0 + per);
   while (true) {
     __syncthreads();
     const int node = s_node, len = s_len, d = len - 1;
@@ -228,18 +257,16 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
     }
     __syncthreads();
     const int nk = s_nk;
-    const float* z = logits + ((size_t)b * n_rows + node) * V;
-    const double l = lse64[(size_t)b * n_rows + node];
-    unsigned long long mine = 0ull;
-    for (int v = v0; v < v1; ++v) mine += int_weight(z, v, temp, l);
-    const unsigned long long S = block_prefix(scan, mine);
+    const size_t rrow = (size_t)b * n_rows + node;
     if (tid < nk) {
       const int x = tk[kid[tid]];
-      wkid[tid] = (x >= 0 && x < V) ? int_weight(z, x, temp, l) : 0ull;
+      wkid[tid] = (x >= 0 && x < V) ? int_weight(logits + rrow * V, x, temp, lse64[rrow]) : 0ull;
     }
+    if (tid < ns) wsl[tid] = wsum[rrow * ns + tid];
     __syncthreads();
     if (tid == 0) {
-      unsigned long long rem = S;
+      unsigned long long rem = 0ull;  // the node's integer mass, less the rejected candidates'
+      for (int j = 0; j < ns; ++j) rem += wsl[j];
       int acc = -1, i = 0;
       for (; i < nk; ++i) {
         const int x = tk[kid[i]];
@@ -262,6 +289,7 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
         s_go = 1;
       } else {
         s_nrej = i;
+        s_rem = rem;
         s_go = 0;
       }
     }
@@ -270,26 +298,53 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
   }
   // final draw from the residual at the last node: its p with the rejected candidates removed
   const int node = s_node, nrej = s_nrej;
-  const float* z = logits + ((size_t)b * n_rows + node) * V;
-  const double l = lse64[(size_t)b * n_rows + node];
-  auto w_res = [&](int v) -> unsigned long long {
-    for (int j = 0; j < nrej; ++j)
-      if (rej[j] == v) return 0ull;
-    return int_weight(z, v, temp, l);
-  };
-  unsigned long long mine = 0ull;
-  for (int v = v0; v < v1; ++v) mine += w_res(v);
-  const unsigned long long S = block_prefix(scan, mine);
-  const unsigned long long uu = (unsigned long long)(u[(size_t)maxd * topk] * 16777216.0f);
-  const unsigned long long r = (S >> 24) * uu + (((S & 0xffffffull) * uu) >> 24);
-  const unsigned long long lo = tid ? scan[tid - 1] : 0ull;
-  if (S > 0ull && r >= lo && r < scan[tid]) {  // exactly one thread's slice holds the pick
-    unsigned long long acc = lo;
-    for (int v = v0; v < v1; ++v) {
-      acc += w_res(v);
-      if (acc > r) {
-        s_pick = v;
+  const size_t rrow = (size_t)b * n_rows + node;
+  const float* z = logits + rrow * V;
+  const double l = lse64[rrow];
+  if (tid == 0) {
+    const unsigned long long S = s_rem;
+    const unsigned long long uu = (unsigned long long)(u[(size_t)maxd * topk] * 16777216.0f);
+    const unsigned long long r = (S >> 24) * uu + (((S & 0xffffffull) * uu) >> 24);
+    // remove each distinct rejected token's weight from its slice, then find the slice holding r
+    for (int i = 0; i < nrej; ++i) {
+      bool dup = false;
+      for (int k = 0; k < i; ++k) dup |= rej[k] == rej[i];
+      if (!dup && rej[i] >= 0 && rej[i] < V) wsl[rej[i] / WS_SLICE] -= wkid[i];
+    }
+    int slice = -1;
+    unsigned long long cum = 0ull;
+    for (int j = 0; j < ns && S > 0ull; ++j) {
+      if (r < cum + wsl[j]) {
+        slice = j;
         break;
+      }
+      cum += wsl[j];
+    }
+    s_slice = slice;
+    s_rin = r - cum;
+  }
+  __syncthreads();
+  const int slice = s_slice;
+  if (slice >= 0) {
+    constexpr int PER = WS_SLICE / 1024;
+    const int v0 = slice * WS_SLICE + tid * PER, v1 = min(V, v0 + PER);
+    auto w_res = [&](int v) -> unsigned long long {
+      for (int j = 0; j < nrej; ++j)
+        if (rej[j] == v) return 0ull;
+      return int_weight(z, v, temp, l);
+    };
+    unsigned long long mine = 0ull;
+    for (int v = v0; v < v1; ++v) mine += w_res(v);
+    block_prefix(scan, mine);
+    const unsigned long long r = s_rin, lo = tid ? scan[tid - 1] : 0ull;
+    if (r >= lo && r < scan[tid]) {  // exactly one thread's range holds the pick
+      unsigned long long acc = lo;
+      for (int v = v0; v < v1; ++v) {
+        acc += w_res(v);
+        if (acc > r) {
+          s_pick = v;
+          break;
+        }
       }
     }
   }
@@ -393,11 +448,16 @@ void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const in
                                         emitted, status);
 }
 
+int accept_tree_slices(int V) { return (V + WS_SLICE - 1) / WS_SLICE; }
+
 void accept_tree(int batch, int n_rows, int V, int topk, int depth, const int* tokens, const int* parents,
-                 const float* logits, const double* lse64, float temperature, const float* uniforms, int* path,
-                 int* path_len, int* next_root, int* emitted, int* status, hipStream_t st) {
-  k_accept_tree<<<batch, 1024, 0, st>>>(n_rows, V, topk, depth, tokens, parents, logits, lse64, (double)temperature,
-                                        uniforms, path, path_len, next_root, emitted, status);
+                 const float* logits, const double* lse64, unsigned long long* wsum, float temperature,
+                 const float* uniforms, int* path, int* path_len, int* next_root, int* emitted, int* status,
+                 hipStream_t st) {
+  const int ns = accept_tree_slices(V);
+  k_row_wsum<<<dim3(ns, batch * n_rows), 256, 0, st>>>(V, ns, logits, lse64, (double)temperature, wsum);
+  k_accept_tree<<<batch, 1024, 0, st>>>(n_rows, V, topk, depth, ns, tokens, parents, logits, lse64, wsum,
+                                        (double)temperature, uniforms, path, path_len, next_root, emitted, status);
 }
 
 void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,

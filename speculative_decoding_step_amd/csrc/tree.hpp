@@ -64,10 +64,14 @@ void chain_finalize(int K, const int* roots, const int* seq_lens, int* chain_tok
 // ------------------------------------------------------------ accept/compact
 void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const int* parents, const int* argmax,
                    int* path, int* path_len, int* next_root, int* emitted, int* status, hipStream_t st);
-// Tree rejection sampling (one 1024-thread block per sequence; n_rows, topk <= 64).
+// Tree rejection sampling: slice sums of the integer weights of every row (wsum holds
+// rows * accept_tree_slices(V) values), then one 1024-thread block per sequence walks the
+// tree (n_rows, topk <= 64).
+int accept_tree_slices(int V);
 void accept_tree(int batch, int n_rows, int V, int topk, int depth, const int* tokens, const int* parents,
-                 const float* logits, const double* lse64, float temperature, const float* uniforms, int* path,
-                 int* path_len, int* next_root, int* emitted, int* status, hipStream_t st);
+                 const float* logits, const double* lse64, unsigned long long* wsum, float temperature,
+                 const float* uniforms, int* path, int* path_len, int* next_root, int* emitted, int* status,
+                 hipStream_t st);
 void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,
                   float temperature, const float* q, const float* uniforms, int* path, int* path_len,
                   int* next_root, int* emitted, hipStream_t st);
