@@ -11,6 +11,7 @@
 #include "../../include/eagle3.h"
 #include "common.hpp"
 #include "kernels.hpp"
+#include "sampler.hpp"
 #include "tree.hpp"
 
 using namespace e3;
@@ -67,6 +68,7 @@ struct eagle3_ctx {
   int *tk_pi, *tk_ids;
   double *tk_psum, *tk_lse64;
   unsigned long long* tk_wsum;  // per-row slice sums of integer sampling weights
+  int* acc_sel;                 // chain acceptance: drafts accepted per sequence
   RowMeta rm;
   int *rtok, *gidx, *roots;
   float *a_last, *a_rows;
@@ -114,7 +116,8 @@ size_t carve(eagle3_ctx* c, char* base) {
   c->tk_vals = cv.take<float>((size_t)R * KMAX);
   c->tk_lse = cv.take<float>(R);
   c->tk_lse64 = cv.take<double>(R);
-  c->tk_wsum = cv.take<unsigned long long>((size_t)R * accept_tree_slices(V));
+  c->tk_wsum = cv.take<unsigned long long>((size_t)R * sampler_slices(V));
+  c->acc_sel = cv.take<int>(B);
   c->rm.seq = cv.take<int>(R);
   c->rm.pos = cv.take<int>(R);
   c->rm.slot = cv.take<int>(R);
@@ -523,7 +526,8 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
     const float T = c->cfg.temperature;
     const float* z0 = table ? table : c->logits;
     const int ld0 = table ? (int)tstride : V;
-    chain_draw(0, K, z0, ld0, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok, batch, st);
+    chain_draw(0, K, z0, ld0, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok, batch,
+               c->tk_wsum, st);
     for (int j = 1; j < K; ++j) {
       if (table) {
         const float* zj = table + (size_t)j * V;
@@ -531,7 +535,7 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
           topk_lse(zj + b * tstride, 1, V, V, 1, T, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids + b,
                    c->tk_vals + b, c->tk_lse + b, c->tk_lse64 + b, st);
         chain_draw(j, K, zj, (int)tstride, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok,
-                   batch, st);
+                   batch, c->tk_wsum, st);
       } else {
         chain_rows(j - 1, K, c->chain_tok, seq_lens, c->emax, dr, c->S_cap, st);
         tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, batch, d, st);
@@ -539,7 +543,7 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
         if (j + 1 < K) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, batch, 1, c->emax, d, st);
         draft_lm(c, batch, c->dx, 1, T);
         chain_draw(j, K, c->logits, V, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok,
-                   batch, st);
+                   batch, c->tk_wsum, st);
       }
     }
     chain_finalize(K, c->roots, seq_lens, c->chain_tok, out, batch, st);
@@ -774,7 +778,7 @@ eagle3_status eagle3_accept(eagle3_ctx* c, int32_t batch, int32_t n_rows, const 
     topk_lse(logits, batch * n_rows, V, V, 1, c->cfg.temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum,
              c->tk_ids, c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
     accept_chain(batch, K, V, tokens, logits, c->tk_lse64, c->cfg.temperature, q, uniforms, path, path_len, next_root,
-                 emitted, c->st);
+                 emitted, c->acc_sel, c->tk_wsum, c->st);
   }
   return last_error();
 }
@@ -802,7 +806,7 @@ eagle3_status eagle3_sample(eagle3_ctx* c, int32_t n, const float* logits, float
   const int V = c->sh.vocab;
   topk_lse(logits, n, V, V, 1, temperature > 0.f ? temperature : 1.f, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum,
            c->tk_ids, c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
-  sample_rows(n, logits, V, temperature, c->tk_lse64, c->tk_ids, uniforms, tokens, c->st);
+  sample_rows(n, logits, V, temperature, c->tk_lse64, c->tk_ids, uniforms, tokens, c->tk_wsum, c->st);
   return last_error();
 }
 

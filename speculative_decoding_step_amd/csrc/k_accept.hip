@@ -20,6 +20,7 @@
 // Compaction: the accepted nodes' K/V move to consecutive slots after the
 // committed prefix (the page's note on compacting KV slots).
 #include "common.hpp"
+#include "sampler.hpp"
 #include "tree.hpp"
 
 namespace e3 {
@@ -67,118 +68,141 @@ __global__ __launch_bounds__(64) void k_accept_greedy(int batch, int n_rows, int
   }
 }
 
-// One block of 1024 threads per sequence.  lse64[b*(K+1)+i] = log-sum-exp of
-// row i's logits / T in double; p_i(v) = fl32(exp(z / T - lse)).
-__global__ __launch_bounds__(1024) void k_accept_chain(int K, int V, const int* __restrict__ tokens,
-                                                       const float* __restrict__ logits,
-                                                       const double* __restrict__ lse64, double temp,
-                                                       const float* __restrict__ q, const float* __restrict__ uniforms,
-                                                       int* __restrict__ path, int* __restrict__ path_len,
-                                                       int* __restrict__ next_root, int* __restrict__ emitted) {
-  __shared__ unsigned long long scan[1024];
-  __shared__ int nacc, pick, use_p;
-  const int b = blockIdx.x, tid = threadIdx.x;
+// Chain acceptance in three launches.  lse64[b*(K+1)+i] = log-sum-exp of row
+// i's logits / T in double; p_i(v) = fl32(exp(z / T - lse)).
+// k_chain_decide (one wave per sequence): the K ratio tests front to back,
+// sel[b] = the number accepted.  k_chain_slices, grid (slices, B): at row
+// n = sel[b], the slice sums of floor(p_n * 2^48) and, when n < K, of
+// floor(max(0, p_n - q_n) * 2^48).  k_chain_pick (one 1024-thread block per
+// sequence): the bonus (n = K) draws from p_K; a rejection draws from the
+// residual, or from p_n when the residual is all zero in fp32; the pick comes
+// from the slice sums and one slice's scan.
+__global__ __launch_bounds__(64) void k_chain_decide(int K, int V, const int* __restrict__ tokens,
+                                                     const float* __restrict__ logits,
+                                                     const double* __restrict__ lse64, double temp,
+                                                     const float* __restrict__ q, const float* __restrict__ uniforms,
+                                                     int* __restrict__ sel) {
+  const int b = blockIdx.x;
+  if (threadIdx.x != 0) return;
   const int rows = K + 1;
   const int* tk = tokens + (size_t)b * rows;
   const float* u = uniforms + (size_t)b * rows;
+  int n = K;
+  for (int i = 0; i < K; ++i) {
+    const int t = tk[i + 1];
+    const float p = sample_prob(logits + ((size_t)b * rows + i) * V, t, temp, lse64[(size_t)b * rows + i]);
+    const float qq = q[((size_t)b * K + i) * V + t];
+    const float ratio = p / qq;
+    if (!(u[i] < ratio)) {
+      n = i;
+      break;
+    }
+  }
+  sel[b] = n;
+}
+
+__global__ __launch_bounds__(256) void k_chain_slices(int K, int V, const float* __restrict__ logits,
+                                                      const double* __restrict__ lse64, double temp,
+                                                      const float* __restrict__ q, const int* __restrict__ sel, int ns,
+                                                      unsigned long long* __restrict__ wsum_p,
+                                                      unsigned long long* __restrict__ wsum_r) {
+  __shared__ unsigned long long red[256];
+  const int sl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int rows = K + 1, n = sel[b];
+  const float* z = logits + ((size_t)b * rows + n) * V;
+  const double l = lse64[(size_t)b * rows + n];
+  const float* qr = n < K ? q + ((size_t)b * K + n) * V : nullptr;
+  const int v1 = min(V, (sl + 1) * SAMPLE_SLICE);
+  unsigned long long ap = 0ull, ar = 0ull;
+  for (int v = sl * SAMPLE_SLICE + tid; v < v1; v += 256) {
+    const float p = sample_prob(z, v, temp, l);
+    ap += int_weight_of(p);
+    if (qr) ar += int_weight_of(fmaxf(p - qr[v], 0.f));
+  }
+  const unsigned long long tp = block_sum256(red, ap);
+  const unsigned long long tr = block_sum256(red, ar);
   if (tid == 0) {
-    int n = K;
-    for (int i = 0; i < K; ++i) {
-      const int t = tk[i + 1];
-      const float* z = logits + ((size_t)b * rows + i) * V;
-      const float p = (float)exp((double)z[t] / temp - lse64[(size_t)b * rows + i]);
-      const float qq = q[((size_t)b * K + i) * V + t];
-      const float ratio = p / qq;
-      if (!(u[i] < ratio)) {
-        n = i;
+    wsum_p[(size_t)b * ns + sl] = tp;
+    wsum_r[(size_t)b * ns + sl] = tr;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_chain_pick(int K, int V, const int* __restrict__ tokens,
+                                                     const float* __restrict__ logits,
+                                                     const double* __restrict__ lse64, double temp,
+                                                     const float* __restrict__ q, const float* __restrict__ uniforms,
+                                                     const int* __restrict__ sel, int ns,
+                                                     const unsigned long long* __restrict__ wsum_p,
+                                                     const unsigned long long* __restrict__ wsum_r,
+                                                     int* __restrict__ path, int* __restrict__ path_len,
+                                                     int* __restrict__ next_root, int* __restrict__ emitted) {
+  __shared__ unsigned long long scan[1024];
+  __shared__ unsigned long long s_rin;
+  __shared__ int s_slice, s_usep, pick;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int rows = K + 1, n = sel[b];
+  const int* tk = tokens + (size_t)b * rows;
+  if (tid == 0) {
+    unsigned long long Sp = 0ull, Sr = 0ull;
+    for (int j = 0; j < ns; ++j) {
+      Sp += wsum_p[(size_t)b * ns + j];
+      Sr += wsum_r[(size_t)b * ns + j];
+    }
+    const bool use_p = n == K || Sr == 0ull;  // the bonus, or a residual that is all zero in fp32
+    const unsigned long long* ws = (use_p ? wsum_p : wsum_r) + (size_t)b * ns;
+    const unsigned long long S = use_p ? Sp : Sr;
+    const unsigned long long r = floor_u_times(S, uniform24(uniforms[(size_t)b * rows + K]));
+    int slice = -1;
+    unsigned long long cum = 0ull;
+    for (int j = 0; j < ns && S > 0ull; ++j) {
+      if (r < cum + ws[j]) {
+        slice = j;
         break;
       }
+      cum += ws[j];
     }
-    nacc = n;
-    use_p = n == K;  // bonus: draw from p_K
+    s_slice = slice;
+    s_rin = r - cum;
+    s_usep = use_p;
     pick = -1;
   }
   __syncthreads();
-  const int row = nacc;
-  const float* z = logits + ((size_t)b * rows + row) * V;
-  const float* qr = q + ((size_t)b * K + (row < K ? row : 0)) * V;
-  const double l = lse64[(size_t)b * rows + row];
-  const int per = (V + 1023) / 1024;
-  const int v0 = tid * per, v1 = min(V, v0 + per);
-  const unsigned long long uu = (unsigned long long)(u[K] * 16777216.0f);
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    const bool fromp = use_p;
+  const int slice = s_slice;
+  if (slice >= 0) {
+    const float* z = logits + ((size_t)b * rows + n) * V;
+    const double l = lse64[(size_t)b * rows + n];
+    const float* qr = s_usep ? nullptr : q + ((size_t)b * K + n) * V;
+    auto w = [&](int v) -> unsigned long long {
+      const float p = sample_prob(z, v, temp, l);
+      return int_weight_of(qr ? fmaxf(p - qr[v], 0.f) : p);
+    };
+    constexpr int PER = SAMPLE_SLICE / 1024;
+    const int v0 = slice * SAMPLE_SLICE + tid * PER, v1 = min(V, v0 + PER);
     unsigned long long mine = 0ull;
-    for (int v = v0; v < v1; ++v) {
-      const float p = (float)exp((double)z[v] / temp - l);
-      const float w = fromp ? p : fmaxf(p - qr[v], 0.f);
-      mine += (unsigned long long)ldexpf(w, 48);
-    }
-    scan[tid] = mine;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-      const unsigned long long add = tid >= o ? scan[tid - o] : 0ull;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
-    }
-    const unsigned long long S = scan[1023];
-    if (S == 0ull) {  // residual all zero in fp32: draw from p instead
-      __syncthreads();
-      if (tid == 0) use_p = 1;
-      __syncthreads();
-      continue;
-    }
-    const unsigned long long r = (S >> 24) * uu + (((S & 0xffffffull) * uu) >> 24);
-    const unsigned long long lo = tid ? scan[tid - 1] : 0ull;
-    if (r >= lo && r < scan[tid]) {
+    for (int v = v0; v < v1; ++v) mine += w(v);
+    block_prefix(scan, mine);
+    const unsigned long long r = s_rin, lo = tid ? scan[tid - 1] : 0ull;
+    if (r >= lo && r < scan[tid]) {  // exactly one thread's range holds the pick
       unsigned long long acc = lo;
       for (int v = v0; v < v1; ++v) {
-        const float p = (float)exp((double)z[v] / temp - l);
-        const float w = fromp ? p : fmaxf(p - qr[v], 0.f);
-        acc += (unsigned long long)ldexpf(w, 48);
+        acc += w(v);
         if (acc > r) {
           pick = v;
           break;
         }
       }
     }
-    break;
   }
   __syncthreads();
+  if (tid < rows) {
+    path[(size_t)b * rows + tid] = tid <= n ? tid : -1;
+    if (emitted) emitted[(size_t)b * rows + tid] = tid <= n ? tk[tid] : -1;
+  }
   if (tid == 0) {
-    const int maxp = K + 1;
-    for (int j = 0; j < maxp; ++j) {
-      path[(size_t)b * maxp + j] = j <= nacc ? j : -1;
-      if (emitted) emitted[(size_t)b * maxp + j] = j <= nacc ? tk[j] : -1;
-    }
-    path_len[b] = nacc + 1;
+    path_len[b] = n + 1;
     next_root[b] = pick;
   }
 }
-
-// Block-wide inclusive prefix sum of one value per thread (1024 threads):
-// sc[tid] receives the prefix, the total is returned to every thread.
-__device__ unsigned long long block_prefix(unsigned long long* sc, unsigned long long x) {
-  const int tid = threadIdx.x;
-  __syncthreads();  // earlier readers of sc are done
-  sc[tid] = x;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const unsigned long long add = tid >= o ? sc[tid - o] : 0ull;
-    __syncthreads();
-    sc[tid] += add;
-    __syncthreads();
-  }
-  return sc[1023];
-}
-
-// floor(p(v) * 2^48), p(v) = fl32(exp(z_v / T - lse)) (the samplers' integer weight)
-__device__ __forceinline__ unsigned long long int_weight(const float* z, int v, double temp, double lse) {
-  return (unsigned long long)ldexpf((float)exp((double)z[v] / temp - lse), 48);
-}
-
-constexpr int WS_SLICE = 4096;  // vocabulary entries per weight slice
 
 // grid (slices, rows), 256 threads: wsum[row * ns + s] = sum of the integer
 // weights floor(p(v) * 2^48) over slice s of the row (exact, order-free).
@@ -189,16 +213,11 @@ __global__ __launch_bounds__(256) void k_row_wsum(int V, int ns, const float* __
   const int s = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const float* z = logits + (size_t)row * V;
   const double l = lse64[row];
-  const int v1 = min(V, (s + 1) * WS_SLICE);
+  const int v1 = min(V, (s + 1) * SAMPLE_SLICE);
   unsigned long long acc = 0ull;
-  for (int v = s * WS_SLICE + tid; v < v1; v += 256) acc += int_weight(z, v, temp, l);
-  red[tid] = acc;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  if (tid == 0) wsum[(size_t)row * ns + s] = red[0];
+  for (int v = s * SAMPLE_SLICE + tid; v < v1; v += 256) acc += int_weight(z, v, temp, l);
+  const unsigned long long tot = block_sum256(red, acc);
+  if (tid == 0) wsum[(size_t)row * ns + s] = tot;
 }
 
 // One block of 1024 threads per sequence, n_rows <= 64, topk <= 64, ns <= 64,
@@ -273,8 +292,7 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
         bool dup = false;
         for (int j = 0; j < i; ++j) dup |= rej[j] == x;
         const unsigned long long wx = dup ? 0ull : wkid[i];
-        const unsigned long long uu = (unsigned long long)(u[d * topk + i] * 16777216.0f);
-        const unsigned long long r = (rem >> 24) * uu + (((rem & 0xffffffull) * uu) >> 24);  // floor(u * rem)
+        const unsigned long long r = floor_u_times(rem, uniform24(u[d * topk + i]));
         if (r < wx) {
           acc = kid[i];
           break;
@@ -303,13 +321,12 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
   const double l = lse64[rrow];
   if (tid == 0) {
     const unsigned long long S = s_rem;
-    const unsigned long long uu = (unsigned long long)(u[(size_t)maxd * topk] * 16777216.0f);
-    const unsigned long long r = (S >> 24) * uu + (((S & 0xffffffull) * uu) >> 24);
+    const unsigned long long r = floor_u_times(S, uniform24(u[(size_t)maxd * topk]));
     // remove each distinct rejected token's weight from its slice, then find the slice holding r
     for (int i = 0; i < nrej; ++i) {
       bool dup = false;
       for (int k = 0; k < i; ++k) dup |= rej[k] == rej[i];
-      if (!dup && rej[i] >= 0 && rej[i] < V) wsl[rej[i] / WS_SLICE] -= wkid[i];
+      if (!dup && rej[i] >= 0 && rej[i] < V) wsl[rej[i] / SAMPLE_SLICE] -= wkid[i];
     }
     int slice = -1;
     unsigned long long cum = 0ull;
@@ -326,8 +343,8 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
   __syncthreads();
   const int slice = s_slice;
   if (slice >= 0) {
-    constexpr int PER = WS_SLICE / 1024;
-    const int v0 = slice * WS_SLICE + tid * PER, v1 = min(V, v0 + PER);
+    constexpr int PER = SAMPLE_SLICE / 1024;
+    const int v0 = slice * SAMPLE_SLICE + tid * PER, v1 = min(V, v0 + PER);
     auto w_res = [&](int v) -> unsigned long long {
       for (int j = 0; j < nrej; ++j)
         if (rej[j] == v) return 0ull;
@@ -448,13 +465,11 @@ void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const in
                                         emitted, status);
 }
 
-int accept_tree_slices(int V) { return (V + WS_SLICE - 1) / WS_SLICE; }
-
 void accept_tree(int batch, int n_rows, int V, int topk, int depth, const int* tokens, const int* parents,
                  const float* logits, const double* lse64, unsigned long long* wsum, float temperature,
                  const float* uniforms, int* path, int* path_len, int* next_root, int* emitted, int* status,
                  hipStream_t st) {
-  const int ns = accept_tree_slices(V);
+  const int ns = sampler_slices(V);
   k_row_wsum<<<dim3(ns, batch * n_rows), 256, 0, st>>>(V, ns, logits, lse64, (double)temperature, wsum);
   k_accept_tree<<<batch, 1024, 0, st>>>(n_rows, V, topk, depth, ns, tokens, parents, logits, lse64, wsum,
                                         (double)temperature, uniforms, path, path_len, next_root, emitted, status);
@@ -462,9 +477,14 @@ void accept_tree(int batch, int n_rows, int V, int topk, int depth, const int* t
 
 void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,
                   float temperature, const float* q, const float* uniforms, int* path, int* path_len, int* next_root,
-                  int* emitted, hipStream_t st) {
-  k_accept_chain<<<batch, 1024, 0, st>>>(K, V, tokens, logits, lse64, (double)temperature, q, uniforms, path,
-                                         path_len, next_root, emitted);
+                  int* emitted, int* sel, unsigned long long* wsum, hipStream_t st) {
+  const int ns = sampler_slices(V);
+  const double T = temperature;
+  k_chain_decide<<<batch, 64, 0, st>>>(K, V, tokens, logits, lse64, T, q, uniforms, sel);
+  k_chain_slices<<<dim3(ns, batch), 256, 0, st>>>(K, V, logits, lse64, T, q, sel, ns, wsum,
+                                                  wsum + (size_t)batch * ns);
+  k_chain_pick<<<batch, 1024, 0, st>>>(K, V, tokens, logits, lse64, T, q, uniforms, sel, ns, wsum,
+                                       wsum + (size_t)batch * ns, path, path_len, next_root, emitted);
 }
 
 void compact_kv(bool bf16, int batch, const int* seq_lens, const int* path, const int* path_len, int maxp, int n_rows, void* kv,

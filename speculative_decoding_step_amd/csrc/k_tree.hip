@@ -16,6 +16,7 @@
 // mask (bits of the expansion rows on its ancestor chain and itself) is
 // emask[b][e].
 #include "common.hpp"
+#include "sampler.hpp"
 #include "tree.hpp"
 
 namespace e3 {
@@ -226,57 +227,90 @@ __global__ __launch_bounds__(512) void k_tree_finalize(TreeState ts, int n_cand,
 }
 
 // ---------------------------------------------------------------- sampled chain
-// Per row b: draw from q = softmax(z / T) (z = logits row b) by the integer
-// inverse CDF over W_v = floor(q_v * 2^48), r = floor(u * sum W); or take the
-// argmax (top1) for greedy drafts.  q_out (optional) receives q (one-hot for
-// greedy drafts).  out_tok[b * tok_stride + tok_off] receives the token.
-__global__ __launch_bounds__(1024) void k_draw(const float* __restrict__ logits, int ld, int V, double temp,
-                                               const double* __restrict__ lse64, const int* __restrict__ top1,
-                                               const float* __restrict__ uniforms, int u_stride, int greedy,
-                                               float* __restrict__ q_out, size_t q_stride, int* __restrict__ out_tok,
-                                               int tok_stride) {
-  __shared__ unsigned long long scan[1024];
-  __shared__ int pick;
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const float* z = logits + (size_t)b * ld;
+// Draws one token per row from q = softmax(logits / T), in two launches.
+// k_draw_slices, grid (slices, rows): q(v) = fl32(exp(z_v / T - lse)) (stored
+// when q_out is given) and the slice's sum of integer weights floor(q * 2^48);
+// greedy rows (draft_greedy, or temperature 0) store the one-hot q of top1.
+// k_draw_pick, one 1024-thread block per row: r = floor(u * S) from the slice
+// sums, the slice holding r, and the first entry of that slice whose prefix
+// exceeds r (greedy rows: top1).
+__global__ __launch_bounds__(256) void k_draw_slices(const float* __restrict__ logits, int ld, int V, double temp,
+                                                     const double* __restrict__ lse64, const int* __restrict__ top1,
+                                                     int greedy, float* __restrict__ q_out, size_t q_stride, int ns,
+                                                     unsigned long long* __restrict__ wsum) {
+  __shared__ unsigned long long red[256];
+  const int sl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int v0 = sl * SAMPLE_SLICE, v1 = min(V, v0 + SAMPLE_SLICE);
   float* q = q_out ? q_out + (size_t)b * q_stride : nullptr;
   if (greedy) {
-    const int t = top1[b];
-    if (q)
-      for (int v = tid; v < V; v += blockDim.x) q[v] = v == t ? 1.f : 0.f;
-    if (tid == 0) out_tok[(size_t)b * tok_stride] = t;
+    if (q) {
+      const int t = top1[b];
+      for (int v = v0 + tid; v < v1; v += 256) q[v] = v == t ? 1.f : 0.f;
+    }
     return;
   }
+  const float* z = logits + (size_t)b * ld;
   const double l = lse64[b];
-  const int per = (V + blockDim.x - 1) / blockDim.x;
-  const int v0 = tid * per, v1 = min(V, v0 + per);
-  unsigned long long mine = 0ull;
-  for (int v = v0; v < v1; ++v) {
-    const float qv = (float)exp((double)z[v] / temp - l);
+  unsigned long long acc = 0ull;
+  for (int v = v0 + tid; v < v1; v += 256) {
+    const float qv = sample_prob(z, v, temp, l);
     if (q) q[v] = qv;
-    mine += (unsigned long long)ldexpf(qv, 48);
+    acc += int_weight_of(qv);
   }
-  scan[tid] = mine;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan of the per-thread totals
-    const unsigned long long add = tid >= o ? scan[tid - o] : 0ull;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
+  const unsigned long long tot = block_sum256(red, acc);
+  if (tid == 0) wsum[(size_t)b * ns + sl] = tot;
+}
+
+__global__ __launch_bounds__(1024) void k_draw_pick(const float* __restrict__ logits, int ld, int V, double temp,
+                                                    const double* __restrict__ lse64, const int* __restrict__ top1,
+                                                    const float* __restrict__ uniforms, int u_stride, int greedy,
+                                                    int ns, const unsigned long long* __restrict__ wsum,
+                                                    int* __restrict__ out_tok, int tok_stride) {
+  __shared__ unsigned long long scan[1024];
+  __shared__ unsigned long long s_rin;
+  __shared__ int s_slice, pick;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (greedy) {
+    if (tid == 0) out_tok[(size_t)b * tok_stride] = top1[b];
+    return;
   }
-  const unsigned long long S = scan[1023];
-  const unsigned long long u = (unsigned long long)(uniforms[(size_t)b * u_stride] * 16777216.0f);
-  const unsigned long long r = (S >> 24) * u + (((S & 0xffffffull) * u) >> 24);
-  if (tid == 0) pick = -1;
-  __syncthreads();
-  const unsigned long long lo = tid ? scan[tid - 1] : 0ull;
-  if (S > 0 && r >= lo && r < scan[tid]) {
-    unsigned long long acc = lo;
-    for (int v = v0; v < v1; ++v) {
-      acc += (unsigned long long)ldexpf((float)exp((double)z[v] / temp - l), 48);
-      if (acc > r) {
-        pick = v;
+  if (tid == 0) {
+    unsigned long long S = 0ull;
+    for (int j = 0; j < ns; ++j) S += wsum[(size_t)b * ns + j];
+    const unsigned long long r = floor_u_times(S, uniform24(uniforms[(size_t)b * u_stride]));
+    int slice = -1;
+    unsigned long long cum = 0ull;
+    for (int j = 0; j < ns && S > 0ull; ++j) {
+      const unsigned long long sj = wsum[(size_t)b * ns + j];
+      if (r < cum + sj) {
+        slice = j;
         break;
+      }
+      cum += sj;
+    }
+    s_slice = slice;
+    s_rin = r - cum;
+    pick = -1;
+  }
+  __syncthreads();
+  const int slice = s_slice;
+  if (slice >= 0) {
+    const float* z = logits + (size_t)b * ld;
+    const double l = lse64[b];
+    constexpr int PER = SAMPLE_SLICE / 1024;
+    const int v0 = slice * SAMPLE_SLICE + tid * PER, v1 = min(V, v0 + PER);
+    unsigned long long mine = 0ull;
+    for (int v = v0; v < v1; ++v) mine += int_weight(z, v, temp, l);
+    block_prefix(scan, mine);
+    const unsigned long long r = s_rin, lo = tid ? scan[tid - 1] : 0ull;
+    if (r >= lo && r < scan[tid]) {  // exactly one thread's range holds the pick
+      unsigned long long acc = lo;
+      for (int v = v0; v < v1; ++v) {
+        acc += int_weight(z, v, temp, l);
+        if (acc > r) {
+          pick = v;
+          break;
+        }
       }
     }
   }
@@ -338,14 +372,21 @@ void tree_finalize(const TreeState& ts, int n_cand, int n_nodes, const int* root
 }
 void chain_draw(int j, int K, const float* logits, int ld, int V, float temperature, const double* lse64,
                 const int* top1, const float* uniforms, int draft_greedy, float* q_out, int* chain_tok, int batch,
-                hipStream_t st) {
-  k_draw<<<batch, 1024, 0, st>>>(logits, ld, V, (double)temperature, lse64, top1, uniforms ? uniforms + j : nullptr, K,
-                                 draft_greedy, q_out + (size_t)j * V, (size_t)K * V, chain_tok + 1 + j, K + 1);
+                unsigned long long* wsum, hipStream_t st) {
+  const int ns = sampler_slices(V);
+  k_draw_slices<<<dim3(ns, batch), 256, 0, st>>>(logits, ld, V, (double)temperature, lse64, top1, draft_greedy,
+                                                 q_out + (size_t)j * V, (size_t)K * V, ns, wsum);
+  k_draw_pick<<<batch, 1024, 0, st>>>(logits, ld, V, (double)temperature, lse64, top1, uniforms ? uniforms + j : nullptr,
+                                      K, draft_greedy, ns, wsum, chain_tok + 1 + j, K + 1);
 }
 void sample_rows(int n, const float* logits, int V, float temperature, const double* lse64, const int* top1,
-                 const float* uniforms, int* tokens, hipStream_t st) {
-  k_draw<<<n, 1024, 0, st>>>(logits, V, V, (double)temperature, lse64, top1, uniforms, 1, temperature == 0.f, nullptr,
-                             0, tokens, 1);
+                 const float* uniforms, int* tokens, unsigned long long* wsum, hipStream_t st) {
+  const int ns = sampler_slices(V), greedy = temperature == 0.f;
+  if (!greedy)
+    k_draw_slices<<<dim3(ns, n), 256, 0, st>>>(logits, V, V, (double)temperature, lse64, top1, 0, nullptr, 0, ns,
+                                               wsum);
+  k_draw_pick<<<n, 1024, 0, st>>>(logits, V, V, (double)temperature, lse64, top1, uniforms, 1, greedy, ns, wsum, tokens,
+                                  1);
 }
 void chain_rows(int j, int K, const int* chain_tok, const int* seq_lens, int emax, const DraftRows& dr, int S_cap,
                 hipStream_t st) {

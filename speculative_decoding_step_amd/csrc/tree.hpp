@@ -53,9 +53,9 @@ void tree_finalize(const TreeState& ts, int n_cand, int n_nodes, const int* root
                    const TreeOut& out, int* status, hipStream_t st);
 void chain_draw(int j, int K, const float* logits, int ld, int V, float temperature, const double* lse64,
                 const int* top1, const float* uniforms, int draft_greedy, float* q_out, int* chain_tok, int batch,
-                hipStream_t st);
+                unsigned long long* wsum, hipStream_t st);
 void sample_rows(int n, const float* logits, int V, float temperature, const double* lse64, const int* top1,
-                 const float* uniforms, int* tokens, hipStream_t st);
+                 const float* uniforms, int* tokens, unsigned long long* wsum, hipStream_t st);
 void chain_rows(int j, int K, const int* chain_tok, const int* seq_lens, int emax, const DraftRows& dr, int S_cap,
                 hipStream_t st);
 void chain_finalize(int K, const int* roots, const int* seq_lens, int* chain_tok, const TreeOut& out, int batch,
@@ -65,16 +65,16 @@ void chain_finalize(int K, const int* roots, const int* seq_lens, int* chain_tok
 void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const int* parents, const int* argmax,
                    int* path, int* path_len, int* next_root, int* emitted, int* status, hipStream_t st);
 // Tree rejection sampling: slice sums of the integer weights of every row (wsum holds
-// rows * accept_tree_slices(V) values), then one 1024-thread block per sequence walks the
+// rows * sampler_slices(V) values), then one 1024-thread block per sequence walks the
 // tree (n_rows, topk <= 64).
-int accept_tree_slices(int V);
 void accept_tree(int batch, int n_rows, int V, int topk, int depth, const int* tokens, const int* parents,
                  const float* logits, const double* lse64, unsigned long long* wsum, float temperature,
                  const float* uniforms, int* path, int* path_len, int* next_root, int* emitted, int* status,
                  hipStream_t st);
+// Chain acceptance: sel [batch] ints and wsum [2 * batch * sampler_slices(V)] are scratch.
 void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,
-                  float temperature, const float* q, const float* uniforms, int* path, int* path_len,
-                  int* next_root, int* emitted, hipStream_t st);
+                  float temperature, const float* q, const float* uniforms, int* path, int* path_len, int* next_root,
+                  int* emitted, int* sel, unsigned long long* wsum, hipStream_t st);
 void compact_kv(bool bf16, int batch, const int* seq_lens, const int* path, const int* path_len, int maxp,
                 int n_rows, void* kv, int n_layers, int max_batch, int Hkv, int S_cap, int hd, int* status, hipStream_t st);
 void compact_finish(bool bf16, int batch, int* seq_lens, int n_rows, int maxp, const int* path, const int* path_len,
