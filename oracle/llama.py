@@ -182,6 +182,10 @@ def draft_layer(H: dict, W: dict, shp: Shape, e_tokens, x: np.ndarray, positions
 
 
 def draft_logits(H: dict, W: dict, shp: Shape, a: np.ndarray) -> np.ndarray:
-    """logits = lm_head(norm(a)) with the draft's own final norm and the shared LM head."""
+    """logits = lm_head(norm(a)) with the draft's own final norm.  The head is the
+    target's (shared, full vocabulary), or the draft's own head over a reduced draft
+    vocabulary when H holds "lm_head" ("EAGLE-3: Engineering Implementation of LLM
+    Inference Acceleration", VIII.5-VIII.6: logits over V_d, d2t back to target ids)."""
     rnd = rounder(shp.dtype)
-    return rnd(rms_norm(a, H["final_norm"], shp.eps)) @ W["lm_head"].T
+    head = H["lm_head"] if "lm_head" in H else W["lm_head"]
+    return rnd(rms_norm(a, H["final_norm"], shp.eps)) @ head.T

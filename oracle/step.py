@@ -51,22 +51,32 @@ def f32(x):
 
 
 def build_sampled_chain(root: int, root_logits32, expand, K: int, temperature: float,
-                        u_draft, draft_greedy: bool):
+                        u_draft, draft_greedy: bool, d2t=None, vocab: int = None):
     """Chain draft by sampling: d_j ~ q_j, q_j = softmax(logits_j / T) (fp32).
 
     expand(d, [(token, parent_row)]) follows the same contract as in
     build_dynamic_tree.  Returns (tokens [K+1] root first, q [K, V] float32).
+    With a reduced draft vocabulary (d2t, ascending target ids) the draw is over
+    the draft ids, the token is d2t[id], and q is scattered into the target
+    vocabulary of size `vocab` so that p and q share a support ("EAGLE-3:
+    Engineering Implementation of LLM Inference Acceleration", VIII.6, X.2).
     """
     toks, qs = [root], []
     logits = f32(root_logits32)
     for j in range(K):
         if draft_greedy:
             t = argmax_first(logits)
-            q = np.zeros(logits.shape, dtype=np.float32)
-            q[t] = 1.0
+            qd = np.zeros(logits.shape, dtype=np.float32)
+            qd[t] = 1.0
         else:
-            q = probs_f32(logits, temperature)
-            t = sample_inverse_cdf(q, u_draft[j])
+            qd = probs_f32(logits, temperature)
+            t = sample_inverse_cdf(qd, u_draft[j])
+        if d2t is None:
+            q = qd
+        else:
+            t = int(d2t[t])
+            q = np.zeros(vocab, dtype=np.float32)
+            q[np.asarray(d2t)] = qd
         toks.append(int(t))
         qs.append(q)
         if j + 1 < K:
@@ -174,9 +184,10 @@ class OracleSequence:
         expand = self._expander(a_last)
         s = self.spec
         if s.mode in ("greedy_tree", "sample_tree"):
-            return build_dynamic_tree(self.root, root_logits, expand, s.depth, s.topk, s.n_nodes), None
+            return build_dynamic_tree(self.root, root_logits, expand, s.depth, s.topk, s.n_nodes,
+                                      self.H.get("d2t")), None
         toks, q = build_sampled_chain(self.root, root_logits, expand, s.depth, s.temperature,
-                                      u_draft, s.draft_greedy)
+                                      u_draft, s.draft_greedy, self.H.get("d2t"), self.shp.vocab)
         K = s.depth
         tree = Tree(toks, [-1] + list(range(K)), list(range(K + 1)), [np.float32(0)] * (K + 1),
                     [-2] + list(range(K - 1)) + [-1])

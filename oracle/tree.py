@@ -85,7 +85,8 @@ class Tree:
                        # the catch-up row, reported as -2)
 
 
-def build_dynamic_tree(root: int, root_logits32, expand, depth: int, topk: int, n_nodes: int) -> Tree:
+def build_dynamic_tree(root: int, root_logits32, expand, depth: int, topk: int, n_nodes: int,
+                       d2t=None) -> Tree:
     """Dynamic draft tree ranked by cumulative draft log-probability.  Parity unpinned
     as a policy (the pages name EAGLE-2's confidence-driven expansion and final
     pruning but do not spell it out); the reading implemented here:
@@ -108,6 +109,11 @@ def build_dynamic_tree(root: int, root_logits32, expand, depth: int, topk: int, 
     the node's parent (-1 when the parent is the root); the frontier nodes
     themselves become expansion rows numbered consecutively from 0 in call
     order.  It returns the float32 draft logits of each frontier row.
+
+    d2t: with a reduced draft vocabulary the rows are over the draft ids and a
+    child's token is d2t[draft id] (ascending target ids), ranked and scored in
+    draft space ("EAGLE-3: Engineering Implementation of LLM Inference
+    Acceleration", VIII.6); None is the identity.
     """
     cand_tok, cand_par, cand_dep, cand_score = [], [], [], []   # indexed by creation index
     row_of = {}                                                  # creation index -> expansion row
@@ -115,7 +121,7 @@ def build_dynamic_tree(root: int, root_logits32, expand, depth: int, topk: int, 
     def add_children(parent_cid, parent_score, logits32):
         lp = draft_logprobs_f32(logits32)
         for t in topk_desc(np.asarray(logits32, dtype=np.float32), topk):
-            cand_tok.append(int(t))
+            cand_tok.append(int(t) if d2t is None else int(d2t[t]))
             cand_par.append(parent_cid)
             cand_dep.append(1 if parent_cid < 0 else cand_dep[parent_cid] + 1)
             cand_score.append(np.float32(np.float32(parent_score) + lp[t]))
@@ -147,11 +153,12 @@ def build_dynamic_tree(root: int, root_logits32, expand, depth: int, topk: int, 
     return Tree(tokens, parents, dep, score, exp_as)
 
 
-def tree_from_table(root: int, table32, depth: int, topk: int, n_nodes: int) -> Tree:
+def tree_from_table(root: int, table32, depth: int, topk: int, n_nodes: int, d2t=None) -> Tree:
     """build_dynamic_tree with draft logits taken from a table instead of a draft model.
 
     table32[0] is the root's draft row; table32[1 + r] is expansion row r's
-    (expansion rows are numbered in creation order across depths).
+    (expansion rows are numbered in creation order across depths).  With a reduced
+    draft vocabulary the rows are over draft ids and d2t maps them to tokens.
     """
     table32 = np.asarray(table32, dtype=np.float32)
     count = [0]
@@ -161,4 +168,4 @@ def tree_from_table(root: int, table32, depth: int, topk: int, n_nodes: int) -> 
         count[0] += len(info)
         return rows
 
-    return build_dynamic_tree(root, table32[0], expand, depth, topk, n_nodes)
+    return build_dynamic_tree(root, table32[0], expand, depth, topk, n_nodes, d2t)

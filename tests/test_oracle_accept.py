@@ -285,3 +285,50 @@ def test_tree_rejection_special_cases():
     rows.append(p)
     u = _u_grid(rng, 3 * 1 + 1)
     assert tree_rejection(toks, pars, np.stack(rows), u, 1, 3) == ([0, 1, 2, 3], sample_inverse_cdf(p, u[3]))
+
+
+# ------------------------------------------------ reduced draft vocabulary
+
+def test_reduced_vocab_chain_draw_is_the_scattered_draw():
+    """Drawing over the draft ids and mapping through the ascending d2t picks the same
+    token as drawing over q scattered into the target vocabulary (the nonzero entries
+    keep their order, so the integer prefix sums agree); the scattered q sums to 1 on
+    d2t and is 0 elsewhere."""
+    from oracle.numerics import probs_f32
+    from oracle.step import build_sampled_chain
+    rng = np.random.default_rng(21)
+    V, Vd, K = 300, 71, 3
+    d2t = np.sort(rng.choice(V, Vd, replace=False))
+    rows = rng.normal(0, 1.5, size=(K, Vd)).astype(np.float32)
+    for s in range(60):
+        u = (rng.integers(0, 1 << 24, K) * 2.0 ** -24).astype(np.float32)
+        toks, q = build_sampled_chain(5, rows[0], lambda d, info: [rows[d]], K, 1.0, u, False, d2t, V)
+        for j in range(K):
+            assert q[j][np.setdiff1d(np.arange(V), d2t)].sum() == 0
+            assert abs(float(q[j][d2t].astype(np.float64).sum()) - 1) < 1e-5
+            assert toks[1 + j] == sample_inverse_cdf(q[j], u[j])
+            assert toks[1 + j] == int(d2t[sample_inverse_cdf(probs_f32(rows[j], 1.0), u[j])])
+
+
+def test_reduced_vocab_rejection_keeps_the_target_distribution_v64():
+    """A draft that can only propose 40 of 64 tokens: the first emitted token still
+    follows the target p (tokens outside the draft vocabulary come from the residual
+    or bonus draw)."""
+    rng = np.random.default_rng(61)
+    V, Vd, K = 64, 40, 1
+    d2t = np.sort(rng.choice(V, Vd, replace=False))
+    p = np.stack([_rand_dist(rng, V) for _ in range(K + 1)])
+    qd = _rand_dist(rng, Vd)
+    q = np.zeros((K, V), np.float32)
+    q[0, d2t] = qd
+    n = 100_000
+    first = np.empty(n, dtype=np.int64)
+    for s in range(n):
+        u = (rng.integers(0, 1 << 24, K + 2) * 2.0 ** -24).astype(np.float32)
+        d = int(d2t[sample_inverse_cdf(qd, u[K + 1])])
+        n_acc, nxt = chain_rejection([d], q, p, u[:K + 1])
+        first[s] = d if n_acc >= 1 else nxt
+    outside = np.setdiff1d(np.arange(V), d2t)
+    counts = np.bincount(first, minlength=V).astype(float)
+    assert counts[outside].sum() > 0
+    assert _chi2_pvalue(counts, p[0].astype(np.float64)) > 1e-3

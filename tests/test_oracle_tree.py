@@ -162,3 +162,39 @@ def test_depth1_tree_is_topk():
     t = tree_from_table(0, row, 1, 7, 7)
     assert t.tokens[1:] == list(np.argsort(-row[0])[:7])
     assert t.parents == [-1] + [0] * 7
+
+
+# ------------------------------------------------ reduced draft vocabulary
+# ("EAGLE-3: Engineering Implementation of LLM Inference Acceleration", VIII.6: a
+# draft-owned head over V_d ids, d2t back to target ids, ascending)
+
+def _subset(rng, V, Vd):
+    return np.sort(rng.choice(V, Vd, replace=False))
+
+
+def test_reduced_vocab_tree_equals_masked_full_vocab_tree():
+    """A tree drafted over V_d draft ids and mapped through d2t is the tree the full
+    vocabulary would give if every non-draft token's logit were -inf: the same
+    tokens, parents and scores (softmax over the draft ids only)."""
+    rng = np.random.default_rng(12)
+    V, Vd, D, k, N = 200, 57, 4, 3, 12
+    d2t = _subset(rng, V, Vd)
+    n_exp = (D - 1) * k
+    small = rng.normal(0, 2, size=(1 + n_exp, Vd)).astype(np.float32)
+    full = np.full((1 + n_exp, V), -np.inf, dtype=np.float32)
+    full[:, d2t] = small
+    t_red = tree_from_table(7, small, D, k, N, d2t)
+    t_full = tree_from_table(7, full, D, k, N)
+    assert t_red.tokens == t_full.tokens
+    assert t_red.parents == t_full.parents
+    assert [float(x) for x in t_red.score] == [float(x) for x in t_full.score]
+    assert all(t in set(d2t.tolist()) for t in t_red.tokens[1:])
+
+
+def test_reduced_vocab_identity_map_is_the_full_tree():
+    rng = np.random.default_rng(13)
+    V, D, k, N = 90, 3, 3, 8
+    table = rng.normal(0, 2, size=(1 + (D - 1) * k, V)).astype(np.float32)
+    a = tree_from_table(3, table, D, k, N, np.arange(V))
+    b = tree_from_table(3, table, D, k, N)
+    assert (a.tokens, a.parents) == (b.tokens, b.parents)
