@@ -79,6 +79,14 @@ typedef struct {
   int32_t taps[3];    /* residual stream entering 0-indexed layer taps[i], i.e.
                          HF hidden_states[taps[i]] ("EAGLE-3: Engineering ...",
                          IX.1-IX.3); concatenated as [l ; m ; h]                 */
+  int32_t draft_vocab; /* 0: the draft head shares the target's full-vocabulary
+                          LM head; else V_d in [topk, vocab]: the draft owns a head
+                          over V_d ids mapped to target ids by d2t ("EAGLE-3:
+                          Engineering ...", VIII.6).  Draft top-k, scores and
+                          draws are over the draft ids; trees hold target ids;
+                          sampled chains return q scattered into the target
+                          vocabulary (zero off d2t), so p and q share a support
+                          (X.2).                                                   */
 } eagle3_shape;
 
 /* Draft policy.  GREEDY_TREE: dynamic tree of `depth` levels, top-`topk` per
@@ -121,7 +129,10 @@ typedef struct {
   const void *post_norm;           /* [d]                                   */
   const void *w_gate, *w_up;       /* [ffn, d]                              */
   const void *w_down;              /* [d, ffn]                              */
-  const void *final_norm;          /* [d]      norm before the shared head  */
+  const void *final_norm;          /* [d]      norm before the head         */
+  const void *lm_head;             /* [draft_vocab, d] the draft-owned head (draft_vocab > 0; NULL otherwise) */
+  const int32_t *d2t;              /* [draft_vocab] strictly ascending target ids in [0, vocab) (draft_vocab > 0;
+                                      NULL otherwise); checked at create: a violation raises BAD_TOKEN */
 } eagle3_head_weights;
 
 typedef struct eagle3_ctx eagle3_ctx;
@@ -221,8 +232,9 @@ eagle3_status eagle3_draft_tree(eagle3_ctx *ctx, int32_t batch, const int32_t *s
                                 uint64_t *mask, float *score, float *q);
 
 /* Tree construction alone, from given draft logits (no draft model): the same
- * kernels as eagle3_draft_tree with logits_table [B, 1 + (depth-1)*topk, V]
- * float, where row 0 is the root's draft row and row 1 + r is expansion row r
+ * kernels as eagle3_draft_tree with logits_table [B, 1 + (depth-1)*topk, V_d]
+ * float (V_d = draft_vocab, or vocab when the head is shared), where row 0 is
+ * the root's draft row and row 1 + r is expansion row r
  * (expansion rows are numbered in creation order across depths).  roots [B].
  * Outputs as eagle3_draft_tree. */
 eagle3_status eagle3_tree_from_logits(eagle3_ctx *ctx, int32_t batch, const int32_t *roots,

@@ -34,7 +34,8 @@ class Eagle3Error(RuntimeError):
 class Shape(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32), ("vocab", C.c_int32),
-                ("rope_theta", C.c_float), ("rms_eps", C.c_float), ("dtype", C.c_int32), ("taps", C.c_int32 * 3)]
+                ("rope_theta", C.c_float), ("rms_eps", C.c_float), ("dtype", C.c_int32), ("taps", C.c_int32 * 3),
+                ("draft_vocab", C.c_int32)]
 
 
 class SpecCfg(C.Structure):
@@ -55,7 +56,7 @@ class TargetWeights(C.Structure):
 class HeadWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in
                 ("fc", "input_norm", "hidden_norm", "wq", "wk", "wv", "wo", "post_norm", "w_gate", "w_up",
-                 "w_down", "final_norm")]
+                 "w_down", "final_norm", "lm_head", "d2t")]
 
 
 _lib = None

@@ -31,6 +31,7 @@ class ModelShape:
     taps: tuple
     dtype: str = "bf16"
     eps: float = 1e-5
+    draft_vocab: int = 0    # 0: the draft shares the target's full-vocabulary head; else its own head over V_d ids
 
 
 @dataclass(frozen=True)
@@ -70,6 +71,7 @@ class Workload:
 TINY = ModelShape(4, 256, 4, 4, 64, 688, 1024, 1e4, (1, 2, 3), dtype="f32")
 SMALL = ModelShape(8, 1024, 16, 16, 64, 2816, 32000, 1e4, (1, 4, 7))
 L8B = ModelShape(32, 4096, 32, 8, 128, 14336, 128256, 5e5, (2, 16, 29))
+L8B_DV32K = replace(L8B, draft_vocab=32000)  # the official recipe's reduced draft vocabulary
 
 WORKLOADS = {
     "tiny_f32_chain": Workload(1, "tiny_f32_chain", TINY, "greedy_tree", 4, 1, 4, 1, 32, 64),
@@ -82,6 +84,8 @@ WORKLOADS = {
     # the batch-1 tree under sampling: the same draft tree, accepted by level-by-level rejection sampling at T = 1
     "llama8b_sample_tree_b1": Workload(6, "llama8b_sample_tree_b1", L8B, "sample_tree", 6, 10, 60, 1, 2048, 128,
                                        temperature=1.0),
+    # the batch-1 tree with a 32,000-id draft vocabulary (draft-owned head, d2t)
+    "llama8b_tree_b1_dv32k": Workload(7, "llama8b_tree_b1_dv32k", L8B_DV32K, "greedy_tree", 6, 10, 60, 1, 2048, 128),
 }
 
 
@@ -136,7 +140,14 @@ def head_tensor_specs(s: ModelShape):
         ("h.w_up", (s.ffn, d), "mat"),
         ("h.w_down", (d, s.ffn), "mat"),
         ("h.final_norm", (d,), "norm"),
-    ]
+    ] + ([("h.lm_head", (s.draft_vocab, d), "mat")] if s.draft_vocab > 0 else [])
+
+
+def d2t_np(s: ModelShape, head_seed: int) -> np.ndarray:
+    """The reduced draft vocabulary's map to target ids (ascending): a seeded subset of
+    V_d ids.  The pages pick the most frequent tokens of the training responses; with
+    synthetic weights any fixed subset has the same shapes."""
+    return synth.subset_np(head_seed, "h.d2t", s.draft_vocab, s.vocab)
 
 
 def tensor_np(seed: int, name: str, shape, kind: str, dtype: str, sigma: float = 0.02) -> np.ndarray:
@@ -167,4 +178,6 @@ def weights_np(s: ModelShape, target_seed: int, head_seed: int, layers=None, sig
     H = {}
     for name, shp, kind in head_tensor_specs(s):
         H[name[2:]] = tensor_np(head_seed, name, shp, kind, s.dtype, sigma).astype(np.float64)
+    if s.draft_vocab > 0:
+        H["d2t"] = d2t_np(s, head_seed)
     return W, H

@@ -49,6 +49,9 @@ struct eagle3_ctx {
   eagle3_target_weights tw;
   std::vector<eagle3_layer_weights> layers;
   eagle3_head_weights hw;
+  int Vd;                  // draft vocabulary (the target's when the head is shared)
+  const void* dhead;       // the draft's LM head: its own [Vd, d], or the target's
+  const int* d2t;          // draft id -> target id (NULL when the head is shared)
   int B, R, S_cap;
   bool bf16;
   size_t esz;
@@ -171,7 +174,9 @@ eagle3_status check_shape(const eagle3_shape* s, const eagle3_spec_cfg* c) {
     if (s->d_model % 256 || qdim % 256 || s->ffn % 256) return EAGLE3_EUNSUPPORTED;
   }
   if (s->vocab > 64 * 4096) return EAGLE3_EUNSUPPORTED;
-  if (c->depth < 1 || c->topk < 1 || c->topk > KMAX || c->n_nodes < 1 || c->topk > s->vocab) return EAGLE3_EINVAL;
+  if (s->draft_vocab < 0 || s->draft_vocab > s->vocab) return EAGLE3_EINVAL;
+  const int Vd = s->draft_vocab > 0 ? s->draft_vocab : s->vocab;
+  if (c->depth < 1 || c->topk < 1 || c->topk > KMAX || c->n_nodes < 1 || c->topk > Vd) return EAGLE3_EINVAL;
   if (c->n_nodes + 1 > 64 || (c->depth - 1) * c->topk > 64) return EAGLE3_EUNSUPPORTED;
   if (c->mode == EAGLE3_GREEDY_TREE || c->mode == EAGLE3_SAMPLE_TREE) {
     const int nc = c->topk + (c->depth - 1) * c->topk * c->topk;
@@ -471,9 +476,10 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
 void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature) {
   const eagle3_shape& s = c->sh;
   rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st);
-  run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->tw.lm_head, s.vocab), c->logits);
-  topk_lse(c->logits, n, s.vocab, s.vocab, K, temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids,
+  run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->dhead, c->Vd), c->logits);
+  topk_lse(c->logits, n, c->Vd, c->Vd, K, temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids,
            c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
+  map_draft_ids(c->tk_ids, n * K, c->d2t, c->Vd, c->st);
 }
 
 RowMeta dr_meta(eagle3_ctx* c) {
@@ -493,13 +499,13 @@ RowMeta dr_meta(eagle3_ctx* c) {
 eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const float* table, const float* uniforms,
                          const TreeOut& out, float* q) {
   const eagle3_shape& s = c->sh;
-  const int D = c->cfg.depth, k = c->cfg.topk, V = s.vocab, d = s.d_model;
+  const int D = c->cfg.depth, k = c->cfg.topk, V = s.vocab, Vd = c->Vd, d = s.d_model;
   hipStream_t st = c->st;
   TreeState ts = c->ts;
   ts.batch = batch;
   DraftRows dr = c->dr;
   dr.batch = batch;
-  const size_t tstride = (size_t)(1 + c->emax) * V;  // table row stride between sequences
+  const size_t tstride = (size_t)(1 + c->emax) * Vd;  // table row stride between sequences
   if (c->cfg.mode != EAGLE3_SAMPLE_CHAIN) {  // trees (greedy or sampled acceptance alike)
     tree_children(ts, 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
     for (int dd = 1; dd < D; ++dd) {
@@ -508,10 +514,12 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
       if (table) {
         // expansion rows (dd-1)k .. dd k - 1 of each sequence
         for (int b = 0; b < batch; ++b)
-          topk_lse(table + b * tstride + (size_t)(1 + (dd - 1) * k) * V, k, V, V, k, 1.f, c->tk_pv + (size_t)b * k * topk_slices(V) * KMAX,
-                   c->tk_pi + (size_t)b * k * topk_slices(V) * KMAX, c->tk_pmax + (size_t)b * k * topk_slices(V),
-                   c->tk_psum + (size_t)b * k * topk_slices(V), c->tk_ids + (size_t)b * k * k, c->tk_vals + (size_t)b * k * k,
-                   c->tk_lse + b * k, c->tk_lse64 + b * k, st);
+          topk_lse(table + b * tstride + (size_t)(1 + (dd - 1) * k) * Vd, k, Vd, Vd, k, 1.f,
+                   c->tk_pv + (size_t)b * k * topk_slices(Vd) * KMAX, c->tk_pi + (size_t)b * k * topk_slices(Vd) * KMAX,
+                   c->tk_pmax + (size_t)b * k * topk_slices(Vd), c->tk_psum + (size_t)b * k * topk_slices(Vd),
+                   c->tk_ids + (size_t)b * k * k, c->tk_vals + (size_t)b * k * k, c->tk_lse + b * k,
+                   c->tk_lse64 + b * k, st);
+        map_draft_ids(c->tk_ids, batch * k * k, c->d2t, c->Vd, st);
       } else {
         tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, n, d, st);
         draft_layer(c, n, k, dr.tok, c->dx, dr_meta(c));
@@ -525,25 +533,26 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
     const int K = D;
     const float T = c->cfg.temperature;
     const float* z0 = table ? table : c->logits;
-    const int ld0 = table ? (int)tstride : V;
-    chain_draw(0, K, z0, ld0, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok, batch,
-               c->tk_wsum, st);
+    const int ld0 = table ? (int)tstride : Vd;
+    chain_draw(0, K, z0, ld0, Vd, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok,
+               batch, c->tk_wsum, c->d2t, st);
     for (int j = 1; j < K; ++j) {
       if (table) {
-        const float* zj = table + (size_t)j * V;
+        const float* zj = table + (size_t)j * Vd;
         for (int b = 0; b < batch; ++b)
-          topk_lse(zj + b * tstride, 1, V, V, 1, T, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids + b,
+          topk_lse(zj + b * tstride, 1, Vd, Vd, 1, T, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids + b,
                    c->tk_vals + b, c->tk_lse + b, c->tk_lse64 + b, st);
-        chain_draw(j, K, zj, (int)tstride, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok,
-                   batch, c->tk_wsum, st);
+        map_draft_ids(c->tk_ids, batch, c->d2t, c->Vd, st);
+        chain_draw(j, K, zj, (int)tstride, Vd, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q,
+                   c->chain_tok, batch, c->tk_wsum, c->d2t, st);
       } else {
         chain_rows(j - 1, K, c->chain_tok, seq_lens, c->emax, dr, c->S_cap, st);
         tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, batch, d, st);
         draft_layer(c, batch, 1, dr.tok, c->dx, dr_meta(c));
         if (j + 1 < K) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, batch, 1, c->emax, d, st);
         draft_lm(c, batch, c->dx, 1, T);
-        chain_draw(j, K, c->logits, V, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q, c->chain_tok,
-                   batch, c->tk_wsum, st);
+        chain_draw(j, K, c->logits, Vd, Vd, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q,
+                   c->chain_tok, batch, c->tk_wsum, c->d2t, st);
       }
     }
     chain_finalize(K, c->roots, seq_lens, c->chain_tok, out, batch, st);
@@ -613,6 +622,7 @@ eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, c
   if (!hw->fc || !hw->input_norm || !hw->hidden_norm || !hw->wq || !hw->wk || !hw->wv || !hw->wo || !hw->post_norm ||
       !hw->w_gate || !hw->w_up || !hw->w_down || !hw->final_norm)
     return EAGLE3_EINVAL;
+  if (s->draft_vocab > 0 && (!hw->lm_head || !hw->d2t)) return EAGLE3_EINVAL;
   eagle3_ctx* c = new (std::nothrow) eagle3_ctx();
   if (!c) return EAGLE3_EINVAL;
   c->sh = *s;
@@ -621,6 +631,9 @@ eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, c
   c->layers.assign(tw->layers, tw->layers + s->n_layers);
   c->tw.layers = nullptr;
   c->hw = *hw;
+  c->Vd = s->draft_vocab > 0 ? s->draft_vocab : s->vocab;
+  c->dhead = s->draft_vocab > 0 ? hw->lm_head : tw->lm_head;
+  c->d2t = s->draft_vocab > 0 ? hw->d2t : nullptr;
   c->B = max_batch;
   c->R = max_rows;
   c->S_cap = max_seq;
@@ -638,6 +651,7 @@ eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, c
     delete c;
     return EAGLE3_EHIP;
   }
+  if (c->d2t) check_d2t(c->d2t, c->Vd, s->vocab, c->status, c->st);  // a bad map raises BAD_TOKEN
   {
     // rotary inverse frequencies theta^(-2i/hd) in double
     std::vector<double> inv(s->head_dim / 2);
@@ -740,13 +754,14 @@ eagle3_status eagle3_tree_from_logits(eagle3_ctx* c, int32_t batch, const int32_
   if (batch < 1 || batch > c->B) return EAGLE3_ECAPACITY;
   const bool chain = c->cfg.mode == EAGLE3_SAMPLE_CHAIN;
   if (chain && ((!uniforms && !c->cfg.draft_greedy) || !q)) return EAGLE3_EINVAL;
-  const int V = c->sh.vocab;
-  const size_t tstride = (size_t)(1 + c->emax) * V;
+  const int Vd = c->Vd;
+  const size_t tstride = (size_t)(1 + c->emax) * Vd;
   k_seq_roots<<<nb(batch, 64), 64, 0, c->st>>>(batch, 0, roots, c->roots);
   const int K = chain ? 1 : c->cfg.topk;
   const float T = chain ? c->cfg.temperature : 1.f;
-  topk_lse(table, batch, V, (int)tstride, K, T, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids, c->tk_vals,
+  topk_lse(table, batch, Vd, (int)tstride, K, T, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids, c->tk_vals,
            c->tk_lse, c->tk_lse64, c->st);
+  map_draft_ids(c->tk_ids, batch * K, c->d2t, c->Vd, c->st);
   TreeOut out{tokens, parents, depth, pos, mask, score};
   build_tree(c, batch, seq_lens, table, uniforms, out, q);
   return last_error();

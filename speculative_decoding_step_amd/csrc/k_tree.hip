@@ -228,33 +228,42 @@ __global__ __launch_bounds__(512) void k_tree_finalize(TreeState ts, int n_cand,
 
 // ---------------------------------------------------------------- sampled chain
 // Draws one token per row from q = softmax(logits / T), in two launches.
+// Logit rows are V entries long (the draft vocabulary); q rows are Vq long
+// (the target vocabulary): with a reduced draft vocabulary q(v) lands at
+// target id d2t[v] (the rest of the row is zeroed beforehand) and the drawn
+// draft id is mapped through d2t.  Since d2t is ascending, this is the draw
+// over the scattered q.
 // k_draw_slices, grid (slices, rows): q(v) = fl32(exp(z_v / T - lse)) (stored
 // when q_out is given) and the slice's sum of integer weights floor(q * 2^48);
-// greedy rows (draft_greedy, or temperature 0) store the one-hot q of top1.
+// greedy rows (draft_greedy, or temperature 0) store the one-hot q of top1
+// (a target id) over the Vq-long row.
 // k_draw_pick, one 1024-thread block per row: r = floor(u * S) from the slice
 // sums, the slice holding r, and the first entry of that slice whose prefix
 // exceeds r (greedy rows: top1).
-__global__ __launch_bounds__(256) void k_draw_slices(const float* __restrict__ logits, int ld, int V, double temp,
-                                                     const double* __restrict__ lse64, const int* __restrict__ top1,
-                                                     int greedy, float* __restrict__ q_out, size_t q_stride, int ns,
+__global__ __launch_bounds__(256) void k_draw_slices(const float* __restrict__ logits, int ld, int V, int Vq,
+                                                     double temp, const double* __restrict__ lse64,
+                                                     const int* __restrict__ top1, int greedy,
+                                                     float* __restrict__ q_out, size_t q_stride,
+                                                     const int* __restrict__ d2t, int ns,
                                                      unsigned long long* __restrict__ wsum) {
   __shared__ unsigned long long red[256];
   const int sl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int v0 = sl * SAMPLE_SLICE, v1 = min(V, v0 + SAMPLE_SLICE);
   float* q = q_out ? q_out + (size_t)b * q_stride : nullptr;
   if (greedy) {
     if (q) {
       const int t = top1[b];
-      for (int v = v0 + tid; v < v1; v += 256) q[v] = v == t ? 1.f : 0.f;
+      const int w1 = min(Vq, (sl + 1) * SAMPLE_SLICE);
+      for (int v = sl * SAMPLE_SLICE + tid; v < w1; v += 256) q[v] = v == t ? 1.f : 0.f;
     }
     return;
   }
+  const int v0 = sl * SAMPLE_SLICE, v1 = min(V, v0 + SAMPLE_SLICE);
   const float* z = logits + (size_t)b * ld;
   const double l = lse64[b];
   unsigned long long acc = 0ull;
   for (int v = v0 + tid; v < v1; v += 256) {
     const float qv = sample_prob(z, v, temp, l);
-    if (q) q[v] = qv;
+    if (q) q[d2t ? d2t[v] : v] = qv;
     acc += int_weight_of(qv);
   }
   const unsigned long long tot = block_sum256(red, acc);
@@ -265,7 +274,8 @@ __global__ __launch_bounds__(1024) void k_draw_pick(const float* __restrict__ lo
                                                     const double* __restrict__ lse64, const int* __restrict__ top1,
                                                     const float* __restrict__ uniforms, int u_stride, int greedy,
                                                     int ns, const unsigned long long* __restrict__ wsum,
-                                                    int* __restrict__ out_tok, int tok_stride) {
+                                                    const int* __restrict__ d2t, int* __restrict__ out_tok,
+                                                    int tok_stride) {
   __shared__ unsigned long long scan[1024];
   __shared__ unsigned long long s_rin;
   __shared__ int s_slice, pick;
@@ -315,7 +325,30 @@ __global__ __launch_bounds__(1024) void k_draw_pick(const float* __restrict__ lo
     }
   }
   __syncthreads();
-  if (tid == 0) out_tok[(size_t)b * tok_stride] = pick;
+  if (tid == 0) out_tok[(size_t)b * tok_stride] = (d2t && pick >= 0) ? d2t[pick] : pick;
+}
+
+// ids[i] <- d2t[ids[i]] (draft ids to target ids; an id outside [0, Vd) becomes -1)
+__global__ void k_map_ids(int* __restrict__ ids, int n, const int* __restrict__ d2t, int Vd) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const int id = ids[i];
+    ids[i] = (id >= 0 && id < Vd) ? d2t[id] : -1;
+  }
+}
+
+// d2t must hold strictly ascending ids in [0, V)
+__global__ void k_check_d2t(const int* __restrict__ d2t, int Vd, int V, int* status) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Vd) return;
+  const int t = d2t[i];
+  if (t < 0 || t >= V || (i > 0 && d2t[i - 1] >= t)) raise_flag(status, E3_DEV_BAD_TOKEN);
+}
+
+// rows [n] of length V at stride ld set to zero
+__global__ void k_zero_rows(float* __restrict__ p, size_t ld, int V) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v < V) p[(size_t)blockIdx.y * ld + v] = 0.f;
 }
 
 // Chain expansion row j (0-based) of sequence b expands draft d_{j+1}.
@@ -370,23 +403,36 @@ void tree_finalize(const TreeState& ts, int n_cand, int n_nodes, const int* root
                    const TreeOut& out, int* status, hipStream_t st) {
   k_tree_finalize<<<ts.batch, 512, 0, st>>>(ts, n_cand, n_nodes, roots, seq_lens, out, status);
 }
-void chain_draw(int j, int K, const float* logits, int ld, int V, float temperature, const double* lse64,
+void chain_draw(int j, int K, const float* logits, int ld, int Vd, int V, float temperature, const double* lse64,
                 const int* top1, const float* uniforms, int draft_greedy, float* q_out, int* chain_tok, int batch,
-                unsigned long long* wsum, hipStream_t st) {
-  const int ns = sampler_slices(V);
-  k_draw_slices<<<dim3(ns, batch), 256, 0, st>>>(logits, ld, V, (double)temperature, lse64, top1, draft_greedy,
-                                                 q_out + (size_t)j * V, (size_t)K * V, ns, wsum);
-  k_draw_pick<<<batch, 1024, 0, st>>>(logits, ld, V, (double)temperature, lse64, top1, uniforms ? uniforms + j : nullptr,
-                                      K, draft_greedy, ns, wsum, chain_tok + 1 + j, K + 1);
+                unsigned long long* wsum, const int* d2t, hipStream_t st) {
+  const int ns = sampler_slices(Vd);
+  float* qj = q_out + (size_t)j * V;
+  if (draft_greedy) {
+    k_draw_slices<<<dim3(sampler_slices(V), batch), 256, 0, st>>>(logits, ld, Vd, V, (double)temperature, lse64, top1,
+                                                                  1, qj, (size_t)K * V, d2t, ns, wsum);
+  } else {
+    if (d2t) k_zero_rows<<<dim3(nblk(V, 256), batch), 256, 0, st>>>(qj, (size_t)K * V, V);
+    k_draw_slices<<<dim3(ns, batch), 256, 0, st>>>(logits, ld, Vd, V, (double)temperature, lse64, top1, 0, qj,
+                                                   (size_t)K * V, d2t, ns, wsum);
+  }
+  k_draw_pick<<<batch, 1024, 0, st>>>(logits, ld, Vd, (double)temperature, lse64, top1, uniforms ? uniforms + j : nullptr,
+                                      K, draft_greedy, ns, wsum, d2t, chain_tok + 1 + j, K + 1);
 }
 void sample_rows(int n, const float* logits, int V, float temperature, const double* lse64, const int* top1,
                  const float* uniforms, int* tokens, unsigned long long* wsum, hipStream_t st) {
   const int ns = sampler_slices(V), greedy = temperature == 0.f;
   if (!greedy)
-    k_draw_slices<<<dim3(ns, n), 256, 0, st>>>(logits, V, V, (double)temperature, lse64, top1, 0, nullptr, 0, ns,
-                                               wsum);
-  k_draw_pick<<<n, 1024, 0, st>>>(logits, V, V, (double)temperature, lse64, top1, uniforms, 1, greedy, ns, wsum, tokens,
-                                  1);
+    k_draw_slices<<<dim3(ns, n), 256, 0, st>>>(logits, V, V, V, (double)temperature, lse64, top1, 0, nullptr, 0,
+                                               nullptr, ns, wsum);
+  k_draw_pick<<<n, 1024, 0, st>>>(logits, V, V, (double)temperature, lse64, top1, uniforms, 1, greedy, ns, wsum,
+                                  nullptr, tokens, 1);
+}
+void map_draft_ids(int* ids, int n, const int* d2t, int Vd, hipStream_t st) {
+  if (d2t && n > 0) k_map_ids<<<nblk(n, 256), 256, 0, st>>>(ids, n, d2t, Vd);
+}
+void check_d2t(const int* d2t, int Vd, int V, int* status, hipStream_t st) {
+  k_check_d2t<<<nblk(Vd, 256), 256, 0, st>>>(d2t, Vd, V, status);
 }
 void chain_rows(int j, int K, const int* chain_tok, const int* seq_lens, int emax, const DraftRows& dr, int S_cap,
                 hipStream_t st) {

@@ -51,9 +51,15 @@ void tree_store_a(float* a_rows, const float* a, const int* slot, const int* seq
                   int d_model, hipStream_t st);
 void tree_finalize(const TreeState& ts, int n_cand, int n_nodes, const int* roots, const int* seq_lens,
                    const TreeOut& out, int* status, hipStream_t st);
-void chain_draw(int j, int K, const float* logits, int ld, int V, float temperature, const double* lse64,
+// Chain draw j for every sequence: logits rows of Vd entries (the draft vocabulary), q rows of V (the target's;
+// scattered through d2t when the draft vocabulary is reduced, d2t NULL otherwise).
+void chain_draw(int j, int K, const float* logits, int ld, int Vd, int V, float temperature, const double* lse64,
                 const int* top1, const float* uniforms, int draft_greedy, float* q_out, int* chain_tok, int batch,
-                unsigned long long* wsum, hipStream_t st);
+                unsigned long long* wsum, const int* d2t, hipStream_t st);
+// ids[i] <- d2t[ids[i]] for i < n, ids outside [0, Vd) -> -1 (no-op when d2t is NULL).
+void map_draft_ids(int* ids, int n, const int* d2t, int Vd, hipStream_t st);
+// Raises BAD_TOKEN unless d2t[0..Vd) is strictly ascending within [0, V).
+void check_d2t(const int* d2t, int Vd, int V, int* status, hipStream_t st);
 void sample_rows(int n, const float* logits, int V, float temperature, const double* lse64, const int* top1,
                  const float* uniforms, int* tokens, unsigned long long* wsum, hipStream_t st);
 void chain_rows(int j, int K, const int* chain_tok, const int* seq_lens, int emax, const DraftRows& dr, int S_cap,

@@ -66,7 +66,7 @@ class Engine:
                     self.w[name] = t
         w = self.w
         self.shape = B.Shape(ms.n_layers, d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, V, ms.rope_theta,
-                             ms.eps, B.BF16 if self.bf16 else B.F32, (C.c_int32 * 3)(*ms.taps))
+                             ms.eps, B.BF16 if self.bf16 else B.F32, (C.c_int32 * 3)(*ms.taps), ms.draft_vocab)
         modes = {"greedy_tree": B.GREEDY_TREE, "sample_chain": B.SAMPLE_CHAIN, "sample_tree": B.SAMPLE_TREE}
         self.cfg = B.SpecCfg(modes[spec.mode], spec.depth, spec.topk,
                              spec.n_nodes, spec.temperature, int(spec.draft_greedy))
@@ -76,9 +76,12 @@ class Engine:
                 setattr(self._layers[l], f, w[f"l{l}.{f}"].data_ptr())
         self.tw = B.TargetWeights(w["embed"].data_ptr(), self._layers, w["final_norm"].data_ptr(),
                                   w["lm_head"].data_ptr())
+        if ms.draft_vocab > 0:  # reduced draft vocabulary: draft-owned head + ascending map to target ids
+            w["h.d2t"] = torch.as_tensor(configs.d2t_np(ms, head_seed), device=self.dev)
         hw = B.HeadWeights()
         for f, _ in B.HeadWeights._fields_:
-            setattr(hw, f, w["h." + f].data_ptr())
+            t = w.get("h." + f)
+            setattr(hw, f, None if t is None else t.data_ptr())
         self.hw = hw
 
         # ---- caches, workspace, context

@@ -108,6 +108,14 @@ def tokens_np(seed: int, name: str, n: int, vocab: int) -> np.ndarray:
     return randint_np(seed, name, n, 0, vocab - 1).astype(np.int32)
 
 
+def subset_np(seed: int, name: str, n: int, vocab: int) -> np.ndarray:
+    """n distinct seeded ids in [0, vocab), ascending: the ids whose hashes are the n
+    smallest (ties by id)."""
+    b = bits32_np(seed, tag_of(name), vocab)
+    order = np.lexsort((np.arange(vocab), b))
+    return np.sort(order[:n]).astype(np.int32)
+
+
 def uniform24_np(seed: int, name: str, n: int) -> np.ndarray:
     """n seeded uniforms in [0, 1), multiples of 2**-24 (exact in float32)."""
     b = bits32_np(seed, tag_of(name), n)

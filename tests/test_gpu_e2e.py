@@ -84,6 +84,56 @@ def test_toy_tree_end_to_end_with_acceptance(dtype):
     eng.close()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_toy_tree_reduced_draft_vocab_end_to_end(dtype):
+    """A draft head over 40 of the 64 ids (own head, d2t): greedy speculative output is
+    still vanilla greedy output (a token outside the draft vocabulary can only come from
+    the target's own argmax), and the tree tokens stay inside the draft vocabulary."""
+    import dataclasses
+    ms = dataclasses.replace(toy_shape(dtype=dtype, vocab=64, layers=2), draft_vocab=40)
+    spec = Spec("greedy_tree", 4, 3, 10)
+    shp, W, H = oracle_weights(ms, seed=21, sigma=0.3)
+    prompt = synth.tokens_np(41, "p", 20, ms.vocab)
+    ref = vanilla_generate(W, shp, prompt, 40)
+    eng = make_engine(ms, spec, max_seq=128, seed=21, sigma=0.3)
+    out, lens = eng.generate([prompt], 40)
+    assert eng.device_status() == 0
+    n, strict = _compare(out[0], ref, W, shp, prompt)
+    inside = set(H["d2t"].tolist())
+    assert all(int(t) in inside for t in eng.tokens[0, 1:].cpu().numpy())
+    pl = [int(x[0]) for x in lens]
+    outside = sum(1 for t in out[0] if t not in inside)
+    print(f"\n  toy {dtype} V_d 40: identical for {n}/40, strict {strict}, path lengths {pl}, "
+          f"{outside} tokens outside the draft vocabulary", flush=True)
+    assert strict >= 20
+    eng.close()
+
+
+def test_draft_tree_reduced_vocab_matches_oracle_f32():
+    """The whole draft stage with a draft-owned head over a reduced vocabulary (fp32)."""
+    import dataclasses
+    ms = dataclasses.replace(toy_shape(dtype="f32", vocab=96, layers=2), draft_vocab=57)
+    spec = Spec("greedy_tree", 4, 3, 10)
+    shp, W, H = oracle_weights(ms, seed=23, sigma=0.3)
+    prompt = synth.tokens_np(42, "p", 30, ms.vocab)
+    eng = make_engine(ms, spec, max_seq=96, seed=23, sigma=0.3)
+    eng.prefill([prompt])
+    eng.draft()
+    torch.cuda.synchronize()
+    seq = OracleSequence(W, H, shp, SpecConfig("greedy_tree", 4, 3, 10), 96)
+    seq.prefill(prompt)
+    t, _ = seq.draft_tree()
+    assert eng.device_status() == 0
+    sc = eng.score[0].cpu().numpy()
+    ref_sc = np.array(t.score, dtype=np.float32)
+    np.testing.assert_allclose(sc, ref_sc, atol=1e-4)
+    ordered = np.sort(ref_sc)
+    if np.min(np.diff(ordered)[ordered[1:] < 0]) > 1e-3:
+        assert list(eng.tokens[0].cpu().numpy()) == t.tokens
+        assert list(eng.parents[0].cpu().numpy()) == t.parents
+    eng.close()
+
+
 def test_small_bf16_config_short_run():
     w = configs.scaled(configs.WORKLOADS["small_bf16_tree"], prompt_len=128, max_new=24)
     print(f"\n[e2e {w.name} short]", flush=True)

@@ -4,6 +4,7 @@ Integer and index work (trees, masks, paths, samples, compaction) must match
 bit for bit given equal float inputs; logits within 2e-2 absolute (bf16) or
 1e-4 relative (fp32); argmax wherever the oracle's top-2 margin exceeds that.
 """
+import dataclasses
 import json
 import os
 
@@ -19,6 +20,7 @@ from oracle.numerics import probs_f32, sample_inverse_cdf
 from oracle.step import build_sampled_chain
 from oracle.tree import mask_words, tree_from_table, tree_mask
 from speculative_decoding_step_amd import binding as B
+from speculative_decoding_step_amd import configs
 from speculative_decoding_step_amd import synth
 from speculative_decoding_step_amd.engine import Spec
 
@@ -99,8 +101,10 @@ def test_verify_prefill_and_tree_vs_oracle(dtype, chunk):
 
 
 # ------------------------------------------------------------- tree from logits
-def _tree_engine(D, k, N, V, mode="greedy_tree", T=0.0, batch=1, draft_greedy=False):
+def _tree_engine(D, k, N, V, mode="greedy_tree", T=0.0, batch=1, draft_greedy=False, dv=0):
     ms = toy_shape(dtype="bf16", vocab=V, layers=1, d=256, heads=4, kv=4, hd=64, ffn=256, taps=(0, 0, 0))
+    if dv:
+        ms = dataclasses.replace(ms, draft_vocab=dv)
     return make_engine(ms, Spec(mode, D, k, N, T, draft_greedy), batch=batch, max_seq=128)
 
 
@@ -185,6 +189,53 @@ def test_sampled_chain_from_logits_matches_oracle(greedy):
         toks, q = build_sampled_chain(int(roots[b]), table[b, 0], expand, K, T, u[b], greedy)
         assert list(r["tokens"][b]) == toks
         assert list(r["parents"][b]) == [-1, 0, 1, 2, 3, 4]
+        np.testing.assert_allclose(r["q"][b], q, rtol=2e-7, atol=0)
+    eng.close()
+
+
+@pytest.mark.parametrize("D,k,N,V,Vd,Bn", [(6, 10, 60, 128256, 32000, 1), (4, 4, 16, 5000, 1234, 3)])
+def test_tree_from_logits_reduced_vocab_matches_oracle(D, k, N, V, Vd, Bn):
+    """Draft rows over a reduced draft vocabulary: top-k and scores in draft space,
+    tokens mapped through d2t, bit-exact against the oracle."""
+    print(f"\n[tree D{D} k{k} N{N} V{V} Vd{Vd} B{Bn}]", flush=True)
+    rng = np.random.default_rng(Vd)
+    E = (D - 1) * k
+    table = rng.normal(0, 3, size=(Bn, 1 + E, Vd)).astype(np.float32)
+    table[:, :, 9] = table[:, :, 4]  # exact ties
+    roots = list(rng.integers(0, V, Bn))
+    eng = _tree_engine(D, k, N, V, batch=Bn, dv=Vd)
+    d2t = configs.d2t_np(eng.ms, 12)
+    r = _run_tree_from_logits(eng, roots, table)
+    assert eng.device_status() == 0
+    for b in range(Bn):
+        t = tree_from_table(int(roots[b]), table[b], D, k, N, d2t)
+        assert list(r["tokens"][b]) == t.tokens
+        assert list(r["parents"][b]) == t.parents
+        assert np.array_equal(r["score"][b], np.array(t.score, dtype=np.float32))
+    eng.close()
+
+
+@pytest.mark.parametrize("greedy", [False, True])
+def test_sampled_chain_reduced_vocab_matches_oracle(greedy):
+    """Chains drawn over a reduced draft vocabulary: tokens are d2t of the draft-space
+    draw and q is scattered into the target vocabulary, exactly as in the oracle."""
+    K, V, Vd, Bn, T = 5, 3000, 701, 4, 1.0
+    rng = np.random.default_rng(19)
+    table = rng.normal(0, 2, size=(Bn, K, Vd)).astype(np.float32)
+    u = synth.uniform24_np(6, "ud", Bn * K).reshape(Bn, K)
+    roots = list(rng.integers(0, V, Bn))
+    eng = _tree_engine(K, 1, K, V, mode="sample_chain", T=T, batch=Bn, draft_greedy=greedy, dv=Vd)
+    d2t = configs.d2t_np(eng.ms, 12)
+    r = _run_tree_from_logits(eng, roots, table, None if greedy else u)
+    for b in range(Bn):
+        cnt = [0]
+
+        def expand(d, info):
+            cnt[0] += 1
+            return [table[b, cnt[0]]]
+
+        toks, q = build_sampled_chain(int(roots[b]), table[b, 0], expand, K, T, u[b], greedy, d2t, V)
+        assert list(r["tokens"][b]) == toks
         np.testing.assert_allclose(r["q"][b], q, rtol=2e-7, atol=0)
     eng.close()
 
