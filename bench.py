@@ -191,8 +191,8 @@ KERNEL_NAMES = {
 
 def step_bytes(w):
     """Algorithmic HBM bytes of one step: every weight the step's passes read
-    (target layers + LM head once; draft FC once; draft layer + LM head per draft
-    forward, depth forwards per step) plus the K/V the attention reads."""
+    (target layers + LM head once; draft FC once; draft layer + draft LM head per
+    draft forward, depth forwards per step) plus the K/V the attention reads."""
     import numpy as np
 
     from speculative_decoding_step_amd import configs
@@ -203,7 +203,8 @@ def step_bytes(w):
     tgt_layer = s.d * q + 2 * s.d * kv + q * s.d + 3 * s.d * s.ffn
     drf_layer = 2 * s.d * q + 2 * 2 * s.d * kv + q * s.d + 3 * s.d * s.ffn
     lm = s.vocab * s.d
-    weights = s.n_layers * tgt_layer + lm + 3 * s.d * s.d + w.depth * (drf_layer + lm)
+    dlm = (s.draft_vocab or s.vocab) * s.d  # the draft's head: its own reduced one, or the shared target head
+    weights = s.n_layers * tgt_layer + lm + 3 * s.d * s.d + w.depth * (drf_layer + dlm)
     ctx = float(np.sum(configs.prompt_lengths(w)))
     kv_bytes = 2 * kv * e * (s.n_layers * (ctx + w.batch * w.rows) + w.depth * ctx)
     return weights * e + kv_bytes
