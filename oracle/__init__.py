@@ -16,6 +16,7 @@ Modules
   accept    greedy longest-path acceptance, chain rejection sampling and
             level-by-level rejection sampling over a tree
   step      KV compaction and the vanilla / speculative driver loops
+  ttt       training-time-test attention (causal native keys + diagonal simulated keys)
 
 Functions whose result no pin fixes say "parity unpinned" in their docstring:
   tree.build_dynamic_tree  (the frontier/re-rank policy is this build's reading
