@@ -301,6 +301,56 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
 
 
+def ttt_bench(steps, warmup, T=2048, S=7, Hq=32, Hkv=8, hd=128):
+    """Training-time-test attention at the 8B draft layer's head layout (T positions,
+    S simulated steps, bf16, seeded N(0, 1) inputs resident on the device).  One step
+    = one eagle3_ttt_attention call.  Roofline: MFMA against the bf16 peak, with the
+    algorithmic flops of the causal QK and PV products plus the diagonal terms."""
+    import torch
+
+    from speculative_decoding_step_amd import binding as B
+    from speculative_decoding_step_amd import synth
+
+    dev = "cuda"
+    ten = {n: synth.normal_t(9, n, shp, dev, 1.0, "bf16")
+           for n, shp in (("q", (T, Hq, hd)), ("k0", (Hkv, T, hd)), ("v0", (Hkv, T, hd)),
+                          ("ks", (S, Hkv, T, hd)), ("vs", (S, Hkv, T, hd)))}
+    out = torch.empty(T, Hq, hd, dtype=torch.bfloat16, device=dev)
+    wsb = B.eagle3_ttt_workspace_bytes(T, Hq, hd)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+
+    def call():
+        B.eagle3_ttt_attention(B.BF16, T, S, Hq, Hkv, hd, ten["q"].data_ptr(), ten["k0"].data_ptr(),
+                               ten["v0"].data_ptr(), ten["ks"].data_ptr(), ten["vs"].data_ptr(), out.data_ptr(),
+                               ws.data_ptr(), wsb, st.cuda_stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(steps):
+        call()
+    b.record(st)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    flops = 4.0 * Hq * hd * (T * (T + 1) / 2 + T * S)
+    nbytes = 2.0 * (2 * T * Hq * hd + 2 * (1 + S) * Hkv * T * hd)  # q, out, and every step's K and V
+    achieved = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "training-time-test attention positions/s", "value": round(T / (ms * 1e-3), 1),
+        "unit": "positions/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q, k, v", "config": {"workload": "ttt_attn_8b", "positions": T,
+                                                                "simulated_steps": S, "q_heads": Hq,
+                                                                "kv_heads": Hkv, "head_dim": hd},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(achieved / 2500.0, 4), "traffic": None, "algorithmic_bytes": nbytes,
+                     "hbm_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,6 +377,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (the step shards by sequence "
               "with no exchange; run one process per GPU). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "ttt_attn_8b":
+        ttt_bench(args.steps, args.warmup)
+        return
     from speculative_decoding_step_amd import configs
 
     w = configs.WORKLOADS[args.workload]

@@ -302,6 +302,25 @@ eagle3_status eagle3_set_stream(eagle3_ctx *ctx, void *stream);
 eagle3_status eagle3_sample(eagle3_ctx *ctx, int32_t n, const float *logits, float temperature,
                             const float *uniforms, int32_t *tokens);
 
+/* Training-time-test attention forward ("EAGLE-3: Engineering Implementation
+ * ...", VII.5 Attention Mask and the draft layer's forward_ttt): the draft
+ * layer's attention while it is trained on its own predictions.  T positions
+ * of one sequence; the native step's keys are attended causally (query i sees
+ * native keys 0..i), and each of the S simulated steps adds one key per
+ * position that only the query at that position sees (the diagonal); all
+ * scores of a query share one softmax, scaled by 1/sqrt(head_dim).  Query head
+ * h reads KV head h / (n_heads / n_kv_heads).  No context is needed.
+ *   dtype: EAGLE3_F32 or EAGLE3_BF16 (every tensor); head_dim % 4 == 0, <= 256
+ *   q, out [T, n_heads, head_dim]; k0, v0 [n_kv_heads, T, head_dim];
+ *   ks, vs [S, n_kv_heads, T, head_dim] (S >= 0; NULL allowed when S == 0)
+ *   ws: caller-owned device workspace of eagle3_ttt_workspace_bytes() bytes,
+ *   256-byte aligned.  Asynchronous on `stream` (a hipStream_t; NULL = null
+ *   stream).  Bad sizes or pointers return EAGLE3_EINVAL and launch nothing. */
+eagle3_status eagle3_ttt_workspace_bytes(int32_t T, int32_t n_heads, int32_t head_dim, size_t *bytes /* host */);
+eagle3_status eagle3_ttt_attention(int32_t dtype, int32_t T, int32_t S, int32_t n_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, const void *q, const void *k0, const void *v0, const void *ks,
+                                   const void *vs, void *out, void *ws, size_t ws_bytes, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *eagle3_status_string(eagle3_status s);
 

@@ -11,14 +11,15 @@ from __future__ import annotations
 import numpy as np
 
 
-def ttt_attention(q, k0, v0, ks, vs):
+def ttt_attention(q, k0, v0, ks, vs, positions=None):
     """q [T, Hq, hd]; k0, v0 [Hkv, T, hd] (native step); ks, vs [S, Hkv, T, hd]
     (simulated steps; S may be 0).  Query head h reads KV head h // (Hq / Hkv).
 
     Scores of query i: scale * q_i . k0_j for j <= i (causal), then one
     diagonal score scale * q_i . ks[s]_i per simulated step; softmax over the
     i + 1 + S scores; output = the weighted sum of the matching values.
-    float64 throughout.  Returns [T, Hq, hd].
+    float64 throughout.  Returns [T, Hq, hd] (only the rows in `positions`
+    filled when it is given; the others are zero).
     """
     q = np.asarray(q, dtype=np.float64)
     k0 = np.asarray(k0, dtype=np.float64)
@@ -31,9 +32,10 @@ def ttt_attention(q, k0, v0, ks, vs):
     G = Hq // Hkv
     scale = 1.0 / np.sqrt(hd)
     out = np.zeros((T, Hq, hd))
+    rows = range(T) if positions is None else positions
     for h in range(Hq):
         g = h // G
-        for i in range(T):
+        for i in rows:
             native = scale * (k0[g, :i + 1] @ q[i, h])                            # [i + 1]
             diag = np.array([scale * (ks[s, g, i] @ q[i, h]) for s in range(S)])  # [S]
             sc = np.concatenate([native, diag])

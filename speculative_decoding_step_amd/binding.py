@@ -23,7 +23,7 @@ EXPORTS = [
     "eagle3_kv_bytes", "eagle3_workspace_bytes", "eagle3_create", "eagle3_destroy", "eagle3_verify_tree",
     "eagle3_draft_prefill", "eagle3_draft_tree", "eagle3_tree_from_logits", "eagle3_accept", "eagle3_compact_kv",
     "eagle3_sample", "eagle3_set_stream", "eagle3_status_string", "eagle3_device_status", "eagle3_profile", "eagle3_profile_read",
-    "eagle3_pack_linear",
+    "eagle3_pack_linear", "eagle3_ttt_workspace_bytes", "eagle3_ttt_attention",
 ]
 
 
@@ -85,6 +85,8 @@ def lib():
             "eagle3_accept": [P, I32, I32, P, P, P, P, P, P, P, P, P, P],
             "eagle3_compact_kv": [P, I32, P, I32, P, P, P, P, P, P, P, P],
             "eagle3_sample": [P, I32, P, C.c_float, P, P],
+            "eagle3_ttt_workspace_bytes": [I32, I32, I32, C.POINTER(C.c_size_t)],
+            "eagle3_ttt_attention": [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, C.c_size_t, P],
             "eagle3_set_stream": [P, P],
             "eagle3_device_status": [P, C.POINTER(I32)],
             "eagle3_profile": [P, I32],
@@ -177,6 +179,17 @@ def eagle3_compact_kv(ctx, batch, seq_lens, n_rows, path, path_len, tokens, next
 
 def eagle3_sample(ctx, n, logits, temperature, uniforms, tokens):
     _check(lib().eagle3_sample(ctx, n, logits, temperature, uniforms, tokens), "eagle3_sample")
+
+
+def eagle3_ttt_workspace_bytes(T, n_heads, head_dim) -> int:
+    b = C.c_size_t()
+    _check(lib().eagle3_ttt_workspace_bytes(T, n_heads, head_dim, C.byref(b)), "eagle3_ttt_workspace_bytes")
+    return b.value
+
+
+def eagle3_ttt_attention(dtype, T, S, n_heads, n_kv_heads, head_dim, q, k0, v0, ks, vs, out, ws, ws_bytes, stream):
+    _check(lib().eagle3_ttt_attention(dtype, T, S, n_heads, n_kv_heads, head_dim, q, k0, v0, ks, vs, out, ws,
+                                      ws_bytes, stream), "eagle3_ttt_attention")
 
 
 def eagle3_set_stream(ctx, stream):

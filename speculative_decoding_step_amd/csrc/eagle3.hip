@@ -825,6 +825,26 @@ eagle3_status eagle3_sample(eagle3_ctx* c, int32_t n, const float* logits, float
   return last_error();
 }
 
+eagle3_status eagle3_ttt_workspace_bytes(int32_t T, int32_t n_heads, int32_t head_dim, size_t* bytes) {
+  if (!bytes || T < 1 || n_heads < 1 || head_dim < 4 || head_dim > 256 || head_dim % 4) return EAGLE3_EINVAL;
+  *bytes = ttt_workspace_bytes(T, n_heads, head_dim);
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_ttt_attention(int32_t dtype, int32_t T, int32_t S, int32_t n_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, const void* q, const void* k0, const void* v0, const void* ks,
+                                   const void* vs, void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != EAGLE3_F32 && dtype != EAGLE3_BF16) return EAGLE3_EINVAL;
+  if (T < 1 || S < 0 || n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || head_dim < 4 || head_dim > 256 ||
+      head_dim % 4)
+    return EAGLE3_EINVAL;
+  if (!q || !k0 || !v0 || !out || !ws || (S > 0 && (!ks || !vs)) || ((uintptr_t)ws & 255)) return EAGLE3_EINVAL;
+  if (ws_bytes < ttt_workspace_bytes(T, n_heads, head_dim)) return EAGLE3_ECAPACITY;
+  ttt_attention(dtype == EAGLE3_BF16, T, S, n_heads, n_kv_heads, head_dim, q, k0, v0, ks, vs, out, ws,
+                (hipStream_t)stream);
+  return last_error();
+}
+
 eagle3_status eagle3_set_stream(eagle3_ctx* c, void* stream) {
   if (!c) return EAGLE3_EINVAL;
   c->st = (hipStream_t)stream;

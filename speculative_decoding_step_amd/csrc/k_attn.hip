@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
                                                       int hd, const int* __restrict__ rseq,
                                                       const int* __restrict__ rlim, const int* __restrict__ rt0,
                                                       const uint64_t* __restrict__ rmask, int S_cap, int chunk,
-                                                      T* __restrict__ out) {
+                                                      int extra, T* __restrict__ out) {
   const int r = blockIdx.x;
   const int tph = hd >> 2;  // threads per head
   const int h = blockIdx.y * (blockDim.x / tph) + threadIdx.x / tph, d4 = threadIdx.x % tph;
@@ -151,6 +151,23 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
         acc.x += o[j].x * e, acc.y += o[j].y * e, acc.z += o[j].z * e, acc.w += o[j].w * e;
       }
   }
+  if (extra >= 0) {  // one more partial merged for every row (not tied to the key chunks)
+    const float2 ve = ml[(size_t)extra * sstride + oi0];
+    if (ve.x != -INFINITY) {
+      const float4 oe = o4[((size_t)extra * sstride + oi0) * tph + d4];
+      if (ve.x > M) {
+        if (M != -INFINITY) {
+          const float c = expf(M - ve.x);
+          den *= c;
+          acc.x *= c, acc.y *= c, acc.z *= c, acc.w *= c;
+        }
+        M = ve.x;
+      }
+      const float e = expf(ve.x - M);
+      den += ve.y * e;
+      acc.x += oe.x * e, acc.y += oe.y * e, acc.z += oe.z * e, acc.w += oe.w * e;
+    }
+  }
   const size_t ob = oi0 * hd + 4 * d4;
   st<T>(out, ob, den > 0.f ? acc.x / den : 0.f);
   st<T>(out, ob + 1, den > 0.f ? acc.y / den : 0.f);
@@ -160,10 +177,10 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 
 template <typename T>
 void combine(const float* o_part, const float* ml_part, int ns, int R, int Hq, int hd, const RowMeta& rm,
-             int key_bound, int chunk, T* out, hipStream_t st) {
+             int key_bound, int chunk, int extra, T* out, hipStream_t st) {
   const int hpb = 256 / (hd / 4);
   k_attn_combine<T><<<dim3(R, (Hq + hpb - 1) / hpb), 256, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, rm.seq, rm.lim,
-                                                                   rm.tail0, rm.mask, key_bound, chunk, out);
+                                                                   rm.tail0, rm.mask, key_bound, chunk, extra, out);
 }
 
 // ---------------------------------------------------------------- MFMA path
@@ -260,7 +277,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (lam >= nwork) return;
   constexpr int QB = 16 * NW;
-  const int qb = lam % qblocks;
+  const int qb = qblocks - 1 - lam % qblocks;  // later query rows first: under a causal mask they see the most keys
   int t = lam / qblocks;
   const int g = t % Hkv;
   t /= Hkv;
@@ -494,10 +511,12 @@ void launch_attn(int nw, unsigned nblocks, hipStream_t st, const bf16_t* q, cons
 #undef E3_ATTN_LAUNCH
 }
 
-void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride, size_t head_stride,
-               const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound, float* o_part,
-               float* ml_part, int max_splits, void* out, hipStream_t st) {
-  if (R <= 0) return;
+// The chunk partials of tree-masked attention (o_part / ml_part, chunk-major);
+// returns the number of key chunks written and their length.
+AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride,
+                              size_t head_stride, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd,
+                              int key_bound, float* o_part, float* ml_part, int max_splits, hipStream_t st,
+                              int chunk_override) {
   int ns = (key_bound + ATT_CHUNK - 1) / ATT_CHUNK;
   if (ns < 1) ns = 1;
   if (ns > max_splits) ns = max_splits;  // the workspace holds ceil(max_seq / chunk) splits
@@ -510,7 +529,8 @@ void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t 
     // Longer key chunks when the launch has work to spare: fewer partials to
     // write and merge, and each workgroup's set-up spread over more tiles.
     const long tiles256 = (long)(R / rps) * qblocks * Hkv * ns;
-    const int chunk = tiles256 >= 8192   ? 6 * ATT_CHUNK
+    const int chunk = chunk_override > 0 ? chunk_override
+                      : tiles256 >= 8192 ? 6 * ATT_CHUNK
                       : tiles256 >= 4096 ? 3 * ATT_CHUNK
                       : tiles256 >= 2048 ? 2 * ATT_CHUNK
                                          : ATT_CHUNK;
@@ -519,24 +539,225 @@ void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t 
     const int nblocks = (nwork + 7) / 8 * 8;
     if (hd == 128)
       launch_attn<128, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
-                       head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part, ml_part);
+                          head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part,
+                          ml_part);
     else
       launch_attn<64, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
-                      head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part, ml_part);
-    combine<bf16_t>(o_part, ml_part, ns, R, Hq, hd, rm, key_bound, chunk, (bf16_t*)out, st);
-    return;
+                         head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part,
+                         ml_part);
+    return AttnSplits{ns, chunk};
   }
   dim3 grid(R, Hq, ns);
-  if (bf16) {
+  if (bf16)
     k_attn_partial<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
                                                 head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, Hq, Hkv, hd,
                                                 key_bound, scale, o_part, ml_part);
-    combine<bf16_t>(o_part, ml_part, ns, R, Hq, hd, rm, key_bound, ATT_CHUNK, (bf16_t*)out, st);
-  } else {
+  else
     k_attn_partial<float><<<grid, 64, 0, st>>>((const float*)q, (const float*)kc, (const float*)vc, seq_stride,
                                                head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, Hq, Hkv, hd, key_bound,
                                                scale, o_part, ml_part);
-    combine<float>(o_part, ml_part, ns, R, Hq, hd, rm, key_bound, ATT_CHUNK, (float*)out, st);
+  return AttnSplits{ns, ATT_CHUNK};
+}
+
+void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride, size_t head_stride,
+               const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound, float* o_part,
+               float* ml_part, int max_splits, void* out, hipStream_t st) {
+  if (R <= 0) return;
+  const AttnSplits sp = attention_partials(bf16, q, kc, vc, seq_stride, head_stride, rm, R, rps, Hq, Hkv, hd,
+                                           key_bound, o_part, ml_part, max_splits, st, 0);
+  if (bf16)
+    combine<bf16_t>(o_part, ml_part, sp.ns, R, Hq, hd, rm, key_bound, sp.chunk, -1, (bf16_t*)out, st);
+  else
+    combine<float>(o_part, ml_part, sp.ns, R, Hq, hd, rm, key_bound, sp.chunk, -1, (float*)out, st);
+}
+
+// ------------------------------------------------------ training-time test
+// Attention of the draft layer during training-time test ("EAGLE-3:
+// Engineering Implementation of LLM Inference Acceleration", VII.5 and the
+// draft layer's forward_ttt): the native step's keys are attended causally,
+// each simulated step adds one key per position that only the query at that
+// position sees.  The causal part is the tree-masked attention above with row
+// i seeing keys [0, i] (lim = i + 1, no tree part); the S diagonal scores of
+// every (position, head) form one more online-softmax partial (k_ttt_diag),
+// merged by the combine kernel with the chunk partials.
+
+// rows i < T: one sequence, causal over the native keys
+__global__ void k_ttt_meta(int T, RowMeta rm) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  rm.seq[i] = 0;
+  rm.pos[i] = i;
+  rm.slot[i] = i;
+  rm.lim[i] = i + 1;
+  rm.tail0[i] = 0;
+  rm.mask[i] = 0ull;
+}
+
+// One wave per (position i, query head h): scores s_j = scale * q . ks[j][g][i]
+// for j < S, partial (m = max s_j, l = sum exp(s_j - m), o = sum exp(s_j - m) vs[j][g][i])
+// written as split `split` of o_part / ml_part (m = -inf, l = 0 when S = 0).
+template <typename T>
+__global__ __launch_bounds__(64) void k_ttt_diag(int Tn, int S, int Hq, int Hkv, int hd, float scale,
+                                                 const T* __restrict__ q, const T* __restrict__ ks,
+                                                 const T* __restrict__ vs, int split, float* __restrict__ o_part,
+                                                 float* __restrict__ ml_part) {
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int g = h / (Hq / Hkv);
+  const size_t oi = ((size_t)split * Tn + i) * Hq + h;
+  const T* qp = q + ((size_t)i * Hq + h) * hd;
+  float m = -INFINITY;
+  for (int j = 0; j < S; ++j) {  // pass 1: the maximum
+    const T* kp = ks + (((size_t)j * Hkv + g) * Tn + i) * hd;
+    float d = 0.f;
+    for (int e = lane; e < hd; e += 64) d += ld<T>(qp, e) * ld<T>(kp, e);
+    m = fmaxf(m, wave_sum(d) * scale);
+  }
+  float l = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};  // dims lane, lane + 64, ... (hd <= 256)
+  for (int j = 0; j < S; ++j) {  // pass 2: weights and the weighted values
+    const T* kp = ks + (((size_t)j * Hkv + g) * Tn + i) * hd;
+    const T* vp = vs + (((size_t)j * Hkv + g) * Tn + i) * hd;
+    float d = 0.f;
+    for (int e = lane; e < hd; e += 64) d += ld<T>(qp, e) * ld<T>(kp, e);
+    const float p = expf(wave_sum(d) * scale - m);
+    l += p;
+    for (int c = 0; c * 64 + lane < hd; ++c) o[c] += p * ld<T>(vp, c * 64 + lane);
+  }
+  for (int c = 0; c * 64 + lane < hd; ++c) o_part[oi * hd + c * 64 + lane] = o[c];
+  if (lane == 0) {
+    ml_part[2 * oi] = m;
+    ml_part[2 * oi + 1] = l;
+  }
+}
+
+// Fused form (one key chunk covers every native key): one wave per (position
+// i, KV head g) handles the G query heads of the group (G * S <= 32).  Two
+// lanes per (head, step) pair each take half of the q . k dot product
+// (16-byte loads, one shuffle to join the halves), the scores go through LDS
+// to every lane, and each lane then folds them into the chunk's partial
+// (m, l, o) of every head for its HD/64 dims and writes the normalised output.
+constexpr int TTT_SMAX = 16, TTT_PAIRS = 32;
+template <int HD>
+__global__ __launch_bounds__(64) void k_ttt_diag_merge(int Tn, int S, int Hq, int Hkv, float scale,
+                                                       const bf16_t* __restrict__ q, const bf16_t* __restrict__ ks,
+                                                       const bf16_t* __restrict__ vs,
+                                                       const float* __restrict__ o_part,
+                                                       const float* __restrict__ ml_part,
+                                                       bf16_t* __restrict__ out) {
+  constexpr int PL = HD / 64;     // output dims per lane: lane + 64 c
+  constexpr int HALF = HD / 2;    // dot-product elements per lane
+  __shared__ float sc[TTT_PAIRS];
+  const int i = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+  const int G = Hq / Hkv;
+  const int pair = lane >> 1, half = lane & 1;
+  const int hp = pair / S, jp = pair % S;
+  const bool pv = pair < G * S;
+  // scores: lane pair (hp, jp), dims [half * HALF, (half + 1) * HALF)
+  float d = 0.f;
+  if (pv) {
+    const u32x4* qp = (const u32x4*)(q + ((size_t)i * Hq + g * G + hp) * HD + half * HALF);
+    const u32x4* kp = (const u32x4*)(ks + (((size_t)jp * Hkv + g) * Tn + i) * HD + half * HALF);
+    u32x4 qa[HALF / 8], ka[HALF / 8];
+#pragma unroll
+    for (int c = 0; c < HALF / 8; ++c) {
+      qa[c] = qp[c];
+      ka[c] = kp[c];
+    }
+#pragma unroll
+    for (int c = 0; c < HALF / 8; ++c) {
+      const bf16_t* a = (const bf16_t*)&qa[c];
+      const bf16_t* b = (const bf16_t*)&ka[c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d += bf2f(a[e]) * bf2f(b[e]);
+    }
+  }
+  d += __shfl_xor(d, 1, 64);
+  if (pv && half == 0) sc[pair] = d * scale;
+  // the values of this lane's output dims, and the heads' partials
+  float vr[TTT_SMAX][PL];
+#pragma unroll
+  for (int j = 0; j < TTT_SMAX; ++j)
+#pragma unroll
+    for (int c = 0; c < PL; ++c)
+      vr[j][c] = j < S ? bf2f(vs[(((size_t)j * Hkv + g) * Tn + i) * HD + c * 64 + lane]) : 0.f;
+  __syncthreads();
+  for (int hl = 0; hl < G; ++hl) {
+    const size_t oi = (size_t)i * Hq + g * G + hl;  // chunk 0 of the partials
+    const float m0 = ml_part[2 * oi], l0 = ml_part[2 * oi + 1];
+    float M = m0;  // natural-log units of the scaled score
+    for (int j = 0; j < S; ++j) M = fmaxf(M, sc[hl * S + j]);
+    const float e0 = expf(m0 - M);
+    float den = l0 * e0;
+    float acc[PL];
+#pragma unroll
+    for (int c = 0; c < PL; ++c) acc[c] = o_part[oi * HD + c * 64 + lane] * e0;
+#pragma unroll
+    for (int j = 0; j < TTT_SMAX; ++j) {
+      if (j >= S) break;
+      const float p = expf(sc[hl * S + j] - M);
+      den += p;
+#pragma unroll
+      for (int c = 0; c < PL; ++c) acc[c] += p * vr[j][c];
+    }
+#pragma unroll
+    for (int c = 0; c < PL; ++c) out[oi * HD + c * 64 + lane] = f2bf(acc[c] / den);
+  }
+}
+
+size_t ttt_workspace_bytes(int T, int Hq, int hd) {
+  const size_t splits = (size_t)(T + ATT_CHUNK - 1) / ATT_CHUNK + 1;  // the key chunks + the diagonal partial
+  size_t b = 0;
+  b += splits * T * Hq * hd * sizeof(float);      // o_part
+  b += splits * T * Hq * 2 * sizeof(float);       // ml_part
+  b += (size_t)T * (5 * sizeof(int) + sizeof(uint64_t));  // row metadata
+  return b + 8 * 256;                                      // each of the 8 arrays starts 256-aligned
+}
+
+void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void* q, const void* k0, const void* v0,
+                   const void* ks, const void* vs, void* out, void* ws, hipStream_t st) {
+  const int max_splits = (T + ATT_CHUNK - 1) / ATT_CHUNK;
+  char* p = (char*)ws;
+  auto take = [&](size_t bytes) {
+    char* r = p;
+    p += (bytes + 255) / 256 * 256;
+    return r;
+  };
+  float* o_part = (float*)take((size_t)(max_splits + 1) * T * Hq * hd * sizeof(float));
+  float* ml_part = (float*)take((size_t)(max_splits + 1) * T * Hq * 2 * sizeof(float));
+  RowMeta rm{};
+  rm.seq = (int*)take(T * sizeof(int));
+  rm.pos = (int*)take(T * sizeof(int));
+  rm.slot = (int*)take(T * sizeof(int));
+  rm.lim = (int*)take(T * sizeof(int));
+  rm.tail0 = (int*)take(T * sizeof(int));
+  rm.mask = (uint64_t*)take(T * sizeof(uint64_t));
+  k_ttt_meta<<<(T + 255) / 256, 256, 0, st>>>(T, rm);
+  const float scale = 1.f / sqrtf((float)hd);
+  if (bf16 && (hd == 64 || hd == 128) && S <= TTT_SMAX && (Hq / Hkv) * S <= TTT_PAIRS) {
+    // one key chunk spans all T native keys (the T rows already fill the chip), then the fused diagonal + merge
+    const int chunk = (T + 63) / 64 * 64;
+    attention_partials(true, q, k0, v0, (size_t)Hkv * T * hd, (size_t)T * hd, rm, T, T, Hq, Hkv, hd, T, o_part,
+                       ml_part, max_splits, st, chunk);
+    if (hd == 128)
+      k_ttt_diag_merge<128><<<dim3(T, Hkv), 64, 0, st>>>(T, S, Hq, Hkv, scale, (const bf16_t*)q, (const bf16_t*)ks,
+                                                         (const bf16_t*)vs, o_part, ml_part, (bf16_t*)out);
+    else
+      k_ttt_diag_merge<64><<<dim3(T, Hkv), 64, 0, st>>>(T, S, Hq, Hkv, scale, (const bf16_t*)q, (const bf16_t*)ks,
+                                                        (const bf16_t*)vs, o_part, ml_part, (bf16_t*)out);
+    return;
+  }
+  // native keys [Hkv][T][hd]: one "sequence" of T slots
+  const AttnSplits sp = attention_partials(bf16, q, k0, v0, (size_t)Hkv * T * hd, (size_t)T * hd, rm, T, T, Hq, Hkv,
+                                           hd, T, o_part, ml_part, max_splits, st, 0);
+  const int extra = max_splits;  // a split index no key chunk uses
+  if (bf16) {
+    k_ttt_diag<bf16_t><<<dim3(T, Hq), 64, 0, st>>>(T, S, Hq, Hkv, hd, scale, (const bf16_t*)q, (const bf16_t*)ks,
+                                                   (const bf16_t*)vs, extra, o_part, ml_part);
+    combine<bf16_t>(o_part, ml_part, sp.ns, T, Hq, hd, rm, T, sp.chunk, extra, (bf16_t*)out, st);
+  } else {
+    k_ttt_diag<float><<<dim3(T, Hq), 64, 0, st>>>(T, S, Hq, Hkv, hd, scale, (const float*)q, (const float*)ks,
+                                                  (const float*)vs, extra, o_part, ml_part);
+    combine<float>(o_part, ml_part, sp.ns, T, Hq, hd, rm, T, sp.chunk, extra, (float*)out, st);
   }
 }
 

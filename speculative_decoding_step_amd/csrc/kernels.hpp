@@ -91,6 +91,18 @@ void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const R
 
 // Attention of rows over their visible keys, split over key chunks, then combined.
 // rps: rows per sequence (rows of one sequence are consecutive; R % rps == 0).
+struct AttnSplits {
+  int ns, chunk;  // key chunks written, keys per chunk
+};
+AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride,
+                              size_t head_stride, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd,
+                              int key_bound, float* o_part, float* ml_part, int max_splits, hipStream_t st,
+                              int chunk_override);  // chunk_override > 0: keys per chunk (else the size policy)
+// Training-time-test attention: q, out [T, Hq, hd]; k0, v0 [Hkv, T, hd]; ks, vs [S, Hkv, T, hd]; ws of
+// ttt_workspace_bytes(T, Hq, hd) bytes.
+size_t ttt_workspace_bytes(int T, int Hq, int hd);
+void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void* q, const void* k0, const void* v0,
+                   const void* ks, const void* vs, void* out, void* ws, hipStream_t st);
 void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride,
                size_t head_stride, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
                float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st);

@@ -419,6 +419,43 @@ def test_accept_tree_flags_malformed_input():
     eng.close()
 
 
+@pytest.mark.parametrize("dtype,T,S,Hq,Hkv,hd", [("bf16", 300, 3, 8, 2, 128), ("bf16", 1, 2, 4, 4, 64),
+                                                ("bf16", 777, 7, 4, 1, 64), ("bf16", 513, 0, 8, 4, 128),
+                                                ("f32", 129, 2, 4, 2, 96), ("f32", 40, 0, 2, 1, 32),
+                                                ("bf16", 2048, 7, 32, 8, 128)])
+def test_ttt_attention_matches_oracle(dtype, T, S, Hq, Hkv, hd):
+    """Training-time-test attention (causal native keys + diagonal simulated keys)
+    against the oracle: every position for the small cases, sampled positions (first,
+    last, chunk boundaries, random) at the 8B head layout with T = 2048, S = 7."""
+    from oracle.ttt import ttt_attention
+    print(f"\n[ttt {dtype} T{T} S{S} Hq{Hq} Hkv{Hkv} hd{hd}]", flush=True)
+    rng = np.random.default_rng(T + 31 * S)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def dev(a):
+        t = torch.as_tensor(a, dtype=torch.float32).to(tdt)
+        return t.cuda(), t.float().numpy().astype(np.float64)  # device copy, and the stored values
+
+    q, qn = dev(rng.normal(size=(T, Hq, hd)))
+    k0, k0n = dev(rng.normal(size=(Hkv, T, hd)))
+    v0, v0n = dev(rng.normal(size=(Hkv, T, hd)))
+    ks, ksn = dev(rng.normal(size=(S, Hkv, T, hd)))
+    vs, vsn = dev(rng.normal(size=(S, Hkv, T, hd)))
+    out = torch.zeros(T, Hq, hd, dtype=tdt, device="cuda")
+    wsb = B.eagle3_ttt_workspace_bytes(T, Hq, hd)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    B.eagle3_ttt_attention(B.BF16 if dtype == "bf16" else B.F32, T, S, Hq, Hkv, hd, _p(q), _p(k0), _p(v0),
+                           _p(ks) if S else None, _p(vs) if S else None, _p(out), _p(ws), wsb, None)
+    torch.cuda.synchronize()
+    pos = list(range(T)) if T * Hq <= 8192 else sorted(set([0, 1, 255, 256, 767, 768, T - 1] +
+                                                            [int(x) for x in rng.integers(0, T, 17)]))
+    ref = ttt_attention(qn, k0n, v0n, ksn, vsn, positions=pos)[pos]
+    got = out.float().cpu().numpy()[pos]
+    err = np.abs(got - ref).max()
+    print(f"  max |diff| {err:.3g} over {len(pos)} positions", flush=True)
+    assert err <= (2e-2 if dtype == "bf16" else 1e-4 * np.abs(ref).max())
+
+
 def test_sample_rows_match_oracle():
     rng = np.random.default_rng(6)
     V, n = 32000, 24
