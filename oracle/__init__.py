@@ -16,6 +16,8 @@ Modules
   accept    greedy longest-path acceptance, chain rejection sampling and
             level-by-level rejection sampling over a tree
   step      KV compaction and the vanilla / speculative driver loops
+  paged     block-table slot mapping, per-request draft lengths and the verify
+            batch's index bookkeeping
   ttt       training-time-test attention (causal native keys + diagonal simulated keys)
 
 Functions whose result no pin fixes say "parity unpinned" in their docstring:

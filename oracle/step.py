@@ -11,7 +11,8 @@ Sources (page title, section):
     the cache, the rest discarded; the next root is the argmax at the end of
     the path) and the vanilla greedy decode it is compared with.
   * "Speculative Decoding (EAGLE3) in the vLLM Neuron Framework", Design
-    Choices (speculation stops near the length limit) and The propose()
+    Choices (speculation stops near the length limit; a request may verify
+    fewer drafts, see paged.truncate_tree) and The propose()
     Method (prefill phase, then recurrent phase at increasing positions).
 
 Readings (the pages leave these open):
@@ -33,6 +34,7 @@ from .accept import argmax_rows_f32, chain_rejection, greedy_walk, tree_rejectio
 from .llama import (KVCache, Shape, causal_visible, draft_fuse, draft_layer, draft_logits,
                     target_forward)
 from .numerics import argmax_first, probs_f32, sample_inverse_cdf
+from .paged import truncate_tree
 from .tree import Tree, build_dynamic_tree, tree_mask
 
 
@@ -208,9 +210,10 @@ class OracleSequence:
         if self.spec.mode == "sample_tree":
             p = np.stack([probs_f32(f32(logits[i]), self.spec.temperature) for i in range(len(tree.tokens))])
             return tree_rejection(tree.tokens, tree.parents, p, u_accept, self.spec.topk, self.spec.depth)
-        K = self.spec.depth
+        K = len(tree.tokens) - 1  # the request's draft length (the chain's full depth unless truncated)
         p = np.stack([probs_f32(f32(logits[i]), self.spec.temperature) for i in range(K + 1)])
-        n_acc, nxt = chain_rejection(tree.tokens[1:], q, p, u_accept)
+        u = list(u_accept[:K]) + [u_accept[self.spec.depth]]  # the final draw keeps the row's last uniform
+        n_acc, nxt = chain_rejection(tree.tokens[1:], q[:K], p, u)
         return list(range(n_acc + 1)), nxt
 
     def compact(self, tree: Tree, path, next_root, k, v, aux):
@@ -221,15 +224,18 @@ class OracleSequence:
         self.emitted += [tree.tokens[i] for i in path]
         self.root = int(next_root)
 
-    def step(self, u_draft=None, u_accept=None, tree=None):
+    def step(self, u_draft=None, u_accept=None, tree=None, n_draft=None):
         """One speculative step.  A given ``tree`` replaces the drafted one (the draft's
         catch-up still runs so its cache stays consistent); tests inject trees that hold
-        a known continuation to exercise multi-token acceptance."""
+        a known continuation to exercise multi-token acceptance.  ``n_draft`` limits the
+        request's verified draft to its first n_draft nodes (paged.truncate_tree)."""
         if tree is None:
             tree, q = self.draft_tree(u_draft)
         else:
             self.draft_catchup()
             q = None
+        if n_draft is not None:
+            tree = truncate_tree(tree, n_draft)
         logits, k, v, aux = self.verify(tree)
         path, nxt = self.accept(tree, logits, q, u_accept)
         self.compact(tree, path, nxt, k, v, aux)
