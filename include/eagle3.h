@@ -163,6 +163,84 @@ eagle3_status eagle3_create(const eagle3_shape *shape /* host */, const eagle3_s
                             eagle3_ctx **out /* host */);
 eagle3_status eagle3_destroy(eagle3_ctx *ctx);
 
+/* Paged KV cache ("Speculative Decoding (EAGLE3) in the vLLM Neuron
+ * Framework", The propose() Method: a position's cache slot comes from its
+ * sequence's block table).  Position pos of context sequence s lives in block
+ * block_table[s * blocks_per_seq + pos / block_size] at offset
+ * pos % block_size; every call of the context (prefill, draft, verify,
+ * compaction) reads and writes K/V through the table.  Pools:
+ *   target: [n_layers][2 (K,V)][n_blocks][Hkv][block_size][hd] of T
+ *   draft : [2 (K,V)][n_blocks][Hkv][block_size][hd] of T
+ * (the draft layer's cache uses the same table).  block_size is a power of
+ * two >= 64, so one 64-key attention tile never spans two blocks.  The table
+ * is caller-owned device memory, read at every launch (it may change between
+ * steps; a graph replay sees its current contents): the caller allocates
+ * blocks for every position a call touches (committed + n_nodes + 1 for the
+ * target, committed + (depth - 1) * topk for the draft).  Entries outside
+ * [0, n_blocks) are never dereferenced: a write through one is dropped and
+ * raises EAGLE3_DEV_KV_OVERFLOW, a read is clamped into the pool. */
+typedef struct {
+  int32_t block_size;           /* positions per block: a power of two, >= 64 */
+  int32_t n_blocks;             /* blocks in each pool */
+  int32_t blocks_per_seq;       /* table entries per sequence; the logical capacity is blocks_per_seq * block_size */
+  const int32_t *block_table;   /* device [max_batch, blocks_per_seq] */
+} eagle3_kv_pages;
+
+/* Bytes of the two paged pools. */
+eagle3_status eagle3_paged_kv_bytes(const eagle3_shape *shape, int32_t block_size, int32_t n_blocks,
+                                    size_t *target_bytes /* host */, size_t *draft_bytes /* host */);
+
+/* eagle3_create for a paged cache: max_seq is pages->blocks_per_seq *
+ * pages->block_size; kv_target / kv_draft are the pools above.  EINVAL for a
+ * block size that is not a power of two >= 64 or sizes < 1. */
+eagle3_status eagle3_create_paged(const eagle3_shape *shape /* host */, const eagle3_spec_cfg *cfg /* host */,
+                                  const eagle3_target_weights *target /* host struct */,
+                                  const eagle3_head_weights *head /* host struct */,
+                                  int32_t max_batch, int32_t max_rows, const eagle3_kv_pages *pages /* host */,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *kv_target, void *kv_draft, void *stream,
+                                  eagle3_ctx **out /* host */);
+
+/* Per-request draft lengths ("Speculative Decoding (EAGLE3) in the vLLM
+ * Neuron Framework", SpecDecodeMetadata and Design Choices: requests verify
+ * different numbers of drafts; one near its length limit verifies none and
+ * decodes a single token).  n_draft: device [max_batch] int32, indexed by
+ * context sequence, read at every later launch; NULL restores the full
+ * budget.  Sequence s verifies the root and its first min(n_draft[s],
+ * n_rows - 1) tree nodes (node order: parents precede children, so they form
+ * a tree); for a chain, its first n_draft[s] drafts.  eagle3_verify_tree
+ * with a mask (a draft's verify; prefill chunks are not affected) writes no
+ * K/V for the other rows and their outputs are unspecified (the capacity
+ * check covers only the active rows); eagle3_accept ignores them;
+ * in chain mode the final draw still uses uniforms[b, depth].  Negative
+ * values count as 0. */
+eagle3_status eagle3_set_draft_lengths(eagle3_ctx *ctx, const int32_t *n_draft);
+
+/* Index bookkeeping of one flat verify batch ("Speculative Decoding (EAGLE3)
+ * in the vLLM Neuron Framework", SpecDecodeMetadata: Index Bookkeeping).
+ * Request b owns flat input positions [cu[b-1], cu[b]) (cu[-1] = 0), the
+ * last num_draft_tokens[b] of which are drafts; its logits are needed at the
+ * nd + 1 positions that end it.  Outputs (device int32):
+ *   cu_num_draft_tokens [batch]: running total of drafts;
+ *   logits_indices [batch + total drafts]: those positions, request by request;
+ *   target_logits_indices [total drafts]: entries of logits_indices that verify a draft;
+ *   bonus_logits_indices [batch]: each request's last entry;
+ *   draft_token_ids [total drafts] (NULL to skip): input_ids at the draft
+ *     positions (input_ids may be NULL when it is skipped).
+ * max_drafts is the capacity of target_logits_indices and draft_token_ids
+ * (logits_indices holds batch + max_drafts).  One workgroup, any batch;
+ * cu_num_scheduled_tokens and num_draft_tokens are device [batch].  A
+ * request with nd < 0, an empty request, nd + 1 > its scheduled tokens, or a
+ * total above max_drafts sets *error (device int32, NULL allowed) to 1 (else
+ * 0); nd is then clamped into [0, scheduled - 1], entries past the
+ * capacities are not written and the outputs are unspecified.
+ * Asynchronous on `stream` (a hipStream_t; NULL = null stream). */
+eagle3_status eagle3_spec_decode_metadata(int32_t batch, int32_t max_drafts, const int32_t *cu_num_scheduled_tokens,
+                                          const int32_t *num_draft_tokens, const int32_t *input_ids,
+                                          int32_t *cu_num_draft_tokens, int32_t *logits_indices,
+                                          int32_t *target_logits_indices, int32_t *bonus_logits_indices,
+                                          int32_t *draft_token_ids, int32_t *error, void *stream);
+
 /* Convert one linear weight W [rows, cols] (row-major, out_features x
  * in_features) into the layout the context's GEMM kernels stream.
  *   EAGLE3_BF16: cols % 128 == 0 (else EUNSUPPORTED); dst receives

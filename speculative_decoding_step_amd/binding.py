@@ -23,7 +23,8 @@ EXPORTS = [
     "eagle3_kv_bytes", "eagle3_workspace_bytes", "eagle3_create", "eagle3_destroy", "eagle3_verify_tree",
     "eagle3_draft_prefill", "eagle3_draft_tree", "eagle3_tree_from_logits", "eagle3_accept", "eagle3_compact_kv",
     "eagle3_sample", "eagle3_set_stream", "eagle3_status_string", "eagle3_device_status", "eagle3_profile", "eagle3_profile_read",
-    "eagle3_pack_linear", "eagle3_ttt_workspace_bytes", "eagle3_ttt_attention",
+    "eagle3_pack_linear", "eagle3_ttt_workspace_bytes", "eagle3_ttt_attention", "eagle3_paged_kv_bytes",
+    "eagle3_create_paged", "eagle3_set_draft_lengths", "eagle3_spec_decode_metadata",
 ]
 
 
@@ -59,6 +60,11 @@ class HeadWeights(C.Structure):
                  "w_down", "final_norm", "lm_head", "d2t")]
 
 
+class KvPages(C.Structure):
+    _fields_ = [("block_size", C.c_int32), ("n_blocks", C.c_int32), ("blocks_per_seq", C.c_int32),
+                ("block_table", C.c_void_p)]
+
+
 _lib = None
 P = C.c_void_p
 I32 = C.c_int32
@@ -77,6 +83,12 @@ def lib():
             "eagle3_create": [C.POINTER(Shape), C.POINTER(SpecCfg), C.POINTER(TargetWeights), C.POINTER(HeadWeights),
                               I32, I32, I32, P, C.c_size_t, P, P, P, C.POINTER(P)],
             "eagle3_destroy": [P],
+            "eagle3_paged_kv_bytes": [C.POINTER(Shape), I32, I32, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)],
+            "eagle3_create_paged": [C.POINTER(Shape), C.POINTER(SpecCfg), C.POINTER(TargetWeights),
+                                    C.POINTER(HeadWeights), I32, I32, C.POINTER(KvPages), P, C.c_size_t, P, P, P,
+                                    C.POINTER(P)],
+            "eagle3_set_draft_lengths": [P, P],
+            "eagle3_spec_decode_metadata": [I32, I32, P, P, P, P, P, P, P, P, P, P],
             "eagle3_pack_linear": [I32, P, P, I32, I32, P],
             "eagle3_verify_tree": [P, I32, I32, P, I32, P, P, P, I32, P, P, P, P],
             "eagle3_draft_prefill": [P, I32, I32, P, I32, P, P],
@@ -133,6 +145,36 @@ def eagle3_create(shape: Shape, cfg: SpecCfg, target: TargetWeights, head: HeadW
                                max_seq, workspace, workspace_bytes, kv_target, kv_draft, stream, C.byref(out)),
            "eagle3_create")
     return out.value
+
+
+def eagle3_paged_kv_bytes(shape: Shape, block_size: int, n_blocks: int):
+    t, d = C.c_size_t(), C.c_size_t()
+    _check(lib().eagle3_paged_kv_bytes(C.byref(shape), block_size, n_blocks, C.byref(t), C.byref(d)),
+           "eagle3_paged_kv_bytes")
+    return t.value, d.value
+
+
+def eagle3_create_paged(shape: Shape, cfg: SpecCfg, target: TargetWeights, head: HeadWeights, max_batch: int,
+                        max_rows: int, pages: KvPages, workspace: int, workspace_bytes: int, kv_target: int,
+                        kv_draft: int, stream: int) -> int:
+    out = P()
+    _check(lib().eagle3_create_paged(C.byref(shape), C.byref(cfg), C.byref(target), C.byref(head), max_batch,
+                                     max_rows, C.byref(pages), workspace, workspace_bytes, kv_target, kv_draft, stream,
+                                     C.byref(out)), "eagle3_create_paged")
+    return out.value
+
+
+def eagle3_set_draft_lengths(ctx, n_draft):
+    _check(lib().eagle3_set_draft_lengths(ctx, n_draft), "eagle3_set_draft_lengths")
+
+
+def eagle3_spec_decode_metadata(batch, max_drafts, cu_num_scheduled_tokens, num_draft_tokens, input_ids,
+                                cu_num_draft_tokens, logits_indices, target_logits_indices, bonus_logits_indices,
+                                draft_token_ids, error, stream):
+    _check(lib().eagle3_spec_decode_metadata(batch, max_drafts, cu_num_scheduled_tokens, num_draft_tokens, input_ids,
+                                             cu_num_draft_tokens, logits_indices, target_logits_indices,
+                                             bonus_logits_indices, draft_token_ids, error, stream),
+           "eagle3_spec_decode_metadata")
 
 
 def eagle3_destroy(ctx: int):

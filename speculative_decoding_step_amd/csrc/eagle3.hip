@@ -58,6 +58,9 @@ struct eagle3_ctx {
   hipStream_t st;
   char* kv_t;
   char* kv_d;
+  KvPages pg;                   // block table of a paged cache (pg.bt null: contiguous)
+  size_t kv_us, kv_hs, kv_le;   // unit stride, head stride, elements per layer's K (or V) array
+  const int* ndraft = nullptr;  // per-request draft lengths (device, [max_batch]) or null
   // workspace
   int* status;
   double* inv_freq;
@@ -194,16 +197,19 @@ eagle3_status check_shape(const eagle3_shape* s, const eagle3_spec_cfg* c) {
 
 __global__ void k_verify_meta(int batch, int seq_begin, int n_rows, const int* __restrict__ seq_lens,
                               const int* __restrict__ tokens, const int* __restrict__ pos_in,
-                              const uint64_t* __restrict__ mask_in, int S_cap, RowMeta rm, int* __restrict__ rtok,
-                              int* __restrict__ gidx, int* status) {
+                              const uint64_t* __restrict__ mask_in, int S_cap, const int* __restrict__ ndraft,
+                              RowMeta rm, int* __restrict__ rtok, int* __restrict__ gidx, int* status) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= batch * n_rows) return;
   const int b = r / n_rows, i = r % n_rows;
   const int P = seq_lens[b];
   const int slot = P + i;
-  const bool ok = P >= 0 && P + n_rows <= S_cap;
+  // with per-request draft lengths, rows of a draft (a masked verify) past the request's first ndraft nodes take
+  // no part (no K/V, no keys); a prefill (no mask) keeps every row
+  const int nr = ndraft && mask_in ? min(max(ndraft[seq_begin + b], 0), n_rows - 1) + 1 : n_rows;
+  const bool ok = P >= 0 && P + nr <= S_cap;
   if (!ok && i == 0) raise_flag(status, E3_DEV_KV_OVERFLOW);
-  rm.seq[r] = ok ? seq_begin + b : -1;
+  rm.seq[r] = ok && i < nr ? seq_begin + b : -1;
   rm.pos[r] = pos_in ? pos_in[r] : slot;
   rm.slot[r] = slot;
   rm.lim[r] = mask_in ? P : slot + 1;
@@ -367,15 +373,14 @@ void run_attention(eagle3_ctx* c, const void* kc, const void* vc, const RowMeta&
   const eagle3_shape& s = c->sh;
   ProfRec rec{};
   prof_begin(c, EAGLE3_PROF_ATTN, 0.0, 0.0, &rec);
-  attention(c->bf16, c->qbuf, kc, vc, (size_t)s.n_kv_heads * c->S_cap * s.head_dim, (size_t)c->S_cap * s.head_dim, rm,
-            R, rps, s.n_heads, s.n_kv_heads, s.head_dim, c->S_cap, c->o_part, c->ml_part, c->att_splits, c->abuf, c->st);
+  attention(c->bf16, c->qbuf, kc, vc, c->kv_us, c->kv_hs, c->pg, rm, R, rps, s.n_heads, s.n_kv_heads, s.head_dim, c->S_cap, c->o_part, c->ml_part, c->att_splits, c->abuf, c->st);
   prof_end(c, &rec);
 }
 
 char* kv_layer(eagle3_ctx* c, char* base, int l, int which) {
   const eagle3_shape& s = c->sh;
-  const size_t blk = (size_t)c->B * s.n_kv_heads * c->S_cap * s.head_dim * c->esz;
-  return base + ((size_t)l * 2 + which) * blk;
+  (void)s;
+  return base + ((size_t)l * 2 + which) * c->kv_le * c->esz;
 }
 
 // Target pass over R rows whose metadata is in c->rm and tokens in c->rtok.
@@ -413,8 +418,7 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
     char* kc = kv_layer(c, c->kv_t, l, 0);
     char* vc = kv_layer(c, c->kv_t, l, 1);
     rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, c->rm, c->inv_freq, c->qbuf, kc, vc,
-            (size_t)s.n_kv_heads * c->S_cap * s.head_dim, (size_t)c->S_cap * s.head_dim, s.n_heads, s.n_kv_heads,
-            s.head_dim, st);
+            c->kv_us, c->kv_hs, c->pg, s.n_heads, s.n_kv_heads, s.head_dim, c->status, st);
     run_attention(c, kc, vc, c->rm, R, rps);
     S = run_gemm(c, c->abuf, R, qdim, make_segs(L.wo, d));
     add_rmsnorm(bf, c->xres, c->part, S, (size_t)R * d, d, L.ffn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
@@ -462,8 +466,7 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
   char* kc = kv_layer(c, c->kv_d, 0, 0);
   char* vc = kv_layer(c, c->kv_d, 0, 1);
   rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, rm, c->inv_freq, c->qbuf, kc, vc,
-          (size_t)s.n_kv_heads * c->S_cap * s.head_dim, (size_t)c->S_cap * s.head_dim, s.n_heads, s.n_kv_heads,
-          s.head_dim, st);
+          c->kv_us, c->kv_hs, c->pg, s.n_heads, s.n_kv_heads, s.head_dim, c->status, st);
   run_attention(c, kc, vc, rm, R, rps);
   S = run_gemm(c, c->abuf, R, qdim, make_segs(H.wo, d));
   add_rmsnorm(bf, x, c->part, S, (size_t)R * d, d, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
@@ -604,9 +607,22 @@ eagle3_status eagle3_workspace_bytes(const eagle3_shape* s, const eagle3_spec_cf
   return EAGLE3_OK;
 }
 
-eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, const eagle3_target_weights* tw,
-                            const eagle3_head_weights* hw, int32_t max_batch, int32_t max_rows, int32_t max_seq,
-                            void* ws, size_t ws_bytes, void* kv_t, void* kv_d, void* stream, eagle3_ctx** out) {
+eagle3_status eagle3_paged_kv_bytes(const eagle3_shape* s, int32_t block_size, int32_t n_blocks, size_t* tb,
+                                    size_t* db) {
+  if (!s || !tb || !db || block_size < 64 || (block_size & (block_size - 1)) || n_blocks < 1) return EAGLE3_EINVAL;
+  const size_t es = s->dtype == EAGLE3_BF16 ? 2 : 4;
+  const size_t per = (size_t)n_blocks * s->n_kv_heads * block_size * s->head_dim * es;
+  *tb = (size_t)s->n_layers * 2 * per;
+  *db = 2 * per;
+  return EAGLE3_OK;
+}
+
+namespace {
+
+eagle3_status create_impl(const eagle3_shape* s, const eagle3_spec_cfg* cfg, const eagle3_target_weights* tw,
+                          const eagle3_head_weights* hw, int32_t max_batch, int32_t max_rows, int32_t max_seq,
+                          const eagle3_kv_pages* pages, void* ws, size_t ws_bytes, void* kv_t, void* kv_d,
+                          void* stream, eagle3_ctx** out) {
   eagle3_status e = check_shape(s, cfg);
   if (e) return e;
   if (!tw || !hw || !out || !ws || !kv_t || !kv_d || !tw->layers || max_batch < 1 || max_rows < 1 || max_seq < 1)
@@ -642,6 +658,19 @@ eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, c
   c->st = (hipStream_t)stream;
   c->kv_t = (char*)kv_t;
   c->kv_d = (char*)kv_d;
+  const size_t hd = s->head_dim, Hkv = s->n_kv_heads;
+  if (pages) {
+    int lbs = 0;
+    while ((1 << lbs) < pages->block_size) ++lbs;
+    c->pg = KvPages{pages->block_table, pages->blocks_per_seq, lbs, pages->n_blocks};
+    c->kv_us = Hkv * pages->block_size * hd;
+    c->kv_hs = (size_t)pages->block_size * hd;
+    c->kv_le = (size_t)pages->n_blocks * c->kv_us;
+  } else {
+    c->kv_us = Hkv * max_seq * hd;
+    c->kv_hs = (size_t)max_seq * hd;
+    c->kv_le = (size_t)max_batch * c->kv_us;
+  }
   const size_t need = carve(c, (char*)ws);
   if (ws_bytes < need) {
     delete c;
@@ -666,6 +695,100 @@ eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, c
   }
   *out = c;
   return EAGLE3_OK;
+}
+
+}  // namespace
+
+eagle3_status eagle3_create(const eagle3_shape* s, const eagle3_spec_cfg* cfg, const eagle3_target_weights* tw,
+                            const eagle3_head_weights* hw, int32_t max_batch, int32_t max_rows, int32_t max_seq,
+                            void* ws, size_t ws_bytes, void* kv_t, void* kv_d, void* stream, eagle3_ctx** out) {
+  return create_impl(s, cfg, tw, hw, max_batch, max_rows, max_seq, nullptr, ws, ws_bytes, kv_t, kv_d, stream, out);
+}
+
+eagle3_status eagle3_create_paged(const eagle3_shape* s, const eagle3_spec_cfg* cfg, const eagle3_target_weights* tw,
+                                  const eagle3_head_weights* hw, int32_t max_batch, int32_t max_rows,
+                                  const eagle3_kv_pages* pages, void* ws, size_t ws_bytes, void* kv_t, void* kv_d,
+                                  void* stream, eagle3_ctx** out) {
+  if (!pages || !pages->block_table || pages->block_size < 64 || (pages->block_size & (pages->block_size - 1)) ||
+      pages->n_blocks < 1 || pages->blocks_per_seq < 1)
+    return EAGLE3_EINVAL;
+  const long long cap = (long long)pages->blocks_per_seq * pages->block_size;
+  if (cap > (1ll << 30)) return EAGLE3_EUNSUPPORTED;
+  return create_impl(s, cfg, tw, hw, max_batch, max_rows, (int32_t)cap, pages, ws, ws_bytes, kv_t, kv_d, stream, out);
+}
+
+eagle3_status eagle3_set_draft_lengths(eagle3_ctx* c, const int32_t* n_draft) {
+  if (!c) return EAGLE3_EINVAL;
+  c->ndraft = n_draft;
+  return EAGLE3_OK;
+}
+
+// One workgroup: request b's drafts nd' = nd clamped into [0, scheduled - 1]; an exclusive scan of nd' over the
+// batch (in chunks of the block, carrying the running total) places every request's entries.
+__global__ __launch_bounds__(1024) void k_spec_meta(int batch, int max_drafts, const int* __restrict__ cu,
+                                                    const int* __restrict__ nd_in, const int* __restrict__ ids,
+                                                    int* __restrict__ cu_nd, int* __restrict__ li, int* __restrict__ tli,
+                                                    int* __restrict__ bli, int* __restrict__ dti, int* __restrict__ err) {
+  __shared__ int scan[1024];
+  __shared__ int s_carry, s_bad;
+  const int tid = threadIdx.x;
+  const int total = cu[batch - 1];  // flat positions (input_ids entries)
+  if (tid == 0) {
+    s_carry = 0;
+    s_bad = 0;
+  }
+  for (int base = 0; base < batch; base += 1024) {
+    __syncthreads();
+    const int b = base + tid;
+    int nd = 0, end = 0;
+    bool bad = false;
+    if (b < batch) {
+      end = cu[b];
+      const int sched = end - (b ? cu[b - 1] : 0);
+      const int want = nd_in[b];
+      nd = max(0, min(want, sched - 1));
+      bad = nd != want || sched < 1;
+    }
+    scan[tid] = nd;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan
+      const int v = tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int carry = s_carry;
+    if (b < batch) {
+      const int incl = carry + scan[tid], excl = incl - nd;
+      const int first = excl + b;  // entries of logits_indices before request b
+      cu_nd[b] = incl;
+      bli[b] = first + nd;
+      for (int t = 0; t <= nd; ++t)
+        if (first + t < batch + max_drafts) li[first + t] = end - nd - 1 + t;
+      for (int t = 0; t < nd; ++t)
+        if (excl + t < max_drafts) {
+          tli[excl + t] = first + t;
+          const int src = end - nd + t;  // inside [0, total) unless cu is not increasing (flagged)
+          if (dti) dti[excl + t] = src >= 0 && src < total ? ids[src] : -1;
+        }
+      bad = bad || incl > max_drafts;
+    }
+    if (bad) s_bad = 1;  // every writer stores the same value
+    __syncthreads();
+    if (tid == 1023) s_carry = carry + scan[1023];
+  }
+  __syncthreads();
+  if (tid == 0 && err) err[0] = s_bad;
+}
+
+eagle3_status eagle3_spec_decode_metadata(int32_t batch, int32_t max_drafts, const int32_t* cu, const int32_t* nd,
+                                          const int32_t* ids, int32_t* cu_nd, int32_t* li, int32_t* tli, int32_t* bli,
+                                          int32_t* dti, int32_t* err, void* stream) {
+  if (batch < 1 || max_drafts < 0 || !cu || !nd || !cu_nd || !li || !bli || (max_drafts > 0 && !tli) ||
+      (dti && !ids))
+    return EAGLE3_EINVAL;
+  k_spec_meta<<<1, 1024, 0, (hipStream_t)stream>>>(batch, max_drafts, cu, nd, ids, cu_nd, li, tli, bli, dti, err);
+  return hipGetLastError() == hipSuccess ? EAGLE3_OK : EAGLE3_EHIP;
 }
 
 eagle3_status eagle3_pack_linear(int32_t dtype, const void* src, void* dst, int32_t rows, int32_t cols,
@@ -701,8 +824,8 @@ eagle3_status eagle3_verify_tree(eagle3_ctx* c, int32_t seq_begin, int32_t batch
   if (mask && n_rows > 64) return EAGLE3_EUNSUPPORTED;
   if (lm_mode < EAGLE3_LM_ALL || lm_mode > EAGLE3_LM_NONE) return EAGLE3_EINVAL;
   const int R = batch * n_rows;
-  k_verify_meta<<<nb(R, 128), 128, 0, c->st>>>(batch, seq_begin, n_rows, seq_lens, tokens, pos, mask, c->S_cap, c->rm,
-                                                c->rtok, c->gidx, c->status);
+  k_verify_meta<<<nb(R, 128), 128, 0, c->st>>>(batch, seq_begin, n_rows, seq_lens, tokens, pos, mask, c->S_cap,
+                                                c->ndraft, c->rm, c->rtok, c->gidx, c->status);
   target_forward(c, R, n_rows, aux, lm_mode, batch, logits, argmax, margin);
   return last_error();
 }
@@ -775,8 +898,8 @@ eagle3_status eagle3_accept(eagle3_ctx* c, int32_t batch, int32_t n_rows, const 
   if (batch > c->B || n_rows > 64) return EAGLE3_ECAPACITY;
   if (c->cfg.mode == EAGLE3_GREEDY_TREE) {
     if (!parents || !argmax) return EAGLE3_EINVAL;
-    accept_greedy(batch, n_rows, c->cfg.depth, tokens, parents, argmax, path, path_len, next_root, emitted, c->status,
-                  c->st);
+    accept_greedy(batch, n_rows, c->cfg.depth, tokens, parents, argmax, path, path_len, next_root, emitted, c->ndraft,
+                  c->status, c->st);
   } else if (c->cfg.mode == EAGLE3_SAMPLE_TREE) {
     if (!parents || !logits || !uniforms) return EAGLE3_EINVAL;
     if ((size_t)batch * n_rows > (size_t)c->R) return EAGLE3_ECAPACITY;
@@ -784,7 +907,7 @@ eagle3_status eagle3_accept(eagle3_ctx* c, int32_t batch, int32_t n_rows, const 
     topk_lse(logits, batch * n_rows, V, V, 1, c->cfg.temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum,
              c->tk_ids, c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
     accept_tree(batch, n_rows, V, c->cfg.topk, c->cfg.depth, tokens, parents, logits, c->tk_lse64, c->tk_wsum,
-                c->cfg.temperature, uniforms, path, path_len, next_root, emitted, c->status, c->st);
+                c->cfg.temperature, uniforms, path, path_len, next_root, emitted, c->ndraft, c->status, c->st);
   } else {
     const int K = c->cfg.depth;
     if (n_rows != K + 1 || !logits || !q || !uniforms) return EAGLE3_EINVAL;
@@ -793,7 +916,7 @@ eagle3_status eagle3_accept(eagle3_ctx* c, int32_t batch, int32_t n_rows, const 
     topk_lse(logits, batch * n_rows, V, V, 1, c->cfg.temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum,
              c->tk_ids, c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
     accept_chain(batch, K, V, tokens, logits, c->tk_lse64, c->cfg.temperature, q, uniforms, path, path_len, next_root,
-                 emitted, c->acc_sel, c->tk_wsum, c->st);
+                 emitted, c->acc_sel, c->tk_wsum, c->ndraft, c->st);
   }
   return last_error();
 }
@@ -806,8 +929,8 @@ eagle3_status eagle3_compact_kv(eagle3_ctx* c, int32_t batch, int32_t* seq_lens,
   if (batch < 1 || batch > c->B || n_rows < 1 || n_rows > 64) return EAGLE3_ECAPACITY;
   const eagle3_shape& s = c->sh;
   const int maxp = c->cfg.depth + 1;
-  compact_kv(c->bf16, batch, seq_lens, path, path_len, maxp, n_rows, c->kv_t, s.n_layers, c->B, s.n_kv_heads, c->S_cap,
-             s.head_dim, c->status, c->st);
+  compact_kv(c->bf16, batch, seq_lens, path, path_len, maxp, n_rows, c->kv_t, s.n_layers, c->kv_le, c->kv_us, c->kv_hs,
+             c->pg, s.n_kv_heads, c->S_cap, s.head_dim, c->status, c->st);
   compact_finish(c->bf16, batch, seq_lens, n_rows, maxp, path, path_len, tokens, next_root, aux_tree, 3 * s.d_model,
                  aux_new, next_tok, new_len, c->st);
   return last_error();

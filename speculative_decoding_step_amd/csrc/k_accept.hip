@@ -27,6 +27,12 @@ namespace e3 {
 
 static inline unsigned nblk(size_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
+// Rows of sequence b's tree that take part in acceptance: the root and its
+// first n_draft[b] nodes (all n_rows without per-request draft lengths).
+E3_DEV int draft_rows(const int* ndraft, int b, int n_rows) {
+  return ndraft ? min(max(ndraft[b], 0), n_rows - 1) + 1 : n_rows;
+}
+
 // One wave per sequence, lane i holding tree row i (n_rows <= 64): the walk
 // reads the current node's argmax as a scalar and finds the matching child
 // with a ballot (the lowest such index).
@@ -34,9 +40,9 @@ __global__ __launch_bounds__(64) void k_accept_greedy(int batch, int n_rows, int
                                                       const int* __restrict__ parents, const int* __restrict__ argmax,
                                                       int* __restrict__ path, int* __restrict__ path_len,
                                                       int* __restrict__ next_root, int* __restrict__ emitted,
-                                                      int* status) {
+                                                      const int* __restrict__ ndraft, int* status) {
   const int b = blockIdx.x, lane = threadIdx.x;
-  const bool in = lane < n_rows;
+  const bool in = lane < draft_rows(ndraft, b, n_rows);
   const size_t rb = (size_t)b * n_rows;
   const int tk = in ? tokens[rb + lane] : -1;
   const int pa = in ? parents[rb + lane] : -2;
@@ -81,14 +87,14 @@ __global__ __launch_bounds__(64) void k_chain_decide(int K, int V, const int* __
                                                      const float* __restrict__ logits,
                                                      const double* __restrict__ lse64, double temp,
                                                      const float* __restrict__ q, const float* __restrict__ uniforms,
-                                                     int* __restrict__ sel) {
+                                                     const int* __restrict__ ndraft, int* __restrict__ sel) {
   const int b = blockIdx.x;
   if (threadIdx.x != 0) return;
-  const int rows = K + 1;
+  const int rows = K + 1, Kb = draft_rows(ndraft, b, rows) - 1;  // this request's drafts
   const int* tk = tokens + (size_t)b * rows;
   const float* u = uniforms + (size_t)b * rows;
-  int n = K;
-  for (int i = 0; i < K; ++i) {
+  int n = Kb;
+  for (int i = 0; i < Kb; ++i) {
     const int t = tk[i + 1];
     const float p = sample_prob(logits + ((size_t)b * rows + i) * V, t, temp, lse64[(size_t)b * rows + i]);
     const float qq = q[((size_t)b * K + i) * V + t];
@@ -104,14 +110,15 @@ __global__ __launch_bounds__(64) void k_chain_decide(int K, int V, const int* __
 __global__ __launch_bounds__(256) void k_chain_slices(int K, int V, const float* __restrict__ logits,
                                                       const double* __restrict__ lse64, double temp,
                                                       const float* __restrict__ q, const int* __restrict__ sel, int ns,
+                                                      const int* __restrict__ ndraft,
                                                       unsigned long long* __restrict__ wsum_p,
                                                       unsigned long long* __restrict__ wsum_r) {
   __shared__ unsigned long long red[256];
   const int sl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int rows = K + 1, n = sel[b];
+  const int rows = K + 1, n = sel[b], Kb = draft_rows(ndraft, b, rows) - 1;
   const float* z = logits + ((size_t)b * rows + n) * V;
   const double l = lse64[(size_t)b * rows + n];
-  const float* qr = n < K ? q + ((size_t)b * K + n) * V : nullptr;
+  const float* qr = n < Kb ? q + ((size_t)b * K + n) * V : nullptr;  // a rejection: the residual's sums too
   const int v1 = min(V, (sl + 1) * SAMPLE_SLICE);
   unsigned long long ap = 0ull, ar = 0ull;
   for (int v = sl * SAMPLE_SLICE + tid; v < v1; v += 256) {
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(1024) void k_chain_pick(int K, int V, const int* __
                                                      const float* __restrict__ logits,
                                                      const double* __restrict__ lse64, double temp,
                                                      const float* __restrict__ q, const float* __restrict__ uniforms,
-                                                     const int* __restrict__ sel, int ns,
+                                                     const int* __restrict__ sel, int ns, const int* __restrict__ ndraft,
                                                      const unsigned long long* __restrict__ wsum_p,
                                                      const unsigned long long* __restrict__ wsum_r,
                                                      int* __restrict__ path, int* __restrict__ path_len,
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(1024) void k_chain_pick(int K, int V, const int* __
   __shared__ unsigned long long s_rin;
   __shared__ int s_slice, s_usep, pick;
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int rows = K + 1, n = sel[b];
+  const int rows = K + 1, n = sel[b], Kb = draft_rows(ndraft, b, rows) - 1;
   const int* tk = tokens + (size_t)b * rows;
   if (tid == 0) {
     unsigned long long Sp = 0ull, Sr = 0ull;
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(1024) void k_chain_pick(int K, int V, const int* __
       Sp += wsum_p[(size_t)b * ns + j];
       Sr += wsum_r[(size_t)b * ns + j];
     }
-    const bool use_p = n == K || Sr == 0ull;  // the bonus, or a residual that is all zero in fp32
+    const bool use_p = n == Kb || Sr == 0ull;  // the bonus, or a residual that is all zero in fp32
     const unsigned long long* ws = (use_p ? wsum_p : wsum_r) + (size_t)b * ns;
     const unsigned long long S = use_p ? Sp : Sr;
     const unsigned long long r = floor_u_times(S, uniform24(uniforms[(size_t)b * rows + K]));
@@ -235,7 +242,8 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
                                                       const unsigned long long* __restrict__ wsum, double temp,
                                                       const float* __restrict__ uniforms, int* __restrict__ path,
                                                       int* __restrict__ path_len, int* __restrict__ next_root,
-                                                      int* __restrict__ emitted, int* status) {
+                                                      int* __restrict__ emitted, const int* __restrict__ ndraft,
+                                                      int* status) {
   __shared__ unsigned long long scan[1024];
   __shared__ unsigned long long wkid[64], wsl[64];
   __shared__ int kid[64], rej[64], pathv[64], tk[64], pa[64];
@@ -244,8 +252,9 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
   __shared__ int s_node, s_len, s_nk, s_nrej, s_go, s_pick, s_slice;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int maxp = maxd + 1, nu = maxd * topk + 1;
+  const int nr = draft_rows(ndraft, b, n_rows);  // rows of this request's draft
   // the sequence's tree and uniforms, staged once (the walk below is sequential)
-  if (tid < n_rows) {
+  if (tid < nr) {
     const int t = tokens[(size_t)b * n_rows + tid], p = parents[(size_t)b * n_rows + tid];
     tk[tid] = t;
     pa[tid] = p;
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
     if (tid == 0) {
       int nk = 0;
       if (d < maxd)
-        for (int j = node + 1; j < n_rows; ++j)
+        for (int j = node + 1; j < nr; ++j)
           if (pa[j] == node) {
             if (nk < topk) kid[nk] = j;
             ++nk;
@@ -378,12 +387,14 @@ __global__ __launch_bounds__(1024) void k_accept_tree(int n_rows, int V, int top
   }
 }
 
-// grid (B, L*2*Hkv): per (sequence, layer, K|V, head) move path rows to slots P..P+n-1.
+// grid (B, L*2*Hkv): per (sequence, layer, K|V, head) move path rows to positions P..P+n-1 (through the
+// block table when the cache is paged; every source row is read before any is written).
 template <typename E>
 __global__ __launch_bounds__(128) void k_compact_kv(const int* __restrict__ seq_lens, const int* __restrict__ path,
                                                     const int* __restrict__ path_len, int maxp, int n_rows,
-                                                    E* __restrict__ kv,
-                                                    int max_batch, int Hkv, int S_cap, int hd, int* status) {
+                                                    E* __restrict__ kv, size_t layer_elems, size_t unit_stride,
+                                                    size_t head_stride, KvPages pg, int Hkv, int S_cap, int hd,
+                                                    int* status) {
   extern __shared__ unsigned char smem[];
   E* buf = (E*)smem;
   const int b = blockIdx.x, lh = blockIdx.y;
@@ -400,15 +411,20 @@ __global__ __launch_bounds__(128) void k_compact_kv(const int* __restrict__ seq_
     if (threadIdx.x == 0 && lh == 0) raise_flag(status, E3_DEV_KV_OVERFLOW);
     return;
   }
-  E* base = kv + ((((size_t)lkv * max_batch + b) * Hkv + g) * S_cap) * hd;
+  E* lay = kv + (size_t)lkv * layer_elems + (size_t)g * head_stride;
   for (int idx = threadIdx.x; idx < n * hd; idx += blockDim.x) {
     const int j = idx / hd, i = idx % hd;
-    buf[idx] = base[(size_t)(P + path[(size_t)b * maxp + j]) * hd + i];
+    const KvLoc a = kv_loc(pg, b, P + pb[j]);
+    buf[idx] = lay[(size_t)a.unit * unit_stride + (size_t)a.row * hd + i];
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < n * hd; idx += blockDim.x) {
     const int j = idx / hd, i = idx % hd;
-    base[(size_t)(P + j) * hd + i] = buf[idx];
+    const KvLoc a = kv_loc_w(pg, b, P + j);
+    if (a.unit >= 0)
+      lay[(size_t)a.unit * unit_stride + (size_t)a.row * hd + i] = buf[idx];
+    else if (i == 0 && lh == 0)
+      raise_flag(status, E3_DEV_KV_OVERFLOW);
   }
 }
 
@@ -460,42 +476,47 @@ __global__ __launch_bounds__(256) void k_compact_finish(int* __restrict__ seq_le
 }
 
 void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const int* parents, const int* argmax,
-                   int* path, int* path_len, int* next_root, int* emitted, int* status, hipStream_t st) {
+                   int* path, int* path_len, int* next_root, int* emitted, const int* ndraft, int* status,
+                   hipStream_t st) {
   k_accept_greedy<<<batch, 64, 0, st>>>(batch, n_rows, depth + 1, tokens, parents, argmax, path, path_len, next_root,
-                                        emitted, status);
+                                        emitted, ndraft, status);
 }
 
 void accept_tree(int batch, int n_rows, int V, int topk, int depth, const int* tokens, const int* parents,
                  const float* logits, const double* lse64, unsigned long long* wsum, float temperature,
-                 const float* uniforms, int* path, int* path_len, int* next_root, int* emitted, int* status,
-                 hipStream_t st) {
+                 const float* uniforms, int* path, int* path_len, int* next_root, int* emitted, const int* ndraft,
+                 int* status, hipStream_t st) {
   const int ns = sampler_slices(V);
   k_row_wsum<<<dim3(ns, batch * n_rows), 256, 0, st>>>(V, ns, logits, lse64, (double)temperature, wsum);
   k_accept_tree<<<batch, 1024, 0, st>>>(n_rows, V, topk, depth, ns, tokens, parents, logits, lse64, wsum,
-                                        (double)temperature, uniforms, path, path_len, next_root, emitted, status);
+                                        (double)temperature, uniforms, path, path_len, next_root, emitted, ndraft,
+                                        status);
 }
 
 void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,
                   float temperature, const float* q, const float* uniforms, int* path, int* path_len, int* next_root,
-                  int* emitted, int* sel, unsigned long long* wsum, hipStream_t st) {
+                  int* emitted, int* sel, unsigned long long* wsum, const int* ndraft, hipStream_t st) {
   const int ns = sampler_slices(V);
   const double T = temperature;
-  k_chain_decide<<<batch, 64, 0, st>>>(K, V, tokens, logits, lse64, T, q, uniforms, sel);
-  k_chain_slices<<<dim3(ns, batch), 256, 0, st>>>(K, V, logits, lse64, T, q, sel, ns, wsum,
+  k_chain_decide<<<batch, 64, 0, st>>>(K, V, tokens, logits, lse64, T, q, uniforms, ndraft, sel);
+  k_chain_slices<<<dim3(ns, batch), 256, 0, st>>>(K, V, logits, lse64, T, q, sel, ns, ndraft, wsum,
                                                   wsum + (size_t)batch * ns);
-  k_chain_pick<<<batch, 1024, 0, st>>>(K, V, tokens, logits, lse64, T, q, uniforms, sel, ns, wsum,
+  k_chain_pick<<<batch, 1024, 0, st>>>(K, V, tokens, logits, lse64, T, q, uniforms, sel, ns, ndraft, wsum,
                                        wsum + (size_t)batch * ns, path, path_len, next_root, emitted);
 }
 
-void compact_kv(bool bf16, int batch, const int* seq_lens, const int* path, const int* path_len, int maxp, int n_rows, void* kv,
-                int n_layers, int max_batch, int Hkv, int S_cap, int hd, int* status, hipStream_t st) {
+void compact_kv(bool bf16, int batch, const int* seq_lens, const int* path, const int* path_len, int maxp, int n_rows,
+                void* kv, int n_layers, size_t layer_elems, size_t unit_stride, size_t head_stride, const KvPages& pg,
+                int Hkv, int S_cap, int hd, int* status, hipStream_t st) {
   dim3 grid(batch, n_layers * 2 * Hkv);
   if (bf16)
-    k_compact_kv<uint16_t><<<grid, 128, maxp * hd * 2, st>>>(seq_lens, path, path_len, maxp, n_rows, (uint16_t*)kv, max_batch,
-                                                             Hkv, S_cap, hd, status);
+    k_compact_kv<uint16_t><<<grid, 128, maxp * hd * 2, st>>>(seq_lens, path, path_len, maxp, n_rows, (uint16_t*)kv,
+                                                             layer_elems, unit_stride, head_stride, pg, Hkv, S_cap,
+                                                             hd, status);
   else
-    k_compact_kv<uint32_t><<<grid, 128, maxp * hd * 4, st>>>(seq_lens, path, path_len, maxp, n_rows, (uint32_t*)kv, max_batch,
-                                                             Hkv, S_cap, hd, status);
+    k_compact_kv<uint32_t><<<grid, 128, maxp * hd * 4, st>>>(seq_lens, path, path_len, maxp, n_rows, (uint32_t*)kv,
+                                                             layer_elems, unit_stride, head_stride, pg, Hkv, S_cap,
+                                                             hd, status);
 }
 
 void compact_finish(bool bf16, int batch, int* seq_lens, int n_rows, int maxp, const int* path, const int* path_len,

@@ -32,8 +32,8 @@ E3_DEV bool visible(int j, int lim, int t0, uint64_t mask) {
 
 template <typename T>
 __global__ __launch_bounds__(64) void k_attn_partial(const T* __restrict__ q, const T* __restrict__ kc,
-                                                     const T* __restrict__ vc, size_t seq_stride, size_t head_stride,
-                                                     const int* __restrict__ rseq, const int* __restrict__ rlim,
+                                                     const T* __restrict__ vc, size_t unit_stride, size_t head_stride,
+                                                     KvPages pg, const int* __restrict__ rseq, const int* __restrict__ rlim,
                                                      const int* __restrict__ rt0, const uint64_t* __restrict__ rmask,
                                                      int R, int Hq, int Hkv, int hd, int S_cap, float scale,
                                                      float* __restrict__ o_part, float* __restrict__ ml_part) {
@@ -57,14 +57,18 @@ __global__ __launch_bounds__(64) void k_attn_partial(const T* __restrict__ q, co
   for (int i = lane; i < hd; i += 64) qs[i] = ld<T>(q, ((size_t)r * Hq + h) * hd + i);
   __syncthreads();
   const int g = h / (Hq / Hkv);
-  const T* kb = kc + (size_t)b * seq_stride + (size_t)g * head_stride;
-  const T* vb = vc + (size_t)b * seq_stride + (size_t)g * head_stride;
+  const T* kb = kc + (size_t)g * head_stride;
+  const T* vb = vc + (size_t)g * head_stride;
+  auto krow = [&](int j) {  // element offset of key j of sequence b
+    const KvLoc at = kv_loc(pg, b, j);
+    return (size_t)at.unit * unit_stride + (size_t)at.row * hd;
+  };
   float mloc = -INFINITY;
   for (int j = c0 + lane; j < c1; j += 64) {
     float sc = -INFINITY;
     if (visible(j, lim, t0, mask)) {
       float acc = 0.f;
-      const T* kr = kb + (size_t)j * hd;
+      const T* kr = kb + krow(j);
       for (int i = 0; i < hd; ++i) acc += qs[i] * ld<T>(kr, i);
       sc = acc * scale;
     }
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(64) void k_attn_partial(const T* __restrict__ q, co
   __syncthreads();
   for (int i = lane; i < hd; i += 64) {
     float acc = 0.f;
-    for (int j = c0; j < c1; ++j) acc += ps[j - c0] * ld<T>(vb, (size_t)j * hd + i);
+    for (int j = c0; j < c1; ++j) acc += ps[j - c0] * ld<T>(vb, krow(j) + i);
     op[i] = acc;
   }
   if (lane == 0) {
@@ -259,8 +263,8 @@ E3_DEV void attn_copy16(const void* sbase, unsigned voff, void* l) {
 
 template <int HD, int NW, int NST>
 __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-                                                       const bf16_t* __restrict__ vc, size_t seq_stride,
-                                                       size_t head_stride, const int* __restrict__ rseq,
+                                                       const bf16_t* __restrict__ vc, size_t unit_stride,
+                                                       size_t head_stride, KvPages pg, const int* __restrict__ rseq,
                                                        const int* __restrict__ rlim, const int* __restrict__ rt0,
                                                        const uint64_t* __restrict__ rmask, int R, int rps,
                                                        int qblocks, int Hq, int Hkv, int ns, int nwork, int S_cap,
@@ -324,8 +328,18 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   for (int o = 32; o > 0; o >>= 1) vis_min = min(vis_min, __shfl_xor(vis_min, o, 64));
   vis_min = __builtin_amdgcn_readfirstlane(vis_min);
 
-  const bf16_t* kb = kc + (size_t)cs * seq_stride + (size_t)g * head_stride;
-  const bf16_t* vb = vc + (size_t)cs * seq_stride + (size_t)g * head_stride;
+  // Tile kt's keys start at kb/vb + tile_off(kt): contiguous, the sequence's unit advanced by kt rows; paged, the
+  // block the table gives for kt (one scalar load per tile: a block holds whole 64-key tiles).
+  const bool paged = pg.bt != nullptr;
+  const size_t seq0 = paged ? 0 : (size_t)cs * unit_stride;
+  const bf16_t* kb = kc + seq0 + (size_t)g * head_stride;
+  const bf16_t* vb = vc + seq0 + (size_t)g * head_stride;
+  const int* btr = paged ? pg.bt + (size_t)cs * pg.stride : nullptr;
+  auto tile_off = [&](int kt) -> size_t {
+    if (!paged) return (size_t)kt * HD;
+    const int e = min(max(btr[kt >> pg.lbs], 0), pg.nblk - 1);
+    return (size_t)e * unit_stride + (size_t)(kt & ((1 << pg.lbs) - 1)) * HD;
+  };
   // this wave's copies of a tile: index f = w + NW i (i < PW), clamped to the last one; the source is a
   // wave-uniform base (K or V of this sequence and head, advanced by whole tiles) plus a per-lane offset
   const bf16_t* cbase[PW];
@@ -351,14 +365,15 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
     voff[i] = (unsigned)(key * HD + d0) * 2u;
   }
   auto issue = [&](bf16_t* stgp, int kt) {
+    const size_t to = tile_off(kt);
     if (kt + AKT <= c1) {  // whole tile inside the chunk
 #pragma unroll
-      for (int i = 0; i < PW; ++i) attn_copy16(cbase[i] + (size_t)kt * HD, voff[i], stgp + dst[i]);
+      for (int i = 0; i < PW; ++i) attn_copy16(cbase[i] + to, voff[i], stgp + dst[i]);
     } else {  // the chunk's last tile: rows past its end repeat its last key (finite data, masked out)
 #pragma unroll
       for (int i = 0; i < PW; ++i) {
         const int back = kt + ckey[i] - min(kt + ckey[i], c1 - 1);  // rows moved back, >= 0
-        attn_copy16(cbase[i] + (size_t)kt * HD, voff[i] - (unsigned)(back * HD * 2), stgp + dst[i]);
+        attn_copy16(cbase[i] + to, voff[i] - (unsigned)(back * HD * 2), stgp + dst[i]);
       }
     }
   };
@@ -495,10 +510,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
 
 template <int HD, int NST>
 void launch_attn(int nw, unsigned nblocks, hipStream_t st, const bf16_t* q, const bf16_t* kc, const bf16_t* vc,
-                 size_t seq_stride, size_t head_stride, const RowMeta& rm, int R, int rps, int qblocks, int Hq,
-                 int Hkv, int ns, int nwork, int key_bound, float scale, int chunk, float* o_part, float* ml_part) {
+                 size_t unit_stride, size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps,
+                 int qblocks, int Hq, int Hkv, int ns, int nwork, int key_bound, float scale, int chunk,
+                 float* o_part, float* ml_part) {
 #define E3_ATTN_LAUNCH(N)                                                                                             \
-  k_attn_mfma<HD, N, NST><<<nblocks, 64 * N, 0, st>>>(q, kc, vc, seq_stride, head_stride, rm.seq, rm.lim, rm.tail0,       \
+  k_attn_mfma<HD, N, NST><<<nblocks, 64 * N, 0, st>>>(q, kc, vc, unit_stride, head_stride, pg, rm.seq, rm.lim, rm.tail0, \
                                                  rm.mask, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, \
                                                  o_part, ml_part)
   switch (nw) {
@@ -513,8 +529,9 @@ void launch_attn(int nw, unsigned nblocks, hipStream_t st, const bf16_t* q, cons
 
 // The chunk partials of tree-masked attention (o_part / ml_part, chunk-major);
 // returns the number of key chunks written and their length.
-AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride,
-                              size_t head_stride, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd,
+AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride,
+                              size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv,
+                              int hd,
                               int key_bound, float* o_part, float* ml_part, int max_splits, hipStream_t st,
                               int chunk_override) {
   int ns = (key_bound + ATT_CHUNK - 1) / ATT_CHUNK;
@@ -538,32 +555,32 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
     const int nwork = (R / rps) * qblocks * Hkv * ns;
     const int nblocks = (nwork + 7) / 8 * 8;
     if (hd == 128)
-      launch_attn<128, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
-                          head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part,
+      launch_attn<128, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, unit_stride,
+                          head_stride, pg, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part,
                           ml_part);
     else
-      launch_attn<64, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
-                         head_stride, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part,
+      launch_attn<64, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, unit_stride,
+                         head_stride, pg, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part,
                          ml_part);
     return AttnSplits{ns, chunk};
   }
   dim3 grid(R, Hq, ns);
   if (bf16)
-    k_attn_partial<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, seq_stride,
-                                                head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, Hq, Hkv, hd,
+    k_attn_partial<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, unit_stride,
+                                                head_stride, pg, rm.seq, rm.lim, rm.tail0, rm.mask, R, Hq, Hkv, hd,
                                                 key_bound, scale, o_part, ml_part);
   else
-    k_attn_partial<float><<<grid, 64, 0, st>>>((const float*)q, (const float*)kc, (const float*)vc, seq_stride,
-                                               head_stride, rm.seq, rm.lim, rm.tail0, rm.mask, R, Hq, Hkv, hd, key_bound,
+    k_attn_partial<float><<<grid, 64, 0, st>>>((const float*)q, (const float*)kc, (const float*)vc, unit_stride,
+                                               head_stride, pg, rm.seq, rm.lim, rm.tail0, rm.mask, R, Hq, Hkv, hd, key_bound,
                                                scale, o_part, ml_part);
   return AttnSplits{ns, ATT_CHUNK};
 }
 
-void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride, size_t head_stride,
-               const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound, float* o_part,
-               float* ml_part, int max_splits, void* out, hipStream_t st) {
+void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride, size_t head_stride,
+               const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
+               float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st) {
   if (R <= 0) return;
-  const AttnSplits sp = attention_partials(bf16, q, kc, vc, seq_stride, head_stride, rm, R, rps, Hq, Hkv, hd,
+  const AttnSplits sp = attention_partials(bf16, q, kc, vc, unit_stride, head_stride, pg, rm, R, rps, Hq, Hkv, hd,
                                            key_bound, o_part, ml_part, max_splits, st, 0);
   if (bf16)
     combine<bf16_t>(o_part, ml_part, sp.ns, R, Hq, hd, rm, key_bound, sp.chunk, -1, (bf16_t*)out, st);
@@ -736,7 +753,7 @@ void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void*
   if (bf16 && (hd == 64 || hd == 128) && S <= TTT_SMAX && (Hq / Hkv) * S <= TTT_PAIRS) {
     // one key chunk spans all T native keys (the T rows already fill the chip), then the fused diagonal + merge
     const int chunk = (T + 63) / 64 * 64;
-    attention_partials(true, q, k0, v0, (size_t)Hkv * T * hd, (size_t)T * hd, rm, T, T, Hq, Hkv, hd, T, o_part,
+    attention_partials(true, q, k0, v0, (size_t)Hkv * T * hd, (size_t)T * hd, KvPages{}, rm, T, T, Hq, Hkv, hd, T, o_part,
                        ml_part, max_splits, st, chunk);
     if (hd == 128)
       k_ttt_diag_merge<128><<<dim3(T, Hkv), 64, 0, st>>>(T, S, Hq, Hkv, scale, (const bf16_t*)q, (const bf16_t*)ks,
@@ -747,7 +764,7 @@ void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void*
     return;
   }
   // native keys [Hkv][T][hd]: one "sequence" of T slots
-  const AttnSplits sp = attention_partials(bf16, q, k0, v0, (size_t)Hkv * T * hd, (size_t)T * hd, rm, T, T, Hq, Hkv,
+  const AttnSplits sp = attention_partials(bf16, q, k0, v0, (size_t)Hkv * T * hd, (size_t)T * hd, KvPages{}, rm, T, T, Hq, Hkv,
                                            hd, T, o_part, ml_part, max_splits, st, 0);
   const int extra = max_splits;  // a split index no key chunk uses
   if (bf16) {

@@ -265,16 +265,25 @@ __global__ __launch_bounds__(64) void k_rope_kv(const float* __restrict__ part, 
                                                 const int* __restrict__ rseq, const int* __restrict__ rpos,
                                                 const int* __restrict__ rslot, const double* __restrict__ inv_freq,
                                                 T* __restrict__ q_out, T* __restrict__ kc, T* __restrict__ vc,
-                                                size_t seq_stride, size_t head_stride, int Hq, int Hkv, int hd) {
+                                                size_t unit_stride, size_t head_stride, KvPages pg, int Hq, int Hkv,
+                                                int hd, int* status) {
   const int r = blockIdx.x, h = blockIdx.y;
-  const int b = rseq[r];
+  int b = rseq[r];
+  KvLoc at{0, 0};
+  if (h >= Hq && b >= 0) {  // K or V head: where the row's position lives
+    at = kv_loc_w(pg, b, rslot[r]);
+    if (at.unit < 0) {
+      if (threadIdx.x == 0 && h == Hq) raise_flag(status, E3_DEV_KV_OVERFLOW);
+      b = -1;
+    }
+  }
   const int ncol = (Hq + 2 * Hkv) * hd;
   const int half = hd / 2;
   const float* pr = part + (size_t)r * ncol + (size_t)h * hd;
   auto val = [&](int c) { return sum_splits(pr + c, S, sstride); };
   if (h >= Hq + Hkv) {  // V: copy
     if (b < 0) return;
-    T* vp = vc + (size_t)b * seq_stride + (size_t)(h - Hq - Hkv) * head_stride + (size_t)rslot[r] * hd;
+    T* vp = vc + (size_t)at.unit * unit_stride + (size_t)(h - Hq - Hkv) * head_stride + (size_t)at.row * hd;
     for (int i = threadIdx.x; i < hd; i += blockDim.x) st<T>(vp, i, val(i));
     return;
   }
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(64) void k_rope_kv(const float* __restrict__ part, 
       st<T>(qp, i, y1);
       st<T>(qp, i + half, y2);
     } else {
-      T* kp = kc + (size_t)b * seq_stride + (size_t)(h - Hq) * head_stride + (size_t)rslot[r] * hd;
+      T* kp = kc + (size_t)at.unit * unit_stride + (size_t)(h - Hq) * head_stride + (size_t)at.row * hd;
       st<T>(kp, i, y1);
       st<T>(kp, i + half, y2);
     }
@@ -301,16 +310,17 @@ __global__ __launch_bounds__(64) void k_rope_kv(const float* __restrict__ part, 
 }
 
 void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const RowMeta& rm, const double* inv_freq,
-             void* q_out, void* kc, void* vc, size_t seq_stride, size_t head_stride, int Hq, int Hkv, int hd,
-             hipStream_t st) {
+             void* q_out, void* kc, void* vc, size_t unit_stride, size_t head_stride, const KvPages& pg, int Hq,
+             int Hkv, int hd, int* status, hipStream_t st) {
   if (R <= 0) return;
   dim3 grid(R, Hq + 2 * Hkv);
   if (bf16)
     k_rope_kv<bf16_t><<<grid, 64, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, inv_freq, (bf16_t*)q_out,
-                                           (bf16_t*)kc, (bf16_t*)vc, seq_stride, head_stride, Hq, Hkv, hd);
+                                           (bf16_t*)kc, (bf16_t*)vc, unit_stride, head_stride, pg, Hq, Hkv, hd,
+                                           status);
   else
     k_rope_kv<float><<<grid, 64, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, inv_freq, (float*)q_out,
-                                          (float*)kc, (float*)vc, seq_stride, head_stride, Hq, Hkv, hd);
+                                          (float*)kc, (float*)vc, unit_stride, head_stride, pg, Hq, Hkv, hd, status);
 }
 
 // ------------------------------------------------------------- top-k + lse

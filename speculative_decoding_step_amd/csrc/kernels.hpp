@@ -73,6 +73,37 @@ void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, in
 void draft_input(bool bf16, const void* embed, const int* tokens, const float* x, const void* w_in,
                  const void* w_hid, void* out, int R, int d, int V, float eps, int* status, hipStream_t st);
 
+// KV cache addressing of one layer's K (or V) array: element (unit u, KV head
+// g, row r, dim i) sits at u * unit_stride + g * head_stride + r * hd + i.
+// Contiguous ([sequences][Hkv][S_cap][hd]): position pos of sequence b is unit
+// b, row pos.  Paged ([blocks][Hkv][2^lbs][hd]): it is unit bt[b * stride +
+// (pos >> lbs)], row pos & (2^lbs - 1) -- the block table's slot mapping.
+// Blocks hold at least 64 positions, so an attention key tile never straddles
+// two blocks.  Table entries outside [0, nblk) are never dereferenced: writers
+// drop the row and raise E3_DEV_KV_OVERFLOW, readers clamp (and read a wrong
+// but existing block).
+struct KvPages {
+  const int* bt = nullptr;  // block table [sequences, stride] (device); null = contiguous
+  int stride = 0;           // table entries per sequence
+  int lbs = 0;              // log2 of the block size (>= 6)
+  int nblk = 0;             // blocks in each pool
+};
+struct KvLoc {
+  int unit, row;
+};
+// Reader's view: entries clamped into the pool.
+__device__ __forceinline__ KvLoc kv_loc(const KvPages& pg, int seq, int pos) {
+  if (!pg.bt) return KvLoc{seq, pos};
+  const int e = pg.bt[(size_t)seq * pg.stride + (pos >> pg.lbs)];
+  return KvLoc{min(max(e, 0), pg.nblk - 1), pos & ((1 << pg.lbs) - 1)};
+}
+// Writer's view: unit -1 when the table entry is outside the pool.
+__device__ __forceinline__ KvLoc kv_loc_w(const KvPages& pg, int seq, int pos) {
+  if (!pg.bt) return KvLoc{seq, pos};
+  const int e = pg.bt[(size_t)seq * pg.stride + (pos >> pg.lbs)];
+  return KvLoc{e >= 0 && e < pg.nblk ? e : -1, pos & ((1 << pg.lbs) - 1)};
+}
+
 // Row metadata of one forward pass.
 struct RowMeta {
   int* seq;        // cache slot (sequence) of the row, -1 = padding row
@@ -84,18 +115,20 @@ struct RowMeta {
 };
 
 // Rotary embedding + KV write from the QKV partials [S][R][(Hq+2Hkv)*hd].
-// inv_freq: [hd/2] doubles theta^(-2i/hd).
+// inv_freq: [hd/2] doubles theta^(-2i/hd).  K/V of row r go to position
+// rm.slot[r] of sequence rm.seq[r] through pg (unit_stride / head_stride as in
+// KvPages); status receives E3_DEV_KV_OVERFLOW for a row whose block is invalid.
 void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const RowMeta& rm,
-             const double* inv_freq, void* q_out, void* kc, void* vc, size_t seq_stride, size_t head_stride,
-             int Hq, int Hkv, int hd, hipStream_t st);
+             const double* inv_freq, void* q_out, void* kc, void* vc, size_t unit_stride, size_t head_stride,
+             const KvPages& pg, int Hq, int Hkv, int hd, int* status, hipStream_t st);
 
 // Attention of rows over their visible keys, split over key chunks, then combined.
 // rps: rows per sequence (rows of one sequence are consecutive; R % rps == 0).
 struct AttnSplits {
   int ns, chunk;  // key chunks written, keys per chunk
 };
-AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride,
-                              size_t head_stride, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd,
+AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride,
+                              size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd,
                               int key_bound, float* o_part, float* ml_part, int max_splits, hipStream_t st,
                               int chunk_override);  // chunk_override > 0: keys per chunk (else the size policy)
 // Training-time-test attention: q, out [T, Hq, hd]; k0, v0 [Hkv, T, hd]; ks, vs [S, Hkv, T, hd]; ws of
@@ -103,8 +136,8 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
 size_t ttt_workspace_bytes(int T, int Hq, int hd);
 void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void* q, const void* k0, const void* v0,
                    const void* ks, const void* vs, void* out, void* ws, hipStream_t st);
-void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t seq_stride,
-               size_t head_stride, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
+void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride,
+               size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
                float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st);
 
 // Row-wise top-k + log-sum-exp over fp32 logits [R, ld] (first V columns).

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"
+
 namespace e3 {
 
 constexpr int TREE_CMAX = 1024;  // candidates per sequence: k + (D-1) k^2
@@ -68,21 +70,26 @@ void chain_finalize(int K, const int* roots, const int* seq_lens, int* chain_tok
                     hipStream_t st);
 
 // ------------------------------------------------------------ accept/compact
+// ndraft (nullable, [batch]): per-request draft lengths; only a request's first ndraft[b] nodes (plus the root)
+// take part, the chain's final draw keeps uniforms[b, K].
 void accept_greedy(int batch, int n_rows, int depth, const int* tokens, const int* parents, const int* argmax,
-                   int* path, int* path_len, int* next_root, int* emitted, int* status, hipStream_t st);
+                   int* path, int* path_len, int* next_root, int* emitted, const int* ndraft, int* status,
+                   hipStream_t st);
 // Tree rejection sampling: slice sums of the integer weights of every row (wsum holds
 // rows * sampler_slices(V) values), then one 1024-thread block per sequence walks the
 // tree (n_rows, topk <= 64).
 void accept_tree(int batch, int n_rows, int V, int topk, int depth, const int* tokens, const int* parents,
                  const float* logits, const double* lse64, unsigned long long* wsum, float temperature,
-                 const float* uniforms, int* path, int* path_len, int* next_root, int* emitted, int* status,
-                 hipStream_t st);
+                 const float* uniforms, int* path, int* path_len, int* next_root, int* emitted, const int* ndraft,
+                 int* status, hipStream_t st);
 // Chain acceptance: sel [batch] ints and wsum [2 * batch * sampler_slices(V)] are scratch.
 void accept_chain(int batch, int K, int V, const int* tokens, const float* logits, const double* lse64,
                   float temperature, const float* q, const float* uniforms, int* path, int* path_len, int* next_root,
-                  int* emitted, int* sel, unsigned long long* wsum, hipStream_t st);
+                  int* emitted, int* sel, unsigned long long* wsum, const int* ndraft, hipStream_t st);
+// kv: n_layers x (K, V) arrays of layer_elems elements each, addressed as in KvPages.
 void compact_kv(bool bf16, int batch, const int* seq_lens, const int* path, const int* path_len, int maxp,
-                int n_rows, void* kv, int n_layers, int max_batch, int Hkv, int S_cap, int hd, int* status, hipStream_t st);
+                int n_rows, void* kv, int n_layers, size_t layer_elems, size_t unit_stride, size_t head_stride,
+                const KvPages& pg, int Hkv, int S_cap, int hd, int* status, hipStream_t st);
 void compact_finish(bool bf16, int batch, int* seq_lens, int n_rows, int maxp, const int* path, const int* path_len,
                     const int* tokens, const int* next_root, const void* aux_tree, int aux_w, void* aux_new,
                     int* next_tok, int* new_len, hipStream_t st);

@@ -38,7 +38,10 @@ def _ptr(t):
 class Engine:
     def __init__(self, ms: configs.ModelShape, spec: Spec, batch: int, max_seq: int, target_seed: int,
                  head_seed: int, max_rows: int | None = None, device: str = "cuda", sigma: float = 0.02,
-                 prefill_chunk: int = 512, weights: dict | None = None):
+                 prefill_chunk: int = 512, weights: dict | None = None, block_size: int = 0, page_seed: int = 0):
+        """block_size > 0 makes the KV caches paged: pools of blocks of that many
+        positions, each sequence's blocks drawn from a seeded shuffle of the pool
+        (three spare blocks), so every K/V access goes through the block table."""
         if not torch.cuda.is_available():
             raise RuntimeError("the EAGLE-3 engine needs a ROCm GPU (gfx950)")
         self.ms, self.spec, self.B, self.max_seq = ms, spec, batch, max_seq
@@ -85,14 +88,30 @@ class Engine:
         self.hw = hw
 
         # ---- caches, workspace, context
-        kvt, kvd = B.eagle3_kv_bytes(self.shape, batch, max_seq)
+        self.block_size = block_size
+        if block_size:
+            bps = -(-max_seq // block_size)
+            max_seq = self.max_seq = bps * block_size
+            self.n_blocks = batch * bps + 3
+            ids = np.random.default_rng(page_seed).permutation(self.n_blocks)[:batch * bps]
+            self.block_table = torch.as_tensor(ids.reshape(batch, bps).astype(np.int32), device=self.dev)
+            self.pages = B.KvPages(block_size, self.n_blocks, bps, self.block_table.data_ptr())
+            kvt, kvd = B.eagle3_paged_kv_bytes(self.shape, block_size, self.n_blocks)
+        else:
+            kvt, kvd = B.eagle3_kv_bytes(self.shape, batch, max_seq)
         self.kv_target = torch.empty(kvt, dtype=torch.uint8, device=self.dev)
         self.kv_draft = torch.empty(kvd, dtype=torch.uint8, device=self.dev)
         wsb = B.eagle3_workspace_bytes(self.shape, self.cfg, batch, self.max_rows, max_seq)
         self.workspace = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
-        self.ctx = B.eagle3_create(self.shape, self.cfg, self.tw, self.hw, batch, self.max_rows, max_seq,
-                                   self.workspace.data_ptr(), wsb, self.kv_target.data_ptr(), self.kv_draft.data_ptr(),
-                                   self.stream.cuda_stream)
+        if block_size:
+            self.ctx = B.eagle3_create_paged(self.shape, self.cfg, self.tw, self.hw, batch, self.max_rows, self.pages,
+                                             self.workspace.data_ptr(), wsb, self.kv_target.data_ptr(),
+                                             self.kv_draft.data_ptr(), self.stream.cuda_stream)
+        else:
+            self.ctx = B.eagle3_create(self.shape, self.cfg, self.tw, self.hw, batch, self.max_rows, max_seq,
+                                       self.workspace.data_ptr(), wsb, self.kv_target.data_ptr(),
+                                       self.kv_draft.data_ptr(), self.stream.cuda_stream)
+        self.n_draft = None
 
         # ---- step state
         i32 = dict(dtype=torch.int32, device=self.dev)
@@ -152,6 +171,32 @@ class Engine:
 
     def device_status(self) -> int:
         return B.eagle3_device_status(self.ctx)
+
+    def set_draft_lengths(self, n_draft=None):
+        """Per-request draft lengths ([B] ints, read at every later step; None = the full budget)."""
+        if n_draft is None:
+            self.n_draft = None
+            B.eagle3_set_draft_lengths(self.ctx, None)
+            return
+        nd = torch.as_tensor(np.asarray(n_draft, dtype=np.int32), device=self.dev)
+        if self.n_draft is None:
+            self.n_draft = nd.clone()
+            B.eagle3_set_draft_lengths(self.ctx, self.n_draft.data_ptr())
+        else:
+            self.n_draft.copy_(nd)  # same buffer: a captured step sees the new lengths
+
+    def kv_logical(self, which: str = "target"):
+        """A cache as [L, 2, B, Hkv, max_seq, hd] in position order: a view of a
+        contiguous cache, a gather through the block table of a paged one."""
+        ms = self.ms
+        L = ms.n_layers if which == "target" else 1
+        buf = self.kv_target if which == "target" else self.kv_draft
+        if not self.block_size:
+            return buf.view(self.tdt).view(L, 2, self.B, ms.n_kv_heads, self.max_seq, ms.head_dim)
+        bs = self.block_size
+        pool = buf.view(self.tdt).view(L, 2, self.n_blocks, ms.n_kv_heads, bs, ms.head_dim)
+        g = pool[:, :, self.block_table.long()]                  # [L, 2, B, bps, Hkv, bs, hd]
+        return g.permute(0, 1, 2, 4, 3, 5, 6).reshape(L, 2, self.B, ms.n_kv_heads, self.max_seq, ms.head_dim)
 
     # ------------------------------------------------------------------ prefill
     def prefill(self, prompts, u_root=None):

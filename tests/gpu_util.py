@@ -21,9 +21,9 @@ def oracle_weights(ms, seed=11, sigma=0.02):
 
 
 def kv_view(eng: Engine):
-    """Target KV cache as [L, 2, B, Hkv, S, hd] (device tensor)."""
-    ms = eng.ms
-    return eng.kv_target.view(eng.tdt).view(ms.n_layers, 2, eng.B, ms.n_kv_heads, eng.max_seq, ms.head_dim)
+    """Target KV cache as [L, 2, B, Hkv, S, hd] in position order (device tensor; a
+    gathered copy when the cache is paged)."""
+    return eng.kv_logical("target")
 
 
 def logits_close(gpu, ref, dtype):
