@@ -39,7 +39,7 @@ def run_gpu(w, steps, warmup):
     t0 = time.time()
     prompts = [p for p in configs.prompts_np(w)]
     eng = Engine(w.shape, Spec.of(w), w.batch, max_seq_for(w, 2 * (steps + warmup)), w.target_seed, w.head_seed,
-                 prefill_chunk=512)
+                 prefill_chunk=512, block_size=w.block_size, page_seed=w.cid)
     print(f"[bench] weights + context ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     if eng.sampling:                             # seeded uniforms, fixed across the replays
         from speculative_decoding_step_amd import synth
@@ -401,7 +401,8 @@ def main():
         "dtype": w.shape.dtype,
         "data": "synthetic: seeded N(0,0.02) weights, uniform prompt ids",
         "config": {"workload": w.name, "batch": w.batch, "prompt_len": w.prompt_len, "tree_depth": w.depth,
-                   "topk": w.topk, "tree_nodes": w.n_nodes, "rows_per_step": rows},
+                   "topk": w.topk, "tree_nodes": w.n_nodes, "rows_per_step": rows,
+                   "kv_block_size": w.block_size or None},
         "roofline": roofline(w, prof, args.steps),
         "hbm_gbps_step": round(step_bytes(w) / (ms / 1e3) / 1e9, 1),
         "cpu_baseline": None,

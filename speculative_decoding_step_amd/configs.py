@@ -50,6 +50,7 @@ class Workload:
     draft_greedy: bool = False
     ragged_min: int = 0     # > 0: prompt lengths uniform in [ragged_min, prompt_len]
     max_len: int = 0        # > 0: sequences stop at this total length
+    block_size: int = 0     # > 0: paged KV caches of blocks of this many positions (shuffled over the pool)
 
     @property
     def rows(self):
@@ -87,6 +88,12 @@ WORKLOADS = {
     # the batch-1 tree with a 32,000-id draft vocabulary (draft-owned head, d2t)
     "llama8b_tree_b1_dv32k": Workload(7, "llama8b_tree_b1_dv32k", L8B_DV32K, "greedy_tree", 6, 10, 60, 1, 2048, 128),
 }
+# the batch-1 and batch-64 trees on paged KV caches of 64-position blocks (same seeds and prompts as the
+# contiguous workloads, so the lines compare directly)
+WORKLOADS["llama8b_tree_b1_paged"] = replace(WORKLOADS["llama8b_tree_b1"], name="llama8b_tree_b1_paged",
+                                             block_size=64)
+WORKLOADS["llama8b_tree_b64_paged"] = replace(WORKLOADS["llama8b_tree_b64"], name="llama8b_tree_b64_paged",
+                                              block_size=64)
 
 
 def scaled(w: Workload, **kw) -> Workload:

@@ -250,3 +250,62 @@ def test_8b_sampling_chain_b4_steps():
     for l in range(2):
         _close(chain_kv[l, 0].transpose(1, 0, 2), tk[l], ("chain K", l))
         _close(chain_kv[l, 1].transpose(1, 0, 2), tv[l], ("chain V", l))
+
+
+def _seq_kv(eng, s, P, layers):
+    """Target K/V of sequence s, positions [0, P), selected layers: [len(layers), 2, Hkv, P, hd]."""
+    ms = eng.ms
+    if not eng.block_size:
+        return eng.kv_target.view(eng.tdt).view(ms.n_layers, 2, eng.B, ms.n_kv_heads, eng.max_seq,
+                                                ms.head_dim)[layers, :, s, :, :P]
+    bs = eng.block_size
+    pool = eng.kv_target.view(eng.tdt).view(ms.n_layers, 2, eng.n_blocks, ms.n_kv_heads, bs, ms.head_dim)
+    blocks = eng.block_table[s, :(P + bs - 1) // bs].long()
+    g = pool[layers][:, :, blocks]                                   # [l, 2, nb, Hkv, bs, hd]
+    return g.permute(0, 1, 3, 2, 4, 5).reshape(len(layers), 2, ms.n_kv_heads, -1, ms.head_dim)[..., :P, :]
+
+
+def test_8b_batch64_paged_step_with_draft_lengths():
+    """The batch-64 ragged workload on a paged cache (64-position blocks shuffled over the
+    pool) with per-request draft lengths 0..16, against the same step on a contiguous
+    cache: trees, verify argmax, paths and next tokens bit-identical where both verify a
+    row; every path equals the greedy walk over the request's truncated tree; committed
+    K/V identical for the shortest, a middle and the longest sequence (all layers' first
+    and last)."""
+    w = configs.WORKLOADS["llama8b_tree_b64_paged"]
+    ms, Bn, n = w.shape, w.batch, w.rows
+    prompts = configs.prompts_np(w)
+    lens = np.array([len(p) for p in prompts])
+    print(f"\n[8B batch {Bn} paged, block {w.block_size}] prompt lengths {lens.min()}..{lens.max()}", flush=True)
+    a = Engine(ms, Spec.of(w), Bn, int(lens.max()) + 64, w.target_seed, w.head_seed, prefill_chunk=512)
+    b = Engine(ms, Spec.of(w), Bn, int(lens.max()) + 64, w.target_seed, w.head_seed, prefill_chunk=512,
+               weights=a.w, block_size=w.block_size, page_seed=w.cid)
+    nd = np.random.default_rng(13).integers(0, n, size=Bn)
+    nd[:4] = [0, n - 1, 1, 0]
+    for e in (a, b):
+        e.prefill(prompts)
+        e.set_draft_lengths(nd)
+        e.step()
+    torch.cuda.synchronize()
+    print("  prefill + one step on both caches done", flush=True)
+    assert a.device_status() == 0 and b.device_status() == 0
+    for name in ("tokens", "parents", "path", "path_len", "next_root", "seq_lens", "next_tok"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    am_a, am_b = a.argmax.view(Bn, n).cpu().numpy(), b.argmax.view(Bn, n).cpu().numpy()
+    tokens, parents = b.tokens.cpu().numpy(), b.parents.cpu().numpy()
+    path, plen = b.path.cpu().numpy(), b.path_len.cpu().numpy()
+    for s in range(Bn):
+        r = int(nd[s]) + 1
+        assert (am_a[s, :r] == am_b[s, :r]).all(), s
+        walk, nxt = greedy_walk(list(tokens[s, :r]), list(parents[s, :r]), list(am_b[s, :r]))
+        assert list(path[s, :plen[s]]) == walk and b.next_root[s].item() == nxt, s
+    order = np.argsort(lens)
+    layers = [0, ms.n_layers - 1]
+    for s in (int(order[0]), int(order[Bn // 2]), int(order[-1])):
+        P = int(b.seq_lens[s])
+        assert torch.equal(_seq_kv(a, s, P, layers), _seq_kv(b, s, P, layers)), s
+    print(f"  path lengths {np.bincount(plen)}; zero-draft requests emitted "
+          f"{sorted(set(plen[nd == 0].tolist()))} token(s)", flush=True)
+    assert (plen[nd == 0] == 1).all()
+    a.close()
+    b.close()
