@@ -329,15 +329,19 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   vis_min = __builtin_amdgcn_readfirstlane(vis_min);
 
   // Tile kt's keys start at kb/vb + tile_off(kt): contiguous, the sequence's unit advanced by kt rows; paged, the
-  // block the table gives for kt (one scalar load per tile: a block holds whole 64-key tiles).
+  // block the table gives for kt (a block holds whole 64-key tiles).  The chunk's block ids are loaded once, lane i
+  // holding tile i's (a chunk has at most 64 tiles), and each tile reads its id with readlane: no memory wait in
+  // the copy ring.
   const bool paged = pg.bt != nullptr;
   const size_t seq0 = paged ? 0 : (size_t)cs * unit_stride;
   const bf16_t* kb = kc + seq0 + (size_t)g * head_stride;
   const bf16_t* vb = vc + seq0 + (size_t)g * head_stride;
-  const int* btr = paged ? pg.bt + (size_t)cs * pg.stride : nullptr;
+  int vblk = 0;
+  if (paged && lane < ((c1 - c0 + AKT - 1) >> 6))
+    vblk = min(max(pg.bt[(size_t)cs * pg.stride + ((c0 + AKT * lane) >> pg.lbs)], 0), pg.nblk - 1);
   auto tile_off = [&](int kt) -> size_t {
     if (!paged) return (size_t)kt * HD;
-    const int e = min(max(btr[kt >> pg.lbs], 0), pg.nblk - 1);
+    const int e = __builtin_amdgcn_readlane(vblk, (kt - c0) >> 6);
     return (size_t)e * unit_stride + (size_t)(kt & ((1 << pg.lbs) - 1)) * HD;
   };
   // this wave's copies of a tile: index f = w + NW i (i < PW), clamped to the last one; the source is a
@@ -551,6 +555,9 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
                       : tiles256 >= 4096 ? 3 * ATT_CHUNK
                       : tiles256 >= 2048 ? 2 * ATT_CHUNK
                                          : ATT_CHUNK;
+    if (pg.bt && chunk > 64 * AKT) return attention_partials(bf16, q, kc, vc, unit_stride, head_stride, pg, rm, R,
+                                                            rps, Hq, Hkv, hd, key_bound, o_part, ml_part, max_splits,
+                                                            st, 64 * AKT);  // paged: at most 64 tiles per chunk
     ns = (key_bound + chunk - 1) / chunk;
     const int nwork = (R / rps) * qblocks * Hkv * ns;
     const int nblocks = (nwork + 7) / 8 * 8;
