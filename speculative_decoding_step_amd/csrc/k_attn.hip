@@ -261,7 +261,10 @@ E3_DEV void attn_copy16(const void* sbase, unsigned voff, void* l) {
                : "memory", "m0");
 }
 
-template <int HD, int NW, int NST>
+// TTT: training-time test.  The rows are the positions of one sequence; after the native keys, the S simulated
+// steps' diagonal keys of each row (dk / dv [S][Hkv][R][HD]) join the same softmax in the epilogue, and the
+// normalised output goes straight to tout [R][Hq][HD] (the launch must cover all keys in one chunk; no partials).
+template <int HD, int NW, int NST, bool TTT>
 __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
                                                        const bf16_t* __restrict__ vc, size_t unit_stride,
                                                        size_t head_stride, KvPages pg, const int* __restrict__ rseq,
@@ -269,7 +272,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
                                                        const uint64_t* __restrict__ rmask, int R, int rps,
                                                        int qblocks, int Hq, int Hkv, int ns, int nwork, int S_cap,
                                                        float scale, int chunk, float* __restrict__ o_part,
-                                                       float* __restrict__ ml_part) {
+                                                       float* __restrict__ ml_part, const bf16_t* __restrict__ dk,
+                                                       const bf16_t* __restrict__ dv, int nstep,
+                                                       bf16_t* __restrict__ tout) {
   constexpr int TILE = AKT * HD;               // bf16 elements of one K (or V) tile
   constexpr int NCP = 2 * TILE / 512;          // 1 KiB copies per tile: K fragments, then V block groups
   constexpr int PW = (NCP + NW - 1) / NW;      // copies per wave and tile
@@ -500,6 +505,54 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
 
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
+  if constexpr (TTT) {
+    // Each simulated step's diagonal key of the lane's position: the score from the lane's quarter of the query
+    // (the B operand: dims 32 kk + 8 lg ..) summed over the query's four lanes, then an online-softmax update of
+    // (m, lsum, O) with the matching value (the lane's output dims 16 b + 4 lg + r).  All lanes take part in
+    // the exchanges; lanes without a query read row `row` (a valid one) and store nothing.
+    for (int js = 0; js < nstep; ++js) {
+      const size_t base = (((size_t)js * Hkv + g) * R + row) * HD;
+      const bf16_t* kp = dk + base + 8 * lg;
+      float dot = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < HD / 32; ++kk) {
+        const u32x4 kv = *(const u32x4*)(kp + 32 * kk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dot = fmaf(__uint_as_float(qf[kk][e] << 16), __uint_as_float(kv[e] << 16), dot);
+          dot = fmaf(__uint_as_float(qf[kk][e] & 0xffff0000u), __uint_as_float(kv[e] & 0xffff0000u), dot);
+        }
+      }
+      dot += __shfl_xor(dot, 16, 64);
+      dot += __shfl_xor(dot, 32, 64);
+      const float sc = dot * qscale;  // log2 units, like m
+      const float mn = fmaxf(m, sc);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn), p = __builtin_amdgcn_exp2f(sc - mn);
+      m = mn;
+      lsum = fmaf(lsum, alpha, p);
+      const bf16_t* vp = dv + base + 4 * lg;
+#pragma unroll
+      for (int b = 0; b < HD / 16; ++b) {
+        const uint2 raw = *(const uint2*)(vp + 16 * b);
+        O[b][0] = fmaf(O[b][0], alpha, p * __uint_as_float(raw.x << 16));
+        O[b][1] = fmaf(O[b][1], alpha, p * __uint_as_float(raw.x & 0xffff0000u));
+        O[b][2] = fmaf(O[b][2], alpha, p * __uint_as_float(raw.y << 16));
+        O[b][3] = fmaf(O[b][3], alpha, p * __uint_as_float(raw.y & 0xffff0000u));
+      }
+    }
+    if (v < nq && ok) {
+      const float inv = 1.f / lsum;
+      bf16_t* op = tout + ((size_t)row * Hq + h) * HD + 4 * lg;
+#pragma unroll
+      for (int b = 0; b < HD / 16; ++b) {
+        uint2 w;
+        w.x = (uint32_t)f2bf(O[b][0] * inv) | ((uint32_t)f2bf(O[b][1] * inv) << 16);
+        w.y = (uint32_t)f2bf(O[b][2] * inv) | ((uint32_t)f2bf(O[b][3] * inv) << 16);
+        *(uint2*)(op + 16 * b) = w;
+      }
+    }
+    return;
+  }
   if (v < nq) {
     const size_t oi = ((size_t)sp * R + row) * Hq + h;
 #pragma unroll
@@ -512,15 +565,15 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   }
 }
 
-template <int HD, int NST>
+template <int HD, int NST, bool TTT>
 void launch_attn(int nw, unsigned nblocks, hipStream_t st, const bf16_t* q, const bf16_t* kc, const bf16_t* vc,
                  size_t unit_stride, size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps,
                  int qblocks, int Hq, int Hkv, int ns, int nwork, int key_bound, float scale, int chunk,
-                 float* o_part, float* ml_part) {
+                 float* o_part, float* ml_part, const bf16_t* dk, const bf16_t* dv, int nstep, bf16_t* tout) {
 #define E3_ATTN_LAUNCH(N)                                                                                             \
-  k_attn_mfma<HD, N, NST><<<nblocks, 64 * N, 0, st>>>(q, kc, vc, unit_stride, head_stride, pg, rm.seq, rm.lim, rm.tail0, \
-                                                 rm.mask, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, \
-                                                 o_part, ml_part)
+  k_attn_mfma<HD, N, NST, TTT><<<nblocks, 64 * N, 0, st>>>(q, kc, vc, unit_stride, head_stride, pg, rm.seq, rm.lim,   \
+                                                      rm.tail0, rm.mask, R, rps, qblocks, Hq, Hkv, ns, nwork,       \
+                                                      key_bound, scale, chunk, o_part, ml_part, dk, dv, nstep, tout)
   switch (nw) {
     case 4: E3_ATTN_LAUNCH(4); break;
     case 5: E3_ATTN_LAUNCH(5); break;
@@ -537,7 +590,7 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
                               size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv,
                               int hd,
                               int key_bound, float* o_part, float* ml_part, int max_splits, hipStream_t st,
-                              int chunk_override) {
+                              int chunk_override, const void* dk, const void* dv, int nstep, void* tout) {
   int ns = (key_bound + ATT_CHUNK - 1) / ATT_CHUNK;
   if (ns < 1) ns = 1;
   if (ns > max_splits) ns = max_splits;  // the workspace holds ceil(max_seq / chunk) splits
@@ -561,14 +614,21 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
     ns = (key_bound + chunk - 1) / chunk;
     const int nwork = (R / rps) * qblocks * Hkv * ns;
     const int nblocks = (nwork + 7) / 8 * 8;
-    if (hd == 128)
-      launch_attn<128, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, unit_stride,
-                          head_stride, pg, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part,
-                          ml_part);
-    else
-      launch_attn<64, 4>(nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, unit_stride,
-                         head_stride, pg, rm, R, rps, qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part,
-                         ml_part);
+#define E3_ATTN_ARGS                                                                                                \
+  nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, unit_stride, head_stride, pg, rm, R, rps,   \
+      qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part, ml_part, (const bf16_t*)dk, (const bf16_t*)dv,      \
+      nstep, (bf16_t*)tout
+    if (tout) {  // training-time test: diagonal keys merged in the epilogue, output written directly
+      if (hd == 128)
+        launch_attn<128, 4, true>(E3_ATTN_ARGS);
+      else
+        launch_attn<64, 4, true>(E3_ATTN_ARGS);
+    } else if (hd == 128) {
+      launch_attn<128, 4, false>(E3_ATTN_ARGS);
+    } else {
+      launch_attn<64, 4, false>(E3_ATTN_ARGS);
+    }
+#undef E3_ATTN_ARGS
     return AttnSplits{ns, chunk};
   }
   dim3 grid(R, Hq, ns);
@@ -601,9 +661,11 @@ void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t 
 // draft layer's forward_ttt): the native step's keys are attended causally,
 // each simulated step adds one key per position that only the query at that
 // position sees.  The causal part is the tree-masked attention above with row
-// i seeing keys [0, i] (lim = i + 1, no tree part); the S diagonal scores of
-// every (position, head) form one more online-softmax partial (k_ttt_diag),
-// merged by the combine kernel with the chunk partials.
+// i seeing keys [0, i] (lim = i + 1, no tree part).  For bf16 at head sizes 64
+// and 128 one key chunk covers every native key and the attention kernel's
+// epilogue folds in the S diagonal keys (TTT = true).  Otherwise the S
+// diagonal scores of every (position, head) form one more online-softmax
+// partial (k_ttt_diag), merged by the combine kernel with the chunk partials.
 
 // rows i < T: one sequence, causal over the native keys
 __global__ void k_ttt_meta(int T, RowMeta rm) {
@@ -654,80 +716,6 @@ __global__ __launch_bounds__(64) void k_ttt_diag(int Tn, int S, int Hq, int Hkv,
   }
 }
 
-// Fused form (one key chunk covers every native key): one wave per (position
-// i, KV head g) handles the G query heads of the group (G * S <= 32).  Two
-// lanes per (head, step) pair each take half of the q . k dot product
-// (16-byte loads, one shuffle to join the halves), the scores go through LDS
-// to every lane, and each lane then folds them into the chunk's partial
-// (m, l, o) of every head for its HD/64 dims and writes the normalised output.
-constexpr int TTT_SMAX = 16, TTT_PAIRS = 32;
-template <int HD>
-__global__ __launch_bounds__(64) void k_ttt_diag_merge(int Tn, int S, int Hq, int Hkv, float scale,
-                                                       const bf16_t* __restrict__ q, const bf16_t* __restrict__ ks,
-                                                       const bf16_t* __restrict__ vs,
-                                                       const float* __restrict__ o_part,
-                                                       const float* __restrict__ ml_part,
-                                                       bf16_t* __restrict__ out) {
-  constexpr int PL = HD / 64;     // output dims per lane: lane + 64 c
-  constexpr int HALF = HD / 2;    // dot-product elements per lane
-  __shared__ float sc[TTT_PAIRS];
-  const int i = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
-  const int G = Hq / Hkv;
-  const int pair = lane >> 1, half = lane & 1;
-  const int hp = pair / S, jp = pair % S;
-  const bool pv = pair < G * S;
-  // scores: lane pair (hp, jp), dims [half * HALF, (half + 1) * HALF)
-  float d = 0.f;
-  if (pv) {
-    const u32x4* qp = (const u32x4*)(q + ((size_t)i * Hq + g * G + hp) * HD + half * HALF);
-    const u32x4* kp = (const u32x4*)(ks + (((size_t)jp * Hkv + g) * Tn + i) * HD + half * HALF);
-    u32x4 qa[HALF / 8], ka[HALF / 8];
-#pragma unroll
-    for (int c = 0; c < HALF / 8; ++c) {
-      qa[c] = qp[c];
-      ka[c] = kp[c];
-    }
-#pragma unroll
-    for (int c = 0; c < HALF / 8; ++c) {
-      const bf16_t* a = (const bf16_t*)&qa[c];
-      const bf16_t* b = (const bf16_t*)&ka[c];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d += bf2f(a[e]) * bf2f(b[e]);
-    }
-  }
-  d += __shfl_xor(d, 1, 64);
-  if (pv && half == 0) sc[pair] = d * scale;
-  // the values of this lane's output dims, and the heads' partials
-  float vr[TTT_SMAX][PL];
-#pragma unroll
-  for (int j = 0; j < TTT_SMAX; ++j)
-#pragma unroll
-    for (int c = 0; c < PL; ++c)
-      vr[j][c] = j < S ? bf2f(vs[(((size_t)j * Hkv + g) * Tn + i) * HD + c * 64 + lane]) : 0.f;
-  __syncthreads();
-  for (int hl = 0; hl < G; ++hl) {
-    const size_t oi = (size_t)i * Hq + g * G + hl;  // chunk 0 of the partials
-    const float m0 = ml_part[2 * oi], l0 = ml_part[2 * oi + 1];
-    float M = m0;  // natural-log units of the scaled score
-    for (int j = 0; j < S; ++j) M = fmaxf(M, sc[hl * S + j]);
-    const float e0 = expf(m0 - M);
-    float den = l0 * e0;
-    float acc[PL];
-#pragma unroll
-    for (int c = 0; c < PL; ++c) acc[c] = o_part[oi * HD + c * 64 + lane] * e0;
-#pragma unroll
-    for (int j = 0; j < TTT_SMAX; ++j) {
-      if (j >= S) break;
-      const float p = expf(sc[hl * S + j] - M);
-      den += p;
-#pragma unroll
-      for (int c = 0; c < PL; ++c) acc[c] += p * vr[j][c];
-    }
-#pragma unroll
-    for (int c = 0; c < PL; ++c) out[oi * HD + c * 64 + lane] = f2bf(acc[c] / den);
-  }
-}
-
 size_t ttt_workspace_bytes(int T, int Hq, int hd) {
   const size_t splits = (size_t)(T + ATT_CHUNK - 1) / ATT_CHUNK + 1;  // the key chunks + the diagonal partial
   size_t b = 0;
@@ -757,17 +745,12 @@ void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void*
   rm.mask = (uint64_t*)take(T * sizeof(uint64_t));
   k_ttt_meta<<<(T + 255) / 256, 256, 0, st>>>(T, rm);
   const float scale = 1.f / sqrtf((float)hd);
-  if (bf16 && (hd == 64 || hd == 128) && S <= TTT_SMAX && (Hq / Hkv) * S <= TTT_PAIRS) {
-    // one key chunk spans all T native keys (the T rows already fill the chip), then the fused diagonal + merge
+  if (bf16 && (hd == 64 || hd == 128)) {
+    // one key chunk spans all T native keys (the T rows already fill the chip); the diagonal keys are merged in
+    // the attention kernel's epilogue, which writes the output
     const int chunk = (T + 63) / 64 * 64;
-    attention_partials(true, q, k0, v0, (size_t)Hkv * T * hd, (size_t)T * hd, KvPages{}, rm, T, T, Hq, Hkv, hd, T, o_part,
-                       ml_part, max_splits, st, chunk);
-    if (hd == 128)
-      k_ttt_diag_merge<128><<<dim3(T, Hkv), 64, 0, st>>>(T, S, Hq, Hkv, scale, (const bf16_t*)q, (const bf16_t*)ks,
-                                                         (const bf16_t*)vs, o_part, ml_part, (bf16_t*)out);
-    else
-      k_ttt_diag_merge<64><<<dim3(T, Hkv), 64, 0, st>>>(T, S, Hq, Hkv, scale, (const bf16_t*)q, (const bf16_t*)ks,
-                                                        (const bf16_t*)vs, o_part, ml_part, (bf16_t*)out);
+    attention_partials(true, q, k0, v0, (size_t)Hkv * T * hd, (size_t)T * hd, KvPages{}, rm, T, T, Hq, Hkv, hd, T,
+                       o_part, ml_part, max_splits, st, chunk, ks, vs, S, out);
     return;
   }
   // native keys [Hkv][T][hd]: one "sequence" of T slots

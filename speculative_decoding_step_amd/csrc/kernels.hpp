@@ -130,7 +130,12 @@ struct AttnSplits {
 AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride,
                               size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd,
                               int key_bound, float* o_part, float* ml_part, int max_splits, hipStream_t st,
-                              int chunk_override);  // chunk_override > 0: keys per chunk (else the size policy)
+                              int chunk_override,  // > 0: keys per chunk (else the size policy)
+                              // training-time test (bf16, hd 64 or 128, one chunk covering every key): the
+                              // diagonal keys dk / dv [nstep][Hkv][R][hd] join each row's softmax and the output
+                              // is written to tout [R][Hq][hd]; no partials
+                              const void* dk = nullptr, const void* dv = nullptr, int nstep = 0,
+                              void* tout = nullptr);
 // Training-time-test attention: q, out [T, Hq, hd]; k0, v0 [Hkv, T, hd]; ks, vs [S, Hkv, T, hd]; ws of
 // ttt_workspace_bytes(T, Hq, hd) bytes.
 size_t ttt_workspace_bytes(int T, int Hq, int hd);

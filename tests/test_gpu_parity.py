@@ -422,7 +422,7 @@ def test_accept_tree_flags_malformed_input():
 @pytest.mark.parametrize("dtype,T,S,Hq,Hkv,hd", [("bf16", 300, 3, 8, 2, 128), ("bf16", 1, 2, 4, 4, 64),
                                                 ("bf16", 777, 7, 4, 1, 64), ("bf16", 513, 0, 8, 4, 128),
                                                 ("f32", 129, 2, 4, 2, 96), ("f32", 40, 0, 2, 1, 32),
-                                                ("bf16", 2048, 7, 32, 8, 128)])
+                                                ("bf16", 200, 20, 8, 2, 128), ("bf16", 2048, 7, 32, 8, 128)])
 def test_ttt_attention_matches_oracle(dtype, T, S, Hq, Hkv, hd):
     """Training-time-test attention (causal native keys + diagonal simulated keys)
     against the oracle: every position for the small cases, sampled positions (first,
