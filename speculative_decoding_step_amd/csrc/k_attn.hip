@@ -300,10 +300,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   const int v = qb * QB + 16 * w + lr;
   bool ok = v < nq;
   const int row = bs * rps + (ok ? v / G : 0), h = g * G + (ok ? v % G : 0);
-  const int sq = ok ? rseq[row] : -1;
+  // training-time test: one sequence, row i sees native keys 0..i (no metadata arrays to read)
+  const int sq = ok ? (TTT ? 0 : rseq[row]) : -1;
   ok = ok && sq >= 0;
-  const int lim = rlim[row], t0 = rt0[row];
-  const uint64_t mask = rmask[row];
+  const int lim = TTT ? row + 1 : rlim[row], t0 = TTT ? 0 : rt0[row];
+  const uint64_t mask = TTT ? 0ull : rmask[row];
   int my_end = ok ? min(key_end(lim, t0, mask), S_cap) : 0;
   int my_seq = ok ? sq : -1;
 #pragma unroll
@@ -743,9 +744,8 @@ void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void*
   rm.lim = (int*)take(T * sizeof(int));
   rm.tail0 = (int*)take(T * sizeof(int));
   rm.mask = (uint64_t*)take(T * sizeof(uint64_t));
-  k_ttt_meta<<<(T + 255) / 256, 256, 0, st>>>(T, rm);
   const float scale = 1.f / sqrtf((float)hd);
-  if (bf16 && (hd == 64 || hd == 128)) {
+  if (bf16 && (hd == 64 || hd == 128)) {  // (the kernel derives each row's metadata itself)
     // one key chunk spans all T native keys (the T rows already fill the chip); the diagonal keys are merged in
     // the attention kernel's epilogue, which writes the output
     const int chunk = (T + 63) / 64 * 64;
@@ -753,6 +753,7 @@ void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void*
                        o_part, ml_part, max_splits, st, chunk, ks, vs, S, out);
     return;
   }
+  k_ttt_meta<<<(T + 255) / 256, 256, 0, st>>>(T, rm);
   // native keys [Hkv][T][hd]: one "sequence" of T slots
   const AttnSplits sp = attention_partials(bf16, q, k0, v0, (size_t)Hkv * T * hd, (size_t)T * hd, KvPages{}, rm, T, T, Hq, Hkv,
                                            hd, T, o_part, ml_part, max_splits, st, 0);
