@@ -458,12 +458,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
                       __builtin_amdgcn_exp2f(fmaf(S[kb4][r + 1], qscale, -m))};
         lsum += p[0] + p[1];
         const bf16x2 hi = __builtin_convertvector(p, bf16x2);
-        const f32x2 rest = p - __builtin_convertvector(hi, f32x2);
-        const bf16x2 lo = __builtin_convertvector(rest, bf16x2);
         ph[kb4 >> 1][4 * (kb4 & 1) + r] = hi[0];
         ph[kb4 >> 1][4 * (kb4 & 1) + r + 1] = hi[1];
-        pl[kb4 >> 1][4 * (kb4 & 1) + r] = lo[0];
-        pl[kb4 >> 1][4 * (kb4 & 1) + r + 1] = lo[1];
+        if constexpr (!TTT) {  // the verify path keeps P's low half too (two MFMAs, ~16 significant bits)
+          const f32x2 rest = p - __builtin_convertvector(hi, f32x2);
+          const bf16x2 lo = __builtin_convertvector(rest, bf16x2);
+          pl[kb4 >> 1][4 * (kb4 & 1) + r] = lo[0];
+          pl[kb4 >> 1][4 * (kb4 & 1) + r + 1] = lo[1];
+        }
       }
     // V^T operand of dim block b, keys {32 k2 + 4 lg + e} then {32 k2 + 16 + 4 lg + e}: the 4-key groups
     // 8 k2 + lg and 8 k2 + 4 + lg, read transposed (lane lr points at 4 lr elements into the block; the
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
         const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
                                                            __builtin_bit_cast(u32x2, v1)[0], __builtin_bit_cast(u32x2, v1)[1]});
         O[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ph[k2], O[b], 0, 0, 0);
-        O[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl[k2], O[b], 0, 0, 0);
+        if constexpr (!TTT) O[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl[k2], O[b], 0, 0, 0);
       }
   };
 
