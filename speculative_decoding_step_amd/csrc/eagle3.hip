@@ -377,9 +377,8 @@ void run_attention(eagle3_ctx* c, const void* kc, const void* vc, const RowMeta&
   prof_end(c, &rec);
 }
 
+// K (which = 0) or V (1) array of layer l: kv_le elements each, in layer order.
 char* kv_layer(eagle3_ctx* c, char* base, int l, int which) {
-  const eagle3_shape& s = c->sh;
-  (void)s;
   return base + ((size_t)l * 2 + which) * c->kv_le * c->esz;
 }
 

@@ -173,10 +173,15 @@ class Engine:
         return B.eagle3_device_status(self.ctx)
 
     def set_draft_lengths(self, n_draft=None):
-        """Per-request draft lengths ([B] ints, read at every later step; None = the full budget)."""
+        """Per-request draft lengths ([B] ints, read at every later step; None = the full budget).
+
+        Once set, the device buffer stays the same (a captured step keeps reading it):
+        None then refills it with the full budget."""
         if n_draft is None:
-            self.n_draft = None
-            B.eagle3_set_draft_lengths(self.ctx, None)
+            if self.n_draft is None:
+                B.eagle3_set_draft_lengths(self.ctx, None)
+            else:
+                self.n_draft.fill_(self.spec.n_nodes)
             return
         nd = torch.as_tensor(np.asarray(n_draft, dtype=np.int32), device=self.dev)
         if self.n_draft is None:
