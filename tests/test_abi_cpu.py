@@ -56,6 +56,36 @@ def test_create_rejects_null_pointers():
         B.eagle3_create(s, cfg, B.TargetWeights(), B.HeadWeights(), 1, 512, 2304, None, 0, None, None, None)
 
 
+def test_paged_and_bookkeeping_entry_points_validate_arguments():
+    """Paged pools, paged create, draft lengths and the verify-batch bookkeeping reject bad
+    arguments before touching the device."""
+    s = _shape8b()
+    t, d = B.eagle3_paged_kv_bytes(s, 64, 100)
+    assert t == 32 * 2 * 100 * 8 * 64 * 128 * 2 and d == 2 * 100 * 8 * 64 * 128 * 2
+    for bs in (0, 16, 48, 96):                                   # a power of two >= 64
+        with pytest.raises(B.Eagle3Error, match="invalid"):
+            B.eagle3_paged_kv_bytes(s, bs, 100)
+    with pytest.raises(B.Eagle3Error, match="invalid"):
+        B.eagle3_paged_kv_bytes(s, 64, 0)
+    cfg = B.SpecCfg(B.GREEDY_TREE, 6, 10, 60, 0.0, 0)
+    table = C.c_void_p(0x1000)                                   # never dereferenced on these paths
+    for pages in (B.KvPages(48, 10, 4, table), B.KvPages(64, 0, 4, table), B.KvPages(64, 10, 0, table),
+                  B.KvPages(64, 10, 4, None)):
+        with pytest.raises(B.Eagle3Error, match="invalid"):
+            B.eagle3_create_paged(s, cfg, B.TargetWeights(), B.HeadWeights(), 1, 512, pages, None, 0, None, None,
+                                  None)
+    with pytest.raises(B.Eagle3Error, match="invalid"):
+        B.eagle3_set_draft_lengths(None, None)
+    p = C.c_void_p(0x1000)
+    for args in ((0, 4, p, p, None, p, p, p, p, None, None, None),      # empty batch
+                 (2, -1, p, p, None, p, p, p, p, None, None, None),     # negative capacity
+                 (2, 4, None, p, None, p, p, p, p, None, None, None),   # missing input
+                 (2, 4, p, p, None, p, p, None, p, None, None, None),   # capacity without an output
+                 (2, 4, p, p, None, p, p, p, p, p, None, None)):        # draft ids without input ids
+        with pytest.raises(B.Eagle3Error, match="invalid"):
+            B.eagle3_spec_decode_metadata(*args)
+
+
 def packed_index(N, K):
     """Destination index of every element (n, k) of a packed bf16 [N, K] weight,
     written from the formula eagle3.h states for eagle3_pack_linear."""
