@@ -309,7 +309,30 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_per_dispatch": n, "dispatches": 5}), flush=True)
 
 
-def ttt_bench(steps, warmup, T=2048, S=7, Hq=32, Hkv=8, hd=128):
+def ttt_cpu_baseline(T, S, Hq, Hkv, hd, n_sample=2048):
+    """The oracle's training-time-test attention (float64 numpy) on n_sample evenly spaced
+    positions of the same call (their mean causal length is the call's; at the default
+    T 2048 every position, ~10 s), timed once; positions/s = n_sample / time."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.ttt import ttt_attention
+    from speculative_decoding_step_amd import synth
+
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    args = [synth.normal_np(9, n, shp, 1.0, "bf16").astype(np.float64)
+            for n, shp in (("q", (T, Hq, hd)), ("k0", (Hkv, T, hd)), ("v0", (Hkv, T, hd)),
+                           ("ks", (S, Hkv, T, hd)), ("vs", (S, Hkv, T, hd)))]
+    pos = sorted(set(int(x) for x in np.linspace(0, T - 1, min(n_sample, T))))
+    t0 = time.perf_counter()
+    ttt_attention(*args, positions=pos)
+    t = time.perf_counter() - t0
+    return {"value": round(len(pos) / t, 2), "unit": "positions/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 numpy oracle: {len(pos)} evenly spaced positions of the same call "
+                      f"(T {T}, S {S}, {Hq}/{Hkv} heads x {hd}), {t:.1f}s"}
+
+
+def ttt_bench(steps, warmup, T=2048, S=7, Hq=32, Hkv=8, hd=128, cpu=True):
     """Training-time-test attention at the 8B draft layer's head layout (T positions,
     S simulated steps, bf16, seeded N(0, 1) inputs resident on the device).  One step
     = one eagle3_ttt_attention call.  Roofline: MFMA against the bf16 peak, with the
@@ -356,7 +379,7 @@ def ttt_bench(steps, warmup, T=2048, S=7, Hq=32, Hkv=8, hd=128):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(achieved / 2500.0, 4), "traffic": None, "algorithmic_bytes": nbytes,
                      "hbm_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)},
-        "cpu_baseline": None}), flush=True)
+        "cpu_baseline": ttt_cpu_baseline(T, S, Hq, Hkv, hd) if cpu else None}), flush=True)
 
 
 def main():
@@ -386,7 +409,7 @@ def main():
               "with no exchange; run one process per GPU). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.workload == "ttt_attn_8b":
-        ttt_bench(args.steps, args.warmup)
+        ttt_bench(args.steps, args.warmup, cpu=not args.no_cpu_baseline)
         return
     from speculative_decoding_step_amd import configs
 
