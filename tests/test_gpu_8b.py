@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from gpu_util import kv_view, random_tree, to_dev
-from oracle.accept import chain_rejection, greedy_walk
+from oracle.accept import chain_rejection, greedy_walk, tree_rejection
 from oracle.llama import KVCache, Shape, causal_visible, target_forward
 from oracle.numerics import probs_f32, sample_inverse_cdf
 from oracle.tree import mask_words, tree_mask
@@ -250,6 +250,42 @@ def test_8b_sampling_chain_b4_steps():
     for l in range(2):
         _close(chain_kv[l, 0].transpose(1, 0, 2), tk[l], ("chain K", l))
         _close(chain_kv[l, 1].transpose(1, 0, 2), tv[l], ("chain V", l))
+
+
+def test_8b_sample_tree_b1_steps():
+    """The batch-1 8B tree accepted by level-by-level rejection sampling at T = 1: three
+    whole steps.  Each step's accepted path and next token must equal the oracle's tree
+    rejection sampler given the GPU's tree, its verify logits (p over all 128,256 ids at
+    every tree row) and the uniforms; compaction advances the sequence by the path."""
+    w = configs.WORKLOADS["llama8b_sample_tree_b1"]
+    ms, D, k = w.shape, w.depth, w.topk
+    prompts = configs.prompts_np(w)
+    eng = Engine(ms, Spec.of(w), 1, w.prompt_len + 256, w.target_seed, w.head_seed, prefill_chunk=512)
+    print(f"\n[8B sampled tree] P={w.prompt_len} D{D} k{k} N{w.n_nodes} T={w.temperature}", flush=True)
+    eng.prefill(prompts, synth.uniform24_t(5000, "u_root", 1, "cuda"))
+    na = eng.n_u_accept
+    lens = []
+    for s in range(3):
+        u_a = synth.uniform24_t(5000, f"u_accept{s}", na, "cuda").view(1, na)
+        eng.set_uniforms(None, u_a)
+        P = int(eng.seq_lens[0])
+        eng.draft()
+        eng.verify()
+        eng.accept()
+        torch.cuda.synchronize()
+        assert eng.device_status() == 0
+        toks, par = eng.tokens[0].cpu().numpy(), eng.parents[0].cpu().numpy()
+        lg = eng.logits.cpu().numpy()
+        p = np.stack([probs_f32(lg[i], w.temperature) for i in range(w.rows)])
+        path, nxt = tree_rejection([int(t) for t in toks], [int(x) for x in par], p, u_a.cpu().numpy()[0], k, D)
+        n = int(eng.path_len[0])
+        assert list(eng.path[0].cpu().numpy()[:n]) == path and int(eng.next_root[0]) == nxt, s
+        eng.compact()
+        torch.cuda.synchronize()
+        assert int(eng.seq_lens[0]) == P + n
+        lens.append(n)
+    print(f"  accepted path lengths {lens}", flush=True)
+    eng.close()
 
 
 def _seq_kv(eng, s, P, layers):
