@@ -264,26 +264,31 @@ def measured_traffic(w, kind):
     return t["bytes_per_launch"]
 
 
-def traffic_from_counters(workload, kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, mib):
+def traffic_from_counters(workload, kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, mib, last=0):
     """Writes profiles/traffic_<workload>.json from rocprofv3 --pmc FETCH_SIZE and
     WRITE_SIZE runs of bench.py and of --copy-probe MIB (the copy kernel reads
-    and writes MIB MiB per dispatch: its counters give the scale factors)."""
+    and writes MIB MiB per dispatch: its counters give the scale factors).
+    last > 0 keeps only the kernel's last `last` dispatches (the profiled eager
+    steps that end a bench run, not the prefill's launches of the same kernel)."""
     import csv
 
     # kernel-name prefixes: the 64-row kernels (plain and fused gate/up), the 16-row ones, the large-M one
     names = {0: "k_gemm_bf16<4, ", 1: "k_gemm_bf16<1, ", 3: "k_gemm_bf16_big"}
 
-    def per_dispatch(path, needle):
-        vals = [float(r["Counter_Value"]) * 1024.0 for r in csv.DictReader(open(path)) if needle in r["Kernel_Name"]]
-        return vals
+    def per_dispatch(path, needle, keep=0):
+        rows = [r for r in csv.DictReader(open(path)) if needle in r["Kernel_Name"]]
+        if rows and "Dispatch_Id" in rows[0]:
+            rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        vals = [float(r["Counter_Value"]) * 1024.0 for r in rows]
+        return vals[-keep:] if keep else vals
 
     nbytes = mib << 20
     f_copy = per_dispatch(copy_fetch_csv, "copyBuffer")
     w_copy = per_dispatch(copy_write_csv, "copyBuffer")
     f_scale = nbytes / (sum(f_copy) / len(f_copy))
     w_scale = nbytes / (sum(w_copy) / len(w_copy))
-    fv = per_dispatch(fetch_csv, names[kind])
-    wv = per_dispatch(write_csv, names[kind])
+    fv = per_dispatch(fetch_csv, names[kind], last)
+    wv = per_dispatch(write_csv, names[kind], last)
     per_launch = sum(fv) / len(fv) * f_scale + sum(wv) / len(wv) * w_scale
     out = {"workload": workload, "kernel_kind": kind, "kernel": names[kind], "source_digest": _kernel_source_digest(kind),
            "bytes_per_launch": round(per_launch), "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
@@ -397,9 +402,12 @@ def main():
                          "--copy-probe run, then exit")
     ap.add_argument("--traffic-kind", type=int, default=0, help="kernel kind for --traffic-from (0, 1 or 3)")
     ap.add_argument("--traffic-mib", type=int, default=1024, help="copy size of the --copy-probe run, MiB")
+    ap.add_argument("--traffic-last", type=int, default=0,
+                    help="for --traffic-from: use only the kernel's last N dispatches (the profiled steps)")
     args = ap.parse_args()
     if args.traffic_from:
-        traffic_from_counters(args.workload, args.traffic_kind, *args.traffic_from, args.traffic_mib)
+        traffic_from_counters(args.workload, args.traffic_kind, *args.traffic_from, args.traffic_mib,
+                              args.traffic_last)
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
