@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
 // The skinny variants: M <= 16: <MB 1, NB 2, 4 waves>; M <= 64: <MB 4, NB 1,
 // 8 waves>; both cover 128 weight rows per workgroup.  Fused gate/up: 4 waves
 // of one gate + one up block, 64 output columns per workgroup.
-constexpr int ROWS16 = 16 * 2 * 4, ROWS64 = 16 * 1 * 8, SILU_COLS = 16 * 4;
+constexpr int ROWS16 = 16 * 2 * 4, ROWS64 = 16 * 1 * 8, ROWS64N = 16 * 1 * 4, SILU_COLS = 16 * 4;
 
 // fp32 GEMM (the tiny fp32 workload): 32 x 64 output tile per workgroup, each
 // thread 2 x 4 outputs, K tiles of 32 staged in LDS for both operands.
@@ -343,21 +343,29 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
          hipEvent_t ev_stop) {
   if (bf16 && m_tile > 64)
     return gemm_big(X, M, K, segs, out, split_stride, splits, st, ev_start, ev_stop);
+  const int ldo = gemm_ntot(segs);
+  // 64-row tiles on matrices of at most 8192 rows: four-wave workgroups of 64 weight rows with half the K
+  // splits (the same number of workgroups, each streaming twice the K; half the partials to read back)
+  const bool narrow = bf16 && m_tile == 64 && ldo <= 8192;
+  if (narrow) splits = std::max(1, splits / 2);
   splits = gemm_splits(bf16, K, splits, m_tile);
   if (M <= 0) return splits;
-  const int ldo = gemm_ntot(segs);
   if (bf16) {
     const int ktiles = K / PACK_KB;
     const int per = (ktiles + splits - 1) / splits;
     const int kchunk = per * PACK_KB;
     const int S = (ktiles + per - 1) / per;
-    const TileMap tm = tile_map(segs, m_tile == 16 ? ROWS16 : ROWS64);
+    const TileMap tm = tile_map(segs, m_tile == 16 ? ROWS16 : (narrow ? ROWS64N : ROWS64));
     const int ntiles = tm.tiles0[segs.nseg];
     const int mtiles = (M + m_tile - 1) / m_tile;
     const int nwork = mtiles * S * ntiles;
     const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
     if (m_tile == 16)
       hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, 4, false>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
+                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
+                            (bf16_t*)nullptr);
+    else if (narrow)
+      hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, 4, false>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                             (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
                             (bf16_t*)nullptr);
     else
