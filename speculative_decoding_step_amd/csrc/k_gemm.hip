@@ -346,7 +346,7 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
   const int ldo = gemm_ntot(segs);
   // 64-row tiles on matrices of at most 8192 rows: four-wave workgroups of 64 weight rows with half the K
   // splits (the same number of workgroups, each streaming twice the K; half the partials to read back)
-  const bool narrow = bf16 && m_tile == 64 && ldo <= 8192;
+  const bool narrow = bf16 && m_tile <= 64 && ldo <= 8192;
   if (narrow) splits = std::max(1, splits / 2);
   splits = gemm_splits(bf16, K, splits, m_tile);
   if (M <= 0) return splits;
@@ -355,12 +355,16 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
     const int per = (ktiles + splits - 1) / splits;
     const int kchunk = per * PACK_KB;
     const int S = (ktiles + per - 1) / per;
-    const TileMap tm = tile_map(segs, m_tile == 16 ? ROWS16 : (narrow ? ROWS64N : ROWS64));
+    const TileMap tm = tile_map(segs, narrow ? ROWS64N : (m_tile == 16 ? ROWS16 : ROWS64));
     const int ntiles = tm.tiles0[segs.nseg];
     const int mtiles = (M + m_tile - 1) / m_tile;
     const int nwork = mtiles * S * ntiles;
     const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
-    if (m_tile == 16)
+    if (m_tile == 16 && narrow)
+      hipExtLaunchKernelGGL((k_gemm_bf16<1, 1, 4, false>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
+                            (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
+                            (bf16_t*)nullptr);
+    else if (m_tile == 16)
       hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, 4, false>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                             (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
                             (bf16_t*)nullptr);
