@@ -234,3 +234,34 @@ def test_paged_graph_replay_sees_current_table_and_lengths():
     assert a.device_status() == 0 and b.device_status() == 0
     a.close()
     b.close()
+
+
+def test_draft_lengths_sampled_tree_match_oracle_f32():
+    """Tree rejection sampling with per-request draft lengths on a paged cache: every
+    request's accepted path and next token equal the oracle's sampler over its truncated
+    draft (children past the budget are never tested)."""
+    ms = toy_shape(dtype="f32", vocab=96, layers=2)
+    D, k, N, T = 3, 3, 8, 0.8
+    spec = Spec("sample_tree", D, k, N, T)
+    shp, W, H = oracle_weights(ms, seed=29, sigma=0.3)
+    prompts = _ragged_prompts(ms, [24, 50], 65)
+    eng = make_engine(ms, spec, batch=2, max_seq=128, seed=29, sigma=0.3, block_size=64, page_seed=4)
+    u_root = synth.uniform24_t(5000, "u_root", 2, "cuda")
+    eng.prefill(prompts, u_root)
+    seqs = _oracle_seqs(W, H, shp, SpecConfig("sample_tree", D, k, N, T), prompts, 128, u_root.cpu().numpy())
+    rng = np.random.default_rng(14)
+    nu = eng.n_u_accept
+    for step in range(6):
+        nd = rng.integers(0, N + 1, size=2)
+        ua = synth.uniform24_t(5003, f"a{step}", 2 * nu, "cuda").view(2, nu)
+        eng.set_uniforms(None, ua)
+        eng.set_draft_lengths(nd)
+        eng.step()
+        assert eng.device_status() == 0
+        for s in range(2):
+            tree, path, nxt = seqs[s].step(u_accept=ua[s].cpu().numpy(), n_draft=int(nd[s]))
+            assert list(eng.tokens[s].cpu().numpy()[:len(tree.tokens)]) == tree.tokens, (step, s)
+            n = eng.path_len[s].item()
+            assert list(eng.path[s].cpu().numpy()[:n]) == path, (step, s, nd[s])
+            assert eng.next_root[s].item() == nxt, (step, s)
+    eng.close()
