@@ -280,7 +280,12 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   constexpr int PW = (NCP + NW - 1) / NW;      // copies per wave and tile
   constexpr int KF = HD / 32;                  // K fragments per 16-key block
   constexpr int VB = HD / 16;                  // V blocks per 4-key group
-  __shared__ __attribute__((aligned(1024))) bf16_t stg[NST][2 * TILE];  // NST stages, each K then V
+  // V: one 4-key group (VB blocks of 4 keys x 16 dims) every VGS elements.  At HD 128 a group is 1 KiB and
+  // gets 128 bytes of padding, so the four 16-lane parts of a transposed read (groups 1 KiB apart otherwise)
+  // fall on alternate halves of the LDS banks.  (At HD 64 one copy fills two groups back to back.)
+  constexpr int VGS = VB * 64 + (HD == 128 ? 64 : 0);
+  constexpr int STG = TILE + (AKT / 4) * VGS;  // elements per stage: K, then V
+  __shared__ __attribute__((aligned(1024))) bf16_t stg[NST][STG];
   __shared__ int red_end[8], red_seq[8];
   const int per = (nwork + 7) >> 3;
   const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
       const int bi = 8 * (f - NCP / 2) + (lane >> 3), c = lane & 7;
       key = 4 * (bi / VB) + (c >> 1);
       d0 = 16 * (bi % VB) + 8 * (c & 1);
-      dst[i] = TILE + (f - NCP / 2) * 512;
+      dst[i] = TILE + (f - NCP / 2) * (512 / (VB * 64)) * VGS;
     }
     ckey[i] = key;  // key within the tile
     cbase[i] = f < NCP / 2 ? kb : vb;
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
 
   auto tile = [&](const bf16_t* stgp, int kt) {
     const bf16_t* ks = stgp + 8 * lane;                                 // + constant fragment offsets
-    const bf16_t* vs = stgp + TILE + lg * (VB * 64) + 4 * lr;          // + constant block offsets
+    const bf16_t* vs = stgp + TILE + lg * VGS + 4 * lr;                // + constant block offsets
     // S^T blocks: S[kb4][r] = raw score(key kt + 16 kb4 + 4 lg + r, the lane's query)
     f32x4 S[4];
 #pragma unroll
@@ -474,8 +479,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int b = 0; b < HD / 16; ++b) {
-        const bf16_t* b0 = vs + (8 * k2 * VB + b) * 64;
-        const bf16_t* b1 = vs + ((8 * k2 + 4) * VB + b) * 64;
+        const bf16_t* b0 = vs + 8 * k2 * VGS + b * 64;
+        const bf16_t* b1 = vs + (8 * k2 + 4) * VGS + b * 64;
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(attn_lds_t)b0);
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(attn_lds_t)b1);
         const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, v0)[0], __builtin_bit_cast(u32x2, v0)[1],
