@@ -495,7 +495,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   // so vmcnt(PW * a) with a = min(NST - 2, ntl - 1 - t) tiles issued after t means tile t has landed.  The
   // barrier then publishes every wave's copies of tile t and guarantees that all waves finished tile t - 1,
   // whose stage the copies of tile t + NST - 1 refill.
-  static_assert(NST == 3 || NST == 4, "the wait below covers at most two tiles in flight after the current one");
+  static_assert(NST >= 2 && NST <= 4, "the wait below covers at most two tiles in flight after the current one");
   static_assert(PW * (NST - 2) <= 63, "copies in flight exceed the vmcnt range");
   const int ntl = (c1 - c0 + AKT - 1) / AKT;
   for (int t = 0; t < NST - 1 && t < ntl; ++t) issue(stg[t], c0 + t * AKT);
@@ -631,6 +631,10 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
         launch_attn<128, 4, true>(E3_ATTN_ARGS);
       else
         launch_attn<64, 4, true>(E3_ATTN_ARGS);
+    } else if (hd == 128 && nwork >= 512) {
+      // More than one round of workgroups: two stages (68 KiB) let two workgroups share a CU, whose waves then
+      // spread over the SIMDs more evenly than one workgroup's (5 waves on 4 SIMDs at 68 queries per tile)
+      launch_attn<128, 2, false>(E3_ATTN_ARGS);
     } else if (hd == 128) {
       launch_attn<128, 4, false>(E3_ATTN_ARGS);
     } else {
