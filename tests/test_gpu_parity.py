@@ -100,6 +100,67 @@ def test_verify_prefill_and_tree_vs_oracle(dtype, chunk):
     eng.close()
 
 
+def test_batched_ragged_tree_verify_vs_oracle():
+    """40 ragged prompts (60..1000 tokens) at head size 128: the verify attention launch has
+    40 sequences x 4 KV heads x 4 key chunks = 640 work items, the size that takes the
+    two-stage ring with two workgroups per CU.  Every sequence gets its own random tree;
+    the shortest, a middle and the longest sequence are checked against the oracle.
+    Weights at sigma 0.02 keep the logits near 2 in magnitude, as in the other cases: at
+    d 512 and sigma 0.05 they reach 5.6, where the bf16 rounding of the final hidden state
+    alone is about 0.02 (2^-8 relative)."""
+    ms = toy_shape(dtype="bf16", vocab=1000, layers=2, d=512, heads=4, kv=4, hd=128, ffn=512)
+    spec = Spec("greedy_tree", 4, 3, 12)
+    Bn, n = 40, 13
+    lens = np.linspace(60, 1000, Bn).astype(int)
+    assert Bn * ms.n_kv_heads * -(-(int(lens.max()) + n) // 256) >= 512
+    print(f"\n[batched ragged verify, {Bn} sequences, {lens.min()}..{lens.max()} tokens]", flush=True)
+    eng = make_engine(ms, spec, batch=Bn, max_seq=1100, sigma=0.02)
+    shp, W, H = oracle_weights(ms, sigma=0.02)
+    prompts = [synth.tokens_np(41, f"r{b}", int(lens[b]), ms.vocab) for b in range(Bn)]
+    eng.prefill(prompts)
+    torch.cuda.synchronize()
+    _status_clear(eng)
+    rng = np.random.default_rng(9)
+    trees = [random_tree(rng, n, ms.vocab) for _ in range(Bn)]
+    deps = []
+    for tokens, parents in trees:
+        dep = [0] * n
+        for i in range(1, n):
+            dep[i] = dep[parents[i]] + 1
+        deps.append(np.array(dep))
+    tok_d = to_dev(np.concatenate([t for t, _ in trees]))
+    pos_d = to_dev(np.concatenate([lens[b] + deps[b] for b in range(Bn)]))
+    mw = torch.as_tensor(np.concatenate([mask_words(p) for _, p in trees]).view(np.int64), device="cuda")
+    seq_lens = to_dev(lens)
+    logits = torch.zeros(Bn * n, ms.vocab, dtype=torch.float32, device="cuda")
+    am = torch.zeros(Bn * n, dtype=torch.int32, device="cuda")
+    mg = torch.zeros(Bn * n, dtype=torch.float32, device="cuda")
+    auxo = torch.zeros(Bn * n, 3 * ms.d, dtype=eng.tdt, device="cuda")
+    B.eagle3_verify_tree(eng.ctx, 0, Bn, _p(seq_lens), n, _p(tok_d), _p(pos_d), _p(mw),
+                         B.LM_ALL, _p(logits), _p(am), _p(mg), _p(auxo))
+    torch.cuda.synchronize()
+    _status_clear(eng)
+    g_all, am_all = logits.cpu().numpy().reshape(Bn, n, -1), am.cpu().numpy().reshape(Bn, n)
+    eng.close()
+    for b in (0, Bn // 2, Bn - 1):
+        P = int(lens[b])
+        cache = KVCache(shp.n_layers, 1100, shp.n_kv_heads, shp.head_dim)
+        _, k, v, _ = target_forward(W, shp, cache, prompts[b], np.arange(P), causal_visible(P))
+        for l in range(shp.n_layers):
+            cache.k[l][:P], cache.v[l][:P] = k[l], v[l]
+        cache.length = P
+        tokens, parents = trees[b]
+        m = tree_mask(parents)
+        ref, _, _, _ = target_forward(W, shp, cache, tokens, P + deps[b],
+                                      [list(np.nonzero(m[i])[0]) for i in range(n)])
+        err, ok = logits_close(g_all[b], ref, "bf16")
+        print(f"  seq {b} (P={P}): tree logits err {err:.3g}", flush=True)
+        assert ok
+        for i in range(n):
+            if top2_margin(ref[i]) > 2 * margin_tol("bf16", ref[i]):
+                assert am_all[b, i] == int(np.argmax(ref[i]))
+
+
 # ------------------------------------------------------------- tree from logits
 def _tree_engine(D, k, N, V, mode="greedy_tree", T=0.0, batch=1, draft_greedy=False, dv=0):
     ms = toy_shape(dtype="bf16", vocab=V, layers=1, d=256, heads=4, kv=4, hd=64, ffn=256, taps=(0, 0, 0))
