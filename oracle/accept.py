@@ -30,20 +30,20 @@ from .numerics import argmax_first, int_weights, sample_inverse_cdf
 def greedy_walk(tokens, parents, argmax_rows):
     """Longest accepted path.  Returns (path node indices, next root token).
 
-    argmax_rows[i] is the target's argmax at tree row i.  Among the children of
-    the current node the lowest-index one whose token equals that argmax is
-    followed (siblings are distinct tokens, so at most one matches).
+    argmax_rows[i] is the target's argmax at tree row i.  A tree edge is named
+    by (parent row, token); from the root the walk keeps taking the edge whose
+    token is the current row's argmax, and stops at the first row where no such
+    edge exists.  Siblings carry distinct tokens, so an edge names at most one
+    row (the lowest one is kept if a malformed tree repeats a token).  The next
+    root is the argmax of the last row reached.
     """
-    path, node = [0], 0
-    n = len(tokens)
-    while True:
-        pred = int(argmax_rows[node])
-        child = next((c for c in range(n) if parents[c] == node and tokens[c] == pred), None)
-        if child is None:
-            break
-        path.append(child)
-        node = child
-    return path, int(argmax_rows[node])
+    edge = {}
+    for row in range(len(tokens) - 1, 0, -1):          # descending: the lowest row wins
+        edge[(int(parents[row]), int(tokens[row]))] = row
+    path = [0]
+    while (path[-1], int(argmax_rows[path[-1]])) in edge:
+        path.append(edge[(path[-1], int(argmax_rows[path[-1]]))])
+    return path, int(argmax_rows[path[-1]])
 
 
 def argmax_rows_f32(logits) -> list:

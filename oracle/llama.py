@@ -159,26 +159,31 @@ def draft_layer(H: dict, W: dict, shp: Shape, e_tokens, x: np.ndarray, positions
               attends to, given this call's rotated, rounded K and V [T, Hkv, hd].
     Returns (a [T, d] float64, the layer output before the final norm;
              k_new, v_new [T, Hkv, hd]).
+
+    Two separate RMSNorms (input_norm on e, hidden_norm on x) feed one 2d-wide
+    input to q/k/v, embedding half first.  Only x is carried forward: the
+    attention and MLP outputs are added to x, and the embedding never enters
+    the sum.  The MLP is SwiGLU on post_norm of that sum.
     """
     rnd = rounder(shp.dtype)
     T = len(e_tokens)
     hq, hkv, hd = shp.n_heads, shp.n_kv_heads, shp.head_dim
     e = W["embed"][np.asarray(e_tokens, dtype=np.int64)].astype(np.float64)
-    x = np.asarray(x, dtype=np.float64)
-    x2 = np.concatenate([rnd(rms_norm(e, H["input_norm"], shp.eps)),
-                         rnd(rms_norm(x, H["hidden_norm"], shp.eps))], axis=-1)
-    q = rnd(rope((x2 @ H["wq"].T).reshape(T, hq, hd), positions, shp.rope_theta))
-    k = rnd(rope((x2 @ H["wk"].T).reshape(T, hkv, hd), positions, shp.rope_theta))
-    v = rnd((x2 @ H["wv"].T).reshape(T, hkv, hd))
-    o = np.empty((T, hq, hd))
-    for i in range(T):
-        keys, vals = context(i, k, v)
-        o[i] = attend(q[i], keys, vals, hkv)
-    x = x + rnd(o).reshape(T, hq * hd) @ H["wo"].T            # residual stream is x, not e
-    h = rnd(rms_norm(x, H["post_norm"], shp.eps))
-    act = rnd(silu(h @ H["w_gate"].T) * (h @ H["w_up"].T))
-    a = x + act @ H["w_down"].T
-    return a, k, v
+    feat = np.asarray(x, dtype=np.float64)
+    joint = np.hstack((rnd(rms_norm(e, H["input_norm"], shp.eps)),
+                       rnd(rms_norm(feat, H["hidden_norm"], shp.eps))))       # [T, 2d]
+
+    def heads(w, n):
+        return (joint @ w.T).reshape(T, n, hd)
+
+    q = rnd(rope(heads(H["wq"], hq), positions, shp.rope_theta))
+    k = rnd(rope(heads(H["wk"], hkv), positions, shp.rope_theta))
+    v = rnd(heads(H["wv"], hkv))
+    att = np.stack([attend(q[i], *context(i, k, v), hkv) for i in range(T)])
+    mid = feat + rnd(att).reshape(T, hq * hd) @ H["wo"].T
+    z = rnd(rms_norm(mid, H["post_norm"], shp.eps))
+    gated = rnd(silu(z @ H["w_gate"].T) * (z @ H["w_up"].T))
+    return mid + gated @ H["w_down"].T, k, v
 
 
 def draft_logits(H: dict, W: dict, shp: Shape, a: np.ndarray) -> np.ndarray:

@@ -53,24 +53,36 @@ def mask_words(parents) -> np.ndarray:
 
 
 def build_static_tree(root: int, branching, children_of):
-    """The pages' static builder: every frontier node gets its top-branching[l] tokens.
+    """Static tree with a fixed branching count per level ("Advanced speculative
+    decoding: tree drafts and EAGLE", Implementation and Exercises).
 
-    children_of(path_tokens, width) -> list of `width` token ids for the node
-    reached by path_tokens (root first).  Returns (tokens, parents).
+    Level 0 is the root; every node of level l has branching[l] children.  The
+    rows of a level are contiguous and the children of a node are contiguous
+    in its level, so level l + 1 has prod(branching[:l + 1]) rows and its j-th
+    row hangs under row j // branching[l] of level l.  children_of(path_tokens,
+    width) gives the `width` tokens under the node reached by path_tokens
+    (root first).  Returns (tokens, parents).
     """
-    tokens, parents, frontier = [root], [-1], [0]
+    sizes = [1]
     for width in branching:
-        nxt = []
-        for node in frontier:
-            path, j = [], node
-            while j != -1:
-                path.append(tokens[j])
-                j = parents[j]
-            for t in children_of(path[::-1], width):
-                tokens.append(int(t))
-                parents.append(node)
-                nxt.append(len(tokens) - 1)
-        frontier = nxt
+        sizes.append(sizes[-1] * int(width))
+    first = [0]
+    for n in sizes[:-1]:
+        first.append(first[-1] + n)
+    total = first[-1] + sizes[-1]
+    parents = [-1] * total
+    tokens = [int(root)] + [None] * (total - 1)
+    prefix = {0: [int(root)]}                       # row -> tokens from the root down to the row
+    for lvl, width in enumerate(branching):
+        for j in range(sizes[lvl + 1]):
+            parents[first[lvl + 1] + j] = first[lvl] + j // int(width)
+        for i in range(sizes[lvl]):
+            row = first[lvl] + i
+            kids = list(children_of(list(prefix[row]), int(width)))
+            for r in range(int(width)):
+                child = first[lvl + 1] + i * int(width) + r
+                tokens[child] = int(kids[r])
+                prefix[child] = prefix[row] + [int(kids[r])]
     return tokens, parents
 
 
