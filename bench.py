@@ -4,8 +4,9 @@ random weights.
 
 Prints ONE JSON line: verified tree tokens/s (= batch * (n_nodes + 1) per step),
 ms per step, the roofline of the dominant kernel (the 64-row MFMA GEMM that
-streams the verify weights) from HIP events on the library's stream, and the
-CPU oracle timed on a bounded sample of the same step.
+streams the verify weights) from HIP events on the library's stream, the verify
+pass as a whole against the same peaks (verify_pass: all of its kernels), and
+the CPU oracle timed on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -64,12 +65,39 @@ def run_gpu(w, steps, warmup):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     print(f"[bench] timed {steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
-    B.eagle3_profile(eng.ctx, True)
-    t0 = time.perf_counter()
+    # the verify pass alone as its own graph (its replays rewrite the same tree rows: idempotent)
+    gv = eng.capture_call(eng.verify)
+    for _ in range(warmup):
+        gv.replay()
+    st = torch.cuda.current_stream()
+    va, vb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    va.record(st)
     for _ in range(steps):
-        eng.step()
+        gv.replay()
+    vb.record(st)
+    torch.cuda.synchronize()
+    verify_ms = va.elapsed_time(vb) / steps
+    del gv
+    B.eagle3_profile(eng.ctx, True)
+    # eager steps with an event pair around each of the four calls (the library launches on this stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(st)
+        eng.draft()
+        ev[i][1].record(st)
+        eng.verify()
+        ev[i][2].record(st)
+        eng.accept()
+        ev[i][3].record(st)
+        eng.compact()
+        ev[i][4].record(st)
+        eng.step_idx += 1
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    phases = {name: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps
+              for j, name in enumerate(("draft", "verify", "accept", "compact"))}
+    phases["verify_graph"] = verify_ms
     prof = {k: B.eagle3_profile_read(eng.ctx, k)
             for k in (B.PROF_GEMM_M64, B.PROF_GEMM_M16, B.PROF_ATTN, B.PROF_GEMM_BIG)}
     B.eagle3_profile(eng.ctx, False)
@@ -77,7 +105,7 @@ def run_gpu(w, steps, warmup):
     if status:
         raise RuntimeError(f"device status flags {status:#x}")
     eng.close()
-    return ms, eager_ms, prof
+    return ms, eager_ms, prof, phases
 
 
 def _slice_weights(w, n_layers):
@@ -115,7 +143,7 @@ def cpu_baseline(w):
     """The oracle (float64 numpy) on a bounded sample of the same step.
 
     Sample: the tree-verify target pass over the step's rows on 1-layer and
-    2-layer slices of the 8B shape (committed KV of prompt_len positions,
+    2-layer slices of the workload's model (committed KV of prompt_len positions,
     seeded), giving the per-layer and LM-head costs, plus the oracle's whole
     draft stage (catch-up row, depth-D expansion, full-vocabulary head) on a
     short committed draft context.  Each piece is timed REPS times and its
@@ -184,7 +212,7 @@ def cpu_baseline(w):
     return {"value": round(w.batch * w.rows / t_step, 3), "unit": "verified tree tokens/s", "cores": int(cores),
             "kind": "oracle",
             "sample": (f"float64 numpy oracle, batch 1: tree verify of {n} rows over {P} committed positions on "
-                       f"1- and 2-layer slices of the 8B shape ({times[1]:.1f}s, {times[2]:.1f}s) and the draft "
+                       f"1- and 2-layer slices of the {w.name} model ({times[1]:.1f}s, {times[2]:.1f}s) and the draft "
                        f"stage ({times['draft']:.1f}s), medians of {REPS} repeats; step = {ms.n_layers} x layer ({t_layer:.2f}s) + LM head "
                        f"({t_head:.2f}s) + draft = {t_step:.1f}s; {work:.0f}s of CPU work "
                        f"(+{t_gen:.0f}s generating the slice's seeded weights)")}
@@ -216,6 +244,38 @@ def step_bytes(w):
     ctx = float(np.sum(configs.prompt_lengths(w)))
     kv_bytes = 2 * kv * e * (s.n_layers * (ctx + w.batch * w.rows) + w.depth * ctx)
     return weights * e + kv_bytes
+
+
+def verify_work(w):
+    """Algorithmic work of one verify pass: HBM bytes (every target weight and the
+    LM head once, the committed K/V the attention reads, the tree rows' K/V and
+    aux rows written) and the GEMM flops (2 x rows x weight elements)."""
+    import numpy as np
+
+    from speculative_decoding_step_amd import configs
+
+    s = w.shape
+    e = 2 if s.dtype == "bf16" else 4
+    q, kv = s.n_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    params = s.n_layers * (s.d * q + 2 * s.d * kv + q * s.d + 3 * s.d * s.ffn) + s.vocab * s.d
+    ctx = float(np.sum(configs.prompt_lengths(w)))
+    rows = w.batch * w.rows
+    nbytes = params * e + 2 * kv * e * s.n_layers * (ctx + rows) + rows * 3 * s.d * e
+    return nbytes, 2.0 * rows * params
+
+
+def verify_pass(w, phases):
+    """The verify pass as a whole (every kernel of eagle3_verify_tree: GEMMs,
+    attention and its merge, norms, RoPE/KV writes, top-2), timed as its own
+    graph replayed back to back: algorithmic bytes against the HBM peak, and
+    GEMM flops against the bf16 MFMA peak.  phases_ms: the four calls of the
+    eager profiled steps (host launch gaps included) and the verify graph."""
+    nbytes, flops = verify_work(w)
+    t = phases["verify_graph"] / 1e3
+    return {"ms": round(phases["verify_graph"], 4), "algorithmic_bytes": round(nbytes), "gemm_flops": round(flops),
+            "hbm_gbps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / HBM_PEAK, 4),
+            "mfma_tflops": round(flops / t / 1e12, 1), "mfma_frac": round(flops / t / BF16_PEAK, 4),
+            "phases_ms": {k: round(v, 4) for k, v in phases.items()}}
 
 
 def roofline(w, prof, steps):
@@ -422,7 +482,7 @@ def main():
     from speculative_decoding_step_amd import configs
 
     w = configs.WORKLOADS[args.workload]
-    ms, eager_ms, prof = run_gpu(w, args.steps, args.warmup)
+    ms, eager_ms, prof, phases = run_gpu(w, args.steps, args.warmup)
     rows = w.batch * w.rows
     line = {
         "metric": "verified tree tokens/s",
@@ -443,9 +503,12 @@ def main():
                    "topk": w.topk, "tree_nodes": w.n_nodes, "rows_per_step": rows,
                    "kv_block_size": w.block_size or None},
         "roofline": roofline(w, prof, args.steps),
+        "verify_pass": verify_pass(w, phases),
         "hbm_gbps_step": round(step_bytes(w) / (ms / 1e3) / 1e9, 1),
         "cpu_baseline": None,
     }
+    vp = line["verify_pass"]
+    line["roofline"]["verify_pass_frac"] = vp["mfma_frac"] if line["roofline"]["bound"] == "mfma" else vp["hbm_frac"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -309,6 +309,32 @@ eagle3_status eagle3_draft_tree(eagle3_ctx *ctx, int32_t batch, const int32_t *s
                                 int32_t *tokens, int32_t *parents, int32_t *depth, int32_t *pos,
                                 uint64_t *mask, float *score, float *q);
 
+/* Residual stream of every later eagle3_verify_tree call ("Advanced
+ * speculative decoding: tree drafts and EAGLE", Implementation: the target
+ * pass over the tree rows; "EAGLE-3: Engineering ...", IX.1: hidden_states[i]
+ * is the stream entering decoder layer i).  buf: device float [n_layers + 1,
+ * R, d] with R = batch * n_rows of the call: entry l is the fp32 residual
+ * entering layer l (entry 0 the embedding rows), entry n_layers the stream
+ * leaving the last layer (the final norm's input).  The caller sizes it for
+ * the calls it makes.  NULL stops the copies.  A parity output: the pass
+ * never reads it; the copies run on the context's stream as the pass goes. */
+eagle3_status eagle3_set_hidden_out(eagle3_ctx *ctx, float *buf);
+
+/* Draft logits of every later eagle3_draft_tree call ("EAGLE-3: Engineering
+ * Implementation ...", VIII.5-VIII.6: the draft head's LM-head output, the
+ * distribution the tree is ranked and drawn from).  table: device float
+ * [max_batch, 1 + E, V_d] (V_d = draft_vocab, or vocab when the head is
+ * shared; E = (depth - 1) * topk for trees, depth - 1 for a sampled chain),
+ * laid out as eagle3_tree_from_logits reads it: row 0 of sequence b is the
+ * root's draft row (the last catch-up row's logits), row 1 + r expansion row
+ * r in creation order (trees: depth-major, frontier rank within a depth;
+ * chains: the row that drew draft r + 2).  Rows of a sequence the call does
+ * not reach keep their old contents.  NULL stops the copies.  The copies are
+ * launched on the context's stream right after each LM-head pass, so a
+ * captured step writes them on every replay.  This is a parity output: the
+ * step itself never reads it. */
+eagle3_status eagle3_set_draft_logits_out(eagle3_ctx *ctx, float *table);
+
 /* Tree construction alone, from given draft logits (no draft model): the same
  * kernels as eagle3_draft_tree with logits_table [B, 1 + (depth-1)*topk, V_d]
  * float (V_d = draft_vocab, or vocab when the head is shared), where row 0 is
@@ -357,11 +383,17 @@ eagle3_status eagle3_accept(eagle3_ctx *ctx, int32_t batch, int32_t n_rows,
  * path_len[b] and seq_lens[b] += path_len[b].  The draft cache needs no move:
  * its speculative entries are simply overwritten by the next step.
  *   aux_tree [B, n_rows, 3d] of T (from eagle3_verify_tree); aux_new
- *   [B, depth+1, 3d] of T; next_tok [B, depth+1]; new_len [B]. */
+ *   [B, depth+1, 3d] of T; next_tok [B, depth+1]; new_len [B].
+ *   src_dst [B, depth+1, 2] int32 or NULL: the moves of sequence b as
+ *   (source position, destination position) pairs, i.e. (P + path[b][j],
+ *   P + j) with P the committed length before the call, for j < path_len[b];
+ *   (-1, -1) after them and for every j of a sequence whose path is malformed
+ *   (which moves nothing and raises EAGLE3_DEV_BAD_PATH).  These are the
+ *   index lists of the page's cache update over the accepted path. */
 eagle3_status eagle3_compact_kv(eagle3_ctx *ctx, int32_t batch, int32_t *seq_lens, int32_t n_rows,
                                 const int32_t *path, const int32_t *path_len, const int32_t *tokens,
                                 const int32_t *next_root, const void *aux_tree,
-                                void *aux_new, int32_t *next_tok, int32_t *new_len);
+                                void *aux_new, int32_t *next_tok, int32_t *new_len, int32_t *src_dst);
 
 /* Rebind the context to another stream (a hipStream_t; NULL = null stream).
  * Later calls launch there.  The step's calls (eagle3_draft_tree,

@@ -98,6 +98,37 @@ def causal_visible(t: int):
     return [list(range(i + 1)) for i in range(t)]
 
 
+def target_layer(L: dict, shp: Shape, x: np.ndarray, past_k: np.ndarray, past_v: np.ndarray, positions, visible):
+    """One target decoder layer over T new rows (Appendix C's LLaMA block; the
+    new rows attend as in the pages' forward_with_mask).
+
+    x: [T, d] residual stream entering the layer.  past_k / past_v: [P, Hkv, hd]
+    the layer's committed keys and values.  Row i sees all P committed keys and
+    the new rows listed in visible[i].  Returns (x leaving the layer, the new
+    rows' rotated, rounded K and V [T, Hkv, hd]).
+    """
+    rnd = rounder(shp.dtype)
+    T = x.shape[0]
+    hq, hkv, hd = shp.n_heads, shp.n_kv_heads, shp.head_dim
+    h = rnd(rms_norm(x, L["attn_norm"], shp.eps))
+    q = rnd(rope((h @ L["wq"].T).reshape(T, hq, hd), positions, shp.rope_theta))
+    k = rnd(rope((h @ L["wk"].T).reshape(T, hkv, hd), positions, shp.rope_theta))
+    v = rnd((h @ L["wv"].T).reshape(T, hkv, hd))
+    o = np.empty((T, hq, hd))
+    for i in range(T):
+        sel = list(visible[i])
+        o[i] = attend(q[i], np.concatenate([past_k, k[sel]], axis=0), np.concatenate([past_v, v[sel]], axis=0), hkv)
+    x = x + rnd(o).reshape(T, hq * hd) @ L["wo"].T
+    h2 = rnd(rms_norm(x, L["ffn_norm"], shp.eps))
+    act = rnd(silu(h2 @ L["w_gate"].T) * (h2 @ L["w_up"].T))
+    return x + act @ L["w_down"].T, k, v
+
+
+def target_logits(W: dict, shp: Shape, x: np.ndarray) -> np.ndarray:
+    """Final RMSNorm, storage rounding, LM head: logits [T, V] of the residual x [T, d]."""
+    return rounder(shp.dtype)(rms_norm(x, W["final_norm"], shp.eps)) @ W["lm_head"].T
+
+
 def target_forward(W: dict, shp: Shape, cache: KVCache, tokens, positions, visible):
     """One target pass over T new rows (the pages' forward_with_mask).
 
@@ -111,7 +142,6 @@ def target_forward(W: dict, shp: Shape, cache: KVCache, tokens, positions, visib
     tokens = np.asarray(tokens, dtype=np.int64)
     T, d = len(tokens), shp.d
     P = cache.length
-    hq, hkv, hd = shp.n_heads, shp.n_kv_heads, shp.head_dim
     x = W["embed"][tokens].astype(np.float64)
     aux = np.zeros((T, len(shp.taps) * d))
     new_k, new_v = [], []
@@ -119,28 +149,13 @@ def target_forward(W: dict, shp: Shape, cache: KVCache, tokens, positions, visib
         for ti, t in enumerate(shp.taps):
             if t == l:
                 aux[:, ti * d:(ti + 1) * d] = rnd(x)
-        L = W["layers"][l]
-        h = rnd(rms_norm(x, L["attn_norm"], shp.eps))
-        q = rnd(rope((h @ L["wq"].T).reshape(T, hq, hd), positions, shp.rope_theta))
-        k = rnd(rope((h @ L["wk"].T).reshape(T, hkv, hd), positions, shp.rope_theta))
-        v = rnd((h @ L["wv"].T).reshape(T, hkv, hd))
+        x, k, v = target_layer(W["layers"][l], shp, x, cache.k[l][:P], cache.v[l][:P], positions, visible)
         new_k.append(k)
         new_v.append(v)
-        o = np.empty((T, hq, hd))
-        for i in range(T):
-            sel = list(visible[i])
-            keys = np.concatenate([cache.k[l][:P], k[sel]], axis=0)
-            vals = np.concatenate([cache.v[l][:P], v[sel]], axis=0)
-            o[i] = attend(q[i], keys, vals, hkv)
-        x = x + rnd(o).reshape(T, hq * hd) @ L["wo"].T
-        h2 = rnd(rms_norm(x, L["ffn_norm"], shp.eps))
-        act = rnd(silu(h2 @ L["w_gate"].T) * (h2 @ L["w_up"].T))
-        x = x + act @ L["w_down"].T
     for ti, t in enumerate(shp.taps):       # hidden_states[L]: the last layer's output
         if t == shp.n_layers:
             aux[:, ti * d:(ti + 1) * d] = rnd(x)
-    logits = rnd(rms_norm(x, W["final_norm"], shp.eps)) @ W["lm_head"].T
-    return logits, new_k, new_v, aux
+    return target_logits(W, shp, x), new_k, new_v, aux
 
 
 # ----------------------------------------------------------------- EAGLE-3 head

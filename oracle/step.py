@@ -86,6 +86,16 @@ def build_sampled_chain(root: int, root_logits32, expand, K: int, temperature: f
     return toks, np.stack(qs)
 
 
+def compaction_moves(P: int, path):
+    """The cache update over an accepted path as explicit moves ("Advanced
+    speculative decoding: tree drafts and EAGLE", Implementation: the accepted
+    nodes' K/V are appended to the cache in path order, the rest discarded).
+    Tree row r of a step verified at committed length P was written at slot
+    P + r; the j-th node of the path ends at slot P + j.  Returns [(source
+    slot, destination slot)] in path order."""
+    return [(int(P) + int(r), int(P) + j) for j, r in enumerate(path)]
+
+
 class OracleSequence:
     """One sequence's full speculative state: target KV, draft KV, pending inputs."""
 

@@ -24,7 +24,8 @@ EXPORTS = [
     "eagle3_draft_prefill", "eagle3_draft_tree", "eagle3_tree_from_logits", "eagle3_accept", "eagle3_compact_kv",
     "eagle3_sample", "eagle3_set_stream", "eagle3_status_string", "eagle3_device_status", "eagle3_profile", "eagle3_profile_read",
     "eagle3_pack_linear", "eagle3_ttt_workspace_bytes", "eagle3_ttt_attention", "eagle3_paged_kv_bytes",
-    "eagle3_create_paged", "eagle3_set_draft_lengths", "eagle3_spec_decode_metadata",
+    "eagle3_create_paged", "eagle3_set_draft_lengths", "eagle3_spec_decode_metadata", "eagle3_set_draft_logits_out",
+    "eagle3_set_hidden_out",
 ]
 
 
@@ -95,7 +96,9 @@ def lib():
             "eagle3_draft_tree": [P, I32, P, P, P, P, P, P, P, P, P, P, P, P],
             "eagle3_tree_from_logits": [P, I32, P, P, P, P, P, P, P, P, P, P, P],
             "eagle3_accept": [P, I32, I32, P, P, P, P, P, P, P, P, P, P],
-            "eagle3_compact_kv": [P, I32, P, I32, P, P, P, P, P, P, P, P],
+            "eagle3_compact_kv": [P, I32, P, I32, P, P, P, P, P, P, P, P, P],
+            "eagle3_set_draft_logits_out": [P, P],
+            "eagle3_set_hidden_out": [P, P],
             "eagle3_sample": [P, I32, P, C.c_float, P, P],
             "eagle3_ttt_workspace_bytes": [I32, I32, I32, C.POINTER(C.c_size_t)],
             "eagle3_ttt_attention": [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, C.c_size_t, P],
@@ -214,9 +217,17 @@ def eagle3_accept(ctx, batch, n_rows, tokens, parents, argmax, logits, q, unifor
 
 
 def eagle3_compact_kv(ctx, batch, seq_lens, n_rows, path, path_len, tokens, next_root, aux_tree, aux_new, next_tok,
-                      new_len):
+                      new_len, src_dst=None):
     _check(lib().eagle3_compact_kv(ctx, batch, seq_lens, n_rows, path, path_len, tokens, next_root, aux_tree, aux_new,
-                                   next_tok, new_len), "eagle3_compact_kv")
+                                   next_tok, new_len, src_dst), "eagle3_compact_kv")
+
+
+def eagle3_set_hidden_out(ctx, buf):
+    _check(lib().eagle3_set_hidden_out(ctx, buf), "eagle3_set_hidden_out")
+
+
+def eagle3_set_draft_logits_out(ctx, table):
+    _check(lib().eagle3_set_draft_logits_out(ctx, table), "eagle3_set_draft_logits_out")
 
 
 def eagle3_sample(ctx, n, logits, temperature, uniforms, tokens):

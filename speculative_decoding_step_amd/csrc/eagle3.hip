@@ -61,6 +61,8 @@ struct eagle3_ctx {
   KvPages pg;                   // block table of a paged cache (pg.bt null: contiguous)
   size_t kv_us, kv_hs, kv_le;   // unit stride, head stride, elements per layer's K (or V) array
   const int* ndraft = nullptr;  // per-request draft lengths (device, [max_batch]) or null
+  float* dl_out = nullptr;      // draft logits table [max_batch, 1 + emax, Vd] (parity output) or null
+  float* hid_out = nullptr;     // verify residual streams [n_layers + 1, R, d] (parity output) or null
   // workspace
   int* status;
   double* inv_freq;
@@ -285,6 +287,28 @@ __global__ void k_seq_roots(int batch, int K1, const int* __restrict__ roots_in,
 
 inline unsigned nb(size_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
+// n floats src -> dst (n % 4 == 0), 256 threads, one float4 per thread.
+__global__ void k_copy_f32x4(const float* __restrict__ src, float* __restrict__ dst, size_t n4) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) ((float4*)dst)[i] = ((const float4*)src)[i];
+}
+
+// Draft logits table output: rows [b * per, (b + 1) * per) of src (Vd floats
+// each) go to rows row0 .. row0 + per - 1 of sequence b's table block.
+// grid (ceil(Vd / 1024), batch * per), 256 threads, float4 when Vd % 4 == 0.
+__global__ void k_copy_logit_rows(const float* __restrict__ src, int per, int Vd, float* __restrict__ dst,
+                                  size_t seq_stride, int row0) {
+  const int r = blockIdx.y, b = r / per, i = r % per;
+  const float* s = src + (size_t)r * Vd;
+  float* d = dst + (size_t)b * seq_stride + (size_t)(row0 + i) * Vd;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if ((Vd & 3) == 0) {
+    if (c < Vd) *(float4*)(d + c) = *(const float4*)(s + c);
+  } else {
+    for (int j = c; j < min(c + 4, Vd); ++j) d[j] = s[j];
+  }
+}
+
 // ------------------------------------------------------------ profiling
 // With record = false the caller hands the event pair to a launch that records
 // it itself (at the kernel's start and end).
@@ -390,7 +414,16 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
   const int d = s.d_model, qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
   const bool bf = c->bf16;
   hipStream_t st = c->st;
+  auto record = [&](int l) {  // parity output: the residual entering layer l (l = n_layers: leaving the last)
+    if (!c->hid_out) return;
+    const size_t n = (size_t)R * d;
+    if (n % 4 == 0)
+      k_copy_f32x4<<<nb(n / 4, 256), 256, 0, st>>>(c->xres, c->hid_out + (size_t)l * n, n / 4);
+    else
+      (void)hipMemcpyAsync(c->hid_out + (size_t)l * n, c->xres, n * sizeof(float), hipMemcpyDeviceToDevice, st);
+  };
   embed_rows(bf, c->tw.embed, c->rtok, c->xres, R, d, s.vocab, c->status, st);
+  record(0);
   // Residual entering layer l (after adding S partials of the previous GEMM, if
   // any): captured into the aux columns of every tap equal to l and normalised
   // with w into out.
@@ -432,6 +465,7 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
     } else {
       resid_add(c->xres, c->part, S, (size_t)R * d, R, d, d, st);
     }
+    record(l + 1);
   }
   if (lm == EAGLE3_LM_NONE) return;
   int n = R;
@@ -452,14 +486,17 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
 }
 
 // The draft decoder layer over R rows: x (fp32 [R, d]) is g or a on entry and
-// a on exit; tokens in tok; row metadata rm (draft KV cache).
-void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const RowMeta& rm) {
+// a on exit; tokens in tok; row metadata rm (draft KV cache).  fc_splits > 0:
+// x is formed on entry from that many fusion-FC split partials in c->part
+// (g = W_fc [l; m; h]) by the same kernel that builds the layer's input.
+void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const RowMeta& rm, int fc_splits = 0) {
   const eagle3_shape& s = c->sh;
   const eagle3_head_weights& H = c->hw;
   const int d = s.d_model, qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
   const bool bf = c->bf16;
   hipStream_t st = c->st;
-  draft_input(bf, c->tw.embed, tok, x, H.input_norm, H.hidden_norm, c->hbuf, R, d, s.vocab, s.rms_eps, c->status, st);
+  draft_input(bf, c->tw.embed, tok, x, fc_splits ? c->part : nullptr, fc_splits, (size_t)R * d, H.input_norm,
+              H.hidden_norm, c->hbuf, R, d, s.vocab, s.rms_eps, c->status, st);
   const GemmSegs qkv = make_segs(H.wq, qdim, H.wk, kvdim, H.wv, kvdim);
   int S = run_gemm(c, c->hbuf, R, 2 * d, qkv);
   char* kc = kv_layer(c, c->kv_d, 0, 0);
@@ -474,11 +511,16 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
   resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
 }
 
-// Draft logits of n rows of a (fp32 [n, d]) -> c->logits; top-K + lse.
-void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature) {
+// Draft logits of n rows of a (fp32 [n, d]) -> c->logits; top-K + lse.  With a
+// draft logits table set, the n rows (per rows of each of n / per sequences)
+// are also copied to table rows row0 .. row0 + per - 1.
+void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, int per, int row0) {
   const eagle3_shape& s = c->sh;
   rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st);
   run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->dhead, c->Vd), c->logits);
+  if (c->dl_out && n > 0)
+    k_copy_logit_rows<<<dim3(nb(c->Vd, 1024), n), 256, 0, c->st>>>(c->logits, per, c->Vd, c->dl_out,
+                                                                   (size_t)(1 + c->emax) * c->Vd, row0);
   topk_lse(c->logits, n, c->Vd, c->Vd, K, temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids,
            c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
   map_draft_ids(c->tk_ids, n * K, c->d2t, c->Vd, c->st);
@@ -526,7 +568,7 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
         tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, n, d, st);
         draft_layer(c, n, k, dr.tok, c->dx, dr_meta(c));
         if (dd + 1 < D) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, n, k, c->emax, d, st);
-        draft_lm(c, n, c->dx, k, 1.f);
+        draft_lm(c, n, c->dx, k, 1.f, k, 1 + (dd - 1) * k);
       }
       tree_children(ts, dd + 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
     }
@@ -552,7 +594,7 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
         tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, batch, d, st);
         draft_layer(c, batch, 1, dr.tok, c->dx, dr_meta(c));
         if (j + 1 < K) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, batch, 1, c->emax, d, st);
-        draft_lm(c, batch, c->dx, 1, T);
+        draft_lm(c, batch, c->dx, 1, T, 1, j);
         chain_draw(j, K, c->logits, Vd, Vd, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q,
                    c->chain_tok, batch, c->tk_wsum, c->d2t, st);
       }
@@ -716,6 +758,18 @@ eagle3_status eagle3_create_paged(const eagle3_shape* s, const eagle3_spec_cfg* 
   return create_impl(s, cfg, tw, hw, max_batch, max_rows, (int32_t)cap, pages, ws, ws_bytes, kv_t, kv_d, stream, out);
 }
 
+eagle3_status eagle3_set_hidden_out(eagle3_ctx* c, float* buf) {
+  if (!c) return EAGLE3_EINVAL;
+  c->hid_out = buf;
+  return EAGLE3_OK;
+}
+
+eagle3_status eagle3_set_draft_logits_out(eagle3_ctx* c, float* table) {
+  if (!c) return EAGLE3_EINVAL;
+  c->dl_out = table;
+  return EAGLE3_OK;
+}
+
 eagle3_status eagle3_set_draft_lengths(eagle3_ctx* c, const int32_t* n_draft) {
   if (!c) return EAGLE3_EINVAL;
   c->ndraft = n_draft;
@@ -837,9 +891,8 @@ eagle3_status eagle3_draft_prefill(eagle3_ctx* c, int32_t seq_begin, int32_t bat
   const int R = batch * n_rows, d = c->sh.d_model;
   k_prefill_meta<<<nb(R, 128), 128, 0, c->st>>>(batch, seq_begin, n_rows, start, next_tok, c->S_cap, c->rm, c->rtok,
                                                  c->status);
-  int S = run_gemm(c, aux, R, 3 * d, make_segs(c->hw.fc, d));
-  sum_store(c->dx, c->part, S, (size_t)R * d, R, d, d, c->st);
-  draft_layer(c, R, n_rows, c->rtok, c->dx, c->rm);
+  const int S = run_gemm(c, aux, R, 3 * d, make_segs(c->hw.fc, d));
+  draft_layer(c, R, n_rows, c->rtok, c->dx, c->rm, S);
   return last_error();
 }
 
@@ -858,11 +911,10 @@ eagle3_status eagle3_draft_tree(eagle3_ctx* c, int32_t batch, const int32_t* seq
   hipStream_t st = c->st;
   k_catchup_meta<<<nb(Rc, 128), 128, 0, st>>>(batch, W, seq_lens, new_len, next_tok, c->S_cap, c->rm, c->rtok,
                                                c->gidx, c->roots, c->status);
-  int S = run_gemm(c, aux_new, Rc, 3 * d, make_segs(c->hw.fc, d));
-  sum_store(c->dx, c->part, S, (size_t)Rc * d, Rc, d, d, st);
-  draft_layer(c, Rc, W, c->rtok, c->dx, c->rm);
+  const int S = run_gemm(c, aux_new, Rc, 3 * d, make_segs(c->hw.fc, d));
+  draft_layer(c, Rc, W, c->rtok, c->dx, c->rm, S);
   gather_rows_f32(c->a_last, c->dx, c->gidx, batch, d, st);
-  draft_lm(c, batch, c->a_last, chain ? 1 : c->cfg.topk, chain ? c->cfg.temperature : 1.f);
+  draft_lm(c, batch, c->a_last, chain ? 1 : c->cfg.topk, chain ? c->cfg.temperature : 1.f, 1, 0);
   TreeOut out{tokens, parents, depth, pos, mask, score};
   build_tree(c, batch, seq_lens, nullptr, uniforms, out, q);
   return last_error();
@@ -922,7 +974,8 @@ eagle3_status eagle3_accept(eagle3_ctx* c, int32_t batch, int32_t n_rows, const 
 
 eagle3_status eagle3_compact_kv(eagle3_ctx* c, int32_t batch, int32_t* seq_lens, int32_t n_rows, const int32_t* path,
                                 const int32_t* path_len, const int32_t* tokens, const int32_t* next_root,
-                                const void* aux_tree, void* aux_new, int32_t* next_tok, int32_t* new_len) {
+                                const void* aux_tree, void* aux_new, int32_t* next_tok, int32_t* new_len,
+                                int32_t* src_dst) {
   if (!c || !seq_lens || !path || !path_len || !tokens || !next_root || !aux_tree || !aux_new || !next_tok || !new_len)
     return EAGLE3_EINVAL;
   if (batch < 1 || batch > c->B || n_rows < 1 || n_rows > 64) return EAGLE3_ECAPACITY;
@@ -931,7 +984,7 @@ eagle3_status eagle3_compact_kv(eagle3_ctx* c, int32_t batch, int32_t* seq_lens,
   compact_kv(c->bf16, batch, seq_lens, path, path_len, maxp, n_rows, c->kv_t, s.n_layers, c->kv_le, c->kv_us, c->kv_hs,
              c->pg, s.n_kv_heads, c->S_cap, s.head_dim, c->status, c->st);
   compact_finish(c->bf16, batch, seq_lens, n_rows, maxp, path, path_len, tokens, next_root, aux_tree, 3 * s.d_model,
-                 aux_new, next_tok, new_len, c->st);
+                 aux_new, next_tok, new_len, src_dst, c->st);
   return last_error();
 }
 

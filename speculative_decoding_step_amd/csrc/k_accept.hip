@@ -429,19 +429,26 @@ __global__ __launch_bounds__(128) void k_compact_kv(const int* __restrict__ seq_
 }
 
 // grid (B, maxp): block (b, j) copies the aux row of path node j (if j < n)
-// in 16-byte chunks; block (b, 0) also writes next_tok, new_len and seq_lens.
+// in 16-byte chunks; block (b, 0) also writes next_tok, new_len, the move list
+// src_dst (if given) and seq_lens.
 template <typename E>
 __global__ __launch_bounds__(256) void k_compact_finish(int* __restrict__ seq_lens, int n_rows, int maxp,
                                                         const int* __restrict__ path, const int* __restrict__ path_len,
                                                         const int* __restrict__ tokens, const int* __restrict__ next_root,
                                                         const E* __restrict__ aux_tree, int aux_w, E* __restrict__ aux_new,
-                                                        int* __restrict__ next_tok, int* __restrict__ new_len) {
+                                                        int* __restrict__ next_tok, int* __restrict__ new_len,
+                                                        int* __restrict__ src_dst) {
   const int b = blockIdx.x, jrow = blockIdx.y;
   const int n = path_len[b];
+  const int P = seq_lens[b];  // read by every thread before thread 0 of block (b, 0) advances it
   const int* pb = path + (size_t)b * maxp;
   bool ok = n >= 1 && n <= maxp && pb[0] == 0;
   for (int j = 1; ok && j < n; ++j) ok = pb[j] > pb[j - 1] && pb[j] < n_rows;
-  if (!ok) return;
+  if (!ok) {
+    if (jrow == 0 && src_dst)
+      for (int j = threadIdx.x; j < 2 * maxp; j += blockDim.x) src_dst[(size_t)b * maxp * 2 + j] = -1;
+    return;
+  }
   if (jrow < n) {
     const E* src = aux_tree + ((size_t)b * n_rows + pb[jrow]) * aux_w;
     E* dst = aux_new + ((size_t)b * maxp + jrow) * aux_w;
@@ -466,12 +473,18 @@ __global__ __launch_bounds__(256) void k_compact_finish(int* __restrict__ seq_le
     }
   }
   if (jrow != 0) return;
-  for (int j = threadIdx.x; j < maxp; j += blockDim.x)
+  for (int j = threadIdx.x; j < maxp; j += blockDim.x) {
     next_tok[(size_t)b * maxp + j] =
         j < n ? (j + 1 < n ? tokens[(size_t)b * n_rows + pb[j + 1]] : next_root[b]) : -1;
+    if (src_dst) {
+      src_dst[((size_t)b * maxp + j) * 2] = j < n ? P + pb[j] : -1;
+      src_dst[((size_t)b * maxp + j) * 2 + 1] = j < n ? P + j : -1;
+    }
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     new_len[b] = n;
-    seq_lens[b] += n;
+    seq_lens[b] = P + n;
   }
 }
 
@@ -521,15 +534,15 @@ void compact_kv(bool bf16, int batch, const int* seq_lens, const int* path, cons
 
 void compact_finish(bool bf16, int batch, int* seq_lens, int n_rows, int maxp, const int* path, const int* path_len,
                     const int* tokens, const int* next_root, const void* aux_tree, int aux_w, void* aux_new,
-                    int* next_tok, int* new_len, hipStream_t st) {
+                    int* next_tok, int* new_len, int* src_dst, hipStream_t st) {
   if (bf16)
     k_compact_finish<uint16_t><<<dim3(batch, maxp), 256, 0, st>>>(seq_lens, n_rows, maxp, path, path_len, tokens, next_root,
                                                       (const uint16_t*)aux_tree, aux_w, (uint16_t*)aux_new, next_tok,
-                                                      new_len);
+                                                      new_len, src_dst);
   else
     k_compact_finish<uint32_t><<<dim3(batch, maxp), 256, 0, st>>>(seq_lens, n_rows, maxp, path, path_len, tokens, next_root,
                                                       (const uint32_t*)aux_tree, aux_w, (uint32_t*)aux_new, next_tok,
-                                                      new_len);
+                                                      new_len, src_dst);
 }
 
 }  // namespace e3

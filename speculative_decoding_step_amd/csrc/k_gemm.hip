@@ -397,15 +397,6 @@ __global__ void k_resid_add(float* __restrict__ x, const float* __restrict__ par
   x[i] += sum_splits(part + (size_t)m * ldp + n, S, sstride);
 }
 
-__global__ void k_sum_store(float* __restrict__ out, const float* __restrict__ part, int S, size_t sstride,
-                            int M, int N, int ldp) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (size_t)M * N) return;
-  const int m = i / N, n = i % N;
-  const float s = sum_splits(part + (size_t)m * ldp + n, S, sstride);
-  out[i] = s;
-}
-
 template <typename T>
 __global__ void k_silu_mul(T* __restrict__ out, const float* __restrict__ part, int S, size_t sstride, int M,
                            int F, int ldp) {
@@ -422,10 +413,6 @@ static inline unsigned nblk(size_t n, int b) { return (unsigned)((n + b - 1) / b
 void resid_add(float* x, const float* part, int S, size_t sstride, int M, int N, int ldp, hipStream_t st) {
   if (M <= 0) return;
   k_resid_add<<<nblk((size_t)M * N, 256), 256, 0, st>>>(x, part, S, sstride, M, N, ldp);
-}
-void sum_store(float* out, const float* part, int S, size_t sstride, int M, int N, int ldp, hipStream_t st) {
-  if (M <= 0) return;
-  k_sum_store<<<nblk((size_t)M * N, 256), 256, 0, st>>>(out, part, S, sstride, M, N, ldp);
 }
 void silu_mul(bool bf16, void* out, const float* part, int S, size_t sstride, int M, int F, int ldp,
               hipStream_t st) {

@@ -158,10 +158,15 @@ void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, in
 // ---------------------------------------------------------------- draft input
 // One block per row, one float4 column group per thread (NV groups when the
 // row is wider): out[r] = [input_norm(embed[token]) ; hidden_norm(x[r])].
-// Rows whose width is not a multiple of 4 use the element loop.
+// With split partials (part != null, the fusion FC's K splits) the feature row
+// is first formed from them, x[r] = sum of the S splits in split order, and
+// stored as the layer's residual stream: the FC's reduction, the two norms
+// and the concatenation are one pass.  Rows whose width is not a multiple of 4
+// use the element loop.
 template <typename T, int NV>
 __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embed, const int* __restrict__ tokens,
-                                                      const float* __restrict__ x, const T* __restrict__ w_in,
+                                                      float* __restrict__ x, const float* __restrict__ part, int S,
+                                                      size_t sstride, const T* __restrict__ w_in,
                                                       const T* __restrict__ w_hid, T* __restrict__ out, int d,
                                                       int V, float eps, int* status) {
   __shared__ float red[16];
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embe
   const bool ok = t >= 0 && t < V;
   if (!ok && tid == 0 && t != -1) raise_flag(status, E3_DEV_BAD_TOKEN);
   if (!ok) t = 0;
-  const float* xr = x + (size_t)r * d;
+  float* xr = x + (size_t)r * d;
   const T* er = embed + (size_t)t * d;
   float4 e[NV], h[NV];
   float se = 0.f, sx = 0.f;
@@ -179,7 +184,12 @@ __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embe
     const int c = tid + nt * i;
     if (c < d4) {
       e[i] = ok ? ld4<T>(er, 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      h[i] = *(const float4*)(xr + 4 * c);
+      if (part) {
+        h[i] = sum_splits4((const float4*)(part + (size_t)r * d) + c, S, sstride >> 2);
+        *(float4*)(xr + 4 * c) = h[i];
+      } else {
+        h[i] = *(const float4*)(xr + 4 * c);
+      }
       se += e[i].x * e[i].x + e[i].y * e[i].y + e[i].z * e[i].z + e[i].w * e[i].w;
       sx += h[i].x * h[i].x + h[i].y * h[i].y + h[i].z * h[i].z + h[i].w * h[i].w;
     }
@@ -202,7 +212,8 @@ __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embe
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ embed, const int* __restrict__ tokens,
-                                                         const float* __restrict__ x, const T* __restrict__ w_in,
+                                                         float* __restrict__ x, const float* __restrict__ part, int S,
+                                                         size_t sstride, const T* __restrict__ w_in,
                                                          const T* __restrict__ w_hid, T* __restrict__ out, int d,
                                                          int V, float eps, int* status) {
   __shared__ float red[16];
@@ -211,10 +222,11 @@ __global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ e
   const bool ok = t >= 0 && t < V;
   if (!ok && threadIdx.x == 0 && t != -1) raise_flag(status, E3_DEV_BAD_TOKEN);
   if (!ok) t = 0;
-  const float* xr = x + (size_t)r * d;
+  float* xr = x + (size_t)r * d;
   float se = 0.f, sx = 0.f;
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
     const float e = ok ? ld<T>(embed, (size_t)t * d + i) : 0.f;
+    if (part) xr[i] = sum_splits(part + (size_t)r * d + i, S, sstride);
     se += e * e;
     sx += xr[i] * xr[i];
   }
@@ -230,29 +242,31 @@ __global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ e
 }
 
 template <typename T>
-static void launch_draft_input(const T* embed, const int* tokens, const float* x, const T* w_in, const T* w_hid,
-                               T* out, int R, int d, int V, float eps, int* status, hipStream_t st) {
+static void launch_draft_input(const T* embed, const int* tokens, float* x, const float* part, int S, size_t sstride,
+                               const T* w_in, const T* w_hid, T* out, int R, int d, int V, float eps, int* status,
+                               hipStream_t st) {
   const int d4 = d / 4;
   if (d % 4 == 0 && d4 <= 2048) {
     const int nt = std::min(1024, (d4 + 63) / 64 * 64);
     if (d4 <= nt)
-      k_draft_input<T, 1><<<R, nt, 0, st>>>(embed, tokens, x, w_in, w_hid, out, d, V, eps, status);
+      k_draft_input<T, 1><<<R, nt, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status);
     else
-      k_draft_input<T, 2><<<R, nt, 0, st>>>(embed, tokens, x, w_in, w_hid, out, d, V, eps, status);
+      k_draft_input<T, 2><<<R, nt, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status);
   } else {
-    k_draft_input_any<T><<<R, 256, 0, st>>>(embed, tokens, x, w_in, w_hid, out, d, V, eps, status);
+    k_draft_input_any<T><<<R, 256, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status);
   }
 }
 
-void draft_input(bool bf16, const void* embed, const int* tokens, const float* x, const void* w_in,
-                 const void* w_hid, void* out, int R, int d, int V, float eps, int* status, hipStream_t st) {
+void draft_input(bool bf16, const void* embed, const int* tokens, float* x, const float* part, int S,
+                 size_t sstride, const void* w_in, const void* w_hid, void* out, int R, int d, int V, float eps,
+                 int* status, hipStream_t st) {
   if (R <= 0) return;
   if (bf16)
-    launch_draft_input<bf16_t>((const bf16_t*)embed, tokens, x, (const bf16_t*)w_in, (const bf16_t*)w_hid,
-                               (bf16_t*)out, R, d, V, eps, status, st);
+    launch_draft_input<bf16_t>((const bf16_t*)embed, tokens, x, part, S, sstride, (const bf16_t*)w_in,
+                               (const bf16_t*)w_hid, (bf16_t*)out, R, d, V, eps, status, st);
   else
-    launch_draft_input<float>((const float*)embed, tokens, x, (const float*)w_in, (const float*)w_hid, (float*)out,
-                              R, d, V, eps, status, st);
+    launch_draft_input<float>((const float*)embed, tokens, x, part, S, sstride, (const float*)w_in,
+                              (const float*)w_hid, (float*)out, R, d, V, eps, status, st);
 }
 
 // ----------------------------------------------------------- rope + KV write

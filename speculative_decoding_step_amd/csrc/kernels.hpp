@@ -58,7 +58,6 @@ int gemm_ntot(const GemmSegs& s);
 void resid_add(float* x, const float* part, int S, size_t sstride, int M, int N, int ldp, hipStream_t st);
 void silu_mul(bool bf16, void* out, const float* part, int S, size_t sstride, int M, int F, int ldp,
               hipStream_t st);
-void sum_store(float* out, const float* part, int S, size_t sstride, int M, int N, int ldp, hipStream_t st);
 
 // Embedding rows (T) -> fp32 residual rows; invalid token -> zeros + flag.
 void embed_rows(bool bf16, const void* table, const int* tokens, float* x, int R, int d, int V,
@@ -69,9 +68,12 @@ void add_rmsnorm(bool bf16, float* x, const float* part, int S, size_t sstride, 
                  int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st);
 void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, int R, int d, float eps,
              void* tap, int tap_ld, hipStream_t st);
-// Draft input: out[r] = [T(rms(embed[tok[r]]) * w_in) ; T(rms(x[r]) * w_hid)], [R, 2d].
-void draft_input(bool bf16, const void* embed, const int* tokens, const float* x, const void* w_in,
-                 const void* w_hid, void* out, int R, int d, int V, float eps, int* status, hipStream_t st);
+// Draft input: out[r] = [T(rms(embed[tok[r]]) * w_in) ; T(rms(x[r]) * w_hid)], [R, 2d].  With part != null
+// x[r] is first set to the sum of the S split partials part[s][r][0..d) (split stride sstride): the fusion
+// FC's reduction in the same pass.
+void draft_input(bool bf16, const void* embed, const int* tokens, float* x, const float* part, int S,
+                 size_t sstride, const void* w_in, const void* w_hid, void* out, int R, int d, int V, float eps,
+                 int* status, hipStream_t st);
 
 // KV cache addressing of one layer's K (or V) array: element (unit u, KV head
 // g, row r, dim i) sits at u * unit_stride + g * head_stride + r * hd + i.

@@ -92,6 +92,6 @@ void compact_kv(bool bf16, int batch, const int* seq_lens, const int* path, cons
                 const KvPages& pg, int Hkv, int S_cap, int hd, int* status, hipStream_t st);
 void compact_finish(bool bf16, int batch, int* seq_lens, int n_rows, int maxp, const int* path, const int* path_len,
                     const int* tokens, const int* next_root, const void* aux_tree, int aux_w, void* aux_new,
-                    int* next_tok, int* new_len, hipStream_t st);
+                    int* next_tok, int* new_len, int* src_dst, hipStream_t st);
 
 }  // namespace e3

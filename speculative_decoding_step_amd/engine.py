@@ -99,8 +99,9 @@ class Engine:
             kvt, kvd = B.eagle3_paged_kv_bytes(self.shape, block_size, self.n_blocks)
         else:
             kvt, kvd = B.eagle3_kv_bytes(self.shape, batch, max_seq)
-        self.kv_target = torch.empty(kvt, dtype=torch.uint8, device=self.dev)
-        self.kv_draft = torch.empty(kvd, dtype=torch.uint8, device=self.dev)
+        # zero-filled, so slots no call has written compare equal between engines (and hold finite values)
+        self.kv_target = torch.zeros(kvt, dtype=torch.uint8, device=self.dev)
+        self.kv_draft = torch.zeros(kvd, dtype=torch.uint8, device=self.dev)
         wsb = B.eagle3_workspace_bytes(self.shape, self.cfg, batch, self.max_rows, max_seq)
         self.workspace = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
         if block_size:
@@ -189,6 +190,20 @@ class Engine:
             B.eagle3_set_draft_lengths(self.ctx, self.n_draft.data_ptr())
         else:
             self.n_draft.copy_(nd)  # same buffer: a captured step sees the new lengths
+
+    def record_draft_logits(self, on: bool = True):
+        """Make every later draft also write its draft-logits table (a parity output,
+        eagle3_set_draft_logits_out): self.draft_table [B, 1 + E, V_d] float32, row 0
+        the root's draft row, row 1 + r expansion row r in creation order."""
+        if on:
+            s = self.spec
+            e = max(1, (s.depth - 1) * s.topk) if not self.chain else max(1, s.depth - 1)
+            vd = self.ms.draft_vocab or self.ms.vocab
+            self.draft_table = torch.full((self.B, 1 + e, vd), float("nan"), dtype=torch.float32, device=self.dev)
+            B.eagle3_set_draft_logits_out(self.ctx, self.draft_table.data_ptr())
+        else:
+            B.eagle3_set_draft_logits_out(self.ctx, None)
+            self.draft_table = None
 
     def kv_logical(self, which: str = "target"):
         """A cache as [L, 2, B, Hkv, max_seq, hd] in position order: a view of a
@@ -296,6 +311,22 @@ class Engine:
             B.eagle3_set_stream(self.ctx, self.stream.cuda_stream)
         self.stream.wait_stream(cap)
         self.graph = g
+        return g
+
+    def capture_call(self, fn):
+        """Capture one call sequence fn() into its own HIP graph (the same way as the
+        step); returns the graph.  For timing a part of the step alone, e.g. the
+        verify pass, whose replays are idempotent."""
+        cap = torch.cuda.Stream(self.dev)
+        cap.wait_stream(self.stream)
+        g = torch.cuda.CUDAGraph()
+        B.eagle3_set_stream(self.ctx, cap.cuda_stream)
+        try:
+            with torch.cuda.graph(g, stream=cap):
+                fn()
+        finally:
+            B.eagle3_set_stream(self.ctx, self.stream.cuda_stream)
+        self.stream.wait_stream(cap)
         return g
 
     def replay(self):

@@ -63,3 +63,42 @@ def random_tree(rng, n_rows, vocab):
 
 def to_dev(a, dtype=torch.int32):
     return torch.as_tensor(np.asarray(a), device="cuda").to(dtype)
+
+
+def dev_weight_np(seed, name, shape, dtype="bf16", sigma=0.02, rows=None):
+    """A seeded weight generated on the device exactly as the engine generates it,
+    returned as float64 numpy (optionally only the given rows)."""
+    from speculative_decoding_step_amd import synth
+    t = synth.normal_t(seed, name, shape, "cuda", sigma, dtype)
+    if rows is not None:
+        t = t[torch.as_tensor(np.asarray(rows, dtype=np.int64), device="cuda")]
+    out = t.to(torch.float64).cpu().numpy()
+    del t
+    return out
+
+
+class LazyLayers:
+    """W["layers"] for the oracle at the 8B shape: layer l's float64 weights are made
+    on first access (seeded on the device, as the engine makes them) and the previous
+    layer's are dropped, so a full-depth oracle pass holds one layer at a time."""
+
+    def __init__(self, ms, seed, log=None):
+        self.ms, self.seed, self.log = ms, seed, log
+        self.cur, self.layer = -1, None
+
+    def __len__(self):
+        return self.ms.n_layers
+
+    def __getitem__(self, l):
+        if l != self.cur:
+            ms = self.ms
+            d, qd, kvd = ms.d, ms.n_heads * ms.head_dim, ms.n_kv_heads * ms.head_dim
+            self.layer = None
+            L = {"attn_norm": np.ones(d), "ffn_norm": np.ones(d)}
+            for key, shape in [("wq", (qd, d)), ("wk", (kvd, d)), ("wv", (kvd, d)), ("wo", (d, qd)),
+                               ("w_gate", (ms.ffn, d)), ("w_up", (ms.ffn, d)), ("w_down", (d, ms.ffn))]:
+                L[key] = dev_weight_np(self.seed, f"l{l}.{key}", shape, ms.dtype)
+            self.layer, self.cur = L, l
+            if self.log:
+                self.log(l)
+        return self.layer

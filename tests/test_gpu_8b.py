@@ -154,8 +154,12 @@ def test_8b_batch64_ragged_tree_step():
     eng.prefill(prompts)
     torch.cuda.synchronize()
     print("  prefill done", flush=True)
+    eng.logits = torch.zeros(Bn * n, ms.vocab, dtype=torch.float32, device="cuda")  # verify writes every row's logits
+    hid = torch.zeros(ms.n_layers + 1, Bn * n, ms.d, dtype=torch.float32, device="cuda")
+    B.eagle3_set_hidden_out(eng.ctx, hid.data_ptr())
     eng.draft()
     eng.verify()
+    B.eagle3_set_hidden_out(eng.ctx, None)
     eng.accept()
     torch.cuda.synchronize()
     assert eng.device_status() == 0
@@ -169,6 +173,13 @@ def test_8b_batch64_ragged_tree_step():
     kv = kv_view(eng)
     layers = [0, 1, ms.n_layers - 1]
     pre = [kv[layers, :, b, :, int(lens[b]):int(lens[b]) + n].clone() for b in range(Bn)]
+    s0 = int(np.argmin(lens))
+    P0 = int(lens[s0])
+    kv_s0 = kv[:, :, s0, :, :P0].to(torch.float64).cpu().numpy()             # committed prefix, all layers
+    tkv_s0 = kv[:, :, s0, :, P0:P0 + n].float().cpu().numpy()               # the tree rows' K/V, all layers
+    hid_s0 = hid[:, s0 * n:(s0 + 1) * n].cpu().numpy()
+    g_logits = eng.logits[s0 * n:(s0 + 1) * n].cpu().numpy()
+    del hid
     eng.compact()
     torch.cuda.synchronize()
     assert eng.device_status() == 0
@@ -188,6 +199,9 @@ def test_8b_batch64_ragged_tree_step():
     eng.close()
     del eng, pre, kv
     torch.cuda.empty_cache()
+    from test_gpu_8b_logits import per_layer_parity
+    per_layer_parity(ms, w.target_seed, kv_s0, hid_s0, tkv_s0, tokens[s0], [int(x) for x in parents[s0]], P0,
+                     g_logits, f"batch-64 seq {s0} (P={P0}, large-M GEMMs)")
     for b in checks:
         k, tk, tv, aux = _two_layer_oracle(w.target_seed, prompts[b], tokens[b], list(parents[b]))
         e, _ = _close(aux_tree[b], aux, ("tap 2", b))

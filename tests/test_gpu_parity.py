@@ -15,6 +15,7 @@ import torch
 from gpu_util import (kv_view, logits_close, make_engine, margin_tol, oracle_weights, random_tree, to_dev,
                       toy_shape, top2_margin)
 from oracle.accept import chain_rejection, greedy_walk, tree_rejection
+from oracle.step import compaction_moves
 from oracle.llama import KVCache, causal_visible, target_forward
 from oracle.numerics import probs_f32, sample_inverse_cdf
 from oracle.step import build_sampled_chain
@@ -567,10 +568,16 @@ def test_compact_kv_moves_path_rows():
     ntok = torch.zeros(Bn, maxp, dtype=torch.int32, device="cuda")
     nlen = torch.zeros(Bn, dtype=torch.int32, device="cuda")
     keep = [to_dev(paths), to_dev(lens), to_dev(toks)]
+    src_dst = torch.full((Bn, maxp, 2), 12345, dtype=torch.int32, device="cuda")
     B.eagle3_compact_kv(eng.ctx, Bn, _p(seq), n, _p(keep[0]), _p(keep[1]), _p(keep[2]), _p(nroot),
-                        _p(aux_tree), _p(aux_new), _p(ntok), _p(nlen))
+                        _p(aux_tree), _p(aux_new), _p(ntok), _p(nlen), _p(src_dst))
     torch.cuda.synchronize()
     _status_clear(eng)
+    moves = src_dst.cpu().numpy()
+    for b in range(Bn):
+        ref = compaction_moves(P[b], paths[b][:lens[b]])
+        assert [tuple(m) for m in moves[b, :lens[b]]] == ref, b
+        assert (moves[b, lens[b]:] == -1).all(), b
     after = kv
     for b in range(Bn):
         L = lens[b]
@@ -600,9 +607,11 @@ def test_device_status_flags_bad_inputs():
     aux = torch.zeros(1, n, 3 * eng.ms.d, device="cuda").to(eng.tdt)
     keep = [to_dev([5]), to_dev([3]), to_dev([1]), torch.zeros(1, D + 1, 3 * eng.ms.d, device="cuda").to(eng.tdt),
             torch.zeros(1, D + 1, dtype=torch.int32, device="cuda"), torch.zeros(1, dtype=torch.int32, device="cuda")]
+    moves = torch.zeros(1, D + 1, 2, dtype=torch.int32, device="cuda")
     B.eagle3_compact_kv(eng.ctx, 1, _p(keep[0]), n, _p(bad_path), _p(keep[1]), _p(toks), _p(keep[2]),
-                        _p(aux), _p(keep[3]), _p(keep[4]), _p(keep[5]))
+                        _p(aux), _p(keep[3]), _p(keep[4]), _p(keep[5]), _p(moves))
     assert eng.device_status() & B.DEV_BAD_PATH
+    assert (moves.cpu().numpy() == -1).all() and keep[0].item() == 5     # nothing moved, length unchanged
     with pytest.raises(B.Eagle3Error):
         B.eagle3_verify_tree(eng.ctx, 0, 1, _p(seq), 65, _p(toks), None, _p(toks), B.LM_ALL, None, None, None, None)
     eng.close()

@@ -98,3 +98,27 @@ def test_greedy_spec_equals_vanilla_small_config_short():
     van = vanilla_generate(W, shp, prompt, 6)
     out, _ = spec_generate(W, H, shp, SpecConfig(w.mode, w.depth, w.topk, w.n_nodes), prompt, 6)
     assert out == van
+
+
+def test_compaction_moves_match_the_commit(toy_model):
+    """The move list (source slot P + path[j] -> destination P + j) is exactly what
+    the oracle's commit does to the cache: every destination holds the K/V the
+    verify pass computed for the source row, rows off the path are dropped, and a
+    brute-force search over the tree rows finds each source."""
+    from oracle.step import compaction_moves
+    ms, shp, W, H = toy_model("f32")
+    seq = OracleSequence(W, H, shp, SpecConfig("greedy_tree", 3, 2, 6), 64)
+    seq.prefill(synth.tokens_np(5, "p", 9, ms.vocab))
+    P = seq.P
+    tree = Tree([4, 1, 2, 7, 3, 5, 6], [-1, 0, 0, 1, 1, 2, 4], [0, 1, 1, 2, 2, 2, 3], [np.float32(0)] * 7, [-2] * 7)
+    logits, k, v, aux = seq.verify(tree)
+    path = [0, 1, 4, 6]
+    seq.compact(tree, path, 9, k, v, aux)
+    moves = compaction_moves(P, path)
+    assert [dst for _, dst in moves] == list(range(P, P + len(path)))
+    for j, (src, dst) in enumerate(moves):
+        row = next(r for r in range(len(tree.tokens)) if P + r == src)     # brute force over the tree rows
+        assert row == path[j]
+        for l in range(shp.n_layers):
+            assert np.array_equal(seq.cache.k[l][dst], k[l][row]) and np.array_equal(seq.cache.v[l][dst], v[l][row])
+    assert seq.P == P + len(path)
