@@ -431,6 +431,23 @@ eagle3_status eagle3_ttt_attention(int32_t dtype, int32_t T, int32_t S, int32_t 
                                    int32_t head_dim, const void *q, const void *k0, const void *v0, const void *ks,
                                    const void *vs, void *out, void *ws, size_t ws_bytes, void *stream);
 
+/* eagle3_ttt_attention for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * allocation.  Same computation and arguments, without ws / ws_bytes: the
+ * scratch is a fixed array of EAGLE3_TTT_STATIC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends.  The bf16 path at
+ * head_dim 64 or 128 uses none of it; fp32 and other head sizes need
+ * eagle3_ttt_workspace_bytes(T, n_heads, head_dim), and a call that needs
+ * more than the array returns EAGLE3_ECAPACITY and launches nothing.  Nothing
+ * must start at zero: every call writes all the scratch it reads.  Every call
+ * on one GPU shares that GPU's array, so calls that overlap on one GPU (other
+ * streams or threads) race; calls on one stream are ordered.  No device
+ * memory is allocated or freed. */
+#define EAGLE3_TTT_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+eagle3_status eagle3_ttt_attention_static(int32_t dtype, int32_t T, int32_t S, int32_t n_heads, int32_t n_kv_heads,
+                                          int32_t head_dim, const void *q, const void *k0, const void *v0,
+                                          const void *ks, const void *vs, void *out, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *eagle3_status_string(eagle3_status s);
 

@@ -25,7 +25,7 @@ EXPORTS = [
     "eagle3_sample", "eagle3_set_stream", "eagle3_status_string", "eagle3_device_status", "eagle3_profile", "eagle3_profile_read",
     "eagle3_pack_linear", "eagle3_ttt_workspace_bytes", "eagle3_ttt_attention", "eagle3_paged_kv_bytes",
     "eagle3_create_paged", "eagle3_set_draft_lengths", "eagle3_spec_decode_metadata", "eagle3_set_draft_logits_out",
-    "eagle3_set_hidden_out",
+    "eagle3_set_hidden_out", "eagle3_ttt_attention_static",
 ]
 
 
@@ -99,6 +99,7 @@ def lib():
             "eagle3_compact_kv": [P, I32, P, I32, P, P, P, P, P, P, P, P, P],
             "eagle3_set_draft_logits_out": [P, P],
             "eagle3_set_hidden_out": [P, P],
+            "eagle3_ttt_attention_static": [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P],
             "eagle3_sample": [P, I32, P, C.c_float, P, P],
             "eagle3_ttt_workspace_bytes": [I32, I32, I32, C.POINTER(C.c_size_t)],
             "eagle3_ttt_attention": [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, C.c_size_t, P],
@@ -243,6 +244,11 @@ def eagle3_ttt_workspace_bytes(T, n_heads, head_dim) -> int:
 def eagle3_ttt_attention(dtype, T, S, n_heads, n_kv_heads, head_dim, q, k0, v0, ks, vs, out, ws, ws_bytes, stream):
     _check(lib().eagle3_ttt_attention(dtype, T, S, n_heads, n_kv_heads, head_dim, q, k0, v0, ks, vs, out, ws,
                                       ws_bytes, stream), "eagle3_ttt_attention")
+
+
+def eagle3_ttt_attention_static(dtype, T, S, n_heads, n_kv_heads, head_dim, q, k0, v0, ks, vs, out, stream):
+    _check(lib().eagle3_ttt_attention_static(dtype, T, S, n_heads, n_kv_heads, head_dim, q, k0, v0, ks, vs, out,
+                                             stream), "eagle3_ttt_attention_static")
 
 
 def eagle3_set_stream(ctx, stream):

@@ -1020,6 +1020,23 @@ eagle3_status eagle3_ttt_attention(int32_t dtype, int32_t T, int32_t S, int32_t 
   return last_error();
 }
 
+eagle3_status eagle3_ttt_attention_static(int32_t dtype, int32_t T, int32_t S, int32_t n_heads, int32_t n_kv_heads,
+                                          int32_t head_dim, const void* q, const void* k0, const void* v0,
+                                          const void* ks, const void* vs, void* out, void* stream) {
+  static_assert(EAGLE3_TTT_STATIC_SCRATCH_BYTES == TTT_STATIC_SCRATCH, "header and library agree on the limit");
+  if (dtype != EAGLE3_F32 && dtype != EAGLE3_BF16) return EAGLE3_EINVAL;
+  if (T < 1 || S < 0 || n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || head_dim < 4 || head_dim > 256 ||
+      head_dim % 4)
+    return EAGLE3_EINVAL;
+  if (!q || !k0 || !v0 || !out || (S > 0 && (!ks || !vs))) return EAGLE3_EINVAL;
+  const bool bf = dtype == EAGLE3_BF16;
+  if (ttt_scratch_bytes(bf, T, n_heads, head_dim) > TTT_STATIC_SCRATCH) return EAGLE3_ECAPACITY;
+  void* ws = nullptr;
+  if (ttt_static_scratch(&ws) != hipSuccess) return EAGLE3_EHIP;
+  ttt_attention(bf, T, S, n_heads, n_kv_heads, head_dim, q, k0, v0, ks, vs, out, ws, (hipStream_t)stream);
+  return last_error();
+}
+
 eagle3_status eagle3_set_stream(eagle3_ctx* c, void* stream) {
   if (!c) return EAGLE3_EINVAL;
   c->st = (hipStream_t)stream;

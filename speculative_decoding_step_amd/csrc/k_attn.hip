@@ -10,6 +10,7 @@
 // -inf.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -728,6 +729,12 @@ __global__ __launch_bounds__(64) void k_ttt_diag(int Tn, int S, int Hq, int Hkv,
   }
 }
 
+// Workspace the call really touches: none on the fused path (bf16 at head size 64 or 128, where the attention
+// kernel derives the rows' metadata itself and writes the output without partials), else the general path's.
+size_t ttt_scratch_bytes(bool bf16, int T, int Hq, int hd) {
+  return bf16 && (hd == 64 || hd == 128) ? 0 : ttt_workspace_bytes(T, Hq, hd);
+}
+
 size_t ttt_workspace_bytes(int T, int Hq, int hd) {
   const size_t splits = (size_t)(T + ATT_CHUNK - 1) / ATT_CHUNK + 1;  // the key chunks + the diagonal partial
   size_t b = 0;
@@ -778,6 +785,38 @@ void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void*
                                                   (const float*)vs, extra, o_part, ml_part);
     combine<float>(o_part, ml_part, sp.ns, T, Hq, hd, rm, T, sp.chunk, extra, (float*)out, st);
   }
+}
+
+// ---------------------------------------------- allocation-free entry point
+// The training-time-test call for callers that cannot allocate: its scratch is
+// this fixed per-device array (every GPU the library runs on holds its own
+// copy until the process ends).  Host code never uses the array's name as an
+// address: on the first call on a device its device address is looked up once
+// (with that device current) and kept per device.
+}  // namespace e3
+
+static __device__ __align__(256) unsigned char scratch[e3::TTT_STATIC_SCRATCH];
+
+namespace e3 {
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};  // per device ordinal: the array's device address
+}  // namespace
+
+hipError_t ttt_static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace e3

@@ -141,6 +141,12 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
 // Training-time-test attention: q, out [T, Hq, hd]; k0, v0 [Hkv, T, hd]; ks, vs [S, Hkv, T, hd]; ws of
 // ttt_workspace_bytes(T, Hq, hd) bytes.
 size_t ttt_workspace_bytes(int T, int Hq, int hd);
+// Bytes of that workspace a call with these sizes actually uses (0 on the fused bf16 path).
+size_t ttt_scratch_bytes(bool bf16, int T, int Hq, int hd);
+// The allocation-free call's scratch: a fixed per-device array of TTT_STATIC_SCRATCH bytes; *out receives its
+// device address on the current device (looked up once per device).
+constexpr size_t TTT_STATIC_SCRATCH = (size_t)32 << 20;
+hipError_t ttt_static_scratch(void** out);
 void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void* q, const void* k0, const void* v0,
                    const void* ks, const void* vs, void* out, void* ws, hipStream_t st);
 void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride,
