@@ -98,45 +98,42 @@ __global__ __launch_bounds__(64) void k_attn_partial(const T* __restrict__ q, co
 }
 
 // Merge the chunk partials of each (row, head): out = sum_s e_s o_s / sum_s e_s l_s
-// with e_s = exp(m_s - M), M = max_s m_s, summed in chunk order.  Only the
-// chunks that can hold a key the row sees are read (the row's key end comes
-// from its metadata).  A workgroup covers 256 / (hd / 4) heads of one row and
-// a thread one 4-dim slice of one head; the (m, l) pairs and output slices of
-// up to CMB_BATCH chunks are loaded together, so a row costs two dependent
-// memory round trips (metadata, then partials).  Past CMB_BATCH chunks the
-// running sums are rescaled when a later batch raises the maximum.
+// with e_s = exp(m_s - M), M = max_s m_s, summed in chunk order.  Every chunk
+// has an entry for every (row, head): a chunk without keys for the row holds
+// m = -inf (written by the attention kernel, also for workgroups that had no
+// key at all), and its output slice is then not used.  A workgroup covers
+// 256 / (hd / 4) heads of one row and a thread one 4-dim slice of one head;
+// the (m, l) pairs and output slices of up to CMB_BATCH chunks are loaded
+// together.  EAGER: the output slices are loaded with the (m, l) pairs, empty
+// chunks included (one memory round trip per row: launches of few rows, where
+// latency decides); otherwise only the non-empty chunks' slices, after the
+// pairs (two round trips, no bytes spent on empty chunks: many rows of ragged
+// lengths).  Past CMB_BATCH chunks the running sums are rescaled when a later
+// batch raises the maximum.
 constexpr int CMB_BATCH = 16;
-template <typename T>
+template <typename T, bool EAGER>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ o_part,
                                                       const float* __restrict__ ml_part, int ns, int R, int Hq,
-                                                      int hd, const int* __restrict__ rseq,
-                                                      const int* __restrict__ rlim, const int* __restrict__ rt0,
-                                                      const uint64_t* __restrict__ rmask, int S_cap, int chunk,
-                                                      int extra, T* __restrict__ out) {
+                                                      int hd, int extra, T* __restrict__ out) {
   const int r = blockIdx.x;
   const int tph = hd >> 2;  // threads per head
   const int h = blockIdx.y * (blockDim.x / tph) + threadIdx.x / tph, d4 = threadIdx.x % tph;
   if (h >= Hq) return;  // no barrier below
   const size_t sstride = (size_t)R * Hq;  // (row, head) entries per chunk
   const size_t oi0 = (size_t)r * Hq + h;
-  int nsr = 0;
-  if (rseq[r] >= 0) {
-    const int kend = min(key_end(rlim[r], rt0[r], rmask[r]), S_cap);
-    nsr = min(ns, (kend + chunk - 1) / chunk);
-  }
   const float2* ml = (const float2*)ml_part;
   const float4* o4 = (const float4*)o_part;
   float M = -INFINITY, den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < nsr; s0 += CMB_BATCH) {
+  for (int s0 = 0; s0 < ns; s0 += CMB_BATCH) {
     float2 v[CMB_BATCH];
     float4 o[CMB_BATCH];
 #pragma unroll
-    for (int j = 0; j < CMB_BATCH; ++j) {
-      const bool in = s0 + j < nsr;
-      v[j] = in ? ml[(s0 + j) * sstride + oi0] : make_float2(-INFINITY, 0.f);
-      o[j] = in ? o4[((s0 + j) * sstride + oi0) * tph + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int j = 0; j < CMB_BATCH; ++j) v[j] = s0 + j < ns ? ml[(s0 + j) * sstride + oi0] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int j = 0; j < CMB_BATCH; ++j)
+      o[j] = s0 + j < ns && (EAGER || v[j].x != -INFINITY) ? o4[((s0 + j) * sstride + oi0) * tph + d4]
+                                                             : make_float4(0.f, 0.f, 0.f, 0.f);
     float Mb = M;
 #pragma unroll
     for (int j = 0; j < CMB_BATCH; ++j) Mb = fmaxf(Mb, v[j].x);
@@ -150,7 +147,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     }
 #pragma unroll
     for (int j = 0; j < CMB_BATCH; ++j)
-      if (v[j].x != -INFINITY) {
+      if (v[j].x != -INFINITY) {  // an empty chunk's output slice is never used (it may hold older data)
         const float e = expf(v[j].x - M);
         den += v[j].y * e;
         acc.x += o[j].x * e, acc.y += o[j].y * e, acc.z += o[j].z * e, acc.w += o[j].w * e;
@@ -181,11 +178,14 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 }
 
 template <typename T>
-void combine(const float* o_part, const float* ml_part, int ns, int R, int Hq, int hd, const RowMeta& rm,
-             int key_bound, int chunk, int extra, T* out, hipStream_t st) {
+void combine(const float* o_part, const float* ml_part, int ns, int R, int Hq, int hd, int extra, T* out,
+             hipStream_t st) {
   const int hpb = 256 / (hd / 4);
-  k_attn_combine<T><<<dim3(R, (Hq + hpb - 1) / hpb), 256, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, rm.seq, rm.lim,
-                                                                   rm.tail0, rm.mask, key_bound, chunk, extra, out);
+  const dim3 grid(R, (Hq + hpb - 1) / hpb);
+  if (R <= 256)
+    k_attn_combine<T, true><<<grid, 256, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, extra, out);
+  else
+    k_attn_combine<T, false><<<grid, 256, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, extra, out);
 }
 
 // ---------------------------------------------------------------- MFMA path
@@ -331,7 +331,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   kend = __builtin_amdgcn_readfirstlane(kend);
   cs = __builtin_amdgcn_readfirstlane(cs);
   const int c0 = sp * chunk, c1 = min(c0 + chunk, kend);
-  if (cs < 0 || c0 >= c1) return;  // no row of the block sees a key of this chunk
+  if (cs < 0 || c0 >= c1) {  // no row of the block sees a key of this chunk: an empty partial for each row
+    if (!TTT && v < nq && lg == 0) {
+      const size_t oi = ((size_t)sp * R + row) * Hq + h;
+      ml_part[2 * oi] = -INFINITY;
+      ml_part[2 * oi + 1] = 0.f;
+    }
+    return;
+  }
   // Keys below vis_min are visible to every query of the wave, so tiles below it need no mask (a wave-uniform
   // test).  Lanes without a query vector never force masking (their results are not stored); rows without a
   // sequence see no key.
@@ -394,6 +401,11 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
     }
   };
 
+  // The first NST - 1 tiles' copies go out before the query loads, so their latencies overlap (the query
+  // must be complete before the first tile, which waits for everything issued so far anyway).
+  const int ntl = (c1 - c0 + AKT - 1) / AKT;
+  for (int t = 0; t < NST - 1 && t < ntl; ++t) issue(stg[t], c0 + t * AKT);
+
   float m = M_EMPTY, lsum = 0.f;  // running maximum (log2 units) and the lane's share of the sum
   f32x4 O[HD / 16];               // O^T: dims 16b + 4lg + r of the lane's query
 #pragma unroll
@@ -406,8 +418,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
 #pragma unroll
     for (int kk = 0; kk < HD / 32; ++kk) qf[kk] = ok ? *(const u32x4*)(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
   }
-  // Complete the query loads here, visibly to the compiler: its own wait for them would otherwise land inside
-  // the tile loop, where (not seeing the asm copies) it would drain every tile in flight.
+  // Complete the query loads (and the first tiles' copies issued above) here, visibly to the compiler: its own
+  // wait for them would otherwise land inside the tile loop, where (not seeing the asm copies) it would drain
+  // every tile in flight.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   auto tile = [&](const bf16_t* stgp, int kt) {
@@ -498,8 +511,6 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   // whose stage the copies of tile t + NST - 1 refill.
   static_assert(NST >= 2 && NST <= 4, "the wait below covers at most two tiles in flight after the current one");
   static_assert(PW * (NST - 2) <= 63, "copies in flight exceed the vmcnt range");
-  const int ntl = (c1 - c0 + AKT - 1) / AKT;
-  for (int t = 0; t < NST - 1 && t < ntl; ++t) issue(stg[t], c0 + t * AKT);
   for (int t = 0; t < ntl; ++t) {
     const int after = min(NST - 2, ntl - 1 - t);
     if (after >= 2)
@@ -663,9 +674,9 @@ void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t 
   const AttnSplits sp = attention_partials(bf16, q, kc, vc, unit_stride, head_stride, pg, rm, R, rps, Hq, Hkv, hd,
                                            key_bound, o_part, ml_part, max_splits, st, 0);
   if (bf16)
-    combine<bf16_t>(o_part, ml_part, sp.ns, R, Hq, hd, rm, key_bound, sp.chunk, -1, (bf16_t*)out, st);
+    combine<bf16_t>(o_part, ml_part, sp.ns, R, Hq, hd, -1, (bf16_t*)out, st);
   else
-    combine<float>(o_part, ml_part, sp.ns, R, Hq, hd, rm, key_bound, sp.chunk, -1, (float*)out, st);
+    combine<float>(o_part, ml_part, sp.ns, R, Hq, hd, -1, (float*)out, st);
 }
 
 // ------------------------------------------------------ training-time test
@@ -779,11 +790,11 @@ void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void*
   if (bf16) {
     k_ttt_diag<bf16_t><<<dim3(T, Hq), 64, 0, st>>>(T, S, Hq, Hkv, hd, scale, (const bf16_t*)q, (const bf16_t*)ks,
                                                    (const bf16_t*)vs, extra, o_part, ml_part);
-    combine<bf16_t>(o_part, ml_part, sp.ns, T, Hq, hd, rm, T, sp.chunk, extra, (bf16_t*)out, st);
+    combine<bf16_t>(o_part, ml_part, sp.ns, T, Hq, hd, extra, (bf16_t*)out, st);
   } else {
     k_ttt_diag<float><<<dim3(T, Hq), 64, 0, st>>>(T, S, Hq, Hkv, hd, scale, (const float*)q, (const float*)ks,
                                                   (const float*)vs, extra, o_part, ml_part);
-    combine<float>(o_part, ml_part, sp.ns, T, Hq, hd, rm, T, sp.chunk, extra, (float*)out, st);
+    combine<float>(o_part, ml_part, sp.ns, T, Hq, hd, extra, (float*)out, st);
   }
 }
 

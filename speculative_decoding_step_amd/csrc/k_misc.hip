@@ -375,18 +375,21 @@ E3_DEV VI wave_best(VI x) {
   return vi_best(h0, h1);
 }
 
-// grid (R, nslices), block 256.  Per slice: the K best (value, index) and the
-// slice's max and sum of exp(z - max) in double, with z = logit / temperature.
-// The slice is held in registers (16 values per thread, loaded at once); each
-// of the K rounds picks the best value not yet taken, a thread marking its
-// winner in a 16-bit mask.
+// grid (R, nslices), block 256.  Per slice: the K best (value, index) and,
+// when LSE, the slice's max and sum of exp(z - max) in double, with z = logit /
+// temperature.  The slice is held in registers (16 values per thread, loaded
+// at once).  Each wave first finds the K best of its own 1024 entries in K
+// rounds with no barrier (a lane marks its winner in a 16-bit mask), then
+// wave 0 merges the four waves' lists (4K <= 64 candidates, one per lane) in
+// K more rounds.  The (value, index) order is total, so the result does not
+// depend on how the entries are split.
 constexpr int TK_PER = TK_SLICE / 256;  // values per thread
 
+template <bool LSE>
 __global__ __launch_bounds__(256) void k_topk_partial(const float* __restrict__ logits, int V, int ld, int K,
                                                       double temp, float* __restrict__ pv, int* __restrict__ pi,
                                                       float* __restrict__ pmax, double* __restrict__ psum) {
-  __shared__ VI wred[2][4];
-  __shared__ VI res[TK_KMAX];
+  __shared__ VI cand[4][TK_KMAX];
   __shared__ double dred[4];
   const int r = blockIdx.x, sl = blockIdx.y, ns = gridDim.y;
   const int v0 = sl * TK_SLICE, n = min(TK_SLICE, V - v0);
@@ -411,36 +414,39 @@ __global__ __launch_bounds__(256) void k_topk_partial(const float* __restrict__ 
     }
     return b;
   };
-  VI best = wave_best(local_best());
-  if (lane == 0) wred[0][w] = best;
-  __syncthreads();
-  const VI top = vi_best(vi_best(wred[0][0], wred[0][1]), vi_best(wred[0][2], wred[0][3]));
-  const double m = (double)top.v / temp;
-  double s = 0.0;
-#pragma unroll
-  for (int j = 0; j < TK_PER; ++j)
-    if (tid + 256 * j < n) s += exp((double)v[j] / temp - m);
-  s = wave_sum_d(s);
-  if (lane == 0) dred[w] = s;
-  const size_t o = (size_t)r * ns + sl;
   for (int k = 0; k < K; ++k) {
     const VI b = wave_best(local_best());
-    if (lane == 0) wred[(k + 1) & 1][w] = b;
-    __syncthreads();  // one barrier per round: the two halves of wred alternate
-    const VI t = vi_best(vi_best(wred[(k + 1) & 1][0], wred[(k + 1) & 1][1]),
-                         vi_best(wred[(k + 1) & 1][2], wred[(k + 1) & 1][3]));
-    if (tid == 0) res[k] = t;  // global stores wait until after the rounds: a barrier would drain them
-    const int li = t.i - v0;
+    if (lane == 0) cand[w][k] = b;
+    const int li = b.i - v0;
     if (li >= 0 && li < n && (li & 255) == tid) taken |= 1u << (li >> 8);
   }
   __syncthreads();
-  if (tid < K) {
-    pv[o * K + tid] = res[tid].v;
-    pi[o * K + tid] = res[tid].i;
+  const size_t o = (size_t)r * ns + sl;
+  if (LSE) {
+    const float top = fmaxf(fmaxf(cand[0][0].v, cand[1][0].v), fmaxf(cand[2][0].v, cand[3][0].v));
+    const double m = (double)top / temp;
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < TK_PER; ++j)
+      if (tid + 256 * j < n) s += exp((double)v[j] / temp - m);
+    s = wave_sum_d(s);
+    if (lane == 0) dred[w] = s;
+    if (tid == 0) pmax[o] = top;
   }
-  if (tid == 0) {
-    pmax[o] = (float)top.v;
-    psum[o] = dred[0] + dred[1] + dred[2] + dred[3];
+  if (w == 0) {
+    VI mine = lane < 4 * K ? cand[lane / K][lane % K] : VI{-INFINITY, 0x7fffffff};
+    for (int k = 0; k < K; ++k) {
+      const VI b = wave_best(mine);
+      if (lane == 0) {
+        pv[o * K + k] = b.v;
+        pi[o * K + k] = b.i;
+      }
+      if (mine.i == b.i && mine.v == b.v) mine = VI{-INFINITY, 0x7fffffff};
+    }
+  }
+  if (LSE) {
+    __syncthreads();
+    if (tid == 0) psum[o] = dred[0] + dred[1] + dred[2] + dred[3];
   }
 }
 
@@ -468,8 +474,8 @@ __global__ __launch_bounds__(64) void k_topk_merge(int ns, int K, double temp, c
     if (c >= nc) taken |= 1u << j;
   }
   // slice maxima and sums: lane s holds slice s (ns <= 64 for V <= 64 * 4096)
-  const float pm = tid < ns ? pmax[(size_t)r * ns + tid] : -INFINITY;
-  const double ps = tid < ns ? psum[(size_t)r * ns + tid] : 0.0;
+  const float pm = pmax && tid < ns ? pmax[(size_t)r * ns + tid] : -INFINITY;
+  const double ps = pmax && tid < ns ? psum[(size_t)r * ns + tid] : 0.0;
   for (int k = 0; k < K; ++k) {
     VI b{-INFINITY, 0x7fffffff};
     int bj = -1;
@@ -486,6 +492,7 @@ __global__ __launch_bounds__(64) void k_topk_merge(int ns, int K, double temp, c
       out_vals[(size_t)r * K + k] = wb.v;
     }
   }
+  if (!pmax) return;  // no log-sum-exp asked for
   const float mx = wave_max(pm);
   const double M = (double)mx / temp;
   const double S = wave_sum_d(tid < ns ? ps * exp((double)pm / temp - M) : 0.0);
@@ -501,8 +508,12 @@ void topk_lse(const float* logits, int R, int V, int ld, int K, float temperatur
   if (R <= 0) return;
   const int ns = topk_slices(V);
   const double t = (double)temperature;
-  k_topk_partial<<<dim3(R, ns), 256, 0, st>>>(logits, V, ld, K, t, pv, pi, pmax, psum);
-  k_topk_merge<<<R, 64, 0, st>>>(ns, K, t, pv, pi, pmax, psum, out_ids, out_vals, lse32, lse64);
+  const bool lse = lse32 || lse64;  // the argmax / top-2 of a verify needs no log-sum-exp
+  if (lse)
+    k_topk_partial<true><<<dim3(R, ns), 256, 0, st>>>(logits, V, ld, K, t, pv, pi, pmax, psum);
+  else
+    k_topk_partial<false><<<dim3(R, ns), 256, 0, st>>>(logits, V, ld, K, t, pv, pi, pmax, psum);
+  k_topk_merge<<<R, 64, 0, st>>>(ns, K, t, pv, pi, lse ? pmax : nullptr, psum, out_ids, out_vals, lse32, lse64);
 }
 
 // -------------------------------------------------------------- row gather
