@@ -107,10 +107,12 @@ size_t carve(eagle3_ctx* c, char* base) {
   const size_t prow = std::max(R, 512);
   c->part_elems = prow * nmax;
   c->part = cv.take<float>(c->part_elems);
-  c->hbuf = cv.take<char>((size_t)R * 2 * d * es);
-  c->abuf = cv.take<char>((size_t)R * std::max(qdim, s.ffn) * es);
+  // GEMM inputs (hbuf, abuf, gbuf) take the packed slab layout in passes of more than 64 rows: rows padded to 16
+  const size_t R16 = (size_t)(R + 15) / 16 * 16;
+  c->hbuf = cv.take<char>(R16 * 2 * d * es);
+  c->abuf = cv.take<char>(R16 * std::max(qdim, s.ffn) * es);
   c->qbuf = cv.take<char>((size_t)R * qdim * es);
-  c->gbuf = cv.take<char>((size_t)R * d * es);
+  c->gbuf = cv.take<char>(R16 * d * es);
   c->att_splits = std::max(1, (c->S_cap + ATT_CHUNK - 1) / ATT_CHUNK);
   c->o_part = cv.take<float>((size_t)c->att_splits * R * qdim);
   c->ml_part = cv.take<float>((size_t)c->att_splits * R * s.n_heads * 2);
@@ -356,8 +358,14 @@ int plan_splits(eagle3_ctx* c, int M, int N, int K, int m_tile) {
   return gemm_splits(true, K, S, m_tile);
 }
 
-// X [M, K] of T times the stacked weights; returns the number of splits in c->part.
-int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, float* out_direct = nullptr) {
+// Whether a pass of M rows keeps its bf16 GEMM inputs (the norm outputs, the draft input, the attention output,
+// SiLU(g)*u) in the packed slab layout: the large-M GEMM reads them as contiguous fragments.
+inline bool packed_inputs(const eagle3_ctx* c, int M) { return c->bf16 && M > 64; }
+
+// X [M, K] of T times the stacked weights; returns the number of splits in c->part.  X is in the packed slab
+// layout when packed_inputs(M), except for a row-major input (x_rowmajor: the fusion FC's tap rows).
+int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, float* out_direct = nullptr,
+             bool x_rowmajor = false) {
   const int N = gemm_ntot(sg);
   const int m_tile = M <= 16 ? 16 : (M <= 64 ? 64 : 128);
   const int S = out_direct ? 1 : plan_splits(c, M, N, K, m_tile);
@@ -367,7 +375,7 @@ int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, flo
   // the bf16 kernels record the pair at their own start and end
   prof_begin(c, kid, bytes, 2.0 * M * N * K, &rec, !c->bf16);
   const int used = gemm(c->bf16, X, M, K, sg, out_direct ? out_direct : c->part, (size_t)M * N, S, m_tile, c->st,
-                        c->bf16 ? rec.a : nullptr, c->bf16 ? rec.b : nullptr);
+                        c->bf16 ? rec.a : nullptr, c->bf16 ? rec.b : nullptr, packed_inputs(c, M) && !x_rowmajor);
   prof_end(c, &rec, !c->bf16);
   return used;
 }
@@ -397,7 +405,8 @@ void run_attention(eagle3_ctx* c, const void* kc, const void* vc, const RowMeta&
   const eagle3_shape& s = c->sh;
   ProfRec rec{};
   prof_begin(c, EAGLE3_PROF_ATTN, 0.0, 0.0, &rec);
-  attention(c->bf16, c->qbuf, kc, vc, c->kv_us, c->kv_hs, c->pg, rm, R, rps, s.n_heads, s.n_kv_heads, s.head_dim, c->S_cap, c->o_part, c->ml_part, c->att_splits, c->abuf, c->st);
+  attention(c->bf16, c->qbuf, kc, vc, c->kv_us, c->kv_hs, c->pg, rm, R, rps, s.n_heads, s.n_kv_heads, s.head_dim,
+            c->S_cap, c->o_part, c->ml_part, c->att_splits, c->abuf, c->st, packed_inputs(c, R));
   prof_end(c, &rec);
 }
 
@@ -413,6 +422,7 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
   const eagle3_shape& s = c->sh;
   const int d = s.d_model, qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
   const bool bf = c->bf16;
+  const bool pk = packed_inputs(c, R);
   hipStream_t st = c->st;
   auto record = [&](int l) {  // parity output: the residual entering layer l (l = n_layers: leaving the last)
     if (!c->hid_out) return;
@@ -432,7 +442,8 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
     for (int t = 0; t < 3; ++t)
       if (aux && s.taps[t] == l && first < 0) first = t;
     void* tap = first < 0 ? nullptr : (char*)aux + (size_t)first * d * c->esz;
-    add_rmsnorm(bf, c->xres, S ? c->part : nullptr, S, (size_t)R * d, d, w, out, d, R, d, s.rms_eps, tap, 3 * d, st);
+    add_rmsnorm(bf, c->xres, S ? c->part : nullptr, S, (size_t)R * d, d, w, out, d, R, d, s.rms_eps, tap, 3 * d, st,
+                pk);
     for (int t = first + 1; first >= 0 && t < 3; ++t)
       if (s.taps[t] == l) {
         if (bf)
@@ -453,14 +464,15 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
             c->kv_us, c->kv_hs, c->pg, s.n_heads, s.n_kv_heads, s.head_dim, c->status, st);
     run_attention(c, kc, vc, c->rm, R, rps);
     S = run_gemm(c, c->abuf, R, qdim, make_segs(L.wo, d));
-    add_rmsnorm(bf, c->xres, c->part, S, (size_t)R * d, d, L.ffn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
+    add_rmsnorm(bf, c->xres, c->part, S, (size_t)R * d, d, L.ffn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st,
+                pk);
     run_gateup(c, c->hbuf, R, d, L.w_gate, L.w_up, s.ffn);
     S = run_gemm(c, c->abuf, R, s.ffn, make_segs(L.w_down, d));
     if (l + 1 < s.n_layers) {
       enter(l + 1, S, c->layers[l + 1].attn_norm, c->hbuf);
     } else if (lm == EAGLE3_LM_ALL) {
       add_rmsnorm(bf, c->xres, c->part, S, (size_t)R * d, d, c->tw.final_norm, c->gbuf, d, R, d, s.rms_eps, nullptr,
-                  0, st);
+                  0, st, pk);
       final_normed = true;
     } else {
       resid_add(c->xres, c->part, S, (size_t)R * d, R, d, d, st);
@@ -475,7 +487,7 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
     fin = c->dx;
     n = nlast;
   }
-  if (!final_normed) rmsnorm(bf, fin, c->tw.final_norm, c->gbuf, d, n, d, s.rms_eps, nullptr, 0, st);
+  if (!final_normed) rmsnorm(bf, fin, c->tw.final_norm, c->gbuf, d, n, d, s.rms_eps, nullptr, 0, st, packed_inputs(c, n));
   float* lg = logits ? logits : c->logits;
   run_gemm(c, c->gbuf, n, d, make_segs(c->tw.lm_head, s.vocab), lg);
   if (argmax || margin) {
@@ -495,8 +507,9 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
   const int d = s.d_model, qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
   const bool bf = c->bf16;
   hipStream_t st = c->st;
+  const bool pk = packed_inputs(c, R);
   draft_input(bf, c->tw.embed, tok, x, fc_splits ? c->part : nullptr, fc_splits, (size_t)R * d, H.input_norm,
-              H.hidden_norm, c->hbuf, R, d, s.vocab, s.rms_eps, c->status, st);
+              H.hidden_norm, c->hbuf, R, d, s.vocab, s.rms_eps, c->status, st, pk);
   const GemmSegs qkv = make_segs(H.wq, qdim, H.wk, kvdim, H.wv, kvdim);
   int S = run_gemm(c, c->hbuf, R, 2 * d, qkv);
   char* kc = kv_layer(c, c->kv_d, 0, 0);
@@ -505,7 +518,7 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
           c->kv_us, c->kv_hs, c->pg, s.n_heads, s.n_kv_heads, s.head_dim, c->status, st);
   run_attention(c, kc, vc, rm, R, rps);
   S = run_gemm(c, c->abuf, R, qdim, make_segs(H.wo, d));
-  add_rmsnorm(bf, x, c->part, S, (size_t)R * d, d, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st);
+  add_rmsnorm(bf, x, c->part, S, (size_t)R * d, d, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st, pk);
   run_gateup(c, c->hbuf, R, d, H.w_gate, H.w_up, s.ffn);
   S = run_gemm(c, c->abuf, R, s.ffn, make_segs(H.w_down, d));
   resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
@@ -516,7 +529,8 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
 // are also copied to table rows row0 .. row0 + per - 1.
 void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, int per, int row0) {
   const eagle3_shape& s = c->sh;
-  rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st);
+  rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st,
+          packed_inputs(c, n));
   run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->dhead, c->Vd), c->logits);
   if (c->dl_out && n > 0)
     k_copy_logit_rows<<<dim3(nb(c->Vd, 1024), n), 256, 0, c->st>>>(c->logits, per, c->Vd, c->dl_out,
@@ -891,7 +905,7 @@ eagle3_status eagle3_draft_prefill(eagle3_ctx* c, int32_t seq_begin, int32_t bat
   const int R = batch * n_rows, d = c->sh.d_model;
   k_prefill_meta<<<nb(R, 128), 128, 0, c->st>>>(batch, seq_begin, n_rows, start, next_tok, c->S_cap, c->rm, c->rtok,
                                                  c->status);
-  const int S = run_gemm(c, aux, R, 3 * d, make_segs(c->hw.fc, d));
+  const int S = run_gemm(c, aux, R, 3 * d, make_segs(c->hw.fc, d), nullptr, true);
   draft_layer(c, R, n_rows, c->rtok, c->dx, c->rm, S);
   return last_error();
 }
@@ -911,7 +925,7 @@ eagle3_status eagle3_draft_tree(eagle3_ctx* c, int32_t batch, const int32_t* seq
   hipStream_t st = c->st;
   k_catchup_meta<<<nb(Rc, 128), 128, 0, st>>>(batch, W, seq_lens, new_len, next_tok, c->S_cap, c->rm, c->rtok,
                                                c->gidx, c->roots, c->status);
-  const int S = run_gemm(c, aux_new, Rc, 3 * d, make_segs(c->hw.fc, d));
+  const int S = run_gemm(c, aux_new, Rc, 3 * d, make_segs(c->hw.fc, d), nullptr, true);
   draft_layer(c, Rc, W, c->rtok, c->dx, c->rm, S);
   gather_rows_f32(c->a_last, c->dx, c->gidx, batch, d, st);
   draft_lm(c, batch, c->a_last, chain ? 1 : c->cfg.topk, chain ? c->cfg.temperature : 1.f, 1, 0);

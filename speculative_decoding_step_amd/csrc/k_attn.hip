@@ -114,7 +114,7 @@ constexpr int CMB_BATCH = 16;
 template <typename T, bool EAGER>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ o_part,
                                                       const float* __restrict__ ml_part, int ns, int R, int Hq,
-                                                      int hd, int extra, T* __restrict__ out) {
+                                                      int hd, int extra, T* __restrict__ out, bool packed) {
   const int r = blockIdx.x;
   const int tph = hd >> 2;  // threads per head
   const int h = blockIdx.y * (blockDim.x / tph) + threadIdx.x / tph, d4 = threadIdx.x % tph;
@@ -170,7 +170,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
       acc.x += oe.x * e, acc.y += oe.y * e, acc.z += oe.z * e, acc.w += oe.w * e;
     }
   }
-  const size_t ob = oi0 * hd + 4 * d4;
+  // row r, columns h hd + 4 d4 .. + 3 of the [R, Hq hd] output: row-major, or the packed slab layout of a
+  // large-M GEMM input (the 4 columns stay inside one 8-column group)
+  const size_t ob = packed ? pack_index(r, h * hd + 4 * d4, R, Hq * hd) : oi0 * hd + 4 * d4;
   st<T>(out, ob, den > 0.f ? acc.x / den : 0.f);
   st<T>(out, ob + 1, den > 0.f ? acc.y / den : 0.f);
   st<T>(out, ob + 2, den > 0.f ? acc.z / den : 0.f);
@@ -179,13 +181,13 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 
 template <typename T>
 void combine(const float* o_part, const float* ml_part, int ns, int R, int Hq, int hd, int extra, T* out,
-             hipStream_t st) {
+             hipStream_t st, bool packed = false) {
   const int hpb = 256 / (hd / 4);
   const dim3 grid(R, (Hq + hpb - 1) / hpb);
   if (R <= 256)
-    k_attn_combine<T, true><<<grid, 256, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, extra, out);
+    k_attn_combine<T, true><<<grid, 256, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, extra, out, packed);
   else
-    k_attn_combine<T, false><<<grid, 256, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, extra, out);
+    k_attn_combine<T, false><<<grid, 256, 0, st>>>(o_part, ml_part, ns, R, Hq, hd, extra, out, packed);
 }
 
 // ---------------------------------------------------------------- MFMA path
@@ -669,14 +671,14 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
 
 void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride, size_t head_stride,
                const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
-               float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st) {
+               float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st, bool packed) {
   if (R <= 0) return;
   const AttnSplits sp = attention_partials(bf16, q, kc, vc, unit_stride, head_stride, pg, rm, R, rps, Hq, Hkv, hd,
                                            key_bound, o_part, ml_part, max_splits, st, 0);
   if (bf16)
-    combine<bf16_t>(o_part, ml_part, sp.ns, R, Hq, hd, -1, (bf16_t*)out, st);
+    combine<bf16_t>(o_part, ml_part, sp.ns, R, Hq, hd, -1, (bf16_t*)out, st, packed);
   else
-    combine<float>(o_part, ml_part, sp.ns, R, Hq, hd, -1, (float*)out, st);
+    combine<float>(o_part, ml_part, sp.ns, R, Hq, hd, -1, (float*)out, st, packed);
 }
 
 // ------------------------------------------------------ training-time test

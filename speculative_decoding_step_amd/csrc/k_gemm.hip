@@ -340,9 +340,9 @@ int gemm_rows_per_tile(bool bf16, int m_tile) {
 
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out, size_t split_stride,
          int splits, int m_tile, hipStream_t st, hipEvent_t ev_start,
-         hipEvent_t ev_stop) {
+         hipEvent_t ev_stop, bool a_packed) {
   if (bf16 && m_tile > 64)
-    return gemm_big(X, M, K, segs, out, split_stride, splits, st, ev_start, ev_stop);
+    return gemm_big(X, M, K, segs, out, split_stride, splits, st, ev_start, ev_stop, a_packed);
   const int ldo = gemm_ntot(segs);
   // 64-row tiles on matrices of at most 8192 rows: four-wave workgroups of 64 weight rows with half the K
   // splits (the same number of workgroups, each streaming twice the K; half the partials to read back)

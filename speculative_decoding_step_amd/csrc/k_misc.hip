@@ -61,7 +61,7 @@ template <typename T, int NV>
 __global__ __launch_bounds__(1024) void k_add_rmsnorm(float* __restrict__ x, const float* __restrict__ part, int S,
                                                       size_t sstride, int ldp, const T* __restrict__ w,
                                                       T* __restrict__ out, int out_ld, int d, float eps,
-                                                      T* __restrict__ tap, int tap_ld) {
+                                                      T* __restrict__ tap, int tap_ld, bool packed) {
   __shared__ float red[16];
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, d4 = d >> 2;
   float4* xr = (float4*)(x + (size_t)r * d);
@@ -90,8 +90,8 @@ __global__ __launch_bounds__(1024) void k_add_rmsnorm(float* __restrict__ x, con
   for (int i = 0; i < NV; ++i) {
     const int c = tid + nt * i;
     if (c < d4) {
-      const int e = 4 * c;
-      T* op = out + (size_t)r * out_ld + e;
+      const int e = 4 * c;  // the 4 columns stay inside one 8-column group of the packed layout
+      T* op = out + (packed ? pack_index(r, e, gridDim.x, d) : (size_t)r * out_ld + e);
       st<T>(op, 0, v[i].x * inv * ld<T>(w, e));
       st<T>(op, 1, v[i].y * inv * ld<T>(w, e + 1));
       st<T>(op, 2, v[i].z * inv * ld<T>(w, e + 2));
@@ -105,7 +105,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_add_rmsnorm_any(float* __restrict__ x, const float* __restrict__ part,
                                                          int S, size_t sstride, int ldp, const T* __restrict__ w,
                                                          T* __restrict__ out, int out_ld, int d, float eps,
-                                                         T* __restrict__ tap, int tap_ld) {
+                                                         T* __restrict__ tap, int tap_ld, bool packed) {
   __shared__ float red[16];
   const int r = blockIdx.x, tid = threadIdx.x;
   float* xr = x + (size_t)r * d;
@@ -121,38 +121,39 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_any(float* __restrict__ x, 
   }
   ss = block_sum(ss, red);
   const float inv = 1.f / sqrtf(ss / (float)d + eps);
-  for (int i = tid; i < d; i += 256) st<T>(out, (size_t)r * out_ld + i, xr[i] * inv * ld<T>(w, i));
+  for (int i = tid; i < d; i += 256)
+    st<T>(out, packed ? pack_index(r, i, gridDim.x, d) : (size_t)r * out_ld + i, xr[i] * inv * ld<T>(w, i));
 }
 
 template <typename T>
 static void launch_add_rmsnorm(float* x, const float* part, int S, size_t sstride, int ldp, const T* w, T* out,
-                               int out_ld, int R, int d, float eps, T* tap, int tap_ld, hipStream_t st) {
+                               int out_ld, int R, int d, float eps, T* tap, int tap_ld, hipStream_t st, bool pk) {
   const int d4 = d / 4;
   if (d % 4 == 0 && d4 <= 2048) {
     const int nt = std::min(1024, (d4 + 63) / 64 * 64);
     if (d4 <= nt)
-      k_add_rmsnorm<T, 1><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld);
+      k_add_rmsnorm<T, 1><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk);
     else
-      k_add_rmsnorm<T, 2><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld);
+      k_add_rmsnorm<T, 2><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk);
   } else {
-    k_add_rmsnorm_any<T><<<R, 256, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld);
+    k_add_rmsnorm_any<T><<<R, 256, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk);
   }
 }
 
 void add_rmsnorm(bool bf16, float* x, const float* part, int S, size_t sstride, int ldp, const void* w, void* out,
-                 int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st) {
+                 int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st, bool packed) {
   if (R <= 0) return;
   if (bf16)
     launch_add_rmsnorm<bf16_t>(x, part, S, sstride, ldp, (const bf16_t*)w, (bf16_t*)out, out_ld, R, d, eps,
-                               (bf16_t*)tap, tap_ld, st);
+                               (bf16_t*)tap, tap_ld, st, packed);
   else
     launch_add_rmsnorm<float>(x, part, S, sstride, ldp, (const float*)w, (float*)out, out_ld, R, d, eps,
-                              (float*)tap, tap_ld, st);
+                              (float*)tap, tap_ld, st, packed);
 }
 
 void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, int R, int d, float eps, void* tap,
-             int tap_ld, hipStream_t st) {
-  add_rmsnorm(bf16, (float*)x, nullptr, 0, 0, 0, w, out, out_ld, R, d, eps, tap, tap_ld, st);
+             int tap_ld, hipStream_t st, bool packed) {
+  add_rmsnorm(bf16, (float*)x, nullptr, 0, 0, 0, w, out, out_ld, R, d, eps, tap, tap_ld, st, packed);
 }
 
 // ---------------------------------------------------------------- draft input
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embe
                                                       float* __restrict__ x, const float* __restrict__ part, int S,
                                                       size_t sstride, const T* __restrict__ w_in,
                                                       const T* __restrict__ w_hid, T* __restrict__ out, int d,
-                                                      int V, float eps, int* status) {
+                                                      int V, float eps, int* status, bool packed) {
   __shared__ float red[16];
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, d4 = d >> 2;
   int t = tokens[r];
@@ -197,14 +198,16 @@ __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embe
   se = block_sum(se, red);
   sx = block_sum(sx, red);
   const float ie = 1.f / sqrtf(se / (float)d + eps), ix = 1.f / sqrtf(sx / (float)d + eps);
-  T* o = out + (size_t)r * 2 * d;
+  // column c of the row: row-major, or the packed slab layout of an [R, 2d] matrix (4-column groups stay whole)
+  auto at = [&](int col) { return packed ? pack_index(r, col, gridDim.x, 2 * d) : (size_t)r * 2 * d + col; };
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = tid + nt * i;
     if (c < d4) {
       const float4 wi = ld4<T>(w_in, 4 * c), wh = ld4<T>(w_hid, 4 * c);
-      st4<T>(o, 4 * c, make_float4(e[i].x * ie * wi.x, e[i].y * ie * wi.y, e[i].z * ie * wi.z, e[i].w * ie * wi.w));
-      st4<T>(o, d + 4 * c,
+      st4<T>(out, at(4 * c),
+             make_float4(e[i].x * ie * wi.x, e[i].y * ie * wi.y, e[i].z * ie * wi.z, e[i].w * ie * wi.w));
+      st4<T>(out, at(d + 4 * c),
              make_float4(h[i].x * ix * wh.x, h[i].y * ix * wh.y, h[i].z * ix * wh.z, h[i].w * ix * wh.w));
     }
   }
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ e
                                                          float* __restrict__ x, const float* __restrict__ part, int S,
                                                          size_t sstride, const T* __restrict__ w_in,
                                                          const T* __restrict__ w_hid, T* __restrict__ out, int d,
-                                                         int V, float eps, int* status) {
+                                                         int V, float eps, int* status, bool packed) {
   __shared__ float red[16];
   const int r = blockIdx.x;
   int t = tokens[r];
@@ -233,40 +236,43 @@ __global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ e
   se = block_sum(se, red);
   sx = block_sum(sx, red);
   const float ie = 1.f / sqrtf(se / (float)d + eps), ix = 1.f / sqrtf(sx / (float)d + eps);
-  T* o = out + (size_t)r * 2 * d;
+  auto at = [&](int col) { return packed ? pack_index(r, col, gridDim.x, 2 * d) : (size_t)r * 2 * d + col; };
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
     const float e = ok ? ld<T>(embed, (size_t)t * d + i) : 0.f;
-    st<T>(o, i, e * ie * ld<T>(w_in, i));
-    st<T>(o, d + i, xr[i] * ix * ld<T>(w_hid, i));
+    st<T>(out, at(i), e * ie * ld<T>(w_in, i));
+    st<T>(out, at(d + i), xr[i] * ix * ld<T>(w_hid, i));
   }
 }
 
 template <typename T>
 static void launch_draft_input(const T* embed, const int* tokens, float* x, const float* part, int S, size_t sstride,
                                const T* w_in, const T* w_hid, T* out, int R, int d, int V, float eps, int* status,
-                               hipStream_t st) {
+                               hipStream_t st, bool pk) {
   const int d4 = d / 4;
   if (d % 4 == 0 && d4 <= 2048) {
     const int nt = std::min(1024, (d4 + 63) / 64 * 64);
     if (d4 <= nt)
-      k_draft_input<T, 1><<<R, nt, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status);
+      k_draft_input<T, 1><<<R, nt, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status,
+                                            pk);
     else
-      k_draft_input<T, 2><<<R, nt, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status);
+      k_draft_input<T, 2><<<R, nt, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status,
+                                            pk);
   } else {
-    k_draft_input_any<T><<<R, 256, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status);
+    k_draft_input_any<T><<<R, 256, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status,
+                                            pk);
   }
 }
 
 void draft_input(bool bf16, const void* embed, const int* tokens, float* x, const float* part, int S,
                  size_t sstride, const void* w_in, const void* w_hid, void* out, int R, int d, int V, float eps,
-                 int* status, hipStream_t st) {
+                 int* status, hipStream_t st, bool packed) {
   if (R <= 0) return;
   if (bf16)
     launch_draft_input<bf16_t>((const bf16_t*)embed, tokens, x, part, S, sstride, (const bf16_t*)w_in,
-                               (const bf16_t*)w_hid, (bf16_t*)out, R, d, V, eps, status, st);
+                               (const bf16_t*)w_hid, (bf16_t*)out, R, d, V, eps, status, st, packed);
   else
     launch_draft_input<float>((const float*)embed, tokens, x, part, S, sstride, (const float*)w_in,
-                              (const float*)w_hid, (float*)out, R, d, V, eps, status, st);
+                              (const float*)w_hid, (float*)out, R, d, V, eps, status, st, packed);
 }
 
 // ----------------------------------------------------------- rope + KV write
