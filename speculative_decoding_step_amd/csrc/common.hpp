@@ -47,19 +47,14 @@ template <> E3_DEV void st4<bf16_t>(bf16_t* p, size_t i, float4 v) {
   *(uint2*)(p + i) = u;
 }
 
-// ------------------------------------------------------- packed slab layout
-// Index of element (row r, column k) of an [R, K] bf16 matrix in the packed
-// slab layout (rows padded to R16 = 16 ceil(R / 16); K % 128 == 0): K is cut
-// into 128-wide slabs stored one after the other, each holding the 16-row
-// blocks in order as four 16 x 32 MFMA fragments of 64 lanes x 8 elements.
-// The weights use it (eagle3_pack_linear), and so do the inputs of the
-// large-M GEMM (more than 64 rows), written this way by their producers.
-E3_DEV size_t pack_index(int r, int k, int R, int K) {
-  (void)K;
-  const size_t nb16 = (size_t)((R + 15) >> 4);
-  return (((size_t)(k >> 7) * nb16 + (r >> 4)) * 4 + ((k & 127) >> 5)) * 512 + ((r & 15) + 16 * ((k & 31) >> 3)) * 8 +
-         (k & 7);
-}
+// ------------------------------------------------ column-slab activations
+// Index of element (row r, column k) of an [R, K] matrix stored as column
+// slabs of 32: slab k / 32 holds every row's 32 columns of it, row after row
+// (64 bytes per row in bf16).  The large-M GEMM reads its activations this
+// way: 16 consecutive rows of one slab, one MFMA operand fragment, are one
+// contiguous KiB; a kernel that produces one row at a time still writes
+// 64-byte pieces.  The inputs of passes of more than 64 rows use it.
+E3_DEV size_t slab32_index(int r, int k, int R) { return ((size_t)(k >> 5) * R + r) * 32 + (k & 31); }
 
 // ---------------------------------------------------------------- reductions
 E3_DEV float wave_sum(float v) {

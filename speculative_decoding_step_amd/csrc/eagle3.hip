@@ -107,7 +107,8 @@ size_t carve(eagle3_ctx* c, char* base) {
   const size_t prow = std::max(R, 512);
   c->part_elems = prow * nmax;
   c->part = cv.take<float>(c->part_elems);
-  // GEMM inputs (hbuf, abuf, gbuf) take the packed slab layout in passes of more than 64 rows: rows padded to 16
+  // GEMM inputs (hbuf, abuf, gbuf) are stored in column slabs of 32 in passes of more than 64 rows (sized for
+  // rows padded to 16)
   const size_t R16 = (size_t)(R + 15) / 16 * 16;
   c->hbuf = cv.take<char>(R16 * 2 * d * es);
   c->abuf = cv.take<char>(R16 * std::max(qdim, s.ffn) * es);
@@ -359,11 +360,11 @@ int plan_splits(eagle3_ctx* c, int M, int N, int K, int m_tile) {
 }
 
 // Whether a pass of M rows keeps its bf16 GEMM inputs (the norm outputs, the draft input, the attention output,
-// SiLU(g)*u) in the packed slab layout: the large-M GEMM reads them as contiguous fragments.
+// SiLU(g)*u) in column slabs of 32 (slab32_index): the large-M GEMM reads them as contiguous fragments.
 inline bool packed_inputs(const eagle3_ctx* c, int M) { return c->bf16 && M > 64; }
 
-// X [M, K] of T times the stacked weights; returns the number of splits in c->part.  X is in the packed slab
-// layout when packed_inputs(M), except for a row-major input (x_rowmajor: the fusion FC's tap rows).
+// X [M, K] of T times the stacked weights; returns the number of splits in c->part.  X is in column slabs of 32
+// when packed_inputs(M), except for a row-major input (x_rowmajor: the fusion FC's tap rows).
 int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, float* out_direct = nullptr,
              bool x_rowmajor = false) {
   const int N = gemm_ntot(sg);

@@ -170,13 +170,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
       acc.x += oe.x * e, acc.y += oe.y * e, acc.z += oe.z * e, acc.w += oe.w * e;
     }
   }
-  // row r, columns h hd + 4 d4 .. + 3 of the [R, Hq hd] output: row-major, or the packed slab layout of a
-  // large-M GEMM input (the 4 columns stay inside one 8-column group)
-  const size_t ob = packed ? pack_index(r, h * hd + 4 * d4, R, Hq * hd) : oi0 * hd + 4 * d4;
-  st<T>(out, ob, den > 0.f ? acc.x / den : 0.f);
-  st<T>(out, ob + 1, den > 0.f ? acc.y / den : 0.f);
-  st<T>(out, ob + 2, den > 0.f ? acc.z / den : 0.f);
-  st<T>(out, ob + 3, den > 0.f ? acc.w / den : 0.f);
+  // row r, columns h hd + 4 d4 .. + 3 of the [R, Hq hd] output: row-major, or column slabs of 32 of a
+  // large-M GEMM input (the 4 columns stay inside one slab)
+  const size_t ob = packed ? slab32_index(r, h * hd + 4 * d4, R) : oi0 * hd + 4 * d4;
+  const float id = den > 0.f ? 1.f / den : 0.f;
+  st4<T>(out, ob, make_float4(acc.x * id, acc.y * id, acc.z * id, acc.w * id));
 }
 
 template <typename T>

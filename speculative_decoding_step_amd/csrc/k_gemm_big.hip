@@ -1,5 +1,5 @@
 // Large-M bf16 GEMM (prefill chunks, batch-64 verify): out = X W^T with
-// X [M, K] row-major and W [N, K] in the packed slab layout, fp32 partials
+// X [M, K] row-major (or in column slabs of 32) and W [N, K] in the packed slab layout, fp32 partials
 // per K split.
 #include <hip/hip_ext.h>
 
@@ -52,13 +52,13 @@ E3_DEV void lds_copy16(const void* g, void* l) {
 // tile covers 128 output columns n0 .. n0 + 127 of both, arranged so that in
 // each wave the 16-column blocks alternate gate, up, gate, up ... over the
 // same columns, and the epilogue writes act[m][n] = bf16(silu(g) * u)
-// directly (no K split), in the packed layout when APACK.
+// directly (no K split), in column slabs of 32 when APACK.
 //
-// APACK: X is in the packed slab layout of the weights (rows padded to a
-// multiple of 16, see pack_index), as the kernels that produce this GEMM's
-// input write it for passes of more than 64 rows: an A fragment (16 rows x 32
-// K) is then one contiguous KiB, like a weight fragment, instead of 16 row
-// pieces of 64 bytes (measured 7-10 % faster on the batch-64 verify shapes).
+// APACK: X is stored in column slabs of 32 (slab32_index), as the kernels
+// that produce this GEMM's input write it for passes of more than 64 rows: an
+// A fragment (16 rows x 32 K) is then one contiguous KiB, like a weight
+// fragment, instead of 16 row pieces of 64 bytes, and a producer writing one
+// row still writes whole 64-byte pieces.
 template <bool FUSE, bool APACK>
 __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
                                                           BigTiles bt, float* __restrict__ out, int ldo,
@@ -84,12 +84,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
   // this wave's copies: A fragments 2 wv, 2 wv + 1 and B fragments 4 wv .. 4 wv + 3 of every stage.
   // Rows past M read row M - 1 and blocks past the segment read block 0; their results are not stored.
   const bf16_t* ap[2];
-  const int mb_last = (M + 15) / 16 - 1;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    ap[i] = APACK ? X + (size_t)min(m0 / 16 + 2 * wv + i, mb_last) * (4 * 512) + 8 * lane
-                  : X + (size_t)min(m0 + 16 * (2 * wv + i) + lr, M - 1) * K + 8 * lg;
-  const size_t aslab = (size_t)(mb_last + 1) * (4 * 512);  // packed X: elements per 128-wide K slab
+    ap[i] = X + (size_t)min(m0 + 16 * (2 * wv + i) + lr, M - 1) * (APACK ? 32 : K) + 8 * lg;
   const bf16_t* bp[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -107,7 +104,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
     bp[i] = Wb + (size_t)(16 * rb < nrows ? rb : 0) * (4 * 512) + 8 * lane;
   }
   auto issue = [&](bf16_t* sa, bf16_t* sb, int k0) {
-    const size_t aoff = APACK ? (size_t)(k0 / PACK_KB) * aslab + ((k0 % PACK_KB) / 32) * 512 : (size_t)k0;
+    const size_t aoff = APACK ? (size_t)(k0 >> 5) * M * 32 : (size_t)k0;  // slab k0 / 32, or column k0
 #pragma unroll
     for (int i = 0; i < 2; ++i) lds_copy16(ap[i] + aoff, sa + (2 * wv + i) * 512);
     const size_t off = (size_t)(k0 / PACK_KB) * slab + ((k0 % PACK_KB) / 32) * 512;
@@ -164,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
         for (int r = 0; r < 4; ++r) {
           const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
           const float g = acc[i][2 * t][r], u = acc[i][2 * t + 1][r];
-          if (m < M) act[APACK ? pack_index(m, n, M, F) : (size_t)m * F + n] = f2bf(g / (1.f + expf(-g)) * u);
+          if (m < M) act[APACK ? slab32_index(m, n, M) : (size_t)m * F + n] = f2bf(g / (1.f + expf(-g)) * u);
         }
     }
     return;
@@ -218,7 +215,7 @@ void gemm_big_silu(const void* X, int M, int K, const void* w_gate, const void* 
   const int mtiles = (M + BM - 1) / BM;
   const int nwork = mtiles * ((F + 127) / 128);
   const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
-  // passes of more than 64 rows read and write the packed layout (the input from the RMSNorm, the output for
+  // passes of more than 64 rows read and write column slabs of 32 (the input from the RMSNorm, the output for
   // the down projection)
   hipExtLaunchKernelGGL((k_gemm_bf16_big<true, true>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                         (const bf16_t*)X, M, K, segs, bt, (float*)nullptr, 0, (size_t)0, K, 1, mtiles, nwork,

@@ -78,10 +78,7 @@ __global__ __launch_bounds__(1024) void k_add_rmsnorm(float* __restrict__ x, con
         xr[c] = v[i];
       }
       ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
-      if (tap) {
-        T* tp = tap + (size_t)r * tap_ld + 4 * c;
-        st<T>(tp, 0, v[i].x); st<T>(tp, 1, v[i].y); st<T>(tp, 2, v[i].z); st<T>(tp, 3, v[i].w);
-      }
+      if (tap) st4<T>(tap, (size_t)r * tap_ld + 4 * c, v[i]);
     }
   }
   ss = block_sum(ss, red);
@@ -90,12 +87,10 @@ __global__ __launch_bounds__(1024) void k_add_rmsnorm(float* __restrict__ x, con
   for (int i = 0; i < NV; ++i) {
     const int c = tid + nt * i;
     if (c < d4) {
-      const int e = 4 * c;  // the 4 columns stay inside one 8-column group of the packed layout
-      T* op = out + (packed ? pack_index(r, e, gridDim.x, d) : (size_t)r * out_ld + e);
-      st<T>(op, 0, v[i].x * inv * ld<T>(w, e));
-      st<T>(op, 1, v[i].y * inv * ld<T>(w, e + 1));
-      st<T>(op, 2, v[i].z * inv * ld<T>(w, e + 2));
-      st<T>(op, 3, v[i].w * inv * ld<T>(w, e + 3));
+      const int e = 4 * c;  // the 4 columns stay inside one 32-column slab
+      const float4 wv = ld4<T>(w, e);
+      st4<T>(out, packed ? slab32_index(r, e, gridDim.x) : (size_t)r * out_ld + e,
+             make_float4(v[i].x * inv * wv.x, v[i].y * inv * wv.y, v[i].z * inv * wv.z, v[i].w * inv * wv.w));
     }
   }
 }
@@ -122,14 +117,18 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_any(float* __restrict__ x, 
   ss = block_sum(ss, red);
   const float inv = 1.f / sqrtf(ss / (float)d + eps);
   for (int i = tid; i < d; i += 256)
-    st<T>(out, packed ? pack_index(r, i, gridDim.x, d) : (size_t)r * out_ld + i, xr[i] * inv * ld<T>(w, i));
+    st<T>(out, packed ? slab32_index(r, i, gridDim.x) : (size_t)r * out_ld + i, xr[i] * inv * ld<T>(w, i));
 }
 
 template <typename T>
 static void launch_add_rmsnorm(float* x, const float* part, int S, size_t sstride, int ldp, const T* w, T* out,
                                int out_ld, int R, int d, float eps, T* tap, int tap_ld, hipStream_t st, bool pk) {
   const int d4 = d / 4;
-  if (d % 4 == 0 && d4 <= 2048) {
+  // the float4 kernel moves 4 elements at a time: every row start must be aligned to 4 of them
+  const size_t al = 4 * sizeof(T);
+  const bool aligned = (size_t)out % al == 0 && (size_t)w % al == 0 && out_ld % 4 == 0 &&
+                       (!tap || ((size_t)tap % al == 0 && tap_ld % 4 == 0));
+  if (d % 4 == 0 && d4 <= 2048 && aligned) {
     const int nt = std::min(1024, (d4 + 63) / 64 * 64);
     if (d4 <= nt)
       k_add_rmsnorm<T, 1><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk);
@@ -198,8 +197,8 @@ __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embe
   se = block_sum(se, red);
   sx = block_sum(sx, red);
   const float ie = 1.f / sqrtf(se / (float)d + eps), ix = 1.f / sqrtf(sx / (float)d + eps);
-  // column c of the row: row-major, or the packed slab layout of an [R, 2d] matrix (4-column groups stay whole)
-  auto at = [&](int col) { return packed ? pack_index(r, col, gridDim.x, 2 * d) : (size_t)r * 2 * d + col; };
+  // column c of the row: row-major, or column slabs of 32 of an [R, 2d] matrix
+  auto at = [&](int col) { return packed ? slab32_index(r, col, gridDim.x) : (size_t)r * 2 * d + col; };
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = tid + nt * i;
@@ -236,7 +235,7 @@ __global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ e
   se = block_sum(se, red);
   sx = block_sum(sx, red);
   const float ie = 1.f / sqrtf(se / (float)d + eps), ix = 1.f / sqrtf(sx / (float)d + eps);
-  auto at = [&](int col) { return packed ? pack_index(r, col, gridDim.x, 2 * d) : (size_t)r * 2 * d + col; };
+  auto at = [&](int col) { return packed ? slab32_index(r, col, gridDim.x) : (size_t)r * 2 * d + col; };
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
     const float e = ok ? ld<T>(embed, (size_t)t * d + i) : 0.f;
     st<T>(out, at(i), e * ie * ld<T>(w_in, i));
@@ -249,7 +248,11 @@ static void launch_draft_input(const T* embed, const int* tokens, float* x, cons
                                const T* w_in, const T* w_hid, T* out, int R, int d, int V, float eps, int* status,
                                hipStream_t st, bool pk) {
   const int d4 = d / 4;
-  if (d % 4 == 0 && d4 <= 2048) {
+  // the float4 kernel moves 4 elements at a time: every row start must be aligned to 4 of them
+  const size_t al = 4 * sizeof(T);
+  const bool aligned = (size_t)out % al == 0 && (size_t)embed % al == 0 && (size_t)w_in % al == 0 &&
+                       (size_t)w_hid % al == 0;
+  if (d % 4 == 0 && d4 <= 2048 && aligned) {
     const int nt = std::min(1024, (d4 + 63) / 64 * 64);
     if (d4 <= nt)
       k_draft_input<T, 1><<<R, nt, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status,

@@ -34,8 +34,8 @@ GemmSegs make_segs(const void* w0, int r0, const void* w1 = nullptr, int r1 = 0,
 // kernel); ignored for float.  When
 // ev_start/ev_stop are given, the bf16 launch records them at the kernel's own
 // start and end (profiling).
-// a_packed: X is in the packed slab layout (pack_index), which the large-M
-// kernel (m_tile 128) reads; the skinny kernels read X row-major.
+// a_packed: X is stored in column slabs of 32 (slab32_index), which the
+// large-M kernel (m_tile 128) reads; the skinny kernels read X row-major.
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out,
          size_t split_stride, int splits, int m_tile, hipStream_t st,
          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr, bool a_packed = false);
@@ -46,7 +46,7 @@ int gemm_big(const void* X, int M, int K, const GemmSegs& segs, float* out, size
              hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop, bool a_packed = false);
 // act[m][n] = bf16(silu(X w_gate^T) * (X w_up^T)) in one GEMM launch, no partials:
 // gemm_silu for bf16 with M <= 64 (skinny kernels, X and act row-major),
-// gemm_big_silu for M > 64 (X and act in the packed slab layout).
+// gemm_big_silu for M > 64 (X and act in column slabs of 32).
 void gemm_silu(const void* X, int M, int K, const void* w_gate, const void* w_up, int F, void* act, hipStream_t st,
                hipEvent_t ev_start, hipEvent_t ev_stop);
 void gemm_big_silu(const void* X, int M, int K, const void* w_gate, const void* w_up, int F, void* act,
@@ -67,7 +67,7 @@ void embed_rows(bool bf16, const void* table, const int* tokens, float* x, int R
                 int* status, hipStream_t st);
 // out[r] = T(x[r] * rsqrt(mean(x^2)+eps) * w); if tap != null also tap[r*tap_ld] = T(x[r]).
 // add_rmsnorm first adds the S split partials part[s][r][0..d) (row stride ldp) into x.
-// packed: out is written in the packed slab layout of an [R, d] matrix (a large-M GEMM input) instead of
+// packed: out is written in column slabs of 32 of an [R, d] matrix (a large-M GEMM input) instead of
 // row-major with stride out_ld; tap is always row-major.
 void add_rmsnorm(bool bf16, float* x, const float* part, int S, size_t sstride, int ldp, const void* w, void* out,
                  int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st, bool packed = false);
@@ -76,7 +76,7 @@ void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, in
 // Draft input: out[r] = [T(rms(embed[tok[r]]) * w_in) ; T(rms(x[r]) * w_hid)], [R, 2d].  With part != null
 // x[r] is first set to the sum of the S split partials part[s][r][0..d) (split stride sstride): the fusion
 // FC's reduction in the same pass.
-// packed: out ([R, 2d]) in the packed slab layout.
+// packed: out ([R, 2d]) in column slabs of 32.
 void draft_input(bool bf16, const void* embed, const int* tokens, float* x, const float* part, int S,
                  size_t sstride, const void* w_in, const void* w_hid, void* out, int R, int d, int V, float eps,
                  int* status, hipStream_t st, bool packed = false);
@@ -155,7 +155,7 @@ constexpr size_t TTT_STATIC_SCRATCH = (size_t)32 << 20;
 hipError_t ttt_static_scratch(void** out);
 void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void* q, const void* k0, const void* v0,
                    const void* ks, const void* vs, void* out, void* ws, hipStream_t st);
-// out [R, Hq * hd] of T, row-major, or in the packed slab layout when packed.
+// out [R, Hq * hd] of T, row-major, or in column slabs of 32 when packed.
 void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride,
                size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
                float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st, bool packed = false);
