@@ -123,6 +123,63 @@ E3_DEV bool better(float va, int ia, float vb, int ib) {
   return (va > vb) | ((va == vb) & ((unsigned)ia < (unsigned)ib));
 }
 
+struct VI {
+  float v;
+  int i;
+};
+
+E3_DEV VI vi_best(VI a, VI b) { return better(a.v, a.i, b.v, b.i) ? a : b; }
+
+// Best (value, index) of a full wave, returned to every lane.  Within each
+// 16-lane row: DPP exchanges with lanes xor 1, xor 2 (quad permutes), then the
+// half-row and row mirrors; across rows: the gfx950 permlane swaps, which
+// hand each lane the value of lane xor 16, then of lane xor 32, in registers
+// (no trip through LDS).  The order is a total order, so the result does not
+// depend on the reduction tree.  Every lane must be active.
+template <int CTRL>
+E3_DEV VI vi_dpp(VI a) {
+  const VI b{__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a.v), CTRL, 0xF, 0xF, false)),
+             __builtin_amdgcn_update_dpp(0, a.i, CTRL, 0xF, 0xF, false)};
+  return vi_best(a, b);
+}
+
+// Best (value, index) of each 16-lane row, returned to every lane of the row.
+E3_DEV VI row16_best(VI x) {
+  x = vi_dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = vi_dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = vi_dpp<0x141>(x);  // row_half_mirror
+  return vi_dpp<0x140>(x);  // row_mirror
+}
+
+// Sum over each 16-lane row (double), returned to every lane of the row.
+template <int CTRL>
+E3_DEV double dpp_d(double a) {
+  const unsigned long long u = __double_as_longlong(a);
+  const unsigned lo = __builtin_amdgcn_update_dpp(0u, (unsigned)u, CTRL, 0xF, 0xF, false);
+  const unsigned hi = __builtin_amdgcn_update_dpp(0u, (unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+E3_DEV double row16_sum_d(double x) {
+  x += dpp_d<0xB1>(x);
+  x += dpp_d<0x4E>(x);
+  x += dpp_d<0x141>(x);
+  return x + dpp_d<0x140>(x);
+}
+
+// The better of the two (value, index) pairs a permlane swap hands a lane: its own and its partner's.
+E3_DEV VI vi_swap16(VI x) {
+  const auto v = __builtin_amdgcn_permlane16_swap(__float_as_uint(x.v), __float_as_uint(x.v), false, false);
+  const auto i = __builtin_amdgcn_permlane16_swap((unsigned)x.i, (unsigned)x.i, false, false);
+  return vi_best(VI{__uint_as_float(v[0]), (int)i[0]}, VI{__uint_as_float(v[1]), (int)i[1]});
+}
+E3_DEV VI vi_swap32(VI x) {
+  const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(x.v), __float_as_uint(x.v), false, false);
+  const auto i = __builtin_amdgcn_permlane32_swap((unsigned)x.i, (unsigned)x.i, false, false);
+  return vi_best(VI{__uint_as_float(v[0]), (int)i[0]}, VI{__uint_as_float(v[1]), (int)i[1]});
+}
+
+E3_DEV VI wave_best(VI x) { return vi_swap32(vi_swap16(row16_best(x))); }
+
 // Status bits (mirrors eagle3.h).
 #define E3_DEV_KV_OVERFLOW 0x1
 #define E3_DEV_BAD_TREE 0x2

@@ -75,6 +75,7 @@ struct eagle3_ctx {
   float *tk_pv, *tk_pmax, *tk_vals, *tk_lse;
   int *tk_pi, *tk_ids;
   double *tk_psum, *tk_lse64;
+  SliceTopk tf;  // candidates of the LM-head GEMMs with the top-k in their epilogue (passes of <= 64 rows)
   unsigned long long* tk_wsum;  // per-row slice sums of integer sampling weights
   int* acc_sel;                 // chain acceptance: drafts accepted per sequence
   RowMeta rm;
@@ -127,6 +128,13 @@ size_t carve(eagle3_ctx* c, char* base) {
   c->tk_vals = cv.take<float>((size_t)R * KMAX);
   c->tk_lse = cv.take<float>(R);
   c->tk_lse64 = cv.take<double>(R);
+  {
+    const size_t rows = (size_t)std::min(R, 64), nsf = (size_t)(V + TOPK_SLICE - 1) / TOPK_SLICE;
+    c->tf.pv = cv.take<float>(rows * nsf * KMAX);
+    c->tf.pi = cv.take<int>(rows * nsf * KMAX);
+    c->tf.pmax = cv.take<float>(rows * nsf);
+    c->tf.psum = cv.take<double>(rows * nsf);
+  }
   c->tk_wsum = cv.take<unsigned long long>((size_t)R * sampler_slices(V));
   c->acc_sel = cv.take<int>(B);
   c->rm.seq = cv.take<int>(R);
@@ -381,6 +389,32 @@ int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, flo
   return used;
 }
 
+// LM head over n rows of X (bf16, n <= 64) with the top-k of every row taken in the GEMM's epilogue
+// (per 128-id slice) and merged by one more kernel: logits [n, V] as run_gemm writes them, the k best (id,
+// value) of each row in tk_ids / tk_vals, and the log-sum-exp of logits / temperature in tk_lse / tk_lse64
+// when lse.  Returns false, launching nothing, for shapes the fused kernel does not cover.
+bool run_lm_topk(eagle3_ctx* c, const void* X, int n, const void* W, int V, float* logits, int k, float temperature,
+                 bool lse) {
+  const int d = c->sh.d_model;
+  if (!c->bf16 || n <= 0 || n > 64) return false;
+  SliceTopk tk = c->tf;
+  tk.k = k;
+  tk.ns = (V + TOPK_SLICE - 1) / TOPK_SLICE;
+  tk.temp = (double)temperature;
+  if (!lse) {
+    tk.pmax = nullptr;
+    tk.psum = nullptr;
+  }
+  ProfRec rec{};
+  const double bytes = (double)V * d * c->esz + (double)n * d * c->esz + (double)n * V * 4.0;
+  prof_begin(c, n <= 16 ? EAGLE3_PROF_GEMM_M16 : EAGLE3_PROF_GEMM_M64, bytes, 2.0 * n * V * d, &rec, false);
+  const bool ok = gemm_lm_topk(X, n, d, W, V, logits, V, tk, c->st, rec.a, rec.b);
+  prof_end(c, &rec, false);
+  if (!ok) return false;
+  topk_merge_slices(n, tk, c->tk_ids, c->tk_vals, lse ? c->tk_lse : nullptr, lse ? c->tk_lse64 : nullptr, c->st);
+  return true;
+}
+
 // abuf = T(silu(X w_gate^T) * (X w_up^T)) for X [M, K]: fused into the GEMM's
 // epilogue for bf16 when the fused launch has enough workgroups without a K
 // split (M > 64, or F / 64 >= 128 column groups), else GEMM partials +
@@ -490,6 +524,10 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
   }
   if (!final_normed) rmsnorm(bf, fin, c->tw.final_norm, c->gbuf, d, n, d, s.rms_eps, nullptr, 0, st, packed_inputs(c, n));
   float* lg = logits ? logits : c->logits;
+  if ((argmax || margin) && run_lm_topk(c, c->gbuf, n, c->tw.lm_head, s.vocab, lg, 2, 1.f, false)) {
+    k_argmax_margin<<<nb(n, 128), 128, 0, st>>>(n, c->tk_ids, c->tk_vals, 2, argmax, margin);
+    return;
+  }
   run_gemm(c, c->gbuf, n, d, make_segs(c->tw.lm_head, s.vocab), lg);
   if (argmax || margin) {
     topk_lse(lg, n, s.vocab, s.vocab, 2, 1.f, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids, c->tk_vals,
@@ -532,12 +570,14 @@ void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, in
   const eagle3_shape& s = c->sh;
   rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st,
           packed_inputs(c, n));
-  run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->dhead, c->Vd), c->logits);
+  const bool fused = run_lm_topk(c, c->gbuf, n, c->dhead, c->Vd, c->logits, K, temperature, true);
+  if (!fused) run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->dhead, c->Vd), c->logits);
   if (c->dl_out && n > 0)
     k_copy_logit_rows<<<dim3(nb(c->Vd, 1024), n), 256, 0, c->st>>>(c->logits, per, c->Vd, c->dl_out,
                                                                    (size_t)(1 + c->emax) * c->Vd, row0);
-  topk_lse(c->logits, n, c->Vd, c->Vd, K, temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids,
-           c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
+  if (!fused)
+    topk_lse(c->logits, n, c->Vd, c->Vd, K, temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids,
+             c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
   map_draft_ids(c->tk_ids, n * K, c->d2t, c->Vd, c->st);
 }
 

@@ -109,12 +109,19 @@ void pack_linear(const void* src, void* dst, int N, int K, hipStream_t st) {
 // projections (F rows each); wave w's block 0 is gate rows and block 1 the up
 // rows of the same 16 columns, and the epilogue writes
 // act[m][n] = bf16(silu(g) * u) straight from the accumulators.
-template <int MB, int NB, int NW, bool FUSE>
+//
+// TOPK (one segment, no K split, 128 columns per workgroup): after storing
+// its logits the workgroup stages them in LDS and takes, for each of its
+// rows, the tk.k best (value, id) pairs of its 128 ids with tk.k rounds of a
+// wave-wide argmax (one wave per row, two ids per lane; taken ids drop out),
+// plus the slice's maximum and sum of exponentials for the log-sum-exp.
+template <int MB, int NB, int NW, bool FUSE, bool TOPK = false>
 __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
                                                    TileMap tm, float* __restrict__ out, int ldo, size_t split_stride,
                                                    int kchunk, int mtiles, int S, int nwork,
-                                                   bf16_t* __restrict__ act) {
+                                                   bf16_t* __restrict__ act, SliceTopk tk) {
   static_assert(!FUSE || NB == 2, "the fused gate/up epilogue pairs a gate and an up block in each wave");
+  static_assert(!TOPK || (!FUSE && 16 * NB * NW == TOPK_SLICE), "a top-k workgroup owns one 128-id slice");
   constexpr int KT = PACK_KB;               // K per step: one slab
   constexpr int KS = KT / 32;               // fragments per block and step
   constexpr int NT = 64 * NW;               // threads
@@ -255,6 +262,70 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
         if (m < M) o[(size_t)m * ldo] = acc[nb][mb][r];
       }
   }
+  if constexpr (TOPK) {
+    // The tile goes to LDS, over the activation buffers (free: the K loop ended with a barrier); ids past the
+    // vocabulary are -inf and marked taken.  Each 16-lane row of a wave then owns one tile row: a lane holds 8
+    // of its 128 values, and each of the tk.k rounds takes the row's best (value, id) with four DPP steps.
+    static_assert(sizeof(xs) >= sizeof(float) * 16 * MB * (TOPK_SLICE + 1), "the logit tile fits the LDS buffers");
+    float(*tt)[TOPK_SLICE + 1] = reinterpret_cast<float(*)[TOPK_SLICE + 1]>(&xs[0][0][0]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int c = 16 * (NB * wv + nb) + lr;
+      const bool in = n0 + c < nrows;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tt[16 * mb + 4 * lg + r][c] = in ? acc[nb][mb][r] : -INFINITY;
+    }
+    __syncthreads();
+    const int rows = min(16 * MB, M - m0);
+    const int slice = ntile;
+    for (int rb = 4 * wv; rb < rows; rb += 4 * NW) {  // wave-uniform; row rb + lg in lane row lg
+      const int rr = rb + lg;
+      const bool live = rr < rows;  // uniform within the lane row
+      float x[8];
+      int id[8];
+      unsigned taken = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = lr + 16 * j;
+        x[j] = live ? tt[rr][c] : -INFINITY;
+        id[j] = n0 + c;
+        if (!live || id[j] >= nrows) taken |= 1u << j;
+      }
+      const size_t o = (size_t)(m0 + rr) * tk.ns + slice;
+      float top = -INFINITY;
+      for (int k = 0; k < tk.k; ++k) {
+        VI b{-INFINITY, 0x7fffffff};
+        int bj = -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool take = !((taken >> j) & 1u) & better(x[j], id[j], b.v, b.i);
+          b = take ? VI{x[j], id[j]} : b;
+          bj = take ? j : bj;
+        }
+        const VI rbst = row16_best(b);
+        if (bj >= 0 && b.i == rbst.i && b.v == rbst.v) taken |= 1u << bj;
+        if (k == 0) top = rbst.v;
+        if (live && lr == 0) {
+          tk.pv[o * tk.k + k] = rbst.v;
+          tk.pi[o * tk.k + k] = rbst.i;
+        }
+      }
+      if (tk.pmax) {  // the slice's maximum and sum of exp(z / T - max / T) in double, as the separate pass takes them
+        const double mt = (double)top / tk.temp;
+        double sum = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (live && id[j] < nrows) sum += exp((double)x[j] / tk.temp - mt);
+        sum = row16_sum_d(sum);
+        if (live && lr == 0) {
+          tk.pmax[o] = top;
+          tk.psum[o] = sum;
+        }
+      }
+    }
+  }
 }
 
 // The skinny variants: M <= 16: <MB 1, NB 2, 4 waves>; M <= 64: <MB 4, NB 1,
@@ -326,11 +397,32 @@ void gemm_silu(const void* X, int M, int K, const void* w_gate, const void* w_up
   if (M <= 16)
     hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, 4, true>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                           (const bf16_t*)X, M, K, segs, tm, (float*)nullptr, 0, (size_t)0, K, 1, 1, nwork,
-                          (bf16_t*)act);
+                          (bf16_t*)act, SliceTopk{});
   else
     hipExtLaunchKernelGGL((k_gemm_bf16<4, 2, 4, true>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                           (const bf16_t*)X, M, K, segs, tm, (float*)nullptr, 0, (size_t)0, K, 1, 1, nwork,
-                          (bf16_t*)act);
+                          (bf16_t*)act, SliceTopk{});
+}
+
+bool gemm_lm_topk(const void* X, int M, int K, const void* W, int V, float* logits, int ldo, const SliceTopk& tk,
+                  hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const int ns = (V + TOPK_SLICE - 1) / TOPK_SLICE;
+  if (M <= 0 || M > 64 || K <= 0 || K % PACK_KB || V <= 0 || tk.k < 1 || tk.k > 16 || tk.ns != ns || ns > 1024 ||
+      !tk.pv || !tk.pi || (tk.pmax && !tk.psum))
+    return false;
+  const GemmSegs segs = make_segs(W, V);
+  const TileMap tm = tile_map(segs, TOPK_SLICE);
+  const int nwork = tm.tiles0[1];  // one workgroup per slice, no K split
+  const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
+  if (M <= 16)
+    hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, 4, false, true>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
+                          (const bf16_t*)X, M, K, segs, tm, logits, ldo, (size_t)0, K, 1, 1, nwork, (bf16_t*)nullptr,
+                          tk);
+  else
+    hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, 8, false, true>), dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0,
+                          (const bf16_t*)X, M, K, segs, tm, logits, ldo, (size_t)0, K, 1, 1, nwork, (bf16_t*)nullptr,
+                          tk);
+  return true;
 }
 
 int gemm_rows_per_tile(bool bf16, int m_tile) {
@@ -363,19 +455,19 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
     if (m_tile == 16 && narrow)
       hipExtLaunchKernelGGL((k_gemm_bf16<1, 1, 4, false>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                             (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
-                            (bf16_t*)nullptr);
+                            (bf16_t*)nullptr, SliceTopk{});
     else if (m_tile == 16)
       hipExtLaunchKernelGGL((k_gemm_bf16<1, 2, 4, false>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                             (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
-                            (bf16_t*)nullptr);
+                            (bf16_t*)nullptr, SliceTopk{});
     else if (narrow)
       hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, 4, false>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                             (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
-                            (bf16_t*)nullptr);
+                            (bf16_t*)nullptr, SliceTopk{});
     else
       hipExtLaunchKernelGGL((k_gemm_bf16<4, 1, 8, false>), dim3(grid), dim3(512), 0, st, ev_start, ev_stop, 0,
                             (const bf16_t*)X, M, K, segs, tm, out, ldo, split_stride, kchunk, mtiles, S, nwork,
-                            (bf16_t*)nullptr);
+                            (bf16_t*)nullptr, SliceTopk{});
   } else {
     const int ntiles = segs.tiles0[segs.nseg];
     const int per = ((K + 31) / 32 + splits - 1) / splits;

@@ -352,38 +352,6 @@ constexpr int TK_KMAX = 16;
 
 int topk_slices(int V) { return (V + TK_SLICE - 1) / TK_SLICE; }
 
-struct VI {
-  float v;
-  int i;
-};
-
-E3_DEV VI vi_best(VI a, VI b) { return better(a.v, a.i, b.v, b.i) ? a : b; }
-
-// Best (value, index) of a full wave, returned uniformly to every lane.  Within
-// each 16-lane row: DPP exchanges with lanes xor 1, xor 2 (quad permutes), then
-// the half-row and row mirrors; across rows: a swizzle with lane xor 16, then
-// lanes 0 and 32 are read as scalars.  The order is a total order, so the
-// result does not depend on the reduction tree.  Every lane must be active.
-template <int CTRL>
-E3_DEV VI vi_dpp(VI a) {
-  const VI b{__int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a.v), CTRL, 0xF, 0xF, false)),
-             __builtin_amdgcn_update_dpp(0, a.i, CTRL, 0xF, 0xF, false)};
-  return vi_best(a, b);
-}
-
-E3_DEV VI wave_best(VI x) {
-  x = vi_dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  x = vi_dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  x = vi_dpp<0x141>(x);  // row_half_mirror
-  x = vi_dpp<0x140>(x);  // row_mirror
-  const VI y{__int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x.v), 0x401F)),
-             __builtin_amdgcn_ds_swizzle(x.i, 0x401F)};  // lane xor 16 within each 32
-  x = vi_best(x, y);
-  const VI h0{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x.v), 0)), __builtin_amdgcn_readlane(x.i, 0)};
-  const VI h1{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x.v), 32)), __builtin_amdgcn_readlane(x.i, 32)};
-  return vi_best(h0, h1);
-}
-
 // grid (R, nslices), block 256.  Per slice: the K best (value, index) and,
 // when LSE, the slice's max and sum of exp(z - max) in double, with z = logit /
 // temperature.  The slice is held in registers (16 values per thread, loaded
@@ -523,6 +491,122 @@ void topk_lse(const float* logits, int R, int V, int ld, int K, float temperatur
   else
     k_topk_partial<false><<<dim3(R, ns), 256, 0, st>>>(logits, V, ld, K, t, pv, pi, pmax, psum);
   k_topk_merge<<<R, 64, 0, st>>>(ns, K, t, pv, pi, lse ? pmax : nullptr, psum, out_ids, out_vals, lse32, lse64);
+}
+
+// grid (R), block 256: merge the 128-id slices of the fused LM-head top-k.
+// The k best of a row lie in the k slices whose own best (value, id) pairs
+// rank highest: a pair among the k best has its slice's best at or above it,
+// and k slices ranked above that slice would hold k pairs above it.  So the
+// kernel first picks those k slices (a thread holds the best of up to 4
+// slices; each wave takes its k best in k rounds, wave 0 merges the four
+// lists), then wave 0 takes the k best of their k x k candidates.  The
+// log-sum-exp combines the slices' maxima and sums as the separate merge does.
+__global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __restrict__ out_ids,
+                                                           float* __restrict__ out_vals, float* __restrict__ lse32,
+                                                           double* __restrict__ lse64) {
+  __shared__ VI cand[4][TK_KMAX];
+  __shared__ int sel[TK_KMAX];
+  __shared__ float fred[4];
+  __shared__ double dred[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int K = tk.k, ns = tk.ns;
+  const float* cv = tk.pv + (size_t)r * ns * K;
+  const int* ci = tk.pi + (size_t)r * ns * K;
+  float v[4];
+  int id[4];
+  unsigned taken = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // slice s = tid + 256 j: its best pair is its candidate 0
+    const int sl = tid + 256 * j;
+    v[j] = sl < ns ? cv[(size_t)sl * K] : -INFINITY;
+    id[j] = sl < ns ? ci[(size_t)sl * K] : 0x7fffffff;
+    if (sl >= ns) taken |= 1u << j;
+  }
+  for (int k = 0; k < K; ++k) {
+    VI b{-INFINITY, 0x7fffffff};
+    int bj = -1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool take = !((taken >> j) & 1u) & better(v[j], id[j], b.v, b.i);
+      b = take ? VI{v[j], id[j]} : b;
+      bj = take ? j : bj;
+    }
+    const VI wb = wave_best(b);
+    if (bj >= 0 && b.i == wb.i && b.v == wb.v) taken |= 1u << bj;
+    if (lane == 0) cand[w][k] = wb;
+  }
+  __syncthreads();
+  if (w == 0) {
+    // the k best slices (a slice is known by its best id: ids of slice s are s * 128 ..)
+    VI mine = lane < 4 * K ? cand[lane / K][lane % K] : VI{-INFINITY, 0x7fffffff};
+    for (int k = 0; k < K; ++k) {
+      const VI wb = wave_best(mine);
+      if (mine.i == wb.i && mine.v == wb.v) mine = VI{-INFINITY, 0x7fffffff};
+      if (lane == 0) sel[k] = wb.i == 0x7fffffff ? -1 : wb.i / TOPK_SLICE;
+    }
+    // their k x k candidates, up to 4 per lane
+    VI c4[4];
+    unsigned t4 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = lane + 64 * i;
+      const int sl = c < K * K ? sel[c / K] : -1;
+      c4[i] = sl >= 0 ? VI{cv[(size_t)sl * K + c % K], ci[(size_t)sl * K + c % K]} : VI{-INFINITY, 0x7fffffff};
+      if (sl < 0) t4 |= 1u << i;
+    }
+    for (int k = 0; k < K; ++k) {
+      VI b{-INFINITY, 0x7fffffff};
+      int bj = -1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool take = !((t4 >> i) & 1u) & better(c4[i].v, c4[i].i, b.v, b.i);
+        b = take ? c4[i] : b;
+        bj = take ? i : bj;
+      }
+      const VI wb = wave_best(b);
+      if (bj >= 0 && b.i == wb.i && b.v == wb.v) t4 |= 1u << bj;
+      if (lane == 0) {
+        out_ids[(size_t)r * K + k] = wb.i;
+        out_vals[(size_t)r * K + k] = wb.v;
+      }
+    }
+  }
+  if (!tk.pmax) return;  // uniform: no log-sum-exp asked for
+  float pm[4];
+  double ps[4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sl = tid + 256 * j;
+    pm[j] = sl < ns ? tk.pmax[(size_t)r * ns + sl] : -INFINITY;
+    ps[j] = sl < ns ? tk.psum[(size_t)r * ns + sl] : 0.0;
+    mloc = fmaxf(mloc, pm[j]);
+  }
+  const float wm = wave_max(mloc);
+  if (lane == 0) fred[w] = wm;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
+  const double M = (double)mx / tk.temp;
+  double sloc = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (tid + 256 * j < ns) sloc += ps[j] * exp((double)pm[j] / tk.temp - M);
+  const double sw = wave_sum_d(sloc);
+  if (lane == 0) dred[w] = sw;
+  __syncthreads();
+  if (tid == 0) {
+    const double l = M + log(dred[0] + dred[1] + dred[2] + dred[3]);
+    if (lse64) lse64[r] = l;
+    if (lse32) lse32[r] = (float)l;
+  }
+}
+
+void topk_merge_slices(int R, const SliceTopk& tk, int* out_ids, float* out_vals, float* lse32, double* lse64,
+                       hipStream_t st) {
+  if (R <= 0) return;
+  SliceTopk t = tk;
+  if (!lse32 && !lse64) t.pmax = nullptr;
+  k_topk_merge_slices<<<R, 256, 0, st>>>(t, out_ids, out_vals, lse32, lse64);
 }
 
 // -------------------------------------------------------------- row gather

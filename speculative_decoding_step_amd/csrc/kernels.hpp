@@ -25,6 +25,23 @@ struct GemmSegs {
   int nseg;
 };
 
+// Per-slice top-k of an LM-head GEMM's logits, taken in the GEMM's epilogue:
+// every workgroup owns 128 consecutive vocabulary ids (one slice) of every
+// row, and writes for each row its k best (value, id) pairs to
+// pv / pi [row][slice][k] and, when pmax is non-null, the slice's largest
+// logit and sum of exp(z / temp - max / temp) (in double) to pmax / psum
+// [row][slice].  topk_merge_slices combines the slices of each row.
+struct SliceTopk {
+  int k = 0;  // 0: no top-k epilogue
+  int ns = 0;  // slices per row (vocabulary / 128, rounded up)
+  double temp = 1.0;
+  float* pv = nullptr;
+  int* pi = nullptr;
+  float* pmax = nullptr;
+  double* psum = nullptr;
+};
+constexpr int TOPK_SLICE = 128;  // vocabulary ids per slice of the fused LM-head top-k
+
 GemmSegs make_segs(const void* w0, int r0, const void* w1 = nullptr, int r1 = 0,
                    const void* w2 = nullptr, int r2 = 0);
 
@@ -39,6 +56,18 @@ GemmSegs make_segs(const void* w0, int r0, const void* w1 = nullptr, int r1 = 0,
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out,
          size_t split_stride, int splits, int m_tile, hipStream_t st,
          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr, bool a_packed = false);
+// LM head with its top-k taken in the epilogue (bf16, M <= 64 rows, W [V, K]
+// packed): logits [M, ldo] fp32 as gemm() writes them, plus the per-slice
+// candidates of tk (tk.ns = ceil(V / TOPK_SLICE)).  Returns false, launching
+// nothing, when the shape is not covered (M > 64, K not a multiple of 128,
+// tk.k outside 1..16, more than 1024 slices).
+bool gemm_lm_topk(const void* X, int M, int K, const void* W, int V, float* logits, int ldo, const SliceTopk& tk,
+                  hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+// Merge the slices of gemm_lm_topk: the k best (value, id) of every row in
+// (value desc, id asc) order, and its log-sum-exp of z / temp when pmax was
+// written (lse32 / lse64 may be null).
+void topk_merge_slices(int R, const SliceTopk& tk, int* out_ids, float* out_vals, float* lse32, double* lse64,
+                       hipStream_t st);
 // The large-M kernel behind gemm() for m_tile 128: weight rows per tile and
 // K step (K must be a multiple of it); returns the number of splits used.
 constexpr int GEMM_BIG_ROWS = 256, GEMM_BIG_KSTEP = 32;
