@@ -181,7 +181,8 @@ def cpu_baseline(w):
     samples = {1: [], 2: [], "draft": []}
     shp2 = Shape(2, ms.d, ms.n_heads, ms.n_kv_heads, ms.head_dim, ms.ffn, ms.vocab, ms.rope_theta, ms.eps,
                  ms.dtype, (0, 0, 1))
-    spec = SpecConfig(w.mode, w.depth, w.topk, w.n_nodes)
+    spec = SpecConfig(w.mode, w.depth, w.topk, w.n_nodes, w.temperature)
+    u_draft = synth.uniform24_np(10, "cpu_u_draft", w.depth + 1)  # the sampled chain's draws (seeded)
     Pd = 32
     dk = synth.normal_np(8, "dk", (Pd - 1, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
     dv = synth.normal_np(8, "dv", (Pd - 1, ms.n_kv_heads, ms.head_dim), 1.0, "bf16")
@@ -202,7 +203,7 @@ def cpu_baseline(w):
         seq.next_tok = [int(toks[0])]
         seq.root = int(toks[0])
         t0 = time.perf_counter()
-        seq.draft_tree()
+        seq.draft_tree(u_draft)
         samples["draft"].append(time.perf_counter() - t0)
     times = {k: float(np.median(v)) for k, v in samples.items()}
     t_layer = times[2] - times[1]
