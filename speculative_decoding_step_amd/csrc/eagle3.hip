@@ -390,7 +390,8 @@ int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, flo
 }
 
 // LM head over n rows of X (bf16, n <= 64) with the top-k of every row taken in the GEMM's epilogue
-// (per 128-id slice) and merged by one more kernel: logits [n, V] as run_gemm writes them, the k best (id,
+// (per 128-id slice) and merged by one more kernel: logits [n, V] as run_gemm writes them (none when logits
+// is null), the k best (id,
 // value) of each row in tk_ids / tk_vals, and the log-sum-exp of logits / temperature in tk_lse / tk_lse64
 // when lse.  Returns false, launching nothing, for shapes the fused kernel does not cover.
 bool run_lm_topk(eagle3_ctx* c, const void* X, int n, const void* W, int V, float* logits, int k, float temperature,
@@ -524,7 +525,8 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
   }
   if (!final_normed) rmsnorm(bf, fin, c->tw.final_norm, c->gbuf, d, n, d, s.rms_eps, nullptr, 0, st, packed_inputs(c, n));
   float* lg = logits ? logits : c->logits;
-  if ((argmax || margin) && run_lm_topk(c, c->gbuf, n, c->tw.lm_head, s.vocab, lg, 2, 1.f, false)) {
+  // the fused head writes the logits only when the caller asked for them
+  if ((argmax || margin) && run_lm_topk(c, c->gbuf, n, c->tw.lm_head, s.vocab, logits, 2, 1.f, false)) {
     k_argmax_margin<<<nb(n, 128), 128, 0, st>>>(n, c->tk_ids, c->tk_vals, 2, argmax, margin);
     return;
   }

@@ -249,10 +249,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_bf16(const bf16_t* __restrict_
       }
     return;
   }
-  // result: acc[nb][mb][r] = out[m0 + 16 mb + 4 lg + r][n0 + 16 (NB wv + nb) + lr]
+  // result: acc[nb][mb][r] = out[m0 + 16 mb + 4 lg + r][n0 + 16 (NB wv + nb) + lr]  (TOPK: out may be null)
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    if (n0 + 16 * (NB * wv + nb) + lr >= nrows) continue;
+    if ((TOPK && !out) || n0 + 16 * (NB * wv + nb) + lr >= nrows) continue;
     float* o = out + split * split_stride + segs.col0[seg] + n0 + 16 * (NB * wv + nb) + lr;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)

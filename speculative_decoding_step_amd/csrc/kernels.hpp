@@ -57,7 +57,8 @@ int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* ou
          size_t split_stride, int splits, int m_tile, hipStream_t st,
          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr, bool a_packed = false);
 // LM head with its top-k taken in the epilogue (bf16, M <= 64 rows, W [V, K]
-// packed): logits [M, ldo] fp32 as gemm() writes them, plus the per-slice
+// packed): logits [M, ldo] fp32 as gemm() writes them (not written when
+// logits is null), plus the per-slice
 // candidates of tk (tk.ns = ceil(V / TOPK_SLICE)).  Returns false, launching
 // nothing, when the shape is not covered (M > 64, K not a multiple of 128,
 // tk.k outside 1..16, more than 1024 slices).
