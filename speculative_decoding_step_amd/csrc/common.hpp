@@ -180,6 +180,31 @@ E3_DEV VI vi_swap32(VI x) {
 
 E3_DEV VI wave_best(VI x) { return vi_swap32(vi_swap16(row16_best(x))); }
 
+// Wave-wide maximum and float64 sum in registers only (DPP within rows, permlane swaps across them); every lane
+// must be active.  The sum's lane 0 is the same on every run (a fixed order of additions).
+E3_DEV float wave_max_reg(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+E3_DEV double swap_sum_d(double x, bool wide) {
+  const unsigned long long u = __double_as_longlong(x);
+  const unsigned lo = (unsigned)u, hi = (unsigned)(u >> 32);
+  const auto l = wide ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                      : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = wide ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                      : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const double a = __longlong_as_double((long long)(((unsigned long long)h[0] << 32) | l[0]));
+  const double b = __longlong_as_double((long long)(((unsigned long long)h[1] << 32) | l[1]));
+  return a + b;
+}
+E3_DEV double wave_sum_d_reg(double x) { return swap_sum_d(swap_sum_d(row16_sum_d(x), false), true); }
+
 // Status bits (mirrors eagle3.h).
 #define E3_DEV_KV_OVERFLOW 0x1
 #define E3_DEV_BAD_TREE 0x2

@@ -572,7 +572,9 @@ void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, in
   const eagle3_shape& s = c->sh;
   rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st,
           packed_inputs(c, n));
-  const bool fused = run_lm_topk(c, c->gbuf, n, c->dhead, c->Vd, c->logits, K, temperature, true);
+  // the logits themselves are read only by the chain sampler and the draft-logits table
+  const bool keep = c->dl_out || c->cfg.mode == EAGLE3_SAMPLE_CHAIN;
+  const bool fused = run_lm_topk(c, c->gbuf, n, c->dhead, c->Vd, keep ? c->logits : nullptr, K, temperature, true);
   if (!fused) run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->dhead, c->Vd), c->logits);
   if (c->dl_out && n > 0)
     k_copy_logit_rows<<<dim3(nb(c->Vd, 1024), n), 256, 0, c->st>>>(c->logits, per, c->Vd, c->dl_out,

@@ -512,6 +512,15 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
   const int K = tk.k, ns = tk.ns;
   const float* cv = tk.pv + (size_t)r * ns * K;
   const int* ci = tk.pi + (size_t)r * ns * K;
+  // the slices' log-sum-exp partials, loaded first so that their latency hides under the selection
+  float pm[4];
+  double ps[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sl = tid + 256 * j;
+    pm[j] = tk.pmax && sl < ns ? tk.pmax[(size_t)r * ns + sl] : -INFINITY;
+    ps[j] = tk.pmax && sl < ns ? tk.psum[(size_t)r * ns + sl] : 0.0;
+  }
   float v[4];
   int id[4];
   unsigned taken = 0;
@@ -572,17 +581,10 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
     }
   }
   if (!tk.pmax) return;  // uniform: no log-sum-exp asked for
-  float pm[4];
-  double ps[4];
   float mloc = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int sl = tid + 256 * j;
-    pm[j] = sl < ns ? tk.pmax[(size_t)r * ns + sl] : -INFINITY;
-    ps[j] = sl < ns ? tk.psum[(size_t)r * ns + sl] : 0.0;
-    mloc = fmaxf(mloc, pm[j]);
-  }
-  const float wm = wave_max(mloc);
+  for (int j = 0; j < 4; ++j) mloc = fmaxf(mloc, pm[j]);
+  const float wm = wave_max_reg(mloc);
   if (lane == 0) fred[w] = wm;
   __syncthreads();
   const float mx = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
@@ -591,7 +593,7 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     if (tid + 256 * j < ns) sloc += ps[j] * exp((double)pm[j] / tk.temp - M);
-  const double sw = wave_sum_d(sloc);
+  const double sw = wave_sum_d_reg(sloc);
   if (lane == 0) dred[w] = sw;
   __syncthreads();
   if (tid == 0) {
