@@ -75,7 +75,8 @@ struct eagle3_ctx {
   float *tk_pv, *tk_pmax, *tk_vals, *tk_lse;
   int *tk_pi, *tk_ids;
   double *tk_psum, *tk_lse64;
-  SliceTopk tf;  // candidates of the LM-head GEMMs with the top-k in their epilogue (passes of <= 64 rows)
+  SliceTopk tf;  // candidates of the LM-head GEMMs with the top-k in their epilogue
+  int tf_k = 0;  // the largest k they are sized for
   unsigned long long* tk_wsum;  // per-row slice sums of integer sampling weights
   int* acc_sel;                 // chain acceptance: drafts accepted per sequence
   RowMeta rm;
@@ -128,12 +129,13 @@ size_t carve(eagle3_ctx* c, char* base) {
   c->tk_vals = cv.take<float>((size_t)R * KMAX);
   c->tk_lse = cv.take<float>(R);
   c->tk_lse64 = cv.take<double>(R);
-  {
-    const size_t rows = (size_t)std::min(R, 64), nsf = (size_t)(V + TOPK_SLICE - 1) / TOPK_SLICE;
-    c->tf.pv = cv.take<float>(rows * nsf * KMAX);
-    c->tf.pi = cv.take<int>(rows * nsf * KMAX);
-    c->tf.pmax = cv.take<float>(rows * nsf);
-    c->tf.psum = cv.take<double>(rows * nsf);
+  {  // fused LM-head top-k: up to R rows, k up to the tree's top-k (2 for the verify's argmax and margin)
+    const size_t nsf = (size_t)(V + TOPK_SLICE - 1) / TOPK_SLICE;
+    c->tf_k = std::max(2, c->cfg.topk);
+    c->tf.pv = cv.take<float>((size_t)R * nsf * c->tf_k);
+    c->tf.pi = cv.take<int>((size_t)R * nsf * c->tf_k);
+    c->tf.pmax = cv.take<float>((size_t)R * nsf);
+    c->tf.psum = cv.take<double>((size_t)R * nsf);
   }
   c->tk_wsum = cv.take<unsigned long long>((size_t)R * sampler_slices(V));
   c->acc_sel = cv.take<int>(B);
@@ -389,7 +391,7 @@ int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, flo
   return used;
 }
 
-// LM head over n rows of X (bf16, n <= 64) with the top-k of every row taken in the GEMM's epilogue
+// LM head over n rows of X (bf16) with the top-k of every row taken in the GEMM's epilogue
 // (per 128-id slice) and merged by one more kernel: logits [n, V] as run_gemm writes them (none when logits
 // is null), the k best (id,
 // value) of each row in tk_ids / tk_vals, and the log-sum-exp of logits / temperature in tk_lse / tk_lse64
@@ -397,7 +399,7 @@ int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, flo
 bool run_lm_topk(eagle3_ctx* c, const void* X, int n, const void* W, int V, float* logits, int k, float temperature,
                  bool lse) {
   const int d = c->sh.d_model;
-  if (!c->bf16 || n <= 0 || n > 64) return false;
+  if (!c->bf16 || n <= 0 || n > c->R || k > c->tf_k) return false;
   SliceTopk tk = c->tf;
   tk.k = k;
   tk.ns = (V + TOPK_SLICE - 1) / TOPK_SLICE;
@@ -408,7 +410,8 @@ bool run_lm_topk(eagle3_ctx* c, const void* X, int n, const void* W, int V, floa
   }
   ProfRec rec{};
   const double bytes = (double)V * d * c->esz + (double)n * d * c->esz + (double)n * V * 4.0;
-  prof_begin(c, n <= 16 ? EAGLE3_PROF_GEMM_M16 : EAGLE3_PROF_GEMM_M64, bytes, 2.0 * n * V * d, &rec, false);
+  prof_begin(c, n <= 16 ? EAGLE3_PROF_GEMM_M16 : (n <= 64 ? EAGLE3_PROF_GEMM_M64 : EAGLE3_PROF_GEMM_BIG), bytes,
+             2.0 * n * V * d, &rec, false);
   const bool ok = gemm_lm_topk(X, n, d, W, V, logits, V, tk, c->st, rec.a, rec.b);
   prof_end(c, &rec, false);
   if (!ok) return false;

@@ -407,9 +407,13 @@ void gemm_silu(const void* X, int M, int K, const void* w_gate, const void* w_up
 bool gemm_lm_topk(const void* X, int M, int K, const void* W, int V, float* logits, int ldo, const SliceTopk& tk,
                   hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int ns = (V + TOPK_SLICE - 1) / TOPK_SLICE;
-  if (M <= 0 || M > 64 || K <= 0 || K % PACK_KB || V <= 0 || tk.k < 1 || tk.k > 16 || tk.ns != ns || ns > 1024 ||
-      !tk.pv || !tk.pi || (tk.pmax && !tk.psum))
+  if (M <= 0 || K <= 0 || K % PACK_KB || V <= 0 || tk.k < 1 || tk.k > 16 || tk.ns != ns || ns > 1024 || !tk.pv ||
+      !tk.pi || (tk.pmax && !tk.psum))
     return false;
+  if (M > 64) {
+    gemm_big_lm_topk(X, M, K, W, V, logits, ldo, tk, st, ev_start, ev_stop);
+    return true;
+  }
   const GemmSegs segs = make_segs(W, V);
   const TileMap tm = tile_map(segs, TOPK_SLICE);
   const int nwork = tm.tiles0[1];  // one workgroup per slice, no K split

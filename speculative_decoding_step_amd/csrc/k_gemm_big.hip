@@ -59,11 +59,20 @@ E3_DEV void lds_copy16(const void* g, void* l) {
 // A fragment (16 rows x 32 K) is then one contiguous KiB, like a weight
 // fragment, instead of 16 row pieces of 64 bytes, and a producer writing one
 // row still writes whole 64-byte pieces.
-template <bool FUSE, bool APACK>
+//
+// TOPK (an LM head: one segment, no K split): each wave's 64 x 128 sub-tile
+// is one 128-id slice of 64 rows.  Row 64 wm + 16 i + 4 lg + r of it lives
+// in the 16 lanes of lane row lg, 8 values per lane (acc[i][0..7][r]), so
+// each of tk.k rounds takes the row's best (value, id) pair with four DPP
+// steps, straight from the accumulators; then the slice's maximum and sum of
+// exponentials for the log-sum-exp.  The fp32 logits are stored only when out
+// is non-null.
+template <bool FUSE, bool APACK, bool TOPK = false>
 __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restrict__ X, int M, int K, GemmSegs segs,
                                                           BigTiles bt, float* __restrict__ out, int ldo,
                                                           size_t split_stride, int kchunk, int S, int mtiles,
-                                                          int nwork, bf16_t* __restrict__ act, int F) {
+                                                          int nwork, bf16_t* __restrict__ act, int F, SliceTopk tk) {
+  static_assert(!TOPK || (!FUSE && BN == 2 * TOPK_SLICE), "a top-k wave owns one 128-id slice");
   __shared__ __attribute__((aligned(1024))) bf16_t sa0[AFR * 512], sa1[AFR * 512], sa2[AFR * 512];
   __shared__ __attribute__((aligned(1024))) bf16_t sb0[BFR * 512], sb1[BFR * 512], sb2[BFR * 512];
   const int per = (nwork + 7) >> 3;
@@ -167,17 +176,67 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_big(const bf16_t* __restri
     return;
   }
   // acc[i][j][r] = out[m0 + 64 wm + 16 i + 4 lg + r][n0 + 128 wn + 16 j + lr]
-  float* o = out + split * split_stride + segs.col0[seg];
+  if (!TOPK || out) {
+    float* o = out + split * split_stride + segs.col0[seg];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int n = n0 + 128 * wn + 16 * j + lr;
-    if (n >= nrows) continue;
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + 128 * wn + 16 * j + lr;
+      if (n >= nrows) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
+          if (m < M) o[(size_t)m * ldo + n] = acc[i][j][r];
+        }
+    }
+  }
+  if constexpr (TOPK) {
+    const int slice = (n0 >> 7) + wn;
+    int id[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) id[j] = n0 + 128 * wn + 16 * j + lr;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
-        if (m < M) o[(size_t)m * ldo + n] = acc[i][j][r];
+        const bool live = m < M;  // uniform within the lane row
+        unsigned taken = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (!live || id[j] >= nrows) taken |= 1u << j;
+        const size_t o = (size_t)m * tk.ns + slice;
+        float top = -INFINITY;
+        for (int k = 0; k < tk.k; ++k) {
+          VI b{-INFINITY, 0x7fffffff};
+          int bj = -1;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const bool take = !((taken >> j) & 1u) & better(acc[i][j][r], id[j], b.v, b.i);
+            b = take ? VI{acc[i][j][r], id[j]} : b;
+            bj = take ? j : bj;
+          }
+          const VI rb = row16_best(b);
+          if (bj >= 0 && b.i == rb.i && b.v == rb.v) taken |= 1u << bj;
+          if (k == 0) top = rb.v;
+          if (live && lr == 0) {
+            tk.pv[o * tk.k + k] = rb.v;
+            tk.pi[o * tk.k + k] = rb.i;
+          }
+        }
+        if (tk.pmax) {  // the slice's maximum and sum of exp(z / T - max / T) in double
+          const double mt = (double)top / tk.temp;
+          double sum = 0.0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (live && id[j] < nrows) sum += exp((double)acc[i][j][r] / tk.temp - mt);
+          sum = row16_sum_d(sum);
+          if (live && lr == 0) {
+            tk.pmax[o] = top;
+            tk.psum[o] = sum;
+          }
+        }
       }
   }
 }
@@ -198,13 +257,27 @@ int gemm_big(const void* X, int M, int K, const GemmSegs& segs, float* out, size
     if (a_packed)
       hipExtLaunchKernelGGL((k_gemm_bf16_big<false, true>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                             (const bf16_t*)X, M, K, segs, bt, out, gemm_ntot(segs), split_stride, kchunk, S, mtiles,
-                            nwork, (bf16_t*)nullptr, 0);
+                            nwork, (bf16_t*)nullptr, 0, SliceTopk{});
     else
       hipExtLaunchKernelGGL((k_gemm_bf16_big<false, false>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                             (const bf16_t*)X, M, K, segs, bt, out, gemm_ntot(segs), split_stride, kchunk, S, mtiles,
-                            nwork, (bf16_t*)nullptr, 0);
+                            nwork, (bf16_t*)nullptr, 0, SliceTopk{});
   }
   return S;
+}
+
+void gemm_big_lm_topk(const void* X, int M, int K, const void* W, int V, float* logits, int ldo, const SliceTopk& tk,
+                      hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const GemmSegs segs = make_segs(W, V);
+  BigTiles bt;
+  bt.tiles0[0] = 0;
+  bt.tiles0[1] = bt.tiles0[2] = bt.tiles0[3] = (V + BN - 1) / BN;
+  const int mtiles = (M + BM - 1) / BM;
+  const int nwork = mtiles * bt.tiles0[1];
+  const unsigned grid = 8u * (unsigned)((nwork + 7) / 8);
+  hipExtLaunchKernelGGL((k_gemm_bf16_big<false, true, true>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
+                        (const bf16_t*)X, M, K, segs, bt, logits, ldo, (size_t)0, K, 1, mtiles, nwork,
+                        (bf16_t*)nullptr, 0, tk);
 }
 
 void gemm_big_silu(const void* X, int M, int K, const void* w_gate, const void* w_up, int F, void* act,
@@ -219,7 +292,7 @@ void gemm_big_silu(const void* X, int M, int K, const void* w_gate, const void* 
   // the down projection)
   hipExtLaunchKernelGGL((k_gemm_bf16_big<true, true>), dim3(grid), dim3(256), 0, st, ev_start, ev_stop, 0,
                         (const bf16_t*)X, M, K, segs, bt, (float*)nullptr, 0, (size_t)0, K, 1, mtiles, nwork,
-                        (bf16_t*)act, F);
+                        (bf16_t*)act, F, SliceTopk{});
 }
 
 }  // namespace e3

@@ -56,12 +56,12 @@ GemmSegs make_segs(const void* w0, int r0, const void* w1 = nullptr, int r1 = 0,
 int gemm(bool bf16, const void* X, int M, int K, const GemmSegs& segs, float* out,
          size_t split_stride, int splits, int m_tile, hipStream_t st,
          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr, bool a_packed = false);
-// LM head with its top-k taken in the epilogue (bf16, M <= 64 rows, W [V, K]
-// packed): logits [M, ldo] fp32 as gemm() writes them (not written when
-// logits is null), plus the per-slice
-// candidates of tk (tk.ns = ceil(V / TOPK_SLICE)).  Returns false, launching
-// nothing, when the shape is not covered (M > 64, K not a multiple of 128,
-// tk.k outside 1..16, more than 1024 slices).
+// LM head with its top-k taken in the epilogue (bf16, W [V, K] packed; X
+// row-major for M <= 64 rows, in column slabs of 32 above, as the large-M GEMM
+// reads it): logits [M, ldo] fp32 as gemm() writes them (not written when
+// logits is null), plus the per-slice candidates of tk (tk.ns = ceil(V /
+// TOPK_SLICE)).  Returns false, launching nothing, when the shape is not
+// covered (K not a multiple of 128, tk.k outside 1..16, more than 1024 slices).
 bool gemm_lm_topk(const void* X, int M, int K, const void* W, int V, float* logits, int ldo, const SliceTopk& tk,
                   hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 // Merge the slices of gemm_lm_topk: the k best (value, id) of every row in
@@ -69,6 +69,9 @@ bool gemm_lm_topk(const void* X, int M, int K, const void* W, int V, float* logi
 // written (lse32 / lse64 may be null).
 void topk_merge_slices(int R, const SliceTopk& tk, int* out_ids, float* out_vals, float* lse32, double* lse64,
                        hipStream_t st);
+// The large-M form of gemm_lm_topk (M > 64, X in column slabs of 32).
+void gemm_big_lm_topk(const void* X, int M, int K, const void* W, int V, float* logits, int ldo, const SliceTopk& tk,
+                      hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
 // The large-M kernel behind gemm() for m_tile 128: weight rows per tile and
 // K step (K must be a multiple of it); returns the number of splits used.
 constexpr int GEMM_BIG_ROWS = 256, GEMM_BIG_KSTEP = 32;
