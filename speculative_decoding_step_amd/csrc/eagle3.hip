@@ -545,7 +545,20 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
 // a on exit; tokens in tok; row metadata rm (draft KV cache).  fc_splits > 0:
 // x is formed on entry from that many fusion-FC split partials in c->part
 // (g = W_fc [l; m; h]) by the same kernel that builds the layer's input.
-void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const RowMeta& rm, int fc_splits = 0) {
+// io (optional): the layer's input rows gathered from their parents' outputs by the kernel that builds the
+// layer's input (src / a_rows / a_last, as draft_input takes them), and, with norm_out, the layer's last
+// kernel also forms the draft LM head's input (x += partials; gbuf = T(rmsnorm(x) * final_norm)) and copies
+// the rows to the tree's expansion-row store (keep).
+struct DraftIo {
+  const int* src = nullptr;
+  const float* a_rows = nullptr;
+  const float* a_last = nullptr;
+  bool norm_out = false;
+  RowCopy keep;
+};
+
+void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const RowMeta& rm, int fc_splits = 0,
+                 const DraftIo* io = nullptr) {
   const eagle3_shape& s = c->sh;
   const eagle3_head_weights& H = c->hw;
   const int d = s.d_model, qdim = s.n_heads * s.head_dim, kvdim = s.n_kv_heads * s.head_dim;
@@ -553,7 +566,8 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
   hipStream_t st = c->st;
   const bool pk = packed_inputs(c, R);
   draft_input(bf, c->tw.embed, tok, x, fc_splits ? c->part : nullptr, fc_splits, (size_t)R * d, H.input_norm,
-              H.hidden_norm, c->hbuf, R, d, s.vocab, s.rms_eps, c->status, st, pk);
+              H.hidden_norm, c->hbuf, R, d, s.vocab, s.rms_eps, c->status, st, pk, io ? io->src : nullptr,
+              io ? io->a_rows : nullptr, io ? io->a_last : nullptr);
   const GemmSegs qkv = make_segs(H.wq, qdim, H.wk, kvdim, H.wv, kvdim);
   int S = run_gemm(c, c->hbuf, R, 2 * d, qkv);
   char* kc = kv_layer(c, c->kv_d, 0, 0);
@@ -565,16 +579,22 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
   add_rmsnorm(bf, x, c->part, S, (size_t)R * d, d, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st, pk);
   run_gateup(c, c->hbuf, R, d, H.w_gate, H.w_up, s.ffn);
   S = run_gemm(c, c->abuf, R, s.ffn, make_segs(H.w_down, d));
-  resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
+  if (io && io->norm_out)
+    add_rmsnorm(bf, x, c->part, S, (size_t)R * d, d, H.final_norm, c->gbuf, d, R, d, s.rms_eps, nullptr, 0, st, pk,
+                io->keep);
+  else
+    resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
 }
 
 // Draft logits of n rows of a (fp32 [n, d]) -> c->logits; top-K + lse.  With a
 // draft logits table set, the n rows (per rows of each of n / per sequences)
-// are also copied to table rows row0 .. row0 + per - 1.
-void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, int per, int row0) {
+// are also copied to table rows row0 .. row0 + per - 1.  normed: the head's
+// input (the rows' final norm, in c->gbuf) is already there.
+void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, int per, int row0, bool normed = false) {
   const eagle3_shape& s = c->sh;
-  rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st,
-          packed_inputs(c, n));
+  if (!normed)
+    rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st,
+            packed_inputs(c, n));
   // the logits themselves are read only by the chain sampler and the draft-logits table
   const bool keep = c->dl_out || c->cfg.mode == EAGLE3_SAMPLE_CHAIN;
   const bool fused = run_lm_topk(c, c->gbuf, n, c->dhead, c->Vd, keep ? c->logits : nullptr, K, temperature, true);
@@ -627,10 +647,16 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
                    c->tk_lse64 + b * k, st);
         map_draft_ids(c->tk_ids, batch * k * k, c->d2t, c->Vd, st);
       } else {
-        tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, n, d, st);
-        draft_layer(c, n, k, dr.tok, c->dx, dr_meta(c));
-        if (dd + 1 < D) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, n, k, c->emax, d, st);
-        draft_lm(c, n, c->dx, k, 1.f, k, 1 + (dd - 1) * k);
+        // the rows' inputs gathered from their parents inside the layer's first kernel; its last kernel forms the
+        // head's input and keeps the rows for their children
+        DraftIo io;
+        io.src = dr.src;
+        io.a_rows = c->a_rows;
+        io.a_last = c->a_last;
+        io.norm_out = true;
+        if (dd + 1 < D) io.keep = RowCopy{c->a_rows, dr.slot, seq_lens, k, c->emax};
+        draft_layer(c, n, k, dr.tok, c->dx, dr_meta(c), 0, &io);
+        draft_lm(c, n, c->dx, k, 1.f, k, 1 + (dd - 1) * k, true);
       }
       tree_children(ts, dd + 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
     }
@@ -653,10 +679,14 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
                    c->chain_tok, batch, c->tk_wsum, c->d2t, st);
       } else {
         chain_rows(j - 1, K, c->chain_tok, seq_lens, c->emax, dr, c->S_cap, st);
-        tree_gather_x(c->dx, dr.src, c->a_rows, c->a_last, batch, d, st);
-        draft_layer(c, batch, 1, dr.tok, c->dx, dr_meta(c));
-        if (j + 1 < K) tree_store_a(c->a_rows, c->dx, dr.slot, seq_lens, batch, 1, c->emax, d, st);
-        draft_lm(c, batch, c->dx, 1, T, 1, j);
+        DraftIo io;
+        io.src = dr.src;
+        io.a_rows = c->a_rows;
+        io.a_last = c->a_last;
+        io.norm_out = true;
+        if (j + 1 < K) io.keep = RowCopy{c->a_rows, dr.slot, seq_lens, 1, c->emax};
+        draft_layer(c, batch, 1, dr.tok, c->dx, dr_meta(c), 0, &io);
+        draft_lm(c, batch, c->dx, 1, T, 1, j, true);
         chain_draw(j, K, c->logits, Vd, Vd, V, T, c->tk_lse64, c->tk_ids, uniforms, c->cfg.draft_greedy, q,
                    c->chain_tok, batch, c->tk_wsum, c->d2t, st);
       }

@@ -61,10 +61,15 @@ template <typename T, int NV>
 __global__ __launch_bounds__(1024) void k_add_rmsnorm(float* __restrict__ x, const float* __restrict__ part, int S,
                                                       size_t sstride, int ldp, const T* __restrict__ w,
                                                       T* __restrict__ out, int out_ld, int d, float eps,
-                                                      T* __restrict__ tap, int tap_ld, bool packed) {
+                                                      T* __restrict__ tap, int tap_ld, bool packed, RowCopy rc) {
   __shared__ float red[16];
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, d4 = d >> 2;
   float4* xr = (float4*)(x + (size_t)r * d);
+  float4* cr = nullptr;
+  if (rc.dst) {
+    const int b = r / rc.k;
+    cr = (float4*)(rc.dst + ((size_t)b * rc.emax + rc.slot[r] - rc.seq_lens[b]) * d);
+  }
   float4 v[NV];
   float ss = 0.f;
 #pragma unroll
@@ -77,6 +82,7 @@ __global__ __launch_bounds__(1024) void k_add_rmsnorm(float* __restrict__ x, con
         v[i].x += a.x; v[i].y += a.y; v[i].z += a.z; v[i].w += a.w;
         xr[c] = v[i];
       }
+      if (cr) cr[c] = v[i];
       ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
       if (tap) st4<T>(tap, (size_t)r * tap_ld + 4 * c, v[i]);
     }
@@ -100,10 +106,15 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_add_rmsnorm_any(float* __restrict__ x, const float* __restrict__ part,
                                                          int S, size_t sstride, int ldp, const T* __restrict__ w,
                                                          T* __restrict__ out, int out_ld, int d, float eps,
-                                                         T* __restrict__ tap, int tap_ld, bool packed) {
+                                                         T* __restrict__ tap, int tap_ld, bool packed, RowCopy rc) {
   __shared__ float red[16];
   const int r = blockIdx.x, tid = threadIdx.x;
   float* xr = x + (size_t)r * d;
+  float* cr = nullptr;
+  if (rc.dst) {
+    const int b = r / rc.k;
+    cr = rc.dst + ((size_t)b * rc.emax + rc.slot[r] - rc.seq_lens[b]) * d;
+  }
   float ss = 0.f;
   for (int i = tid; i < d; i += 256) {
     float v = xr[i];
@@ -111,6 +122,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_any(float* __restrict__ x, 
       v += sum_splits(part + (size_t)r * ldp + i, S, sstride);
       xr[i] = v;
     }
+    if (cr) cr[i] = v;
     ss += v * v;
     if (tap) st<T>(tap, (size_t)r * tap_ld + i, v);
   }
@@ -122,38 +134,53 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm_any(float* __restrict__ x, 
 
 template <typename T>
 static void launch_add_rmsnorm(float* x, const float* part, int S, size_t sstride, int ldp, const T* w, T* out,
-                               int out_ld, int R, int d, float eps, T* tap, int tap_ld, hipStream_t st, bool pk) {
+                               int out_ld, int R, int d, float eps, T* tap, int tap_ld, hipStream_t st, bool pk,
+                               const RowCopy& rc) {
   const int d4 = d / 4;
   // the float4 kernel moves 4 elements at a time: every row start must be aligned to 4 of them
   const size_t al = 4 * sizeof(T);
   const bool aligned = (size_t)out % al == 0 && (size_t)w % al == 0 && out_ld % 4 == 0 &&
-                       (!tap || ((size_t)tap % al == 0 && tap_ld % 4 == 0));
+                       (!tap || ((size_t)tap % al == 0 && tap_ld % 4 == 0)) && (size_t)rc.dst % 16 == 0;
   if (d % 4 == 0 && d4 <= 2048 && aligned) {
     const int nt = std::min(1024, (d4 + 63) / 64 * 64);
     if (d4 <= nt)
-      k_add_rmsnorm<T, 1><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk);
+      k_add_rmsnorm<T, 1><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk, rc);
     else
-      k_add_rmsnorm<T, 2><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk);
+      k_add_rmsnorm<T, 2><<<R, nt, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk, rc);
   } else {
-    k_add_rmsnorm_any<T><<<R, 256, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk);
+    k_add_rmsnorm_any<T><<<R, 256, 0, st>>>(x, part, S, sstride, ldp, w, out, out_ld, d, eps, tap, tap_ld, pk, rc);
   }
 }
 
 void add_rmsnorm(bool bf16, float* x, const float* part, int S, size_t sstride, int ldp, const void* w, void* out,
-                 int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st, bool packed) {
+                 int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st, bool packed,
+                 const RowCopy& rc) {
   if (R <= 0) return;
   if (bf16)
     launch_add_rmsnorm<bf16_t>(x, part, S, sstride, ldp, (const bf16_t*)w, (bf16_t*)out, out_ld, R, d, eps,
-                               (bf16_t*)tap, tap_ld, st, packed);
+                               (bf16_t*)tap, tap_ld, st, packed, rc);
   else
     launch_add_rmsnorm<float>(x, part, S, sstride, ldp, (const float*)w, (float*)out, out_ld, R, d, eps,
-                              (float*)tap, tap_ld, st, packed);
+                              (float*)tap, tap_ld, st, packed, rc);
 }
 
 void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, int R, int d, float eps, void* tap,
              int tap_ld, hipStream_t st, bool packed) {
   add_rmsnorm(bf16, (float*)x, nullptr, 0, 0, 0, w, out, out_ld, R, d, eps, tap, tap_ld, st, packed);
 }
+
+// Where a draft-input row's features come from: x[r] itself, or (src != null) row src[r] of a_rows, row
+// -1 - src[r] of a_last when src[r] < 0.
+struct RowSrc {
+  const int* src = nullptr;
+  const float* a_rows = nullptr;
+  const float* a_last = nullptr;
+  E3_DEV const float* row(int r, const float* xr, int d) const {
+    if (!src) return xr;
+    const int s = src[r];
+    return s < 0 ? a_last + (size_t)(-1 - s) * d : a_rows + (size_t)s * d;
+  }
+};
 
 // ---------------------------------------------------------------- draft input
 // One block per row, one float4 column group per thread (NV groups when the
@@ -168,7 +195,7 @@ __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embe
                                                       float* __restrict__ x, const float* __restrict__ part, int S,
                                                       size_t sstride, const T* __restrict__ w_in,
                                                       const T* __restrict__ w_hid, T* __restrict__ out, int d,
-                                                      int V, float eps, int* status, bool packed) {
+                                                      int V, float eps, int* status, bool packed, RowSrc gs) {
   __shared__ float red[16];
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x, d4 = d >> 2;
   int t = tokens[r];
@@ -176,6 +203,7 @@ __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embe
   if (!ok && tid == 0 && t != -1) raise_flag(status, E3_DEV_BAD_TOKEN);
   if (!ok) t = 0;
   float* xr = x + (size_t)r * d;
+  const float* hr = gs.row(r, xr, d);  // the feature row: x[r] itself, or the gathered source row
   const T* er = embed + (size_t)t * d;
   float4 e[NV], h[NV];
   float se = 0.f, sx = 0.f;
@@ -188,7 +216,8 @@ __global__ __launch_bounds__(1024) void k_draft_input(const T* __restrict__ embe
         h[i] = sum_splits4((const float4*)(part + (size_t)r * d) + c, S, sstride >> 2);
         *(float4*)(xr + 4 * c) = h[i];
       } else {
-        h[i] = *(const float4*)(xr + 4 * c);
+        h[i] = *(const float4*)(hr + 4 * c);
+        if (gs.src) *(float4*)(xr + 4 * c) = h[i];
       }
       se += e[i].x * e[i].x + e[i].y * e[i].y + e[i].z * e[i].z + e[i].w * e[i].w;
       sx += h[i].x * h[i].x + h[i].y * h[i].y + h[i].z * h[i].z + h[i].w * h[i].w;
@@ -217,7 +246,7 @@ __global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ e
                                                          float* __restrict__ x, const float* __restrict__ part, int S,
                                                          size_t sstride, const T* __restrict__ w_in,
                                                          const T* __restrict__ w_hid, T* __restrict__ out, int d,
-                                                         int V, float eps, int* status, bool packed) {
+                                                         int V, float eps, int* status, bool packed, RowSrc gs) {
   __shared__ float red[16];
   const int r = blockIdx.x;
   int t = tokens[r];
@@ -225,10 +254,12 @@ __global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ e
   if (!ok && threadIdx.x == 0 && t != -1) raise_flag(status, E3_DEV_BAD_TOKEN);
   if (!ok) t = 0;
   float* xr = x + (size_t)r * d;
+  const float* hr = gs.row(r, xr, d);
   float se = 0.f, sx = 0.f;
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
     const float e = ok ? ld<T>(embed, (size_t)t * d + i) : 0.f;
     if (part) xr[i] = sum_splits(part + (size_t)r * d + i, S, sstride);
+    else if (gs.src) xr[i] = hr[i];
     se += e * e;
     sx += xr[i] * xr[i];
   }
@@ -246,7 +277,7 @@ __global__ __launch_bounds__(256) void k_draft_input_any(const T* __restrict__ e
 template <typename T>
 static void launch_draft_input(const T* embed, const int* tokens, float* x, const float* part, int S, size_t sstride,
                                const T* w_in, const T* w_hid, T* out, int R, int d, int V, float eps, int* status,
-                               hipStream_t st, bool pk) {
+                               hipStream_t st, bool pk, const RowSrc& gs) {
   const int d4 = d / 4;
   // the float4 kernel moves 4 elements at a time: every row start must be aligned to 4 of them
   const size_t al = 4 * sizeof(T);
@@ -256,26 +287,31 @@ static void launch_draft_input(const T* embed, const int* tokens, float* x, cons
     const int nt = std::min(1024, (d4 + 63) / 64 * 64);
     if (d4 <= nt)
       k_draft_input<T, 1><<<R, nt, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status,
-                                            pk);
+                                            pk, gs);
     else
       k_draft_input<T, 2><<<R, nt, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status,
-                                            pk);
+                                            pk, gs);
   } else {
     k_draft_input_any<T><<<R, 256, 0, st>>>(embed, tokens, x, part, S, sstride, w_in, w_hid, out, d, V, eps, status,
-                                            pk);
+                                            pk, gs);
   }
 }
 
 void draft_input(bool bf16, const void* embed, const int* tokens, float* x, const float* part, int S,
                  size_t sstride, const void* w_in, const void* w_hid, void* out, int R, int d, int V, float eps,
-                 int* status, hipStream_t st, bool packed) {
+                 int* status, hipStream_t st, bool packed, const int* src, const float* a_rows,
+                 const float* a_last) {
   if (R <= 0) return;
+  RowSrc gs;
+  gs.src = src;
+  gs.a_rows = a_rows;
+  gs.a_last = a_last;
   if (bf16)
     launch_draft_input<bf16_t>((const bf16_t*)embed, tokens, x, part, S, sstride, (const bf16_t*)w_in,
-                               (const bf16_t*)w_hid, (bf16_t*)out, R, d, V, eps, status, st, packed);
+                               (const bf16_t*)w_hid, (bf16_t*)out, R, d, V, eps, status, st, packed, gs);
   else
     launch_draft_input<float>((const float*)embed, tokens, x, part, S, sstride, (const float*)w_in,
-                              (const float*)w_hid, (float*)out, R, d, V, eps, status, st, packed);
+                              (const float*)w_hid, (float*)out, R, d, V, eps, status, st, packed, gs);
 }
 
 // ----------------------------------------------------------- rope + KV write

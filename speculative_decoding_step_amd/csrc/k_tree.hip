@@ -97,45 +97,6 @@ __global__ __launch_bounds__(256) void k_tree_frontier(TreeState ts, int d, cons
   }
 }
 
-// Row copies of d_model floats: each thread moves up to four float4 (loads
-// issued together); d_model % 4 == 0 (checked on the host), else element loop.
-E3_DEV void copy_row(float* __restrict__ dst, const float* __restrict__ src, int d) {
-  if ((d & 3) == 0) {
-    const int d4 = d >> 2;
-    for (int c0 = threadIdx.x; c0 < d4; c0 += 4 * blockDim.x) {
-      float4 v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = c0 + j * blockDim.x;
-        if (c < d4) v[j] = ((const float4*)src)[c];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = c0 + j * blockDim.x;
-        if (c < d4) ((float4*)dst)[c] = v[j];
-      }
-    }
-  } else {
-    for (int i = threadIdx.x; i < d; i += blockDim.x) dst[i] = src[i];
-  }
-}
-
-// x of the expansion rows: a of the parent's expansion row, or of the catch-up row.
-__global__ void k_tree_gather_x(float* __restrict__ x, const int* __restrict__ src, const float* __restrict__ a_rows,
-                                const float* __restrict__ a_last, int d_model) {
-  const int r = blockIdx.x, s = src[r];
-  const float* from = s < 0 ? a_last + (size_t)(-1 - s) * d_model : a_rows + (size_t)s * d_model;
-  copy_row(x + (size_t)r * d_model, from, d_model);
-}
-
-// Store the expansion rows' outputs a (needed as x by their children).
-__global__ void k_tree_store_a(float* __restrict__ a_rows, const float* __restrict__ a, const int* __restrict__ slot,
-                               const int* __restrict__ seq_lens, int k, int emax, int d_model) {
-  const int r = blockIdx.x, b = r / k;
-  const int e = slot[r] - seq_lens[b];
-  copy_row(a_rows + ((size_t)b * emax + e) * d_model, a + (size_t)r * d_model, d_model);
-}
-
 // Final selection, numbering and masks, one block (512 threads) per sequence.
 // The candidates are sorted in LDS (bitonic, by score descending then creation
 // index ascending, as one 64-bit key); the first n_nodes are kept and numbered
@@ -390,14 +351,6 @@ void tree_children(const TreeState& ts, int depth_new, const int* ids, const flo
 void tree_frontier(const TreeState& ts, int d, const int* seq_lens, const DraftRows& dr, int S_cap, int* status,
                    hipStream_t st) {
   k_tree_frontier<<<ts.batch, 256, 0, st>>>(ts, d, seq_lens, dr, S_cap, status);
-}
-void tree_gather_x(float* x, const int* src, const float* a_rows, const float* a_last, int n, int d_model,
-                   hipStream_t st) {
-  if (n > 0) k_tree_gather_x<<<n, 256, 0, st>>>(x, src, a_rows, a_last, d_model);
-}
-void tree_store_a(float* a_rows, const float* a, const int* slot, const int* seq_lens, int n, int k, int emax,
-                  int d_model, hipStream_t st) {
-  if (n > 0) k_tree_store_a<<<n, 256, 0, st>>>(a_rows, a, slot, seq_lens, k, emax, d_model);
 }
 void tree_finalize(const TreeState& ts, int n_cand, int n_nodes, const int* roots, const int* seq_lens,
                    const TreeOut& out, int* status, hipStream_t st) {

@@ -102,17 +102,31 @@ void embed_rows(bool bf16, const void* table, const int* tokens, float* x, int R
 // add_rmsnorm first adds the S split partials part[s][r][0..d) (row stride ldp) into x.
 // packed: out is written in column slabs of 32 of an [R, d] matrix (a large-M GEMM input) instead of
 // row-major with stride out_ld; tap is always row-major.
+// rc: when rc.dst is set, each row's updated x[r] is also copied (fp32) to row
+// (r / rc.k) * rc.emax + rc.slot[r] - rc.seq_lens[r / rc.k] of rc.dst (the draft
+// tree's expansion rows, kept as their children's inputs).
+struct RowCopy {
+  float* dst = nullptr;
+  const int* slot = nullptr;
+  const int* seq_lens = nullptr;
+  int k = 1;
+  int emax = 0;
+};
 void add_rmsnorm(bool bf16, float* x, const float* part, int S, size_t sstride, int ldp, const void* w, void* out,
-                 int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st, bool packed = false);
+                 int out_ld, int R, int d, float eps, void* tap, int tap_ld, hipStream_t st, bool packed = false,
+                 const RowCopy& rc = RowCopy{});
 void rmsnorm(bool bf16, const float* x, const void* w, void* out, int out_ld, int R, int d, float eps,
              void* tap, int tap_ld, hipStream_t st, bool packed = false);
 // Draft input: out[r] = [T(rms(embed[tok[r]]) * w_in) ; T(rms(x[r]) * w_hid)], [R, 2d].  With part != null
 // x[r] is first set to the sum of the S split partials part[s][r][0..d) (split stride sstride): the fusion
 // FC's reduction in the same pass.
 // packed: out ([R, 2d]) in column slabs of 32.
+// With src != null (and no partials) x[r] is first gathered from row src[r] of a_rows, or from row -1 - src[r] of
+// a_last when src[r] < 0 (the tree's expansion rows take their parent's output).
 void draft_input(bool bf16, const void* embed, const int* tokens, float* x, const float* part, int S,
                  size_t sstride, const void* w_in, const void* w_hid, void* out, int R, int d, int V, float eps,
-                 int* status, hipStream_t st, bool packed = false);
+                 int* status, hipStream_t st, bool packed = false, const int* src = nullptr,
+                 const float* a_rows = nullptr, const float* a_last = nullptr);
 
 // KV cache addressing of one layer's K (or V) array: element (unit u, KV head
 // g, row r, dim i) sits at u * unit_stride + g * head_stride + r * hd + i.

@@ -47,10 +47,6 @@ void tree_children(const TreeState& ts, int depth_new, const int* ids, const flo
                    hipStream_t st);
 void tree_frontier(const TreeState& ts, int d, const int* seq_lens, const DraftRows& dr, int S_cap, int* status,
                    hipStream_t st);
-void tree_gather_x(float* x, const int* src, const float* a_rows, const float* a_last, int n, int d_model,
-                   hipStream_t st);
-void tree_store_a(float* a_rows, const float* a, const int* slot, const int* seq_lens, int n, int k, int emax,
-                  int d_model, hipStream_t st);
 void tree_finalize(const TreeState& ts, int n_cand, int n_nodes, const int* roots, const int* seq_lens,
                    const TreeOut& out, int* status, hipStream_t st);
 // Chain draw j for every sequence: logits rows of Vd entries (the draft vocabulary), q rows of V (the target's;
