@@ -397,7 +397,7 @@ int run_gemm(eagle3_ctx* c, const void* X, int M, int K, const GemmSegs& sg, flo
 // value) of each row in tk_ids / tk_vals, and the log-sum-exp of logits / temperature in tk_lse / tk_lse64
 // when lse.  Returns false, launching nothing, for shapes the fused kernel does not cover.
 bool run_lm_topk(eagle3_ctx* c, const void* X, int n, const void* W, int V, float* logits, int k, float temperature,
-                 bool lse) {
+                 bool lse, const TreeKids* kids = nullptr, bool* kids_done = nullptr) {
   const int d = c->sh.d_model;
   if (!c->bf16 || n <= 0 || n > c->R || k > c->tf_k) return false;
   SliceTopk tk = c->tf;
@@ -415,7 +415,9 @@ bool run_lm_topk(eagle3_ctx* c, const void* X, int n, const void* W, int V, floa
   const bool ok = gemm_lm_topk(X, n, d, W, V, logits, V, tk, c->st, rec.a, rec.b);
   prof_end(c, &rec, false);
   if (!ok) return false;
-  topk_merge_slices(n, tk, c->tk_ids, c->tk_vals, lse ? c->tk_lse : nullptr, lse ? c->tk_lse64 : nullptr, c->st);
+  const bool kd = topk_merge_slices(n, tk, c->tk_ids, c->tk_vals, lse ? c->tk_lse : nullptr,
+                                    lse ? c->tk_lse64 : nullptr, c->st, kids);
+  if (kids_done) *kids_done = kd;
   return true;
 }
 
@@ -586,18 +588,25 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
     resid_add(x, c->part, S, (size_t)R * d, R, d, d, st);
 }
 
-// Draft logits of n rows of a (fp32 [n, d]) -> c->logits; top-K + lse.  With a
-// draft logits table set, the n rows (per rows of each of n / per sequences)
-// are also copied to table rows row0 .. row0 + per - 1.  normed: the head's
-// input (the rows' final norm, in c->gbuf) is already there.
-void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, int per, int row0, bool normed = false) {
+// Draft logits of n rows of a (fp32 [n, d]) -> c->logits; top-K + lse, ids
+// through d2t.  With a draft logits table set, the n rows (per rows of each of
+// n / per sequences) are also copied to table rows row0 .. row0 + per - 1.
+// normed: the head's input (the rows' final norm, in c->gbuf) is already
+// there.  kids_depth > 0: the rows are a tree level whose children have depth
+// kids_depth; returns true when the head's merge has recorded them (else the
+// caller runs tree_children).
+bool draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, int per, int row0, bool normed = false,
+              int kids_depth = 0) {
   const eagle3_shape& s = c->sh;
   if (!normed)
     rmsnorm(c->bf16, a, c->hw.final_norm, c->gbuf, s.d_model, n, s.d_model, s.rms_eps, nullptr, 0, c->st,
             packed_inputs(c, n));
   // the logits themselves are read only by the chain sampler and the draft-logits table
   const bool keep = c->dl_out || c->cfg.mode == EAGLE3_SAMPLE_CHAIN;
-  const bool fused = run_lm_topk(c, c->gbuf, n, c->dhead, c->Vd, keep ? c->logits : nullptr, K, temperature, true);
+  TreeKids kids{c->ts, kids_depth, c->d2t, c->Vd};
+  bool kids_done = false;
+  const bool fused = run_lm_topk(c, c->gbuf, n, c->dhead, c->Vd, keep ? c->logits : nullptr, K, temperature, true,
+                                 kids_depth > 0 ? &kids : nullptr, &kids_done);
   if (!fused) run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->dhead, c->Vd), c->logits);
   if (c->dl_out && n > 0)
     k_copy_logit_rows<<<dim3(nb(c->Vd, 1024), n), 256, 0, c->st>>>(c->logits, per, c->Vd, c->dl_out,
@@ -605,7 +614,8 @@ void draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, in
   if (!fused)
     topk_lse(c->logits, n, c->Vd, c->Vd, K, temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids,
              c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
-  map_draft_ids(c->tk_ids, n * K, c->d2t, c->Vd, c->st);
+  if (!fused || kids_depth <= 0) map_draft_ids(c->tk_ids, n * K, c->d2t, c->Vd, c->st);  // else the merge mapped them
+  return kids_done;
 }
 
 RowMeta dr_meta(eagle3_ctx* c) {
@@ -623,7 +633,7 @@ RowMeta dr_meta(eagle3_ctx* c) {
 // (top-k in c->tk_*).  table != null: rows come from the table instead of
 // the draft model.
 eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const float* table, const float* uniforms,
-                         const TreeOut& out, float* q) {
+                         const TreeOut& out, float* q, bool root_kids_done = false) {
   const eagle3_shape& s = c->sh;
   const int D = c->cfg.depth, k = c->cfg.topk, V = s.vocab, Vd = c->Vd, d = s.d_model;
   hipStream_t st = c->st;
@@ -633,10 +643,11 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
   dr.batch = batch;
   const size_t tstride = (size_t)(1 + c->emax) * Vd;  // table row stride between sequences
   if (c->cfg.mode != EAGLE3_SAMPLE_CHAIN) {  // trees (greedy or sampled acceptance alike)
-    tree_children(ts, 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
+    if (!root_kids_done) tree_children(ts, 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
     for (int dd = 1; dd < D; ++dd) {
       const int n = batch * k;
       tree_frontier(ts, dd, seq_lens, dr, c->S_cap, c->status, st);
+      bool kids_done = false;
       if (table) {
         // expansion rows (dd-1)k .. dd k - 1 of each sequence
         for (int b = 0; b < batch; ++b)
@@ -656,9 +667,9 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
         io.norm_out = true;
         if (dd + 1 < D) io.keep = RowCopy{c->a_rows, dr.slot, seq_lens, k, c->emax};
         draft_layer(c, n, k, dr.tok, c->dx, dr_meta(c), 0, &io);
-        draft_lm(c, n, c->dx, k, 1.f, k, 1 + (dd - 1) * k, true);
+        kids_done = draft_lm(c, n, c->dx, k, 1.f, k, 1 + (dd - 1) * k, true, dd + 1);
       }
-      tree_children(ts, dd + 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
+      if (!kids_done) tree_children(ts, dd + 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
     }
     tree_finalize(ts, c->n_cand, c->cfg.n_nodes, c->roots, seq_lens, out, c->status, st);
   } else {
@@ -1006,9 +1017,10 @@ eagle3_status eagle3_draft_tree(eagle3_ctx* c, int32_t batch, const int32_t* seq
   const int S = run_gemm(c, aux_new, Rc, 3 * d, make_segs(c->hw.fc, d), nullptr, true);
   draft_layer(c, Rc, W, c->rtok, c->dx, c->rm, S);
   gather_rows_f32(c->a_last, c->dx, c->gidx, batch, d, st);
-  draft_lm(c, batch, c->a_last, chain ? 1 : c->cfg.topk, chain ? c->cfg.temperature : 1.f, 1, 0);
+  const bool kids = draft_lm(c, batch, c->a_last, chain ? 1 : c->cfg.topk, chain ? c->cfg.temperature : 1.f, 1, 0,
+                             false, chain ? 0 : 1);
   TreeOut out{tokens, parents, depth, pos, mask, score};
-  build_tree(c, batch, seq_lens, nullptr, uniforms, out, q);
+  build_tree(c, batch, seq_lens, nullptr, uniforms, out, q, kids);
   return last_error();
 }
 

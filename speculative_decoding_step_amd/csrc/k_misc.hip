@@ -3,6 +3,7 @@
 // with the KV-cache write, and the vocabulary top-k / log-sum-exp.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tree.hpp"
 
 namespace e3 {
 
@@ -539,8 +540,9 @@ void topk_lse(const float* logits, int R, int V, int ld, int K, float temperatur
 // log-sum-exp combines the slices' maxima and sums as the separate merge does.
 __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __restrict__ out_ids,
                                                            float* __restrict__ out_vals, float* __restrict__ lse32,
-                                                           double* __restrict__ lse64) {
+                                                           double* __restrict__ lse64, TreeKids kids) {
   __shared__ VI cand[4][TK_KMAX];
+  __shared__ VI best[TK_KMAX];
   __shared__ int sel[TK_KMAX];
   __shared__ float fred[4];
   __shared__ double dred[4];
@@ -611,8 +613,10 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
       const VI wb = wave_best(b);
       if (bj >= 0 && b.i == wb.i && b.v == wb.v) t4 |= 1u << bj;
       if (lane == 0) {
-        out_ids[(size_t)r * K + k] = wb.i;
+        const int id = kids.d2t ? (wb.i >= 0 && wb.i < kids.Vd ? kids.d2t[wb.i] : -1) : wb.i;
+        out_ids[(size_t)r * K + k] = id;
         out_vals[(size_t)r * K + k] = wb.v;
+        best[k] = VI{wb.v, id};
       }
     }
   }
@@ -636,15 +640,40 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
     const double l = M + log(dred[0] + dred[1] + dred[2] + dred[3]);
     if (lse64) lse64[r] = l;
     if (lse32) lse32[r] = (float)l;
+    if (kids.depth_new > 0) {  // the row's children: candidates of depth depth_new, log-prob value - (float)lse
+      const TreeState& ts = kids.ts;
+      const int k = ts.topk, dn = kids.depth_new;
+      const int b = dn == 1 ? r : r / k, rank = dn == 1 ? 0 : r % k;
+      const int c0 = (dn == 1 ? 0 : k + (dn - 2) * k * k) + rank * k;
+      int par = -1;
+      float ps = 0.f;
+      if (dn > 1) {
+        par = ts.front[b * k + rank];
+        ps = ts.score[(size_t)b * ts.cmax + par];
+      }
+      const float l32 = (float)l;
+      for (int ch = 0; ch < k; ++ch) {
+        const size_t o = (size_t)b * ts.cmax + c0 + ch;
+        ts.tok[o] = best[ch].i;
+        ts.par[o] = par;
+        ts.dep[o] = dn;
+        ts.score[o] = ps + (best[ch].v - l32);
+        ts.erow[o] = -1;
+      }
+    }
   }
 }
 
-void topk_merge_slices(int R, const SliceTopk& tk, int* out_ids, float* out_vals, float* lse32, double* lse64,
-                       hipStream_t st) {
-  if (R <= 0) return;
+bool topk_merge_slices(int R, const SliceTopk& tk, int* out_ids, float* out_vals, float* lse32, double* lse64,
+                       hipStream_t st, const TreeKids* kids) {
+  if (R <= 0) return false;
   SliceTopk t = tk;
   if (!lse32 && !lse64) t.pmax = nullptr;
-  k_topk_merge_slices<<<R, 256, 0, st>>>(t, out_ids, out_vals, lse32, lse64);
+  TreeKids kd{};
+  if (kids) kd = *kids;
+  if (kd.depth_new > 0 && (!t.pmax || t.k != kd.ts.topk)) kd.depth_new = 0;  // children need the row's k and lse
+  k_topk_merge_slices<<<R, 256, 0, st>>>(t, out_ids, out_vals, lse32, lse64, kd);
+  return kd.depth_new > 0;
 }
 
 // -------------------------------------------------------------- row gather

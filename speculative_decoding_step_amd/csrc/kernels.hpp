@@ -67,8 +67,13 @@ bool gemm_lm_topk(const void* X, int M, int K, const void* W, int V, float* logi
 // Merge the slices of gemm_lm_topk: the k best (value, id) of every row in
 // (value desc, id asc) order, and its log-sum-exp of z / temp when pmax was
 // written (lse32 / lse64 may be null).
-void topk_merge_slices(int R, const SliceTopk& tk, int* out_ids, float* out_vals, float* lse32, double* lse64,
-                       hipStream_t st);
+// With kids (a draft tree level, tree.hpp) the merge also maps the ids through
+// d2t (when set) and, when it computes the log-sum-exp and tk.k is the tree's
+// top-k, records each row's k children as tree candidates, as tree_children
+// does; returns whether it recorded them.
+struct TreeKids;
+bool topk_merge_slices(int R, const SliceTopk& tk, int* out_ids, float* out_vals, float* lse32, double* lse64,
+                       hipStream_t st, const TreeKids* kids = nullptr);
 // The large-M form of gemm_lm_topk (M > 64, X in column slabs of 32).
 void gemm_big_lm_topk(const void* X, int M, int K, const void* W, int V, float* logits, int ldo, const SliceTopk& tk,
                       hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);

@@ -34,6 +34,16 @@ struct DraftRows {
   uint64_t* mask;
 };
 
+// The children of one draft tree level, recorded by the slice merge of that level's LM head: rows are the
+// level's expansion rows (depth_new == 1: one root row per sequence), their k best ids (through d2t when set)
+// and fp32 log-probabilities value - lse become candidates of depth depth_new.
+struct TreeKids {
+  TreeState ts;
+  int depth_new;
+  const int* d2t;
+  int Vd;
+};
+
 struct TreeOut {
   int* tokens;
   int* parents;
