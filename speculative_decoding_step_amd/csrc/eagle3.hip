@@ -71,6 +71,7 @@ struct eagle3_ctx {
   void *hbuf, *abuf, *qbuf, *gbuf;
   float *o_part, *ml_part;
   int att_splits;
+  int* att_plan;  // work order of the attention launches over several sequences
   float* logits;
   float *tk_pv, *tk_pmax, *tk_vals, *tk_lse;
   int *tk_pi, *tk_ids;
@@ -119,6 +120,7 @@ size_t carve(eagle3_ctx* c, char* base) {
   c->att_splits = std::max(1, (c->S_cap + ATT_CHUNK - 1) / ATT_CHUNK);
   c->o_part = cv.take<float>((size_t)c->att_splits * R * qdim);
   c->ml_part = cv.take<float>((size_t)c->att_splits * R * s.n_heads * 2);
+  c->att_plan = cv.take<int>(ATT_PLAN_CAP);
   c->logits = cv.take<float>((size_t)R * V);
   const int ns = topk_slices(V);
   c->tk_pv = cv.take<float>((size_t)R * ns * KMAX);
@@ -442,12 +444,23 @@ void run_gateup(eagle3_ctx* c, const void* X, int M, int K, const void* w_gate, 
   silu_mul(c->bf16, c->abuf, c->part, S, (size_t)M * 2 * F, M, F, 2 * F, c->st);
 }
 
-void run_attention(eagle3_ctx* c, const void* kc, const void* vc, const RowMeta& rm, int R, int rps) {
+// Orders the work of the attention launches over rm that follow (every layer of one pass); false when they
+// take no order.
+bool plan_attention(eagle3_ctx* c, const RowMeta& rm, int R, int rps) {
+  const eagle3_shape& s = c->sh;
+  return attention_plan(c->bf16, c->pg, rm, R, rps, s.n_heads, s.n_kv_heads, s.head_dim, c->S_cap,
+                        c->att_splits, c->att_plan, c->ml_part, c->st);
+}
+
+// planned: plan_attention returned true for these rows since their metadata last changed.
+void run_attention(eagle3_ctx* c, const void* kc, const void* vc, const RowMeta& rm, int R, int rps,
+                   bool planned) {
   const eagle3_shape& s = c->sh;
   ProfRec rec{};
   prof_begin(c, EAGLE3_PROF_ATTN, 0.0, 0.0, &rec);
   attention(c->bf16, c->qbuf, kc, vc, c->kv_us, c->kv_hs, c->pg, rm, R, rps, s.n_heads, s.n_kv_heads, s.head_dim,
-            c->S_cap, c->o_part, c->ml_part, c->att_splits, c->abuf, c->st, packed_inputs(c, R));
+            c->S_cap, c->o_part, c->ml_part, c->att_splits, c->abuf, c->st, packed_inputs(c, R),
+            planned ? c->att_plan : nullptr);
   prof_end(c, &rec);
 }
 
@@ -494,6 +507,7 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
       }
   };
   enter(0, 0, c->layers[0].attn_norm, c->hbuf);
+  const bool planned = plan_attention(c, c->rm, R, rps);
   bool final_normed = false;
   for (int l = 0; l < s.n_layers; ++l) {
     const eagle3_layer_weights& L = c->layers[l];
@@ -503,7 +517,7 @@ void target_forward(eagle3_ctx* c, int R, int rps, void* aux, int lm, int nlast,
     char* vc = kv_layer(c, c->kv_t, l, 1);
     rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, c->rm, c->inv_freq, c->qbuf, kc, vc,
             c->kv_us, c->kv_hs, c->pg, s.n_heads, s.n_kv_heads, s.head_dim, c->status, st);
-    run_attention(c, kc, vc, c->rm, R, rps);
+    run_attention(c, kc, vc, c->rm, R, rps, planned);
     S = run_gemm(c, c->abuf, R, qdim, make_segs(L.wo, d));
     add_rmsnorm(bf, c->xres, c->part, S, (size_t)R * d, d, L.ffn_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st,
                 pk);
@@ -576,7 +590,7 @@ void draft_layer(eagle3_ctx* c, int R, int rps, const int* tok, float* x, const 
   char* vc = kv_layer(c, c->kv_d, 0, 1);
   rope_kv(bf, c->part, S, (size_t)R * gemm_ntot(qkv), R, rm, c->inv_freq, c->qbuf, kc, vc,
           c->kv_us, c->kv_hs, c->pg, s.n_heads, s.n_kv_heads, s.head_dim, c->status, st);
-  run_attention(c, kc, vc, rm, R, rps);
+  run_attention(c, kc, vc, rm, R, rps, plan_attention(c, rm, R, rps));
   S = run_gemm(c, c->abuf, R, qdim, make_segs(H.wo, d));
   add_rmsnorm(bf, x, c->part, S, (size_t)R * d, d, H.post_norm, c->hbuf, d, R, d, s.rms_eps, nullptr, 0, st, pk);
   run_gateup(c, c->hbuf, R, d, H.w_gate, H.w_up, s.ffn);

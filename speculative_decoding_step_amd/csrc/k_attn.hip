@@ -275,7 +275,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
                                                        float scale, int chunk, float* __restrict__ o_part,
                                                        float* __restrict__ ml_part, const bf16_t* __restrict__ dk,
                                                        const bf16_t* __restrict__ dv, int nstep,
-                                                       bf16_t* __restrict__ tout) {
+                                                       bf16_t* __restrict__ tout, const int* __restrict__ plan,
+                                                       bf16_t* __restrict__ dout, int dpacked) {
   constexpr int TILE = AKT * HD;               // bf16 elements of one K (or V) tile
   constexpr int NCP = 2 * TILE / 512;          // 1 KiB copies per tile: K fragments, then V block groups
   constexpr int PW = (NCP + NW - 1) / NW;      // copies per wave and tile
@@ -289,8 +290,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   __shared__ __attribute__((aligned(1024))) bf16_t stg[NST][STG];
   __shared__ int red_end[8], red_seq[8];
   const int per = (nwork + 7) >> 3;
-  const int lam = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lam >= nwork) return;
+  const int lam = plan ? plan[blockIdx.x] : (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lam < 0 || lam >= nwork) return;
   constexpr int QB = 16 * NW;
   const int qb = qblocks - 1 - lam % qblocks;  // later query rows first: under a causal mask they see the most keys
   int t = lam / qblocks;
@@ -332,7 +333,13 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
   cs = __builtin_amdgcn_readfirstlane(cs);
   const int c0 = sp * chunk, c1 = min(c0 + chunk, kend);
   if (cs < 0 || c0 >= c1) {  // no row of the block sees a key of this chunk: an empty partial for each row
-    if (!TTT && v < nq && lg == 0) {
+    if (!TTT && dout && v < nq) {  // one chunk per row: the row's output is zero
+#pragma unroll
+      for (int b = 0; b < HD / 16; ++b) {
+        const int col = h * HD + 16 * b + 4 * lg;
+        *(uint2*)(dout + (dpacked ? slab32_index(row, col, R) : (size_t)row * Hq * HD + col)) = make_uint2(0u, 0u);
+      }
+    } else if (!TTT && v < nq && lg == 0) {
       const size_t oi = ((size_t)sp * R + row) * Hq + h;
       ml_part[2 * oi] = -INFINITY;
       ml_part[2 * oi + 1] = 0.f;
@@ -349,18 +356,23 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
 
   // Tile kt's keys start at kb/vb + tile_off(kt): contiguous, the sequence's unit advanced by kt rows; paged, the
   // block the table gives for kt (a block holds whole 64-key tiles).  The chunk's block ids are loaded once, lane i
-  // holding tile i's (a chunk has at most 64 tiles), and each tile reads its id with readlane: no memory wait in
-  // the copy ring.
+  // holding tile i's and tile 64 + i's (a chunk has at most 128 tiles), and each tile reads its id with readlane:
+  // no memory wait in the copy ring.
   const bool paged = pg.bt != nullptr;
   const size_t seq0 = paged ? 0 : (size_t)cs * unit_stride;
   const bf16_t* kb = kc + seq0 + (size_t)g * head_stride;
   const bf16_t* vb = vc + seq0 + (size_t)g * head_stride;
-  int vblk = 0;
-  if (paged && lane < ((c1 - c0 + AKT - 1) >> 6))
-    vblk = min(max(pg.bt[(size_t)cs * pg.stride + ((c0 + AKT * lane) >> pg.lbs)], 0), pg.nblk - 1);
+  int vblk = 0, vblk_hi = 0;
+  if (paged) {
+    const int nt = (c1 - c0 + AKT - 1) >> 6;
+    if (lane < nt) vblk = min(max(pg.bt[(size_t)cs * pg.stride + ((c0 + AKT * lane) >> pg.lbs)], 0), pg.nblk - 1);
+    if (lane + 64 < nt)
+      vblk_hi = min(max(pg.bt[(size_t)cs * pg.stride + ((c0 + AKT * (lane + 64)) >> pg.lbs)], 0), pg.nblk - 1);
+  }
   auto tile_off = [&](int kt) -> size_t {
     if (!paged) return (size_t)kt * HD;
-    const int e = __builtin_amdgcn_readlane(vblk, (kt - c0) >> 6);
+    const int i = (kt - c0) >> 6;  // wave-uniform
+    const int e = i < 64 ? __builtin_amdgcn_readlane(vblk, i) : __builtin_amdgcn_readlane(vblk_hi, i - 64);
     return (size_t)e * unit_stride + (size_t)(kt & ((1 << pg.lbs) - 1)) * HD;
   };
   // this wave's copies of a tile: index f = w + NW i (i < PW), clamped to the last one; the source is a
@@ -573,6 +585,20 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(const bf16_t* __restrict_
     }
     return;
   }
+  if (dout) {  // one chunk covers every key: the normalised output (zero for a row that sees no key)
+    if (v < nq) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+      for (int b = 0; b < HD / 16; ++b) {
+        const int col = h * HD + 16 * b + 4 * lg;
+        uint2 w;
+        w.x = (uint32_t)f2bf(O[b][0] * inv) | ((uint32_t)f2bf(O[b][1] * inv) << 16);
+        w.y = (uint32_t)f2bf(O[b][2] * inv) | ((uint32_t)f2bf(O[b][3] * inv) << 16);
+        *(uint2*)(dout + (dpacked ? slab32_index(row, col, R) : (size_t)row * Hq * HD + col)) = w;
+      }
+    }
+    return;
+  }
   if (v < nq) {
     const size_t oi = ((size_t)sp * R + row) * Hq + h;
 #pragma unroll
@@ -589,11 +615,13 @@ template <int HD, int NST, bool TTT>
 void launch_attn(int nw, unsigned nblocks, hipStream_t st, const bf16_t* q, const bf16_t* kc, const bf16_t* vc,
                  size_t unit_stride, size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps,
                  int qblocks, int Hq, int Hkv, int ns, int nwork, int key_bound, float scale, int chunk,
-                 float* o_part, float* ml_part, const bf16_t* dk, const bf16_t* dv, int nstep, bf16_t* tout) {
+                 float* o_part, float* ml_part, const bf16_t* dk, const bf16_t* dv, int nstep, bf16_t* tout,
+                 const int* plan, bf16_t* dout, int dpacked) {
 #define E3_ATTN_LAUNCH(N)                                                                                             \
   k_attn_mfma<HD, N, NST, TTT><<<nblocks, 64 * N, 0, st>>>(q, kc, vc, unit_stride, head_stride, pg, rm.seq, rm.lim,   \
                                                       rm.tail0, rm.mask, R, rps, qblocks, Hq, Hkv, ns, nwork,       \
-                                                      key_bound, scale, chunk, o_part, ml_part, dk, dv, nstep, tout)
+                                                      key_bound, scale, chunk, o_part, ml_part, dk, dv, nstep, tout, \
+                                                      plan, dout, dpacked)
   switch (nw) {
     case 4: E3_ATTN_LAUNCH(4); break;
     case 5: E3_ATTN_LAUNCH(5); break;
@@ -604,40 +632,242 @@ void launch_attn(int nw, unsigned nblocks, hipStream_t st, const bf16_t* q, cons
 #undef E3_ATTN_LAUNCH
 }
 
+// Launch geometry of the MFMA path: waves per workgroup, query blocks per
+// sequence, keys per chunk, chunk slots and work items.  mfma false: the
+// scalar kernel runs (ns chunks of ATT_CHUNK).
+struct AttnGeom {
+  bool mfma = false, planned = false, direct = false;
+  int nw = 0, qblocks = 0, chunk = ATT_CHUNK, ns = 1, nwork = 0;
+  unsigned nblocks = 0;
+};
+
+AttnGeom attn_geom(bool bf16, const KvPages& pg, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
+                   int max_splits, int chunk_override, bool ttt, bool can_direct) {
+  AttnGeom g;
+  g.ns = std::min(std::max(1, (key_bound + ATT_CHUNK - 1) / ATT_CHUNK), max_splits);
+  if (!(bf16 && (hd == 64 || hd == 128) && rps > 0 && R % rps == 0)) return g;
+  g.mfma = true;
+  const int G = Hq / Hkv, nq = rps * G, nseq = R / rps;
+  g.nw = std::min(8, std::max(4, (nq + 15) / 16));  // waves: 16 queries each
+  g.qblocks = (nq + 16 * g.nw - 1) / (16 * g.nw);
+  // Longer key chunks when the launch has work to spare: fewer partials to
+  // write and merge, and each workgroup's set-up spread over more tiles.
+  const long tiles256 = (long)nseq * g.qblocks * Hkv * g.ns;
+  int chunk = chunk_override > 0 ? chunk_override
+              : tiles256 >= 8192 ? 6 * ATT_CHUNK
+              : tiles256 >= 4096 ? 3 * ATT_CHUNK
+              : tiles256 >= 2048 ? 2 * ATT_CHUNK
+                                 : ATT_CHUNK;
+  if (pg.bt && chunk > ATT_MAX_TILES * AKT) chunk = ATT_MAX_TILES * AKT;  // paged: block ids in two registers
+  // Several sequences over more than one round of workgroups: their lengths
+  // differ, so the work is ordered by a plan (largest items first, spread over
+  // the XCDs).  When one chunk per (query block, KV head) still gives a full
+  // round of work items and covers every key, each item writes its rows'
+  // normalised output itself (no partials, no merge); otherwise chunks of
+  // ATT_PLAN_CHUNK keys.
+  if (chunk_override <= 0 && !ttt && nseq > 1 && tiles256 >= 2048 && (long)nseq * g.qblocks <= ATT_PLAN_MAX_BLOCKS) {
+    const int one = (key_bound + AKT - 1) / AKT * AKT;
+    const long w1 = (long)nseq * g.qblocks * Hkv;
+    const int pc = can_direct && one <= ATT_MAX_TILES * AKT && w1 >= 512 ? one : ATT_PLAN_CHUNK;
+    const int pns = (key_bound + pc - 1) / pc;
+    const long pwork = w1 * pns;
+    if (pwork >= 512 && pwork <= ATT_PLAN_MAX_WORK && pns <= max_splits) {
+      g.planned = true;
+      g.direct = pns == 1 && can_direct;
+      chunk = pc;
+    }
+  }
+  g.chunk = chunk;
+  g.ns = (key_bound + chunk - 1) / chunk;
+  g.nwork = nseq * g.qblocks * Hkv * g.ns;
+  g.nblocks = (unsigned)((g.nwork + 7) / 8 * 8);
+  return g;
+}
+
+// Work order of the tree-attention launches over several sequences
+// (blockIdx.x > 0: one query block each; blockIdx.x = 0: the order).
+//
+// A work item (query block, KV head, key chunk) costs about its number of key
+// tiles.  The order sorts the non-empty items by tile count, largest first
+// (equal counts in item order), and deals rank i to XCD x(i) in a serpentine
+// over the 8 XCDs (x = i mod 8, reversed on odd rounds), at position i / 8 of
+// that XCD's queue: workgroup 8 (i / 8) + x(i) runs it, since workgroup j runs
+// on XCD j mod 8.  Each XCD gets nearly the same tiles and, within it, its
+// largest items first.  Unused positions hold -1 (the workgroup exits).
+//
+// Items with no key (chunks past the end of a query block's keys) are left
+// out of the order; their partials are marked empty here (m = -inf, l = 0),
+// once for every launch over the same rows, so the combine skips them: every
+// (row, head, chunk) entry is written either here or by its one work item.
+// Both sides compute a query block's key end and sequence exactly as the
+// attention kernel does.
+//
+// keep_empty (one chunk per item, each writing its rows' output): the items
+// without keys stay in the order, after all others, since they write zeros.
+__global__ __launch_bounds__(1024) void k_attn_plan(const int* __restrict__ rseq, const int* __restrict__ rlim,
+                                                    const int* __restrict__ rt0, const uint64_t* __restrict__ rmask,
+                                                    int R, int rps, int qblocks, int QB, int G, int Hq, int Hkv,
+                                                    int ns, int nwork, int S_cap, int chunk, int nblocks,
+                                                    int keep_empty, int* __restrict__ plan,
+                                                    float* __restrict__ ml_part) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nq = rps * G, nbq = (R / rps) * qblocks;
+  // key end and sequence of query block b (largest over its query vectors, as the attention kernel takes them)
+  auto vec_end = [&](int b, int i, int* end, int* seq) {
+    const int bs = b / qblocks, qb = b % qblocks, v = qb * QB + i;
+    *end = 0;
+    *seq = -1;
+    if (i >= QB || v >= nq) return;
+    const int row = bs * rps + v / G, sq = rseq[row];
+    if (sq < 0) return;
+    *end = min(key_end(rlim[row], rt0[row], rmask[row]), S_cap);
+    *seq = sq;
+  };
+  if (blockIdx.x > 0) {  // the empty partials of query block b
+    __shared__ int b_end, b_seq;
+    const int b = blockIdx.x - 1;
+    if (tid == 0) {
+      b_end = 0;
+      b_seq = -1;
+    }
+    __syncthreads();
+    for (int i = tid; i < QB; i += blockDim.x) {
+      int e, sq;
+      vec_end(b, i, &e, &sq);
+      if (sq >= 0) {
+        atomicMax(&b_end, e);
+        atomicMax(&b_seq, sq);
+      }
+    }
+    __syncthreads();
+    const int kend = b_end, bs = b / qblocks, qb = b % qblocks;
+    const int sp0 = b_seq < 0 ? 0 : min(ns, (kend + chunk - 1) / chunk);  // chunks sp0.. have no key
+    const int nv = min(QB, nq - qb * QB);
+    const int total = (ns - sp0) * Hkv * nv;
+    for (int i = tid; i < total; i += blockDim.x) {
+      const int vi = i % nv, t = i / nv, g = t % Hkv, sp = sp0 + t / Hkv;
+      const int v = qb * QB + vi, row = bs * rps + v / G, h = g * G + v % G;
+      const size_t oi = ((size_t)sp * R + row) * Hq + h;
+      *(float2*)&ml_part[2 * oi] = make_float2(-INFINITY, 0.f);
+    }
+    return;
+  }
+  __shared__ int s_end[ATT_PLAN_MAX_BLOCKS], s_seq[ATT_PLAN_MAX_BLOCKS];
+  __shared__ unsigned char s_tiles[ATT_PLAN_MAX_WORK];
+  __shared__ int s_cnt[ATT_PLAN_BINS], s_start[ATT_PLAN_BINS], s_run[ATT_PLAN_BINS];
+  __shared__ int s_wcnt[16][ATT_PLAN_BINS];
+  __shared__ int s_nreal;
+  for (int b = tid; b < nbq; b += blockDim.x) {
+    s_end[b] = 0;
+    s_seq[b] = -1;
+  }
+  for (int i = tid; i < ATT_PLAN_BINS; i += blockDim.x) {
+    s_cnt[i] = 0;
+    s_run[i] = 0;
+  }
+  for (int i = tid; i < 16 * ATT_PLAN_BINS; i += blockDim.x) s_wcnt[i / ATT_PLAN_BINS][i % ATT_PLAN_BINS] = 0;
+  __syncthreads();
+  for (int i = tid; i < nbq * QB; i += blockDim.x) {
+    int e, sq;
+    vec_end(i / QB, i % QB, &e, &sq);
+    if (sq >= 0) {
+      atomicMax(&s_end[i / QB], e);
+      atomicMax(&s_seq[i / QB], sq);
+    }
+  }
+  __syncthreads();
+  // tiles of item lam, decoded as the attention kernel decodes it
+  for (int lam = tid; lam < nwork; lam += blockDim.x) {
+    const int qb = qblocks - 1 - lam % qblocks;
+    const int t = lam / qblocks / Hkv;
+    const int sp = t % ns, bs = t / ns, b = bs * qblocks + qb;
+    const int c0 = sp * chunk, c1 = min(c0 + chunk, s_end[b]);
+    const int tiles = (s_seq[b] < 0 || c0 >= c1) ? 0 : min((c1 - c0 + AKT - 1) / AKT, ATT_PLAN_BINS - 1);
+    s_tiles[lam] = (unsigned char)tiles;
+    if (tiles || keep_empty) atomicAdd(&s_cnt[tiles], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int t = ATT_PLAN_BINS - 1; t >= 0; --t) {
+      s_start[t] = acc;
+      acc += s_cnt[t];
+    }
+    s_nreal = acc;
+  }
+  __syncthreads();
+  auto slot = [](int i) {
+    const int r = i >> 3, j = i & 7;
+    return 8 * r + ((r & 1) ? 7 - j : j);
+  };
+  // ranks: bin start + items of the same tile count before this one (earlier passes, earlier waves, lower lanes)
+  for (int base = 0; base < nwork; base += blockDim.x) {
+    const int lam = base + tid;
+    int t = lam < nwork ? s_tiles[lam] : -1;
+    if (t == 0 && !keep_empty) t = -1;  // left out of the order
+    unsigned long long todo = __ballot(t >= 0);
+    int rank = 0;
+    while (todo) {  // one round per distinct tile count in the wave
+      const int leader = __ffsll((long long)todo) - 1;
+      const int tk = __shfl(t, leader, 64);
+      const unsigned long long m = __ballot(t == tk);
+      if (t == tk) rank = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == leader) s_wcnt[w][tk] = __popcll(m);
+      todo &= ~m;
+    }
+    __syncthreads();
+    if (t >= 0) {
+      int off = s_run[t];
+      for (int u = 0; u < w; ++u) off += s_wcnt[u][t];
+      plan[slot(s_start[t] + off + rank)] = lam;
+    }
+    __syncthreads();
+    if (tid < ATT_PLAN_BINS) {
+      int sum = 0;
+      for (int u = 0; u < 16; ++u) {
+        sum += s_wcnt[u][tid];
+        s_wcnt[u][tid] = 0;
+      }
+      s_run[tid] += sum;
+    }
+    __syncthreads();
+  }
+  for (int i = s_nreal + tid; i < nblocks; i += blockDim.x) plan[slot(i)] = -1;
+}
+
+bool attention_plan(bool bf16, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd,
+                    int key_bound, int max_splits, int* plan, float* ml_part, hipStream_t st) {
+  if (R <= 0 || !plan) return false;
+  const AttnGeom g = attn_geom(bf16, pg, R, rps, Hq, Hkv, hd, key_bound, max_splits, 0, false, true);
+  if (!g.planned) return false;
+  const int nbq = (R / rps) * g.qblocks;
+  // direct output: no partials to mark, every item stays in the order
+  k_attn_plan<<<g.direct ? 1 : 1 + nbq, 1024, 0, st>>>(rm.seq, rm.lim, rm.tail0, rm.mask, R, rps, g.qblocks,
+                                                       16 * g.nw, Hq / Hkv, Hq, Hkv, g.ns, g.nwork, key_bound, g.chunk,
+                                                       (int)g.nblocks, g.direct ? 1 : 0, plan, ml_part);
+  return true;
+}
+
 // The chunk partials of tree-masked attention (o_part / ml_part, chunk-major);
 // returns the number of key chunks written and their length.
 AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride,
                               size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv,
                               int hd,
                               int key_bound, float* o_part, float* ml_part, int max_splits, hipStream_t st,
-                              int chunk_override, const void* dk, const void* dv, int nstep, void* tout) {
-  int ns = (key_bound + ATT_CHUNK - 1) / ATT_CHUNK;
-  if (ns < 1) ns = 1;
-  if (ns > max_splits) ns = max_splits;  // the workspace holds ceil(max_seq / chunk) splits
+                              int chunk_override, const void* dk, const void* dv, int nstep, void* tout,
+                              const int* plan, void* dout, bool dpacked) {
+  const AttnGeom g = attn_geom(bf16, pg, R, rps, Hq, Hkv, hd, key_bound, max_splits, chunk_override, tout != nullptr,
+                               dout != nullptr);
   const float scale = 1.f / sqrtf((float)hd);
-  if (bf16 && (hd == 64 || hd == 128) && rps > 0 && R % rps == 0) {
-    const int G = Hq / Hkv;
-    const int nq = rps * G;
-    const int nw = std::min(8, std::max(4, (nq + 15) / 16));  // waves: 16 queries each
-    const int qblocks = (nq + 16 * nw - 1) / (16 * nw);
-    // Longer key chunks when the launch has work to spare: fewer partials to
-    // write and merge, and each workgroup's set-up spread over more tiles.
-    const long tiles256 = (long)(R / rps) * qblocks * Hkv * ns;
-    const int chunk = chunk_override > 0 ? chunk_override
-                      : tiles256 >= 8192 ? 6 * ATT_CHUNK
-                      : tiles256 >= 4096 ? 3 * ATT_CHUNK
-                      : tiles256 >= 2048 ? 2 * ATT_CHUNK
-                                         : ATT_CHUNK;
-    if (pg.bt && chunk > 64 * AKT) return attention_partials(bf16, q, kc, vc, unit_stride, head_stride, pg, rm, R,
-                                                            rps, Hq, Hkv, hd, key_bound, o_part, ml_part, max_splits,
-                                                            st, 64 * AKT);  // paged: at most 64 tiles per chunk
-    ns = (key_bound + chunk - 1) / chunk;
-    const int nwork = (R / rps) * qblocks * Hkv * ns;
-    const int nblocks = (nwork + 7) / 8 * 8;
+  if (g.mfma) {
+    const int nw = g.nw, qblocks = g.qblocks, ns = g.ns, nwork = g.nwork, chunk = g.chunk;
+    const unsigned nblocks = g.nblocks;
+    const int* pl = g.planned ? plan : nullptr;  // a plan made for this geometry (attention_plan) or none
+    bf16_t* dot = g.direct ? (bf16_t*)dout : nullptr;
 #define E3_ATTN_ARGS                                                                                                \
   nw, nblocks, st, (const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, unit_stride, head_stride, pg, rm, R, rps,   \
       qblocks, Hq, Hkv, ns, nwork, key_bound, scale, chunk, o_part, ml_part, (const bf16_t*)dk, (const bf16_t*)dv,      \
-      nstep, (bf16_t*)tout
+      nstep, (bf16_t*)tout, pl, dot, dpacked ? 1 : 0
     if (tout) {  // training-time test: diagonal keys merged in the epilogue, output written directly
       if (hd == 128)
         launch_attn<128, 4, true>(E3_ATTN_ARGS);
@@ -653,8 +883,9 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
       launch_attn<64, 4, false>(E3_ATTN_ARGS);
     }
 #undef E3_ATTN_ARGS
-    return AttnSplits{ns, chunk};
+    return AttnSplits{ns, chunk, g.direct};
   }
+  const int ns = g.ns;
   dim3 grid(R, Hq, ns);
   if (bf16)
     k_attn_partial<bf16_t><<<grid, 64, 0, st>>>((const bf16_t*)q, (const bf16_t*)kc, (const bf16_t*)vc, unit_stride,
@@ -669,10 +900,13 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
 
 void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride, size_t head_stride,
                const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
-               float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st, bool packed) {
+               float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st, bool packed,
+               const int* plan) {
   if (R <= 0) return;
   const AttnSplits sp = attention_partials(bf16, q, kc, vc, unit_stride, head_stride, pg, rm, R, rps, Hq, Hkv, hd,
-                                           key_bound, o_part, ml_part, max_splits, st, 0);
+                                           key_bound, o_part, ml_part, max_splits, st, 0, nullptr, nullptr, 0,
+                                           nullptr, plan, bf16 ? out : nullptr, packed);
+  if (sp.direct) return;  // the attention kernel wrote the output
   if (bf16)
     combine<bf16_t>(o_part, ml_part, sp.ns, R, Hq, hd, -1, (bf16_t*)out, st, packed);
   else

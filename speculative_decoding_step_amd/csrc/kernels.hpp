@@ -186,6 +186,7 @@ void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const R
 // rps: rows per sequence (rows of one sequence are consecutive; R % rps == 0).
 struct AttnSplits {
   int ns, chunk;  // key chunks written, keys per chunk
+  bool direct;    // one chunk: the output was written by the attention kernel (dout), no partials
 };
 AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride,
                               size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd,
@@ -195,7 +196,22 @@ AttnSplits attention_partials(bool bf16, const void* q, const void* kc, const vo
                               // diagonal keys dk / dv [nstep][Hkv][R][hd] join each row's softmax and the output
                               // is written to tout [R][Hq][hd]; no partials
                               const void* dk = nullptr, const void* dv = nullptr, int nstep = 0,
-                              void* tout = nullptr);
+                              void* tout = nullptr, const int* plan = nullptr,
+                              // bf16 [R, Hq * hd] (column slabs of 32 when dpacked): output written directly
+                              // when a planned launch covers every key in one chunk (AttnSplits::direct)
+                              void* dout = nullptr, bool dpacked = false);
+// Work order for the attention launches over rows rm (same sizes, until the row metadata changes) when they
+// cover several sequences in more than one round of workgroups: writes the order to plan (ATT_PLAN_CAP ints)
+// and marks the partials of work items without keys as empty in ml_part; returns false (nothing launched)
+// when such launches take no plan.  Launches given the plan must follow on the same stream.
+constexpr int ATT_PLAN_CHUNK = 3072;       // keys per chunk of planned launches that need several chunks
+constexpr int ATT_MAX_TILES = 128;         // 64-key tiles per chunk at most (paged caches)
+constexpr int ATT_PLAN_MAX_WORK = 16384;   // work items a plan orders
+constexpr int ATT_PLAN_MAX_BLOCKS = 2048;  // query blocks (sequences x query blocks per sequence)
+constexpr int ATT_PLAN_BINS = ATT_MAX_TILES + 1;  // key tiles per work item: 0..128
+constexpr int ATT_PLAN_CAP = ATT_PLAN_MAX_WORK + 8;
+bool attention_plan(bool bf16, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd,
+                    int key_bound, int max_splits, int* plan, float* ml_part, hipStream_t st);
 // Training-time-test attention: q, out [T, Hq, hd]; k0, v0 [Hkv, T, hd]; ks, vs [S, Hkv, T, hd]; ws of
 // ttt_workspace_bytes(T, Hq, hd) bytes.
 size_t ttt_workspace_bytes(int T, int Hq, int hd);
@@ -210,7 +226,8 @@ void ttt_attention(bool bf16, int T, int S, int Hq, int Hkv, int hd, const void*
 // out [R, Hq * hd] of T, row-major, or in column slabs of 32 when packed.
 void attention(bool bf16, const void* q, const void* kc, const void* vc, size_t unit_stride,
                size_t head_stride, const KvPages& pg, const RowMeta& rm, int R, int rps, int Hq, int Hkv, int hd, int key_bound,
-               float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st, bool packed = false);
+               float* o_part, float* ml_part, int max_splits, void* out, hipStream_t st, bool packed = false,
+               const int* plan = nullptr);
 
 // Row-wise top-k + log-sum-exp over fp32 logits [R, ld] (first V columns).
 // z = logits / temperature (in double); ids/vals are of the raw logits.
