@@ -718,9 +718,11 @@ __global__ __launch_bounds__(1024) void k_attn_plan(const int* __restrict__ rseq
     *end = 0;
     *seq = -1;
     if (i >= QB || v >= nq) return;
-    const int row = bs * rps + v / G, sq = rseq[row];
+    const int row = bs * rps + v / G;
+    const int sq = rseq[row], lim = rlim[row], t0 = rt0[row];  // loaded together: one memory round trip
+    const uint64_t mk = rmask[row];
     if (sq < 0) return;
-    *end = min(key_end(rlim[row], rt0[row], rmask[row]), S_cap);
+    *end = min(key_end(lim, t0, mk), S_cap);
     *seq = sq;
   };
   if (blockIdx.x > 0) {  // the empty partials of query block b
@@ -767,12 +769,15 @@ __global__ __launch_bounds__(1024) void k_attn_plan(const int* __restrict__ rseq
   }
   for (int i = tid; i < 16 * ATT_PLAN_BINS; i += blockDim.x) s_wcnt[i / ATT_PLAN_BINS][i % ATT_PLAN_BINS] = 0;
   __syncthreads();
-  for (int i = tid; i < nbq * QB; i += blockDim.x) {
-    int e, sq;
-    vec_end(i / QB, i % QB, &e, &sq);
-    if (sq >= 0) {
-      atomicMax(&s_end[i / QB], e);
-      atomicMax(&s_seq[i / QB], sq);
+  // per row (its G query vectors lie in one or two query blocks of its sequence)
+  for (int r = tid; r < R; r += blockDim.x) {
+    const int sq = rseq[r], lim = rlim[r], t0 = rt0[r];
+    const uint64_t mk = rmask[r];
+    if (sq < 0) continue;
+    const int e = min(key_end(lim, t0, mk), S_cap), bs = r / rps, v0 = (r - bs * rps) * G;
+    for (int qb = v0 / QB; qb <= (v0 + G - 1) / QB; ++qb) {
+      atomicMax(&s_end[bs * qblocks + qb], e);
+      atomicMax(&s_seq[bs * qblocks + qb], sq);
     }
   }
   __syncthreads();
@@ -787,13 +792,29 @@ __global__ __launch_bounds__(1024) void k_attn_plan(const int* __restrict__ rseq
     if (tiles || keep_empty) atomicAdd(&s_cnt[tiles], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int t = ATT_PLAN_BINS - 1; t >= 0; --t) {
-      s_start[t] = acc;
-      acc += s_cnt[t];
+  if (w == 0) {  // bin starts, largest tile count first: an exclusive scan over the bins in descending order
+    static_assert(3 * 64 >= ATT_PLAN_BINS, "three bins per lane");
+    int v[3], sum = 0;
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      const int t = ATT_PLAN_BINS - 1 - (3 * lane + e);
+      v[e] = t >= 0 ? s_cnt[t] : 0;
+      sum += v[e];
     }
-    s_nreal = acc;
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    int ex = inc - sum;
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      const int t = ATT_PLAN_BINS - 1 - (3 * lane + e);
+      if (t >= 0) s_start[t] = ex;
+      ex += v[e];
+    }
+    if (lane == 63) s_nreal = inc;
   }
   __syncthreads();
   auto slot = [](int i) {

@@ -369,10 +369,83 @@ __global__ __launch_bounds__(64) void k_rope_kv(const float* __restrict__ part, 
   }
 }
 
+// The same, four rotation pairs per thread (float4 partial loads, 4-wide stores): a block covers 256 / (hd / 8)
+// heads of one row, and the row's cos/sin of each pair index are formed once per block into LDS.  Same
+// arithmetic and summation order as k_rope_kv.  Needs hd % 8 == 0, hd <= 128 and 256 % (hd / 8) == 0.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_kv4(const float* __restrict__ part, int S, size_t sstride,
+                                                  const int* __restrict__ rseq, const int* __restrict__ rpos,
+                                                  const int* __restrict__ rslot, const double* __restrict__ inv_freq,
+                                                  T* __restrict__ q_out, T* __restrict__ kc, T* __restrict__ vc,
+                                                  size_t unit_stride, size_t head_stride, KvPages pg, int Hq, int Hkv,
+                                                  int hd, int* status) {
+  __shared__ __attribute__((aligned(16))) float cs_l[64], sn_l[64];
+  const int r = blockIdx.x, tph = hd >> 3, half = hd >> 1;
+  const int h = blockIdx.y * (256 / tph) + threadIdx.x / tph, j = threadIdx.x % tph;
+  // the partial loads go out first; the row's cos/sin are formed while they are in flight
+  int b = rseq[r];
+  KvLoc at{0, 0};
+  if (h >= Hq && h < Hq + 2 * Hkv && b >= 0) {  // K or V head: where the row's position lives
+    at = kv_loc_w(pg, b, rslot[r]);
+    if (at.unit < 0) {
+      if (j == 0 && h == Hq) raise_flag(status, E3_DEV_KV_OVERFLOW);
+      b = -1;
+    }
+  }
+  const bool live = h < Hq || (h < Hq + 2 * Hkv && b >= 0);
+  float4 x1 = make_float4(0.f, 0.f, 0.f, 0.f), x2 = x1;
+  if (live) {
+    const int ncol = (Hq + 2 * Hkv) * hd;
+    const float* pr = part + (size_t)r * ncol + (size_t)h * hd + 4 * j;
+    x1 = sum_splits4((const float4*)pr, S, sstride / 4);
+    x2 = sum_splits4((const float4*)(pr + half), S, sstride / 4);
+  }
+  constexpr double TWO_PI = 6.283185307179586476925286766559;
+  const double pos = (double)rpos[r];
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double ang = pos * inv_freq[i];
+    const float red = (float)(ang - TWO_PI * rint(ang / TWO_PI));
+    float sn, cs;
+    sincosf(red, &sn, &cs);
+    cs_l[i] = cs;
+    sn_l[i] = sn;
+  }
+  __syncthreads();
+  if (!live) return;
+  T* dst = h < Hq ? q_out + ((size_t)r * Hq + h) * hd
+                  : (h < Hq + Hkv ? kc : vc) + (size_t)at.unit * unit_stride +
+                        (size_t)(h < Hq + Hkv ? h - Hq : h - Hq - Hkv) * head_stride + (size_t)at.row * hd;
+  if (h >= Hq + Hkv) {  // V: copy
+    st4<T>(dst, 4 * j, x1);
+    st4<T>(dst, half + 4 * j, x2);
+    return;
+  }
+  const float4 c = *(const float4*)&cs_l[4 * j], sn = *(const float4*)&sn_l[4 * j];
+  st4<T>(dst, 4 * j,
+         make_float4(x1.x * c.x - x2.x * sn.x, x1.y * c.y - x2.y * sn.y, x1.z * c.z - x2.z * sn.z,
+                     x1.w * c.w - x2.w * sn.w));
+  st4<T>(dst, half + 4 * j,
+         make_float4(x2.x * c.x + x1.x * sn.x, x2.y * c.y + x1.y * sn.y, x2.z * c.z + x1.z * sn.z,
+                     x2.w * c.w + x1.w * sn.w));
+}
+
 void rope_kv(bool bf16, const float* part, int S, size_t sstride, int R, const RowMeta& rm, const double* inv_freq,
              void* q_out, void* kc, void* vc, size_t unit_stride, size_t head_stride, const KvPages& pg, int Hq,
              int Hkv, int hd, int* status, hipStream_t st) {
   if (R <= 0) return;
+  const int tph = hd / 8;
+  if (hd % 8 == 0 && hd <= 128 && 256 % tph == 0) {
+    const dim3 grid4(R, (Hq + 2 * Hkv + 256 / tph - 1) / (256 / tph));
+    if (bf16)
+      k_rope_kv4<bf16_t><<<grid4, 256, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, inv_freq,
+                                                (bf16_t*)q_out, (bf16_t*)kc, (bf16_t*)vc, unit_stride, head_stride,
+                                                pg, Hq, Hkv, hd, status);
+    else
+      k_rope_kv4<float><<<grid4, 256, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, inv_freq, (float*)q_out,
+                                               (float*)kc, (float*)vc, unit_stride, head_stride, pg, Hq, Hkv, hd,
+                                               status);
+    return;
+  }
   dim3 grid(R, Hq + 2 * Hkv);
   if (bf16)
     k_rope_kv<bf16_t><<<grid, 64, 0, st>>>(part, S, sstride, rm.seq, rm.pos, rm.slot, inv_freq, (bf16_t*)q_out,
