@@ -203,3 +203,38 @@ def test_planned_draft_ragged_vs_oracle(heads, kv, hd, max_seq):
         worst = max(worst, err)
         assert err <= 2e-2, (b, P, err)
     print(f"  draft logits: largest error over all sequences {worst:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("heads,kv,hd,max_seq", [(8, 8, 64, 2100), (4, 4, 128, 3200)])
+def test_planned_graph_replay_matches_eager(heads, kv, hd, max_seq):
+    """A step over 64 ragged sequences captured into a graph (its draft levels and verify
+    planned: one chunk per item, then 3,072-key chunks) and replayed four times equals
+    four eager steps bit for bit: the work order is recomputed inside the graph from the
+    lengths each replay finds."""
+    ms = toy_shape(dtype="bf16", vocab=1000, layers=2, d=512, heads=heads, kv=kv, hd=hd, ffn=512)
+    D, k, N, Bn, steps = 4, 4, 12, 64, 4
+    assert _policy(Bn, N + 1, ms, max_seq)[0] and _policy(Bn, k, ms, max_seq)[0]
+    spec = Spec("greedy_tree", D, k, N)
+    lens = _lengths(N + 1, max_seq - (N + 1) - (D - 1) * k - steps * (D + 1))
+    print(f"\n[planned graph replay: {Bn} sequences, {lens.min()}..{lens.max()} tokens]", flush=True)
+    prompts = [synth.tokens_np(75, f"g{b}", int(lens[b]), ms.vocab) for b in range(Bn)]
+    a = make_engine(ms, spec, batch=Bn, max_seq=max_seq, seed=31, sigma=0.3)
+    b = make_engine(ms, spec, batch=Bn, max_seq=max_seq, seed=31, sigma=0.3)
+    a.prefill(prompts)
+    b.prefill(prompts)
+    b.capture()
+    for i in range(steps):
+        a.step()
+        b.replay()
+        torch.cuda.synchronize()
+        for name in ("tokens", "parents", "path", "path_len", "next_root", "seq_lens", "next_tok"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), (i, name)
+    assert a.device_status() == 0 and b.device_status() == 0
+    plen = a.path_len.cpu().numpy()
+    ka, kb = a.kv_logical(), b.kv_logical()
+    for s in (int(np.argmin(lens)), int(np.argmax(lens))):
+        P = int(a.seq_lens[s])
+        assert torch.equal(ka[:, :, s, :, :P], kb[:, :, s, :, :P]), s
+    print(f"  last step's path lengths {np.bincount(plen).tolist()}", flush=True)
+    a.close()
+    b.close()
