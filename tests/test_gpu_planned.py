@@ -63,15 +63,19 @@ def _policy(n_seq, rows, ms, max_seq, paged=False):
 # (heads, KV heads, head size, d, cache length, paged block size): chunked plans at head sizes 128 (two query
 # vectors per KV head: one query block) and 64 (four: two query blocks); one-chunk plans (direct output) at
 # head sizes 64 and 128, and on a paged cache whose one chunk spans more than 64 tiles
-VERIFY_CASES = [(4, 4, 128, 512, 3200, 0), (8, 2, 64, 512, 3200, 0), (8, 8, 64, 512, 2100, 0),
-                (8, 8, 128, 1024, 2100, 0), (8, 8, 64, 512, 4300, 64)]
+VERIFY_CASES = [(4, 4, 128, 512, 3200, 0, False), (8, 2, 64, 512, 3200, 0, False), (8, 8, 64, 512, 2100, 0, False),
+                (8, 8, 128, 1024, 2100, 0, False), (8, 8, 64, 512, 4300, 64, False),
+                (4, 4, 128, 512, 3200, 0, True), (8, 8, 64, 512, 2100, 0, True)]
 
 
-@pytest.mark.parametrize("heads,kv,hd,d,max_seq,bs", VERIFY_CASES)
-def test_planned_verify_ragged_vs_oracle(heads, kv, hd, d, max_seq, bs):
+@pytest.mark.parametrize("heads,kv,hd,d,max_seq,bs,lengths", VERIFY_CASES)
+def test_planned_verify_ragged_vs_oracle(heads, kv, hd, d, max_seq, bs, lengths):
     """64 sequences, each with its own random 40-node tree, verified in one call: every
     sequence's tree logits within 2e-2 of the oracle's over the GPU prefill's K/V, argmax
-    wherever the oracle's top-2 margin clears twice that, and the tree rows' K/V."""
+    wherever the oracle's top-2 margin clears twice that, and the tree rows' K/V.  With
+    per-request draft lengths (0 .. 39 nodes, several 0) only each request's first nodes
+    take part: those rows are checked, the others (padding rows in the planned launches)
+    write no K/V."""
     ms = toy_shape(dtype="bf16", vocab=1000, layers=2, d=d, heads=heads, kv=kv, hd=hd, ffn=512)
     n, Bn = 40, 64
     planned, direct, qblocks = _policy(Bn, n, ms, max_seq, bs > 0)
@@ -80,13 +84,19 @@ def test_planned_verify_ragged_vs_oracle(heads, kv, hd, d, max_seq, bs):
     lens = _lengths(n, max_seq - n - 3 * 13)  # the longest prompt a step of this tree budget fits
     print(f"\n[planned verify: {Bn} sequences, {lens.min()}..{lens.max()} tokens, {heads}/{kv} heads x {hd}, "
           f"{qblocks} query block(s) per sequence, {'one chunk' if direct else 'chunked'}"
-          f"{f', paged ({bs}-key blocks)' if bs else ''}]", flush=True)
+          f"{f', paged ({bs}-key blocks)' if bs else ''}{', draft lengths' if lengths else ''}]", flush=True)
     eng = make_engine(ms, spec, batch=Bn, max_seq=max_seq, sigma=0.02, block_size=bs, page_seed=5 if bs else 0)
+    nd = np.full(Bn, n - 1)
+    if lengths:
+        nd = np.random.default_rng(23).integers(0, n, size=Bn)
+        nd[::7] = 0
+        eng.set_draft_lengths(nd)
     shp, W, H = oracle_weights(ms, sigma=0.02)
     prompts = [synth.tokens_np(71, f"r{b}", int(lens[b]), ms.vocab) for b in range(Bn)]
     eng.prefill(prompts)
     torch.cuda.synchronize()
     assert eng.device_status() == 0
+    kv_before = eng.kv_logical("target").cpu() if lengths else None
     rng = np.random.default_rng(17)
     trees = [random_tree(rng, n, ms.vocab) for _ in range(Bn)]
     deps = []
@@ -125,15 +135,18 @@ def test_planned_verify_ragged_vs_oracle(heads, kv, hd, d, max_seq, bs):
         m = tree_mask(parents)
         ref, rk, rv, _ = target_forward(W, shp, cache, tokens, P + deps[b],
                                         [list(np.nonzero(m[i])[0]) for i in range(n)])
-        err, ok = logits_close(g_all[b], ref, "bf16")
+        nr = int(nd[b]) + 1  # the rows that take part
+        err, ok = logits_close(g_all[b][:nr], ref[:nr], "bf16")
         worst = max(worst, err)
         assert ok, (b, P, err)
-        for i in range(n):
+        for i in range(nr):
             if top2_margin(ref[i]) > 2 * margin_tol("bf16", ref[i]):
                 assert am_all[b, i] == int(np.argmax(ref[i])), (b, i)
         for l in range(shp.n_layers):
-            assert np.abs(kvb[l, 0, :, P:].transpose(1, 0, 2) - rk[l]).max() < 2e-2
-            assert np.abs(kvb[l, 1, :, P:].transpose(1, 0, 2) - rv[l]).max() < 2e-2
+            assert np.abs(kvb[l, 0, :, P:P + nr].transpose(1, 0, 2) - rk[l][:nr]).max() < 2e-2
+            assert np.abs(kvb[l, 1, :, P:P + nr].transpose(1, 0, 2) - rv[l][:nr]).max() < 2e-2
+        if lengths:  # the other rows wrote no K/V
+            assert torch.equal(kv[:, :, b, :, P + nr:P + n], kv_before[:, :, b, :, P + nr:P + n]), b
     print(f"  tree logits: largest error over all sequences {worst:.3g}", flush=True)
 
 
