@@ -632,6 +632,14 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
     pm[j] = tk.pmax && sl < ns ? tk.pmax[(size_t)r * ns + sl] : -INFINITY;
     ps[j] = tk.pmax && sl < ns ? tk.psum[(size_t)r * ns + sl] : 0.0;
   }
+  // the parent of this row's children (the previous level's output), loaded now rather than after the merge
+  int kpar = -1;
+  float kps = 0.f;
+  if (tid == 0 && kids.depth_new > 1) {
+    const int k = kids.ts.topk, b = r / k, rank = r % k;
+    kpar = kids.ts.front[b * k + rank];
+    kps = kids.ts.score[(size_t)b * kids.ts.cmax + kpar];
+  }
   float v[4];
   int id[4];
   unsigned taken = 0;
@@ -655,7 +663,24 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
     if (bj >= 0 && b.i == wb.i && b.v == wb.v) taken |= 1u << bj;
     if (lane == 0) cand[w][k] = wb;
   }
+  if (tk.pmax) {  // the wave's largest slice maximum, for the log-sum-exp (published by the barrier below)
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mloc = fmaxf(mloc, pm[j]);
+    const float wm = wave_max_reg(mloc);
+    if (lane == 0) fred[w] = wm;
+  }
   __syncthreads();
+  // waves 1-3 form their log-sum-exp shares while wave 0 selects; wave 0 forms its share afterwards
+  double sloc = 0.0, M = 0.0;
+  auto lse_share = [&]() {
+    const float mx = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
+    M = (double)mx / tk.temp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (tid + 256 * j < ns) sloc += ps[j] * exp((double)pm[j] / tk.temp - M);
+  };
+  if (tk.pmax && w > 0) lse_share();
   if (w == 0) {
     // the k best slices (a slice is known by its best id: ids of slice s are s * 128 ..)
     VI mine = lane < 4 * K ? cand[lane / K][lane % K] : VI{-INFINITY, 0x7fffffff};
@@ -694,18 +719,7 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
     }
   }
   if (!tk.pmax) return;  // uniform: no log-sum-exp asked for
-  float mloc = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) mloc = fmaxf(mloc, pm[j]);
-  const float wm = wave_max_reg(mloc);
-  if (lane == 0) fred[w] = wm;
-  __syncthreads();
-  const float mx = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
-  const double M = (double)mx / tk.temp;
-  double sloc = 0.0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (tid + 256 * j < ns) sloc += ps[j] * exp((double)pm[j] / tk.temp - M);
+  if (w == 0) lse_share();
   const double sw = wave_sum_d_reg(sloc);
   if (lane == 0) dred[w] = sw;
   __syncthreads();
@@ -718,12 +732,8 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
       const int k = ts.topk, dn = kids.depth_new;
       const int b = dn == 1 ? r : r / k, rank = dn == 1 ? 0 : r % k;
       const int c0 = (dn == 1 ? 0 : k + (dn - 2) * k * k) + rank * k;
-      int par = -1;
-      float ps = 0.f;
-      if (dn > 1) {
-        par = ts.front[b * k + rank];
-        ps = ts.score[(size_t)b * ts.cmax + par];
-      }
+      const int par = dn > 1 ? kpar : -1;
+      const float ps = dn > 1 ? kps : 0.f;
       const float l32 = (float)l;
       for (int ch = 0; ch < k; ++ch) {
         const size_t o = (size_t)b * ts.cmax + c0 + ch;
