@@ -112,50 +112,79 @@ __global__ __launch_bounds__(512) void k_tree_finalize(TreeState ts, int n_cand,
                                                        TreeOut out, int* status) {
   __shared__ int node_of[TREE_CMAX];  // creation index -> node index (0 = not kept)
   __shared__ unsigned long long keys[TREE_CMAX];
-  __shared__ int kept[64], kdep[64];
+  __shared__ int c_tok[TREE_CMAX], c_par[TREE_CMAX], c_dep[TREE_CMAX];  // the candidates, read once
+  __shared__ float c_score[TREE_CMAX];
   __shared__ int pidx[65];
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const size_t base = (size_t)b * ts.cmax;
   const int rows = n_nodes + 1;
+  const int P = seq_lens[b], root = roots[b];
   int np = 1;
   while (np < n_cand) np <<= 1;  // n_cand <= TREE_CMAX (checked on the host)
   for (int c = tid; c < np; c += nt) {
-    keys[c] = c < n_cand ? cand_key(ts.score[base + c], c) : ~0ull;
+    if (c < n_cand) {
+      const float sc = ts.score[base + c];
+      c_score[c] = sc;
+      c_tok[c] = ts.tok[base + c];
+      c_par[c] = ts.par[base + c];
+      c_dep[c] = ts.dep[base + c];
+      keys[c] = cand_key(sc, c);
+    } else {
+      keys[c] = ~0ull;
+    }
     node_of[c] = 0;
   }
   __syncthreads();
-  for (int k = 2; k <= np; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < np; i += nt) {
-        const int l = i ^ j;
-        if (l > i) {
-          const unsigned long long x = keys[i], y = keys[l];
-          if ((x > y) == ((i & k) == 0)) {
-            keys[i] = y;
-            keys[l] = x;
+  if (np <= nt) {
+    // Bitonic sort with one key per thread: partners in the same wave (distance < 64) are exchanged by
+    // shuffles, farther ones through LDS; the thread keeps the smaller key when its position and the block
+    // direction agree, else the larger.
+    unsigned long long key = tid < np ? keys[tid] : ~0ull;
+    for (int k = 2; k <= np; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        unsigned long long other;
+        if (j >= 64) {
+          __syncthreads();  // the previous exchange's reads are done
+          if (tid < np) keys[tid] = key;
+          __syncthreads();
+          other = tid < np ? keys[tid ^ j] : key;
+        } else {
+          other = __shfl_xor(key, j, 64);
+        }
+        const bool keep_min = ((tid & j) == 0) == ((tid & k) == 0);
+        key = keep_min ? (other < key ? other : key) : (other > key ? other : key);
+      }
+    __syncthreads();
+    if (tid < np) keys[tid] = key;
+    __syncthreads();
+  } else {
+    for (int k = 2; k <= np; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < np; i += nt) {
+          const int l = i ^ j;
+          if (l > i) {
+            const unsigned long long x = keys[i], y = keys[l];
+            if ((x > y) == ((i & k) == 0)) {
+              keys[i] = y;
+              keys[l] = x;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
-    }
-  const int nk = min(n_nodes, n_cand);
-  if (tid < nk) {
-    const int c = (int)(uint32_t)keys[tid];
-    kept[tid] = c;
-    kdep[tid] = ts.dep[base + c];
   }
-  __syncthreads();
-  if (tid < nk) {
-    const int c = kept[tid], dc = kdep[tid];
+  const int nk = min(n_nodes, n_cand);  // <= 63: the kept candidates fit one wave
+  if (tid < 64) {  // BFS number of kept candidate c: 1 + the kept candidates before it in (depth, creation) order
+    const int c = tid < nk ? (int)(uint32_t)keys[tid] : 0;
+    const int mine = tid < nk ? c_dep[c] * TREE_CMAX + c : INT_MAX;
     int pos = 1;
-    for (int o = 0; o < nk; ++o) pos += (kdep[o] < dc) || (kdep[o] == dc && kept[o] < c);
-    node_of[c] = pos;
+    for (int o = 0; o < nk; ++o) pos += __builtin_amdgcn_readlane(mine, o) < mine;
+    if (tid < nk) node_of[c] = pos;
   }
   __syncthreads();
-  const int P = seq_lens[b];
   const size_t ob = (size_t)b * rows;
   if (tid == 0) {
-    out.tokens[ob] = roots[b];
+    out.tokens[ob] = root;
     out.parents[ob] = -1;
     out.depth[ob] = 0;
     out.pos[ob] = P;
@@ -165,14 +194,14 @@ __global__ __launch_bounds__(512) void k_tree_finalize(TreeState ts, int n_cand,
   for (int c = tid; c < n_cand; c += blockDim.x) {
     const int i = node_of[c];
     if (i <= 0) continue;
-    const int pc = ts.par[base + c];
+    const int pc = c_par[c];
     const int pi = pc < 0 ? 0 : node_of[pc];
     if (pc >= 0 && pi <= 0) raise_flag(status, E3_DEV_BAD_TREE);
-    out.tokens[ob + i] = ts.tok[base + c];
+    out.tokens[ob + i] = c_tok[c];
     out.parents[ob + i] = pi;
-    out.depth[ob + i] = ts.dep[base + c];
-    out.pos[ob + i] = P + ts.dep[base + c];
-    out.score[ob + i] = ts.score[base + c];
+    out.depth[ob + i] = c_dep[c];
+    out.pos[ob + i] = P + c_dep[c];
+    out.score[ob + i] = c_score[c];
     pidx[i] = pi;
   }
   __syncthreads();
