@@ -60,25 +60,33 @@ E3_DEV bool cand_better(float sa, int ca, float sb, int cb) { return sa > sb || 
 __global__ __launch_bounds__(256) void k_tree_frontier(TreeState ts, int d, const int* __restrict__ seq_lens,
                                                        DraftRows dr, int S_cap, int* status) {
   __shared__ float sc_s[256];  // k * k <= 256 (k <= 16)
+  __shared__ int tok_s[256], par_s[256], front_s[16];
   const int b = blockIdx.x, k = ts.topk;
   const int c0 = d == 1 ? 0 : k + (d - 2) * k * k;
   const int n = d == 1 ? k : k * k;
   const size_t base = (size_t)b * ts.cmax;
-  for (int c = threadIdx.x; c < n; c += blockDim.x) sc_s[c] = ts.score[base + c0 + c];
+  const int P = seq_lens[b];
+  for (int c = threadIdx.x; c < n; c += blockDim.x) {  // the level's candidates, read once
+    sc_s[c] = ts.score[base + c0 + c];
+    tok_s[c] = ts.tok[base + c0 + c];
+    par_s[c] = ts.par[base + c0 + c];
+  }
   __syncthreads();
   for (int c = threadIdx.x; c < n; c += blockDim.x) {
     const float sc = sc_s[c];
     int rank = 0;
     for (int o = 0; o < n; ++o) rank += cand_better(sc_s[o], c0 + o, sc, c0 + c);
-    if (rank < k) ts.front[b * k + rank] = c0 + c;
+    if (rank < k) {
+      ts.front[b * k + rank] = c0 + c;
+      front_s[rank] = c;
+    }
   }
   __syncthreads();
-  const int P = seq_lens[b];
   for (int rank = threadIdx.x; rank < k; rank += blockDim.x) {
-    const int c = ts.front[b * k + rank];
+    const int cl = front_s[rank], c = c0 + cl;
     const int e = (d - 1) * k + rank;
     ts.erow[base + c] = e;
-    const int par = ts.par[base + c];
+    const int par = par_s[cl];
     const int pe = par < 0 ? -1 : ts.erow[base + par];
     const uint64_t pm = pe < 0 ? 0ull : ts.emask[(size_t)b * ts.emax + pe];
     const uint64_t m = pm | (1ull << e);
@@ -86,7 +94,7 @@ __global__ __launch_bounds__(256) void k_tree_frontier(TreeState ts, int d, cons
     const int r = b * k + rank;
     const bool fits = P >= 0 && P + e < S_cap;
     if (!fits) raise_flag(status, E3_DEV_KV_OVERFLOW);
-    dr.tok[r] = ts.tok[base + c];
+    dr.tok[r] = tok_s[cl];
     dr.src[r] = pe < 0 ? -1 - b : b * ts.emax + pe;  // -1-b: the catch-up row's a
     dr.seq[r] = fits ? b : -1;
     dr.pos[r] = P + d - 1;
