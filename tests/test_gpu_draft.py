@@ -12,6 +12,8 @@ own logits (integer parity given equal logits), and, where the seed's
 decisions clear the measured logits error (asserted for the toy seed), the
 one the oracle makes from its own logits.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -61,20 +63,26 @@ def _check_ranked(picks, ref, k, tol):
     return strict
 
 
-def test_draft_stage_bf16_mfma_matches_oracle():
+@pytest.mark.parametrize("dv,seed", [(0, 39), (3000, 41)])
+def test_draft_stage_bf16_mfma_matches_oracle(dv, seed):
     """Toy bf16 model on the MFMA kernels (d 256, 4x64 heads over 2 KV heads, FFN
     512, vocabulary 10,240 so the draft LM head takes the wide 16-row GEMM): the
     whole draft stage after a 40-token prefill, depth 4, top-3, 10 nodes.  The
     oracle starts from the GPU prefill's outputs (tap row, root, committed draft
     K/V), so the comparison covers exactly the draft stage: catch-up (fusion FC,
     decoder layer), every expansion (speculative draft K/V seen by descendants
-    only) and the LM head."""
+    only) and the LM head.  dv > 0: the draft's own head over a reduced vocabulary
+    of dv ids (a partial last 128-id slice), its rows over draft ids and the tree's
+    tokens mapped through d2t ("EAGLE-3: Engineering Implementation of LLM
+    Inference Acceleration", VIII.5-VIII.6)."""
     ms = toy_shape(dtype="bf16", vocab=10240, layers=2)
+    if dv:
+        ms = dataclasses.replace(ms, draft_vocab=dv)
     D, k, N, P = 4, 3, 10, 40
     spec = Spec("greedy_tree", D, k, N)
-    shp, W, H = oracle_weights(ms, seed=39, sigma=0.07)
+    shp, W, H = oracle_weights(ms, seed=seed, sigma=0.07)
     prompt = synth.tokens_np(42, "p", P, ms.vocab)
-    eng = make_engine(ms, spec, max_seq=128, seed=39, sigma=0.07)
+    eng = make_engine(ms, spec, max_seq=128, seed=seed, sigma=0.07)
     eng.prefill([prompt])
     # the draft stage's inputs as the GPU's prefill left them: the tap row of position P - 1, the root and
     # the committed draft K/V of positions [0, P - 1)
@@ -108,7 +116,8 @@ def test_draft_stage_bf16_mfma_matches_oracle():
         nxt[0] += len(info)
         return out
 
-    implied = build_dynamic_tree(root, table[0], from_table, D, k, N)
+    d2t = H.get("d2t")
+    implied = build_dynamic_tree(root, table[0], from_table, D, k, N, d2t)
     assert g_tok == implied.tokens and g_par == implied.parents
     assert np.array_equal(g_score, np.array(implied.score, dtype=np.float32))
 
@@ -125,7 +134,7 @@ def test_draft_stage_bf16_mfma_matches_oracle():
 
     # (3) the oracle's own tree from its own logits: equal to the GPU's when the seed's decisions clear the
     #     measured error (asserted, so the seed is not near a tie)
-    own = tree_from_table(root, np.stack(rows), D, k, N)
+    own = tree_from_table(root, np.stack(rows), D, k, N, d2t)
     ok, lg, sg = _clearance(own, rows, k, D, eps)
     print(f"\n  draft logits max err per row {np.round(errs, 5).tolist()}; decision gaps: logits {lg:.4f}, "
           f"scores {sg:.4f}", flush=True)
