@@ -61,7 +61,7 @@ struct eagle3_ctx {
   KvPages pg;                   // block table of a paged cache (pg.bt null: contiguous)
   size_t kv_us, kv_hs, kv_le;   // unit stride, head stride, elements per layer's K (or V) array
   const int* ndraft = nullptr;  // per-request draft lengths (device, [max_batch]) or null
-  float* dl_out = nullptr;      // draft logits table [max_batch, 1 + emax, Vd] (parity output) or null
+  float* dl_out = nullptr;      // draft logits table [max_batch, tab_rows, Vd] (parity output) or null
   float* hid_out = nullptr;     // verify residual streams [n_layers + 1, R, d] (parity output) or null
   // workspace
   int* status;
@@ -87,6 +87,7 @@ struct eagle3_ctx {
   TreeState ts;
   int* chain_tok;
   int emax, n_cand;
+  int tab_rows;  // rows per sequence of a draft-logits table: the root row + (depth - 1) * topk expansions
   // profiling
   bool prof = false;
   std::vector<ProfRec> recs;
@@ -151,7 +152,8 @@ size_t carve(eagle3_ctx* c, char* base) {
   c->gidx = cv.take<int>(R);
   c->roots = cv.take<int>(B);
   const int D = c->cfg.depth, k = c->cfg.topk;
-  c->emax = std::max(1, (D - 1) * k);
+  c->emax = std::max(1, (D - 1) * k);  // scratch row count, at least one so depth 1 carves no empty arrays
+  c->tab_rows = 1 + (D - 1) * k;
   c->n_cand = c->cfg.mode != EAGLE3_SAMPLE_CHAIN ? k + (D - 1) * k * k : D;
   c->a_last = cv.take<float>((size_t)B * d);
   c->a_rows = cv.take<float>((size_t)B * c->emax * d);
@@ -624,7 +626,7 @@ bool draft_lm(eagle3_ctx* c, int n, const float* a, int K, float temperature, in
   if (!fused) run_gemm(c, c->gbuf, n, s.d_model, make_segs(c->dhead, c->Vd), c->logits);
   if (c->dl_out && n > 0)
     k_copy_logit_rows<<<dim3(nb(c->Vd, 1024), n), 256, 0, c->st>>>(c->logits, per, c->Vd, c->dl_out,
-                                                                   (size_t)(1 + c->emax) * c->Vd, row0);
+                                                                   (size_t)c->tab_rows * c->Vd, row0);
   if (!fused)
     topk_lse(c->logits, n, c->Vd, c->Vd, K, temperature, c->tk_pv, c->tk_pi, c->tk_pmax, c->tk_psum, c->tk_ids,
              c->tk_vals, c->tk_lse, c->tk_lse64, c->st);
@@ -655,7 +657,7 @@ eagle3_status build_tree(eagle3_ctx* c, int batch, const int* seq_lens, const fl
   ts.batch = batch;
   DraftRows dr = c->dr;
   dr.batch = batch;
-  const size_t tstride = (size_t)(1 + c->emax) * Vd;  // table row stride between sequences
+  const size_t tstride = (size_t)c->tab_rows * Vd;  // table row stride between sequences
   if (c->cfg.mode != EAGLE3_SAMPLE_CHAIN) {  // trees (greedy or sampled acceptance alike)
     if (!root_kids_done) tree_children(ts, 1, c->tk_ids, c->tk_vals, c->tk_lse, k, st);
     for (int dd = 1; dd < D; ++dd) {
@@ -1047,7 +1049,7 @@ eagle3_status eagle3_tree_from_logits(eagle3_ctx* c, int32_t batch, const int32_
   const bool chain = c->cfg.mode == EAGLE3_SAMPLE_CHAIN;
   if (chain && ((!uniforms && !c->cfg.draft_greedy) || !q)) return EAGLE3_EINVAL;
   const int Vd = c->Vd;
-  const size_t tstride = (size_t)(1 + c->emax) * Vd;
+  const size_t tstride = (size_t)c->tab_rows * Vd;
   k_seq_roots<<<nb(batch, 64), 64, 0, c->st>>>(batch, 0, roots, c->roots);
   const int K = chain ? 1 : c->cfg.topk;
   const float T = chain ? c->cfg.temperature : 1.f;

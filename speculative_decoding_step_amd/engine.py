@@ -197,7 +197,7 @@ class Engine:
         the root's draft row, row 1 + r expansion row r in creation order."""
         if on:
             s = self.spec
-            e = max(1, (s.depth - 1) * s.topk) if not self.chain else max(1, s.depth - 1)
+            e = (s.depth - 1) * s.topk  # a chain has topk 1
             vd = self.ms.draft_vocab or self.ms.vocab
             self.draft_table = torch.full((self.B, 1 + e, vd), float("nan"), dtype=torch.float32, device=self.dev)
             B.eagle3_set_draft_logits_out(self.ctx, self.draft_table.data_ptr())

@@ -84,6 +84,29 @@ def test_toy_tree_end_to_end_with_acceptance(dtype):
     eng.close()
 
 
+@pytest.mark.parametrize("D,k,N", [(1, 3, 3), (2, 1, 1), (6, 1, 6), (2, 8, 12)])
+def test_degenerate_trees_end_to_end(D, k, N):
+    """Trees at the edges of the budget: one level (the root's children only), a
+    single draft node, a chain of single children, and a wide shallow tree whose N is
+    not a multiple of k.  Greedy speculative output is vanilla greedy output and every
+    accepted path fits the tree ("Advanced speculative decoding: tree drafts and
+    EAGLE", Implementation: the accepted path is the longest prefix the target agrees
+    with, so the output is the target's own greedy sequence)."""
+    ms = toy_shape(dtype="f32", vocab=64, layers=2)
+    spec = Spec("greedy_tree", D, k, N)
+    shp, W, H = oracle_weights(ms, seed=21, sigma=0.3)
+    prompt = synth.tokens_np(43, "p", 20, ms.vocab)
+    ref = vanilla_generate(W, shp, prompt, 30)
+    eng = make_engine(ms, spec, max_seq=128, seed=21, sigma=0.3)
+    out, lens = eng.generate([prompt], 30)
+    assert eng.device_status() == 0
+    n, strict = _compare(out[0], ref, W, shp, prompt)
+    pl = [int(x[0]) for x in lens]
+    print(f"\n  D{D} k{k} N{N}: identical for {n}/30, strict {strict}, path lengths {pl}", flush=True)
+    assert strict >= 15 and max(pl) <= D + 1
+    eng.close()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_toy_tree_reduced_draft_vocab_end_to_end(dtype):
     """A draft head over 40 of the 64 ids (own head, d2t): greedy speculative output is

@@ -38,14 +38,15 @@ def _implied_tree(table, root, D, k, N):
     return build_dynamic_tree(root, table[0], from_table, D, k, N)
 
 
-@pytest.mark.parametrize("Bn,D,k,N", [(1, 3, 16, 20), (1, 5, 15, 63), (2, 4, 8, 32)])
+@pytest.mark.parametrize("Bn,D,k,N", [(1, 3, 16, 20), (1, 5, 15, 63), (2, 4, 8, 32), (3, 1, 6, 6)])
 def test_fused_head_topk_tree_and_verify_argmax(Bn, D, k, N):
     """Greedy trees with top-k up to 16 over a vocabulary ending in a partial slice:
     each sequence's tree (ids, parents, fp32 scores) equals the oracle's builder over
     the GPU's own draft logits table, so every draft row's ranked top-k and
     log-sum-exp are exact (draft passes of 16 and 32 rows); the verify's argmax and
     top-2 margin equal the oracle's on the GPU's verify logits for every row (21
-    and 64 rows in the fused kernels, 2 x 33 rows on the large-M path)."""
+    and 64 rows in the fused kernels, 2 x 33 rows on the large-M path).  Depth 1
+    (the root's children only) keeps one table row per sequence."""
     ms = toy_shape(dtype="bf16", vocab=VOCAB, layers=2)
     spec = Spec("greedy_tree", D, k, N)
     eng = make_engine(ms, spec, batch=Bn, max_seq=192, seed=57, sigma=0.07)
@@ -61,6 +62,7 @@ def test_fused_head_topk_tree_and_verify_argmax(Bn, D, k, N):
     table = eng.draft_table.cpu().numpy()
     g_tok, g_par = eng.tokens.cpu().numpy(), eng.parents.cpu().numpy()
     g_score = eng.score.cpu().numpy()
+    assert table.shape == (Bn, 1 + (D - 1) * k, ms.vocab) and not np.isnan(table).any()
     rows = Bn * (N + 1)
     lg = eng.logits.cpu().numpy().reshape(-1, ms.vocab)[:rows]
     am = eng.argmax.cpu().numpy()[:rows]
@@ -77,13 +79,15 @@ def test_fused_head_topk_tree_and_verify_argmax(Bn, D, k, N):
         assert mg[r] == np.float32(lg[r][t2[0]] - lg[r][t2[1]]), (r, mg[r])
 
 
-def test_fused_head_sampled_chain_q_rows():
-    """Sampled chain (K = 4, T = 0.7, batch 3) on the fused draft head: every q row
-    the draft outputs equals exp(z / T - lse) with the log-sum-exp taken by the
-    oracle (float64, by definition) over the GPU's own draft logits row z, and
-    every draft token is the inverse-CDF draw from that row."""
+@pytest.mark.parametrize("K", [4, 1])
+def test_fused_head_sampled_chain_q_rows(K):
+    """Sampled chain (K = 4 and the one-draft chain, T = 0.7, batch 3) on the fused
+    draft head: every q row the draft outputs equals exp(z / T - lse) with the
+    log-sum-exp taken by the oracle (float64, by definition) over the GPU's own
+    draft logits row z, and every draft token is the inverse-CDF draw from that
+    row."""
     ms = toy_shape(dtype="bf16", vocab=VOCAB, layers=2)
-    K, Bn, T = 4, 3, 0.7
+    Bn, T = 3, 0.7
     spec = Spec("sample_chain", K, 1, K, T)
     eng = make_engine(ms, spec, batch=Bn, max_seq=96, seed=61, sigma=0.07)
     prompts = [list(synth.tokens_np(62 + b, "p", 24 + 5 * b, ms.vocab)) for b in range(Bn)]
@@ -100,6 +104,7 @@ def test_fused_head_sampled_chain_q_rows():
     toks = eng.tokens.cpu().numpy()
     ud = u_d.cpu().numpy()
     eng.close()
+    assert table.shape == (Bn, K, ms.vocab) and not np.isnan(table).any()
 
     worst, mism = 0.0, 0
     for b in range(Bn):
