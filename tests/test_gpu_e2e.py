@@ -293,11 +293,13 @@ def test_sampled_tree_first_token_distribution_v64():
     eng.close()
 
 
-def test_sampled_tree_steps_match_oracle_f32():
-    """Tree drafts accepted by rejection sampling, six steps on an fp32 toy model: every
-    step's tree, accepted path and next token equal the oracle's for the same uniforms."""
+@pytest.mark.parametrize("D,k,N", [(3, 3, 8), (1, 4, 4)])
+def test_sampled_tree_steps_match_oracle_f32(D, k, N):
+    """Tree drafts accepted by rejection sampling, eight steps on an fp32 toy model: every
+    step's tree, accepted path and next token equal the oracle's for the same uniforms
+    (also for a one-level tree, whose root children are the only candidates)."""
     ms = toy_shape(dtype="f32", vocab=96, layers=2)
-    D, k, N, T = 3, 3, 8, 0.8
+    T = 0.8
     spec = Spec("sample_tree", D, k, N, T)
     shp, W, H = oracle_weights(ms, seed=29, sigma=0.3)
     prompt = synth.tokens_np(52, "p", 24, ms.vocab)
@@ -309,8 +311,10 @@ def test_sampled_tree_steps_match_oracle_f32():
     assert eng.next_tok[0, 0].item() == seq.root
     nu = eng.n_u_accept
     lens = []
-    for s in range(6):
+    for s in range(8):
         u = synth.uniform24_t(5000, f"u_acc{s}", nu, "cuda").view(1, nu)
+        if s % 2:  # uniforms scaled by 2^-24 (exact): acceptances under the peaked toy target, longer paths
+            u = u * 2.0 ** -24
         eng.set_uniforms(None, u)
         eng.step()
         tree, path, nxt = seq.step(u_accept=u.cpu().numpy()[0])
@@ -321,6 +325,7 @@ def test_sampled_tree_steps_match_oracle_f32():
         assert eng.next_root[0].item() == nxt
         lens.append(n)
     print(f"\n  accepted path lengths {lens}", flush=True)
+    assert max(lens) >= 2
     eng.close()
 
 

@@ -166,11 +166,13 @@ def test_draft_lengths_greedy_match_oracle_f32(bs):
     eng.close()
 
 
-def test_draft_lengths_sampled_chain_match_oracle_f32():
+@pytest.mark.parametrize("K", [4, 1])
+def test_draft_lengths_sampled_chain_match_oracle_f32(K):
     """Sampled chains with per-request draft lengths: the accepted count and the
-    resampled or bonus token equal the oracle's for the same uniforms."""
+    resampled or bonus token equal the oracle's for the same uniforms (K = 1: a
+    one-draft chain, lengths 0 or 1)."""
     ms = toy_shape(dtype="f32", vocab=96, layers=2)
-    K, T = 4, 0.8
+    T = 0.8
     spec = Spec("sample_chain", K, 1, K, T)
     shp, W, H = oracle_weights(ms, seed=29, sigma=0.3)
     prompts = _ragged_prompts(ms, [24, 40], 63)
@@ -179,10 +181,13 @@ def test_draft_lengths_sampled_chain_match_oracle_f32():
     eng.prefill(prompts, u_root)
     seqs = _oracle_seqs(W, H, shp, SpecConfig("sample_chain", K, 1, K, T), prompts, 128, u_root.cpu().numpy())
     rng = np.random.default_rng(10)
+    lens = []
     for step in range(8):
         nd = rng.integers(0, K + 1, size=2)
         ud = synth.uniform24_t(5001, f"d{step}", 2 * K, "cuda").view(2, K)
         ua = synth.uniform24_t(5002, f"a{step}", 2 * (K + 1), "cuda").view(2, K + 1)
+        if step % 2:  # acceptance uniforms scaled by 2^-24 (exact): the peaked toy target then accepts drafts
+            ua = ua * 2.0 ** -24
         eng.set_uniforms(ud, ua)
         eng.set_draft_lengths(nd)
         eng.step()
@@ -192,6 +197,9 @@ def test_draft_lengths_sampled_chain_match_oracle_f32():
             n = eng.path_len[s].item()
             assert list(eng.path[s].cpu().numpy()[:n]) == path, (step, s, nd[s])
             assert eng.next_root[s].item() == nxt, (step, s)
+            lens.append(n)
+    print(f"\n  path lengths {lens}", flush=True)
+    assert max(lens) >= 2
     eng.close()
 
 
