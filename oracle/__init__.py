@@ -20,9 +20,13 @@ Modules
             batch's index bookkeeping
   ttt       training-time-test attention (causal native keys + diagonal simulated keys)
 
-Functions whose result no pin fixes say "parity unpinned" in their docstring:
-  tree.build_dynamic_tree  (the frontier/re-rank policy is this build's reading
-                            of a step the pages name but do not spell out;
-                            its invariants and hand-worked cases are pinned, the
-                            policy itself is not)
+Every function is pinned by a test in tests/test_oracle_*.py.  One of them
+computes a reading rather than a formula the pages print:
+  tree.build_dynamic_tree  (the frontier / re-rank policy of a step the pages
+                            name but do not spell out; pinned against that
+                            reading by an independent enumeration of the
+                            candidates, by its k = 1 and depth-1 reductions
+                            to the greedy chain and the top-k, and by a
+                            hand-worked case; no page gives another engine's
+                            policy to compare it with)
 """

@@ -99,9 +99,11 @@ class Tree:
 
 def build_dynamic_tree(root: int, root_logits32, expand, depth: int, topk: int, n_nodes: int,
                        d2t=None) -> Tree:
-    """Dynamic draft tree ranked by cumulative draft log-probability.  Parity unpinned
-    as a policy (the pages name EAGLE-2's confidence-driven expansion and final
-    pruning but do not spell it out); the reading implemented here:
+    """Dynamic draft tree ranked by cumulative draft log-probability.  The pages
+    name EAGLE-2's confidence-driven expansion and final pruning but do not
+    spell it out; this is a reading of it, pinned against itself by an
+    independent enumeration of the candidates and against the pages by its
+    k = 1 (greedy chain) and depth-1 (top-k) reductions.  The reading:
 
     * score(root) = 0; a child's score is fl32(score(parent) + logp(child)),
       with logp from :func:`draft_logprobs_f32` of the expanded row's logits.
