@@ -79,6 +79,54 @@ def test_fused_head_topk_tree_and_verify_argmax(Bn, D, k, N):
         assert mg[r] == np.float32(lg[r][t2[0]] - lg[r][t2[1]]), (r, mg[r])
 
 
+@pytest.mark.parametrize("Bn,D,k,N", [(2, 3, 8, 20), (1, 4, 5, 17)])
+def test_fused_head_exact_ties(Bn, D, k, N):
+    """LM-head rows planted in groups of four equal rows (ids 2m, 2m + 1, 2m + 4500,
+    2m + 4501: two in one 128-id slice, two in another), so every logit value occurs
+    exactly four times: each top-k pick ties across and within slices, and the order
+    must be the lower id first (the tie rule of "Advanced speculative decoding: tree
+    drafts and EAGLE", Implementation, argmax: the first maximal index).  Trees
+    equal the oracle's builder over the GPU's own draft logits; verify argmax is
+    the lowest id of the top group and the top-2 margin is zero."""
+    ms = toy_shape(dtype="bf16", vocab=VOCAB, layers=2)
+    eng = make_engine(ms, Spec("greedy_tree", D, k, N), batch=Bn, max_seq=160, seed=67, sigma=0.07)
+    t = eng._tensor(67, "lm_head", (VOCAB, ms.d), "mat", 0.07)
+    half = 4500
+    src = (torch.arange(VOCAB, device="cuda") % half) // 2 * 2
+    eng.w["lm_head"].copy_(eng._pack(t[src].contiguous()))
+    torch.cuda.synchronize()
+    prompts = [list(synth.tokens_np(68 + b, "p", 30 + 4 * b, ms.vocab)) for b in range(Bn)]
+    eng.prefill(prompts)
+    roots = [int(eng.next_tok[b, 0]) for b in range(Bn)]
+    eng.record_draft_logits()
+    eng.logits = torch.zeros(Bn * eng.rows, ms.vocab, dtype=torch.float32, device="cuda")
+    eng.draft()
+    eng.verify()
+    torch.cuda.synchronize()
+    assert eng.device_status() == 0
+    table = eng.draft_table.cpu().numpy()
+    g_tok, g_par = eng.tokens.cpu().numpy(), eng.parents.cpu().numpy()
+    g_score = eng.score.cpu().numpy()
+    rows = Bn * (N + 1)
+    lg = eng.logits.cpu().numpy().reshape(-1, ms.vocab)[:rows]
+    am = eng.argmax.cpu().numpy()[:rows]
+    mg = eng.margin.cpu().numpy()[:rows]
+    eng.close()
+    ids = np.arange(VOCAB)
+    grp = (ids % half) // 2 * 2
+    # the ties are exact in the GPU's own logits
+    assert np.array_equal(table[..., ids], table[..., grp]) and np.array_equal(lg[:, ids], lg[:, grp])
+    for b in range(Bn):
+        implied = _implied_tree(table[b], roots[b], D, k, N)
+        assert list(g_tok[b]) == implied.tokens and list(g_par[b]) == implied.parents
+        assert np.array_equal(g_score[b], np.array(implied.score, dtype=np.float32))
+        kids = [int(x) for x in g_tok[b][1:k + 1]]
+        assert kids[:4] == sorted(kids[:4]) and len({grp[x] for x in kids[:4]}) == 1  # one tied group, ids ascending
+    for r in range(rows):
+        t2 = topk_desc(lg[r], 2)
+        assert am[r] == int(t2[0]) == grp[am[r]] and mg[r] == 0.0, (r, am[r], t2, mg[r])
+
+
 @pytest.mark.parametrize("K", [4, 1])
 def test_fused_head_sampled_chain_q_rows(K):
     """Sampled chain (K = 4 and the one-draft chain, T = 0.7, batch 3) on the fused
