@@ -603,18 +603,73 @@ void topk_lse(const float* logits, int R, int V, int ld, int K, float temperatur
   k_topk_merge<<<R, 64, 0, st>>>(ns, K, t, pv, pi, lse ? pmax : nullptr, psum, out_ids, out_vals, lse32, lse64);
 }
 
+// A (value, index) pair as a 64-bit key ordered as better() orders pairs (a
+// larger key is better): the value's bits mapped monotonically, -0.0 as +0.0
+// (the two compare equal), then the complemented index.  Values are not NaN.
+// One unsigned compare then decides what better() decides with three.
+E3_DEV uint64_t pair_key(float v, int i) {
+  unsigned u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)~(unsigned)i;
+}
+E3_DEV int pair_key_index(uint64_t k) { return (int)~(unsigned)k; }
+template <int CTRL>
+E3_DEV uint64_t key_dpp_max(uint64_t a) {
+  const unsigned lo = __builtin_amdgcn_update_dpp(0u, (unsigned)a, CTRL, 0xF, 0xF, false);
+  const unsigned hi = __builtin_amdgcn_update_dpp(0u, (unsigned)(a >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t b = ((uint64_t)hi << 32) | lo;
+  return a > b ? a : b;
+}
+E3_DEV uint64_t key_swap_max(uint64_t a, bool wide) {
+  const unsigned lo = (unsigned)a, hi = (unsigned)(a >> 32);
+  const auto l = wide ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                      : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = wide ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                      : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const uint64_t x = ((uint64_t)h[0] << 32) | l[0], y = ((uint64_t)h[1] << 32) | l[1];
+  return x > y ? x : y;
+}
+// The wave's largest key, to every lane: the exchanges of wave_best on keys.
+E3_DEV uint64_t wave_max_key(uint64_t x) {
+  x = key_dpp_max<0xB1>(x);
+  x = key_dpp_max<0x4E>(x);
+  x = key_dpp_max<0x141>(x);
+  x = key_dpp_max<0x140>(x);
+  return key_swap_max(key_swap_max(x, false), true);
+}
+// Keys among the n (non-increasing) at p that are larger than x.
+E3_DEV int keys_above(const uint64_t* p, int n, uint64_t x) {
+  int lo = 0, hi = n;  // p[0, lo) > x >= p[hi, n)
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (p[mid] > x)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
 // grid (R), block 256: merge the 128-id slices of the fused LM-head top-k.
 // The k best of a row lie in the k slices whose own best (value, id) pairs
 // rank highest: a pair among the k best has its slice's best at or above it,
 // and k slices ranked above that slice would hold k pairs above it.  So the
-// kernel first picks those k slices (a thread holds the best of up to 4
-// slices; each wave takes its k best in k rounds, wave 0 merges the four
-// lists), then wave 0 takes the k best of their k x k candidates.  The
-// log-sum-exp combines the slices' maxima and sums as the separate merge does.
+// kernel first picks those k slices: a thread holds the best of up to 4
+// slices and each wave takes its k best in k rounds (one wave-wide maximum of
+// 64-bit keys per round); a candidate's rank among the four waves' lists is
+// its place in its own list plus the keys above it in the other three.  Then
+// the k x k candidates of those slices, one per thread, are ranked the same
+// way (each slice's list is in order), and the k with ranks below k are the
+// row's k best in rank order.  Keys are distinct (distinct ids) except for
+// the (-inf, INT_MAX) filler of slots without a candidate, which never ranks
+// among real pairs.  The log-sum-exp combines the slices' maxima and sums as
+// the separate merge does.
 __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __restrict__ out_ids,
                                                            float* __restrict__ out_vals, float* __restrict__ lse32,
                                                            double* __restrict__ lse64, TreeKids kids) {
-  __shared__ VI cand[4][TK_KMAX];
+  __shared__ uint64_t wk[4][TK_KMAX];         // each wave's k best slice maxima, in order
+  __shared__ uint64_t gk[TK_KMAX * TK_KMAX];  // the chosen slices' candidates, slice-major (0: no slice)
   __shared__ VI best[TK_KMAX];
   __shared__ int sel[TK_KMAX];
   __shared__ float fred[4];
@@ -623,6 +678,7 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
   const int K = tk.k, ns = tk.ns;
   const float* cv = tk.pv + (size_t)r * ns * K;
   const int* ci = tk.pi + (size_t)r * ns * K;
+  const uint64_t FILL = pair_key(-INFINITY, 0x7fffffff);
   // the slices' log-sum-exp partials, loaded first so that their latency hides under the selection
   float pm[4];
   double ps[4];
@@ -640,28 +696,28 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
     kpar = kids.ts.front[b * k + rank];
     kps = kids.ts.score[(size_t)b * kids.ts.cmax + kpar];
   }
-  float v[4];
-  int id[4];
-  unsigned taken = 0;
+  uint64_t key[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {  // slice s = tid + 256 j: its best pair is its candidate 0
     const int sl = tid + 256 * j;
-    v[j] = sl < ns ? cv[(size_t)sl * K] : -INFINITY;
-    id[j] = sl < ns ? ci[(size_t)sl * K] : 0x7fffffff;
-    if (sl >= ns) taken |= 1u << j;
+    key[j] = sl < ns ? pair_key(cv[(size_t)sl * K], ci[(size_t)sl * K]) : FILL;
   }
-  for (int k = 0; k < K; ++k) {
-    VI b{-INFINITY, 0x7fffffff};
+  if (tid < TK_KMAX) sel[tid] = -1;
+  for (int k = 0; k < K; ++k) {  // a lane's taken keys become 0; one with nothing left offers the filler
+    uint64_t b = FILL;
     int bj = -1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool take = !((taken >> j) & 1u) & better(v[j], id[j], b.v, b.i);
-      b = take ? VI{v[j], id[j]} : b;
+      const bool take = key[j] > b;
+      b = take ? key[j] : b;
       bj = take ? j : bj;
     }
-    const VI wb = wave_best(b);
-    if (bj >= 0 && b.i == wb.i && b.v == wb.v) taken |= 1u << bj;
-    if (lane == 0) cand[w][k] = wb;
+    const uint64_t wb = wave_max_key(b);
+    if (bj >= 0 && b == wb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[j] = bj == j ? 0ull : key[j];
+    }
+    if (lane == 0) wk[w][k] = wb;
   }
   if (tk.pmax) {  // the wave's largest slice maximum, for the log-sum-exp (published by the barrier below)
     float mloc = -INFINITY;
@@ -671,55 +727,47 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
     if (lane == 0) fred[w] = wm;
   }
   __syncthreads();
-  // waves 1-3 form their log-sum-exp shares while wave 0 selects; wave 0 forms its share afterwards
+  if (w == 0 && lane < 4 * K) {  // the k best slices (a slice is known by its best id: ids of slice s are s * 128 ..)
+    const int lw = lane / K, lp = lane % K;
+    const uint64_t x = wk[lw][lp];
+    int rank = lp;
+#pragma unroll
+    for (int o = 1; o < 4; ++o) rank += keys_above(wk[(lw + o) & 3], K, x);
+    if (rank < K && x != FILL) sel[rank] = pair_key_index(x) / TOPK_SLICE;
+  }
   double sloc = 0.0, M = 0.0;
-  auto lse_share = [&]() {
+  if (tk.pmax) {  // this thread's share of the log-sum-exp
     const float mx = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
     M = (double)mx / tk.temp;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (tid + 256 * j < ns) sloc += ps[j] * exp((double)pm[j] / tk.temp - M);
-  };
-  if (tk.pmax && w > 0) lse_share();
-  if (w == 0) {
-    // the k best slices (a slice is known by its best id: ids of slice s are s * 128 ..)
-    VI mine = lane < 4 * K ? cand[lane / K][lane % K] : VI{-INFINITY, 0x7fffffff};
-    for (int k = 0; k < K; ++k) {
-      const VI wb = wave_best(mine);
-      if (mine.i == wb.i && mine.v == wb.v) mine = VI{-INFINITY, 0x7fffffff};
-      if (lane == 0) sel[k] = wb.i == 0x7fffffff ? -1 : wb.i / TOPK_SLICE;
-    }
-    // their k x k candidates, up to 4 per lane
-    VI c4[4];
-    unsigned t4 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = lane + 64 * i;
-      const int sl = c < K * K ? sel[c / K] : -1;
-      c4[i] = sl >= 0 ? VI{cv[(size_t)sl * K + c % K], ci[(size_t)sl * K + c % K]} : VI{-INFINITY, 0x7fffffff};
-      if (sl < 0) t4 |= 1u << i;
-    }
-    for (int k = 0; k < K; ++k) {
-      VI b{-INFINITY, 0x7fffffff};
-      int bj = -1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool take = !((t4 >> i) & 1u) & better(c4[i].v, c4[i].i, b.v, b.i);
-        b = take ? c4[i] : b;
-        bj = take ? i : bj;
-      }
-      const VI wb = wave_best(b);
-      if (bj >= 0 && b.i == wb.i && b.v == wb.v) t4 |= 1u << bj;
-      if (lane == 0) {
-        const int id = kids.d2t ? (wb.i >= 0 && wb.i < kids.Vd ? kids.d2t[wb.i] : -1) : wb.i;
-        out_ids[(size_t)r * K + k] = id;
-        out_vals[(size_t)r * K + k] = wb.v;
-        best[k] = VI{wb.v, id};
-      }
+  }
+  __syncthreads();
+  // the chosen slices' k x k candidates, one per thread
+  const int li = tid / K, lp = tid % K;
+  const int sl = tid < K * K ? sel[li] : -1;
+  float cval = -INFINITY;
+  int cid = 0x7fffffff;
+  if (sl >= 0) {
+    cval = cv[(size_t)sl * K + lp];
+    cid = ci[(size_t)sl * K + lp];
+  }
+  const uint64_t x = sl >= 0 ? pair_key(cval, cid) : 0ull;
+  if (tid < K * K) gk[tid] = x;
+  __syncthreads();
+  if (sl >= 0) {
+    int rank = lp;
+    for (int o = 0; o < K; ++o)
+      if (o != li) rank += keys_above(gk + o * K, K, x);
+    if (rank < K) {
+      const int id = kids.d2t ? (cid >= 0 && cid < kids.Vd ? kids.d2t[cid] : -1) : cid;
+      out_ids[(size_t)r * K + rank] = id;
+      out_vals[(size_t)r * K + rank] = cval;
+      best[rank] = VI{cval, id};
     }
   }
   if (!tk.pmax) return;  // uniform: no log-sum-exp asked for
-  if (w == 0) lse_share();
   const double sw = wave_sum_d_reg(sloc);
   if (lane == 0) dred[w] = sw;
   __syncthreads();
@@ -733,14 +781,14 @@ __global__ __launch_bounds__(256) void k_topk_merge_slices(SliceTopk tk, int* __
       const int b = dn == 1 ? r : r / k, rank = dn == 1 ? 0 : r % k;
       const int c0 = (dn == 1 ? 0 : k + (dn - 2) * k * k) + rank * k;
       const int par = dn > 1 ? kpar : -1;
-      const float ps = dn > 1 ? kps : 0.f;
+      const float ps0 = dn > 1 ? kps : 0.f;
       const float l32 = (float)l;
       for (int ch = 0; ch < k; ++ch) {
         const size_t o = (size_t)b * ts.cmax + c0 + ch;
         ts.tok[o] = best[ch].i;
         ts.par[o] = par;
         ts.dep[o] = dn;
-        ts.score[o] = ps + (best[ch].v - l32);
+        ts.score[o] = ps0 + (best[ch].v - l32);
         ts.erow[o] = -1;
       }
     }
