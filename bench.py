@@ -474,7 +474,7 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the step shards by sequence "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the step shards by sequence "
               "with no exchange; run one process per GPU). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.workload == "ttt_attn_8b":
