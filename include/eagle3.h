@@ -153,7 +153,8 @@ eagle3_status eagle3_workspace_bytes(const eagle3_shape *shape, const eagle3_spe
 
 /* Create a context.  All pointers are borrowed.  `stream` is a hipStream_t
  * (NULL = the null stream).  Returns EINVAL for an inconsistent shape or cfg
- * and EUNSUPPORTED for n_nodes + 1 > 64 or (depth - 1) * topk > 64. */
+ * (among them a tree of more nodes than its topk + (depth - 1) * topk^2
+ * candidates) and EUNSUPPORTED for n_nodes + 1 > 64 or (depth - 1) * topk > 64. */
 eagle3_status eagle3_create(const eagle3_shape *shape /* host */, const eagle3_spec_cfg *cfg /* host */,
                             const eagle3_target_weights *target /* host struct */,
                             const eagle3_head_weights *head /* host struct */,

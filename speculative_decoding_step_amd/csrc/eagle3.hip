@@ -202,7 +202,8 @@ eagle3_status check_shape(const eagle3_shape* s, const eagle3_spec_cfg* c) {
   if (c->n_nodes + 1 > 64 || (c->depth - 1) * c->topk > 64) return EAGLE3_EUNSUPPORTED;
   if (c->mode == EAGLE3_GREEDY_TREE || c->mode == EAGLE3_SAMPLE_TREE) {
     const int nc = c->topk + (c->depth - 1) * c->topk * c->topk;
-    if (nc < c->n_nodes || nc > TREE_CMAX) return EAGLE3_EUNSUPPORTED;
+    if (nc < c->n_nodes) return EAGLE3_EINVAL;  // more nodes than the tree has candidates
+    if (nc > TREE_CMAX) return EAGLE3_EUNSUPPORTED;
     if (c->mode == EAGLE3_SAMPLE_TREE && !(c->temperature > 0.f)) return EAGLE3_EINVAL;
   } else if (c->mode == EAGLE3_SAMPLE_CHAIN) {
     if (c->topk != 1 || c->n_nodes != c->depth || !(c->temperature > 0.f)) return EAGLE3_EINVAL;

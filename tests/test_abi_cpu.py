@@ -40,9 +40,17 @@ def test_sizes_and_validation():
                       (B.SpecCfg(B.GREEDY_TREE, 8, 10, 60, 0.0, 0), "unsupported"),   # 70 draft rows
                       (B.SpecCfg(B.SAMPLE_CHAIN, 5, 2, 5, 1.0, 0), "invalid"),         # chain needs k = 1
                       (B.SpecCfg(B.SAMPLE_CHAIN, 5, 1, 5, 0.0, 0), "invalid"),         # and T > 0
-                      (B.SpecCfg(B.GREEDY_TREE, 1, 17, 4, 0.0, 0), "invalid")]:        # k <= 16
+                      (B.SpecCfg(B.GREEDY_TREE, 1, 17, 4, 0.0, 0), "invalid"),         # k <= 16
+                      (B.SpecCfg(B.GREEDY_TREE, 1, 3, 4, 0.0, 0), "invalid"),          # one level: 3 candidates
+                      (B.SpecCfg(B.GREEDY_TREE, 2, 2, 7, 0.0, 0), "invalid"),          # 2 + 4 candidates
+                      (B.SpecCfg(B.GREEDY_TREE, 0, 2, 1, 0.0, 0), "invalid"),          # depth >= 1
+                      (B.SpecCfg(B.GREEDY_TREE, 3, 2, 0, 0.0, 0), "invalid")]:         # n_nodes >= 1
         with pytest.raises(B.Eagle3Error, match=code):
             B.eagle3_workspace_bytes(s, bad, 1, 512, 2304)
+    for edge in [B.SpecCfg(B.GREEDY_TREE, 1, 3, 3, 0.0, 0), B.SpecCfg(B.GREEDY_TREE, 2, 2, 6, 0.0, 0),
+                 B.SpecCfg(B.GREEDY_TREE, 1, 1, 1, 0.0, 0), B.SpecCfg(B.SAMPLE_CHAIN, 1, 1, 1, 0.7, 0),
+                 B.SpecCfg(B.SAMPLE_TREE, 1, 4, 4, 0.8, 0)]:                     # the degenerate trees are valid
+        assert B.eagle3_workspace_bytes(s, edge, 1, 512, 2304) > 0
     odd = B.Shape(2, 300, 4, 2, 64, 512, 1000, 1e4, 1e-5, B.BF16, (C.c_int32 * 3)(0, 1, 1))
     with pytest.raises(B.Eagle3Error, match="unsupported"):                         # bf16 needs d % 256
         B.eagle3_workspace_bytes(odd, ok, 1, 64, 128)
