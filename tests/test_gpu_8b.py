@@ -359,3 +359,35 @@ def test_8b_batch64_paged_step_with_draft_lengths():
     assert (plen[nd == 0] == 1).all()
     a.close()
     b.close()
+
+
+def test_8b_graph_replay_matches_eager_steps():
+    """Config 3 in the form the measurement times it: the whole step (draft,
+    verify, accept, compact) captured once as a HIP graph and replayed, with
+    eager work and synchronisations between the replays, gives bit-identical
+    trees, accepted paths, next tokens and target K/V to eager steps of a
+    second engine built from the same seeds."""
+    w = configs.WORKLOADS["llama8b_tree_b1"]
+    ms = w.shape
+    prompt = configs.prompts_np(w)[0]
+    print(f"\n[8B graph replay] P={len(prompt)}", flush=True)
+    a = Engine(ms, Spec.of(w), 1, w.prompt_len + 256, w.target_seed, w.head_seed, prefill_chunk=512)
+    b = Engine(ms, Spec.of(w), 1, w.prompt_len + 256, w.target_seed, w.head_seed, prefill_chunk=512)
+    a.prefill([prompt])
+    b.prefill([prompt])
+    torch.cuda.synchronize()
+    assert torch.equal(a.kv_target, b.kv_target) and torch.equal(a.next_tok, b.next_tok)
+    b.capture()
+    for i in range(4):
+        a.step()
+        b.replay()
+        torch.cuda.synchronize()
+        _ = b.seq_lens.sum().item()            # eager work between replays
+        for name in ("tokens", "parents", "mask", "path", "path_len", "next_root", "seq_lens", "next_tok",
+                     "argmax"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), (i, name)
+        assert torch.equal(a.kv_target, b.kv_target), i
+        print(f"  step {i}: path length {int(a.path_len[0])}, next root {int(a.next_root[0])}", flush=True)
+    assert a.device_status() == 0 and b.device_status() == 0
+    a.close()
+    b.close()
