@@ -391,3 +391,34 @@ def test_8b_graph_replay_matches_eager_steps():
     assert a.device_status() == 0 and b.device_status() == 0
     a.close()
     b.close()
+
+
+def test_8b_batch64_graph_replay_matches_eager_steps():
+    """Config 5 (64 ragged prompts, planned attention with one chunk per item) as
+    the measurement times it: the captured step graph, replayed twice, equals two
+    eager steps of a second engine bit for bit (trees, paths, next tokens, caches)."""
+    w = configs.WORKLOADS["llama8b_tree_b64"]
+    ms, Bn = w.shape, w.batch
+    prompts = configs.prompts_np(w)
+    max_seq = int(max(len(p) for p in prompts)) + 64
+    print(f"\n[8B batch {Bn} graph replay]", flush=True)
+    a = Engine(ms, Spec.of(w), Bn, max_seq, w.target_seed, w.head_seed, prefill_chunk=512)
+    b = Engine(ms, Spec.of(w), Bn, max_seq, w.target_seed, w.head_seed, prefill_chunk=512)
+    a.prefill(prompts)
+    b.prefill(prompts)
+    torch.cuda.synchronize()
+    print("  prefill done", flush=True)
+    b.capture()
+    for i in range(2):
+        a.step()
+        b.replay()
+        torch.cuda.synchronize()
+        _ = b.seq_lens.sum().item()
+        for name in ("tokens", "parents", "mask", "path", "path_len", "next_root", "seq_lens", "next_tok",
+                     "argmax"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), (i, name)
+        assert torch.equal(a.kv_target, b.kv_target) and torch.equal(a.kv_draft, b.kv_draft), i
+        print(f"  step {i}: path lengths {np.bincount(a.path_len.cpu().numpy()).tolist()}", flush=True)
+    assert a.device_status() == 0 and b.device_status() == 0
+    a.close()
+    b.close()
