@@ -38,16 +38,19 @@ def _implied_tree(table, root, D, k, N):
     return build_dynamic_tree(root, table[0], from_table, D, k, N)
 
 
-@pytest.mark.parametrize("Bn,D,k,N", [(1, 3, 16, 20), (1, 5, 15, 63), (2, 4, 8, 32), (3, 1, 6, 6)])
-def test_fused_head_topk_tree_and_verify_argmax(Bn, D, k, N):
+@pytest.mark.parametrize("Bn,D,k,N,V", [(1, 3, 16, 20, VOCAB), (1, 5, 15, 63, VOCAB), (2, 4, 8, 32, VOCAB),
+                                        (3, 1, 6, 6, VOCAB), (2, 3, 8, 20, 140000)])
+def test_fused_head_topk_tree_and_verify_argmax(Bn, D, k, N, V):
     """Greedy trees with top-k up to 16 over a vocabulary ending in a partial slice:
     each sequence's tree (ids, parents, fp32 scores) equals the oracle's builder over
     the GPU's own draft logits table, so every draft row's ranked top-k and
     log-sum-exp are exact (draft passes of 16 and 32 rows); the verify's argmax and
     top-2 margin equal the oracle's on the GPU's verify logits for every row (21
     and 64 rows in the fused kernels, 2 x 33 rows on the large-M path).  Depth 1
-    (the root's children only) keeps one table row per sequence."""
-    ms = toy_shape(dtype="bf16", vocab=VOCAB, layers=2)
+    (the root's children only) keeps one table row per sequence.  A vocabulary of
+    140,000 ids (over the 1,024 slices the fused epilogue takes) runs the heads
+    with a separate top-k pass over their logits."""
+    ms = toy_shape(dtype="bf16", vocab=V, layers=2)
     spec = Spec("greedy_tree", D, k, N)
     eng = make_engine(ms, spec, batch=Bn, max_seq=192, seed=57, sigma=0.07)
     prompts = [list(synth.tokens_np(58 + b, "p", 40 - 3 * b, ms.vocab)) for b in range(Bn)]

@@ -212,7 +212,9 @@ def test_tree_from_logits_hand_worked_golden():
 @pytest.mark.parametrize("D,k,N,V,Bn", [(6, 4, 32, 32000, 2), (6, 10, 60, 128256, 1), (4, 4, 16, 5000, 3),
                                         (4, 1, 4, 1024, 2), (3, 2, 5, 7, 4),
                                         # degenerate shapes: one level, a single node, one node per level
-                                        (1, 5, 5, 300, 2), (2, 3, 1, 50, 1), (1, 1, 1, 16, 3), (6, 1, 6, 90, 2)])
+                                        (1, 5, 5, 300, 2), (2, 3, 1, 50, 1), (1, 1, 1, 16, 3), (6, 1, 6, 90, 2),
+                                        # the largest vocabulary and top-k the library takes (64 slices of 4096)
+                                        (3, 16, 40, 262144, 1)])
 def test_tree_from_logits_matches_oracle(D, k, N, V, Bn):
     print(f"\n[tree D{D} k{k} N{N} V{V} B{Bn}]", flush=True)
     rng = np.random.default_rng(D * 1000 + k * 100 + N)
