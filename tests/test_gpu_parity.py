@@ -356,9 +356,10 @@ def _chain_inputs(rng, Bn, K, V, T):
     return logits, q, drafts
 
 
-def test_accept_chain_matches_oracle():
+@pytest.mark.parametrize("V,Bn", [(4000, 16), (262144, 6)])
+def test_accept_chain_matches_oracle(V, Bn):
     rng = np.random.default_rng(4)
-    K, V, Bn, T = 5, 4000, 16, 1.0
+    K, T = 5, 1.0
     eng = _tree_engine(K, 1, K, V, mode="sample_chain", T=T, batch=Bn)
     logits, q, drafts = _chain_inputs(rng, Bn, K, V, T)
     u = (rng.integers(0, 1 << 24, size=(Bn, K + 1)) * 2.0 ** -24).astype(np.float32)
