@@ -415,13 +415,15 @@ def _random_tree(rng, D, k, N, V):
             [depth[o] for o in order])
 
 
-@pytest.mark.parametrize("T", [1.0, 0.7])
-def test_accept_tree_matches_oracle(T):
+@pytest.mark.parametrize("T,V,Bn,bump", [(1.0, 3000, 24, (2.0, 7.0)), (0.7, 3000, 24, (2.0, 7.0)),
+                                         (1.0, 262144, 16, (10.0, 15.0))])
+def test_accept_tree_matches_oracle(T, V, Bn, bump):
     """Level-by-level rejection sampling over trees: path, path length, next token and the
     emitted row equal the oracle's bit for bit on random trees, target rows that favour
-    each node's candidates (so long paths occur) and seeded uniforms."""
+    each node's candidates (so long paths occur) and seeded uniforms; also at the largest
+    vocabulary (262,144 ids)."""
     rng = np.random.default_rng(11)
-    D, k, N, V, Bn = 4, 3, 14, 3000, 24
+    D, k, N = 4, 3, 14
     eng = _tree_engine(D, k, N, V, mode="sample_tree", T=T, batch=Bn)
     R = N + 1
     toks = np.zeros((Bn, R), np.int32)
@@ -435,7 +437,7 @@ def test_accept_tree_matches_oracle(T):
     logits = rng.normal(0, 1.0, size=(Bn, R, V)).astype(np.float32)
     for b in range(Bn):
         for i in range(1, R):
-            logits[b, pars[b, i], toks[b, i]] += rng.uniform(2.0, 7.0)
+            logits[b, pars[b, i], toks[b, i]] += rng.uniform(*bump)
     nu = D * k + 1
     u = (rng.integers(0, 1 << 24, size=(Bn, nu)) * 2.0 ** -24).astype(np.float32)
     maxp = D + 1
